@@ -1,0 +1,211 @@
+"""Plain CPU fp64 oracle of the Mixtral-style sparse MoE feed-forward layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the package entry's smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code with the HIP path; the
+two meet only in the seeded inputs they are both handed.
+
+Every step follows the definitions on the pages, in fp64, with numpy's matmul
+and sort as library primitives and no blocking, fusion or reordering beyond
+what the definitions state:
+
+* "Mistral/Mixtralのアーキテクチャ" (disassemble-channel.com), section
+  "Top-2ゲーティングの定式化": router scores s = W_g x with no bias term;
+  the top-2 indices i1, i2 with s_i1 >= s_i2; gates g_ik = exp(s_ik) /
+  (exp(s_i1) + exp(s_i2)), a softmax over the selected scores only; and
+  MoE(x) = g_i1 E_i1(x) + g_i2 E_i2(x).
+* same page, section "各エキスパートの構造": E_i(x) applies SiLU to W1 x,
+  multiplies elementwise by W3 x and projects with W2, where W1, W3 are
+  d_ff x d_model, W2 is d_model x d_ff and SiLU(z) = z * sigma(z).  The
+  equation as printed right-multiplies by W2, which does not type-check with
+  those shapes; the page's SwiGLUExpert code (section "MoEレイヤー全体の実装")
+  applies w2 to silu(w1 x) * w3 x, and that reading is taken here.
+* same page, section "ロードバランス損失": f_i, p_i and L_balance.
+* "Mixtral of Experts" (singularity-lens.com), the layer-output formula
+  y = sum_i g_i(x) E_i(x) with g(x) = Softmax(KeepTopK(H(x), 2)) and
+  H(x)_i = (x . W_g)_i: the router matrix is stored here as W_router[d][E],
+  the orientation of that formula.
+
+Readings where the pages are silent (each also listed in the design notes):
+top-k is generalised from top-2 to any 1 <= k <= E; equal scores are broken
+in favour of the lower expert index, both for membership and for order; an
+optional per-expert router bias (an extension the pages do not have) is added
+to the scores before both the selection and the softmax; every token is
+routed to exactly k experts (no capacity limit or token dropping).
+
+Parity pins: every function here is pinned by tests/test_oracle_pins.py
+against closed forms, brute force and special cases fixed by the pages.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# input decoding (exact): bf16 patterns -> float64, float32 -> float64
+# ----------------------------------------------------------------------------
+
+def to_f64(a: np.ndarray) -> np.ndarray:
+    """Exact conversion of a host array to float64.  uint16 arrays hold
+    bfloat16 bit patterns (the top half of a float32)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if a.dtype in (np.float32, np.float64):
+        return a.astype(np.float64)
+    raise TypeError(f"unsupported dtype {a.dtype}")
+
+
+# ----------------------------------------------------------------------------
+# router
+# ----------------------------------------------------------------------------
+
+def router_logits(x, W_router, bias=None) -> np.ndarray:
+    """Scores s[t][e] = sum_j x[t][j] * W_router[j][e]  (+ bias[e]).
+
+    "Top-2ゲーティングの定式化" eq. s = W_g x (W_g in R^{N x d}); stored
+    transposed as W_router[d][E], i.e. H(x)_i = (x . W_g)_i of the
+    "Mixtral of Experts" layer formula.  The pages' router has no bias; the
+    optional bias is an extension used only by the skewed workload."""
+    s = to_f64(x) @ to_f64(W_router)
+    if bias is not None:
+        s = s + to_f64(bias)[None, :]
+    return s
+
+
+def select_topk(s: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest scores per token, in descending score order;
+    equal scores go to the lower expert index first.
+
+    "Top-2ゲーティングの定式化": {i1, i2} = Top-2(s) with s_i1 >= s_i2,
+    generalised to k."""
+    T, E = s.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    order = np.argsort(-s, axis=1, kind="stable")
+    return np.ascontiguousarray(order[:, :k])
+
+
+def topk_gates(s: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Gate weights: softmax over the selected scores only.
+
+    "Top-2ゲーティングの定式化" eq. g_ik = exp(s_ik) / sum_l exp(s_il).
+    Subtracting the largest selected score first leaves the ratio unchanged
+    and keeps exp finite."""
+    sel = np.take_along_axis(s, idx, axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def routing_gaps(s: np.ndarray, k: int):
+    """(gap, order_gap) per token.  gap = k-th largest score minus the
+    (k+1)-th (+inf when k = E): below a small threshold the selected set is
+    not robustly defined.  order_gap = the smallest difference between
+    adjacent selected scores (+inf when k = 1): below a threshold the order
+    inside the set is not robust."""
+    T, E = s.shape
+    srt = -np.sort(-s, axis=1)
+    gap = srt[:, k - 1] - srt[:, k] if k < E else np.full(T, np.inf)
+    if k > 1:
+        order_gap = (srt[:, :k - 1] - srt[:, 1:k]).min(axis=1)
+    else:
+        order_gap = np.full(T, np.inf)
+    return gap, order_gap
+
+
+# ----------------------------------------------------------------------------
+# expert
+# ----------------------------------------------------------------------------
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigma(z), sigma the logistic function
+    ("各エキスパートの構造")."""
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_expert(xrows, W_gate_e, W_up_e, W_down_e) -> np.ndarray:
+    """One expert on a block of rows: W2 (SiLU(W1 x) * W3 x), with
+    W_gate = W1 [d_ff][d], W_up = W3 [d_ff][d], W_down = W2 [d][d_ff]
+    ("各エキスパートの構造"; the page's SwiGLUExpert code fixes the order)."""
+    xr = to_f64(xrows)
+    u = xr @ to_f64(W_gate_e).T        # W1 x       [n][d_ff]
+    v = xr @ to_f64(W_up_e).T          # W3 x       [n][d_ff]
+    a = silu(u) * v                    # SiLU(W1 x) * W3 x
+    return a @ to_f64(W_down_e).T      # W2 (...)   [n][d]
+
+
+# ----------------------------------------------------------------------------
+# layer
+# ----------------------------------------------------------------------------
+
+def moe_forward(x, W_router, W_gate, W_up, W_down, k, bias=None, tokens=None,
+                forced_idx=None, keep_expert_outputs=False) -> dict:
+    """The MoE layer, MoE(x) = sum_j g_ij E_ij(x) over the k selected experts
+    ("Top-2ゲーティングの定式化", last equation; "Mixtral of Experts" layer
+    formula), token by token.
+
+    tokens:      optional 1-D array of token ids: the routing is computed for
+                 every token, the expert outputs only for these (rows of
+                 ``out`` follow this order).
+    forced_idx:  optional [T][k] expert ids to use instead of the router's
+                 choice (gates are then the softmax over those scores); used
+                 to value-check tokens whose selection is a near tie.
+    Returns a dict: out [n][d] fp64, idx [T][k], gates [T][k], logits [T][E],
+    counts [E], gap [T], order_gap [T], tokens [n], and with
+    keep_expert_outputs the per-(token, slot) expert outputs y [n][k][d]."""
+    xf = to_f64(x)
+    T = xf.shape[0]
+    E = np.asarray(W_router).shape[1]
+    s = router_logits(xf, W_router, bias)
+    idx = select_topk(s, k) if forced_idx is None else np.asarray(forced_idx, dtype=np.int64)
+    if idx.shape != (T, k):
+        raise ValueError("forced_idx must be [T][k]")
+    g = topk_gates(s, idx)
+    gap, order_gap = routing_gaps(s, k)
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    n = tok.shape[0]
+    d = xf.shape[1]
+    y = np.zeros((n, k, d))
+    sub_idx = idx[tok]                                  # [n][k]
+    for e in range(E):
+        rows, slots = np.nonzero(sub_idx == e)
+        if rows.size == 0:
+            continue
+        y[rows, slots] = swiglu_expert(xf[tok[rows]], W_gate[e], W_up[e], W_down[e])
+    out = np.zeros((n, d))
+    for j in range(k):                                  # sum in slot order
+        out += g[tok, j][:, None] * y[:, j]
+    res = dict(out=out, idx=idx, gates=g, logits=s, counts=counts, gap=gap,
+               order_gap=order_gap, tokens=tok)
+    if keep_expert_outputs:
+        res["y"] = y
+    return res
+
+
+# ----------------------------------------------------------------------------
+# router statistics and load-balancing loss (forward value only)
+# ----------------------------------------------------------------------------
+
+def balance_stats(logits: np.ndarray, idx: np.ndarray, alpha: float = 0.01) -> dict:
+    """Router statistics of "ロードバランス損失":
+      f_i = (1/T) sum_t 1[i in TopK(s_t)]   (fraction of tokens routed to i)
+      p_i = (1/T) sum_t softmax(s_t)_i      (full softmax over all N experts)
+      L   = alpha * N * sum_i f_i p_i
+    f sums to k (the page's own uniform example has f_i = 2/N for top-2), so
+    under uniform routing L = k * alpha.  The page's remark that uniform use
+    gives L = alpha conflicts with that example; the definitions are taken
+    as written."""
+    s = np.asarray(logits, dtype=np.float64)
+    T, E = s.shape
+    f = np.bincount(np.asarray(idx).reshape(-1), minlength=E) / T
+    z = np.exp(s - s.max(axis=1, keepdims=True))
+    p = (z / z.sum(axis=1, keepdims=True)).mean(axis=0)
+    return dict(f=f, p=p, loss=alpha * E * float((f * p).sum()))
+
+
+def expert_param_count(d_model: int, d_ff: int) -> int:
+    """Parameters of one SwiGLU expert: W1, W3 (d_ff x d_model) and W2
+    (d_model x d_ff), "各エキスパートの構造"."""
+    return 3 * d_model * d_ff

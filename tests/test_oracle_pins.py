@@ -1,0 +1,336 @@
+"""Pins of the fp64 oracle to facts other than its own code: closed forms,
+special cases that reduce to plain definitions, brute force on tiny inputs,
+an independent formulation of the layer, and the parameter counts printed on
+the pages.  CPU only.
+
+Pages: "Mistral/Mixtralのアーキテクチャ" (disassemble-channel.com) and
+"Mixtral of Experts" (singularity-lens.com)."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_layer(rng, T=12, d=6, f=5, E=4, bf16=False):
+    x = rng.standard_normal((T, d))
+    Wr = rng.standard_normal((d, E)) / math.sqrt(d)
+    Wg = rng.standard_normal((E, f, d)) / math.sqrt(d)
+    Wu = rng.standard_normal((E, f, d)) / math.sqrt(d)
+    Wd = rng.standard_normal((E, d, f)) / math.sqrt(f)
+    return x, Wr, Wg, Wu, Wd
+
+
+# ---------------------------------------------------------------- brute force
+def bf_silu(z):
+    return z * (1.0 / (1.0 + math.exp(-z)))
+
+
+def bf_expert(xrow, Wg, Wu, Wd):
+    """Scalar loops over the expert definition (W2 applied last)."""
+    d = len(xrow)
+    f = len(Wg)
+    a = []
+    for i in range(f):
+        u = sum(Wg[i][j] * xrow[j] for j in range(d))
+        v = sum(Wu[i][j] * xrow[j] for j in range(d))
+        a.append(bf_silu(u) * v)
+    return [sum(Wd[o][i] * a[i] for i in range(f)) for o in range(d)]
+
+
+# ---------------------------------------------------------------- input decode
+def test_bf16_patterns_decode_exactly():
+    bits = np.array([0x3F80, 0xC000, 0x3F81, 0x0000, 0x8000, 0x7F7F], dtype=np.uint16)
+    want = [1.0, -2.0, 1.0 + 2.0 ** -7, 0.0, -0.0, (2 - 2.0 ** -7) * 2.0 ** 127]
+    assert oracle.to_f64(bits).tolist() == want
+
+
+# ---------------------------------------------------------------- router
+def test_logits_orientation_one_hot_rows():
+    # x = e_j picks row j of W_router[d][E]: H(x)_i = (x . W_g)_i
+    rng = np.random.default_rng(1)
+    d, E = 7, 5
+    Wr = rng.standard_normal((d, E))
+    s = oracle.router_logits(np.eye(d), Wr)
+    assert s.shape == (d, E)
+    np.testing.assert_array_equal(s, Wr)
+
+
+def test_logits_bias_only_and_linearity():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((4, 6))
+    b = np.array([0.5, -1.0, 2.0], dtype=np.float32)
+    np.testing.assert_array_equal(oracle.router_logits(x, np.zeros((6, 3)), b),
+                                  np.broadcast_to(b.astype(np.float64), (4, 3)))
+    Wr = rng.standard_normal((6, 3))
+    s1 = oracle.router_logits(x, Wr)
+    s2 = oracle.router_logits(2.0 * x, Wr)
+    np.testing.assert_allclose(s2, 2.0 * s1, rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("E", [2, 3, 5, 8, 12])
+def test_topk_matches_brute_force_enumeration(E):
+    rng = np.random.default_rng(10 + E)
+    s = rng.standard_normal((40, E))
+    for k in range(1, E + 1):
+        idx = oracle.select_topk(s, k)
+        for t in range(s.shape[0]):
+            best = max(itertools.combinations(range(E), k),
+                       key=lambda c: sum(s[t][i] for i in c))
+            assert set(idx[t].tolist()) == set(best)
+            vals = [s[t][i] for i in idx[t]]
+            assert all(vals[i] >= vals[i + 1] for i in range(k - 1))
+            assert min(vals) >= max([s[t][e] for e in range(E) if e not in best],
+                                    default=-np.inf)
+
+
+def test_topk_fine_grained_against_python_sort():
+    rng = np.random.default_rng(3)
+    s = rng.standard_normal((64, 64))
+    idx = oracle.select_topk(s, 8)
+    for t in range(64):
+        want = sorted(range(64), key=lambda e: (-s[t][e], e))[:8]
+        assert idx[t].tolist() == want
+
+
+def test_topk_ties_go_to_lower_index():
+    s = np.zeros((3, 8))
+    assert oracle.select_topk(s, 3).tolist() == [[0, 1, 2]] * 3
+    s = np.array([[1.0, 3.0, 3.0, 0.0, 3.0]])
+    assert oracle.select_topk(s, 2).tolist() == [[1, 2]]
+    assert oracle.select_topk(s, 4).tolist() == [[1, 2, 4, 0]]
+
+
+def test_gates_closed_forms():
+    rng = np.random.default_rng(4)
+    s = rng.standard_normal((50, 8)) * 3
+    for k in (1, 2, 3, 8):
+        idx = oracle.select_topk(s, k)
+        g = oracle.topk_gates(s, idx)
+        np.testing.assert_allclose(g.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+        sel = np.take_along_axis(s, idx, 1)
+        for a in range(k):
+            for b in range(k):
+                np.testing.assert_allclose(g[:, a] / g[:, b], np.exp(sel[:, a] - sel[:, b]),
+                                           rtol=1e-12)
+        if k == 1:
+            np.testing.assert_array_equal(g, 1.0)
+    # top-2: the first (larger-score) gate is >= 1/2 >= the second
+    g2 = oracle.topk_gates(s, oracle.select_topk(s, 2))
+    assert (g2[:, 0] >= 0.5).all() and (g2[:, 1] <= 0.5).all()
+    # two-expert closed form: g1 = sigma(s_i1 - s_i2)
+    idx = oracle.select_topk(s, 2)
+    sel = np.take_along_axis(s, idx, 1)
+    np.testing.assert_allclose(g2[:, 0], 1 / (1 + np.exp(-(sel[:, 0] - sel[:, 1]))), rtol=1e-14)
+
+
+def test_gap_definitions():
+    s = np.array([[3.0, 1.0, 2.0, 2.5], [0.0, 0.0, 0.0, 0.0]])
+    gap, og = oracle.routing_gaps(s, 2)
+    assert gap.tolist() == [0.5, 0.0]
+    assert og.tolist() == [0.5, 0.0]
+    gap, og = oracle.routing_gaps(s, 4)
+    assert np.isinf(gap).all()
+
+
+# ---------------------------------------------------------------- expert
+def test_silu_closed_forms():
+    z = np.array([0.0, 1.0, -1.0, 5.0, -5.0, 40.0, -40.0])
+    y = oracle.silu(z)
+    assert y[0] == 0.0
+    # z*sigma(z) - (-z)*sigma(-z) = z  (sigma(z) + sigma(-z) = 1)
+    np.testing.assert_allclose(y - oracle.silu(-z), z, rtol=1e-15, atol=1e-15)
+    assert y[1] == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    assert y[5] == pytest.approx(40.0, rel=1e-15)
+    assert abs(y[6]) < 1e-15
+
+
+def test_expert_scalar_worked_example():
+    # d_model = d_ff = 1: x = 2, W1 = 1, W3 = 3, W2 = 5 gives
+    # 5 * (SiLU(1*2) * (3*2)) = 30 * 2 / (1 + e^-2): SiLU on the W1 branch,
+    # W3 the multiplier, W2 applied last.
+    y = oracle.swiglu_expert(np.array([[2.0]]), np.array([[1.0]]), np.array([[3.0]]),
+                             np.array([[5.0]]))
+    assert y[0, 0] == pytest.approx(30.0 * 2.0 / (1.0 + math.exp(-2.0)), rel=1e-15)
+    # swapping the roles of W1 and W3 changes the value
+    y2 = oracle.swiglu_expert(np.array([[2.0]]), np.array([[3.0]]), np.array([[1.0]]),
+                              np.array([[5.0]]))
+    assert abs(y2[0, 0] - y[0, 0]) > 1.0
+
+
+def test_expert_brute_force():
+    rng = np.random.default_rng(5)
+    x, _, Wg, Wu, Wd = rand_layer(rng, T=3, d=5, f=7, E=1)
+    y = oracle.swiglu_expert(x, Wg[0], Wu[0], Wd[0])
+    for t in range(3):
+        np.testing.assert_allclose(y[t], bf_expert(x[t].tolist(), Wg[0].tolist(),
+                                                   Wu[0].tolist(), Wd[0].tolist()),
+                                   rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- layer
+def test_single_expert_layer_is_dense_swiglu():
+    # E = 1, k = 1: every gate is 1 and the layer is one dense SwiGLU FFN
+    rng = np.random.default_rng(6)
+    x, Wr, Wg, Wu, Wd = rand_layer(rng, T=5, d=4, f=6, E=1)
+    r = oracle.moe_forward(x, Wr, Wg, Wu, Wd, 1)
+    np.testing.assert_array_equal(r["gates"], 1.0)
+    for t in range(5):
+        np.testing.assert_allclose(r["out"][t], bf_expert(x[t].tolist(), Wg[0].tolist(),
+                                                          Wu[0].tolist(), Wd[0].tolist()),
+                                   rtol=1e-12, atol=1e-14)
+
+
+def test_uniform_router_all_experts_is_mean():
+    # k = E with a zero router: all scores tie, every gate is 1/E, and the
+    # layer is the mean of all experts
+    rng = np.random.default_rng(7)
+    E = 4
+    x, _, Wg, Wu, Wd = rand_layer(rng, T=3, d=4, f=5, E=E)
+    r = oracle.moe_forward(x, np.zeros((4, E)), Wg, Wu, Wd, E)
+    np.testing.assert_allclose(r["gates"], 1.0 / E, rtol=1e-15)
+    for t in range(3):
+        mean = np.mean([bf_expert(x[t].tolist(), Wg[e].tolist(), Wu[e].tolist(),
+                                  Wd[e].tolist()) for e in range(E)], axis=0)
+        np.testing.assert_allclose(r["out"][t], mean, rtol=1e-12, atol=1e-14)
+
+
+def test_uniform_router_partial_k_uses_lowest_experts():
+    rng = np.random.default_rng(8)
+    E, k = 5, 2
+    x, _, Wg, Wu, Wd = rand_layer(rng, T=3, d=4, f=3, E=E)
+    r = oracle.moe_forward(x, np.zeros((4, E)), Wg, Wu, Wd, k)
+    assert r["idx"].tolist() == [[0, 1]] * 3
+    for t in range(3):
+        want = 0.5 * (np.array(bf_expert(x[t].tolist(), Wg[0].tolist(), Wu[0].tolist(),
+                                         Wd[0].tolist()))
+                      + np.array(bf_expert(x[t].tolist(), Wg[1].tolist(), Wu[1].tolist(),
+                                           Wd[1].tolist())))
+        np.testing.assert_allclose(r["out"][t], want, rtol=1e-12, atol=1e-14)
+
+
+def dense_keep_topk_layer(x, Wr, Wg, Wu, Wd, k):
+    """The "Mixtral of Experts" formulation, independent of the sparse one:
+    g = Softmax(KeepTopK(H(x), k)) over all E (non-kept entries -> -inf,
+    hence weight 0), y = sum over ALL experts of g_i E_i(x)."""
+    T, E = x.shape[0], Wr.shape[1]
+    out = []
+    for t in range(T):
+        h = [sum(x[t][j] * Wr[j][e] for j in range(x.shape[1])) for e in range(E)]
+        kth = sorted(h, reverse=True)[k - 1]
+        kept = [v if v >= kth else -math.inf for v in h]
+        m = max(kept)
+        ex = [math.exp(v - m) if v != -math.inf else 0.0 for v in kept]
+        z = sum(ex)
+        y = np.zeros(x.shape[1])
+        for e in range(E):
+            y += (ex[e] / z) * np.array(bf_expert(x[t].tolist(), Wg[e].tolist(),
+                                                  Wu[e].tolist(), Wd[e].tolist()))
+        out.append(y)
+    return np.array(out)
+
+
+@pytest.mark.parametrize("E,k", [(4, 2), (6, 1), (6, 3), (5, 5)])
+def test_layer_equals_dense_keep_topk_formulation(E, k):
+    rng = np.random.default_rng(20 + E * 10 + k)
+    x, Wr, Wg, Wu, Wd = rand_layer(rng, T=6, d=5, f=4, E=E)
+    r = oracle.moe_forward(x, Wr, Wg, Wu, Wd, k)
+    np.testing.assert_allclose(r["out"], dense_keep_topk_layer(x, Wr, Wg, Wu, Wd, k),
+                               rtol=1e-11, atol=1e-13)
+
+
+def test_expert_relabelling_and_token_permutation():
+    rng = np.random.default_rng(9)
+    E, k = 6, 2
+    x, Wr, Wg, Wu, Wd = rand_layer(rng, T=10, d=5, f=4, E=E)
+    r = oracle.moe_forward(x, Wr, Wg, Wu, Wd, k)
+    perm = rng.permutation(E)              # new expert e is old expert perm[e]
+    inv = np.argsort(perm)
+    r2 = oracle.moe_forward(x, Wr[:, perm], Wg[perm], Wu[perm], Wd[perm], k)
+    np.testing.assert_allclose(r2["out"], r["out"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(inv[r["idx"]], r2["idx"])
+    tp = rng.permutation(10)
+    r3 = oracle.moe_forward(x[tp], Wr, Wg, Wu, Wd, k)
+    np.testing.assert_allclose(r3["out"], r["out"][tp], rtol=1e-12, atol=1e-14)
+
+
+def test_linear_in_down_and_up_projections():
+    rng = np.random.default_rng(11)
+    x, Wr, Wg, Wu, Wd = rand_layer(rng, T=8, d=5, f=4, E=4)
+    r = oracle.moe_forward(x, Wr, Wg, Wu, Wd, 2)
+    np.testing.assert_allclose(oracle.moe_forward(x, Wr, Wg, Wu, 3 * Wd, 2)["out"],
+                               3 * r["out"], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oracle.moe_forward(x, Wr, Wg, -2 * Wu, Wd, 2)["out"],
+                               -2 * r["out"], rtol=1e-13, atol=1e-15)
+
+
+def test_token_subset_and_forced_routing():
+    rng = np.random.default_rng(12)
+    x, Wr, Wg, Wu, Wd = rand_layer(rng, T=9, d=5, f=4, E=5)
+    r = oracle.moe_forward(x, Wr, Wg, Wu, Wd, 2)
+    sub = oracle.moe_forward(x, Wr, Wg, Wu, Wd, 2, tokens=[7, 2, 4])
+    # BLAS may block a different row set differently: equal up to rounding
+    np.testing.assert_allclose(sub["out"], r["out"][[7, 2, 4]], rtol=1e-13, atol=1e-15)
+    f = oracle.moe_forward(x, Wr, Wg, Wu, Wd, 2, forced_idx=r["idx"])
+    np.testing.assert_array_equal(f["out"], r["out"])
+    # forcing the second-best pair [i2, i1] swaps the slot order only
+    f2 = oracle.moe_forward(x, Wr, Wg, Wu, Wd, 2, forced_idx=r["idx"][:, ::-1])
+    np.testing.assert_allclose(f2["out"], r["out"], rtol=1e-13, atol=1e-15)
+
+
+def test_bf16_and_f32_inputs_decode_identically():
+    from sparse_mixture_experts_scan_amd.inputs import f32_to_bf16_bits, bf16_bits_to_f32
+    rng = np.random.default_rng(13)
+    x, Wr, Wg, Wu, Wd = rand_layer(rng, T=6, d=8, f=4, E=3)
+    xb = f32_to_bf16_bits(x.astype(np.float32))
+    Wgb, Wub, Wdb = (f32_to_bf16_bits(w.astype(np.float32)) for w in (Wg, Wu, Wd))
+    Wr32 = Wr.astype(np.float32)
+    a = oracle.moe_forward(xb, Wr32, Wgb, Wub, Wdb, 2)
+    b = oracle.moe_forward(bf16_bits_to_f32(xb), Wr32, bf16_bits_to_f32(Wgb),
+                           bf16_bits_to_f32(Wub), bf16_bits_to_f32(Wdb), 2)
+    np.testing.assert_array_equal(a["out"], b["out"])
+
+
+# ---------------------------------------------------------------- balance loss
+def test_balance_uniform_router_closed_form():
+    # zero router: p_i = 1/N exactly; the first k experts get every token,
+    # so f = (1,..,1,0,..) and L = alpha * N * k / N = k * alpha
+    E, k, T = 8, 2, 16
+    s = np.zeros((T, E))
+    idx = oracle.select_topk(s, k)
+    st = oracle.balance_stats(s, idx, alpha=0.01)
+    np.testing.assert_allclose(st["p"], 1.0 / E, rtol=1e-15)
+    assert st["f"].tolist() == [1.0, 1.0] + [0.0] * 6
+    assert st["loss"] == pytest.approx(k * 0.01, rel=1e-14)
+
+
+def test_balance_f_sums_to_k_and_perfect_balance():
+    rng = np.random.default_rng(14)
+    s = rng.standard_normal((100, 8))
+    st = oracle.balance_stats(s, oracle.select_topk(s, 2))
+    assert st["f"].sum() == pytest.approx(2.0, rel=1e-14)
+    assert st["p"].sum() == pytest.approx(1.0, rel=1e-14)
+    # perfectly balanced assignments (f_i = k/N) with uniform p: L = k * alpha
+    idx = np.array([[2 * (t % 4), 2 * (t % 4) + 1] for t in range(8)])
+    st = oracle.balance_stats(np.zeros((8, 8)), idx, alpha=0.01)
+    np.testing.assert_allclose(st["f"], 2.0 / 8)
+    assert st["loss"] == pytest.approx(0.02, rel=1e-14)
+
+
+# ---------------------------------------------------------------- printed counts
+def test_mixtral_parameter_counts_from_the_page():
+    with open(os.path.join(GOLDEN, "mixtral_param_counts.json")) as fh:
+        g = json.load(fh)
+    per_layer = oracle.expert_param_count(g["d_model"], g["d_ff"])
+    p_ffn = g["layers"] * per_layer
+    assert abs(p_ffn - g["P_FFN"]) / g["P_FFN"] < 0.005
+    p_attn = g["P_total"] - g["N"] * p_ffn
+    assert abs(p_attn + g["k"] * p_ffn - g["P_active"]) / g["P_active"] < 0.01
+    # one layer's 8 bf16 experts: about 2.8 GB
+    assert 8 * per_layer * 2 == pytest.approx(2.818e9, rel=1e-3)
