@@ -1,0 +1,197 @@
+"""Benchmark of the sparse MoE feed-forward layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+A step is one full forward of the layer (router, permutation, gate/up GEMM,
+down GEMM, combine) over one batch of seeded synthetic tokens, with inputs and
+weights already resident in HBM.  The default workload is the Mixtral-shaped
+decode layer (T = 16, d_model 4096, d_ff 14336, 8 experts, top-2, bf16).
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (timed
+live with HIP events recorded on the launch stream) and the fp64 CPU oracle
+timed on a bounded sample of the same workload."""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+from sparse_mixture_experts_scan_amd.inputs import CONFIGS, make_inputs
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3         # MI355X dense fp32 MFMA / vector
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode", choices=sorted(CONFIGS))
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-tokens", type=int, default=0,
+                   help="tokens of the oracle sample (0 = per-workload default)")
+    return p.parse_args()
+
+
+def algorithmic_work(cfg, counts):
+    """Per-step bytes the method must move and flops it must do (no padding,
+    no intermediates, only the experts that received tokens), and the same
+    per kernel for the two GEMMs."""
+    w = 2 if cfg.dtype == "bf16" else 4
+    T, d, f, E, k = cfg.T, cfg.d_model, cfg.d_ff, cfg.E, cfg.k
+    A = T * k
+    touched = int((counts > 0).sum())
+    layer_bytes = touched * 3 * d * f * w + 2 * T * d * w + d * E * 4
+    layer_flops = 2 * A * 3 * d * f + 2 * T * d * E
+    gateup_bytes = touched * 2 * d * f * w + A * d * w + A * f * w
+    gateup_flops = 2 * A * 2 * d * f
+    down_bytes = touched * d * f * w + A * f * w + A * d * 4
+    down_flops = 2 * A * d * f
+    return dict(touched=touched, layer_bytes=layer_bytes, layer_flops=layer_flops,
+                gateup=(gateup_bytes, gateup_flops), down=(down_bytes, down_flops))
+
+
+def cpu_baseline(cfg, inp, n_tokens):
+    """The fp64 oracle as it stands, timed on a bounded token sample."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    rng = np.random.default_rng(123)
+    toks = np.sort(rng.choice(cfg.T, size=min(n_tokens, cfg.T), replace=False))
+    t0 = time.perf_counter()
+    oracle.moe_forward(inp["x"], inp["W_router"], inp["W_gate"], inp["W_up"], inp["W_down"],
+                       cfg.k, bias=inp["bias"], tokens=toks)
+    dt = time.perf_counter() - t0
+    return {"value": len(toks) / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(toks)} of {cfg.T} tokens of the {cfg.name} workload "
+                      f"(routing for all {cfg.T}), fp64 numpy, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer's multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_mixture_experts_scan_amd as moe
+    from sparse_mixture_experts_scan_amd.binding import MOE_NUM_STAGES, STAGE_NAMES
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = make_inputs(cfg, seed=args.seed)
+
+    def up(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    d = {k: up(v) for k, v in inp.items()}
+    T, E, k = cfg.T, cfg.E, cfg.k
+    dt = moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32
+    ws = torch.empty(moe.moe_ffn_workspace_size(T, cfg.d_model, cfg.d_ff, E, k, dt),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(d["x"])
+    counts = torch.zeros(E, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        moe.forward(d["x"], d["W_router"], d["W_gate"], d["W_up"], d["W_down"], k,
+                    bias=d["bias"], out=out, workspace=ws, expert_counts=counts, stream=stream,
+                    stage_events=events)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # per-kernel split: HIP events recorded by the library between its launches
+    evs = []
+    for _ in range(args.steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(MOE_NUM_STAGES + 1)]
+        for ev in row:
+            ev.record(stream)          # creates the underlying event
+        evs.append(row)
+    torch.cuda.synchronize()
+    for row in evs:
+        step(row)
+    torch.cuda.synchronize()
+    split = {name: float(np.mean([row[i].elapsed_time(row[i + 1]) for row in evs]))
+             for i, name in enumerate(STAGE_NAMES)}
+
+    cnt = counts.cpu().numpy()
+    work = algorithmic_work(cfg, cnt)
+    gateup_bytes, gateup_flops = work["gateup"]
+    gu_s = split["gateup"] * 1e-3
+    if cfg.dtype == "f32":
+        roof = {"bound": "mfma", "achieved": gateup_flops / gu_s / 1e12, "peak": FP32_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    elif cfg.T * k / E <= 64:
+        roof = {"bound": "hbm", "achieved": gateup_bytes / gu_s / 1e9, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": gateup_flops / gu_s / 1e12, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "gateup"
+    roof["kernel_ms"] = split["gateup"]
+
+    secs = ms_step * 1e-3
+    record = {
+        "metric": "MoE-layer tokens/s + % of HBM BW (T=16) / % bf16 MFMA peak (T=4096)",
+        "value": T / secs,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) random-init weights)",
+        "config": {"workload": cfg.name, "T": T, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
+                   "E": E, "k": k, "router_bias": cfg.router_bias, "seed": args.seed,
+                   "parallelism": "single GPU"},
+        "layer": {"GB/s": work["layer_bytes"] / secs / 1e9,
+                  "hbm_frac": work["layer_bytes"] / secs / 1e9 / HBM_PEAK_GBS,
+                  "TFLOP/s": work["layer_flops"] / secs / 1e12,
+                  "mfma_frac": work["layer_flops"] / secs / 1e12 / (
+                      BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS),
+                  "experts_touched": work["touched"], "kernel_ms": split},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample_tokens or {"tiny": 64, "decode": 16}.get(cfg.name, 64)
+        print(f"[bench] cpu baseline on {n} tokens", file=sys.stderr, flush=True)
+        record["cpu_baseline"] = cpu_baseline(cfg, inp, n)
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * moe_ffn.h -- C ABI of the sparse Mixture-of-Experts feed-forward layer
+ * (forward pass) for AMD Instinct MI355X (gfx950).
+ *
+ * The layer ("Mistral/Mixtralのアーキテクチャ", disassemble-channel.com,
+ * section "Top-2ゲーティングの定式化" and section "各エキスパートの構造";
+ * "Mixtral of Experts", singularity-lens.com, the layer-output formula):
+ *
+ *   s_t      = x_t . W_router  (+ bias)                 router scores, [E]
+ *   i_t1..k  = the k largest scores, descending; equal scores -> lower index
+ *   g_tj     = exp(s_t,ij) / sum_l exp(s_t,il)           softmax over the k only
+ *   E_e(x)   = W_down[e] (SiLU(W_gate[e] x) * W_up[e] x), SiLU(z) = z sigma(z)
+ *   out_t    = sum_j g_tj E_ij(x_t)                      summed in slot order
+ *
+ * W_gate, W_up, W_down are the page's W1, W3, W2.  Every token is routed to
+ * exactly k experts; nothing is dropped.  The router bias is an extension
+ * (the pages' router has none) used to build skewed routing.
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers, row-major and contiguous, owned by
+ *    the caller; x, W_router, W_gate, W_up, W_down and out 16-byte aligned,
+ *    the bias and the optional outputs 4-byte aligned.  The library never frees them and keeps no reference after
+ *    the work it enqueued has run.
+ *  - Calls are asynchronous on the given stream (NULL = the default stream);
+ *    device faults surface at the caller's next synchronisation.  Nothing on
+ *    the forward path synchronises with the host or calls hipMemset, so the
+ *    forward call can be captured into a HIP graph when a caller-owned
+ *    workspace is passed.
+ *  - Arguments are validated on the host before any HIP call; a failed
+ *    validation enqueues nothing.  Non-finite inputs give undefined results.
+ *  - Return value: a moe_status_t.  On MOE_ERR_HIP, moe_last_error() holds
+ *    the HIP error text (thread-local, valid until the next call on that
+ *    thread); other failures also leave a short reason there.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null pointer, size out of range, k > E, ...  */
+  MOE_ERR_UNSUPPORTED = 2, /* legal layer, but outside the library's limits */
+  MOE_ERR_WORKSPACE = 3,   /* caller workspace too small or misaligned      */
+  MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed    */
+} moe_status_t;
+
+/* Element type of x, W_gate, W_up, W_down and out.  W_router, the bias and
+ * all accumulation are always float32. */
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype_t;
+
+/* Limits (checked; MOE_ERR_UNSUPPORTED beyond them). */
+#define MOE_MAX_EXPERTS 64
+#define MOE_MAX_TOPK 8
+#define MOE_DIM_ALIGN 64 /* d_model and d_ff must be multiples of this */
+
+typedef struct moe_opts {
+  int32_t dtype;              /* moe_dtype_t; default MOE_BF16                   */
+  void* stream;               /* hipStream_t; NULL = default stream              */
+  const float* router_bias;   /* [E] fp32 device pointer or NULL                 */
+  void* workspace;            /* device buffer, 256-byte aligned, or NULL: then a
+                                 library-owned buffer (per device, grown on demand,
+                                 freed by moe_release) is used                   */
+  size_t workspace_bytes;     /* size of `workspace`                             */
+  int32_t* topk_idx_out;      /* [T][k] device or NULL: selected expert ids       */
+  float* topk_w_out;          /* [T][k] device or NULL: their gate weights        */
+  int32_t* expert_counts_out; /* [E] device or NULL: tokens routed to each expert */
+  void* const* stage_events;  /* NULL, or MOE_NUM_STAGES + 1 hipEvent_t recorded on
+                                 the stream before the first kernel and after each
+                                 stage (router, scan, scatter, gate/up, down,
+                                 combine), for per-kernel timing                 */
+} moe_opts_t;
+
+#define MOE_NUM_STAGES 6
+
+/* Fill `opts` with the defaults (bf16, default stream, no bias, library
+ * workspace, no extra outputs). */
+void moe_opts_init(moe_opts_t* opts);
+
+/*
+ * The whole layer: router -> top-k -> gates -> permutation -> grouped
+ * gate/up GEMM with SiLU(gate)*up -> grouped down GEMM -> gate-weighted
+ * combine.  Matches the module call on "Mistral/Mixtralのアーキテクチャ",
+ * section "MoEレイヤー全体の実装": out has x's shape and dtype, tokens
+ * flattened to T = batch * seq_len.
+ *
+ *   x         [T][d_model]             dtype
+ *   W_router  [d_model][E]             float32
+ *   W_gate    [E][d_ff][d_model]       dtype  (W1, nn.Linear [out][in] layout)
+ *   W_up      [E][d_ff][d_model]       dtype  (W3)
+ *   W_down    [E][d_model][d_ff]       dtype  (W2)
+ *   out       [T][d_model]             dtype  (written, never read)
+ *   1 <= T <= 2^24; 1 <= k <= E <= 64; k <= 8; d_model, d_ff multiples of 64.
+ *   opts      NULL = defaults.
+ */
+int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate,
+                    const void* W_up, const void* W_down, void* out, int64_t T,
+                    int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                    const moe_opts_t* opts);
+
+/* Bytes of workspace moe_ffn_forward needs for this shape (0 if the shape is
+ * invalid or unsupported). */
+size_t moe_ffn_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
+                              int32_t k, int32_t dtype);
+
+/*
+ * Where the forward pass keeps its intermediates inside a caller workspace,
+ * for inspection after the call (byte offsets from the workspace start; all
+ * int32 unless noted).  Row r of the permuted layout belongs to expert e when
+ * offsets[e] <= r < offsets[e+1]; each expert's segment is padded to a
+ * multiple of `block_rows`; rows at or beyond offsets[e] + counts[e] are
+ * padding (row_token = -1, H rows zero).
+ */
+typedef struct moe_ws_layout {
+  int64_t block_rows;       /* padding unit of expert segments (token tile)   */
+  int64_t max_rows;         /* rows reserved for the permuted layout          */
+  int64_t router_blocks;    /* token blocks of the router / scatter kernels   */
+  int32_t gemm_variant;     /* 0 = weight-streaming, 1 = LDS-tiled             */
+  int32_t reserved;
+  size_t topk_idx;          /* [T][k]                                          */
+  size_t topk_w;            /* [T][k] float32                                  */
+  size_t block_counts;      /* [router_blocks][E]: per-block counts, then bases */
+  size_t counts;            /* [E]                                             */
+  size_t offsets;           /* [E+1] padded segment starts; offsets[E] = rows  */
+  size_t num_tiles;         /* [1] token tiles in use                          */
+  size_t tile_expert;       /* [max_rows / block_rows] expert of each tile     */
+  size_t row_token;         /* [max_rows] token of each permuted row or -1     */
+  size_t tok_row;           /* [T][k] permuted row of each (token, slot)       */
+  size_t xs;                /* [max_rows][d_model] dtype: gathered tokens      */
+  size_t h;                 /* [max_rows][d_ff] dtype: SiLU(gate) * up         */
+  size_t y;                 /* [max_rows][d_model] float32: expert outputs     */
+  size_t total;             /* bytes                                           */
+} moe_ws_layout_t;
+
+int moe_ffn_workspace_layout(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
+                             int32_t k, int32_t dtype, moe_ws_layout_t* layout);
+
+/* Static, human-readable text for a status code. */
+const char* moe_status_string(int status);
+
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/* Free the library-owned workspaces (all devices).  The caller must make sure
+ * no enqueued forward call still uses them (synchronise first). */
+void moe_release(void);
+
+/* Library version as "major.minor.patch" (static string). */
+const char* moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

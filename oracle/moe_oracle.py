@@ -123,15 +123,20 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu_expert(xrows, W_gate_e, W_up_e, W_down_e) -> np.ndarray:
-    """One expert on a block of rows: W2 (SiLU(W1 x) * W3 x), with
-    W_gate = W1 [d_ff][d], W_up = W3 [d_ff][d], W_down = W2 [d][d_ff]
-    ("各エキスパートの構造"; the page's SwiGLUExpert code fixes the order)."""
+def expert_hidden(xrows, W_gate_e, W_up_e) -> np.ndarray:
+    """The expert's hidden activation SiLU(W1 x) * W3 x, [n][d_ff], with
+    W_gate = W1 [d_ff][d] and W_up = W3 [d_ff][d] ("各エキスパートの構造")."""
     xr = to_f64(xrows)
     u = xr @ to_f64(W_gate_e).T        # W1 x       [n][d_ff]
     v = xr @ to_f64(W_up_e).T          # W3 x       [n][d_ff]
-    a = silu(u) * v                    # SiLU(W1 x) * W3 x
-    return a @ to_f64(W_down_e).T      # W2 (...)   [n][d]
+    return silu(u) * v
+
+
+def swiglu_expert(xrows, W_gate_e, W_up_e, W_down_e) -> np.ndarray:
+    """One expert on a block of rows: W2 (SiLU(W1 x) * W3 x), W_down = W2
+    [d][d_ff] ("各エキスパートの構造"; the page's SwiGLUExpert code fixes the
+    order: w2 is applied to the product)."""
+    return expert_hidden(xrows, W_gate_e, W_up_e) @ to_f64(W_down_e).T   # [n][d]
 
 
 # ----------------------------------------------------------------------------

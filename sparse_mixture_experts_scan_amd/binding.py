@@ -1,0 +1,195 @@
+"""ctypes binding of libmoe_ffn.so: the C ABI's entry points under the same
+names, plus `forward`, which marshals torch device tensors into one
+`moe_ffn_forward` call.  Argument marshalling only: every step of the layer
+runs in the library's HIP kernels.  There is no fallback: if the library is
+not built, every call raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_ffn.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_BF16, MOE_F32 = 0, 1
+
+EXPORTED = ("moe_opts_init", "moe_ffn_forward", "moe_ffn_workspace_size",
+            "moe_ffn_workspace_layout", "moe_status_string", "moe_last_error",
+            "moe_release", "moe_version")
+
+
+class MoeOpts(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32),
+                ("stream", ctypes.c_void_p),
+                ("router_bias", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t),
+                ("topk_idx_out", ctypes.c_void_p),
+                ("topk_w_out", ctypes.c_void_p),
+                ("expert_counts_out", ctypes.c_void_p),
+                ("stage_events", ctypes.c_void_p)]
+
+MOE_NUM_STAGES = 6
+STAGE_NAMES = ("router", "scan", "scatter", "gateup", "down", "combine")
+
+
+class MoeWsLayout(ctypes.Structure):
+    _fields_ = [("block_rows", ctypes.c_int64),
+                ("max_rows", ctypes.c_int64),
+                ("router_blocks", ctypes.c_int64),
+                ("gemm_variant", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)] + [
+        (name, ctypes.c_size_t) for name in
+        ("topk_idx", "topk_w", "block_counts", "counts", "offsets", "num_tiles",
+         "tile_expert", "row_token", "tok_row", "xs", "h", "y", "total")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {moe_status_string(status)} ({status}): {moe_last_error()}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run "
+                               "`python -m sparse_mixture_experts_scan_amd.build` first")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+        L.moe_opts_init.argtypes = [ctypes.POINTER(MoeOpts)]
+        L.moe_opts_init.restype = None
+        L.moe_ffn_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
+                                      ctypes.POINTER(MoeOpts)]
+        L.moe_ffn_forward.restype = ctypes.c_int
+        L.moe_ffn_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
+        L.moe_ffn_workspace_size.restype = sz
+        L.moe_ffn_workspace_layout.argtypes = [i64, i64, i64, i32, i32, i32,
+                                               ctypes.POINTER(MoeWsLayout)]
+        L.moe_ffn_workspace_layout.restype = ctypes.c_int
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_release.argtypes = []
+        L.moe_release.restype = None
+        L.moe_version.argtypes = []
+        L.moe_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------- raw C ABI
+def moe_opts_init() -> MoeOpts:
+    o = MoeOpts()
+    lib().moe_opts_init(ctypes.byref(o))
+    return o
+
+
+def moe_ffn_forward(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E, k,
+                    opts: Optional[MoeOpts] = None) -> int:
+    """Raw entry point: integer device addresses, returns the status code."""
+    return lib().moe_ffn_forward(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E,
+                                 k, ctypes.byref(opts) if opts is not None else None)
+
+
+def moe_ffn_workspace_size(T, d_model, d_ff, E, k, dtype=MOE_BF16) -> int:
+    return lib().moe_ffn_workspace_size(T, d_model, d_ff, E, k, dtype)
+
+
+def moe_ffn_workspace_layout(T, d_model, d_ff, E, k, dtype=MOE_BF16) -> MoeWsLayout:
+    lay = MoeWsLayout()
+    st = lib().moe_ffn_workspace_layout(T, d_model, d_ff, E, k, dtype, ctypes.byref(lay))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_ffn_workspace_layout")
+    return lay
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def moe_last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def moe_release() -> None:
+    lib().moe_release()
+
+
+def moe_version() -> str:
+    return lib().moe_version().decode()
+
+
+# ---------------------------------------------------------------- torch marshalling
+def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
+            workspace=None, topk_idx=None, topk_w=None, expert_counts=None, stream=None,
+            stage_events=None):
+    """One moe_ffn_forward call on torch device tensors.
+
+    x [T][d] (bf16 or fp32), W_router [d][E] fp32, W_gate/W_up [E][d_ff][d],
+    W_down [E][d][d_ff] (x's dtype), bias [E] fp32 or None.  Optional outputs
+    topk_idx [T][k] int32, topk_w [T][k] fp32, expert_counts [E] int32 are
+    filled when given.  `workspace` is a uint8 device tensor (see
+    moe_ffn_workspace_size) or None for the library's own.  Returns out."""
+    import torch
+
+    T, d = x.shape
+    E = W_router.shape[1]
+    d_ff = W_gate.shape[1]
+    if x.dtype == torch.bfloat16:
+        dtype = MOE_BF16
+    elif x.dtype == torch.float32:
+        dtype = MOE_F32
+    else:
+        raise TypeError("x must be bfloat16 or float32")
+    checks = [(W_router, (d, E), torch.float32), (W_gate, (E, d_ff, d), x.dtype),
+              (W_up, (E, d_ff, d), x.dtype), (W_down, (E, d, d_ff), x.dtype)]
+    if bias is not None:
+        checks.append((bias, (E,), torch.float32))
+    if out is None:
+        out = torch.empty_like(x)
+    checks.append((out, (T, d), x.dtype))
+    for t, shape in ((topk_idx, (T, k)), (expert_counts, (E,))):
+        if t is not None:
+            checks.append((t, shape, torch.int32))
+    if topk_w is not None:
+        checks.append((topk_w, (T, k), torch.float32))
+    for t, shape, dt in [(x, (T, d), x.dtype)] + checks:
+        if tuple(t.shape) != tuple(shape) or t.dtype != dt:
+            raise ValueError(f"tensor {tuple(t.shape)} {t.dtype}: expected {shape} {dt}")
+        if not t.is_cuda or not t.is_contiguous() or t.device != x.device:
+            raise ValueError("every tensor must be a contiguous device tensor on x's device")
+    o = moe_opts_init()
+    o.dtype = dtype
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    o.stream = st.cuda_stream
+    o.router_bias = bias.data_ptr() if bias is not None else None
+    if workspace is not None:
+        if workspace.device != x.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on x's device")
+        o.workspace = workspace.data_ptr()
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
+    o.topk_idx_out = topk_idx.data_ptr() if topk_idx is not None else None
+    o.topk_w_out = topk_w.data_ptr() if topk_w is not None else None
+    o.expert_counts_out = expert_counts.data_ptr() if expert_counts is not None else None
+    if stage_events is not None:
+        # MOE_NUM_STAGES + 1 created torch.cuda.Event objects (record() once first)
+        if len(stage_events) != MOE_NUM_STAGES + 1:
+            raise ValueError("stage_events needs MOE_NUM_STAGES + 1 events")
+        arr = (ctypes.c_void_p * len(stage_events))(*[ev.cuda_event for ev in stage_events])
+        o.stage_events = ctypes.cast(arr, ctypes.c_void_p)
+    with torch.cuda.device(x.device):
+        status = moe_ffn_forward(x.data_ptr(), W_router.data_ptr(), W_gate.data_ptr(),
+                                 W_up.data_ptr(), W_down.data_ptr(), out.data_ptr(), T, d, d_ff,
+                                 E, k, o)
+    if status != MOE_OK:
+        raise MoeError(status, "moe_ffn_forward")
+    return out

@@ -1,0 +1,58 @@
+// Device-side types and helpers shared by the MoE kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_ffn.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t bf16_t;  // storage type of bfloat16 data
+
+constexpr int kWave = 64;
+constexpr int kRouterTokens = 32;   // tokens per router / scatter block
+constexpr int kRouterThreads = 256;
+
+// Element-type traits: how a 16-byte chunk of K is fed to 16x16 MFMA.
+// bf16: one chunk = 8 elements = one v_mfma_f32_16x16x32_bf16 k-group.
+// f32:  one chunk = 4 elements = four v_mfma_f32_16x16x4_f32, element i of the
+//       chunk feeding the i-th instruction.  A and B use the same mapping, so
+//       every k is paired with itself exactly once.
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+  static constexpr int kVec = 8;  // elements per 16-byte chunk
+  __device__ static inline float to_f32(bf16_t v) {
+    return __uint_as_float(static_cast<uint32_t>(v) << 16);
+  }
+  __device__ static inline bf16_t from_f32(float f) {
+    __bf16 b = static_cast<__bf16>(f);  // round to nearest even
+    return __builtin_bit_cast(bf16_t, b);
+  }
+  __device__ static inline f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;
+  __device__ static inline float to_f32(float v) { return v; }
+  __device__ static inline float from_f32(float f) { return f; }
+  __device__ static inline f32x4 mfma16(uint4 a, uint4 b, f32x4 c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    return c;
+  }
+};
+
+__device__ inline float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+__device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ inline void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+}  // namespace moe

@@ -1,0 +1,41 @@
+// Host-side launchers of the MoE kernels (internal to libmoe_ffn.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct Dims {
+  int T, d, f, E, k;   // tokens, d_model, d_ff, experts, top-k
+  int Epow2;           // smallest power of two >= E
+  int nblk;            // router / scatter blocks (kRouterTokens tokens each)
+  int BT;              // token tile = padding unit of expert segments
+  int max_rows;        // rows reserved for the permuted layout
+  int max_tiles;       // max_rows / BT
+  bool bf16;           // element type of x / weights / out
+};
+
+// a1: scores, top-k, softmax over the k, per-block expert histogram
+void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
+                   int32_t* idx, float* w, int32_t* blk_counts, hipStream_t s);
+// a2: histogram reduce, padded offsets, per-block bases, tile table
+void launch_scan(const Dims& D, int32_t* blk_counts, int32_t* counts, int32_t* offsets,
+                 int32_t* num_tiles, int32_t* tile_expert, int32_t* row_token,
+                 int32_t* counts_out, hipStream_t s);
+// a2: stable row maps and gather of x into expert-contiguous rows
+void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int32_t* blk_base,
+                    const int32_t* offsets, int32_t* tok_row, int32_t* row_token, void* xs,
+                    hipStream_t s);
+// a3 + a4: grouped GEMMs, weight-streaming form (few rows per expert)
+void launch_gateup_stream(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* h,
+                          const int32_t* counts, const int32_t* offsets,
+                          const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s);
+void launch_down_stream(const Dims& D, const void* h, const void* Wd, float* y,
+                        const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
+                        const int32_t* tile_expert, hipStream_t s);
+// a5: gate-weighted gather-sum back to token order
+void launch_combine(const Dims& D, const float* y, const int32_t* tok_row, const float* w,
+                    void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,258 @@
+// C ABI of the sparse MoE feed-forward layer: argument validation, the
+// launch plan, the workspace layout and the launch sequence
+//   router -> scan -> scatter/gather -> gate/up GEMM -> down GEMM -> combine,
+// all asynchronous on the caller's stream with no host synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+
+#include "common.h"
+#include "launch.h"
+#include "moe_ffn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const std::string& why) {
+  g_last_error = why;
+  return status;
+}
+
+struct Plan {
+  moe::Dims D;
+  moe_ws_layout_t L;
+};
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Validates a shape and builds the launch plan and workspace layout.
+// Touches no HIP API.
+int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dtype, Plan* p) {
+  if (T < 1 || d < 1 || f < 1 || E < 1 || k < 1)
+    return fail(MOE_ERR_INVALID_ARG, "T, d_model, d_ff, E and k must be >= 1");
+  if (k > E) return fail(MOE_ERR_INVALID_ARG, "k must be <= E");
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E > 64");
+  if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k > 8");
+  if (d % MOE_DIM_ALIGN || f % MOE_DIM_ALIGN)
+    return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
+  if (T > (int64_t(1) << 24)) return fail(MOE_ERR_UNSUPPORTED, "T > 2^24");
+  if (d > 32768 || f > 131072) return fail(MOE_ERR_UNSUPPORTED, "d_model > 32768 or d_ff > 131072");
+
+  moe::Dims& D = p->D;
+  D.T = (int)T;
+  D.d = (int)d;
+  D.f = (int)f;
+  D.E = E;
+  D.k = k;
+  D.bf16 = dtype == MOE_BF16;
+  D.Epow2 = 1;
+  while (D.Epow2 < E) D.Epow2 *= 2;
+  D.nblk = (D.T + moe::kRouterTokens - 1) / moe::kRouterTokens;
+  const int64_t A = T * k;                       // (token, slot) assignments
+  const int64_t rows_avg = (A + E - 1) / E;
+  int variant = 0;
+  D.BT = rows_avg <= 16 ? 16 : 32;
+  int64_t max_rows = A + (int64_t)E * (D.BT - 1);
+  max_rows = (max_rows + D.BT - 1) / D.BT * D.BT;
+  if (max_rows > (int64_t(1) << 30)) return fail(MOE_ERR_UNSUPPORTED, "too many rows");
+  D.max_rows = (int)max_rows;
+  D.max_tiles = (int)(max_rows / D.BT);
+
+  moe_ws_layout_t& L = p->L;
+  std::memset(&L, 0, sizeof(L));
+  L.block_rows = D.BT;
+  L.max_rows = D.max_rows;
+  L.router_blocks = D.nblk;
+  L.gemm_variant = variant;
+  const size_t es = D.bf16 ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.topk_idx = take(sizeof(int32_t) * A);
+  L.topk_w = take(sizeof(float) * A);
+  L.block_counts = take(sizeof(int32_t) * D.nblk * E);
+  L.counts = take(sizeof(int32_t) * E);
+  L.offsets = take(sizeof(int32_t) * (E + 1));
+  L.num_tiles = take(sizeof(int32_t));
+  L.tile_expert = take(sizeof(int32_t) * D.max_tiles);
+  L.row_token = take(sizeof(int32_t) * D.max_rows);
+  L.tok_row = take(sizeof(int32_t) * A);
+  L.xs = take(es * D.max_rows * d);
+  L.h = take(es * D.max_rows * f);
+  L.y = take(sizeof(float) * D.max_rows * d);
+  L.total = off;
+  return MOE_OK;
+}
+
+struct CachedWs {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<int, CachedWs> g_ws;
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+void moe_opts_init(moe_opts_t* o) {
+  if (!o) return;
+  std::memset(o, 0, sizeof(*o));
+  o->dtype = MOE_BF16;
+}
+
+size_t moe_ffn_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                              int32_t dtype) {
+  Plan p;
+  if (make_plan(T, d_model, d_ff, E, k, dtype, &p) != MOE_OK) return 0;
+  return p.L.total;
+}
+
+int moe_ffn_workspace_layout(int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                             int32_t dtype, moe_ws_layout_t* layout) {
+  g_last_error.clear();
+  if (!layout) return fail(MOE_ERR_INVALID_ARG, "layout is NULL");
+  Plan p;
+  const int st = make_plan(T, d_model, d_ff, E, k, dtype, &p);
+  if (st != MOE_OK) return st;
+  *layout = p.L;
+  return MOE_OK;
+}
+
+int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                    const void* W_down, void* out, int64_t T, int64_t d_model, int64_t d_ff,
+                    int32_t E, int32_t k, const moe_opts_t* opts) {
+  g_last_error.clear();
+  moe_opts_t o;
+  if (opts) o = *opts;
+  else moe_opts_init(&o);
+  if (!x || !W_router || !W_gate || !W_up || !W_down || !out)
+    return fail(MOE_ERR_INVALID_ARG, "null tensor pointer");
+  // rows are moved with 16-byte vector loads and stores
+  for (const void* ptr : {x, (const void*)W_router, W_gate, W_up, W_down, (const void*)out})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16)
+      return fail(MOE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  for (const void* ptr : {(const void*)o.router_bias, (const void*)o.topk_idx_out,
+                          (const void*)o.topk_w_out, (const void*)o.expert_counts_out})
+    if (reinterpret_cast<uintptr_t>(ptr) % 4)
+      return fail(MOE_ERR_INVALID_ARG, "optional outputs and bias must be 4-byte aligned");
+  Plan p;
+  int st = make_plan(T, d_model, d_ff, E, k, o.dtype, &p);
+  if (st != MOE_OK) return st;
+  if (o.workspace) {
+    if (reinterpret_cast<uintptr_t>(o.workspace) % 256)
+      return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (o.workspace_bytes < p.L.total)
+      return fail(MOE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(p.L.total) +
+                                         " bytes");
+  }
+
+  // ---- validated; from here on HIP calls
+  hipStream_t s = reinterpret_cast<hipStream_t>(o.stream);
+  char* ws = static_cast<char*>(o.workspace);
+  if (!ws) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    CachedWs& c = g_ws[dev];
+    if (c.bytes < p.L.total) {
+      if (c.ptr) {
+        e = hipDeviceSynchronize();  // the old buffer may still be in use
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        (void)hipFree(c.ptr);
+        c.ptr = nullptr;
+        c.bytes = 0;
+      }
+      e = hipMalloc(&c.ptr, p.L.total);
+      if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+      c.bytes = p.L.total;
+    }
+    ws = static_cast<char*>(c.ptr);
+  }
+  const moe::Dims& D = p.D;
+  const moe_ws_layout_t& L = p.L;
+  int32_t* idx = o.topk_idx_out ? o.topk_idx_out : reinterpret_cast<int32_t*>(ws + L.topk_idx);
+  float* w = o.topk_w_out ? o.topk_w_out : reinterpret_cast<float*>(ws + L.topk_w);
+  int32_t* blk = reinterpret_cast<int32_t*>(ws + L.block_counts);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* num_tiles = reinterpret_cast<int32_t*>(ws + L.num_tiles);
+  int32_t* tile_expert = reinterpret_cast<int32_t*>(ws + L.tile_expert);
+  int32_t* row_token = reinterpret_cast<int32_t*>(ws + L.row_token);
+  int32_t* tok_row = reinterpret_cast<int32_t*>(ws + L.tok_row);
+  void* xs = ws + L.xs;
+  void* h = ws + L.h;
+  float* y = reinterpret_cast<float*>(ws + L.y);
+
+  hipError_t e;
+  auto mark = [&](int i) -> hipError_t {
+    return o.stage_events ? hipEventRecord(static_cast<hipEvent_t>(o.stage_events[i]), s)
+                          : hipSuccess;
+  };
+  if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  moe::launch_router(D, x, W_router, o.router_bias, idx, w, blk, s);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess)
+    return hip_fail(e, "router launch");
+  moe::launch_scan(D, blk, counts, offsets, num_tiles, tile_expert, row_token,
+                   o.expert_counts_out, s);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess)
+    return hip_fail(e, "scan launch");
+  moe::launch_scatter(D, x, idx, blk, offsets, tok_row, row_token, xs, s);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess)
+    return hip_fail(e, "scatter launch");
+  moe::launch_gateup_stream(D, xs, W_gate, W_up, h, counts, offsets, num_tiles, tile_expert, s);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess)
+    return hip_fail(e, "gate/up launch");
+  moe::launch_down_stream(D, h, W_down, y, counts, offsets, num_tiles, tile_expert, s);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(5)) != hipSuccess)
+    return hip_fail(e, "down launch");
+  moe::launch_combine(D, y, tok_row, w, out, s);
+  if ((e = hipGetLastError()) != hipSuccess || (e = mark(6)) != hipSuccess)
+    return hip_fail(e, "combine launch");
+  return MOE_OK;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+void moe_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  int cur = 0;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (auto& kv : g_ws) {
+    if (kv.second.ptr) {
+      if (hipSetDevice(kv.first) == hipSuccess) (void)hipFree(kv.second.ptr);
+    }
+    kv.second = CachedWs();
+  }
+  g_ws.clear();
+  if (have_cur) (void)hipSetDevice(cur);
+}
+
+const char* moe_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,315 @@
+// Router (scores -> top-k -> softmax over the k), permutation (histogram ->
+// prefix scan -> padded offsets -> stable row maps -> gather) and the
+// gate-weighted combine of the sparse MoE layer.
+//
+// "Mistral/Mixtralのアーキテクチャ" (disassemble-channel.com):
+//   section "Top-2ゲーティングの定式化": s = W_g x (no bias), Top-k of s,
+//     gates = softmax over the selected scores only, MoE(x) = sum_j g_j E_j(x);
+//   section "MoEレイヤー全体の実装": the per-expert token mask and gather,
+//     and the weighted scatter-add back into a zeros_like(x) output, which is
+//     done here as a gather-sum (each token reads its k expert rows).
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// a1: router.  One block = kRouterTokens tokens x all E experts.
+// Scores: fp32 FMA over d in ascending order, x and W_router staged in LDS.
+// Top-k: one thread per token, k passes of an arg-max over E (strict '>' in
+// ascending expert order, so equal scores go to the lower index).
+// Softmax over the selected k, shifted by the largest selected score.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
+    const T* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
+    int nT, int d, int E, int k, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+    int32_t* __restrict__ blk_counts) {
+  constexpr int TB = kRouterTokens;
+  constexpr int DC = 64;                       // d-chunk staged per step
+  constexpr int QMAX = TB * 64 / kRouterThreads;  // (token, expert) pairs per thread
+  __shared__ float xs[TB][DC + 1];
+  __shared__ float ws[DC][64];
+  __shared__ float slog[TB][65];
+  __shared__ int hist[64];
+
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * TB;
+  const int npairs = TB * E;
+  float acc[QMAX];
+#pragma unroll
+  for (int q = 0; q < QMAX; ++q) acc[q] = 0.f;
+  if (tid < 64) hist[tid] = 0;
+
+  for (int j0 = 0; j0 < d; j0 += DC) {
+    for (int i = tid; i < TB * DC; i += kRouterThreads) {
+      const int tt = i / DC, jj = i % DC, t = t0 + tt;
+      xs[tt][jj] = t < nT ? Elem<T>::to_f32(x[(size_t)t * d + j0 + jj]) : 0.f;
+    }
+    for (int i = tid; i < DC * E; i += kRouterThreads) {
+      const int jj = i / E, e = i % E;
+      ws[jj][e] = Wr[(size_t)(j0 + jj) * E + e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+      const int p = tid + kRouterThreads * q;
+      if (p < npairs) {
+        const int tt = p / E, e = p % E;
+        float a = acc[q];
+#pragma unroll 16
+        for (int jj = 0; jj < DC; ++jj) a = fmaf(xs[tt][jj], ws[jj][e], a);
+        acc[q] = a;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < QMAX; ++q) {
+    const int p = tid + kRouterThreads * q;
+    if (p < npairs) {
+      const int tt = p / E, e = p % E;
+      slog[tt][e] = acc[q] + (bias ? bias[e] : 0.f);
+    }
+  }
+  __syncthreads();
+
+  if (tid < TB) {
+    const int t = t0 + tid;
+    if (t < nT) {
+      uint64_t taken = 0;
+      float sel[MOE_MAX_TOPK];
+      int sid[MOE_MAX_TOPK];
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+        if (j < k) {
+          float best = 0.f;
+          int bi = -1;
+          for (int e = 0; e < E; ++e) {
+            const float v = slog[tid][e];
+            if (!((taken >> e) & 1ull) && (bi < 0 || v > best)) {
+              best = v;
+              bi = e;
+            }
+          }
+          taken |= 1ull << bi;
+          sel[j] = best;
+          sid[j] = bi;
+        }
+      }
+      float z[MOE_MAX_TOPK];
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_TOPK; ++j)
+        if (j < k) {
+          z[j] = expf(sel[j] - sel[0]);
+          sum += z[j];
+        }
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_TOPK; ++j)
+        if (j < k) {
+          idx_out[(size_t)t * k + j] = sid[j];
+          w_out[(size_t)t * k + j] = z[j] / sum;
+          atomicAdd(&hist[sid[j]], 1);
+        }
+    }
+  }
+  __syncthreads();
+  if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = hist[tid];
+}
+
+// ---------------------------------------------------------------------------
+// a2 (part 1): one block.  counts[e] = sum over router blocks; the per-block
+// counts are rewritten in place as exclusive per-expert bases; segments are
+// padded to BT rows (offsets = exclusive scan of padded counts); each token
+// tile gets its expert (or -1); padding rows of row_token are set to -1.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void expert_scan_kernel(
+    int32_t* __restrict__ blk, int nblk, int E, int Epow2, int BT, int max_rows, int max_tiles,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ num_tiles,
+    int32_t* __restrict__ tile_expert, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ counts_out) {
+  __shared__ int part[256];
+  __shared__ int s_cnt[64];
+  __shared__ int s_off[65];
+  const int tid = threadIdx.x;
+  const int C = 256 / Epow2;       // block chunks scanned in parallel per expert
+  const int e = tid % Epow2, c = tid / Epow2;
+  const int per = (nblk + C - 1) / C;
+  const int b0 = min(nblk, c * per), b1 = min(nblk, b0 + per);
+  int sum = 0;
+  if (e < E)
+    for (int b = b0; b < b1; ++b) sum += blk[(size_t)b * E + e];
+  part[tid] = sum;
+  __syncthreads();
+  if (tid < E) {
+    int run = 0;
+    for (int cc = 0; cc < C; ++cc) {
+      const int v = part[cc * Epow2 + tid];
+      part[cc * Epow2 + tid] = run;
+      run += v;
+    }
+    s_cnt[tid] = run;
+  }
+  __syncthreads();
+  if (e < E) {
+    int run = part[tid];
+    for (int b = b0; b < b1; ++b) {
+      const int v = blk[(size_t)b * E + e];
+      blk[(size_t)b * E + e] = run;
+      run += v;
+    }
+  }
+  if (tid == 0) {
+    int off = 0;
+    for (int x = 0; x < E; ++x) {
+      s_off[x] = off;
+      off += (s_cnt[x] + BT - 1) / BT * BT;
+    }
+    s_off[E] = off;
+  }
+  __syncthreads();
+  if (tid < E) {
+    counts[tid] = s_cnt[tid];
+    if (counts_out) counts_out[tid] = s_cnt[tid];
+  }
+  if (tid <= E) offsets[tid] = s_off[tid];
+  const int P = s_off[E];
+  const int ntiles = P / BT;
+  if (tid == 0) *num_tiles = ntiles;
+  for (int i = tid; i < max_tiles; i += 256) {
+    int ex = -1;
+    if (i < ntiles) {
+      const int r = i * BT;
+      ex = 0;
+      while (s_off[ex + 1] <= r) ++ex;
+    }
+    tile_expert[i] = ex;
+  }
+  for (int x = 0; x < E; ++x)
+    for (int r = s_off[x] + s_cnt[x] + tid; r < s_off[x + 1]; r += 256) row_token[r] = -1;
+  for (int r = P + tid; r < max_rows; r += 256) row_token[r] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// a2 (part 2): per router block, rank of each (token, slot) among the
+// block's earlier pairs routed to the same expert -> permuted row
+// offsets[e] + base[blk][e] + rank, so rows inside an expert segment are in
+// ascending (token, slot) order.  Then copy x[t] to Xs[row], 16 B per lane.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kRouterThreads) void scatter_gather_kernel(
+    const T* __restrict__ x, const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ offsets, int nT, int d, int E, int k,
+    int32_t* __restrict__ tok_row, int32_t* __restrict__ row_token, T* __restrict__ xs) {
+  __shared__ int sE[kRouterThreads];
+  __shared__ int sRow[kRouterThreads];
+  __shared__ int sTok[kRouterThreads];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * kRouterTokens;
+  const int np = kRouterTokens * k;
+  int e = -1, t = -1;
+  if (tid < np) {
+    t = t0 + tid / k;
+    if (t < nT) e = idx[(size_t)t0 * k + tid];
+    else t = -1;
+  }
+  sE[tid] = e;
+  __syncthreads();
+  int row = -1;
+  if (e >= 0) {
+    int rank = 0;
+    for (int q = 0; q < tid; ++q) rank += (sE[q] == e);
+    row = offsets[e] + base[(size_t)blockIdx.x * E + e] + rank;
+    tok_row[(size_t)t0 * k + tid] = row;
+    row_token[row] = t;
+  }
+  sRow[tid] = row;
+  sTok[tid] = t;
+  __syncthreads();
+  const int cpr = d * (int)sizeof(T) / 16;  // 16-byte chunks per row
+  const int per_chunk = 16 / (int)sizeof(T);
+  for (int i = tid; i < np * cpr; i += kRouterThreads) {
+    const int p = i / cpr, c = i - p * cpr;
+    const int r = sRow[p];
+    if (r >= 0)
+      st16(xs + (size_t)r * d + c * per_chunk, ld16(x + (size_t)sTok[p] * d + c * per_chunk));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// a5: out[t] = sum_j w[t][j] * Y[tok_row[t][j]], fp32 FMA in slot order,
+// one rounding to the output type.  A gather, so no atomics.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+                                                      const int32_t* __restrict__ tok_row,
+                                                      const float* __restrict__ w, int d, int k,
+                                                      T* __restrict__ out) {
+  const int t = blockIdx.x;
+  __shared__ int s_row[MOE_MAX_TOPK];
+  __shared__ float s_w[MOE_MAX_TOPK];
+  if (threadIdx.x < k) {
+    s_row[threadIdx.x] = tok_row[(size_t)t * k + threadIdx.x];
+    s_w[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < d / 4; c += 256) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const float4 v = reinterpret_cast<const float4*>(y + (size_t)s_row[j] * d)[c];
+      const float g = s_w[j];
+      a.x = fmaf(g, v.x, a.x);
+      a.y = fmaf(g, v.y, a.y);
+      a.z = fmaf(g, v.z, a.z);
+      a.w = fmaf(g, v.w, a.w);
+    }
+    T* o = out + (size_t)t * d + 4 * c;
+    o[0] = Elem<T>::from_f32(a.x);
+    o[1] = Elem<T>::from_f32(a.y);
+    o[2] = Elem<T>::from_f32(a.z);
+    o[3] = Elem<T>::from_f32(a.w);
+  }
+}
+
+// ---------------------------------------------------------------------------
+void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
+                   int32_t* idx, float* w, int32_t* blk_counts, hipStream_t s) {
+  if (D.bf16)
+    router_topk_kernel<bf16_t><<<D.nblk, kRouterThreads, 0, s>>>(
+        (const bf16_t*)x, Wr, bias, D.T, D.d, D.E, D.k, idx, w, blk_counts);
+  else
+    router_topk_kernel<float><<<D.nblk, kRouterThreads, 0, s>>>(
+        (const float*)x, Wr, bias, D.T, D.d, D.E, D.k, idx, w, blk_counts);
+}
+
+void launch_scan(const Dims& D, int32_t* blk_counts, int32_t* counts, int32_t* offsets,
+                 int32_t* num_tiles, int32_t* tile_expert, int32_t* row_token,
+                 int32_t* counts_out, hipStream_t s) {
+  expert_scan_kernel<<<1, 256, 0, s>>>(blk_counts, D.nblk, D.E, D.Epow2, D.BT, D.max_rows,
+                                       D.max_tiles, counts, offsets, num_tiles, tile_expert,
+                                       row_token, counts_out);
+}
+
+void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int32_t* blk_base,
+                    const int32_t* offsets, int32_t* tok_row, int32_t* row_token, void* xs,
+                    hipStream_t s) {
+  if (D.bf16)
+    scatter_gather_kernel<bf16_t><<<D.nblk, kRouterThreads, 0, s>>>(
+        (const bf16_t*)x, idx, blk_base, offsets, D.T, D.d, D.E, D.k, tok_row, row_token,
+        (bf16_t*)xs);
+  else
+    scatter_gather_kernel<float><<<D.nblk, kRouterThreads, 0, s>>>(
+        (const float*)x, idx, blk_base, offsets, D.T, D.d, D.E, D.k, tok_row, row_token,
+        (float*)xs);
+}
+
+void launch_combine(const Dims& D, const float* y, const int32_t* tok_row, const float* w,
+                    void* out, hipStream_t s) {
+  if (D.bf16)
+    combine_kernel<bf16_t><<<D.T, 256, 0, s>>>(y, tok_row, w, D.d, D.k, (bf16_t*)out);
+  else
+    combine_kernel<float><<<D.T, 256, 0, s>>>(y, tok_row, w, D.d, D.k, (float*)out);
+}
+
+}  // namespace moe

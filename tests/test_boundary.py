@@ -1,0 +1,120 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects bad arguments before any HIP call (so these run with
+no GPU; the dummy addresses below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mixture_experts_scan_amd as moe
+from sparse_mixture_experts_scan_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "moe_ffn.h")
+DUMMY = 0x100000  # 256-byte aligned, never dereferenced
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = moe.lib()
+    declared = header_functions()
+    assert set(declared) == set(B.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert re.match(r"^\d+\.\d+\.\d+$", moe.moe_version())
+    for st in range(5):
+        assert moe.moe_status_string(st)
+    assert moe.moe_status_string(99) == "unknown status"
+
+
+def fwd(T=16, d=256, f=512, E=8, k=2, opts=None, ptrs=None):
+    p = ptrs or [DUMMY] * 6
+    return moe.moe_ffn_forward(*p, T, d, f, E, k, opts)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=9, E=8), B.MOE_ERR_INVALID_ARG),
+    (dict(k=0), B.MOE_ERR_INVALID_ARG),
+    (dict(T=0), B.MOE_ERR_INVALID_ARG),
+    (dict(T=-5), B.MOE_ERR_INVALID_ARG),
+    (dict(E=65, k=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(E=16, k=9), B.MOE_ERR_UNSUPPORTED),
+    (dict(d=100), B.MOE_ERR_UNSUPPORTED),
+    (dict(f=96), B.MOE_ERR_UNSUPPORTED),
+    (dict(T=(1 << 24) + 1), B.MOE_ERR_UNSUPPORTED),
+])
+def test_rejects_bad_shapes(kw, status):
+    assert fwd(**kw) == status
+    assert moe.moe_last_error() != ""
+
+
+def test_rejects_null_pointers_and_bad_dtype():
+    for i in range(6):
+        p = [DUMMY] * 6
+        p[i] = None
+        assert fwd(ptrs=p) == B.MOE_ERR_INVALID_ARG
+    o = moe.moe_opts_init()
+    o.dtype = 7
+    assert fwd(opts=o) == B.MOE_ERR_INVALID_ARG
+
+
+def test_rejects_misaligned_tensors():
+    for i in range(6):
+        p = [DUMMY] * 6
+        p[i] = DUMMY + 8
+        assert fwd(ptrs=p) == B.MOE_ERR_INVALID_ARG
+    o = moe.moe_opts_init()
+    o.topk_idx_out = DUMMY + 2
+    assert fwd(opts=o) == B.MOE_ERR_INVALID_ARG
+
+
+def test_rejects_small_or_misaligned_workspace():
+    need = moe.moe_ffn_workspace_size(16, 256, 512, 8, 2, B.MOE_BF16)
+    assert need > 0
+    o = moe.moe_opts_init()
+    o.workspace = DUMMY
+    o.workspace_bytes = need - 1
+    assert fwd(opts=o) == B.MOE_ERR_WORKSPACE
+    o.workspace = DUMMY + 16
+    o.workspace_bytes = need
+    assert fwd(opts=o) == B.MOE_ERR_WORKSPACE
+
+
+def test_workspace_layout_is_consistent():
+    for (T, d, f, E, k, dt) in [(16, 4096, 14336, 8, 2, 0), (4096, 4096, 14336, 8, 2, 0),
+                                (4096, 4096, 3584, 64, 8, 0), (64, 128, 512, 8, 2, 1),
+                                (1, 64, 64, 1, 1, 1)]:
+        lay = moe.moe_ffn_workspace_layout(T, d, f, E, k, dt)
+        assert lay.total == moe.moe_ffn_workspace_size(T, d, f, E, k, dt)
+        BT = lay.block_rows
+        # worst case of the padded permuted layout fits
+        assert lay.max_rows >= T * k + E * (BT - 1) and lay.max_rows % BT == 0
+        assert lay.router_blocks == (T + 31) // 32
+        es = 2 if dt == 0 else 4
+        fields = [("topk_idx", 4 * T * k), ("topk_w", 4 * T * k),
+                  ("block_counts", 4 * lay.router_blocks * E), ("counts", 4 * E),
+                  ("offsets", 4 * (E + 1)), ("num_tiles", 4),
+                  ("tile_expert", 4 * lay.max_rows // BT), ("row_token", 4 * lay.max_rows),
+                  ("tok_row", 4 * T * k), ("xs", es * lay.max_rows * d),
+                  ("h", es * lay.max_rows * f), ("y", 4 * lay.max_rows * d)]
+        spans = sorted((getattr(lay, n), getattr(lay, n) + size) for n, size in fields)
+        for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+            assert a1 <= b0                      # no overlap
+        assert all(s % 256 == 0 for s, _ in spans)
+        assert spans[-1][1] <= lay.total
+    with pytest.raises(moe.MoeError):
+        moe.moe_ffn_workspace_layout(16, 100, 512, 8, 2, 0)
+    assert moe.moe_ffn_workspace_size(16, 100, 512, 8, 2, 0) == 0
+
+
+def test_opts_defaults():
+    o = moe.moe_opts_init()
+    assert o.dtype == B.MOE_BF16 and not o.stream and not o.workspace and not o.router_bias

@@ -1,0 +1,120 @@
+"""GPU parity of the HIP layer against the fp64 oracle, through the C ABI.
+
+Small cases: every token is value-checked; they span several token tiles,
+a ragged router block and the degenerate shapes (T = 1, k = 1, k = E, E = 1,
+all tokens on one expert, empty experts, a zero router whose exact ties must
+go to the lowest expert ids).  Full workload shapes: routing and the
+permutation are checked on every token, values on a sample of tokens that
+includes the first, the last, the ragged tail and one token of every expert."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from sparse_mixture_experts_scan_amd.inputs import CONFIGS, MoEConfig, make_inputs  # noqa: E402
+import oracle  # noqa: E402
+from tests import gpu_harness as H  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    print(f"[gpu-parity] {msg}", file=sys.stderr, flush=True)
+
+
+def full_check(cfg: MoEConfig, seed=0, inp=None, value_tokens=None, n_hidden=2):
+    announce(f"case {cfg.name} T={cfg.T} d={cfg.d_model} f={cfg.d_ff} E={cfg.E} k={cfg.k} "
+             f"{cfg.dtype} seed={seed}")
+    inp = inp if inp is not None else make_inputs(cfg, seed)
+    dinp = H.upload(inp)
+    res = H.run_gpu(cfg, dinp)
+    s = oracle.router_logits(inp["x"], inp["W_router"], inp["bias"])
+    idx = oracle.select_topk(s, cfg.k)
+    gap, order_gap = oracle.routing_gaps(s, cfg.k)
+    orc = dict(idx=idx, gates=oracle.topk_gates(s, idx), gap=gap, order_gap=order_gap)
+    rinfo = H.check_routing(cfg, orc, res)
+    H.check_permutation(cfg, inp, res)
+    toks = np.arange(cfg.T) if value_tokens is None else value_tokens
+    valid_rows = np.nonzero(res["row_token"] >= 0)[0]
+    H.check_gather(cfg, inp, res, valid_rows[:: max(1, valid_rows.size // 64)])
+    err = H.check_values(cfg, inp, res, toks)
+    eh, ey = H.check_hidden_and_expert_outputs(cfg, inp, res, toks[:n_hidden])
+    # padding rows of H are exactly zero
+    lay = res["layout"]
+    pad = [r for r in range(min(lay.max_rows, res["offsets"][-1]))
+           if res["row_token"][r] < 0][:8]
+    if pad:
+        assert (H.ws_rows(res, cfg, "h", pad) == 0).all()
+    announce(f"  ok: max|err|/max|ref| out={err:.2e} H={eh:.2e} Y={ey:.2e} "
+             f"near_ties={rinfo['near_ties']} mismatched={rinfo['near_tie_mismatches']}")
+    return res, inp
+
+
+SMALL = [
+    MoEConfig("small_bf16", 300, 256, 512, 8, 2, "bf16"),
+    MoEConfig("small_f32", 300, 256, 512, 8, 2, "f32"),
+    MoEConfig("small_fine", 200, 128, 192, 64, 8, "bf16"),
+    MoEConfig("single_token", 1, 128, 256, 8, 2, "bf16"),
+    MoEConfig("top1", 77, 128, 256, 8, 1, "bf16"),
+    MoEConfig("k_equals_E", 50, 128, 128, 4, 4, "f32"),
+    MoEConfig("one_expert", 40, 64, 64, 1, 1, "f32"),
+    MoEConfig("ragged33", 33, 192, 320, 6, 3, "bf16"),
+    MoEConfig("many_tiles", 1000, 128, 256, 8, 2, "bf16"),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_small_shapes(cfg):
+    full_check(cfg, seed=1)
+
+
+def test_all_tokens_to_one_expert():
+    # a large bias on expert 5 puts it first for every token; the others
+    # split the second slot, some experts stay empty with E = 16
+    cfg = MoEConfig("skew_one", 130, 128, 256, 16, 2, "bf16",
+                    router_bias=tuple([0.0] * 5 + [50.0] + [-50.0] * 8 + [0.0, 0.0]))
+    res, _ = full_check(cfg, seed=2)
+    assert (res["idx"][:, 0] == 5).all()
+    assert (res["counts"][6:14] == 0).all()
+
+
+def test_zero_router_ties_go_to_lowest_ids():
+    cfg = MoEConfig("zero_router", 70, 128, 128, 8, 3, "bf16")
+    inp = make_inputs(cfg, seed=3)
+    inp["W_router"] = np.zeros_like(inp["W_router"])
+    res = H.run_gpu(cfg, H.upload(inp))
+    assert (res["idx"] == np.array([0, 1, 2])).all()
+    np.testing.assert_allclose(res["w"], 1.0 / 3, rtol=0, atol=1e-7)
+    H.check_permutation(cfg, inp, res)
+    H.check_values(cfg, inp, res, np.arange(cfg.T))
+
+
+def test_deterministic_bitwise():
+    cfg = MoEConfig("det", 500, 256, 384, 8, 2, "bf16")
+    inp = make_inputs(cfg, seed=4)
+    dinp = H.upload(inp)
+    a = H.run_gpu(cfg, dinp, keep_ws=False)
+    b = H.run_gpu(cfg, dinp, keep_ws=False)
+    np.testing.assert_array_equal(a["out"], b["out"])
+    np.testing.assert_array_equal(a["idx"], b["idx"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode"])
+def test_workload_all_tokens(name):
+    full_check(CONFIGS[name], seed=0)
+
+
+@pytest.mark.parametrize("name", ["prefill", "skewed", "fine"])
+def test_workload_sampled(name):
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, seed=0)
+    s = oracle.router_logits(inp["x"], inp["W_router"], inp["bias"])
+    toks = H.sample_tokens(cfg, oracle.select_topk(s, cfg.k), 40)
+    res, _ = full_check(cfg, inp=inp, value_tokens=toks)
+    if name == "skewed":
+        share = res["counts"] / res["counts"].sum()
+        announce(f"  skewed shares {np.round(share, 4).tolist()}")
+        assert 0.55 < share[0] + share[1] < 0.67 and share.min() < 0.02
