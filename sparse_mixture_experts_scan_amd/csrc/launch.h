@@ -34,6 +34,15 @@ void launch_gateup_stream(const Dims& D, const void* xs, const void* Wg, const v
 void launch_down_stream(const Dims& D, const void* h, const void* Wd, float* y,
                         const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                         const int32_t* tile_expert, hipStream_t s);
+// a3 + a4: grouped GEMMs, LDS-tiled MFMA form (many rows per expert, bf16)
+constexpr int kTileTokens = 256;  // token tile of the tiled form (= padding unit)
+bool tile_shape_ok(const Dims& D);
+void launch_gateup_tile(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* h,
+                        const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
+                        const int32_t* tile_expert, hipStream_t s);
+void launch_down_tile(const Dims& D, const void* h, const void* Wd, float* y,
+                      const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
+                      const int32_t* tile_expert, hipStream_t s);
 // a5: gate-weighted gather-sum back to token order
 void launch_combine(const Dims& D, const float* y, const int32_t* tok_row, const float* w,
                     void* out, hipStream_t s);

@@ -30,6 +30,9 @@ struct Plan {
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// average rows per expert from which the LDS-tiled GEMMs are used
+constexpr int64_t kTileMinRows = 96;
+
 // Validates a shape and builds the launch plan and workspace layout.
 // Touches no HIP API.
 int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dtype, Plan* p) {
@@ -56,8 +59,14 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   D.nblk = (D.T + moe::kRouterTokens - 1) / moe::kRouterTokens;
   const int64_t A = T * k;                       // (token, slot) assignments
   const int64_t rows_avg = (A + E - 1) / E;
-  int variant = 0;
-  D.BT = rows_avg <= 16 ? 16 : 32;
+  // GEMM form: weight-streaming for few rows per expert (weights read once,
+  // HBM-bound), LDS-tiled MFMA for many (compute-bound).
+  D.BT = moe::kTileTokens;
+  int variant = 1;
+  if (!(D.bf16 && rows_avg >= kTileMinRows && moe::tile_shape_ok(D))) {
+    variant = 0;
+    D.BT = rows_avg <= 16 ? 16 : 32;
+  }
   int64_t max_rows = A + (int64_t)E * (D.BT - 1);
   max_rows = (max_rows + D.BT - 1) / D.BT * D.BT;
   if (max_rows > (int64_t(1) << 30)) return fail(MOE_ERR_UNSUPPORTED, "too many rows");
@@ -214,10 +223,16 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, co
   moe::launch_scatter(D, x, idx, blk, offsets, tok_row, row_token, xs, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess)
     return hip_fail(e, "scatter launch");
-  moe::launch_gateup_stream(D, xs, W_gate, W_up, h, counts, offsets, num_tiles, tile_expert, s);
+  if (L.gemm_variant == 1)
+    moe::launch_gateup_tile(D, xs, W_gate, W_up, h, counts, offsets, num_tiles, tile_expert, s);
+  else
+    moe::launch_gateup_stream(D, xs, W_gate, W_up, h, counts, offsets, num_tiles, tile_expert, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess)
     return hip_fail(e, "gate/up launch");
-  moe::launch_down_stream(D, h, W_down, y, counts, offsets, num_tiles, tile_expert, s);
+  if (L.gemm_variant == 1)
+    moe::launch_down_tile(D, h, W_down, y, counts, offsets, num_tiles, tile_expert, s);
+  else
+    moe::launch_down_stream(D, h, W_down, y, counts, offsets, num_tiles, tile_expert, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(5)) != hipSuccess)
     return hip_fail(e, "down launch");
   moe::launch_combine(D, y, tok_row, w, out, s);

@@ -14,63 +14,108 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// a1: router.  One block = kRouterTokens tokens x all E experts.
-// Scores: fp32 FMA over d in ascending order, x and W_router staged in LDS.
+// a1: router.  One block = kRouterTokens tokens (two 16-token MFMA columns) x
+// all E experts (16-expert MFMA rows, zero-padded).  Scores are an fp32 GEMM
+// on v_mfma_f32_16x16x4_f32: A = W_router^T (expert rows), B = x^T (token
+// columns, bf16 widened exactly), K = d_model split over the 4 waves in
+// interleaved 16-element groups; wave partials are added in fixed order.
 // Top-k: one thread per token, k passes of an arg-max over E (strict '>' in
 // ascending expert order, so equal scores go to the lower index).
 // Softmax over the selected k, shifted by the largest selected score.
 // ---------------------------------------------------------------------------
+template <typename T>
+__device__ inline f32x4 load4_f32(const T* p);
+template <>
+__device__ inline f32x4 load4_f32<float>(const float* p) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  return f32x4{v.x, v.y, v.z, v.w};
+}
+template <>
+__device__ inline f32x4 load4_f32<bf16_t>(const bf16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+               __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+}
+
 template <typename T>
 __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
     int nT, int d, int E, int k, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
     int32_t* __restrict__ blk_counts) {
   constexpr int TB = kRouterTokens;
-  constexpr int DC = 64;                       // d-chunk staged per step
-  constexpr int QMAX = TB * 64 / kRouterThreads;  // (token, expert) pairs per thread
-  __shared__ float xs[TB][DC + 1];
-  __shared__ float ws[DC][64];
+  constexpr int NB = TB / 16;            // token column blocks
+  constexpr int MB = 64 / 16;            // expert row blocks (max)
+  constexpr int NWAVE = kRouterThreads / kWave;
+  __shared__ f32x4 red[NWAVE - 1][MB * NB][kWave];
   __shared__ float slog[TB][65];
   __shared__ int hist[64];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * TB;
-  const int npairs = TB * E;
-  float acc[QMAX];
-#pragma unroll
-  for (int q = 0; q < QMAX; ++q) acc[q] = 0.f;
+  const int mb_used = (E + 15) / 16;
+  const int m = lane & 15, g = lane >> 4;
   if (tid < 64) hist[tid] = 0;
 
-  for (int j0 = 0; j0 < d; j0 += DC) {
-    for (int i = tid; i < TB * DC; i += kRouterThreads) {
-      const int tt = i / DC, jj = i % DC, t = t0 + tt;
-      xs[tt][jj] = t < nT ? Elem<T>::to_f32(x[(size_t)t * d + j0 + jj]) : 0.f;
-    }
-    for (int i = tid; i < DC * E; i += kRouterThreads) {
-      const int jj = i / E, e = i % E;
-      ws[jj][e] = Wr[(size_t)(j0 + jj) * E + e];
-    }
-    __syncthreads();
+  f32x4 acc[MB][NB];
 #pragma unroll
-    for (int q = 0; q < QMAX; ++q) {
-      const int p = tid + kRouterThreads * q;
-      if (p < npairs) {
-        const int tt = p / E, e = p % E;
-        float a = acc[q];
-#pragma unroll 16
-        for (int jj = 0; jj < DC; ++jj) a = fmaf(xs[tt][jj], ws[jj][e], a);
-        acc[q] = a;
+  for (int a = 0; a < MB; ++a)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  bool tok_ok[NB];
+  const T* xp[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int t = t0 + b * 16 + m;
+    tok_ok[b] = t < nT;
+    xp[b] = x + (size_t)(tok_ok[b] ? t : 0) * d + 4 * g;
+  }
+  const int ngroups = d / 16;
+  for (int kg = wave; kg < ngroups; kg += NWAVE) {
+    const int k0 = kg * 16 + 4 * g;       // this lane's 4 consecutive k
+    f32x4 bv[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      bv[b] = tok_ok[b] ? load4_f32<T>(xp[b] + kg * 16) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int a = 0; a < MB; ++a) {
+      if (a < mb_used) {
+        const int ex = a * 16 + m;
+        f32x4 av = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (ex < E) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) av[i] = Wr[(size_t)(k0 + i) * E + ex];
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[b][i], acc[a][b], 0, 0, 0);
       }
     }
-    __syncthreads();
   }
+  if (wave > 0) {
 #pragma unroll
-  for (int q = 0; q < QMAX; ++q) {
-    const int p = tid + kRouterThreads * q;
-    if (p < npairs) {
-      const int tt = p / E, e = p % E;
-      slog[tt][e] = acc[q] + (bias ? bias[e] : 0.f);
-    }
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) red[wave - 1][a * NB + b][lane] = acc[a][b];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    // D[m][n]: lane holds experts a*16 + 4*g + i of token b*16 + m
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        f32x4 v = acc[a][b];
+#pragma unroll
+        for (int q = 0; q < NWAVE - 1; ++q) v += red[q][a * NB + b][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ex = a * 16 + 4 * g + i;
+          if (ex < E) slog[b * 16 + m][ex] = v[i] + (bias ? bias[ex] : 0.f);
+        }
+      }
   }
   __syncthreads();
 
@@ -193,19 +238,23 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(
 
 // ---------------------------------------------------------------------------
 // a2 (part 2): per router block, rank of each (token, slot) among the
-// block's earlier pairs routed to the same expert -> permuted row
+// block's earlier pairs routed to the same expert (wave ballots per expert,
+// plus the counts of earlier waves) -> permuted row
 // offsets[e] + base[blk][e] + rank, so rows inside an expert segment are in
 // ascending (token, slot) order.  Then copy x[t] to Xs[row], 16 B per lane.
+// blockIdx.y splits the row copy into column slices (small T has few token
+// blocks); only slice 0 writes the row maps.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kRouterThreads) void scatter_gather_kernel(
     const T* __restrict__ x, const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
     const int32_t* __restrict__ offsets, int nT, int d, int E, int k,
     int32_t* __restrict__ tok_row, int32_t* __restrict__ row_token, T* __restrict__ xs) {
-  __shared__ int sE[kRouterThreads];
+  constexpr int NWAVE = kRouterThreads / kWave;
+  __shared__ int wcnt[NWAVE][64];
   __shared__ int sRow[kRouterThreads];
   __shared__ int sTok[kRouterThreads];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kRouterTokens;
   const int np = kRouterTokens * k;
   int e = -1, t = -1;
@@ -214,23 +263,33 @@ __global__ __launch_bounds__(kRouterThreads) void scatter_gather_kernel(
     if (t < nT) e = idx[(size_t)t0 * k + tid];
     else t = -1;
   }
-  sE[tid] = e;
+  int rank_w = 0;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int ex = 0; ex < E; ++ex) {
+    const uint64_t msk = __ballot(e == ex);
+    if (e == ex) rank_w = __popcll(msk & lt);
+    if (lane == 0) wcnt[wave][ex] = __popcll(msk);
+  }
   __syncthreads();
   int row = -1;
   if (e >= 0) {
-    int rank = 0;
-    for (int q = 0; q < tid; ++q) rank += (sE[q] == e);
+    int rank = rank_w;
+    for (int w = 0; w < wave; ++w) rank += wcnt[w][e];
     row = offsets[e] + base[(size_t)blockIdx.x * E + e] + rank;
-    tok_row[(size_t)t0 * k + tid] = row;
-    row_token[row] = t;
+    if (blockIdx.y == 0) {
+      tok_row[(size_t)t0 * k + tid] = row;
+      row_token[row] = t;
+    }
   }
   sRow[tid] = row;
   sTok[tid] = t;
   __syncthreads();
-  const int cpr = d * (int)sizeof(T) / 16;  // 16-byte chunks per row
   const int per_chunk = 16 / (int)sizeof(T);
-  for (int i = tid; i < np * cpr; i += kRouterThreads) {
-    const int p = i / cpr, c = i - p * cpr;
+  const int cpr = d / per_chunk;                       // 16-byte chunks per row
+  const int cps = cpr / gridDim.y;                     // chunks in this column slice
+  const int c0 = blockIdx.y * cps;
+  for (int i = tid; i < np * cps; i += kRouterThreads) {
+    const int p = i / cps, c = c0 + (i - p * cps);
     const int r = sRow[p];
     if (r >= 0)
       st16(xs + (size_t)r * d + c * per_chunk, ld16(x + (size_t)sTok[p] * d + c * per_chunk));
@@ -294,12 +353,17 @@ void launch_scan(const Dims& D, int32_t* blk_counts, int32_t* counts, int32_t* o
 void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int32_t* blk_base,
                     const int32_t* offsets, int32_t* tok_row, int32_t* row_token, void* xs,
                     hipStream_t s) {
+  // column slices so that small T still spreads the copy over many blocks
+  const int cpr = D.d * (D.bf16 ? 2 : 4) / 16;
+  int cs = 1;
+  while (D.nblk * cs < 256 && cs * 2 <= cpr / 16 && cpr % (cs * 2) == 0) cs *= 2;
+  const dim3 grid(D.nblk, cs);
   if (D.bf16)
-    scatter_gather_kernel<bf16_t><<<D.nblk, kRouterThreads, 0, s>>>(
+    scatter_gather_kernel<bf16_t><<<grid, kRouterThreads, 0, s>>>(
         (const bf16_t*)x, idx, blk_base, offsets, D.T, D.d, D.E, D.k, tok_row, row_token,
         (bf16_t*)xs);
   else
-    scatter_gather_kernel<float><<<D.nblk, kRouterThreads, 0, s>>>(
+    scatter_gather_kernel<float><<<grid, kRouterThreads, 0, s>>>(
         (const float*)x, idx, blk_base, offsets, D.T, D.d, D.E, D.k, tok_row, row_token,
         (float*)xs);
 }

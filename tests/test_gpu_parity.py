@@ -63,12 +63,19 @@ SMALL = [
     MoEConfig("one_expert", 40, 64, 64, 1, 1, "f32"),
     MoEConfig("ragged33", 33, 192, 320, 6, 3, "bf16"),
     MoEConfig("many_tiles", 1000, 128, 256, 8, 2, "bf16"),
+    # LDS-tiled variant (>= 96 rows per expert, bf16, d % 256, d_ff % 128)
+    MoEConfig("tile_small", 1000, 256, 384, 8, 2, "bf16"),
+    MoEConfig("tile_ragged", 777, 512, 256, 4, 1, "bf16"),
+    MoEConfig("tile_fine", 900, 256, 128, 16, 4, "bf16"),
 ]
+
+TILED = {"tile_small", "tile_ragged", "tile_fine"}
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_small_shapes(cfg):
-    full_check(cfg, seed=1)
+    res, _ = full_check(cfg, seed=1)
+    assert res["layout"].gemm_variant == (1 if cfg.name in TILED else 0)
 
 
 def test_all_tokens_to_one_expert():
@@ -114,6 +121,7 @@ def test_workload_sampled(name):
     s = oracle.router_logits(inp["x"], inp["W_router"], inp["bias"])
     toks = H.sample_tokens(cfg, oracle.select_topk(s, cfg.k), 40)
     res, _ = full_check(cfg, inp=inp, value_tokens=toks)
+    assert res["layout"].gemm_variant == 1
     if name == "skewed":
         share = res["counts"] / res["counts"].sum()
         announce(f"  skewed shares {np.round(share, 4).tolist()}")
