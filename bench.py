@@ -36,6 +36,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
                    help="tokens of the oracle sample (0 = per-workload default)")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="before warmup, run one device-to-device copy of this many MiB "
+                        "(a known-size reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -114,6 +117,13 @@ def main():
                     bias=d["bias"], out=out, workspace=ws, expert_counts=counts, stream=stream,
                     stage_events=events)
 
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()

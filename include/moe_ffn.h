@@ -121,7 +121,9 @@ typedef struct moe_ws_layout {
   int64_t max_rows;         /* rows reserved for the permuted layout          */
   int64_t router_blocks;    /* token blocks of the router / scatter kernels   */
   int32_t gemm_variant;     /* 0 = weight-streaming, 1 = LDS-tiled             */
-  int32_t reserved;
+  int32_t down_splits;      /* K-splits of the down GEMM: y holds this many
+                               partial [max_rows][d_model] blocks, summed by
+                               the combine                                     */
   size_t topk_idx;          /* [T][k]                                          */
   size_t topk_w;            /* [T][k] float32                                  */
   size_t block_counts;      /* [router_blocks][E]: per-block counts, then bases */
@@ -133,7 +135,8 @@ typedef struct moe_ws_layout {
   size_t tok_row;           /* [T][k] permuted row of each (token, slot)       */
   size_t xs;                /* [max_rows][d_model] dtype: gathered tokens      */
   size_t h;                 /* [max_rows][d_ff] dtype: SiLU(gate) * up         */
-  size_t y;                 /* [max_rows][d_model] float32: expert outputs     */
+  size_t y;                 /* [down_splits][max_rows][d_model] float32:
+                               partial expert outputs (their sum is W2 H)       */
   size_t total;             /* bytes                                           */
 } moe_ws_layout_t;
 

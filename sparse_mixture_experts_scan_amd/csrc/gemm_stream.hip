@@ -10,11 +10,13 @@
 // exactly once and nothing is reused, so this form goes straight from HBM to
 // registers (no LDS staging of weights): the MFMA A operand is 16 weight rows
 // (output features), the B operand 16 token rows, both K-contiguous, 16 bytes
-// per lane per load.  A workgroup owns FT output features of one token tile;
-// its 4 waves split K by interleaved 16-byte k-groups so that the 4 waves
-// together read contiguous 256-byte runs of each weight row; the partial sums
-// are added in fixed wave order through LDS (deterministic), then the
-// epilogue (SiLU(gate)*up, or plain fp32) is applied and stored.
+// per lane per raw buffer load (scalar resource, loop-invariant lane offsets,
+// the K advance in the scalar offset).  A workgroup owns FT output features
+// of one token tile; its 4 waves split K in interleaved runs of k-steps and
+// keep the next batch of loads in flight while the current batch's MFMAs
+// run.  The partial sums are added in fixed wave order through LDS
+// (deterministic), then the epilogue (SiLU(gate)*up, or plain fp32) is
+// applied and stored.
 //
 // Token rows past the expert's count (segment padding) read as zero, so the
 // padding rows of H are exactly zero and every row stored is in bounds.
@@ -24,71 +26,66 @@
 namespace moe {
 
 constexpr int kStreamThreads = 256;
+#ifndef MOE_STREAM_U
+#define MOE_STREAM_U 8       // k-steps per run (per batch of loads)
+#endif
+#ifndef MOE_STREAM_FT_GU
+#define MOE_STREAM_FT_GU 16
+#endif
+#ifndef MOE_STREAM_FT_DN
+#define MOE_STREAM_FT_DN 32
+#endif
+constexpr int kBufCfg = 0x00020000;  // raw buffer, 32-bit data format
 
+// Buffer resources must sit in scalar registers: make every field provably
+// wave-uniform.
+__device__ inline __amdgpu_buffer_rsrc_t stream_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, kBufCfg);
+}
+
+__device__ __forceinline__ uint4 sload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// One batch = a run of U consecutive k-steps (16 bytes per lane each) of one
+// wave; run r belongs to wave r % 4, so the 4 waves' runs interleave along K.
 template <typename T, int BT, int FT, bool GATEUP, int U>
-__global__ __launch_bounds__(kStreamThreads) void stream_gemm_kernel(
-    const T* __restrict__ act, const T* __restrict__ W0, const T* __restrict__ W1,
-    void* __restrict__ outp, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ num_tiles,
-    const int32_t* __restrict__ tile_expert, int N, int K) {
-  constexpr int VEC = Elem<T>::kVec;
-  constexpr int KSTEP = 4 * VEC;          // K covered by one 16x16 MFMA k-group set
-  constexpr int NF = FT / 16;             // 16-row weight fragments per wave
-  constexpr int NT = BT / 16;             // 16-row token fragments
-  constexpr int NW = GATEUP ? 2 : 1;      // weight stacks (gate, up) or (down)
-  constexpr int NWAVE = kStreamThreads / kWave;
-  __shared__ f32x4 red[NWAVE - 1][NW * NF * NT][kWave];
+struct StreamBatch {
+  static constexpr int VEC = Elem<T>::kVec;
+  static constexpr int KSTEP = 4 * VEC;   // K covered by one 16-byte k-group set
+  static constexpr int NF = FT / 16;      // 16-row weight fragments
+  static constexpr int NT = BT / 16;      // 16-row token fragments
+  static constexpr int NW = GATEUP ? 2 : 1;
+  uint4 wv[NW][NF][U], av[NT][U];
 
-  const int tile = blockIdx.y;
-  if (tile >= *num_tiles) return;
-  const int e = tile_expert[tile];
-  const int row0 = tile * BT;
-  const int valid_end = offsets[e] + counts[e];
-  const int f0 = blockIdx.x * FT;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-  const int lr = lane & 15, kg = lane >> 4;
-
-  const T* wp[NW];
-  wp[0] = W0 + ((size_t)e * N + f0 + lr) * K + kg * VEC;
-  if constexpr (GATEUP) wp[1] = W1 + ((size_t)e * N + f0 + lr) * K + kg * VEC;
-  const T* ap[NT];
-  bool aok[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const int r = row0 + n * 16 + lr;
-    aok[n] = r < valid_end;
-    ap[n] = act + (size_t)r * K + kg * VEC;
-  }
-
-  f32x4 acc[NW][NF][NT];
-#pragma unroll
-  for (int w = 0; w < NW; ++w)
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int n = 0; n < NT; ++n) acc[w][f][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nks = K / KSTEP;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  for (int ks0 = wave; ks0 < nks; ks0 += NWAVE * U) {
-    uint4 wv[NW][NF][U];
-    uint4 av[NT][U];
+  template <bool FULL>
+  __device__ __forceinline__ void load(const __amdgpu_buffer_rsrc_t (&rw)[NW],
+                                       __amdgpu_buffer_rsrc_t ra, const uint32_t (&wo)[NF],
+                                       const uint32_t (&ao)[NT], int run, int valid) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int ks = ks0 + NWAVE * u;
-      if (ks < nks) {
-        const size_t ko = (size_t)ks * KSTEP;
+      if (FULL || u < valid) {
+        const uint32_t so = (uint32_t)(run * U + u) * KSTEP * sizeof(T);
 #pragma unroll
         for (int w = 0; w < NW; ++w)
 #pragma unroll
-          for (int f = 0; f < NF; ++f) wv[w][f][u] = ld16(wp[w] + (size_t)f * 16 * K + ko);
+          for (int f = 0; f < NF; ++f) wv[w][f][u] = sload(rw[w], wo[f], so);
 #pragma unroll
-        for (int n = 0; n < NT; ++n) av[n][u] = aok[n] ? ld16(ap[n] + ko) : zero;
+        for (int n = 0; n < NT; ++n) av[n][u] = sload(ra, ao[n], so);
       }
     }
+  }
+  template <bool FULL>
+  __device__ __forceinline__ void compute(f32x4 (&acc)[NW][NF][NT], int valid) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (ks0 + NWAVE * u < nks) {
+      if (FULL || u < valid) {
 #pragma unroll
         for (int w = 0; w < NW; ++w)
 #pragma unroll
@@ -98,6 +95,68 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gemm_kernel(
               acc[w][f][n] = Elem<T>::mfma16(wv[w][f][u], av[n][u], acc[w][f][n]);
       }
     }
+  }
+};
+
+template <typename T, int BT, int FT, bool GATEUP, int U>
+__global__ __launch_bounds__(kStreamThreads) void stream_gemm_kernel(
+    const T* __restrict__ act, const T* __restrict__ W0, const T* __restrict__ W1,
+    void* __restrict__ outp, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ num_tiles,
+    const int32_t* __restrict__ tile_expert, int N, int K) {
+  using SB = StreamBatch<T, BT, FT, GATEUP, U>;
+  constexpr int NF = SB::NF, NT = SB::NT, NW = SB::NW, KSTEP = SB::KSTEP;
+  constexpr int NWAVE = kStreamThreads / kWave;
+  __shared__ f32x4 red[NWAVE - 1][NW * NF * NT][kWave];
+
+  const int tile = blockIdx.y;
+  if (tile >= *num_tiles) return;
+  const int e = tile_expert[tile];
+  const int row0 = tile * BT;
+  const int valid_end = offsets[e] + counts[e];
+  const int f0 = blockIdx.x * FT;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+  const int lr = lane & 15, kg = lane >> 4;
+
+  const uint32_t row_bytes = (uint32_t)K * sizeof(T);
+  __amdgpu_buffer_rsrc_t rw[NW];
+  rw[0] = stream_rsrc(W0 + ((size_t)e * N + f0) * K, FT * row_bytes);
+  if constexpr (GATEUP) rw[1] = stream_rsrc(W1 + ((size_t)e * N + f0) * K, FT * row_bytes);
+  // token rows past the expert's count fall outside the resource: read as 0
+  const int nvalid = max(0, min(BT, valid_end - row0));
+  const __amdgpu_buffer_rsrc_t ra = stream_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
+  uint32_t wo[NF], ao[NT];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) wo[f] = (uint32_t)(f * 16 + lr) * row_bytes + kg * 16;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) ao[n] = (uint32_t)(n * 16 + lr) * row_bytes + kg * 16;
+
+  f32x4 acc[NW][NF][NT];
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[w][f][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Full runs r < nruns; this wave owns runs wave, wave + 4, ...  Software
+  // pipeline: run b + 1's loads are issued before run b's MFMAs.
+  const int nks = K / KSTEP;
+  const int nruns = nks / U, rem = nks % U;
+  const int nb = nruns > wave ? (nruns - wave + NWAVE - 1) / NWAVE : 0;
+  SB A, B;
+  if (nb > 0) A.template load<true>(rw, ra, wo, ao, wave, U);
+  for (int b = 0; b < nb; b += 2) {
+    if (b + 1 < nb) B.template load<true>(rw, ra, wo, ao, wave + (b + 1) * NWAVE, U);
+    A.template compute<true>(acc, U);
+    if (b + 1 >= nb) break;
+    if (b + 2 < nb) A.template load<true>(rw, ra, wo, ao, wave + (b + 2) * NWAVE, U);
+    B.template compute<true>(acc, U);
+  }
+  if (rem > 0 && wave == nruns % NWAVE) {  // the one partial run
+    A.template load<false>(rw, ra, wo, ao, nruns, rem);
+    A.template compute<false>(acc, rem);
   }
 
   // cross-wave reduction in fixed order 0,1,2,3
@@ -148,9 +207,9 @@ template <typename T, int BT>
 static void gateup_stream(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* h,
                           const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                           const int32_t* tile_expert, hipStream_t s) {
-  constexpr int FT = 32;
+  constexpr int FT = MOE_STREAM_FT_GU;
   dim3 grid(D.f / FT, D.max_tiles);
-  stream_gemm_kernel<T, BT, FT, true, 8><<<grid, kStreamThreads, 0, s>>>(
+  stream_gemm_kernel<T, BT, FT, true, MOE_STREAM_U><<<grid, kStreamThreads, 0, s>>>(
       (const T*)xs, (const T*)Wg, (const T*)Wu, h, counts, offsets, num_tiles, tile_expert, D.f,
       D.d);
 }
@@ -159,9 +218,9 @@ template <typename T, int BT>
 static void down_stream(const Dims& D, const void* h, const void* Wd, float* y,
                         const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                         const int32_t* tile_expert, hipStream_t s) {
-  constexpr int FT = 64;
+  constexpr int FT = MOE_STREAM_FT_DN;
   dim3 grid(D.d / FT, D.max_tiles);
-  stream_gemm_kernel<T, BT, FT, false, 8><<<grid, kStreamThreads, 0, s>>>(
+  stream_gemm_kernel<T, BT, FT, false, MOE_STREAM_U><<<grid, kStreamThreads, 0, s>>>(
       (const T*)h, (const T*)Wd, nullptr, y, counts, offsets, num_tiles, tile_expert, D.d, D.f);
 }
 

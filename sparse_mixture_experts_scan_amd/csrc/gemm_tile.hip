@@ -21,6 +21,8 @@
 // that are entirely past it skip their MFMAs.  Work-group ids are remapped
 // so that consecutive tiles (same expert, neighbouring feature tiles) land on
 // the same XCD and share its L2.
+#include <cmath>
+
 #include "common.h"
 #include "launch.h"
 
@@ -28,15 +30,38 @@ namespace moe {
 
 constexpr int kTileThreads = 256;
 constexpr int kTileBT = kTileTokens;  // token rows per tile (= padding unit)
-constexpr int kTileBK = 64;           // K per LDS stage
 constexpr int kTileRows = 256;        // weight rows per tile
-constexpr int kTileStageBytes = 2 * kTileRows * kTileBK * 2;  // A + B per stage
-constexpr int kTileLds = 2 * kTileStageBytes;                 // double buffered
+#ifndef MOE_TILE_BK
+#define MOE_TILE_BK 64
+#endif
+#ifndef MOE_TILE_NS
+#define MOE_TILE_NS 2
+#endif
+constexpr int kTileBK = MOE_TILE_BK;  // K per LDS stage
+constexpr int kTileNS = MOE_TILE_NS;  // LDS ring depth (stages)
 constexpr int kXcds = 8;
-constexpr int kFeatGroup = 8;         // feature tiles per XCD-local group
+#ifndef MOE_TILE_FEAT_GROUP
+#define MOE_TILE_FEAT_GROUP 8
+#endif
+constexpr int kFeatGroup = MOE_TILE_FEAT_GROUP;  // feature tiles per XCD-local group
 
+constexpr int kRowBytes = kTileBK * 2;              // LDS bytes per tile row
+constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per row
+constexpr int kOperBytes = 256 * kRowBytes;         // one operand tile in LDS
+constexpr int kStageBytes = 2 * kOperBytes;         // A + B
+constexpr int kDmaPerWave = 256 * kChunks / 64 / 4; // 1 KiB DMA loads per wave per operand
+constexpr int kKSteps = kTileBK / 16;               // 32x32x16 MFMA k-steps per stage
+static_assert(kTileBK == 32 || kTileBK == 64, "stage K must be 32 or 64");
+static_assert(kTileNS >= 2 && kTileNS <= 4, "ring depth 2..4");
+static_assert(kTileNS * kStageBytes <= 160 * 1024, "LDS ring exceeds 160 KiB");
+
+// XOR swizzle of the 16-byte chunks of LDS row r: the 32 rows an MFMA fragment
+// reads (and the rows a DMA fills) fall in distinct banks.
+__device__ inline int swz_key(int r) {
+  return kChunks == 8 ? ((r ^ (r >> 3)) & 7) : (((r >> 1) ^ (r >> 3)) & 3);
+}
 __device__ inline int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+  return row * kRowBytes + ((chunk ^ swz_key(row)) << 4);
 }
 
 __device__ inline f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
@@ -44,19 +69,179 @@ __device__ inline f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kBufferCfg = 0x00020000;  // raw buffer, 32-bit data format
+
+// Buffer resources must live in scalar registers: the fields are made provably
+// wave-uniform, otherwise each load is wrapped in a per-lane loop.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, kBufferCfg);
+}
+
+// Wait until at most N of this wave's vector-memory operations (here: LDS DMA
+// loads) are outstanding; lgkm/exp counters untouched.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// All of this wave's LDS reads done, then the workgroup barrier.  No memory
+// fence: LDS DMA completion is waited for explicitly with wait_vmcnt.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+struct TileCtx {
+  __amdgpu_buffer_rsrc_t rA, rB;   // this wave's A resource (gate or up half), B
+  uint32_t voffA[kDmaPerWave], voffB[kDmaPerWave];
+  int dma_base;                    // this wave's first DMA slot (1 KiB units)
+  uint32_t k_byte0;                // byte offset of this part's first K column
+  int arow[4];
+  int brow;                        // first token row of this wave inside the tile
+};
+
+// Issue stage ks's DMA loads into stage buffer `buf`: each lane fetches the
+// global 16 bytes that belong at LDS slot (dma_base + j) * 64 + lane.
+__device__ __forceinline__ void tile_issue(const TileCtx& c, char* buf, int ks) {
+  const uint32_t so = c.k_byte0 + (uint32_t)ks * kTileBK * 2;
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        c.rA, (lds_void*)(buf + (c.dma_base + j) * 1024), 16, c.voffA[j], so, 0, 0);
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        c.rB, (lds_void*)(buf + kOperBytes + (c.dma_base + j) * 1024), 16, c.voffB[j], so, 0, 0);
+}
+
+template <int NBV>
+__device__ __forceinline__ void tile_frags(const TileCtx& c, const char* buf, int kk, int lane,
+                                           uint4 (&af)[4], uint4 (&bf)[4]) {
+  const char* A = buf;
+  const char* B = buf + kOperBytes;
+  const int r32 = lane & 31, chunk = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) af[a] = *reinterpret_cast<const uint4*>(A + swz(c.arow[a] + r32, chunk));
+#pragma unroll
+  for (int b = 0; b < NBV; ++b)
+    bf[b] = *reinterpret_cast<const uint4*>(B + swz(c.brow + b * 32 + r32, chunk));
+}
+
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+template <int NBV>
+__device__ __forceinline__ void tile_compute(const TileCtx& c, const char* buf, int lane,
+                                             f32x16 (&acc)[4][4]) {
+  uint4 af[4], bf[4], na[4], nb[4];
+  tile_frags<NBV>(c, buf, 0, lane, af, bf);
+#pragma unroll
+  for (int kk = 0; kk < kKSteps; ++kk) {
+    if (kk + 1 < kKSteps) tile_frags<NBV>(c, buf, kk + 1, lane, na, nb);
+#pragma unroll
+    for (int b = 0; b < NBV; ++b)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) acc[a][b] = mfma32(af[a], bf[b], acc[a][b]);
+    // order: the next k-step's fragment reads one per MFMA, then the rest
+    // of the MFMAs, so the reads overlap this k-step's matrix work
+    if (kk + 1 < kKSteps) {
+      constexpr int nr = 4 + NBV, nm = 4 * NBV;
+      constexpr int pairs = nr < nm ? nr : nm;
+#pragma unroll
+      for (int i = 0; i < pairs; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      if (nm > pairs) __builtin_amdgcn_sched_group_barrier(kSchedMfma, nm - pairs, 0);
+      if (nr > pairs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, nr - pairs, 0);
+    }
+    if (kk + 1 < kKSteps) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) af[a] = na[a];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bf[b] = nb[b];
+    }
+  }
+}
+
+// Wait for stage ks's loads: the loads of the n_after stages issued after it
+// may stay in flight.
+__device__ __forceinline__ void wait_stage(int n_after) {
+  constexpr int per_stage = 2 * kDmaPerWave;
+  if (n_after >= 2) wait_vmcnt<2 * per_stage>();
+  else if (n_after == 1) wait_vmcnt<per_stage>();
+  else wait_vmcnt<0>();
+}
+
+// Main loop over K.  Ring of kTileNS stage buffers: stage ks lives in buffer
+// ks % NS; after the barrier that opens stage ks (all waves have finished
+// stage ks - 1), the loads of stage ks + NS - 1 are issued into the buffer
+// stage ks - 1 used, so loads run NS - 1 stages ahead of the MFMAs.
+// nk is a multiple of kTileNS (checked on the host), so every pass of the
+// outer loop runs all kTileNS stages: no early exit inside the unrolled body.
+template <int NBV>
+__device__ __forceinline__ void tile_main_loop(const TileCtx& c, char* const (&bufs)[kTileNS],
+                                               int nk, int lane, f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int s = 0; s < kTileNS - 1; ++s) tile_issue(c, bufs[s], s);
+  for (int ks0 = 0; ks0 < nk; ks0 += kTileNS) {
+    const bool last = ks0 + kTileNS >= nk;
+#pragma unroll
+    for (int u = 0; u < kTileNS; ++u) {
+      const int ks = ks0 + u;
+      // stages issued after ks: NS - 2 in steady state; in the last pass the
+      // loads stop at stage nk - 1 (issued at u = 0)
+      wait_stage(last ? min(kTileNS - 2, kTileNS - 1 - u) : kTileNS - 2);
+      lds_barrier();
+      // keep the DMA issue right after the barrier: the scheduler would
+      // otherwise sink it behind the MFMAs and shrink the prefetch distance
+      __builtin_amdgcn_sched_barrier(0);
+      if (!last || u == 0) tile_issue(c, bufs[(u + kTileNS - 1) % kTileNS], ks + kTileNS - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      tile_compute<NBV>(c, bufs[u], lane, acc);
+    }
+  }
+}
+
 template <bool GATEUP>
 __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
     const bf16_t* __restrict__ act, const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
     void* __restrict__ outp, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ num_tiles,
-    const int32_t* __restrict__ tile_expert, int N, int K, int n_ft, int n_tt, int per_xcd) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int32_t* __restrict__ tile_expert, int N, int K, int n_ft, int n_tt, int per_xcd,
+    int parts, size_t part_stride) {
+  // one __shared__ array per ring stage, so that the compiler can tell which
+  // DMA each LDS read depends on
+  __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
+#if MOE_TILE_NS > 2
+  __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
+#endif
+#if MOE_TILE_NS > 3
+  __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
+#endif
+  char* const bufs[kTileNS] = {st0, st1
+#if MOE_TILE_NS > 2
+                               , st2
+#endif
+#if MOE_TILE_NS > 3
+                               , st3
+#endif
+  };
   constexpr int FB = GATEUP ? kTileRows / 2 : kTileRows;  // output features per tile
 
   // ---- tile id: XCD-contiguous remap, then groups of kFeatGroup feature tiles
   const int L = blockIdx.x;
-  const int Lp = (L % kXcds) * per_xcd + L / kXcds;
-  if (Lp >= n_ft * n_tt) return;
+  int Lp = (L % kXcds) * per_xcd + L / kXcds;
+  if (Lp >= parts * n_ft * n_tt) return;
+  const int part = Lp / (n_ft * n_tt);      // K-split part (slowest)
+  Lp -= part * n_ft * n_tt;
   const int grp = Lp / (kFeatGroup * n_tt);
   const int rem = Lp - grp * kFeatGroup * n_tt;
   const int gsize = min(kFeatGroup, n_ft - grp * kFeatGroup);
@@ -68,53 +253,43 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
   const int valid_end = offsets[e] + counts[e];
   const int f0 = ft * FB;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wf = wave & 1, wt = wave >> 1;
 
-  // ---- global -> register -> LDS staging: thread owns rows rbase + 32 i, chunk kc
-  const int kc = tid & 7, rbase = tid >> 3;
-  const bf16_t* gA0;
-  const bf16_t* gA1;
-  if constexpr (GATEUP) {
-    gA0 = W0 + ((size_t)e * N + f0 + rbase) * K + kc * 8;   // gate rows 0..127
-    gA1 = W1 + ((size_t)e * N + f0 + rbase) * K + kc * 8;   // up rows 128..255
-  } else {
-    gA0 = W0 + ((size_t)e * N + f0 + rbase) * K + kc * 8;
-    gA1 = gA0 + (size_t)128 * K;
+  // ---- DMA assignment: wave w fills LDS slots [w * kDmaPerWave, +kDmaPerWave)
+  // of each operand (1 KiB each); slot q's lane i holds LDS chunk position
+  // p = q * 64 + i = row * kChunks + swizzled chunk.
+  TileCtx c;
+  c.dma_base = wave * kDmaPerWave;
+  const int Kp = K / parts;                 // K columns of this part
+  c.k_byte0 = (uint32_t)(part * Kp) * 2;
+  const uint32_t row_bytes = (uint32_t)K * 2;
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int p = (c.dma_base + j) * 64 + lane;
+    const int r = p / kChunks, cs = p % kChunks;
+    const int cg = cs ^ swz_key(r);                         // global chunk stored there
+    const int ra = GATEUP ? (r & (kTileRows / 2 - 1)) : r;  // row inside A's resource
+    c.voffA[j] = (uint32_t)ra * row_bytes + cg * 16;
+    c.voffB[j] = (uint32_t)r * row_bytes + cg * 16;
   }
-  const bf16_t* gB = act + (size_t)(row0 + rbase) * K + kc * 8;
-  const int bvalid = valid_end - row0 - rbase;  // token row rbase + 32 i valid iff 32 i < bvalid
-  uint4 ra[8], rb[8];
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-
-  auto gload = [&](int ks) {
-    const size_t ko = (size_t)ks * kTileBK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = ld16(gA0 + (size_t)(32 * i) * K + ko);
-      ra[i + 4] = ld16(gA1 + (size_t)(32 * i) * K + ko);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rb[i] = (32 * i < bvalid) ? ld16(gB + (size_t)(32 * i) * K + ko) : zero;
-  };
-  auto sstore = [&](int buf) {
-    char* A = smem + buf * kTileStageBytes;
-    char* B = A + kTileStageBytes / 2;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int off = swz(rbase + 32 * i, kc);
-      *reinterpret_cast<uint4*>(A + off) = ra[i];
-      *reinterpret_cast<uint4*>(B + off) = rb[i];
-    }
-  };
-
-  // ---- wave's fragments: A rows (weights), B rows (tokens)
-  int arow[4];
+  if constexpr (GATEUP) {
+    // waves 0, 1 fill A rows 0..127 (gate), waves 2, 3 rows 128..255 (up)
+    const bf16_t* Wsrc = (wave < 2 ? W0 : W1) + ((size_t)e * N + f0) * K;
+    c.rA = make_rsrc(Wsrc, 128 * row_bytes);
+  } else {
+    c.rA = make_rsrc(W0 + ((size_t)e * N + f0) * K, 256 * row_bytes);
+  }
+  // token rows past the expert's count fall outside the resource: read as 0
+  const int nvalid = max(0, min(kTileBT, valid_end - row0));
+  c.rB = make_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    if constexpr (GATEUP) arow[a] = (a < 2 ? 0 : 128) + wf * 64 + (a & 1) * 32;
-    else arow[a] = wf * 128 + a * 32;
+    if constexpr (GATEUP) c.arow[a] = (a < 2 ? 0 : 128) + wf * 64 + (a & 1) * 32;
+    else c.arow[a] = wf * 128 + a * 32;
   }
+  c.brow = wt * 128;
   const int nbv = max(0, min(4, (valid_end - (row0 + wt * 128) + 31) / 32));
 
   f32x16 acc[4][4];
@@ -125,43 +300,19 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
 
-  auto compute = [&](int buf) {
-    const char* A = smem + buf * kTileStageBytes;
-    const char* B = A + kTileStageBytes / 2;
-    const int r32 = lane & 31, khalf = lane >> 5;
-#pragma unroll
-    for (int kk = 0; kk < kTileBK / 16; ++kk) {
-      const int chunk = kk * 2 + khalf;
-      uint4 af[4], bfr[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        af[a] = *reinterpret_cast<const uint4*>(A + swz(arow[a] + r32, chunk));
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (b < nbv) bfr[b] = *reinterpret_cast<const uint4*>(B + swz(wt * 128 + b * 32 + r32, chunk));
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        if (b < nbv) {
-#pragma unroll
-          for (int a = 0; a < 4; ++a) acc[a][b] = mfma32(af[a], bfr[b], acc[a][b]);
-        }
-    }
-  };
-
-  const int nk = K / kTileBK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1;
-    if (ks + 1 < nk) gload(ks + 1);
-    compute(cur);
-    if (ks + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+  // wave-uniform choice; every variant runs the same loads and barriers
+  const int nk = Kp / kTileBK;
+  switch (nbv) {
+    case 4: tile_main_loop<4>(c, bufs, nk, lane, acc); break;
+    case 3: tile_main_loop<3>(c, bufs, nk, lane, acc); break;
+    case 2: tile_main_loop<2>(c, bufs, nk, lane, acc); break;
+    case 1: tile_main_loop<1>(c, bufs, nk, lane, acc); break;
+    default: tile_main_loop<0>(c, bufs, nk, lane, acc); break;
   }
 
   // ---- epilogue.  D of a 32x32 MFMA: lane holds column n = lane % 32 and rows
-  // 8 * (j / 4) + 4 * (lane / 32) + j % 4, j = 0..15: four consecutive features.
+  // 8 * (j / 4) + 4 * (lane / 32) + j % 4, j = 0..15: four consecutive
+  // features.  Skipped fragments hold zeros (padding rows).
   const int r32 = lane & 31, half = lane >> 5;
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -184,7 +335,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
           *reinterpret_cast<uint2*>(h + feat) = make_uint2(p[0], p[1]);
         }
     } else {
-      float* y = reinterpret_cast<float*>(outp) + row * N;
+      float* y = reinterpret_cast<float*>(outp) + part * part_stride + row * N;
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -207,22 +358,35 @@ static void tile_launch(const Dims& D, const void* act, const void* W0, const vo
   const int FB = GATEUP ? kTileRows / 2 : kTileRows;
   const int n_ft = N / FB;
   const int n_tt = D.max_tiles;
-  const int total = n_ft * n_tt;
+  const int parts = GATEUP ? 1 : D.down_splits;
+  const int total = parts * n_ft * n_tt;
   const int per_xcd = (total + kXcds - 1) / kXcds;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tile_gemm_kernel<GATEUP>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, kTileLds);
-    attr_set = true;
-  }
-  tile_gemm_kernel<GATEUP><<<per_xcd * kXcds, kTileThreads, kTileLds, s>>>(
+  tile_gemm_kernel<GATEUP><<<per_xcd * kXcds, kTileThreads, 0, s>>>(
       (const bf16_t*)act, (const bf16_t*)W0, (const bf16_t*)W1, out, counts, offsets, num_tiles,
-      tile_expert, N, K, n_ft, n_tt, per_xcd);
+      tile_expert, N, K, n_ft, n_tt, per_xcd, parts, (size_t)D.max_rows * N);
 }
 
 bool tile_shape_ok(const Dims& D) {
+  // buffer offsets are 32-bit: 256 rows of either K must stay below 2 GiB
+  const int64_t kmax = D.d > D.f ? D.d : D.f;
   return D.bf16 && D.BT == kTileBT && D.f % (kTileRows / 2) == 0 && D.d % kTileRows == 0 &&
-         D.d % kTileBK == 0 && D.f % kTileBK == 0;
+         D.d % (kTileBK * kTileNS) == 0 && D.f % (kTileBK * kTileNS) == 0 &&
+         kTileRows * kmax * 2 < (int64_t(1) << 31);
+}
+
+// K-splits of the down GEMM: the expected tile count (ceil(rows / BT) plus
+// about half a tile of padding per expert) is spread over the CUs; a split
+// that fills the last round of workgroups markedly better is taken.
+int tile_down_splits(const Dims& D) {
+  constexpr int kCus = 256;
+  const int n_ft = D.d / kTileRows;
+  const double tiles = n_ft * ((double)D.T * D.k / kTileBT + D.E * 0.5);
+  auto fill = [&](int sp) {
+    const double t = tiles * sp;
+    return t / (std::ceil(t / kCus) * kCus);
+  };
+  const bool can2 = D.f % (2 * kTileBK * kTileNS) == 0;
+  return (can2 && fill(1) < 0.9 && fill(2) > fill(1) + 0.05) ? 2 : 1;
 }
 
 void launch_gateup_tile(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* h,

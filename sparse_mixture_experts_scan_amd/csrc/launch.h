@@ -13,6 +13,7 @@ struct Dims {
   int BT;              // token tile = padding unit of expert segments
   int max_rows;        // rows reserved for the permuted layout
   int max_tiles;       // max_rows / BT
+  int down_splits;     // K-splits of the down GEMM (partial Y blocks)
   bool bf16;           // element type of x / weights / out
 };
 
@@ -37,6 +38,7 @@ void launch_down_stream(const Dims& D, const void* h, const void* Wd, float* y,
 // a3 + a4: grouped GEMMs, LDS-tiled MFMA form (many rows per expert, bf16)
 constexpr int kTileTokens = 256;  // token tile of the tiled form (= padding unit)
 bool tile_shape_ok(const Dims& D);
+int tile_down_splits(const Dims& D);  // K-split count for the tiled down GEMM
 void launch_gateup_tile(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* h,
                         const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                         const int32_t* tile_expert, hipStream_t s);

@@ -67,11 +67,13 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
     variant = 0;
     D.BT = rows_avg <= 16 ? 16 : 32;
   }
+  D.down_splits = 1;
   int64_t max_rows = A + (int64_t)E * (D.BT - 1);
   max_rows = (max_rows + D.BT - 1) / D.BT * D.BT;
   if (max_rows > (int64_t(1) << 30)) return fail(MOE_ERR_UNSUPPORTED, "too many rows");
   D.max_rows = (int)max_rows;
   D.max_tiles = (int)(max_rows / D.BT);
+  if (variant == 1) D.down_splits = moe::tile_down_splits(D);
 
   moe_ws_layout_t& L = p->L;
   std::memset(&L, 0, sizeof(L));
@@ -79,6 +81,7 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   L.max_rows = D.max_rows;
   L.router_blocks = D.nblk;
   L.gemm_variant = variant;
+  L.down_splits = D.down_splits;
   const size_t es = D.bf16 ? 2 : 4;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -97,7 +100,7 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   L.tok_row = take(sizeof(int32_t) * A);
   L.xs = take(es * D.max_rows * d);
   L.h = take(es * D.max_rows * f);
-  L.y = take(sizeof(float) * D.max_rows * d);
+  L.y = take(sizeof(float) * D.down_splits * D.max_rows * d);
   L.total = off;
   return MOE_OK;
 }

@@ -17,7 +17,7 @@ namespace moe {
 // a1: router.  One block = kRouterTokens tokens (two 16-token MFMA columns) x
 // all E experts (16-expert MFMA rows, zero-padded).  Scores are an fp32 GEMM
 // on v_mfma_f32_16x16x4_f32: A = W_router^T (expert rows), B = x^T (token
-// columns, bf16 widened exactly), K = d_model split over the 4 waves in
+// columns, bf16 widened exactly), K = d_model split over 8 waves in
 // interleaved 16-element groups; wave partials are added in fixed order.
 // Top-k: one thread per token, k passes of an arg-max over E (strict '>' in
 // ascending expert order, so equal scores go to the lower index).
@@ -37,16 +37,20 @@ __device__ inline f32x4 load4_f32<bf16_t>(const bf16_t* p) {
                __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
 }
 
+constexpr int kRouterMfmaThreads = 512;  // 8 waves split K
+constexpr int kRouterUnroll = 4;         // k-groups whose loads are issued together
+
 template <typename T>
-__global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
+__global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
     int nT, int d, int E, int k, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
     int32_t* __restrict__ blk_counts) {
   constexpr int TB = kRouterTokens;
   constexpr int NB = TB / 16;            // token column blocks
   constexpr int MB = 64 / 16;            // expert row blocks (max)
-  constexpr int NWAVE = kRouterThreads / kWave;
-  __shared__ f32x4 red[NWAVE - 1][MB * NB][kWave];
+  constexpr int NWAVE = kRouterMfmaThreads / kWave;
+  constexpr int U = kRouterUnroll;
+  __shared__ f32x4 red[4][MB * NB][kWave];
   __shared__ float slog[TB][65];
   __shared__ int hist[64];
 
@@ -71,30 +75,57 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
     xp[b] = x + (size_t)(tok_ok[b] ? t : 0) * d + 4 * g;
   }
   const int ngroups = d / 16;
-  for (int kg = wave; kg < ngroups; kg += NWAVE) {
-    const int k0 = kg * 16 + 4 * g;       // this lane's 4 consecutive k
-    f32x4 bv[NB];
+  for (int kb = wave; kb < ngroups; kb += NWAVE * U) {
+    // U k-groups of 16: all loads first, then the MFMAs
+    f32x4 bv[U][NB];
+    f32x4 av[U][MB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-      bv[b] = tok_ok[b] ? load4_f32<T>(xp[b] + kg * 16) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < U; ++u) {
+      const int kg = kb + NWAVE * u;
+      const bool kok = kg < ngroups;
+      const int k0 = kg * 16 + 4 * g;     // this lane's 4 consecutive k
 #pragma unroll
-    for (int a = 0; a < MB; ++a) {
-      if (a < mb_used) {
+      for (int b = 0; b < NB; ++b)
+        bv[u][b] = (kok && tok_ok[b]) ? load4_f32<T>(xp[b] + kg * 16) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int a = 0; a < MB; ++a) {
         const int ex = a * 16 + m;
-        f32x4 av = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (ex < E) {
+        av[u][a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (kok && a < mb_used && ex < E) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) av[i] = Wr[(size_t)(k0 + i) * E + ex];
+          for (int i = 0; i < 4; ++i) av[u][a][i] = Wr[(size_t)(k0 + i) * E + ex];
         }
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[b][i], acc[a][b], 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int a = 0; a < MB; ++a)
+        if (a < mb_used) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][a][i], bv[u][b][i], acc[a][b], 0, 0, 0);
+        }
   }
-  if (wave > 0) {
+  // fixed-order reduction of the 8 wave partials: (w + w+4), then 0 + 1 + 2 + 3
+  static_assert(NWAVE == 8, "two-phase reduction assumes 8 waves");
+  if (wave >= 4) {
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) red[wave - 4][a * NB + b][lane] = acc[a][b];
+  }
+  __syncthreads();
+  if (wave < 4) {
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[a][b] += red[wave][a * NB + b][lane];
+  }
+  __syncthreads();
+  if (wave >= 1 && wave < 4) {
 #pragma unroll
     for (int a = 0; a < MB; ++a)
 #pragma unroll
@@ -109,7 +140,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
       for (int b = 0; b < NB; ++b) {
         f32x4 v = acc[a][b];
 #pragma unroll
-        for (int q = 0; q < NWAVE - 1; ++q) v += red[q][a * NB + b][lane];
+        for (int q = 0; q < 3; ++q) v += red[q][a * NB + b][lane];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ex = a * 16 + 4 * g + i;
@@ -298,12 +329,15 @@ __global__ __launch_bounds__(kRouterThreads) void scatter_gather_kernel(
 
 // ---------------------------------------------------------------------------
 // a5: out[t] = sum_j w[t][j] * Y[tok_row[t][j]], fp32 FMA in slot order,
-// one rounding to the output type.  A gather, so no atomics.
+// one rounding to the output type.  A gather, so no atomics.  When the down
+// GEMM was split along K, Y[r] is the sum of its partial blocks, added in
+// block order before the gate weight is applied.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ tok_row,
                                                       const float* __restrict__ w, int d, int k,
+                                                      int splits, size_t split_stride,
                                                       T* __restrict__ out) {
   const int t = blockIdx.x;
   __shared__ int s_row[MOE_MAX_TOPK];
@@ -316,7 +350,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int c = threadIdx.x; c < d / 4; c += 256) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
-      const float4 v = reinterpret_cast<const float4*>(y + (size_t)s_row[j] * d)[c];
+      float4 v = reinterpret_cast<const float4*>(y + (size_t)s_row[j] * d)[c];
+      for (int p = 1; p < splits; ++p) {   // partial K blocks, fixed order
+        const float4 q = reinterpret_cast<const float4*>(y + p * split_stride + (size_t)s_row[j] * d)[c];
+        v.x += q.x;
+        v.y += q.y;
+        v.z += q.z;
+        v.w += q.w;
+      }
       const float g = s_w[j];
       a.x = fmaf(g, v.x, a.x);
       a.y = fmaf(g, v.y, a.y);
@@ -335,10 +376,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
                    int32_t* idx, float* w, int32_t* blk_counts, hipStream_t s) {
   if (D.bf16)
-    router_topk_kernel<bf16_t><<<D.nblk, kRouterThreads, 0, s>>>(
+    router_topk_kernel<bf16_t><<<D.nblk, kRouterMfmaThreads, 0, s>>>(
         (const bf16_t*)x, Wr, bias, D.T, D.d, D.E, D.k, idx, w, blk_counts);
   else
-    router_topk_kernel<float><<<D.nblk, kRouterThreads, 0, s>>>(
+    router_topk_kernel<float><<<D.nblk, kRouterMfmaThreads, 0, s>>>(
         (const float*)x, Wr, bias, D.T, D.d, D.E, D.k, idx, w, blk_counts);
 }
 
@@ -370,10 +411,13 @@ void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int3
 
 void launch_combine(const Dims& D, const float* y, const int32_t* tok_row, const float* w,
                     void* out, hipStream_t s) {
+  const size_t stride = (size_t)D.max_rows * D.d;
   if (D.bf16)
-    combine_kernel<bf16_t><<<D.T, 256, 0, s>>>(y, tok_row, w, D.d, D.k, (bf16_t*)out);
+    combine_kernel<bf16_t><<<D.T, 256, 0, s>>>(y, tok_row, w, D.d, D.k, D.down_splits, stride,
+                                                (bf16_t*)out);
   else
-    combine_kernel<float><<<D.T, 256, 0, s>>>(y, tok_row, w, D.d, D.k, (float*)out);
+    combine_kernel<float><<<D.T, 256, 0, s>>>(y, tok_row, w, D.d, D.k, D.down_splits, stride,
+                                               (float*)out);
 }
 
 }  // namespace moe

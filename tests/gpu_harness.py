@@ -73,19 +73,26 @@ def run_gpu(cfg: MoEConfig, dinp: dict, *, device="cuda", keep_ws=True) -> dict:
 
 
 def ws_rows(res, cfg: MoEConfig, which: str, rows) -> np.ndarray:
-    """Rows of a workspace matrix (xs, h: element type; y: fp32) as float32."""
+    """Rows of a workspace matrix (xs, h: element type; y: fp32, the sum of
+    its K-split partial blocks) as float32 (float64 for y)."""
     lay = res["layout"]
     ws = res["_ws"]
     width = cfg.d_ff if which == "h" else cfg.d_model
     es = 4 if (which == "y" or cfg.dtype == "f32") else 2
     off = getattr(lay, which)
+    parts = lay.down_splits if which == "y" else 1
     out = []
     for r in rows:
-        b = ws[off + r * width * es: off + (r + 1) * width * es]
-        if es == 2:
-            out.append(as_f32(b.view(torch.int16).cpu().numpy().view(np.uint16)))
-        else:
-            out.append(b.view(torch.float32).cpu().numpy())
+        acc = None
+        for p in range(parts):
+            base = off + p * lay.max_rows * width * es
+            b = ws[base + r * width * es: base + (r + 1) * width * es]
+            if es == 2:
+                v = as_f32(b.view(torch.int16).cpu().numpy().view(np.uint16))
+            else:
+                v = b.view(torch.float32).cpu().numpy()
+            acc = v.astype(np.float64) if acc is None else acc + v
+        out.append(acc if which == "y" else acc.astype(np.float32))
     return np.array(out)
 
 

@@ -104,12 +104,17 @@ def test_workspace_layout_is_consistent():
                   ("offsets", 4 * (E + 1)), ("num_tiles", 4),
                   ("tile_expert", 4 * lay.max_rows // BT), ("row_token", 4 * lay.max_rows),
                   ("tok_row", 4 * T * k), ("xs", es * lay.max_rows * d),
-                  ("h", es * lay.max_rows * f), ("y", 4 * lay.max_rows * d)]
+                  ("h", es * lay.max_rows * f), ("y", 4 * lay.down_splits * lay.max_rows * d)]
         spans = sorted((getattr(lay, n), getattr(lay, n) + size) for n, size in fields)
         for (a0, a1), (b0, _) in zip(spans, spans[1:]):
             assert a1 <= b0                      # no overlap
         assert all(s % 256 == 0 for s, _ in spans)
         assert spans[-1][1] <= lay.total
+    # the tiled down GEMM of the Mixtral prefill shape is split along K (its
+    # 576 tiles fill 256 CUs badly), the fine-grained shape's is not
+    assert moe.moe_ffn_workspace_layout(4096, 4096, 14336, 8, 2, 0).down_splits == 2
+    assert moe.moe_ffn_workspace_layout(4096, 4096, 3584, 64, 8, 0).down_splits == 1
+    assert moe.moe_ffn_workspace_layout(16, 4096, 14336, 8, 2, 0).down_splits == 1
     with pytest.raises(moe.MoeError):
         moe.moe_ffn_workspace_layout(16, 100, 512, 8, 2, 0)
     assert moe.moe_ffn_workspace_size(16, 100, 512, 8, 2, 0) == 0

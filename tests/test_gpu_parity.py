@@ -67,15 +67,17 @@ SMALL = [
     MoEConfig("tile_small", 1000, 256, 384, 8, 2, "bf16"),
     MoEConfig("tile_ragged", 777, 512, 256, 4, 1, "bf16"),
     MoEConfig("tile_fine", 900, 256, 128, 16, 4, "bf16"),
+    MoEConfig("tile_split", 800, 1024, 512, 8, 2, "bf16"),   # down GEMM split along K
 ]
 
-TILED = {"tile_small", "tile_ragged", "tile_fine"}
+TILED = {"tile_small", "tile_ragged", "tile_fine", "tile_split"}
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_small_shapes(cfg):
     res, _ = full_check(cfg, seed=1)
     assert res["layout"].gemm_variant == (1 if cfg.name in TILED else 0)
+    assert res["layout"].down_splits == (2 if cfg.name == "tile_split" else 1)
 
 
 def test_all_tokens_to_one_expert():
