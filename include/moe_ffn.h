@@ -137,6 +137,8 @@ typedef struct moe_ws_layout {
   size_t h;                 /* [max_rows][d_ff] dtype: SiLU(gate) * up         */
   size_t y;                 /* [down_splits][max_rows][d_model] float32:
                                partial expert outputs (their sum is W2 H)       */
+  size_t router_partial;    /* router scratch: partial scores when the score GEMM
+                               is split over d_model (few token blocks)        */
   size_t total;             /* bytes                                           */
 } moe_ws_layout_t;
 

@@ -43,7 +43,7 @@ class MoeWsLayout(ctypes.Structure):
                 ("down_splits", ctypes.c_int32)] + [
         (name, ctypes.c_size_t) for name in
         ("topk_idx", "topk_w", "block_counts", "counts", "offsets", "num_tiles",
-         "tile_expert", "row_token", "tok_row", "xs", "h", "y", "total")]
+         "tile_expert", "row_token", "tok_row", "xs", "h", "y", "router_partial", "total")]
 
 
 class MoeError(RuntimeError):

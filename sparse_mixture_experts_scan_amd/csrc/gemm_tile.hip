@@ -5,22 +5,27 @@
 // Gate/up: H[r][f] = SiLU(sum_c W_gate[e][f][c] Xs[r][c]) * sum_c W_up[e][f][c] Xs[r][c]
 // Down:    Y[r][o] = sum_f W_down[e][o][f] H[r][f]   (fp32 out)
 //
-// Tile: 256 weight rows x 256 token rows per workgroup, K staged 64 at a time
-// through double-buffered LDS (2 x 64 KiB), 4 waves as 2 (weights) x 2
-// (tokens), each wave 128 x 128 outputs in sixteen 32x32 fp32 accumulators
-// fed by v_mfma_f32_32x32x16_bf16 (A = weight rows, B = token rows, both
+// Tile: 256 weight rows x 256 token rows per workgroup of 8 waves (two per
+// SIMD, so one wave's MFMAs cover the other's LDS and barrier stalls), each
+// wave 128 weight rows x 64 token rows in eight 32x32 fp32 accumulators fed
+// by v_mfma_f32_32x32x16_bf16 (A = weight rows, B = token rows, both
 // K-contiguous).  For gate/up the 256 weight rows are 128 gate rows and the
 // same 128 up rows, and each wave holds gate and up accumulators of the same
 // features, so SiLU(gate) * up is applied in registers and only H is stored.
 //
-// LDS rows are 128 bytes (64 bf16); the eight 16-byte chunks of row r are
-// XOR-swizzled by (r ^ r >> 3) & 7 so that the 32 rows one MFMA fragment
-// reads, and the rows a wave writes, fall in distinct banks.
+// K is staged 64 at a time through a ring of LDS stage buffers filled by
+// gfx950 buffer loads straight to LDS (no VGPR staging): each lane fetches the
+// 16 bytes that belong at its slot of the XOR-swizzled layout, the next stage
+// is issued right after the barrier that opens the current one, and each
+// wave waits for its own loads before that barrier.  LDS rows are 128 bytes;
+// chunk c of row r sits at c ^ ((r ^ r >> 3) & 7), so the 32 rows an MFMA
+// fragment reads fall in distinct banks (no bank conflicts measured).
 //
-// Token rows past the expert's count read as zero; 32-row token fragments
-// that are entirely past it skip their MFMAs.  Work-group ids are remapped
-// so that consecutive tiles (same expert, neighbouring feature tiles) land on
-// the same XCD and share its L2.
+// Token rows past the expert's count lie outside the token operand's buffer
+// range, so the hardware loads zeros; 32-row token fragments entirely past it
+// skip their MFMAs.  Work-group ids are remapped so that the tiles an XCD
+// runs together share weight and token panels in its L2.
+
 #include <cmath>
 
 #include "common.h"
@@ -28,7 +33,13 @@
 
 namespace moe {
 
-constexpr int kTileThreads = 256;
+#ifndef MOE_TILE_WAVES
+#define MOE_TILE_WAVES 8
+#endif
+constexpr int kTileWaves = MOE_TILE_WAVES;          // 4 (1 per SIMD) or 8 (2 per SIMD)
+constexpr int kTileThreads = 64 * kTileWaves;
+constexpr int kWaveTok = 256 / (kTileWaves / 2);    // token rows per wave (128 or 64)
+constexpr int kBFrags = kWaveTok / 32;              // 32-row token fragments per wave
 constexpr int kTileBT = kTileTokens;  // token rows per tile (= padding unit)
 constexpr int kTileRows = 256;        // weight rows per tile
 #ifndef MOE_TILE_BK
@@ -41,7 +52,7 @@ constexpr int kTileBK = MOE_TILE_BK;  // K per LDS stage
 constexpr int kTileNS = MOE_TILE_NS;  // LDS ring depth (stages)
 constexpr int kXcds = 8;
 #ifndef MOE_TILE_FEAT_GROUP
-#define MOE_TILE_FEAT_GROUP 8
+#define MOE_TILE_FEAT_GROUP 4
 #endif
 constexpr int kFeatGroup = MOE_TILE_FEAT_GROUP;  // feature tiles per XCD-local group
 
@@ -49,7 +60,7 @@ constexpr int kRowBytes = kTileBK * 2;              // LDS bytes per tile row
 constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per row
 constexpr int kOperBytes = 256 * kRowBytes;         // one operand tile in LDS
 constexpr int kStageBytes = 2 * kOperBytes;         // A + B
-constexpr int kDmaPerWave = 256 * kChunks / 64 / 4; // 1 KiB DMA loads per wave per operand
+constexpr int kDmaPerWave = 256 * kChunks / 64 / kTileWaves;  // 1 KiB DMA loads per wave per operand
 constexpr int kKSteps = kTileBK / 16;               // 32x32x16 MFMA k-steps per stage
 static_assert(kTileBK == 32 || kTileBK == 64, "stage K must be 32 or 64");
 static_assert(kTileNS >= 2 && kTileNS <= 4, "ring depth 2..4");
@@ -121,7 +132,7 @@ __device__ __forceinline__ void tile_issue(const TileCtx& c, char* buf, int ks) 
 
 template <int NBV>
 __device__ __forceinline__ void tile_frags(const TileCtx& c, const char* buf, int kk, int lane,
-                                           uint4 (&af)[4], uint4 (&bf)[4]) {
+                                           uint4 (&af)[4], uint4 (&bf)[kBFrags]) {
   const char* A = buf;
   const char* B = buf + kOperBytes;
   const int r32 = lane & 31, chunk = kk * 2 + (lane >> 5);
@@ -136,10 +147,28 @@ __device__ __forceinline__ void tile_frags(const TileCtx& c, const char* buf, in
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
+#ifndef MOE_TILE_PRELOAD
+#define MOE_TILE_PRELOAD 0
+#endif
+
 template <int NBV>
 __device__ __forceinline__ void tile_compute(const TileCtx& c, const char* buf, int lane,
-                                             f32x16 (&acc)[4][4]) {
-  uint4 af[4], bf[4], na[4], nb[4];
+                                             f32x16 (&acc)[4][kBFrags]) {
+#if MOE_TILE_PRELOAD
+  // all of the stage's fragments first (LDS returns in order, so each
+  // k-step's MFMAs wait only for their own reads), then the MFMAs
+  uint4 fa[kKSteps][4], fb[kKSteps][kBFrags];
+#pragma unroll
+  for (int kk = 0; kk < kKSteps; ++kk) tile_frags<NBV>(c, buf, kk, lane, fa[kk], fb[kk]);
+#pragma unroll
+  for (int kk = 0; kk < kKSteps; ++kk)
+#pragma unroll
+    for (int b = 0; b < NBV; ++b)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) acc[a][b] = mfma32(fa[kk][a], fb[kk][b], acc[a][b]);
+  return;
+#endif
+  uint4 af[4], bf[kBFrags], na[4], nb[kBFrags];
   tile_frags<NBV>(c, buf, 0, lane, af, bf);
 #pragma unroll
   for (int kk = 0; kk < kKSteps; ++kk) {
@@ -165,7 +194,7 @@ __device__ __forceinline__ void tile_compute(const TileCtx& c, const char* buf, 
 #pragma unroll
       for (int a = 0; a < 4; ++a) af[a] = na[a];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bf[b] = nb[b];
+      for (int b = 0; b < kBFrags; ++b) bf[b] = nb[b];
     }
   }
 }
@@ -187,7 +216,7 @@ __device__ __forceinline__ void wait_stage(int n_after) {
 // outer loop runs all kTileNS stages: no early exit inside the unrolled body.
 template <int NBV>
 __device__ __forceinline__ void tile_main_loop(const TileCtx& c, char* const (&bufs)[kTileNS],
-                                               int nk, int lane, f32x16 (&acc)[4][4]) {
+                                               int nk, int lane, f32x16 (&acc)[4][kBFrags]) {
 #pragma unroll
   for (int s = 0; s < kTileNS - 1; ++s) tile_issue(c, bufs[s], s);
   for (int ks0 = 0; ks0 < nk; ks0 += kTileNS) {
@@ -209,8 +238,14 @@ __device__ __forceinline__ void tile_main_loop(const TileCtx& c, char* const (&b
   }
 }
 
+#ifdef MOE_TILE_WPE
+#define MOE_TILE_WPE_ATTR __attribute__((amdgpu_waves_per_eu(MOE_TILE_WPE, MOE_TILE_WPE)))
+#else
+#define MOE_TILE_WPE_ATTR
+#endif
+
 template <bool GATEUP>
-__global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
+__global__ __launch_bounds__(kTileThreads, 1) MOE_TILE_WPE_ATTR void tile_gemm_kernel(
     const bf16_t* __restrict__ act, const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
     void* __restrict__ outp, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ num_tiles,
@@ -255,7 +290,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wf = wave & 1, wt = wave >> 1;
+  const int wf = wave & 1, wt = wave >> 1;   // weight half, token slice
 
   // ---- DMA assignment: wave w fills LDS slots [w * kDmaPerWave, +kDmaPerWave)
   // of each operand (1 KiB each); slot q's lane i holds LDS chunk position
@@ -275,8 +310,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
     c.voffB[j] = (uint32_t)r * row_bytes + cg * 16;
   }
   if constexpr (GATEUP) {
-    // waves 0, 1 fill A rows 0..127 (gate), waves 2, 3 rows 128..255 (up)
-    const bf16_t* Wsrc = (wave < 2 ? W0 : W1) + ((size_t)e * N + f0) * K;
+    // the first half of the waves fills A rows 0..127 (gate), the second
+    // half rows 128..255 (up)
+    const bf16_t* Wsrc = (wave < kTileWaves / 2 ? W0 : W1) + ((size_t)e * N + f0) * K;
     c.rA = make_rsrc(Wsrc, 128 * row_bytes);
   } else {
     c.rA = make_rsrc(W0 + ((size_t)e * N + f0) * K, 256 * row_bytes);
@@ -289,22 +325,24 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
     if constexpr (GATEUP) c.arow[a] = (a < 2 ? 0 : 128) + wf * 64 + (a & 1) * 32;
     else c.arow[a] = wf * 128 + a * 32;
   }
-  c.brow = wt * 128;
-  const int nbv = max(0, min(4, (valid_end - (row0 + wt * 128) + 31) / 32));
+  c.brow = wt * kWaveTok;
+  const int nbv = max(0, min(kBFrags, (valid_end - (row0 + wt * kWaveTok) + 31) / 32));
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][kBFrags];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < kBFrags; ++b)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
 
   // wave-uniform choice; every variant runs the same loads and barriers
   const int nk = Kp / kTileBK;
   switch (nbv) {
+#if MOE_TILE_WAVES == 4
     case 4: tile_main_loop<4>(c, bufs, nk, lane, acc); break;
     case 3: tile_main_loop<3>(c, bufs, nk, lane, acc); break;
+#endif
     case 2: tile_main_loop<2>(c, bufs, nk, lane, acc); break;
     case 1: tile_main_loop<1>(c, bufs, nk, lane, acc); break;
     default: tile_main_loop<0>(c, bufs, nk, lane, acc); break;
@@ -315,8 +353,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
   // features.  Skipped fragments hold zeros (padding rows).
   const int r32 = lane & 31, half = lane >> 5;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const size_t row = (size_t)(row0 + wt * 128 + b * 32 + r32);
+  for (int b = 0; b < kBFrags; ++b) {
+    const size_t row = (size_t)(row0 + wt * kWaveTok + b * 32 + r32);
     if constexpr (GATEUP) {
       bf16_t* h = reinterpret_cast<bf16_t*>(outp) + row * N;
 #pragma unroll

@@ -14,12 +14,15 @@ struct Dims {
   int max_rows;        // rows reserved for the permuted layout
   int max_tiles;       // max_rows / BT
   int down_splits;     // K-splits of the down GEMM (partial Y blocks)
+  int router_splits;   // d_model splits of the router scores (1 = fused kernel)
   bool bf16;           // element type of x / weights / out
 };
 
 // a1: scores, top-k, softmax over the k, per-block expert histogram
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
-                   int32_t* idx, float* w, int32_t* blk_counts, hipStream_t s);
+                   int32_t* idx, float* w, int32_t* blk_counts, float* part, hipStream_t s);
+int router_splits_for(int nblk, int d);
+constexpr int kRouterPartStride = 64;  // floats per token row of the partial scores
 // a2: histogram reduce, padded offsets, per-block bases, tile table
 void launch_scan(const Dims& D, int32_t* blk_counts, int32_t* counts, int32_t* offsets,
                  int32_t* num_tiles, int32_t* tile_expert, int32_t* row_token,

@@ -57,6 +57,7 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   D.Epow2 = 1;
   while (D.Epow2 < E) D.Epow2 *= 2;
   D.nblk = (D.T + moe::kRouterTokens - 1) / moe::kRouterTokens;
+  D.router_splits = moe::router_splits_for(D.nblk, D.d);
   const int64_t A = T * k;                       // (token, slot) assignments
   const int64_t rows_avg = (A + E - 1) / E;
   // GEMM form: weight-streaming for few rows per expert (weights read once,
@@ -101,6 +102,9 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   L.xs = take(es * D.max_rows * d);
   L.h = take(es * D.max_rows * f);
   L.y = take(sizeof(float) * D.down_splits * D.max_rows * d);
+  L.router_partial = take(D.router_splits > 1 ? sizeof(float) * D.router_splits * D.nblk *
+                                                    moe::kRouterTokens * moe::kRouterPartStride
+                                              : 0);
   L.total = off;
   return MOE_OK;
 }
@@ -209,6 +213,7 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, co
   void* xs = ws + L.xs;
   void* h = ws + L.h;
   float* y = reinterpret_cast<float*>(ws + L.y);
+  float* rpart = reinterpret_cast<float*>(ws + L.router_partial);
 
   hipError_t e;
   auto mark = [&](int i) -> hipError_t {
@@ -216,7 +221,7 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, co
                           : hipSuccess;
   };
   if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  moe::launch_router(D, x, W_router, o.router_bias, idx, w, blk, s);
+  moe::launch_router(D, x, W_router, o.router_bias, idx, w, blk, rpart, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess)
     return hip_fail(e, "router launch");
   moe::launch_scan(D, blk, counts, offsets, num_tiles, tile_expert, row_token,

@@ -40,11 +40,60 @@ __device__ inline f32x4 load4_f32<bf16_t>(const bf16_t* p) {
 constexpr int kRouterMfmaThreads = 512;  // 8 waves split K
 constexpr int kRouterUnroll = 4;         // k-groups whose loads are issued together
 
+
+// Top-k of one token's E scores (k passes of an arg-max, strict '>' in
+// ascending expert order: equal scores go to the lower index), then the
+// softmax over the selected k shifted by the largest.  Counts the choices in
+// the block histogram.
+__device__ inline void select_topk_token(const float* srow, int E, int k, size_t t,
+                                         int32_t* __restrict__ idx_out,
+                                         float* __restrict__ w_out, int* hist) {
+  uint64_t taken = 0;
+  float sel[MOE_MAX_TOPK];
+  int sid[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    if (j < k) {
+      float best = 0.f;
+      int bi = -1;
+      for (int e = 0; e < E; ++e) {
+        const float v = srow[e];
+        if (!((taken >> e) & 1ull) && (bi < 0 || v > best)) {
+          best = v;
+          bi = e;
+        }
+      }
+      taken |= 1ull << bi;
+      sel[j] = best;
+      sid[j] = bi;
+    }
+  }
+  float z[MOE_MAX_TOPK];
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j)
+    if (j < k) {
+      z[j] = expf(sel[j] - sel[0]);
+      sum += z[j];
+    }
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j)
+    if (j < k) {
+      idx_out[t * k + j] = sid[j];
+      w_out[t * k + j] = z[j] / sum;
+      atomicAdd(&hist[sid[j]], 1);
+    }
+}
+
+// Scores of kRouterTokens tokens over the d_model range of split blockIdx.y
+// (all of d_model when splits == 1).  splits == 1: adds the bias, selects
+// and writes the routing; splits > 1: writes the partial scores to `part`
+// ([split][token][kRouterPartStride]) for router_select_kernel.
 template <typename T>
 __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
-    int nT, int d, int E, int k, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-    int32_t* __restrict__ blk_counts) {
+    int nT, int d, int E, int k, int splits, float* __restrict__ part,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ blk_counts) {
   constexpr int TB = kRouterTokens;
   constexpr int NB = TB / 16;            // token column blocks
   constexpr int MB = 64 / 16;            // expert row blocks (max)
@@ -54,7 +103,8 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
   __shared__ float slog[TB][65];
   __shared__ int hist[64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * TB;
   const int mb_used = (E + 15) / 16;
   const int m = lane & 15, g = lane >> 4;
@@ -74,15 +124,17 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
     tok_ok[b] = t < nT;
     xp[b] = x + (size_t)(tok_ok[b] ? t : 0) * d + 4 * g;
   }
-  const int ngroups = d / 16;
-  for (int kb = wave; kb < ngroups; kb += NWAVE * U) {
+  const int ngroups = d / 16;                      // 16-element k-groups
+  const int gps = ngroups / splits;                // k-groups of this split
+  const int g0 = blockIdx.y * gps, g1 = g0 + gps;
+  for (int kb = g0 + wave; kb < g1; kb += NWAVE * U) {
     // U k-groups of 16: all loads first, then the MFMAs
     f32x4 bv[U][NB];
     f32x4 av[U][MB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int kg = kb + NWAVE * u;
-      const bool kok = kg < ngroups;
+      const bool kok = kg < g1;
       const int k0 = kg * 16 + 4 * g;     // this lane's 4 consecutive k
 #pragma unroll
       for (int b = 0; b < NB; ++b)
@@ -144,52 +196,46 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ex = a * 16 + 4 * g + i;
-          if (ex < E) slog[b * 16 + m][ex] = v[i] + (bias ? bias[ex] : 0.f);
+          if (ex < E) {
+            if (splits > 1)
+              part[((size_t)blockIdx.y * gridDim.x * TB + t0 + b * 16 + m) * kRouterPartStride + ex] = v[i];
+            else
+              slog[b * 16 + m][ex] = v[i] + (bias ? bias[ex] : 0.f);
+          }
         }
       }
+  }
+  if (splits > 1) return;
+  __syncthreads();
+  if (tid < TB && t0 + tid < nT)
+    select_topk_token(slog[tid], E, k, (size_t)(t0 + tid), idx_out, w_out, hist);
+  __syncthreads();
+  if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = hist[tid];
+}
+
+// Second pass of a split router: per token, the split partial scores are
+// added in split order (deterministic), the bias added, then top-k/softmax.
+__global__ __launch_bounds__(kRouterTokens * 2) void router_select_kernel(
+    const float* __restrict__ part, const float* __restrict__ bias, int nT, int E, int k,
+    int splits, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+    int32_t* __restrict__ blk_counts) {
+  constexpr int TB = kRouterTokens;
+  __shared__ float slog[TB][65];
+  __shared__ int hist[64];
+  const int tid = threadIdx.x;
+  const int t0 = blockIdx.x * TB;
+  if (tid < 64) hist[tid] = 0;
+  const size_t split_stride = (size_t)gridDim.x * TB * kRouterPartStride;
+  for (int i = tid; i < TB * E; i += blockDim.x) {
+    const int tt = i / E, e = i % E;
+    const size_t o = (size_t)(t0 + tt) * kRouterPartStride + e;
+    float v = part[o];
+    for (int sp = 1; sp < splits; ++sp) v += part[sp * split_stride + o];
+    slog[tt][e] = v + (bias ? bias[e] : 0.f);
   }
   __syncthreads();
-
-  if (tid < TB) {
-    const int t = t0 + tid;
-    if (t < nT) {
-      uint64_t taken = 0;
-      float sel[MOE_MAX_TOPK];
-      int sid[MOE_MAX_TOPK];
-#pragma unroll
-      for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-        if (j < k) {
-          float best = 0.f;
-          int bi = -1;
-          for (int e = 0; e < E; ++e) {
-            const float v = slog[tid][e];
-            if (!((taken >> e) & 1ull) && (bi < 0 || v > best)) {
-              best = v;
-              bi = e;
-            }
-          }
-          taken |= 1ull << bi;
-          sel[j] = best;
-          sid[j] = bi;
-        }
-      }
-      float z[MOE_MAX_TOPK];
-      float sum = 0.f;
-#pragma unroll
-      for (int j = 0; j < MOE_MAX_TOPK; ++j)
-        if (j < k) {
-          z[j] = expf(sel[j] - sel[0]);
-          sum += z[j];
-        }
-#pragma unroll
-      for (int j = 0; j < MOE_MAX_TOPK; ++j)
-        if (j < k) {
-          idx_out[(size_t)t * k + j] = sid[j];
-          w_out[(size_t)t * k + j] = z[j] / sum;
-          atomicAdd(&hist[sid[j]], 1);
-        }
-    }
-  }
+  if (tid < TB && t0 + tid < nT)
+    select_topk_token(slog[tid], E, k, (size_t)(t0 + tid), idx_out, w_out, hist);
   __syncthreads();
   if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = hist[tid];
 }
@@ -374,13 +420,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 // ---------------------------------------------------------------------------
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
-                   int32_t* idx, float* w, int32_t* blk_counts, hipStream_t s) {
+                   int32_t* idx, float* w, int32_t* blk_counts, float* part, hipStream_t s) {
+  const dim3 grid(D.nblk, D.router_splits);
   if (D.bf16)
-    router_topk_kernel<bf16_t><<<D.nblk, kRouterMfmaThreads, 0, s>>>(
-        (const bf16_t*)x, Wr, bias, D.T, D.d, D.E, D.k, idx, w, blk_counts);
+    router_topk_kernel<bf16_t><<<grid, kRouterMfmaThreads, 0, s>>>(
+        (const bf16_t*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts);
   else
-    router_topk_kernel<float><<<D.nblk, kRouterMfmaThreads, 0, s>>>(
-        (const float*)x, Wr, bias, D.T, D.d, D.E, D.k, idx, w, blk_counts);
+    router_topk_kernel<float><<<grid, kRouterMfmaThreads, 0, s>>>(
+        (const float*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts);
+  if (D.router_splits > 1)
+    router_select_kernel<<<D.nblk, kRouterTokens * 2, 0, s>>>(part, bias, D.T, D.E, D.k,
+                                                              D.router_splits, idx, w, blk_counts);
+}
+
+int router_splits_for(int nblk, int d) {
+  // split d_model over blocks until about 128 blocks run; each split keeps
+  // a whole number of 16-element k-groups
+  const int groups = d / 16;
+  int sp = 1;
+  while (nblk * sp < 128 && sp * 2 <= 16 && groups % (sp * 2) == 0) sp *= 2;
+  return sp;
 }
 
 void launch_scan(const Dims& D, int32_t* blk_counts, int32_t* counts, int32_t* offsets,

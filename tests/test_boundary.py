@@ -105,6 +105,8 @@ def test_workspace_layout_is_consistent():
                   ("tile_expert", 4 * lay.max_rows // BT), ("row_token", 4 * lay.max_rows),
                   ("tok_row", 4 * T * k), ("xs", es * lay.max_rows * d),
                   ("h", es * lay.max_rows * f), ("y", 4 * lay.down_splits * lay.max_rows * d)]
+        assert lay.router_partial >= lay.y + 4 * lay.down_splits * lay.max_rows * d
+        assert lay.router_partial <= lay.total
         spans = sorted((getattr(lay, n), getattr(lay, n) + size) for n, size in fields)
         for (a0, a1), (b0, _) in zip(spans, spans[1:]):
             assert a1 <= b0                      # no overlap
