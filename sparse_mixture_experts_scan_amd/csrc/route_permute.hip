@@ -215,7 +215,10 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
 
 // Second pass of a split router: per token, the split partial scores are
 // added in split order (deterministic), the bias added, then top-k/softmax.
-__global__ __launch_bounds__(kRouterTokens * 2) void router_select_kernel(
+constexpr int kSelectThreads = 256;
+constexpr int kMaxRouterSplits = 16;
+
+__global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int nT, int E, int k,
     int splits, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
     int32_t* __restrict__ blk_counts) {
@@ -226,11 +229,17 @@ __global__ __launch_bounds__(kRouterTokens * 2) void router_select_kernel(
   const int t0 = blockIdx.x * TB;
   if (tid < 64) hist[tid] = 0;
   const size_t split_stride = (size_t)gridDim.x * TB * kRouterPartStride;
-  for (int i = tid; i < TB * E; i += blockDim.x) {
+  for (int i = tid; i < TB * E; i += kSelectThreads) {
     const int tt = i / E, e = i % E;
     const size_t o = (size_t)(t0 + tt) * kRouterPartStride + e;
-    float v = part[o];
-    for (int sp = 1; sp < splits; ++sp) v += part[sp * split_stride + o];
+    float p[kMaxRouterSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMaxRouterSplits; ++sp)   // all loads in flight together
+      p[sp] = sp < splits ? part[sp * split_stride + o] : 0.f;
+    float v = p[0];
+#pragma unroll
+    for (int sp = 1; sp < kMaxRouterSplits; ++sp)   // added in split order
+      if (sp < splits) v += p[sp];
     slog[tt][e] = v + (bias ? bias[e] : 0.f);
   }
   __syncthreads();
@@ -429,7 +438,7 @@ void launch_router(const Dims& D, const void* x, const float* Wr, const float* b
     router_topk_kernel<float><<<grid, kRouterMfmaThreads, 0, s>>>(
         (const float*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts);
   if (D.router_splits > 1)
-    router_select_kernel<<<D.nblk, kRouterTokens * 2, 0, s>>>(part, bias, D.T, D.E, D.k,
+    router_select_kernel<<<D.nblk, kSelectThreads, 0, s>>>(part, bias, D.T, D.E, D.k,
                                                               D.router_splits, idx, w, blk_counts);
 }
 
@@ -438,7 +447,7 @@ int router_splits_for(int nblk, int d) {
   // a whole number of 16-element k-groups
   const int groups = d / 16;
   int sp = 1;
-  while (nblk * sp < 128 && sp * 2 <= 16 && groups % (sp * 2) == 0) sp *= 2;
+  while (nblk * sp < 128 && sp * 2 <= kMaxRouterSplits && groups % (sp * 2) == 0) sp *= 2;
   return sp;
 }
 

@@ -1,0 +1,157 @@
+"""Summaries of rocprofv3 output for the MoE layer's kernels.
+
+    python -m sparse_mixture_experts_scan_amd.prof_summary \\
+        --workload decode --kt <dir> --fetch <dir> --write <dir> \\
+        --command-kt "<cmd>" --command-pmc "<cmd>" --out profiles/<name>.md
+
+<dir> are rocprofv3 ``-d`` output directories (``--output-format csv``):
+``--kt`` from ``--kernel-trace --stats``, ``--fetch``/``--write`` from
+``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of ``bench.py
+--copy-calibration-mib N``.  That option runs, before the timed steps, a
+plain elementwise kernel that reads N MiB and writes N MiB; what the two
+counters read for it gives the scale factor from counter units to bytes,
+applied to every other kernel.  The per-kernel traffic is also merged into
+``profiles/traffic.json`` keyed by workload and kernel, with the SHA-256 of
+the kernel's source files, so a reader can tell when the numbers no longer
+describe the code."""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+KERNEL_SOURCES = {
+    "gateup": {"stream": ["gemm_stream.hip", "common.h"], "tile": ["gemm_tile.hip", "common.h"]},
+    "down": {"stream": ["gemm_stream.hip", "common.h"], "tile": ["gemm_tile.hip", "common.h"]},
+}
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def kernel_key(name: str) -> str:
+    """Short role of a kernel from its demangled name."""
+    if "stream_gemm_kernel" in name:
+        return "gateup" if ", true," in name else "down"
+    if "tile_gemm_kernel" in name:
+        return "gateup" if "<true>" in name else "down"
+    for k in ("router_topk", "router_select", "expert_scan", "scatter_gather", "combine"):
+        if k in name:
+            return k
+    if "elementwise" in name:
+        return "elementwise"
+    if "copyBuffer" in name:
+        return "copyBuffer"
+    return name[:40]
+
+
+def read_counter(d: str):
+    """{kernel_key: [value per dispatch]} and the dispatches' kernel names."""
+    path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+    per = defaultdict(lambda: defaultdict(float))
+    names = {}
+    for r in csv.DictReader(open(path)):
+        key = kernel_key(r["Kernel_Name"])
+        per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        names[key] = r["Kernel_Name"]
+    return {k: list(v.values()) for k, v in per.items()}, names
+
+
+def calibration(values, cal_mib: int, kind: str) -> float:
+    """Bytes per counter unit from the reference elementwise kernel.  Its
+    dispatches are: torch.zeros of the count buffer (tiny), torch.ones of the
+    N MiB source (writes N MiB), and the add (reads N MiB, writes N MiB)."""
+    ref = sorted(values["elementwise"])
+    known = cal_mib << 20
+    if kind == "fetch":
+        return known / ref[-1]                    # only the add reads N MiB
+    return 2 * known / sum(ref)                    # ones + add write 2 N MiB
+
+
+def read_stats(d: str):
+    path = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)[0]
+    return list(csv.DictReader(open(path)))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", required=True)
+    ap.add_argument("--variant", choices=("stream", "tile"), required=True)
+    ap.add_argument("--kt", required=True)
+    ap.add_argument("--fetch", required=True)
+    ap.add_argument("--write", required=True)
+    ap.add_argument("--cal-mib", type=int, default=512)
+    ap.add_argument("--command-kt", required=True)
+    ap.add_argument("--command-pmc", required=True)
+    ap.add_argument("--algorithmic", default="{}",
+                    help="JSON {kernel: algorithmic bytes per launch} for the table")
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--traffic-json", default=os.path.join(os.path.dirname(PKG), "profiles",
+                                                           "traffic.json"))
+    a = ap.parse_args()
+
+    stats = read_stats(a.kt)
+    fetch, names = read_counter(a.fetch)
+    write, _ = read_counter(a.write)
+    cf = calibration(fetch, a.cal_mib, "fetch")
+    cw = calibration(write, a.cal_mib, "write")
+    alg = json.loads(a.algorithmic)
+
+    lines = [f"# rocprofv3 summary: MoE layer, workload `{a.workload}`", "",
+             "Kernel trace (`--kernel-trace --stats`):", "", "```", a.command_kt, "```", "",
+             "| kernel | calls | avg us | min us | max us | share % |",
+             "|---|---|---|---|---|---|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
+                     f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    lines += ["", "HBM traffic per launch (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, "
+              "one run each):", "", "```", a.command_pmc.replace("<COUNTER>", "FETCH_SIZE"),
+              a.command_pmc.replace("<COUNTER>", "WRITE_SIZE"), "```", "",
+              f"Scale from counter units to bytes, from the reference elementwise kernel "
+              f"that reads {a.cal_mib} MiB and writes {a.cal_mib} MiB: FETCH_SIZE x {cf:.4g} "
+              f"B/unit, WRITE_SIZE x {cw:.4g} B/unit.", "",
+              "| kernel | fetch GB | write GB | algorithmic GB | traffic / algorithmic |",
+              "|---|---|---|---|---|"]
+    record = {}
+    for key in ("router_topk", "router_select", "expert_scan", "scatter_gather", "gateup",
+                "down", "combine"):
+        if key not in fetch:
+            continue
+        fb = sum(fetch[key]) / len(fetch[key]) * cf
+        wb = sum(write.get(key, [0.0])) / max(1, len(write.get(key, [0.0]))) * cw
+        al = alg.get(key)
+        ratio = f"{(fb + wb) / al:.2f}" if al else "-"
+        lines.append(f"| {key} | {fb/1e9:.4f} | {wb/1e9:.4f} | "
+                     f"{al/1e9 if al else float('nan'):.4f} | {ratio} |")
+        if key in KERNEL_SOURCES:
+            files = KERNEL_SOURCES[key][a.variant]
+            record[key] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb,
+                           "source_files": files, "source_sha256": source_hash(files),
+                           "profile": os.path.basename(a.out)}
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    try:
+        with open(a.traffic_json) as fh:
+            db = json.load(fh)
+    except FileNotFoundError:
+        db = {}
+    db.setdefault(a.workload, {}).update(record)
+    with open(a.traffic_json, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
+    print(f"wrote {a.out} and {a.traffic_json}")
+
+
+if __name__ == "__main__":
+    main()
