@@ -26,6 +26,7 @@
 // skip their MFMAs.  Work-group ids are remapped so that the tiles an XCD
 // runs together share weight and token panels in its L2.
 
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -51,6 +52,9 @@ constexpr int kTileRows = 256;        // weight rows per tile
 constexpr int kTileBK = MOE_TILE_BK;  // K per LDS stage
 constexpr int kTileNS = MOE_TILE_NS;  // LDS ring depth (stages)
 constexpr int kXcds = 8;
+#ifndef MOE_TILE_PERSISTENT
+#define MOE_TILE_PERSISTENT 0
+#endif
 #ifndef MOE_TILE_FEAT_GROUP
 #define MOE_TILE_FEAT_GROUP 4
 #endif
@@ -173,13 +177,26 @@ __device__ __forceinline__ void tile_compute(const TileCtx& c, const char* buf, 
 #pragma unroll
   for (int kk = 0; kk < kKSteps; ++kk) {
     if (kk + 1 < kKSteps) tile_frags<NBV>(c, buf, kk + 1, lane, na, nb);
+#if MOE_TILE_SCHED
+    __builtin_amdgcn_sched_barrier(0);
+#endif
 #pragma unroll
     for (int b = 0; b < NBV; ++b)
 #pragma unroll
       for (int a = 0; a < 4; ++a) acc[a][b] = mfma32(af[a], bf[b], acc[a][b]);
+#ifndef MOE_TILE_SCHED
+#define MOE_TILE_SCHED 0
+#endif
+#if MOE_TILE_SCHED
+    // hard grouping: the next k-step's reads were issued before this
+    // k-step's MFMAs and both fragment sets stay live
+    __builtin_amdgcn_sched_barrier(0);
+    if (false) {
+#else
     // order: the next k-step's fragment reads one per MFMA, then the rest
     // of the MFMAs, so the reads overlap this k-step's matrix work
     if (kk + 1 < kKSteps) {
+#endif
       constexpr int nr = 4 + NBV, nm = 4 * NBV;
       constexpr int pairs = nr < nm ? nr : nm;
 #pragma unroll
@@ -272,9 +289,21 @@ __global__ __launch_bounds__(kTileThreads, 1) MOE_TILE_WPE_ATTR void tile_gemm_k
   constexpr int FB = GATEUP ? kTileRows / 2 : kTileRows;  // output features per tile
 
   // ---- tile id: XCD-contiguous remap, then groups of kFeatGroup feature tiles
+#if MOE_TILE_PERSISTENT
+  // persistent: workgroup j of XCD x walks positions j, j + W, ... of that
+  // XCD's contiguous range, W = workgroups per XCD, so the W tiles an XCD runs
+  // together are W consecutive positions (shared panels) and stay in step
+  const int xcd = blockIdx.x % kXcds;
+  const int wg_per_xcd = gridDim.x / kXcds;
+  for (int pos = blockIdx.x / kXcds; pos < per_xcd; pos += wg_per_xcd) {
+  int Lp = xcd * per_xcd + pos;
+  if (Lp >= parts * n_ft * n_tt) break;
+#else
+  do {                                      // one tile; `continue` leaves
   const int L = blockIdx.x;
   int Lp = (L % kXcds) * per_xcd + L / kXcds;
   if (Lp >= parts * n_ft * n_tt) return;
+#endif
   const int part = Lp / (n_ft * n_tt);      // K-split part (slowest)
   Lp -= part * n_ft * n_tt;
   const int grp = Lp / (kFeatGroup * n_tt);
@@ -282,7 +311,7 @@ __global__ __launch_bounds__(kTileThreads, 1) MOE_TILE_WPE_ATTR void tile_gemm_k
   const int gsize = min(kFeatGroup, n_ft - grp * kFeatGroup);
   const int tt = rem / gsize;
   const int ft = grp * kFeatGroup + rem % gsize;
-  if (tt >= *num_tiles) return;
+  if (tt >= *num_tiles) continue;          // past the token tiles in use
   const int e = tile_expert[tt];
   const int row0 = tt * kTileBT;
   const int valid_end = offsets[e] + counts[e];
@@ -385,6 +414,11 @@ __global__ __launch_bounds__(kTileThreads, 1) MOE_TILE_WPE_ATTR void tile_gemm_k
         }
     }
   }
+#if MOE_TILE_PERSISTENT
+  }  // tile loop
+#else
+  } while (0);
+#endif
 }
 
 template <bool GATEUP>
@@ -399,7 +433,21 @@ static void tile_launch(const Dims& D, const void* act, const void* W0, const vo
   const int parts = GATEUP ? 1 : D.down_splits;
   const int total = parts * n_ft * n_tt;
   const int per_xcd = (total + kXcds - 1) / kXcds;
-  tile_gemm_kernel<GATEUP><<<per_xcd * kXcds, kTileThreads, 0, s>>>(
+#if MOE_TILE_PERSISTENT
+  // one workgroup per CU (the LDS ring allows one), at most one per position
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      n_cu = 256;
+  }
+  const int wg_per_xcd = std::max(1, std::min(per_xcd, n_cu / kXcds));
+  const int grid = wg_per_xcd * kXcds;
+#else
+  const int grid = per_xcd * kXcds;
+#endif
+  tile_gemm_kernel<GATEUP><<<grid, kTileThreads, 0, s>>>(
       (const bf16_t*)act, (const bf16_t*)W0, (const bf16_t*)W1, out, counts, offsets, num_tiles,
       tile_expert, N, K, n_ft, n_tt, per_xcd, parts, (size_t)D.max_rows * N);
 }
