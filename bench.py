@@ -36,6 +36,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
                    help="tokens of the oracle sample (0 = per-workload default)")
+    p.add_argument("--router-stats", action="store_true",
+                   help="also produce the router statistics p_i and the load-balancing loss "
+                        "in every step")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="before warmup, run one device-to-device copy of this many MiB "
                         "(a known-size reference for HBM byte counters)")
@@ -127,12 +130,14 @@ def main():
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(d["x"])
     counts = torch.zeros(E, dtype=torch.int32, device=dev)
+    probs = torch.zeros(E, dtype=torch.float32, device=dev) if args.router_stats else None
+    bloss = torch.zeros(1, dtype=torch.float32, device=dev) if args.router_stats else None
     stream = torch.cuda.current_stream(dev)
 
     def step(events=None):
         moe.forward(d["x"], d["W_router"], d["W_gate"], d["W_up"], d["W_down"], k,
                     bias=d["bias"], out=out, workspace=ws, expert_counts=counts, stream=stream,
-                    stage_events=events)
+                    stage_events=events, router_probs=probs, balance_loss=bloss)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -213,6 +218,9 @@ def main():
                   "mfma_frac": work["layer_flops"] / secs / 1e12 / (
                       BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS),
                   "experts_touched": work["touched"], "kernel_ms": split},
+        "router_stats": ({"balance_loss_unscaled": float(bloss.cpu()[0]),
+                          "p": [round(float(v), 6) for v in probs.cpu()]}
+                         if args.router_stats else None),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

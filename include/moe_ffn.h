@@ -70,6 +70,12 @@ typedef struct moe_opts {
   int32_t* topk_idx_out;      /* [T][k] device or NULL: selected expert ids       */
   float* topk_w_out;          /* [T][k] device or NULL: their gate weights        */
   int32_t* expert_counts_out; /* [E] device or NULL: tokens routed to each expert */
+  float* router_prob_out;     /* [E] device or NULL: router statistics p_i, the mean
+                                 over tokens of the full softmax of the scores over
+                                 all E experts ("ロードバランス損失")                */
+  float* balance_loss_out;    /* [1] device or NULL: N * sum_i f_i p_i with
+                                 f_i = tokens routed to i / T; times alpha this is
+                                 the auxiliary load-balancing loss                */
   void* const* stage_events;  /* NULL, or MOE_NUM_STAGES + 1 hipEvent_t recorded on
                                  the stream before the first kernel and after each
                                  stage (router, scan, scatter, gate/up, down,
@@ -137,6 +143,8 @@ typedef struct moe_ws_layout {
   size_t h;                 /* [max_rows][d_ff] dtype: SiLU(gate) * up         */
   size_t y;                 /* [down_splits][max_rows][d_model] float32:
                                partial expert outputs (their sum is W2 H)       */
+  size_t block_probs;       /* [router_blocks][E] float32: per-block sums of the
+                               full-softmax probabilities (router statistics)  */
   size_t router_partial;    /* router scratch: partial scores when the score GEMM
                                is split over d_model (few token blocks)        */
   size_t total;             /* bytes                                           */

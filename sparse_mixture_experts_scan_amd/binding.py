@@ -29,6 +29,8 @@ class MoeOpts(ctypes.Structure):
                 ("topk_idx_out", ctypes.c_void_p),
                 ("topk_w_out", ctypes.c_void_p),
                 ("expert_counts_out", ctypes.c_void_p),
+                ("router_prob_out", ctypes.c_void_p),
+                ("balance_loss_out", ctypes.c_void_p),
                 ("stage_events", ctypes.c_void_p)]
 
 MOE_NUM_STAGES = 6
@@ -43,7 +45,8 @@ class MoeWsLayout(ctypes.Structure):
                 ("down_splits", ctypes.c_int32)] + [
         (name, ctypes.c_size_t) for name in
         ("topk_idx", "topk_w", "block_counts", "counts", "offsets", "num_tiles",
-         "tile_expert", "row_token", "tok_row", "xs", "h", "y", "router_partial", "total")]
+         "tile_expert", "row_token", "tok_row", "xs", "h", "y", "block_probs", "router_partial",
+         "total")]
 
 
 class MoeError(RuntimeError):
@@ -131,13 +134,14 @@ def moe_version() -> str:
 # ---------------------------------------------------------------- torch marshalling
 def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
             workspace=None, topk_idx=None, topk_w=None, expert_counts=None, stream=None,
-            stage_events=None):
+            stage_events=None, router_probs=None, balance_loss=None):
     """One moe_ffn_forward call on torch device tensors.
 
     x [T][d] (bf16 or fp32), W_router [d][E] fp32, W_gate/W_up [E][d_ff][d],
     W_down [E][d][d_ff] (x's dtype), bias [E] fp32 or None.  Optional outputs
-    topk_idx [T][k] int32, topk_w [T][k] fp32, expert_counts [E] int32 are
-    filled when given.  `workspace` is a uint8 device tensor (see
+    topk_idx [T][k] int32, topk_w [T][k] fp32, expert_counts [E] int32,
+    router_probs [E] fp32 (mean full-softmax probability p_i) and
+    balance_loss [1] fp32 (N * sum_i f_i p_i) are filled when given.  `workspace` is a uint8 device tensor (see
     moe_ffn_workspace_size) or None for the library's own.  Returns out."""
     import torch
 
@@ -162,6 +166,10 @@ def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
             checks.append((t, shape, torch.int32))
     if topk_w is not None:
         checks.append((topk_w, (T, k), torch.float32))
+    if router_probs is not None:
+        checks.append((router_probs, (E,), torch.float32))
+    if balance_loss is not None:
+        checks.append((balance_loss, (1,), torch.float32))
     for t, shape, dt in [(x, (T, d), x.dtype)] + checks:
         if tuple(t.shape) != tuple(shape) or t.dtype != dt:
             raise ValueError(f"tensor {tuple(t.shape)} {t.dtype}: expected {shape} {dt}")
@@ -180,6 +188,8 @@ def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
     o.topk_idx_out = topk_idx.data_ptr() if topk_idx is not None else None
     o.topk_w_out = topk_w.data_ptr() if topk_w is not None else None
     o.expert_counts_out = expert_counts.data_ptr() if expert_counts is not None else None
+    o.router_prob_out = router_probs.data_ptr() if router_probs is not None else None
+    o.balance_loss_out = balance_loss.data_ptr() if balance_loss is not None else None
     if stage_events is not None:
         # MOE_NUM_STAGES + 1 created torch.cuda.Event objects (record() once first)
         if len(stage_events) != MOE_NUM_STAGES + 1:

@@ -19,14 +19,18 @@ struct Dims {
 };
 
 // a1: scores, top-k, softmax over the k, per-block expert histogram
+// blk_prob: [nblk][E] per-block full-softmax probability sums, or NULL
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
-                   int32_t* idx, float* w, int32_t* blk_counts, float* part, hipStream_t s);
+                   int32_t* idx, float* w, int32_t* blk_counts, float* part, float* blk_prob,
+                   hipStream_t s);
 int router_splits_for(int nblk, int d);
 constexpr int kRouterPartStride = 64;  // floats per token row of the partial scores
 // a2: histogram reduce, padded offsets, per-block bases, tile table
+// router statistics (when blk_prob is non-NULL): prob_out [E], loss_out [1]
 void launch_scan(const Dims& D, int32_t* blk_counts, int32_t* counts, int32_t* offsets,
                  int32_t* num_tiles, int32_t* tile_expert, int32_t* row_token,
-                 int32_t* counts_out, hipStream_t s);
+                 int32_t* counts_out, const float* blk_prob, float* prob_out, float* loss_out,
+                 hipStream_t s);
 // a2: stable row maps and gather of x into expert-contiguous rows
 void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int32_t* blk_base,
                     const int32_t* offsets, int32_t* tok_row, int32_t* row_token, void* xs,

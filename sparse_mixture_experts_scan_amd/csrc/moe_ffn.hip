@@ -102,6 +102,7 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   L.xs = take(es * D.max_rows * d);
   L.h = take(es * D.max_rows * f);
   L.y = take(sizeof(float) * D.down_splits * D.max_rows * d);
+  L.block_probs = take(sizeof(float) * D.nblk * E);
   L.router_partial = take(D.router_splits > 1 ? sizeof(float) * D.router_splits * D.nblk *
                                                     moe::kRouterTokens * moe::kRouterPartStride
                                               : 0);
@@ -162,7 +163,8 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, co
     if (reinterpret_cast<uintptr_t>(ptr) % 16)
       return fail(MOE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   for (const void* ptr : {(const void*)o.router_bias, (const void*)o.topk_idx_out,
-                          (const void*)o.topk_w_out, (const void*)o.expert_counts_out})
+                          (const void*)o.topk_w_out, (const void*)o.expert_counts_out,
+                          (const void*)o.router_prob_out, (const void*)o.balance_loss_out})
     if (reinterpret_cast<uintptr_t>(ptr) % 4)
       return fail(MOE_ERR_INVALID_ARG, "optional outputs and bias must be 4-byte aligned");
   Plan p;
@@ -214,6 +216,8 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, co
   void* h = ws + L.h;
   float* y = reinterpret_cast<float*>(ws + L.y);
   float* rpart = reinterpret_cast<float*>(ws + L.router_partial);
+  float* bprob = (o.router_prob_out || o.balance_loss_out)
+                     ? reinterpret_cast<float*>(ws + L.block_probs) : nullptr;
 
   hipError_t e;
   auto mark = [&](int i) -> hipError_t {
@@ -221,11 +225,11 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, co
                           : hipSuccess;
   };
   if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  moe::launch_router(D, x, W_router, o.router_bias, idx, w, blk, rpart, s);
+  moe::launch_router(D, x, W_router, o.router_bias, idx, w, blk, rpart, bprob, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess)
     return hip_fail(e, "router launch");
   moe::launch_scan(D, blk, counts, offsets, num_tiles, tile_expert, row_token,
-                   o.expert_counts_out, s);
+                   o.expert_counts_out, bprob, o.router_prob_out, o.balance_loss_out, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess)
     return hip_fail(e, "scan launch");
   moe::launch_scatter(D, x, idx, blk, offsets, tok_row, row_token, xs, s);

@@ -85,6 +85,31 @@ __device__ inline void select_topk_token(const float* srow, int E, int k, size_t
     }
 }
 
+// Router statistics of one block ("ロードバランス損失": p_i is the mean over
+// tokens of softmax(s_t)_i over all N experts): for each expert, the sum over
+// the block's valid tokens, in token order, of the full-softmax probability.
+// Called by every thread of the block (contains barriers).
+__device__ inline void block_prob_sums(const float (*slog)[65], int t0, int nT, int E,
+                                       float* smax, float* sinv, float* __restrict__ out_row) {
+  constexpr int TB = kRouterTokens;
+  const int tid = threadIdx.x;
+  if (tid < TB) {
+    float m = slog[tid][0];
+    for (int e = 1; e < E; ++e) m = fmaxf(m, slog[tid][e]);
+    float z = 0.f;
+    for (int e = 0; e < E; ++e) z += expf(slog[tid][e] - m);
+    smax[tid] = m;
+    sinv[tid] = 1.f / z;
+  }
+  __syncthreads();
+  if (tid < E) {
+    float acc = 0.f;
+    for (int t = 0; t < TB; ++t)
+      if (t0 + t < nT) acc += expf(slog[t][tid] - smax[t]) * sinv[t];
+    out_row[tid] = acc;
+  }
+}
+
 // Scores of kRouterTokens tokens over the d_model range of split blockIdx.y
 // (all of d_model when splits == 1).  splits == 1: adds the bias, selects
 // and writes the routing; splits > 1: writes the partial scores to `part`
@@ -93,7 +118,8 @@ template <typename T>
 __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
     int nT, int d, int E, int k, int splits, float* __restrict__ part,
-    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ blk_counts) {
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ blk_counts,
+    float* __restrict__ blk_prob) {
   constexpr int TB = kRouterTokens;
   constexpr int NB = TB / 16;            // token column blocks
   constexpr int MB = 64 / 16;            // expert row blocks (max)
@@ -211,6 +237,10 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
     select_topk_token(slog[tid], E, k, (size_t)(t0 + tid), idx_out, w_out, hist);
   __syncthreads();
   if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = hist[tid];
+  if (blk_prob) {
+    __shared__ float smax[TB], sinv[TB];
+    block_prob_sums(slog, t0, nT, E, smax, sinv, blk_prob + (size_t)blockIdx.x * E);
+  }
 }
 
 // Second pass of a split router: per token, the split partial scores are
@@ -221,7 +251,7 @@ constexpr int kMaxRouterSplits = 16;
 __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int nT, int E, int k,
     int splits, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-    int32_t* __restrict__ blk_counts) {
+    int32_t* __restrict__ blk_counts, float* __restrict__ blk_prob) {
   constexpr int TB = kRouterTokens;
   __shared__ float slog[TB][65];
   __shared__ int hist[64];
@@ -247,6 +277,10 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     select_topk_token(slog[tid], E, k, (size_t)(t0 + tid), idx_out, w_out, hist);
   __syncthreads();
   if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = hist[tid];
+  if (blk_prob) {
+    __shared__ float smax[TB], sinv[TB];
+    block_prob_sums(slog, t0, nT, E, smax, sinv, blk_prob + (size_t)blockIdx.x * E);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -259,7 +293,8 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(
     int32_t* __restrict__ blk, int nblk, int E, int Epow2, int BT, int max_rows, int max_tiles,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ num_tiles,
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ row_token,
-    int32_t* __restrict__ counts_out) {
+    int32_t* __restrict__ counts_out, int nT, const float* __restrict__ blk_prob,
+    float* __restrict__ prob_out, float* __restrict__ loss_out) {
   __shared__ int part[256];
   __shared__ int s_cnt[64];
   __shared__ int s_off[65];
@@ -320,6 +355,25 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(
   for (int x = 0; x < E; ++x)
     for (int r = s_off[x] + s_cnt[x] + tid; r < s_off[x + 1]; r += 256) row_token[r] = -1;
   for (int r = P + tid; r < max_rows; r += 256) row_token[r] = -1;
+
+  // router statistics ("ロードバランス損失"): p_i = mean full-softmax
+  // probability (block sums added in block order), f_i = counts_i / T,
+  // loss = N * sum_i f_i p_i
+  if (blk_prob) {
+    __shared__ float s_p[64];
+    if (tid < E) {
+      float acc = 0.f;
+      for (int b = 0; b < nblk; ++b) acc += blk_prob[(size_t)b * E + tid];
+      s_p[tid] = acc / (float)nT;
+      if (prob_out) prob_out[tid] = s_p[tid];
+    }
+    __syncthreads();
+    if (tid == 0 && loss_out) {
+      float L = 0.f;
+      for (int x = 0; x < E; ++x) L += ((float)s_cnt[x] / (float)nT) * s_p[x];
+      *loss_out = (float)E * L;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -429,17 +483,20 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 // ---------------------------------------------------------------------------
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
-                   int32_t* idx, float* w, int32_t* blk_counts, float* part, hipStream_t s) {
+                   int32_t* idx, float* w, int32_t* blk_counts, float* part, float* blk_prob,
+                   hipStream_t s) {
   const dim3 grid(D.nblk, D.router_splits);
   if (D.bf16)
     router_topk_kernel<bf16_t><<<grid, kRouterMfmaThreads, 0, s>>>(
-        (const bf16_t*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts);
+        (const bf16_t*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts,
+        blk_prob);
   else
     router_topk_kernel<float><<<grid, kRouterMfmaThreads, 0, s>>>(
-        (const float*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts);
+        (const float*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts,
+        blk_prob);
   if (D.router_splits > 1)
-    router_select_kernel<<<D.nblk, kSelectThreads, 0, s>>>(part, bias, D.T, D.E, D.k,
-                                                              D.router_splits, idx, w, blk_counts);
+    router_select_kernel<<<D.nblk, kSelectThreads, 0, s>>>(
+        part, bias, D.T, D.E, D.k, D.router_splits, idx, w, blk_counts, blk_prob);
 }
 
 int router_splits_for(int nblk, int d) {
@@ -453,10 +510,11 @@ int router_splits_for(int nblk, int d) {
 
 void launch_scan(const Dims& D, int32_t* blk_counts, int32_t* counts, int32_t* offsets,
                  int32_t* num_tiles, int32_t* tile_expert, int32_t* row_token,
-                 int32_t* counts_out, hipStream_t s) {
+                 int32_t* counts_out, const float* blk_prob, float* prob_out, float* loss_out,
+                 hipStream_t s) {
   expert_scan_kernel<<<1, 256, 0, s>>>(blk_counts, D.nblk, D.E, D.Epow2, D.BT, D.max_rows,
                                        D.max_tiles, counts, offsets, num_tiles, tile_expert,
-                                       row_token, counts_out);
+                                       row_token, counts_out, D.T, blk_prob, prob_out, loss_out);
 }
 
 void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int32_t* blk_base,
