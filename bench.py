@@ -19,7 +19,7 @@ import time
 
 import numpy as np
 
-from sparse_mixture_experts_scan_amd.inputs import CONFIGS, make_inputs
+from sparse_mixture_experts_scan_amd.inputs import CONFIGS, make_block_inputs, make_inputs
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA
@@ -39,6 +39,9 @@ def parse():
     p.add_argument("--router-stats", action="store_true",
                    help="also produce the router statistics p_i and the load-balancing loss "
                         "in every step")
+    p.add_argument("--block", action="store_true",
+                   help="time the normalised block out = x + layer(RMSNorm(x)) instead of "
+                        "the bare layer")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="before warmup, run one device-to-device copy of this many MiB "
                         "(a known-size reference for HBM byte counters)")
@@ -80,7 +83,7 @@ def measured_traffic(workload, kernel, variant):
     return rec["bytes"]
 
 
-def cpu_baseline(cfg, inp, n_tokens):
+def cpu_baseline(cfg, inp, n_tokens, block=False):
     """The fp64 oracle as it stands, timed on a bounded token sample."""
     import oracle
     try:
@@ -91,8 +94,12 @@ def cpu_baseline(cfg, inp, n_tokens):
     rng = np.random.default_rng(123)
     toks = np.sort(rng.choice(cfg.T, size=min(n_tokens, cfg.T), replace=False))
     t0 = time.perf_counter()
-    oracle.moe_forward(inp["x"], inp["W_router"], inp["W_gate"], inp["W_up"], inp["W_down"],
-                       cfg.k, bias=inp["bias"], tokens=toks)
+    if block:
+        oracle.block_forward(inp["x"], inp["norm_weight"], 1e-5, inp["W_router"], inp["W_gate"],
+                             inp["W_up"], inp["W_down"], cfg.k, bias=inp["bias"], tokens=toks)
+    else:
+        oracle.moe_forward(inp["x"], inp["W_router"], inp["W_gate"], inp["W_up"],
+                           inp["W_down"], cfg.k, bias=inp["bias"], tokens=toks)
     dt = time.perf_counter() - t0
     return {"value": len(toks) / dt, "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
@@ -114,7 +121,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
-    inp = make_inputs(cfg, seed=args.seed)
+    inp = (make_block_inputs if args.block else make_inputs)(cfg, seed=args.seed)
 
     def up(a):
         if a is None:
@@ -137,7 +144,8 @@ def main():
     def step(events=None):
         moe.forward(d["x"], d["W_router"], d["W_gate"], d["W_up"], d["W_down"], k,
                     bias=d["bias"], out=out, workspace=ws, expert_counts=counts, stream=stream,
-                    stage_events=events, router_probs=probs, balance_loss=bloss)
+                    stage_events=events, router_probs=probs, balance_loss=bloss,
+                    norm_weight=d.get("norm_weight"), eps=1e-5)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -211,6 +219,7 @@ def main():
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) random-init weights)",
         "config": {"workload": cfg.name, "T": T, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
                    "E": E, "k": k, "router_bias": cfg.router_bias, "seed": args.seed,
+                   "block": bool(args.block),
                    "parallelism": "single GPU"},
         "layer": {"GB/s": work["layer_bytes"] / secs / 1e9,
                   "hbm_frac": work["layer_bytes"] / secs / 1e9 / HBM_PEAK_GBS,
@@ -226,7 +235,7 @@ def main():
     if not args.no_cpu_baseline:
         n = args.cpu_sample_tokens or {"tiny": 64, "decode": 16}.get(cfg.name, 64)
         print(f"[bench] cpu baseline on {n} tokens", file=sys.stderr, flush=True)
-        record["cpu_baseline"] = cpu_baseline(cfg, inp, n)
+        record["cpu_baseline"] = cpu_baseline(cfg, inp, n, block=args.block)
     print(json.dumps(record), flush=True)
 
 

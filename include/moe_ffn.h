@@ -101,16 +101,37 @@ void moe_opts_init(moe_opts_t* opts);
  *   W_up      [E][d_ff][d_model]       dtype  (W3)
  *   W_down    [E][d_model][d_ff]       dtype  (W2)
  *   out       [T][d_model]             dtype  (written, never read)
- *   1 <= T <= 2^24; 1 <= k <= E <= 64; k <= 8; d_model, d_ff multiples of 64.
+ *   0 <= T <= 2^24; 1 <= k <= E <= 64; k <= 8; d_model, d_ff multiples of 64.
  *   opts      NULL = defaults.
+ * T = 0 (an empty batch) is valid: nothing is read or written except the
+ * optional statistics, which become zero counts, zero p_i and a zero loss.
  */
 int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate,
                     const void* W_up, const void* W_down, void* out, int64_t T,
                     int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
                     const moe_opts_t* opts);
 
+/*
+ * One MoE sub-block of a Mixtral transformer block: out = x + layer(RMSNorm(x)).
+ * "Mistral/Mixtralのアーキテクチャ", section "Mixtralのアーキテクチャ",
+ * lists the second half of each block as normalisation, then the MoE layer,
+ * then a residual connection.  The pages name RMSNorm without a formula; the
+ * plain (LLaMA) definition is taken: RMSNorm(x)[t][j] =
+ * x[t][j] / sqrt(mean_j x[t][j]^2 + eps) * norm_weight[j].
+ *   norm_weight [d_model] float32 device, 4-byte aligned; 0 <= eps <= 1.
+ * The router scores the normalised tokens in fp32 (from x, norm_weight and
+ * the per-token 1/rms); the experts take the normalised tokens rounded to
+ * the element type; the residual is added in fp32 before the single rounding
+ * of out.  out must not alias x.  Other arguments, outputs, limits and errors
+ * as moe_ffn_forward; the same workspace size applies.
+ */
+int moe_block_forward(const void* x, const float* norm_weight, float eps, const float* W_router,
+                      const void* W_gate, const void* W_up, const void* W_down, void* out,
+                      int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                      const moe_opts_t* opts);
+
 /* Bytes of workspace moe_ffn_forward needs for this shape (0 if the shape is
- * invalid or unsupported). */
+ * invalid or unsupported; T = 0 is sized as T = 1). */
 size_t moe_ffn_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
                               int32_t k, int32_t dtype);
 
@@ -145,6 +166,8 @@ typedef struct moe_ws_layout {
                                partial expert outputs (their sum is W2 H)       */
   size_t block_probs;       /* [router_blocks][E] float32: per-block sums of the
                                full-softmax probabilities (router statistics)  */
+  size_t norm_rs;           /* [T] float32: 1/rms of each token (block wrapper)  */
+  size_t xn;                /* [T][d_model] dtype: RMS-normalised tokens        */
   size_t router_partial;    /* router scratch: partial scores when the score GEMM
                                is split over d_model (few token blocks)        */
   size_t total;             /* bytes                                           */

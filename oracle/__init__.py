@@ -1,6 +1,6 @@
 """fp64 CPU oracle of the sparse MoE layer: test infrastructure only (see
 moe_oracle's header for who may use it)."""
-from .moe_oracle import (balance_stats, expert_hidden, expert_param_count,  # noqa: F401
-                         moe_forward,
+from .moe_oracle import (balance_stats, block_forward, expert_hidden,  # noqa: F401
+                         expert_param_count, moe_forward, rms_norm,
                          router_logits, routing_gaps, select_topk, silu,
                          swiglu_expert, to_f64, topk_gates)

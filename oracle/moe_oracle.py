@@ -190,6 +190,37 @@ def moe_forward(x, W_router, W_gate, W_up, W_down, k, bias=None, tokens=None,
 
 
 # ----------------------------------------------------------------------------
+# transformer-block wrapper: RMSNorm before, residual after
+# ----------------------------------------------------------------------------
+
+def rms_norm(x, weight, eps) -> np.ndarray:
+    """RMSNorm(x) = x / sqrt(mean_j x_j^2 + eps) * weight, per token.
+
+    The architecture page (section on Mixtral's block structure) places an
+    RMSNorm before the MoE layer and a residual connection after it, without
+    defining RMSNorm; this is its plain definition, with a per-feature weight
+    and eps as parameters."""
+    xf = to_f64(x)
+    ms = (xf * xf).mean(axis=1, keepdims=True)
+    return xf / np.sqrt(ms + float(eps)) * to_f64(weight)[None, :]
+
+
+def block_forward(x, norm_weight, eps, W_router, W_gate, W_up, W_down, k, bias=None,
+                  tokens=None, forced_idx=None) -> dict:
+    """One MoE sub-block: out = x + MoE(RMSNorm(x)) ("Mistral/Mixtralの
+    アーキテクチャ", section "Mixtralのアーキテクチャ": normalisation, the MoE
+    layer, then a residual connection).  Returns moe_forward's dict with
+    `out` replaced by the block output and `moe_out` the MoE part."""
+    xn = rms_norm(x, norm_weight, eps)
+    r = moe_forward(xn, W_router, W_gate, W_up, W_down, k, bias=bias, tokens=tokens,
+                    forced_idx=forced_idx)
+    r["moe_out"] = r["out"]
+    r["out"] = to_f64(x)[r["tokens"]] + r["moe_out"]
+    r["x_norm"] = xn
+    return r
+
+
+# ----------------------------------------------------------------------------
 # router statistics and load-balancing loss (forward value only)
 # ----------------------------------------------------------------------------
 

@@ -5,6 +5,7 @@ The layer runs in hand-written HIP kernels for gfx950 behind a C ABI
 kernels' sources, the build step, the ctypes binding and the seeded workload
 generator."""
 from .binding import (EXPORTED, MOE_BF16, MOE_F32, MoeError, MoeOpts,  # noqa: F401
-                      MoeWsLayout, forward, lib, moe_ffn_forward, moe_ffn_workspace_layout,
+                      MoeWsLayout, forward, lib, moe_block_forward, moe_ffn_forward,
+                      moe_ffn_workspace_layout,
                       moe_ffn_workspace_size, moe_last_error, moe_opts_init, moe_release,
                       moe_status_string, moe_version)

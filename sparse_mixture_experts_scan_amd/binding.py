@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libmoe_ffn.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_BF16, MOE_F32 = 0, 1
 
-EXPORTED = ("moe_opts_init", "moe_ffn_forward", "moe_ffn_workspace_size",
+EXPORTED = ("moe_opts_init", "moe_ffn_forward", "moe_block_forward", "moe_ffn_workspace_size",
             "moe_ffn_workspace_layout", "moe_status_string", "moe_last_error",
             "moe_release", "moe_version")
 
@@ -45,8 +45,8 @@ class MoeWsLayout(ctypes.Structure):
                 ("down_splits", ctypes.c_int32)] + [
         (name, ctypes.c_size_t) for name in
         ("topk_idx", "topk_w", "block_counts", "counts", "offsets", "num_tiles",
-         "tile_expert", "row_token", "tok_row", "xs", "h", "y", "block_probs", "router_partial",
-         "total")]
+         "tile_expert", "row_token", "tok_row", "xs", "h", "y", "block_probs", "norm_rs", "xn",
+         "router_partial", "total")]
 
 
 class MoeError(RuntimeError):
@@ -72,6 +72,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
                                       ctypes.POINTER(MoeOpts)]
         L.moe_ffn_forward.restype = ctypes.c_int
+        L.moe_block_forward.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, i64, i64,
+                                        i64, i32, i32, ctypes.POINTER(MoeOpts)]
+        L.moe_block_forward.restype = ctypes.c_int
         L.moe_ffn_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
         L.moe_ffn_workspace_size.restype = sz
         L.moe_ffn_workspace_layout.argtypes = [i64, i64, i64, i32, i32, i32,
@@ -101,6 +104,14 @@ def moe_ffn_forward(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E,
     """Raw entry point: integer device addresses, returns the status code."""
     return lib().moe_ffn_forward(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E,
                                  k, ctypes.byref(opts) if opts is not None else None)
+
+
+def moe_block_forward(x, norm_weight, eps, W_router, W_gate, W_up, W_down, out, T, d_model,
+                      d_ff, E, k, opts: Optional[MoeOpts] = None) -> int:
+    """Raw entry point of the block wrapper out = x + layer(RMSNorm(x))."""
+    return lib().moe_block_forward(x, norm_weight, eps, W_router, W_gate, W_up, W_down, out, T,
+                                   d_model, d_ff, E, k,
+                                   ctypes.byref(opts) if opts is not None else None)
 
 
 def moe_ffn_workspace_size(T, d_model, d_ff, E, k, dtype=MOE_BF16) -> int:
@@ -134,15 +145,19 @@ def moe_version() -> str:
 # ---------------------------------------------------------------- torch marshalling
 def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
             workspace=None, topk_idx=None, topk_w=None, expert_counts=None, stream=None,
-            stage_events=None, router_probs=None, balance_loss=None):
+            stage_events=None, router_probs=None, balance_loss=None, norm_weight=None,
+            eps=1e-5):
     """One moe_ffn_forward call on torch device tensors.
 
     x [T][d] (bf16 or fp32), W_router [d][E] fp32, W_gate/W_up [E][d_ff][d],
     W_down [E][d][d_ff] (x's dtype), bias [E] fp32 or None.  Optional outputs
     topk_idx [T][k] int32, topk_w [T][k] fp32, expert_counts [E] int32,
     router_probs [E] fp32 (mean full-softmax probability p_i) and
-    balance_loss [1] fp32 (N * sum_i f_i p_i) are filled when given.  `workspace` is a uint8 device tensor (see
-    moe_ffn_workspace_size) or None for the library's own.  Returns out."""
+    balance_loss [1] fp32 (N * sum_i f_i p_i) are filled when given.  With
+    norm_weight [d] fp32 the call is the block wrapper
+    out = x + layer(RMSNorm(x)) (moe_block_forward, with `eps`).  `workspace`
+    is a uint8 device tensor (see moe_ffn_workspace_size) or None for the
+    library's own.  Returns out."""
     import torch
 
     T, d = x.shape
@@ -168,6 +183,8 @@ def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
         checks.append((topk_w, (T, k), torch.float32))
     if router_probs is not None:
         checks.append((router_probs, (E,), torch.float32))
+    if norm_weight is not None:
+        checks.append((norm_weight, (d,), torch.float32))
     if balance_loss is not None:
         checks.append((balance_loss, (1,), torch.float32))
     for t, shape, dt in [(x, (T, d), x.dtype)] + checks:
@@ -197,9 +214,14 @@ def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
         arr = (ctypes.c_void_p * len(stage_events))(*[ev.cuda_event for ev in stage_events])
         o.stage_events = ctypes.cast(arr, ctypes.c_void_p)
     with torch.cuda.device(x.device):
-        status = moe_ffn_forward(x.data_ptr(), W_router.data_ptr(), W_gate.data_ptr(),
-                                 W_up.data_ptr(), W_down.data_ptr(), out.data_ptr(), T, d, d_ff,
-                                 E, k, o)
+        if norm_weight is not None:
+            status = moe_block_forward(x.data_ptr(), norm_weight.data_ptr(), float(eps),
+                                       W_router.data_ptr(), W_gate.data_ptr(), W_up.data_ptr(),
+                                       W_down.data_ptr(), out.data_ptr(), T, d, d_ff, E, k, o)
+        else:
+            status = moe_ffn_forward(x.data_ptr(), W_router.data_ptr(), W_gate.data_ptr(),
+                                     W_up.data_ptr(), W_down.data_ptr(), out.data_ptr(), T, d,
+                                     d_ff, E, k, o)
     if status != MOE_OK:
         raise MoeError(status, "moe_ffn_forward")
     return out

@@ -19,10 +19,15 @@ struct Dims {
 };
 
 // a1: scores, top-k, softmax over the k, per-block expert histogram
-// blk_prob: [nblk][E] per-block full-softmax probability sums, or NULL
+// block wrapper: rs[t] = 1/rms(x[t]), xn = x * rs * weight (element type)
+void launch_rmsnorm(const Dims& D, const void* x, const float* weight, float eps, float* rs,
+                    void* xn, hipStream_t s);
+// blk_prob: [nblk][E] per-block full-softmax probability sums, or NULL.
+// gamma, rs (both or neither): scores of the RMS-normalised tokens,
+// rs[t] * sum_j x[t][j] gamma[j] W[j][e]
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
                    int32_t* idx, float* w, int32_t* blk_counts, float* part, float* blk_prob,
-                   hipStream_t s);
+                   const float* gamma, const float* rs, hipStream_t s);
 int router_splits_for(int nblk, int d);
 constexpr int kRouterPartStride = 64;  // floats per token row of the partial scores
 // a2: histogram reduce, padded offsets, per-block bases, tile table
@@ -53,7 +58,12 @@ void launch_down_tile(const Dims& D, const void* h, const void* Wd, float* y,
                       const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                       const int32_t* tile_expert, hipStream_t s);
 // a5: gate-weighted gather-sum back to token order
+// resid: x for the block wrapper (out = x + layer), or NULL
+// T = 0: zero the optional statistics outputs (any may be null).
+void launch_empty_stats(int E, int32_t* counts_out, float* prob_out, float* loss_out,
+                        hipStream_t s);
+
 void launch_combine(const Dims& D, const float* y, const int32_t* tok_row, const float* w,
-                    void* out, hipStream_t s);
+                    const void* resid, void* out, hipStream_t s);
 
 }  // namespace moe

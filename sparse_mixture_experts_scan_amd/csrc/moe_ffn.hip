@@ -37,7 +37,7 @@ constexpr int64_t kTileMinRows = 96;
 // Touches no HIP API.
 int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dtype, Plan* p) {
   if (T < 1 || d < 1 || f < 1 || E < 1 || k < 1)
-    return fail(MOE_ERR_INVALID_ARG, "T, d_model, d_ff, E and k must be >= 1");
+    return fail(MOE_ERR_INVALID_ARG, "T must be >= 0; d_model, d_ff, E and k >= 1");
   if (k > E) return fail(MOE_ERR_INVALID_ARG, "k must be <= E");
   if (dtype != MOE_BF16 && dtype != MOE_F32) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
   if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E > 64");
@@ -103,6 +103,8 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   L.h = take(es * D.max_rows * f);
   L.y = take(sizeof(float) * D.down_splits * D.max_rows * d);
   L.block_probs = take(sizeof(float) * D.nblk * E);
+  L.norm_rs = take(sizeof(float) * T);
+  L.xn = take(es * T * d);
   L.router_partial = take(D.router_splits > 1 ? sizeof(float) * D.router_splits * D.nblk *
                                                     moe::kRouterTokens * moe::kRouterPartStride
                                               : 0);
@@ -134,7 +136,7 @@ void moe_opts_init(moe_opts_t* o) {
 size_t moe_ffn_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
                               int32_t dtype) {
   Plan p;
-  if (make_plan(T, d_model, d_ff, E, k, dtype, &p) != MOE_OK) return 0;
+  if (make_plan(T == 0 ? 1 : T, d_model, d_ff, E, k, dtype, &p) != MOE_OK) return 0;
   return p.L.total;
 }
 
@@ -143,19 +145,41 @@ int moe_ffn_workspace_layout(int64_t T, int64_t d_model, int64_t d_ff, int32_t E
   g_last_error.clear();
   if (!layout) return fail(MOE_ERR_INVALID_ARG, "layout is NULL");
   Plan p;
-  const int st = make_plan(T, d_model, d_ff, E, k, dtype, &p);
+  const int st = make_plan(T == 0 ? 1 : T, d_model, d_ff, E, k, dtype, &p);
   if (st != MOE_OK) return st;
   *layout = p.L;
   return MOE_OK;
 }
 
-int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, const void* W_up,
-                    const void* W_down, void* out, int64_t T, int64_t d_model, int64_t d_ff,
-                    int32_t E, int32_t k, const moe_opts_t* opts) {
+}  // extern "C"
+
+namespace {
+
+// The whole launch sequence.  norm_w != NULL selects the block wrapper:
+// out = x + layer(RMSNorm(x)).
+int run_layer(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+              const void* W_down, void* out, int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
+              int32_t k, const float* norm_w, float eps, const moe_opts_t* opts) {
   g_last_error.clear();
   moe_opts_t o;
   if (opts) o = *opts;
   else moe_opts_init(&o);
+  Plan p;
+  // an empty batch checks the other sizes as for one token, reads no tensor
+  // and only clears the optional statistics
+  int st = make_plan(T == 0 ? 1 : T, d_model, d_ff, E, k, o.dtype, &p);
+  if (st != MOE_OK) return st;
+  if (T == 0) {
+    for (const void* ptr : {(const void*)o.expert_counts_out, (const void*)o.router_prob_out,
+                            (const void*)o.balance_loss_out})
+      if (reinterpret_cast<uintptr_t>(ptr) % 4)
+        return fail(MOE_ERR_INVALID_ARG, "optional outputs must be 4-byte aligned");
+    if (!o.expert_counts_out && !o.router_prob_out && !o.balance_loss_out) return MOE_OK;
+    moe::launch_empty_stats(E, o.expert_counts_out, o.router_prob_out, o.balance_loss_out,
+                            reinterpret_cast<hipStream_t>(o.stream));
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "empty-batch launch");
+  }
   if (!x || !W_router || !W_gate || !W_up || !W_down || !out)
     return fail(MOE_ERR_INVALID_ARG, "null tensor pointer");
   // rows are moved with 16-byte vector loads and stores
@@ -164,12 +188,10 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, co
       return fail(MOE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   for (const void* ptr : {(const void*)o.router_bias, (const void*)o.topk_idx_out,
                           (const void*)o.topk_w_out, (const void*)o.expert_counts_out,
-                          (const void*)o.router_prob_out, (const void*)o.balance_loss_out})
+                          (const void*)o.router_prob_out, (const void*)o.balance_loss_out,
+                          (const void*)norm_w})
     if (reinterpret_cast<uintptr_t>(ptr) % 4)
-      return fail(MOE_ERR_INVALID_ARG, "optional outputs and bias must be 4-byte aligned");
-  Plan p;
-  int st = make_plan(T, d_model, d_ff, E, k, o.dtype, &p);
-  if (st != MOE_OK) return st;
+      return fail(MOE_ERR_INVALID_ARG, "optional outputs, bias and norm weight must be 4-byte aligned");
   if (o.workspace) {
     if (reinterpret_cast<uintptr_t>(o.workspace) % 256)
       return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -218,6 +240,8 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, co
   float* rpart = reinterpret_cast<float*>(ws + L.router_partial);
   float* bprob = (o.router_prob_out || o.balance_loss_out)
                      ? reinterpret_cast<float*>(ws + L.block_probs) : nullptr;
+  float* rs = norm_w ? reinterpret_cast<float*>(ws + L.norm_rs) : nullptr;
+  void* xn = ws + L.xn;
 
   hipError_t e;
   auto mark = [&](int i) -> hipError_t {
@@ -225,14 +249,18 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, co
                           : hipSuccess;
   };
   if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
-  moe::launch_router(D, x, W_router, o.router_bias, idx, w, blk, rpart, bprob, s);
+  if (norm_w) {
+    moe::launch_rmsnorm(D, x, norm_w, eps, rs, xn, s);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "rmsnorm launch");
+  }
+  moe::launch_router(D, x, W_router, o.router_bias, idx, w, blk, rpart, bprob, norm_w, rs, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess)
     return hip_fail(e, "router launch");
   moe::launch_scan(D, blk, counts, offsets, num_tiles, tile_expert, row_token,
                    o.expert_counts_out, bprob, o.router_prob_out, o.balance_loss_out, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess)
     return hip_fail(e, "scan launch");
-  moe::launch_scatter(D, x, idx, blk, offsets, tok_row, row_token, xs, s);
+  moe::launch_scatter(D, norm_w ? xn : x, idx, blk, offsets, tok_row, row_token, xs, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess)
     return hip_fail(e, "scatter launch");
   if (L.gemm_variant == 1)
@@ -247,10 +275,33 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, co
     moe::launch_down_stream(D, h, W_down, y, counts, offsets, num_tiles, tile_expert, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(5)) != hipSuccess)
     return hip_fail(e, "down launch");
-  moe::launch_combine(D, y, tok_row, w, out, s);
+  moe::launch_combine(D, y, tok_row, w, norm_w ? x : nullptr, out, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(6)) != hipSuccess)
     return hip_fail(e, "combine launch");
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                    const void* W_down, void* out, int64_t T, int64_t d_model, int64_t d_ff,
+                    int32_t E, int32_t k, const moe_opts_t* opts) {
+  return run_layer(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E, k, nullptr, 0.f,
+                   opts);
+}
+
+int moe_block_forward(const void* x, const float* norm_weight, float eps, const float* W_router,
+                      const void* W_gate, const void* W_up, const void* W_down, void* out,
+                      int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                      const moe_opts_t* opts) {
+  g_last_error.clear();
+  if (!norm_weight) return fail(MOE_ERR_INVALID_ARG, "norm_weight is NULL");
+  if (!(eps >= 0.f) || eps > 1.f) return fail(MOE_ERR_INVALID_ARG, "eps must be in [0, 1]");
+  if (T > 0 && x == out) return fail(MOE_ERR_INVALID_ARG, "out must not alias x");
+  return run_layer(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E, k, norm_weight,
+                   eps, opts);
 }
 
 const char* moe_status_string(int status) {

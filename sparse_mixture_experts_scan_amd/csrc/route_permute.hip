@@ -14,6 +14,44 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
+// Block wrapper, before the layer: RMSNorm of each token ("Mistral/Mixtral
+// のアーキテクチャ", section "Mixtralのアーキテクチャ": the MoE half of a
+// block normalises, applies the layer, then adds the residual):
+//   rs[t] = 1 / sqrt(mean_j x[t][j]^2 + eps)      (fp32, fixed-order sum)
+//   xn[t][j] = x[t][j] * rs[t] * weight[j]        (rounded to the element type)
+// xn feeds the experts; the router uses x, weight and rs directly so that
+// its scores are not computed from the rounded xn.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x,
+                                                      const float* __restrict__ weight, float eps,
+                                                      int d, float* __restrict__ rs_out,
+                                                      T* __restrict__ xn) {
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float wsum[4];
+  __shared__ float s_rs;
+  const T* xr = x + (size_t)t * d;
+  float ss = 0.f;
+  for (int j = tid; j < d; j += 256) {
+    const float v = Elem<T>::to_f32(xr[j]);
+    ss = fmaf(v, v, ss);
+  }
+  // fixed-order reduction: lanes by xor-shuffle, then the 4 waves in order
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if (lane == 0) wsum[wave] = ss;
+  __syncthreads();
+  if (tid == 0) {
+    const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    s_rs = 1.0f / sqrtf(tot / (float)d + eps);
+    rs_out[t] = s_rs;
+  }
+  __syncthreads();
+  const float r = s_rs;
+  for (int j = tid; j < d; j += 256)
+    xn[(size_t)t * d + j] = Elem<T>::from_f32(Elem<T>::to_f32(xr[j]) * r * weight[j]);
+}
+
+// ---------------------------------------------------------------------------
 // a1: router.  One block = kRouterTokens tokens (two 16-token MFMA columns) x
 // all E experts (16-expert MFMA rows, zero-padded).  Scores are an fp32 GEMM
 // on v_mfma_f32_16x16x4_f32: A = W_router^T (expert rows), B = x^T (token
@@ -85,7 +123,7 @@ __device__ inline void select_topk_token(const float* srow, int E, int k, size_t
     }
 }
 
-// Router statistics of one block ("ロードバランス損失": p_i is the mean over
+// Router statistics of one block (load-balancing loss: p_i is the mean over
 // tokens of softmax(s_t)_i over all N experts): for each expert, the sum over
 // the block's valid tokens, in token order, of the full-softmax probability.
 // Called by every thread of the block (contains barriers).
@@ -119,7 +157,7 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
     int nT, int d, int E, int k, int splits, float* __restrict__ part,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ blk_counts,
-    float* __restrict__ blk_prob) {
+    float* __restrict__ blk_prob, const float* __restrict__ gamma, const float* __restrict__ rs) {
   constexpr int TB = kRouterTokens;
   constexpr int NB = TB / 16;            // token column blocks
   constexpr int MB = 64 / 16;            // expert row blocks (max)
@@ -171,7 +209,9 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
         av[u][a] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (kok && a < mb_used && ex < E) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) av[u][a][i] = Wr[(size_t)(k0 + i) * E + ex];
+          for (int i = 0; i < 4; ++i)
+            av[u][a][i] = gamma ? Wr[(size_t)(k0 + i) * E + ex] * gamma[k0 + i]
+                                : Wr[(size_t)(k0 + i) * E + ex];
         }
       }
     }
@@ -225,8 +265,11 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
           if (ex < E) {
             if (splits > 1)
               part[((size_t)blockIdx.y * gridDim.x * TB + t0 + b * 16 + m) * kRouterPartStride + ex] = v[i];
-            else
-              slog[b * 16 + m][ex] = v[i] + (bias ? bias[ex] : 0.f);
+            else {
+              const int t = t0 + b * 16 + m;
+              const float sc = (rs && t < nT) ? rs[t] : 1.f;
+              slog[b * 16 + m][ex] = v[i] * sc + (bias ? bias[ex] : 0.f);
+            }
           }
         }
       }
@@ -251,7 +294,8 @@ constexpr int kMaxRouterSplits = 16;
 __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int nT, int E, int k,
     int splits, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-    int32_t* __restrict__ blk_counts, float* __restrict__ blk_prob) {
+    int32_t* __restrict__ blk_counts, float* __restrict__ blk_prob,
+    const float* __restrict__ rs) {
   constexpr int TB = kRouterTokens;
   __shared__ float slog[TB][65];
   __shared__ int hist[64];
@@ -270,7 +314,8 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
 #pragma unroll
     for (int sp = 1; sp < kMaxRouterSplits; ++sp)   // added in split order
       if (sp < splits) v += p[sp];
-    slog[tt][e] = v + (bias ? bias[e] : 0.f);
+    const float sc = (rs && t0 + tt < nT) ? rs[t0 + tt] : 1.f;
+    slog[tt][e] = v * sc + (bias ? bias[e] : 0.f);
   }
   __syncthreads();
   if (tid < TB && t0 + tid < nT)
@@ -356,7 +401,7 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(
     for (int r = s_off[x] + s_cnt[x] + tid; r < s_off[x + 1]; r += 256) row_token[r] = -1;
   for (int r = P + tid; r < max_rows; r += 256) row_token[r] = -1;
 
-  // router statistics ("ロードバランス損失"): p_i = mean full-softmax
+  // router statistics (the load-balancing loss): p_i = mean full-softmax
   // probability (block sums added in block order), f_i = counts_i / T,
   // loss = N * sum_i f_i p_i
   if (blk_prob) {
@@ -447,6 +492,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const int32_t* __restrict__ tok_row,
                                                       const float* __restrict__ w, int d, int k,
                                                       int splits, size_t split_stride,
+                                                      const T* __restrict__ resid,
                                                       T* __restrict__ out) {
   const int t = blockIdx.x;
   __shared__ int s_row[MOE_MAX_TOPK];
@@ -474,6 +520,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       a.w = fmaf(g, v.w, a.w);
     }
     T* o = out + (size_t)t * d + 4 * c;
+    if (resid) {   // block wrapper: x + MoE(RMSNorm(x)), one rounding
+      const T* xr = resid + (size_t)t * d + 4 * c;
+      a.x += Elem<T>::to_f32(xr[0]);
+      a.y += Elem<T>::to_f32(xr[1]);
+      a.z += Elem<T>::to_f32(xr[2]);
+      a.w += Elem<T>::to_f32(xr[3]);
+    }
     o[0] = Elem<T>::from_f32(a.x);
     o[1] = Elem<T>::from_f32(a.y);
     o[2] = Elem<T>::from_f32(a.z);
@@ -482,21 +535,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
+void launch_rmsnorm(const Dims& D, const void* x, const float* weight, float eps, float* rs,
+                    void* xn, hipStream_t s) {
+  if (D.bf16)
+    rmsnorm_kernel<bf16_t><<<D.T, 256, 0, s>>>((const bf16_t*)x, weight, eps, D.d, rs,
+                                                (bf16_t*)xn);
+  else
+    rmsnorm_kernel<float><<<D.T, 256, 0, s>>>((const float*)x, weight, eps, D.d, rs, (float*)xn);
+}
+
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
                    int32_t* idx, float* w, int32_t* blk_counts, float* part, float* blk_prob,
-                   hipStream_t s) {
+                   const float* gamma, const float* rs, hipStream_t s) {
   const dim3 grid(D.nblk, D.router_splits);
   if (D.bf16)
     router_topk_kernel<bf16_t><<<grid, kRouterMfmaThreads, 0, s>>>(
         (const bf16_t*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts,
-        blk_prob);
+        blk_prob, gamma, rs);
   else
     router_topk_kernel<float><<<grid, kRouterMfmaThreads, 0, s>>>(
         (const float*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts,
-        blk_prob);
+        blk_prob, gamma, rs);
   if (D.router_splits > 1)
     router_select_kernel<<<D.nblk, kSelectThreads, 0, s>>>(
-        part, bias, D.T, D.E, D.k, D.router_splits, idx, w, blk_counts, blk_prob);
+        part, bias, D.T, D.E, D.k, D.router_splits, idx, w, blk_counts, blk_prob, rs);
 }
 
 int router_splits_for(int nblk, int d) {
@@ -535,15 +597,30 @@ void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int3
         (float*)xs);
 }
 
+__global__ void empty_stats_kernel(int E, int32_t* counts_out, float* prob_out,
+                                   float* loss_out) {
+  const int e = threadIdx.x;
+  if (e < E) {
+    if (counts_out) counts_out[e] = 0;
+    if (prob_out) prob_out[e] = 0.f;
+  }
+  if (e == 0 && loss_out) *loss_out = 0.f;
+}
+
+void launch_empty_stats(int E, int32_t* counts_out, float* prob_out, float* loss_out,
+                        hipStream_t s) {
+  empty_stats_kernel<<<1, 64, 0, s>>>(E, counts_out, prob_out, loss_out);
+}
+
 void launch_combine(const Dims& D, const float* y, const int32_t* tok_row, const float* w,
-                    void* out, hipStream_t s) {
+                    const void* resid, void* out, hipStream_t s) {
   const size_t stride = (size_t)D.max_rows * D.d;
   if (D.bf16)
     combine_kernel<bf16_t><<<D.T, 256, 0, s>>>(y, tok_row, w, D.d, D.k, D.down_splits, stride,
-                                                (bf16_t*)out);
+                                                (const bf16_t*)resid, (bf16_t*)out);
   else
     combine_kernel<float><<<D.T, 256, 0, s>>>(y, tok_row, w, D.d, D.k, D.down_splits, stride,
-                                               (float*)out);
+                                               (const float*)resid, (float*)out);
 }
 
 }  // namespace moe

@@ -29,7 +29,7 @@ from typing import Optional
 
 import numpy as np
 
-X_ID, ROUTER_ID, GATE_ID, UP_ID, DOWN_ID = 0, 1, 2, 3, 4
+X_ID, ROUTER_ID, GATE_ID, UP_ID, DOWN_ID, NORM_ID = 0, 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -141,4 +141,24 @@ def make_inputs(cfg: MoEConfig, seed: int = 0, threads: Optional[int] = None,
             res["W_gate"] = _draw_stack(seed, GATE_ID, E, (f, d), 1.0 / np.sqrt(d), bf16, pool)
             res["W_up"] = _draw_stack(seed, UP_ID, E, (f, d), 1.0 / np.sqrt(d), bf16, pool)
             res["W_down"] = _draw_stack(seed, DOWN_ID, E, (d, f), 1.0 / np.sqrt(f), bf16, pool)
+    return res
+
+
+def make_block_inputs(cfg: MoEConfig, seed: int = 0, threads: Optional[int] = None) -> dict:
+    """make_inputs plus what the normalised block needs, with x given the
+    spread of scales a residual stream has:
+      x            rows of N(0, 1) scaled by 2**u, u ~ U(-4, 4) per token (the
+                   scale is a power of two, so bf16 rows stay exact)
+      norm_weight  [d_model] float32, 1 + 0.25 * N(0, 1)
+    """
+    res = make_inputs(cfg, seed, threads)
+    g = _stream(seed, NORM_ID, 0)
+    u = np.floor(g.uniform(-4.0, 4.0, size=cfg.T)).astype(np.int32)
+    scale = np.ldexp(np.float32(1.0), u).astype(np.float32)[:, None]
+    if res["x"].dtype == np.uint16:
+        res["x"] = f32_to_bf16_bits(bf16_bits_to_f32(res["x"]) * scale)
+    else:
+        res["x"] = (res["x"] * scale).astype(np.float32)
+    res["norm_weight"] = (1.0 + 0.25 * g.standard_normal(cfg.d_model, dtype=np.float32)
+                          ).astype(np.float32)
     return res

@@ -43,9 +43,10 @@ def upload(inp: dict, device="cuda") -> dict:
     return {k: (dev_tensor(v, device) if v is not None else None) for k, v in inp.items()}
 
 
-def run_gpu(cfg: MoEConfig, dinp: dict, *, device="cuda", keep_ws=True) -> dict:
+def run_gpu(cfg: MoEConfig, dinp: dict, *, device="cuda", keep_ws=True, block_eps=None) -> dict:
     """One forward through the C ABI with a caller workspace; returns host
-    copies of out, routing outputs and (keep_ws) the workspace intermediates."""
+    copies of out, routing outputs and (keep_ws) the workspace intermediates.
+    block_eps given: the normalised block (dinp["norm_weight"], that eps)."""
     T, d, f, E, k = cfg.T, cfg.d_model, cfg.d_ff, cfg.E, cfg.k
     dt = moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32
     lay = moe.moe_ffn_workspace_layout(T, d, f, E, k, dt)
@@ -55,7 +56,9 @@ def run_gpu(cfg: MoEConfig, dinp: dict, *, device="cuda", keep_ws=True) -> dict:
     cnt = torch.full((E,), -7, dtype=torch.int32, device=device)
     out = moe.forward(dinp["x"], dinp["W_router"], dinp["W_gate"], dinp["W_up"], dinp["W_down"],
                       k, bias=dinp.get("bias"), workspace=ws, topk_idx=idx, topk_w=w,
-                      expert_counts=cnt)
+                      expert_counts=cnt,
+                      norm_weight=dinp["norm_weight"] if block_eps is not None else None,
+                      eps=block_eps if block_eps is not None else 0.0)
     torch.cuda.synchronize()
     res = dict(out=to_host(out), idx=idx.cpu().numpy(), w=w.cpu().numpy(),
                counts=cnt.cpu().numpy(), layout=lay)
@@ -68,6 +71,12 @@ def run_gpu(cfg: MoEConfig, dinp: dict, *, device="cuda", keep_ws=True) -> dict:
             num_tiles=int(i32(lay.num_tiles, 1)[0]),
             tile_expert=i32(lay.tile_expert, R // lay.block_rows),
             row_token=i32(lay.row_token, R), tok_row=i32(lay.tok_row, T * k).reshape(T, k))
+        if block_eps is not None:
+            res["norm_rs"] = ws[lay.norm_rs:lay.norm_rs + 4 * T].view(torch.float32).cpu().numpy()
+            es = 2 if cfg.dtype == "bf16" else 4
+            b = ws[lay.xn:lay.xn + es * T * d]
+            res["xn"] = (b.view(torch.int16).cpu().numpy().view(np.uint16) if es == 2
+                         else b.view(torch.float32).cpu().numpy()).reshape(T, d)
         res["_ws"] = ws
     return res
 

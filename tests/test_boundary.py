@@ -43,7 +43,6 @@ def fwd(T=16, d=256, f=512, E=8, k=2, opts=None, ptrs=None):
 @pytest.mark.parametrize("kw,status", [
     (dict(k=9, E=8), B.MOE_ERR_INVALID_ARG),
     (dict(k=0), B.MOE_ERR_INVALID_ARG),
-    (dict(T=0), B.MOE_ERR_INVALID_ARG),
     (dict(T=-5), B.MOE_ERR_INVALID_ARG),
     (dict(E=65, k=2), B.MOE_ERR_UNSUPPORTED),
     (dict(E=16, k=9), B.MOE_ERR_UNSUPPORTED),
@@ -104,8 +103,10 @@ def test_workspace_layout_is_consistent():
                   ("offsets", 4 * (E + 1)), ("num_tiles", 4),
                   ("tile_expert", 4 * lay.max_rows // BT), ("row_token", 4 * lay.max_rows),
                   ("tok_row", 4 * T * k), ("xs", es * lay.max_rows * d),
-                  ("h", es * lay.max_rows * f), ("y", 4 * lay.down_splits * lay.max_rows * d)]
-        assert lay.router_partial >= lay.y + 4 * lay.down_splits * lay.max_rows * d
+                  ("h", es * lay.max_rows * f), ("y", 4 * lay.down_splits * lay.max_rows * d),
+                  ("block_probs", 4 * lay.router_blocks * E), ("norm_rs", 4 * T),
+                  ("xn", es * T * d)]
+        assert lay.router_partial >= lay.xn + es * T * d
         assert lay.router_partial <= lay.total
         spans = sorted((getattr(lay, n), getattr(lay, n) + size) for n, size in fields)
         for (a0, a1), (b0, _) in zip(spans, spans[1:]):
@@ -125,3 +126,39 @@ def test_workspace_layout_is_consistent():
 def test_opts_defaults():
     o = moe.moe_opts_init()
     assert o.dtype == B.MOE_BF16 and not o.stream and not o.workspace and not o.router_bias
+
+
+def test_empty_batch_is_a_no_op():
+    # T = 0 reads no tensor: null pointers are fine, and with no statistics
+    # requested the call makes no HIP call at all (so it runs without a GPU)
+    assert moe.moe_ffn_forward(None, None, None, None, None, None, 0, 256, 512, 8, 2, None) \
+        == B.MOE_OK
+    assert moe.moe_block_forward(None, DUMMY, 1e-5, None, None, None, None, None, 0, 256, 512,
+                                 8, 2, None) == B.MOE_OK
+    # the other sizes are still checked
+    assert moe.moe_ffn_forward(None, None, None, None, None, None, 0, 100, 512, 8, 2, None) \
+        == B.MOE_ERR_UNSUPPORTED
+    assert moe.moe_ffn_workspace_size(0, 256, 512, 8, 2, B.MOE_BF16) == \
+        moe.moe_ffn_workspace_size(1, 256, 512, 8, 2, B.MOE_BF16)
+
+
+def blk(norm=DUMMY, eps=1e-5, ptrs=None, T=16, opts=None):
+    p = ptrs or [DUMMY * (i + 1) for i in range(6)]
+    return moe.moe_block_forward(p[0], norm, eps, *p[1:], T, 256, 512, 8, 2, opts)
+
+
+def test_block_forward_validation():
+    assert blk(norm=None) == B.MOE_ERR_INVALID_ARG
+    assert "norm_weight" in moe.moe_last_error()
+    assert blk(norm=DUMMY + 2) == B.MOE_ERR_INVALID_ARG
+    for eps in (-1e-6, 1.5, float("nan")):
+        assert blk(eps=eps) == B.MOE_ERR_INVALID_ARG
+    p = [DUMMY * (i + 1) for i in range(6)]
+    p[5] = p[0]                                     # out aliases x
+    assert blk(ptrs=p) == B.MOE_ERR_INVALID_ARG
+    assert "alias" in moe.moe_last_error()
+    assert blk(T=-1) == B.MOE_ERR_INVALID_ARG
+    for i in range(6):
+        q = [DUMMY * (j + 1) for j in range(6)]
+        q[i] = None
+        assert blk(ptrs=q) == B.MOE_ERR_INVALID_ARG

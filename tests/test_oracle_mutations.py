@@ -47,7 +47,20 @@ def router_transposed(x, W_router, bias=None):
     return om.to_f64(x) @ W.reshape(W.shape[1], W.shape[0]).T
 
 
+def rms_mean_abs(x, weight, eps):
+    xf = om.to_f64(x)
+    return xf / (np.abs(xf).mean(axis=1, keepdims=True) + eps) * om.to_f64(weight)[None, :]
+
+
+def rms_centred(x, weight, eps):
+    xf = om.to_f64(x)
+    return (xf - xf.mean(axis=1, keepdims=True)) / np.sqrt(xf.var(axis=1, keepdims=True) + eps) \
+        * om.to_f64(weight)[None, :]
+
+
 MUTANTS = {
+    "rms_norm:mean_abs": ("rms_norm", rms_mean_abs, [pins.test_rms_norm_closed_forms]),
+    "rms_norm:centred": ("rms_norm", rms_centred, [pins.test_rms_norm_closed_forms]),
     "swiglu_expert:swapped_gate_up": ("swiglu_expert", swapped_gate_up,
                                       [pins.test_expert_scalar_worked_example]),
     "swiglu_expert:down_not_transposed": ("swiglu_expert", down_not_transposed,

@@ -334,3 +334,38 @@ def test_mixtral_parameter_counts_from_the_page():
     assert abs(p_attn + g["k"] * p_ffn - g["P_active"]) / g["P_active"] < 0.01
     # one layer's 8 bf16 experts: about 2.8 GB
     assert 8 * per_layer * 2 == pytest.approx(2.818e9, rel=1e-3)
+
+
+# ---------------------------------------------------------------- block wrapper
+def test_rms_norm_closed_forms():
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((6, 16)) * 3
+    w = np.ones(16)
+    y = oracle.rms_norm(x, w, 0.0)
+    np.testing.assert_allclose((y * y).mean(axis=1), 1.0, rtol=1e-14)   # unit RMS
+    np.testing.assert_allclose(oracle.rms_norm(7.5 * x, w, 0.0), y, rtol=1e-14)  # scale-free
+    # a constant row c*1: every entry is c / sqrt(c^2 + eps), times the weight
+    c, eps = -2.0, 0.25
+    wv = np.arange(1, 5, dtype=np.float64)
+    np.testing.assert_allclose(oracle.rms_norm(np.full((1, 4), c), wv, eps)[0],
+                               c / math.sqrt(c * c + eps) * wv, rtol=1e-15)
+    # brute force on one row
+    row = x[2]
+    ms = sum(v * v for v in row) / len(row)
+    np.testing.assert_allclose(oracle.rms_norm(x[2:3], w * 0.5, 1e-3)[0],
+                               [v / math.sqrt(ms + 1e-3) * 0.5 for v in row], rtol=1e-13)
+
+
+def test_block_residual_and_composition():
+    rng = np.random.default_rng(16)
+    x, Wr, Wg, Wu, Wd = rand_layer(rng, T=7, d=6, f=5, E=4)
+    g = rng.standard_normal(6)
+    # zero down projection: the block is the identity (residual only)
+    r0 = oracle.block_forward(x, g, 1e-5, Wr, Wg, Wu, np.zeros_like(Wd), 2)
+    np.testing.assert_array_equal(r0["out"], x)
+    # otherwise x + the layer applied to the normalised tokens
+    r = oracle.block_forward(x, g, 1e-5, Wr, Wg, Wu, Wd, 2)
+    xn = np.array([[v / math.sqrt(sum(u * u for u in row) / 6 + 1e-5) * g[j]
+                    for j, v in enumerate(row)] for row in x])
+    np.testing.assert_allclose(r["out"], x + dense_keep_topk_layer(xn, Wr, Wg, Wu, Wd, 2),
+                               rtol=1e-11, atol=1e-13)
