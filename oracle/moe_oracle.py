@@ -33,6 +33,11 @@ optional per-expert router bias (an extension the pages do not have) is added
 to the scores before both the selection and the softmax; every token is
 routed to exactly k experts (no capacity limit or token dropping).
 
+* "Mixtral of Experts" (singularity-lens.com), its list of limitations, the
+  item on memory requirements and offloading: the model needs INT4
+  quantisation to fit in about 25-30 GB.  The pages give no scheme; the plain
+  weight-only symmetric per-group reading is taken (quantize_int4 below).
+
 Parity pins: every function here is pinned by tests/test_oracle_pins.py
 against closed forms, brute force and special cases fixed by the pages.
 """
@@ -245,3 +250,74 @@ def expert_param_count(d_model: int, d_ff: int) -> int:
     """Parameters of one SwiGLU expert: W1, W3 (d_ff x d_model) and W2
     (d_model x d_ff), "各エキスパートの構造"."""
     return 3 * d_model * d_ff
+
+
+# ----------------------------------------------------------------------------
+# weight-only INT4 expert weights
+# ----------------------------------------------------------------------------
+
+INT4_QMAX = 7          # largest code magnitude used by the scale
+INT4_OFFSET = 8        # stored nibble = code + 8, codes in [-8, 7]
+
+
+def _as_f32(W) -> np.ndarray:
+    """bf16 bit patterns (uint16) or float arrays -> float32, exactly."""
+    W = np.asarray(W)
+    if W.dtype == np.uint16:
+        return (W.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return W.astype(np.float32)
+
+
+def quantize_int4(W, group: int):
+    """Weight-only INT4 quantisation of a weight matrix (any leading shape,
+    last axis = the input features K) in groups of `group` consecutive input
+    features of one row.
+
+    "Mixtral of Experts" (limitations, memory item) names INT4 quantisation
+    without a scheme; the reading taken is symmetric per group:
+        s   = max_{k in group} |w_k| / 7                  (float32)
+        q_k = clamp(rint(w_k / s), -8, 7), q_k = 0 if s = 0 (float32 division,
+                                                           ties to even)
+    The scale and every code are decided in float32 (the precision of the
+    stored scale), so any implementation that divides with IEEE rounding
+    reaches the same codes.  Storage: nibble u = q + 8; element 2b of a row in
+    the low nibble of byte b and element 2b + 1 in the high nibble.
+
+    Returns (packed uint8 [..., K/2], scales float32 [..., K/group])."""
+    Wf = _as_f32(W)
+    K = Wf.shape[-1]
+    if K % group or K % 2:
+        raise ValueError("K must be a multiple of the group size and even")
+    G = Wf.reshape(Wf.shape[:-1] + (K // group, group))
+    absmax = np.abs(G).max(axis=-1)                                 # exact in f32
+    scale = (absmax / np.float32(INT4_QMAX)).astype(np.float32)    # one f32 rounding
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    ratio = (G / safe[..., None]).astype(np.float32)                 # one f32 rounding
+    q = np.clip(np.rint(ratio), -INT4_OFFSET, INT4_QMAX)
+    q = np.where(scale[..., None] > 0, q, 0).astype(np.int64)
+    u = (q + INT4_OFFSET).reshape(Wf.shape).astype(np.uint8)
+    packed = (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+    return packed, scale
+
+
+def dequantize_int4(packed, scales, group: int) -> np.ndarray:
+    """fp64 weights s * q from quantize_int4's storage (exact: s is float32
+    and q a small integer)."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    lo = (packed & 0x0F).astype(np.int64) - INT4_OFFSET
+    hi = (packed >> 4).astype(np.int64) - INT4_OFFSET
+    q = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.int64)
+    q[..., 0::2] = lo
+    q[..., 1::2] = hi
+    s = np.repeat(np.asarray(scales, dtype=np.float64), group, axis=-1)
+    return q.astype(np.float64) * s
+
+
+def moe_forward_int4(x, W_router, qweights: dict, group: int, k, bias=None, tokens=None,
+                     forced_idx=None) -> dict:
+    """The layer with INT4 expert weights: moe_forward on the dequantized
+    weights s * q.  qweights holds (packed, scales) for "W_gate", "W_up" and
+    "W_down" as quantize_int4 returns them."""
+    W = {n: dequantize_int4(*qweights[n], group) for n in ("W_gate", "W_up", "W_down")}
+    return moe_forward(x, W_router, W["W_gate"], W["W_up"], W["W_down"], k, bias=bias,
+                       tokens=tokens, forced_idx=forced_idx)

@@ -58,7 +58,41 @@ def rms_centred(x, weight, eps):
         * om.to_f64(weight)[None, :]
 
 
+def _q4_variant(nibble_swap=False, scale_div=7.0, half_away=False):
+    def q4(W, group):
+        Wf = om._as_f32(W)
+        K = Wf.shape[-1]
+        G = Wf.reshape(Wf.shape[:-1] + (K // group, group))
+        scale = (np.abs(G).max(axis=-1) / np.float32(scale_div)).astype(np.float32)
+        safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+        r = (G / safe[..., None]).astype(np.float32)
+        q = np.sign(r) * np.floor(np.abs(r) + 0.5) if half_away else np.rint(r)
+        q = np.where(scale[..., None] > 0, np.clip(q, -8, 7), 0).astype(np.int64)
+        u = (q + 8).reshape(Wf.shape).astype(np.uint8)
+        a, b = (u[..., 1::2], u[..., 0::2]) if nibble_swap else (u[..., 0::2], u[..., 1::2])
+        return (a | (b << 4)).astype(np.uint8), scale
+    return q4
+
+
+def deq4_no_offset(packed, scales, group):
+    packed = np.asarray(packed, dtype=np.uint8)
+    q = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.int64)
+    q[..., 0::2] = packed & 15
+    q[..., 1::2] = packed >> 4
+    return q * np.repeat(np.asarray(scales, dtype=np.float64), group, axis=-1)
+
+
 MUTANTS = {
+    "quantize_int4:nibbles_swapped": ("quantize_int4", _q4_variant(nibble_swap=True),
+                                      [pins.test_int4_worked_example]),
+    "quantize_int4:scale_over_8": ("quantize_int4", _q4_variant(scale_div=8.0),
+                                   [pins.test_int4_exact_recovery,
+                                    pins.test_int4_error_bound_and_range]),
+    "quantize_int4:round_half_away": ("quantize_int4", _q4_variant(half_away=True),
+                                      [pins.test_int4_worked_example]),
+    "dequantize_int4:no_offset": ("dequantize_int4", deq4_no_offset,
+                                  [pins.test_int4_exact_recovery,
+                                   pins.test_int4_error_bound_and_range]),
     "rms_norm:mean_abs": ("rms_norm", rms_mean_abs, [pins.test_rms_norm_closed_forms]),
     "rms_norm:centred": ("rms_norm", rms_centred, [pins.test_rms_norm_closed_forms]),
     "swiglu_expert:swapped_gate_up": ("swiglu_expert", swapped_gate_up,
@@ -86,3 +120,14 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
     if attr in ("swiglu_expert", "silu", "topk_gates"):
         with pytest.raises(Exception):
             pins.test_layer_equals_dense_keep_topk_formulation(4, 2)
+
+
+def test_int4_mutant_base_is_the_oracle():
+    # the INT4 mutants differ from the oracle only by the planted mistake
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((5, 64)).astype(np.float32)
+    for g in (32, 64):
+        p0, s0 = oracle.quantize_int4(W, g)
+        p1, s1 = _q4_variant()(W, g)
+        np.testing.assert_array_equal(p0, p1)
+        np.testing.assert_array_equal(s0, s1)

@@ -369,3 +369,108 @@ def test_block_residual_and_composition():
                     for j, v in enumerate(row)] for row in x])
     np.testing.assert_allclose(r["out"], x + dense_keep_topk_layer(xn, Wr, Wg, Wu, Wd, 2),
                                rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- INT4 weights
+# "Mixtral of Experts" (limitations, memory item) names INT4 quantisation of
+# the weights; the reading is symmetric per-group absmax with codes offset by
+# 8, two per byte, element 2b in the low nibble.
+
+def test_int4_worked_example():
+    # one group of 8: absmax 7 -> s = 1; q = w rounded to nearest, ties to
+    # even (3.5 -> 4, -2.5 -> -2); nibble = q + 8; byte b = elements 2b
+    # (low nibble) and 2b + 1 (high nibble):
+    #   q = [0, 7, -7, 4, 1, -1, 2, -2] -> u = [8, 15, 1, 12, 9, 7, 10, 6]
+    #   bytes = 0xF8, 0xC1, 0x79, 0x6A
+    W = np.array([[0.0, 7.0, -7.0, 3.5, 1.0, -1.0, 2.0, -2.5]], dtype=np.float32)
+    packed, scale = oracle.quantize_int4(W, 8)
+    assert packed.dtype == np.uint8 and packed.tolist() == [[0xF8, 0xC1, 0x79, 0x6A]]
+    assert scale.dtype == np.float32 and scale.tolist() == [[1.0]]
+    np.testing.assert_array_equal(oracle.dequantize_int4(packed, scale, 8),
+                                  [[0, 7, -7, 4, 1, -1, 2, -2]])
+    # a second group with its own scale: [-5, 4, -2, 2, 7, -14, 14, 0] has
+    # absmax 14 -> s = 2, q = [-2, 2, -1, 1, 4, -7, 7, 0] (-2.5 -> -2,
+    # 3.5 -> 4), u = [6, 10, 7, 9, 12, 1, 15, 8] -> 0xA6, 0x97, 0x1C, 0x8F
+    W2 = np.concatenate([W, 2 * W[:, ::-1]], axis=1)
+    p2, s2 = oracle.quantize_int4(W2, 8)
+    assert s2.tolist() == [[1.0, 2.0]]
+    assert p2[0].tolist() == [0xF8, 0xC1, 0x79, 0x6A, 0xA6, 0x97, 0x1C, 0x8F]
+    np.testing.assert_array_equal(oracle.dequantize_int4(p2, s2, 8)[0, 8:],
+                                  2 * np.array([-2, 2, -1, 1, 4, -7, 7, 0]))
+
+
+def test_int4_exact_recovery():
+    # weights that are exactly s * q with |q| = 7 present in every group come
+    # back unchanged: s = 7s / 7 and w / s = q hold exactly in float32
+    rng = np.random.default_rng(21)
+    rows, K, g = 6, 96, 32
+    q = rng.integers(-7, 8, size=(rows, K // g, g))
+    q[..., 0] = rng.choice([-7, 7], size=(rows, K // g))
+    s = (np.ldexp(1.0, rng.integers(-12, 3, size=(rows, K // g))) *
+         (1 + rng.integers(0, 16, size=(rows, K // g)) / 16)).astype(np.float32)
+    W = (q * s[..., None]).reshape(rows, K).astype(np.float32)
+    packed, scale = oracle.quantize_int4(W, g)
+    np.testing.assert_array_equal(scale, s)
+    np.testing.assert_array_equal(oracle.dequantize_int4(packed, scale, g), W)
+    lo = (packed & 15).astype(int) - 8
+    np.testing.assert_array_equal(lo, q.reshape(rows, K)[:, 0::2])
+
+
+def test_int4_error_bound_and_range():
+    rng = np.random.default_rng(22)
+    W = rng.standard_normal((16, 256)).astype(np.float32) * 0.05
+    W[3, :64] *= 100.0                                # one loud group
+    for g in (32, 128, 256):
+        packed, scale = oracle.quantize_int4(W, g)
+        deq = oracle.dequantize_int4(packed, scale, g)
+        srep = np.repeat(scale.astype(np.float64), g, axis=1)
+        assert (np.abs(W - deq) <= srep * (0.5 + 1e-6)).all()     # round to nearest
+        codes = np.stack([(packed & 15), (packed >> 4)], -1).reshape(W.shape).astype(int) - 8
+        assert codes.min() >= -8 and codes.max() <= 7
+        # the element of largest magnitude of every group maps to +-7
+        G = np.abs(codes).reshape(16, -1, g).max(axis=-1)
+        assert (G == 7).all()
+        # scale = absmax / 7 rounded once to float32
+        am = np.abs(W).reshape(16, -1, g).max(axis=-1)
+        np.testing.assert_array_equal(scale, (am / np.float32(7)).astype(np.float32))
+
+
+def test_int4_zero_group_and_bf16_input():
+    W = np.zeros((2, 64), dtype=np.float32)
+    W[1, 32:] = np.linspace(-1, 1, 32)
+    packed, scale = oracle.quantize_int4(W, 32)
+    assert scale[0].tolist() == [0.0, 0.0] and scale[1, 0] == 0.0
+    assert (packed[0] == 0x88).all() and (packed[1, :16] == 0x88).all()
+    # bf16 bit patterns quantize as the float32 values they encode
+    bits = (W.view(np.uint32) >> 16).astype(np.uint16)           # truncated to bf16
+    Wb = (bits.astype(np.uint32) << 16).view(np.float32)
+    pb, sb = oracle.quantize_int4(bits, 32)
+    pf, sf = oracle.quantize_int4(Wb, 32)
+    np.testing.assert_array_equal(pb, pf)
+    np.testing.assert_array_equal(sb, sf)
+
+
+def test_int4_layer_on_representable_weights_equals_plain_layer():
+    # when every expert weight is exactly s * q, the INT4 layer is the plain
+    # layer on those weights
+    rng = np.random.default_rng(23)
+    T, d, f, E, k, g = 9, 64, 32, 4, 2, 32
+    x = rng.standard_normal((T, d))
+    Wr = rng.standard_normal((d, E)) / 8
+
+    def rep(shape, K):
+        q = rng.integers(-7, 8, size=shape[:-1] + (K // g, g))
+        q[..., 0] = 7
+        s = np.ldexp(1.0, rng.integers(-8, -2, size=shape[:-1] + (K // g,))).astype(np.float32)
+        return (q * s[..., None]).reshape(shape).astype(np.float32)
+
+    Wg, Wu, Wd = rep((E, f, d), d), rep((E, f, d), d), rep((E, d, f), f)
+    qw = {n: oracle.quantize_int4(W, g) for n, W in (("W_gate", Wg), ("W_up", Wu),
+                                                      ("W_down", Wd))}
+    r4 = oracle.moe_forward_int4(x, Wr, qw, g, k)
+    r = oracle.moe_forward(x, Wr, Wg, Wu, Wd, k)
+    np.testing.assert_array_equal(r4["idx"], r["idx"])
+    np.testing.assert_allclose(r4["out"], r["out"], rtol=0, atol=1e-12)
+    # and differs when gate and up are exchanged
+    qs = dict(qw, W_gate=qw["W_up"], W_up=qw["W_gate"])
+    assert np.abs(oracle.moe_forward_int4(x, Wr, qs, g, k)["out"] - r["out"]).max() > 1e-3
