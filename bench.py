@@ -39,6 +39,10 @@ def parse():
     p.add_argument("--router-stats", action="store_true",
                    help="also produce the router statistics p_i and the load-balancing loss "
                         "in every step")
+    p.add_argument("--weights", default="bf16", choices=("bf16", "int4"),
+                   help="expert weights as given (bf16) or INT4 with per-group float32 "
+                        "scales (quantized on the GPU before warmup)")
+    p.add_argument("--group", type=int, default=128, help="INT4 scale group size")
     p.add_argument("--block", action="store_true",
                    help="time the normalised block out = x + layer(RMSNorm(x)) instead of "
                         "the bare layer")
@@ -48,19 +52,21 @@ def parse():
     return p.parse_args()
 
 
-def algorithmic_work(cfg, counts):
+def algorithmic_work(cfg, counts, group=0):
     """Per-step bytes the method must move and flops it must do (no padding,
     no intermediates, only the experts that received tokens), and the same
-    per kernel for the two GEMMs."""
+    per kernel for the two GEMMs.  group > 0: INT4 expert weights (half a
+    byte per weight plus one float32 scale per group)."""
     w = 2 if cfg.dtype == "bf16" else 4
     T, d, f, E, k = cfg.T, cfg.d_model, cfg.d_ff, cfg.E, cfg.k
     A = T * k
     touched = int((counts > 0).sum())
-    layer_bytes = touched * 3 * d * f * w + 2 * T * d * w + d * E * 4
+    ww = (0.5 + 4.0 / group) if group else w        # bytes per expert weight
+    layer_bytes = touched * 3 * d * f * ww + 2 * T * d * w + d * E * 4
     layer_flops = 2 * A * 3 * d * f + 2 * T * d * E
-    gateup_bytes = touched * 2 * d * f * w + A * d * w + A * f * w
+    gateup_bytes = touched * 2 * d * f * ww + A * d * w + A * f * w
     gateup_flops = 2 * A * 2 * d * f
-    down_bytes = touched * d * f * w + A * f * w + A * d * 4
+    down_bytes = touched * d * f * ww + A * f * w + A * d * 4
     down_flops = 2 * A * d * f
     return dict(touched=touched, layer_bytes=layer_bytes, layer_flops=layer_flops,
                 gateup=(gateup_bytes, gateup_flops), down=(down_bytes, down_flops))
@@ -77,7 +83,9 @@ def measured_traffic(workload, kernel, variant):
             rec = json.load(fh)[workload][kernel]
     except (OSError, KeyError, ValueError):
         return None
-    files = prof_summary.KERNEL_SOURCES[kernel][variant]
+    files = prof_summary.KERNEL_SOURCES.get(kernel, {}).get(variant)
+    if files is None:
+        return None
     if rec.get("source_files") != files or rec.get("source_sha256") != prof_summary.source_hash(files):
         return None
     return rec["bytes"]
@@ -133,6 +141,16 @@ def main():
     d = {k: up(v) for k, v in inp.items()}
     T, E, k = cfg.T, cfg.E, cfg.k
     dt = moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32
+    int4 = args.weights == "int4"
+    if int4:
+        if cfg.dtype != "bf16" or args.block:
+            print("INT4 weights take bf16 activations and the bare layer", file=sys.stderr)
+            sys.exit(2)
+        dt = moe.MOE_W4A16
+        q = {n: moe.quantize_int4(d[n], args.group) for n in ("W_gate", "W_up", "W_down")}
+        for n in ("W_gate", "W_up", "W_down"):
+            del d[n]                   # only the INT4 copies stay resident
+        torch.cuda.synchronize()
     ws = torch.empty(moe.moe_ffn_workspace_size(T, cfg.d_model, cfg.d_ff, E, k, dt),
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(d["x"])
@@ -142,6 +160,12 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(events=None):
+        if int4:
+            moe.forward_int4(d["x"], d["W_router"], q["W_gate"], q["W_up"], q["W_down"],
+                             args.group, k, bias=d["bias"], out=out, workspace=ws,
+                             expert_counts=counts, stream=stream, stage_events=events,
+                             router_probs=probs, balance_loss=bloss)
+            return
         moe.forward(d["x"], d["W_router"], d["W_gate"], d["W_up"], d["W_down"], k,
                     bias=d["bias"], out=out, workspace=ws, expert_counts=counts, stream=stream,
                     stage_events=events, router_probs=probs, balance_loss=bloss,
@@ -185,7 +209,7 @@ def main():
              for i, name in enumerate(STAGE_NAMES)}
 
     cnt = counts.cpu().numpy()
-    work = algorithmic_work(cfg, cnt)
+    work = algorithmic_work(cfg, cnt, args.group if int4 else 0)
     gateup_bytes, gateup_flops = work["gateup"]
     gu_s = split["gateup"] * 1e-3
     if cfg.dtype == "f32":
@@ -199,7 +223,8 @@ def main():
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     variant = moe.moe_ffn_workspace_layout(T, cfg.d_model, cfg.d_ff, E, k, dt).gemm_variant
-    roof["traffic"] = measured_traffic(cfg.name, "gateup", "tile" if variant == 1 else "stream")
+    form = ("q4" if variant == 0 else "q4tile") if int4 else ("tile" if variant == 1 else "stream")
+    roof["traffic"] = measured_traffic(cfg.name + ("_int4" if int4 else ""), "gateup", form)
     roof["kernel"] = "gateup"
     roof["kernel_ms"] = split["gateup"]
 
@@ -220,6 +245,7 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d_model": cfg.d_model, "d_ff": cfg.d_ff,
                    "E": E, "k": k, "router_bias": cfg.router_bias, "seed": args.seed,
                    "block": bool(args.block),
+                   "weights": f"int4 (group {args.group}, fp32 scales)" if int4 else cfg.dtype,
                    "parallelism": "single GPU"},
         "layer": {"GB/s": work["layer_bytes"] / secs / 1e9,
                   "hbm_frac": work["layer_bytes"] / secs / 1e9 / HBM_PEAK_GBS,
@@ -232,7 +258,7 @@ def main():
                          if args.router_stats else None),
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not int4:
         n = args.cpu_sample_tokens or {"tiny": 64, "decode": 16}.get(cfg.name, 64)
         print(f"[bench] cpu baseline on {n} tokens", file=sys.stderr, flush=True)
         record["cpu_baseline"] = cpu_baseline(cfg, inp, n, block=args.block)

@@ -51,8 +51,10 @@ typedef enum {
 } moe_status_t;
 
 /* Element type of x, W_gate, W_up, W_down and out.  W_router, the bias and
- * all accumulation are always float32. */
-typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype_t;
+ * all accumulation are always float32.  MOE_W4A16 names the layer of
+ * moe_ffn_forward_int4 (bf16 activations, INT4 expert weights) for the
+ * workspace queries. */
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1, MOE_W4A16 = 2 } moe_dtype_t;
 
 /* Limits (checked; MOE_ERR_UNSUPPORTED beyond them). */
 #define MOE_MAX_EXPERTS 64
@@ -130,6 +132,47 @@ int moe_block_forward(const void* x, const float* norm_weight, float eps, const 
                       int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
                       const moe_opts_t* opts);
 
+/*
+ * Weight-only INT4 quantisation of weight rows.  "Mixtral of Experts"
+ * (singularity-lens.com), list of limitations, memory item: the model fits
+ * in about 25-30 GB only with INT4 weights.  The pages fix no scheme; this
+ * library's (symmetric, per group of `group` consecutive input features):
+ *   s = max |w| / 7 over the group, q = clamp(rint(w / s), -8, 7), q = 0 when
+ *   s = 0, both decided in float32 with IEEE division and ties to even;
+ *   the weight stands for s * q.
+ *   W       [rows][K] dtype (MOE_BF16 or MOE_F32), device, 16-byte aligned
+ *   packed  [rows][K/2] uint8, device, 4-byte aligned (written): nibble
+ *           q + 8; element 2b in the low nibble of byte b, 2b + 1 in the high
+ *   scales  [rows][K/group] float32, device, 4-byte aligned (written)
+ *   group: multiple of 32 dividing K, and either a multiple of 128 or 32/64;
+ *   K a multiple of 128 and at most 65536; rows <= 2^31 - 1.
+ * For an expert stack W_gate [E][d_ff][d_model] pass rows = E * d_ff and
+ * K = d_model (W_down: rows = E * d_model, K = d_ff).  Asynchronous on
+ * `stream` (hipStream_t, NULL = default); validation as moe_ffn_forward.
+ */
+int moe_quantize_int4(const void* W, int32_t dtype, int64_t rows, int64_t K, int32_t group,
+                      uint8_t* packed, float* scales, void* stream);
+
+/*
+ * The layer of moe_ffn_forward with INT4 expert weights as written by
+ * moe_quantize_int4 (each expert matrix s * q); x and out bf16.
+ *   Wg_q, Wu_q [E][d_ff][d_model/2] uint8, Wg_s, Wu_s [E][d_ff][d_model/group]
+ *   Wd_q [E][d_model][d_ff/2] uint8, Wd_s [E][d_model][d_ff/group] float32
+ * (16-byte aligned codes, 4-byte aligned scales); group as for
+ * moe_quantize_int4 and dividing both d_model and d_ff, which must be
+ * multiples of 128.  Few rows per expert (decode): the weight-streaming GEMMs
+ * read the INT4 codes directly.  Many rows: the three stacks are first
+ * dequantized to bf16 into the workspace (layout field wdeq, 6 * E * d_model
+ * * d_ff bytes) and the LDS-tiled GEMMs run on them.  opts->dtype is ignored;
+ * workspace sizes are those of MOE_W4A16.  Other arguments, outputs and
+ * errors as moe_ffn_forward.
+ */
+int moe_ffn_forward_int4(const void* x, const float* W_router, const uint8_t* Wg_q,
+                         const float* Wg_s, const uint8_t* Wu_q, const float* Wu_s,
+                         const uint8_t* Wd_q, const float* Wd_s, int32_t group, void* out,
+                         int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                         const moe_opts_t* opts);
+
 /* Bytes of workspace moe_ffn_forward needs for this shape (0 if the shape is
  * invalid or unsupported; T = 0 is sized as T = 1). */
 size_t moe_ffn_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
@@ -170,6 +213,9 @@ typedef struct moe_ws_layout {
   size_t xn;                /* [T][d_model] dtype: RMS-normalised tokens        */
   size_t router_partial;    /* router scratch: partial scores when the score GEMM
                                is split over d_model (few token blocks)        */
+  size_t wdeq;              /* MOE_W4A16 with the LDS-tiled form only: the three
+                               weight stacks dequantized to bf16, W_gate, W_up,
+                               W_down in their bf16 layouts (else 0 bytes)     */
   size_t total;             /* bytes                                           */
 } moe_ws_layout_t;
 

@@ -313,11 +313,23 @@ def dequantize_int4(packed, scales, group: int) -> np.ndarray:
     return q.astype(np.float64) * s
 
 
+class _Int4Stack:
+    """An expert stack of INT4 weights; indexing expert e gives its
+    dequantized fp64 matrix (one expert at a time, so full-size stacks need
+    no fp64 copy of every expert)."""
+
+    def __init__(self, packed, scales, group):
+        self.packed, self.scales, self.group = packed, scales, group
+
+    def __getitem__(self, e):
+        return dequantize_int4(self.packed[e], self.scales[e], self.group)
+
+
 def moe_forward_int4(x, W_router, qweights: dict, group: int, k, bias=None, tokens=None,
                      forced_idx=None) -> dict:
     """The layer with INT4 expert weights: moe_forward on the dequantized
     weights s * q.  qweights holds (packed, scales) for "W_gate", "W_up" and
     "W_down" as quantize_int4 returns them."""
-    W = {n: dequantize_int4(*qweights[n], group) for n in ("W_gate", "W_up", "W_down")}
+    W = {n: _Int4Stack(*qweights[n], group) for n in ("W_gate", "W_up", "W_down")}
     return moe_forward(x, W_router, W["W_gate"], W["W_up"], W["W_down"], k, bias=bias,
                        tokens=tokens, forced_idx=forced_idx)

@@ -13,9 +13,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_ffn.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_BF16, MOE_F32 = 0, 1
+MOE_BF16, MOE_F32, MOE_W4A16 = 0, 1, 2
 
-EXPORTED = ("moe_opts_init", "moe_ffn_forward", "moe_block_forward", "moe_ffn_workspace_size",
+EXPORTED = ("moe_opts_init", "moe_ffn_forward", "moe_block_forward", "moe_quantize_int4",
+            "moe_ffn_forward_int4", "moe_ffn_workspace_size",
             "moe_ffn_workspace_layout", "moe_status_string", "moe_last_error",
             "moe_release", "moe_version")
 
@@ -46,7 +47,7 @@ class MoeWsLayout(ctypes.Structure):
         (name, ctypes.c_size_t) for name in
         ("topk_idx", "topk_w", "block_counts", "counts", "offsets", "num_tiles",
          "tile_expert", "row_token", "tok_row", "xs", "h", "y", "block_probs", "norm_rs", "xn",
-         "router_partial", "total")]
+         "router_partial", "wdeq", "total")]
 
 
 class MoeError(RuntimeError):
@@ -75,6 +76,11 @@ def lib() -> ctypes.CDLL:
         L.moe_block_forward.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, i64, i64,
                                         i64, i32, i32, ctypes.POINTER(MoeOpts)]
         L.moe_block_forward.restype = ctypes.c_int
+        L.moe_quantize_int4.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
+        L.moe_quantize_int4.restype = ctypes.c_int
+        L.moe_ffn_forward_int4.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64,
+                                           i64, i32, i32, ctypes.POINTER(MoeOpts)]
+        L.moe_ffn_forward_int4.restype = ctypes.c_int
         L.moe_ffn_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
         L.moe_ffn_workspace_size.restype = sz
         L.moe_ffn_workspace_layout.argtypes = [i64, i64, i64, i32, i32, i32,
@@ -114,6 +120,19 @@ def moe_block_forward(x, norm_weight, eps, W_router, W_gate, W_up, W_down, out, 
                                    ctypes.byref(opts) if opts is not None else None)
 
 
+def moe_quantize_int4(W, dtype, rows, K, group, packed, scales, stream=None) -> int:
+    """Raw entry point of the INT4 quantizer."""
+    return lib().moe_quantize_int4(W, dtype, rows, K, group, packed, scales, stream)
+
+
+def moe_ffn_forward_int4(x, W_router, Wg_q, Wg_s, Wu_q, Wu_s, Wd_q, Wd_s, group, out, T,
+                         d_model, d_ff, E, k, opts: Optional[MoeOpts] = None) -> int:
+    """Raw entry point of the layer with INT4 expert weights."""
+    return lib().moe_ffn_forward_int4(x, W_router, Wg_q, Wg_s, Wu_q, Wu_s, Wd_q, Wd_s, group,
+                                      out, T, d_model, d_ff, E, k,
+                                      ctypes.byref(opts) if opts is not None else None)
+
+
 def moe_ffn_workspace_size(T, d_model, d_ff, E, k, dtype=MOE_BF16) -> int:
     return lib().moe_ffn_workspace_size(T, d_model, d_ff, E, k, dtype)
 
@@ -143,6 +162,60 @@ def moe_version() -> str:
 
 
 # ---------------------------------------------------------------- torch marshalling
+def _check(t, shape, dtype, x):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"tensor {tuple(t.shape)} {t.dtype}: expected {tuple(shape)} {dtype}")
+    if not t.is_cuda or not t.is_contiguous() or t.device != x.device:
+        raise ValueError("every tensor must be a contiguous device tensor on x's device")
+
+
+def _opts(x, E, k, dtype, bias, out, workspace, topk_idx, topk_w, expert_counts, stream,
+          stage_events, router_probs, balance_loss):
+    """Checks the common tensors and fills a MoeOpts; returns (opts, out, keepalive)."""
+    import torch
+
+    T, d = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    checks = [(out, (T, d), x.dtype)]
+    if bias is not None:
+        checks.append((bias, (E,), torch.float32))
+    for t, shape in ((topk_idx, (T, k)), (expert_counts, (E,))):
+        if t is not None:
+            checks.append((t, shape, torch.int32))
+    if topk_w is not None:
+        checks.append((topk_w, (T, k), torch.float32))
+    if router_probs is not None:
+        checks.append((router_probs, (E,), torch.float32))
+    if balance_loss is not None:
+        checks.append((balance_loss, (1,), torch.float32))
+    for t, shape, dt in checks:
+        _check(t, shape, dt, x)
+    o = moe_opts_init()
+    o.dtype = dtype
+    st = stream if stream is not None else torch.cuda.current_stream(x.device)
+    o.stream = st.cuda_stream
+    o.router_bias = bias.data_ptr() if bias is not None else None
+    if workspace is not None:
+        if workspace.device != x.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on x's device")
+        o.workspace = workspace.data_ptr()
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
+    o.topk_idx_out = topk_idx.data_ptr() if topk_idx is not None else None
+    o.topk_w_out = topk_w.data_ptr() if topk_w is not None else None
+    o.expert_counts_out = expert_counts.data_ptr() if expert_counts is not None else None
+    o.router_prob_out = router_probs.data_ptr() if router_probs is not None else None
+    o.balance_loss_out = balance_loss.data_ptr() if balance_loss is not None else None
+    arr = None
+    if stage_events is not None:
+        # MOE_NUM_STAGES + 1 created torch.cuda.Event objects (record() once first)
+        if len(stage_events) != MOE_NUM_STAGES + 1:
+            raise ValueError("stage_events needs MOE_NUM_STAGES + 1 events")
+        arr = (ctypes.c_void_p * len(stage_events))(*[ev.cuda_event for ev in stage_events])
+        o.stage_events = ctypes.cast(arr, ctypes.c_void_p)
+    return o, out, arr
+
+
 def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
             workspace=None, topk_idx=None, topk_w=None, expert_counts=None, stream=None,
             stage_events=None, router_probs=None, balance_loss=None, norm_weight=None,
@@ -169,50 +242,14 @@ def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
         dtype = MOE_F32
     else:
         raise TypeError("x must be bfloat16 or float32")
-    checks = [(W_router, (d, E), torch.float32), (W_gate, (E, d_ff, d), x.dtype),
-              (W_up, (E, d_ff, d), x.dtype), (W_down, (E, d, d_ff), x.dtype)]
-    if bias is not None:
-        checks.append((bias, (E,), torch.float32))
-    if out is None:
-        out = torch.empty_like(x)
-    checks.append((out, (T, d), x.dtype))
-    for t, shape in ((topk_idx, (T, k)), (expert_counts, (E,))):
-        if t is not None:
-            checks.append((t, shape, torch.int32))
-    if topk_w is not None:
-        checks.append((topk_w, (T, k), torch.float32))
-    if router_probs is not None:
-        checks.append((router_probs, (E,), torch.float32))
+    _check(x, (T, d), x.dtype, x)
+    for t, shape, dt in ((W_router, (d, E), torch.float32), (W_gate, (E, d_ff, d), x.dtype),
+                         (W_up, (E, d_ff, d), x.dtype), (W_down, (E, d, d_ff), x.dtype)):
+        _check(t, shape, dt, x)
     if norm_weight is not None:
-        checks.append((norm_weight, (d,), torch.float32))
-    if balance_loss is not None:
-        checks.append((balance_loss, (1,), torch.float32))
-    for t, shape, dt in [(x, (T, d), x.dtype)] + checks:
-        if tuple(t.shape) != tuple(shape) or t.dtype != dt:
-            raise ValueError(f"tensor {tuple(t.shape)} {t.dtype}: expected {shape} {dt}")
-        if not t.is_cuda or not t.is_contiguous() or t.device != x.device:
-            raise ValueError("every tensor must be a contiguous device tensor on x's device")
-    o = moe_opts_init()
-    o.dtype = dtype
-    st = stream if stream is not None else torch.cuda.current_stream(x.device)
-    o.stream = st.cuda_stream
-    o.router_bias = bias.data_ptr() if bias is not None else None
-    if workspace is not None:
-        if workspace.device != x.device or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous tensor on x's device")
-        o.workspace = workspace.data_ptr()
-        o.workspace_bytes = workspace.numel() * workspace.element_size()
-    o.topk_idx_out = topk_idx.data_ptr() if topk_idx is not None else None
-    o.topk_w_out = topk_w.data_ptr() if topk_w is not None else None
-    o.expert_counts_out = expert_counts.data_ptr() if expert_counts is not None else None
-    o.router_prob_out = router_probs.data_ptr() if router_probs is not None else None
-    o.balance_loss_out = balance_loss.data_ptr() if balance_loss is not None else None
-    if stage_events is not None:
-        # MOE_NUM_STAGES + 1 created torch.cuda.Event objects (record() once first)
-        if len(stage_events) != MOE_NUM_STAGES + 1:
-            raise ValueError("stage_events needs MOE_NUM_STAGES + 1 events")
-        arr = (ctypes.c_void_p * len(stage_events))(*[ev.cuda_event for ev in stage_events])
-        o.stage_events = ctypes.cast(arr, ctypes.c_void_p)
+        _check(norm_weight, (d,), torch.float32, x)
+    o, out, _keep = _opts(x, E, k, dtype, bias, out, workspace, topk_idx, topk_w,
+                          expert_counts, stream, stage_events, router_probs, balance_loss)
     with torch.cuda.device(x.device):
         if norm_weight is not None:
             status = moe_block_forward(x.data_ptr(), norm_weight.data_ptr(), float(eps),
@@ -224,4 +261,62 @@ def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
                                      d_ff, E, k, o)
     if status != MOE_OK:
         raise MoeError(status, "moe_ffn_forward")
+    return out
+
+
+def quantize_int4(W, group: int = 128, stream=None):
+    """INT4 codes and scales of a bf16 or fp32 device tensor (last axis = the
+    input features K) through moe_quantize_int4.  Returns (packed uint8
+    [..., K/2], scales float32 [..., K/group])."""
+    import torch
+
+    if W.dtype == torch.bfloat16:
+        dtype = MOE_BF16
+    elif W.dtype == torch.float32:
+        dtype = MOE_F32
+    else:
+        raise TypeError("W must be bfloat16 or float32")
+    if not W.is_cuda or not W.is_contiguous():
+        raise ValueError("W must be a contiguous device tensor")
+    K = W.shape[-1]
+    rows = W.numel() // K
+    packed = torch.empty(W.shape[:-1] + (K // 2,), dtype=torch.uint8, device=W.device)
+    scales = torch.empty(W.shape[:-1] + (K // group,), dtype=torch.float32, device=W.device)
+    st = stream if stream is not None else torch.cuda.current_stream(W.device)
+    with torch.cuda.device(W.device):
+        status = moe_quantize_int4(W.data_ptr(), dtype, rows, K, group, packed.data_ptr(),
+                                   scales.data_ptr(), st.cuda_stream)
+    if status != MOE_OK:
+        raise MoeError(status, "moe_quantize_int4")
+    return packed, scales
+
+
+def forward_int4(x, W_router, W_gate, W_up, W_down, group: int, k: int, *, bias=None, out=None,
+                 workspace=None, topk_idx=None, topk_w=None, expert_counts=None, stream=None,
+                 stage_events=None, router_probs=None, balance_loss=None):
+    """One moe_ffn_forward_int4 call.  x [T][d] bf16; W_gate, W_up, W_down are
+    (packed, scales) pairs as quantize_int4 returns them for the [E][d_ff][d],
+    [E][d_ff][d] and [E][d][d_ff] stacks.  Other arguments as forward."""
+    import torch
+
+    T, d = x.shape
+    E = W_router.shape[1]
+    d_ff = W_gate[0].shape[1]
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    _check(x, (T, d), x.dtype, x)
+    _check(W_router, (d, E), torch.float32, x)
+    for (q, sc), N, K in ((W_gate, d_ff, d), (W_up, d_ff, d), (W_down, d, d_ff)):
+        _check(q, (E, N, K // 2), torch.uint8, x)
+        _check(sc, (E, N, K // group), torch.float32, x)
+    o, out, _keep = _opts(x, E, k, MOE_W4A16, bias, out, workspace, topk_idx, topk_w,
+                          expert_counts, stream, stage_events, router_probs, balance_loss)
+    with torch.cuda.device(x.device):
+        status = moe_ffn_forward_int4(x.data_ptr(), W_router.data_ptr(), W_gate[0].data_ptr(),
+                                      W_gate[1].data_ptr(), W_up[0].data_ptr(),
+                                      W_up[1].data_ptr(), W_down[0].data_ptr(),
+                                      W_down[1].data_ptr(), group, out.data_ptr(), T, d, d_ff,
+                                      E, k, o)
+    if status != MOE_OK:
+        raise MoeError(status, "moe_ffn_forward_int4")
     return out

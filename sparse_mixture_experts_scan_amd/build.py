@@ -20,13 +20,14 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_ffn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["route_permute.hip", "gemm_stream.hip", "gemm_tile.hip", "moe_ffn.hip"]
+SOURCES = ["route_permute.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_q4.hip", "moe_ffn.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are switched off for all device code; hipcc's host pass
 # warns that it does not know the feature, which is harmless.
 HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-fhip-fp32-correctly-rounded-divide-sqrt",
              "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 

@@ -16,6 +16,14 @@ struct Dims {
   int down_splits;     // K-splits of the down GEMM (partial Y blocks)
   int router_splits;   // d_model splits of the router scores (1 = fused kernel)
   bool bf16;           // element type of x / weights / out
+  bool w4;             // expert weights in INT4 (bf16 activations)
+  int group;           // INT4 scale group (input features per scale)
+};
+
+// INT4 weights of one matrix stack: packed codes and float32 scales
+struct Q4Weights {
+  const void* q;
+  const float* s;
 };
 
 // a1: scores, top-k, softmax over the k, per-block expert histogram
@@ -57,6 +65,20 @@ void launch_gateup_tile(const Dims& D, const void* xs, const void* Wg, const voi
 void launch_down_tile(const Dims& D, const void* h, const void* Wd, float* y,
                       const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                       const int32_t* tile_expert, hipStream_t s);
+// INT4 expert weights: quantizer, dequantizer (to bf16, for the tiled form)
+// and the weight-streaming GEMMs that read INT4 directly
+bool q4_group_ok(int K, int G);
+int q4_quantize_max_k();
+void launch_quantize_int4(const void* W, bool bf16, int64_t rows, int K, int G, void* packed,
+                          float* scales, hipStream_t s);
+void launch_dequant_int4(const void* packed, const float* scales, int64_t rows, int K, int G,
+                         void* out, hipStream_t s);
+void launch_gateup_q4(const Dims& D, const void* xs, const Q4Weights& Wg, const Q4Weights& Wu,
+                      void* h, const int32_t* counts, const int32_t* offsets,
+                      const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s);
+void launch_down_q4(const Dims& D, const void* h, const Q4Weights& Wd, float* y,
+                    const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
+                    const int32_t* tile_expert, hipStream_t s);
 // a5: gate-weighted gather-sum back to token order
 // resid: x for the block wrapper (out = x + layer), or NULL
 // T = 0: zero the optional statistics outputs (any may be null).

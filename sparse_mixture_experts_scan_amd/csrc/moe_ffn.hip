@@ -39,7 +39,8 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   if (T < 1 || d < 1 || f < 1 || E < 1 || k < 1)
     return fail(MOE_ERR_INVALID_ARG, "T must be >= 0; d_model, d_ff, E and k >= 1");
   if (k > E) return fail(MOE_ERR_INVALID_ARG, "k must be <= E");
-  if (dtype != MOE_BF16 && dtype != MOE_F32) return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
+  if (dtype != MOE_BF16 && dtype != MOE_F32 && dtype != MOE_W4A16)
+    return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
   if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E > 64");
   if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k > 8");
   if (d % MOE_DIM_ALIGN || f % MOE_DIM_ALIGN)
@@ -53,7 +54,9 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   D.f = (int)f;
   D.E = E;
   D.k = k;
-  D.bf16 = dtype == MOE_BF16;
+  D.bf16 = dtype != MOE_F32;
+  D.w4 = dtype == MOE_W4A16;
+  D.group = 0;
   D.Epow2 = 1;
   while (D.Epow2 < E) D.Epow2 *= 2;
   D.nblk = (D.T + moe::kRouterTokens - 1) / moe::kRouterTokens;
@@ -108,6 +111,7 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   L.router_partial = take(D.router_splits > 1 ? sizeof(float) * D.router_splits * D.nblk *
                                                     moe::kRouterTokens * moe::kRouterPartStride
                                               : 0);
+  L.wdeq = take(D.w4 && variant == 1 ? sizeof(uint16_t) * 3 * (size_t)E * d * f : 0);
   L.total = off;
   return MOE_OK;
 }
@@ -159,16 +163,18 @@ namespace {
 // out = x + layer(RMSNorm(x)).
 int run_layer(const void* x, const float* W_router, const void* W_gate, const void* W_up,
               const void* W_down, void* out, int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
-              int32_t k, const float* norm_w, float eps, const moe_opts_t* opts) {
-  g_last_error.clear();
+              int32_t k, const float* norm_w, float eps, const moe_opts_t* opts,
+              const moe::Q4Weights* q4 = nullptr, int group = 0) {
   moe_opts_t o;
   if (opts) o = *opts;
   else moe_opts_init(&o);
+  if (q4) o.dtype = MOE_W4A16;
   Plan p;
   // an empty batch checks the other sizes as for one token, reads no tensor
   // and only clears the optional statistics
   int st = make_plan(T == 0 ? 1 : T, d_model, d_ff, E, k, o.dtype, &p);
   if (st != MOE_OK) return st;
+  p.D.group = group;
   if (T == 0) {
     for (const void* ptr : {(const void*)o.expert_counts_out, (const void*)o.router_prob_out,
                             (const void*)o.balance_loss_out})
@@ -263,13 +269,31 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   moe::launch_scatter(D, norm_w ? xn : x, idx, blk, offsets, tok_row, row_token, xs, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess)
     return hip_fail(e, "scatter launch");
-  if (L.gemm_variant == 1)
+  if (q4 && L.gemm_variant == 1) {
+    // many rows per expert: bf16 copies of the INT4 stacks for the tiled form
+    char* wd = ws + L.wdeq;
+    const size_t mat = sizeof(uint16_t) * (size_t)E * d_model * d_ff;
+    moe::launch_dequant_int4(q4[0].q, q4[0].s, (int64_t)E * d_ff, (int)d_model, group, wd, s);
+    moe::launch_dequant_int4(q4[1].q, q4[1].s, (int64_t)E * d_ff, (int)d_model, group,
+                             wd + mat, s);
+    moe::launch_dequant_int4(q4[2].q, q4[2].s, (int64_t)E * d_model, (int)d_ff, group,
+                             wd + 2 * mat, s);
+    if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "dequantize launch");
+    W_gate = wd;
+    W_up = wd + mat;
+    W_down = wd + 2 * mat;
+  }
+  if (q4 && L.gemm_variant == 0)
+    moe::launch_gateup_q4(D, xs, q4[0], q4[1], h, counts, offsets, num_tiles, tile_expert, s);
+  else if (L.gemm_variant == 1)
     moe::launch_gateup_tile(D, xs, W_gate, W_up, h, counts, offsets, num_tiles, tile_expert, s);
   else
     moe::launch_gateup_stream(D, xs, W_gate, W_up, h, counts, offsets, num_tiles, tile_expert, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess)
     return hip_fail(e, "gate/up launch");
-  if (L.gemm_variant == 1)
+  if (q4 && L.gemm_variant == 0)
+    moe::launch_down_q4(D, h, q4[2], y, counts, offsets, num_tiles, tile_expert, s);
+  else if (L.gemm_variant == 1)
     moe::launch_down_tile(D, h, W_down, y, counts, offsets, num_tiles, tile_expert, s);
   else
     moe::launch_down_stream(D, h, W_down, y, counts, offsets, num_tiles, tile_expert, s);
@@ -288,6 +312,9 @@ extern "C" {
 int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, const void* W_up,
                     const void* W_down, void* out, int64_t T, int64_t d_model, int64_t d_ff,
                     int32_t E, int32_t k, const moe_opts_t* opts) {
+  g_last_error.clear();
+  if (opts && opts->dtype == MOE_W4A16)
+    return fail(MOE_ERR_INVALID_ARG, "MOE_W4A16 weights go through moe_ffn_forward_int4");
   return run_layer(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E, k, nullptr, 0.f,
                    opts);
 }
@@ -300,8 +327,60 @@ int moe_block_forward(const void* x, const float* norm_weight, float eps, const 
   if (!norm_weight) return fail(MOE_ERR_INVALID_ARG, "norm_weight is NULL");
   if (!(eps >= 0.f) || eps > 1.f) return fail(MOE_ERR_INVALID_ARG, "eps must be in [0, 1]");
   if (T > 0 && x == out) return fail(MOE_ERR_INVALID_ARG, "out must not alias x");
+  if (opts && opts->dtype == MOE_W4A16)
+    return fail(MOE_ERR_INVALID_ARG, "the block wrapper takes bf16 or float32 weights");
   return run_layer(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E, k, norm_weight,
                    eps, opts);
+}
+
+int moe_quantize_int4(const void* W, int32_t dtype, int64_t rows, int64_t K, int32_t group,
+                      uint8_t* packed, float* scales, void* stream) {
+  g_last_error.clear();
+  if (!W || !packed || !scales) return fail(MOE_ERR_INVALID_ARG, "null pointer");
+  if (dtype != MOE_BF16 && dtype != MOE_F32)
+    return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_BF16 or MOE_F32");
+  if (rows < 1 || K < 1 || group < 1) return fail(MOE_ERR_INVALID_ARG, "rows, K, group must be >= 1");
+  if (rows > 0x7fffffff) return fail(MOE_ERR_UNSUPPORTED, "rows > 2^31 - 1");
+  if (K > moe::q4_quantize_max_k()) return fail(MOE_ERR_UNSUPPORTED, "K > 65536");
+  if (!moe::q4_group_ok((int)K, group))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "K must be a multiple of 128 and group a multiple of 32 that divides K and is "
+                "32, 64 or a multiple of 128");
+  if (reinterpret_cast<uintptr_t>(W) % 16 || reinterpret_cast<uintptr_t>(packed) % 4 ||
+      reinterpret_cast<uintptr_t>(scales) % 4)
+    return fail(MOE_ERR_INVALID_ARG, "W must be 16-byte aligned, packed and scales 4-byte");
+  moe::launch_quantize_int4(W, dtype == MOE_BF16, rows, (int)K, group, packed, scales,
+                            reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOE_OK : hip_fail(e, "quantize launch");
+}
+
+int moe_ffn_forward_int4(const void* x, const float* W_router, const uint8_t* Wg_q,
+                         const float* Wg_s, const uint8_t* Wu_q, const float* Wu_s,
+                         const uint8_t* Wd_q, const float* Wd_s, int32_t group, void* out,
+                         int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                         const moe_opts_t* opts) {
+  g_last_error.clear();
+  if (d_model % 128 || d_ff % 128 || d_model < 128 || d_ff < 128)
+    return fail(MOE_ERR_UNSUPPORTED, "INT4 weights need d_model and d_ff multiples of 128");
+  if (!moe::q4_group_ok((int)d_model, group) || !moe::q4_group_ok((int)d_ff, group))
+    return fail(MOE_ERR_UNSUPPORTED,
+                "group must be a multiple of 32 dividing d_model and d_ff, and 32, 64 or a "
+                "multiple of 128");
+  if (T > 0) {
+    if (!Wg_q || !Wg_s || !Wu_q || !Wu_s || !Wd_q || !Wd_s)
+      return fail(MOE_ERR_INVALID_ARG, "null weight pointer");
+    for (const void* ptr : {(const void*)Wg_q, (const void*)Wu_q, (const void*)Wd_q})
+      if (reinterpret_cast<uintptr_t>(ptr) % 16)
+        return fail(MOE_ERR_INVALID_ARG, "INT4 codes must be 16-byte aligned");
+    for (const void* ptr : {(const void*)Wg_s, (const void*)Wu_s, (const void*)Wd_s})
+      if (reinterpret_cast<uintptr_t>(ptr) % 4)
+        return fail(MOE_ERR_INVALID_ARG, "scales must be 4-byte aligned");
+  }
+  const moe::Q4Weights q4[3] = {{Wg_q, Wg_s}, {Wu_q, Wu_s}, {Wd_q, Wd_s}};
+  // the weight arguments of the plain path stand in for the non-null checks
+  return run_layer(x, W_router, Wg_q, Wu_q, Wd_q, out, T, d_model, d_ff, E, k, nullptr, 0.f,
+                   opts, q4, group);
 }
 
 const char* moe_status_string(int status) {

@@ -27,8 +27,10 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 KERNEL_SOURCES = {
-    "gateup": {"stream": ["gemm_stream.hip", "common.h"], "tile": ["gemm_tile.hip", "common.h"]},
-    "down": {"stream": ["gemm_stream.hip", "common.h"], "tile": ["gemm_tile.hip", "common.h"]},
+    "gateup": {"stream": ["gemm_stream.hip", "common.h"], "tile": ["gemm_tile.hip", "common.h"],
+               "q4": ["gemm_q4.hip", "common.h"]},
+    "down": {"stream": ["gemm_stream.hip", "common.h"], "tile": ["gemm_tile.hip", "common.h"],
+             "q4": ["gemm_q4.hip", "common.h"]},
 }
 
 
@@ -46,6 +48,11 @@ def kernel_key(name: str) -> str:
         return "gateup" if ", true," in name else "down"
     if "tile_gemm_kernel" in name:
         return "gateup" if "<true>" in name else "down"
+    if "stream_q4_kernel" in name:
+        return "gateup" if ", true," in name else "down"
+    for k in ("quantize_int4", "dequant_int4", "rmsnorm"):
+        if k in name:
+            return k
     for k in ("router_topk", "router_select", "expert_scan", "scatter_gather", "combine"):
         if k in name:
             return k
@@ -87,7 +94,7 @@ def read_stats(d: str):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--variant", choices=("stream", "tile"), required=True)
+    ap.add_argument("--variant", choices=("stream", "tile", "q4"), required=True)
     ap.add_argument("--kt", required=True)
     ap.add_argument("--fetch", required=True)
     ap.add_argument("--write", required=True)
