@@ -269,8 +269,8 @@ def _as_f32(W) -> np.ndarray:
 
 
 def quantize_int4(W, group: int):
-    """Weight-only INT4 quantisation of a weight matrix (any leading shape,
-    last axis = the input features K) in groups of `group` consecutive input
+    """Weight-only INT4 quantisation of weight matrices W [..., N, K] (N
+    output rows, K input features) in groups of `group` consecutive input
     features of one row.
 
     "Mixtral of Experts" (limitations, memory item) names INT4 quantisation
@@ -281,10 +281,14 @@ def quantize_int4(W, group: int):
     The scale and every code are decided in float32 (the precision of the
     stored scale), so any implementation that divides with IEEE rounding
     reaches the same codes.  Storage: nibble u = q + 8; element 2b of a row in
-    the low nibble of byte b and element 2b + 1 in the high nibble.
+    the low nibble of byte b and element 2b + 1 in the high nibble; scales
+    group-major, [..., K/group, N] (the scales of one group of all rows are
+    adjacent).
 
-    Returns (packed uint8 [..., K/2], scales float32 [..., K/group])."""
+    Returns (packed uint8 [..., N, K/2], scales float32 [..., K/group, N])."""
     Wf = _as_f32(W)
+    if Wf.ndim < 2:
+        raise ValueError("W must be [..., N, K]")
     K = Wf.shape[-1]
     if K % group or K % 2:
         raise ValueError("K must be a multiple of the group size and even")
@@ -297,19 +301,19 @@ def quantize_int4(W, group: int):
     q = np.where(scale[..., None] > 0, q, 0).astype(np.int64)
     u = (q + INT4_OFFSET).reshape(Wf.shape).astype(np.uint8)
     packed = (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
-    return packed, scale
+    return packed, np.ascontiguousarray(np.swapaxes(scale, -1, -2))
 
 
 def dequantize_int4(packed, scales, group: int) -> np.ndarray:
-    """fp64 weights s * q from quantize_int4's storage (exact: s is float32
-    and q a small integer)."""
+    """fp64 weights s * q [..., N, K] from quantize_int4's storage (exact: s
+    is float32 and q a small integer)."""
     packed = np.asarray(packed, dtype=np.uint8)
     lo = (packed & 0x0F).astype(np.int64) - INT4_OFFSET
     hi = (packed >> 4).astype(np.int64) - INT4_OFFSET
     q = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.int64)
     q[..., 0::2] = lo
     q[..., 1::2] = hi
-    s = np.repeat(np.asarray(scales, dtype=np.float64), group, axis=-1)
+    s = np.repeat(np.swapaxes(np.asarray(scales, dtype=np.float64), -1, -2), group, axis=-1)
     return q.astype(np.float64) * s
 
 

@@ -70,7 +70,7 @@ def _q4_variant(nibble_swap=False, scale_div=7.0, half_away=False):
         q = np.where(scale[..., None] > 0, np.clip(q, -8, 7), 0).astype(np.int64)
         u = (q + 8).reshape(Wf.shape).astype(np.uint8)
         a, b = (u[..., 1::2], u[..., 0::2]) if nibble_swap else (u[..., 0::2], u[..., 1::2])
-        return (a | (b << 4)).astype(np.uint8), scale
+        return (a | (b << 4)).astype(np.uint8), np.ascontiguousarray(np.swapaxes(scale, -1, -2))
     return q4
 
 
@@ -79,7 +79,8 @@ def deq4_no_offset(packed, scales, group):
     q = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.int64)
     q[..., 0::2] = packed & 15
     q[..., 1::2] = packed >> 4
-    return q * np.repeat(np.asarray(scales, dtype=np.float64), group, axis=-1)
+    return q * np.repeat(np.swapaxes(np.asarray(scales, dtype=np.float64), -1, -2), group,
+                         axis=-1)
 
 
 MUTANTS = {

@@ -393,7 +393,7 @@ def test_int4_worked_example():
     # 3.5 -> 4), u = [6, 10, 7, 9, 12, 1, 15, 8] -> 0xA6, 0x97, 0x1C, 0x8F
     W2 = np.concatenate([W, 2 * W[:, ::-1]], axis=1)
     p2, s2 = oracle.quantize_int4(W2, 8)
-    assert s2.tolist() == [[1.0, 2.0]]
+    assert s2.tolist() == [[1.0], [2.0]]                     # [group][row]
     assert p2[0].tolist() == [0xF8, 0xC1, 0x79, 0x6A, 0xA6, 0x97, 0x1C, 0x8F]
     np.testing.assert_array_equal(oracle.dequantize_int4(p2, s2, 8)[0, 8:],
                                   2 * np.array([-2, 2, -1, 1, 4, -7, 7, 0]))
@@ -410,7 +410,7 @@ def test_int4_exact_recovery():
          (1 + rng.integers(0, 16, size=(rows, K // g)) / 16)).astype(np.float32)
     W = (q * s[..., None]).reshape(rows, K).astype(np.float32)
     packed, scale = oracle.quantize_int4(W, g)
-    np.testing.assert_array_equal(scale, s)
+    np.testing.assert_array_equal(scale, s.T)                 # group-major [K/g][rows]
     np.testing.assert_array_equal(oracle.dequantize_int4(packed, scale, g), W)
     lo = (packed & 15).astype(int) - 8
     np.testing.assert_array_equal(lo, q.reshape(rows, K)[:, 0::2])
@@ -422,8 +422,9 @@ def test_int4_error_bound_and_range():
     W[3, :64] *= 100.0                                # one loud group
     for g in (32, 128, 256):
         packed, scale = oracle.quantize_int4(W, g)
+        assert scale.shape == (256 // g, 16)
         deq = oracle.dequantize_int4(packed, scale, g)
-        srep = np.repeat(scale.astype(np.float64), g, axis=1)
+        srep = np.repeat(scale.T.astype(np.float64), g, axis=1)
         assert (np.abs(W - deq) <= srep * (0.5 + 1e-6)).all()     # round to nearest
         codes = np.stack([(packed & 15), (packed >> 4)], -1).reshape(W.shape).astype(int) - 8
         assert codes.min() >= -8 and codes.max() <= 7
@@ -432,14 +433,14 @@ def test_int4_error_bound_and_range():
         assert (G == 7).all()
         # scale = absmax / 7 rounded once to float32
         am = np.abs(W).reshape(16, -1, g).max(axis=-1)
-        np.testing.assert_array_equal(scale, (am / np.float32(7)).astype(np.float32))
+        np.testing.assert_array_equal(scale.T, (am / np.float32(7)).astype(np.float32))
 
 
 def test_int4_zero_group_and_bf16_input():
     W = np.zeros((2, 64), dtype=np.float32)
     W[1, 32:] = np.linspace(-1, 1, 32)
     packed, scale = oracle.quantize_int4(W, 32)
-    assert scale[0].tolist() == [0.0, 0.0] and scale[1, 0] == 0.0
+    assert scale[:, 0].tolist() == [0.0, 0.0] and scale[0, 1] == 0.0 and scale[1, 1] > 0
     assert (packed[0] == 0x88).all() and (packed[1, :16] == 0x88).all()
     # bf16 bit patterns quantize as the float32 values they encode
     bits = (W.view(np.uint32) >> 16).astype(np.uint16)           # truncated to bf16
