@@ -140,24 +140,25 @@ int moe_block_forward(const void* x, const float* norm_weight, float eps, const 
  *   s = max |w| / 7 over the group, q = clamp(rint(w / s), -8, 7), q = 0 when
  *   s = 0, both decided in float32 with IEEE division and ties to even;
  *   the weight stands for s * q.
- *   W       [rows][K] dtype (MOE_BF16 or MOE_F32), device, 16-byte aligned
- *   packed  [rows][K/2] uint8, device, 4-byte aligned (written): nibble
+ *   W       [batch][N][K] dtype (MOE_BF16 or MOE_F32), device, 16-byte aligned
+ *   packed  [batch][N][K/2] uint8, device, 4-byte aligned (written): nibble
  *           q + 8; element 2b in the low nibble of byte b, 2b + 1 in the high
- *   scales  [rows][K/group] float32, device, 4-byte aligned (written)
+ *   scales  [batch][K/group][N] float32, device, 4-byte aligned (written):
+ *           group-major, the scales of one group of neighbouring rows adjacent
  *   group: multiple of 32 dividing K, and either a multiple of 128 or 32/64;
- *   K a multiple of 128 and at most 65536; rows <= 2^31 - 1.
- * For an expert stack W_gate [E][d_ff][d_model] pass rows = E * d_ff and
- * K = d_model (W_down: rows = E * d_model, K = d_ff).  Asynchronous on
- * `stream` (hipStream_t, NULL = default); validation as moe_ffn_forward.
+ *   K a multiple of 128 and at most 65536; batch * N <= 2^31 - 1.
+ * For an expert stack W_gate [E][d_ff][d_model] pass batch = E, N = d_ff,
+ * K = d_model (W_down: N = d_model, K = d_ff).  Asynchronous on `stream`
+ * (hipStream_t, NULL = default); validation as moe_ffn_forward.
  */
-int moe_quantize_int4(const void* W, int32_t dtype, int64_t rows, int64_t K, int32_t group,
-                      uint8_t* packed, float* scales, void* stream);
+int moe_quantize_int4(const void* W, int32_t dtype, int64_t batch, int64_t N, int64_t K,
+                      int32_t group, uint8_t* packed, float* scales, void* stream);
 
 /*
  * The layer of moe_ffn_forward with INT4 expert weights as written by
  * moe_quantize_int4 (each expert matrix s * q); x and out bf16.
- *   Wg_q, Wu_q [E][d_ff][d_model/2] uint8, Wg_s, Wu_s [E][d_ff][d_model/group]
- *   Wd_q [E][d_model][d_ff/2] uint8, Wd_s [E][d_model][d_ff/group] float32
+ *   Wg_q, Wu_q [E][d_ff][d_model/2] uint8, Wg_s, Wu_s [E][d_model/group][d_ff]
+ *   Wd_q [E][d_model][d_ff/2] uint8, Wd_s [E][d_ff/group][d_model] float32
  * (16-byte aligned codes, 4-byte aligned scales); group as for
  * moe_quantize_int4 and dividing both d_model and d_ff, which must be
  * multiples of 128.  Few rows per expert (decode): the weight-streaming GEMMs

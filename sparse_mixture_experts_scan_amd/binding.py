@@ -76,7 +76,7 @@ def lib() -> ctypes.CDLL:
         L.moe_block_forward.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, i64, i64,
                                         i64, i32, i32, ctypes.POINTER(MoeOpts)]
         L.moe_block_forward.restype = ctypes.c_int
-        L.moe_quantize_int4.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
+        L.moe_quantize_int4.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, vp]
         L.moe_quantize_int4.restype = ctypes.c_int
         L.moe_ffn_forward_int4.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64,
                                            i64, i32, i32, ctypes.POINTER(MoeOpts)]
@@ -120,9 +120,9 @@ def moe_block_forward(x, norm_weight, eps, W_router, W_gate, W_up, W_down, out, 
                                    ctypes.byref(opts) if opts is not None else None)
 
 
-def moe_quantize_int4(W, dtype, rows, K, group, packed, scales, stream=None) -> int:
+def moe_quantize_int4(W, dtype, batch, N, K, group, packed, scales, stream=None) -> int:
     """Raw entry point of the INT4 quantizer."""
-    return lib().moe_quantize_int4(W, dtype, rows, K, group, packed, scales, stream)
+    return lib().moe_quantize_int4(W, dtype, batch, N, K, group, packed, scales, stream)
 
 
 def moe_ffn_forward_int4(x, W_router, Wg_q, Wg_s, Wu_q, Wu_s, Wd_q, Wd_s, group, out, T,
@@ -265,9 +265,9 @@ def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
 
 
 def quantize_int4(W, group: int = 128, stream=None):
-    """INT4 codes and scales of a bf16 or fp32 device tensor (last axis = the
-    input features K) through moe_quantize_int4.  Returns (packed uint8
-    [..., K/2], scales float32 [..., K/group])."""
+    """INT4 codes and scales of a bf16 or fp32 device tensor [..., N, K]
+    (matrices of N rows over K input features) through moe_quantize_int4.
+    Returns (packed uint8 [..., N, K/2], scales float32 [..., K/group, N])."""
     import torch
 
     if W.dtype == torch.bfloat16:
@@ -278,13 +278,15 @@ def quantize_int4(W, group: int = 128, stream=None):
         raise TypeError("W must be bfloat16 or float32")
     if not W.is_cuda or not W.is_contiguous():
         raise ValueError("W must be a contiguous device tensor")
-    K = W.shape[-1]
-    rows = W.numel() // K
+    if W.dim() < 2:
+        raise ValueError("W must be [..., N, K]")
+    N, K = W.shape[-2], W.shape[-1]
+    batch = W.numel() // (N * K)
     packed = torch.empty(W.shape[:-1] + (K // 2,), dtype=torch.uint8, device=W.device)
-    scales = torch.empty(W.shape[:-1] + (K // group,), dtype=torch.float32, device=W.device)
+    scales = torch.empty(W.shape[:-2] + (K // group, N), dtype=torch.float32, device=W.device)
     st = stream if stream is not None else torch.cuda.current_stream(W.device)
     with torch.cuda.device(W.device):
-        status = moe_quantize_int4(W.data_ptr(), dtype, rows, K, group, packed.data_ptr(),
+        status = moe_quantize_int4(W.data_ptr(), dtype, batch, N, K, group, packed.data_ptr(),
                                    scales.data_ptr(), st.cuda_stream)
     if status != MOE_OK:
         raise MoeError(status, "moe_quantize_int4")
@@ -308,7 +310,7 @@ def forward_int4(x, W_router, W_gate, W_up, W_down, group: int, k: int, *, bias=
     _check(W_router, (d, E), torch.float32, x)
     for (q, sc), N, K in ((W_gate, d_ff, d), (W_up, d_ff, d), (W_down, d, d_ff)):
         _check(q, (E, N, K // 2), torch.uint8, x)
-        _check(sc, (E, N, K // group), torch.float32, x)
+        _check(sc, (E, K // group, N), torch.float32, x)
     o, out, _keep = _opts(x, E, k, MOE_W4A16, bias, out, workspace, topk_idx, topk_w,
                           expert_counts, stream, stage_events, router_probs, balance_loss)
     with torch.cuda.device(x.device):

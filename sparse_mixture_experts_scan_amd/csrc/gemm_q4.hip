@@ -8,9 +8,10 @@
 //   q_k = clamp(rint(w_k / s), -8, 7)                (q = 0 when s = 0)
 //   w~_k = s * q_k
 // with groups of `group` consecutive input features of one weight row.
-// Storage: packed[row][K/2] bytes, nibble u = q + 8, element 2b in the low
-// nibble of byte b and element 2b + 1 in the high nibble; scales[row][K/group]
-// float32.
+// Storage of a matrix [N][K]: packed[N][K/2] bytes, nibble u = q + 8,
+// element 2b in the low nibble of byte b and element 2b + 1 in the high
+// nibble; scales[K/group][N] float32, group-major, so that the scales of one
+// group of 16 neighbouring rows sit in one 64-byte line.
 //
 // The GEMM: as the bf16 weight-streaming form, the MFMA A operand is 16
 // weight rows and B 16 token rows.  One 16-byte load gives a lane 32
@@ -81,7 +82,7 @@ __device__ inline uint4 dequant8(uint32_t w, float s) {
 // the scale; pass 3: the codes of each chunk, packed into one 32-bit word.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void quantize_int4_kernel(const T* __restrict__ W, int K,
+__global__ __launch_bounds__(256) void quantize_int4_kernel(const T* __restrict__ W, int N, int K,
                                                             int G, uint32_t* __restrict__ packed,
                                                             float* __restrict__ scales) {
   extern __shared__ float q4_smem[];
@@ -89,6 +90,7 @@ __global__ __launch_bounds__(256) void quantize_int4_kernel(const T* __restrict_
   float* cmax = q4_smem;
   float* gsc = q4_smem + nch;
   const size_t row = blockIdx.x;
+  const size_t mat = row / N, n = row - mat * N;
   const T* w = W + row * (size_t)K;
   for (int c = threadIdx.x; c < nch; c += 256) {
     float m = 0.f;
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(256) void quantize_int4_kernel(const T* __restrict_
     for (int c = g * cpg; c < (g + 1) * cpg; ++c) m = fmaxf(m, cmax[c]);
     const float s = m / 7.0f;
     gsc[g] = s;
-    scales[row * ngr + g] = s;
+    scales[(mat * ngr + g) * N + n] = s;
   }
   __syncthreads();
   for (int c = threadIdx.x; c < nch; c += 256) {
@@ -125,14 +127,15 @@ __global__ __launch_bounds__(256) void quantize_int4_kernel(const T* __restrict_
 // thread, in the layout of the bf16 weights.
 __global__ __launch_bounds__(256) void dequant_int4_kernel(const uint32_t* __restrict__ packed,
                                                            const float* __restrict__ scales,
-                                                           int64_t nchunks, int K, int G,
+                                                           int64_t nchunks, int N, int K, int G,
                                                            uint4* __restrict__ out) {
   const int cpr = K / 8, ngr = K / G;
   for (int64_t i = blockIdx.x * (int64_t)256 + threadIdx.x; i < nchunks;
        i += (int64_t)gridDim.x * 256) {
     const int64_t row = i / cpr;
     const int c = (int)(i - row * cpr);
-    const float s = scales[row * ngr + (c * 8) / G];
+    const int64_t mat = row / N, n = row - mat * N;
+    const float s = scales[(mat * ngr + (c * 8) / G) * N + n];
     out[i] = dequant8(packed[i], s);
   }
 }
@@ -159,13 +162,13 @@ struct Q4Batch {
                                        const __amdgpu_buffer_rsrc_t (&rs)[NW],
                                        __amdgpu_buffer_rsrc_t ra, const uint32_t (&wo)[NF],
                                        const uint32_t (&so)[NF], const uint32_t (&ao)[NT],
-                                       int run, int valid, int cpg, int gpc) {
+                                       int run, int valid, int cpg, int gpc, uint32_t sgrp) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (FULL || u < valid) {
         const uint32_t c = (uint32_t)(run * U + u);
         const uint32_t wsoff = c * (kQ4Chunk / 2);
-        const uint32_t ssoff = (c / cpg) * gpc * 4;
+        const uint32_t ssoff = (c / cpg) * gpc * sgrp;
         const uint32_t asoff = c * kQ4Chunk * 2;
 #pragma unroll
         for (int w = 0; w < NW; ++w)
@@ -207,7 +210,7 @@ struct Q4Batch {
 };
 
 template <int BT, int FT, bool GATEUP, int U>
-__global__ __launch_bounds__(kQ4Threads) void stream_q4_kernel(
+__device__ __forceinline__ void stream_q4_body(
     const bf16_t* __restrict__ act, const uint8_t* __restrict__ Q0,
     const float* __restrict__ S0, const uint8_t* __restrict__ Q1, const float* __restrict__ S1,
     void* __restrict__ outp, const int32_t* __restrict__ counts,
@@ -231,13 +234,15 @@ __global__ __launch_bounds__(kQ4Threads) void stream_q4_kernel(
   const int ngr = K / G;
   const int cpg = G >= kQ4Chunk ? G / kQ4Chunk : 1;   // chunks per group
   const int gpc = G >= kQ4Chunk ? 1 : kQ4Chunk / G;   // groups per chunk
-  const uint32_t qrow = (uint32_t)K / 2, srow = (uint32_t)ngr * 4;
+  // scales of expert e: [ngr][N]; this block's columns f0 .. f0 + FT - 1
+  const uint32_t qrow = (uint32_t)K / 2, sgrp = (uint32_t)N * 4;
+  const uint32_t sbytes = (uint32_t)(ngr - 1) * sgrp + FT * 4;
   __amdgpu_buffer_rsrc_t rw[NW], rs[NW];
   rw[0] = q4_rsrc(Q0 + ((size_t)e * N + f0) * qrow, FT * qrow);
-  rs[0] = q4_rsrc(S0 + ((size_t)e * N + f0) * ngr, FT * srow);
+  rs[0] = q4_rsrc(S0 + (size_t)e * ngr * N + f0, sbytes);
   if constexpr (GATEUP) {
     rw[1] = q4_rsrc(Q1 + ((size_t)e * N + f0) * qrow, FT * qrow);
-    rs[1] = q4_rsrc(S1 + ((size_t)e * N + f0) * ngr, FT * srow);
+    rs[1] = q4_rsrc(S1 + (size_t)e * ngr * N + f0, sbytes);
   }
   const uint32_t arow = (uint32_t)K * 2;
   const int nvalid = max(0, min(BT, valid_end - row0));
@@ -246,7 +251,7 @@ __global__ __launch_bounds__(kQ4Threads) void stream_q4_kernel(
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     wo[f] = (uint32_t)(f * 16 + lr) * qrow + kg * 16;
-    so[f] = (uint32_t)(f * 16 + lr) * srow + (uint32_t)((kg * 32) / G) * 4;
+    so[f] = (uint32_t)(f * 16 + lr) * 4 + (uint32_t)((kg * 32) / G) * sgrp;
   }
 #pragma unroll
   for (int n = 0; n < NT; ++n) ao[n] = (uint32_t)(n * 16 + lr) * arow + kg * 64;
@@ -262,17 +267,32 @@ __global__ __launch_bounds__(kQ4Threads) void stream_q4_kernel(
   const int nch = K / kQ4Chunk;
   const int nruns = nch / U, rem = nch % U;
   const int nb = nruns > wave ? (nruns - wave + NWAVE - 1) / NWAVE : 0;
+  // Steady state with unconditional loads, so that the wait before each
+  // compute counts only the other batch's loads; then a 1- or 2-batch tail.
+  // Scheduling barriers keep each batch's loads ahead of the other batch's
+  // compute (the scheduler would otherwise merge the two phases).
   QB A, B;
-  if (nb > 0) A.template load<true>(rw, rs, ra, wo, so, ao, wave, U, cpg, gpc);
-  for (int b = 0; b < nb; b += 2) {
-    if (b + 1 < nb) B.template load<true>(rw, rs, ra, wo, so, ao, wave + (b + 1) * NWAVE, U, cpg, gpc);
+  int b = 0;
+  if (nb > 0) A.template load<true>(rw, rs, ra, wo, so, ao, wave, U, cpg, gpc, sgrp);
+  for (; b + 2 < nb; b += 2) {
+    B.template load<true>(rw, rs, ra, wo, so, ao, wave + (b + 1) * NWAVE, U, cpg, gpc, sgrp);
+    __builtin_amdgcn_sched_barrier(0);
     A.template compute<true>(acc, U);
-    if (b + 1 >= nb) break;
-    if (b + 2 < nb) A.template load<true>(rw, rs, ra, wo, so, ao, wave + (b + 2) * NWAVE, U, cpg, gpc);
+    __builtin_amdgcn_sched_barrier(0);
+    A.template load<true>(rw, rs, ra, wo, so, ao, wave + (b + 2) * NWAVE, U, cpg, gpc, sgrp);
+    __builtin_amdgcn_sched_barrier(0);
     B.template compute<true>(acc, U);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (b + 1 < nb) {
+    B.template load<true>(rw, rs, ra, wo, so, ao, wave + (b + 1) * NWAVE, U, cpg, gpc, sgrp);
+    A.template compute<true>(acc, U);
+    B.template compute<true>(acc, U);
+  } else if (b < nb) {
+    A.template compute<true>(acc, U);
   }
   if (rem > 0 && wave == nruns % NWAVE) {
-    A.template load<false>(rw, rs, ra, wo, so, ao, nruns, rem, cpg, gpc);
+    A.template load<false>(rw, rs, ra, wo, so, ao, nruns, rem, cpg, gpc, sgrp);
     A.template compute<false>(acc, rem);
   }
 
@@ -320,14 +340,40 @@ __global__ __launch_bounds__(kQ4Threads) void stream_q4_kernel(
   }
 }
 
+// Decode shapes (16-row token tiles) are latency-bound on the weight stream:
+// registers are capped so that 4 waves share each SIMD.
+#ifndef MOE_Q4_WPE16
+#define MOE_Q4_WPE16 4
+#endif
+
+#define MOE_Q4_PARAMS                                                                        \
+  const bf16_t *__restrict__ act, const uint8_t *__restrict__ Q0,                            \
+      const float *__restrict__ S0, const uint8_t *__restrict__ Q1,                          \
+      const float *__restrict__ S1, void *__restrict__ outp,                                 \
+      const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,               \
+      const int32_t *__restrict__ num_tiles, const int32_t *__restrict__ tile_expert, int N, \
+      int K, int G
+#define MOE_Q4_ARGS act, Q0, S0, Q1, S1, outp, counts, offsets, num_tiles, tile_expert, N, K, G
+
+template <int FT, bool GATEUP, int U>
+__global__ __launch_bounds__(kQ4Threads)
+__attribute__((amdgpu_waves_per_eu(MOE_Q4_WPE16, 8))) void stream_q4_kernel16(MOE_Q4_PARAMS) {
+  stream_q4_body<16, FT, GATEUP, U>(MOE_Q4_ARGS);
+}
+
+template <int FT, bool GATEUP, int U>
+__global__ __launch_bounds__(kQ4Threads) void stream_q4_kernel32(MOE_Q4_PARAMS) {
+  stream_q4_body<32, FT, GATEUP, U>(MOE_Q4_ARGS);
+}
+
 #ifndef MOE_Q4_U
-#define MOE_Q4_U 2
+#define MOE_Q4_U 1
 #endif
 #ifndef MOE_Q4_FT_GU
 #define MOE_Q4_FT_GU 32
 #endif
 #ifndef MOE_Q4_FT_DN
-#define MOE_Q4_FT_DN 32
+#define MOE_Q4_FT_DN 64
 #endif
 
 bool q4_group_ok(int K, int G) {
@@ -337,23 +383,23 @@ bool q4_group_ok(int K, int G) {
 
 int q4_quantize_max_k() { return 65536; }
 
-void launch_quantize_int4(const void* W, bool bf16, int64_t rows, int K, int G, void* packed,
-                          float* scales, hipStream_t s) {
+void launch_quantize_int4(const void* W, bool bf16, int64_t rows, int N, int K, int G,
+                          void* packed, float* scales, hipStream_t s) {
   const size_t lds = sizeof(float) * ((size_t)K / 8 + (size_t)K / G);
   if (bf16)
     quantize_int4_kernel<bf16_t><<<(unsigned)rows, 256, lds, s>>>(
-        (const bf16_t*)W, K, G, (uint32_t*)packed, scales);
+        (const bf16_t*)W, N, K, G, (uint32_t*)packed, scales);
   else
-    quantize_int4_kernel<float><<<(unsigned)rows, 256, lds, s>>>((const float*)W, K, G,
+    quantize_int4_kernel<float><<<(unsigned)rows, 256, lds, s>>>((const float*)W, N, K, G,
                                                                   (uint32_t*)packed, scales);
 }
 
-void launch_dequant_int4(const void* packed, const float* scales, int64_t rows, int K, int G,
-                         void* out, hipStream_t s) {
+void launch_dequant_int4(const void* packed, const float* scales, int64_t rows, int N, int K,
+                         int G, void* out, hipStream_t s) {
   const int64_t nchunks = rows * (K / 8);
   const int64_t want = (nchunks + 255) / 256;
   const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
-  dequant_int4_kernel<<<grid, 256, 0, s>>>((const uint32_t*)packed, scales, nchunks, K, G,
+  dequant_int4_kernel<<<grid, 256, 0, s>>>((const uint32_t*)packed, scales, nchunks, N, K, G,
                                            (uint4*)out);
 }
 
@@ -363,9 +409,11 @@ static void gateup_q4(const Dims& D, const void* xs, const Q4Weights& Wg, const 
                       const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s) {
   constexpr int FT = MOE_Q4_FT_GU;
   dim3 grid(D.f / FT, D.max_tiles);
-  stream_q4_kernel<BT, FT, true, MOE_Q4_U><<<grid, kQ4Threads, 0, s>>>(
-      (const bf16_t*)xs, (const uint8_t*)Wg.q, Wg.s, (const uint8_t*)Wu.q, Wu.s, h, counts,
-      offsets, num_tiles, tile_expert, D.f, D.d, D.group);
+  auto kern = BT == 16 ? stream_q4_kernel16<FT, true, MOE_Q4_U>
+                       : stream_q4_kernel32<FT, true, MOE_Q4_U>;
+  kern<<<grid, kQ4Threads, 0, s>>>((const bf16_t*)xs, (const uint8_t*)Wg.q, Wg.s,
+                                   (const uint8_t*)Wu.q, Wu.s, h, counts, offsets, num_tiles,
+                                   tile_expert, D.f, D.d, D.group);
 }
 
 template <int BT>
@@ -374,9 +422,11 @@ static void down_q4(const Dims& D, const void* h, const Q4Weights& Wd, float* y,
                     const int32_t* tile_expert, hipStream_t s) {
   constexpr int FT = MOE_Q4_FT_DN;
   dim3 grid(D.d / FT, D.max_tiles);
-  stream_q4_kernel<BT, FT, false, MOE_Q4_U><<<grid, kQ4Threads, 0, s>>>(
-      (const bf16_t*)h, (const uint8_t*)Wd.q, Wd.s, nullptr, nullptr, y, counts, offsets,
-      num_tiles, tile_expert, D.d, D.f, D.group);
+  auto kern = BT == 16 ? stream_q4_kernel16<FT, false, MOE_Q4_U>
+                       : stream_q4_kernel32<FT, false, MOE_Q4_U>;
+  kern<<<grid, kQ4Threads, 0, s>>>((const bf16_t*)h, (const uint8_t*)Wd.q, Wd.s, nullptr,
+                                   nullptr, y, counts, offsets, num_tiles, tile_expert, D.d,
+                                   D.f, D.group);
 }
 
 void launch_gateup_q4(const Dims& D, const void* xs, const Q4Weights& Wg, const Q4Weights& Wu,

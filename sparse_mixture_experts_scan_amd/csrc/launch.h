@@ -69,10 +69,11 @@ void launch_down_tile(const Dims& D, const void* h, const void* Wd, float* y,
 // and the weight-streaming GEMMs that read INT4 directly
 bool q4_group_ok(int K, int G);
 int q4_quantize_max_k();
-void launch_quantize_int4(const void* W, bool bf16, int64_t rows, int K, int G, void* packed,
-                          float* scales, hipStream_t s);
-void launch_dequant_int4(const void* packed, const float* scales, int64_t rows, int K, int G,
-                         void* out, hipStream_t s);
+// rows = batch * N matrices rows; scales group-major per matrix ([K/G][N])
+void launch_quantize_int4(const void* W, bool bf16, int64_t rows, int N, int K, int G,
+                          void* packed, float* scales, hipStream_t s);
+void launch_dequant_int4(const void* packed, const float* scales, int64_t rows, int N, int K,
+                         int G, void* out, hipStream_t s);
 void launch_gateup_q4(const Dims& D, const void* xs, const Q4Weights& Wg, const Q4Weights& Wu,
                       void* h, const int32_t* counts, const int32_t* offsets,
                       const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s);

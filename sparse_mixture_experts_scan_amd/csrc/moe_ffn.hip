@@ -273,11 +273,12 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
     // many rows per expert: bf16 copies of the INT4 stacks for the tiled form
     char* wd = ws + L.wdeq;
     const size_t mat = sizeof(uint16_t) * (size_t)E * d_model * d_ff;
-    moe::launch_dequant_int4(q4[0].q, q4[0].s, (int64_t)E * d_ff, (int)d_model, group, wd, s);
-    moe::launch_dequant_int4(q4[1].q, q4[1].s, (int64_t)E * d_ff, (int)d_model, group,
-                             wd + mat, s);
-    moe::launch_dequant_int4(q4[2].q, q4[2].s, (int64_t)E * d_model, (int)d_ff, group,
-                             wd + 2 * mat, s);
+    moe::launch_dequant_int4(q4[0].q, q4[0].s, (int64_t)E * d_ff, (int)d_ff, (int)d_model,
+                             group, wd, s);
+    moe::launch_dequant_int4(q4[1].q, q4[1].s, (int64_t)E * d_ff, (int)d_ff, (int)d_model,
+                             group, wd + mat, s);
+    moe::launch_dequant_int4(q4[2].q, q4[2].s, (int64_t)E * d_model, (int)d_model, (int)d_ff,
+                             group, wd + 2 * mat, s);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "dequantize launch");
     W_gate = wd;
     W_up = wd + mat;
@@ -333,14 +334,16 @@ int moe_block_forward(const void* x, const float* norm_weight, float eps, const 
                    eps, opts);
 }
 
-int moe_quantize_int4(const void* W, int32_t dtype, int64_t rows, int64_t K, int32_t group,
-                      uint8_t* packed, float* scales, void* stream) {
+int moe_quantize_int4(const void* W, int32_t dtype, int64_t batch, int64_t N, int64_t K,
+                      int32_t group, uint8_t* packed, float* scales, void* stream) {
   g_last_error.clear();
   if (!W || !packed || !scales) return fail(MOE_ERR_INVALID_ARG, "null pointer");
   if (dtype != MOE_BF16 && dtype != MOE_F32)
     return fail(MOE_ERR_INVALID_ARG, "dtype must be MOE_BF16 or MOE_F32");
-  if (rows < 1 || K < 1 || group < 1) return fail(MOE_ERR_INVALID_ARG, "rows, K, group must be >= 1");
-  if (rows > 0x7fffffff) return fail(MOE_ERR_UNSUPPORTED, "rows > 2^31 - 1");
+  if (batch < 1 || N < 1 || K < 1 || group < 1)
+    return fail(MOE_ERR_INVALID_ARG, "batch, N, K and group must be >= 1");
+  if (N > 0x7fffffff || batch > 0x7fffffff / N)
+    return fail(MOE_ERR_UNSUPPORTED, "batch * N > 2^31 - 1");
   if (K > moe::q4_quantize_max_k()) return fail(MOE_ERR_UNSUPPORTED, "K > 65536");
   if (!moe::q4_group_ok((int)K, group))
     return fail(MOE_ERR_UNSUPPORTED,
@@ -349,8 +352,8 @@ int moe_quantize_int4(const void* W, int32_t dtype, int64_t rows, int64_t K, int
   if (reinterpret_cast<uintptr_t>(W) % 16 || reinterpret_cast<uintptr_t>(packed) % 4 ||
       reinterpret_cast<uintptr_t>(scales) % 4)
     return fail(MOE_ERR_INVALID_ARG, "W must be 16-byte aligned, packed and scales 4-byte");
-  moe::launch_quantize_int4(W, dtype == MOE_BF16, rows, (int)K, group, packed, scales,
-                            reinterpret_cast<hipStream_t>(stream));
+  moe::launch_quantize_int4(W, dtype == MOE_BF16, batch * N, (int)N, (int)K, group, packed,
+                            scales, reinterpret_cast<hipStream_t>(stream));
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? MOE_OK : hip_fail(e, "quantize launch");
 }

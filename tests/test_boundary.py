@@ -201,12 +201,15 @@ def test_int4_forward_validation():
 
 
 def test_quantize_validation():
-    def q(W=DUMMY, dtype=B.MOE_BF16, rows=4, K=256, group=128, pk=DUMMY * 2, sc=DUMMY * 3):
-        return moe.moe_quantize_int4(W, dtype, rows, K, group, pk, sc, None)
+    def q(W=DUMMY, dtype=B.MOE_BF16, rows=4, K=256, group=128, pk=DUMMY * 2, sc=DUMMY * 3,
+          batch=2):
+        return moe.moe_quantize_int4(W, dtype, batch, rows, K, group, pk, sc, None)
     assert q(W=None) == B.MOE_ERR_INVALID_ARG
     assert q(pk=None) == B.MOE_ERR_INVALID_ARG
     assert q(dtype=B.MOE_W4A16) == B.MOE_ERR_INVALID_ARG
     assert q(rows=0) == B.MOE_ERR_INVALID_ARG
+    assert q(batch=0) == B.MOE_ERR_INVALID_ARG
+    assert q(batch=1 << 20, rows=1 << 12) == B.MOE_ERR_UNSUPPORTED
     assert q(K=192) == B.MOE_ERR_UNSUPPORTED
     assert q(K=131072) == B.MOE_ERR_UNSUPPORTED
     assert q(group=96) == B.MOE_ERR_UNSUPPORTED
