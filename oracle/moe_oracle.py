@@ -33,6 +33,10 @@ optional per-expert router bias (an extension the pages do not have) is added
 to the scores before both the selection and the softmax; every token is
 routed to exactly k experts (no capacity limit or token dropping).
 
+* "Mistral/Mixtralのアーキテクチャ", section "ロードバランス損失": the
+  training loss is the language-model loss plus L_balance; moe_backward
+  gives the layer's part of its gradient, that of
+  <dOut, MoE(x)> + alpha * N * sum_i f_i p_i for an upstream gradient dOut.
 * "Mixtral of Experts" (singularity-lens.com), its list of limitations, the
   item on memory requirements and offloading: the model needs INT4
   quantisation to fit in about 25-30 GB.  The pages give no scheme; the plain
@@ -337,3 +341,80 @@ def moe_forward_int4(x, W_router, qweights: dict, group: int, k, bias=None, toke
     W = {n: _Int4Stack(*qweights[n], group) for n in ("W_gate", "W_up", "W_down")}
     return moe_forward(x, W_router, W["W_gate"], W["W_up"], W["W_down"], k, bias=bias,
                        tokens=tokens, forced_idx=forced_idx)
+
+
+# ----------------------------------------------------------------------------
+# backward pass
+# ----------------------------------------------------------------------------
+
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d/dz SiLU(z) = sigma(z) * (1 + z * (1 - sigma(z)))."""
+    sig = 1.0 / (1.0 + np.exp(-z))
+    return sig * (1.0 + z * (1.0 - sig))
+
+
+def moe_backward(x, W_router, W_gate, W_up, W_down, dout, k, bias=None, alpha=0.0,
+                 forced_idx=None) -> dict:
+    """Gradients of  L = <dOut, MoE(x)> + alpha * N * sum_i f_i p_i  with
+    respect to x, W_router, the bias and the three expert stacks.
+
+    "ロードバランス損失" adds the balance loss to the language-model loss; the
+    layer's part of the total gradient is the chain rule through
+    MoE(x) = sum_j g_j E_ij(x) (the upstream gradient dOut stands for the
+    language-model loss above the layer) plus the balance loss's own term.
+    f_i counts top-k selections, which are piecewise constant, so only p_i
+    (the mean full softmax) carries gradient.  Steps, per routed (t, j) with
+    expert e, a = W1 x_t, b = W3 x_t, h = SiLU(a) * b, y = W2 h:
+        dg_tj = <dOut_t, y>,  dy = g_tj dOut_t,  dh = W2^T dy,
+        da = dh * b * SiLU'(a),  db = dh * SiLU(a),
+        dx_t += W1^T da + W3^T db,  dW2 += dy h^T,  dW1 += da x^T,  dW3 += db x^T;
+    the softmax over the selected scores: ds_tij = g_tj (dg_tj - sum_l g_tl dg_tl);
+    the balance term: ds_tm += (alpha N / T) P_tm (f_m - sum_i f_i P_ti);
+    then dW_router = x^T ds, dbias = sum_t ds_t, dx += ds W_router^T.
+    Returns fp64 arrays dx [T][d], dW_router [d][E], dbias [E], dW_gate,
+    dW_up [E][d_ff][d], dW_down [E][d][d_ff], and the routing (idx, gates)."""
+    xf = to_f64(x)
+    T, d = xf.shape
+    Wr = to_f64(W_router)
+    E = Wr.shape[1]
+    go = to_f64(dout)
+    s = router_logits(xf, Wr, bias)
+    idx = select_topk(s, k) if forced_idx is None else np.asarray(forced_idx, dtype=np.int64)
+    g = topk_gates(s, idx)
+    f_dim = np.asarray(W_gate[0]).shape[0]
+    dx = np.zeros((T, d))
+    dg = np.zeros((T, k))
+    dW1 = np.zeros((E, f_dim, d))
+    dW3 = np.zeros((E, f_dim, d))
+    dW2 = np.zeros((E, d, f_dim))
+    for e in range(E):
+        rows, slots = np.nonzero(idx == e)          # a token picks an expert at most once
+        if rows.size == 0:
+            continue
+        W1, W3, W2 = to_f64(W_gate[e]), to_f64(W_up[e]), to_f64(W_down[e])
+        X = xf[rows]
+        a = X @ W1.T
+        b = X @ W3.T
+        h = silu(a) * b
+        y = h @ W2.T
+        dg[rows, slots] = (go[rows] * y).sum(axis=1)
+        dy = g[rows, slots][:, None] * go[rows]
+        dh = dy @ W2
+        da = dh * b * silu_grad(a)
+        db = dh * silu(a)
+        dx[rows] += da @ W1 + db @ W3
+        dW2[e] = dy.T @ h
+        dW1[e] = da.T @ X
+        dW3[e] = db.T @ X
+    ds = np.zeros((T, E))
+    ds_sel = g * (dg - (g * dg).sum(axis=1, keepdims=True))
+    np.put_along_axis(ds, idx, ds_sel, axis=1)
+    if alpha:
+        f = np.bincount(idx.reshape(-1), minlength=E) / T
+        z = np.exp(s - s.max(axis=1, keepdims=True))
+        P = z / z.sum(axis=1, keepdims=True)
+        c = alpha * E * f / T
+        ds += P * (c[None, :] - (P * c[None, :]).sum(axis=1, keepdims=True))
+    dx += ds @ Wr.T
+    return dict(dx=dx, dW_router=xf.T @ ds, dbias=ds.sum(axis=0), dW_gate=dW1, dW_up=dW3,
+                dW_down=dW2, idx=idx, gates=g, ds=ds, dg=dg)

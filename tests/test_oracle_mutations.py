@@ -83,7 +83,13 @@ def deq4_no_offset(packed, scales, group):
                          axis=-1)
 
 
+def silu_grad_sigma_only(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
 MUTANTS = {
+    "silu_grad:sigma_only": ("silu_grad", silu_grad_sigma_only,
+                             [lambda: pins.test_backward_matches_central_differences(0.0, False, 2)]),
     "quantize_int4:nibbles_swapped": ("quantize_int4", _q4_variant(nibble_swap=True),
                                       [pins.test_int4_worked_example]),
     "quantize_int4:scale_over_8": ("quantize_int4", _q4_variant(scale_div=8.0),
@@ -132,3 +138,47 @@ def test_int4_mutant_base_is_the_oracle():
         p1, s1 = _q4_variant()(W, g)
         np.testing.assert_array_equal(p0, p1)
         np.testing.assert_array_equal(s0, s1)
+
+
+# mistakes planted inside moe_backward by editing one line of its source
+BACKWARD_EDITS = {
+    "k_softmax_without_subtraction": ("ds_sel = g * (dg - (g * dg).sum(axis=1, keepdims=True))",
+                                      "ds_sel = g * dg"),
+    "gate_up_swapped_in_dx": ("dx[rows] += da @ W1 + db @ W3", "dx[rows] += da @ W3 + db @ W1"),
+    "up_grad_without_silu": ("db = dh * silu(a)", "db = dh * a"),
+    "balance_sign": ("ds += P * (c[None, :] - (P * c[None, :]).sum(axis=1, keepdims=True))",
+                     "ds -= P * (c[None, :] - (P * c[None, :]).sum(axis=1, keepdims=True))"),
+    "gate_scale_missing": ("dy = g[rows, slots][:, None] * go[rows]", "dy = go[rows]"),
+    "router_path_dropped": ("dx += ds @ Wr.T", "dx += (ds @ Wr.T) * 0"),
+}
+
+
+def _edited_backward(old, new):
+    import inspect
+    import textwrap
+    src = textwrap.dedent(inspect.getsource(om.moe_backward))
+    assert src.count(old) == 1, old
+    ns = dict(vars(om))
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    return ns["moe_backward"]
+
+
+@pytest.mark.parametrize("edit", sorted(BACKWARD_EDITS))
+def test_backward_pins_catch_planted_mistake(edit, monkeypatch):
+    _patch(monkeypatch, "moe_backward", _edited_backward(*BACKWARD_EDITS[edit]))
+    failed = 0
+    for args in ((0.0, False, 2), (0.05, True, 2)):
+        try:
+            pins.test_backward_matches_central_differences(*args)
+        except AssertionError:
+            failed += 1
+    assert failed > 0
+
+
+def test_backward_edit_base_is_the_oracle():
+    fn = _edited_backward("dx += ds @ Wr.T", "dx += ds @ Wr.T")
+    args = pins._bwd_case(5)
+    a = fn(*args[:5], args[6], 2, bias=args[5], alpha=0.1)
+    b = om.moe_backward(*args[:5], args[6], 2, bias=args[5], alpha=0.1)
+    for n in ("dx", "dW_router", "dW_gate", "dW_up", "dW_down", "dbias"):
+        np.testing.assert_array_equal(a[n], b[n])

@@ -475,3 +475,85 @@ def test_int4_layer_on_representable_weights_equals_plain_layer():
     # and differs when gate and up are exchanged
     qs = dict(qw, W_gate=qw["W_up"], W_up=qw["W_gate"])
     assert np.abs(oracle.moe_forward_int4(x, Wr, qs, g, k)["out"] - r["out"]).max() > 1e-3
+
+
+# ---------------------------------------------------------------- backward
+# "ロードバランス損失": the training loss adds alpha * N * sum f_i p_i to the
+# language-model loss; the layer's gradient is pinned by central differences
+# of  <dOut, MoE(x)> + alpha * N * sum f_i p_i  with the routing held fixed.
+
+def _bwd_case(seed, T=5, d=6, f=4, E=4, k=2, bias=True):
+    rng = np.random.default_rng(seed)
+    x, Wr, Wg, Wu, Wd = rand_layer(rng, T=T, d=d, f=f, E=E)
+    b = rng.standard_normal(E) * 0.3 if bias else None
+    dout = rng.standard_normal((T, d))
+    return x, Wr, Wg, Wu, Wd, b, dout
+
+
+def _loss(x, Wr, Wg, Wu, Wd, b, dout, k, idx, alpha):
+    r = oracle.moe_forward(x, Wr, Wg, Wu, Wd, k, bias=b, forced_idx=idx)
+    L = float((dout * r["out"]).sum())
+    if alpha:
+        L += oracle.balance_stats(r["logits"], idx, alpha)["loss"]
+    return L
+
+
+@pytest.mark.parametrize("alpha,bias,k", [(0.0, False, 2), (0.05, True, 2), (0.3, True, 3),
+                                          (0.0, True, 1)])
+def test_backward_matches_central_differences(alpha, bias, k):
+    x, Wr, Wg, Wu, Wd, b, dout = _bwd_case(31 + k, bias=bias)
+    s = oracle.router_logits(x, Wr, b)
+    gap, _ = oracle.routing_gaps(s, k)
+    assert gap.min() > 1e-3                          # the routing is not near a tie
+    idx = oracle.select_topk(s, k)
+    g = oracle.moe_backward(x, Wr, Wg, Wu, Wd, dout, k, bias=b, alpha=alpha)
+    np.testing.assert_array_equal(g["idx"], idx)
+    params = {"dx": x, "dW_router": Wr, "dW_gate": Wg, "dW_up": Wu, "dW_down": Wd}
+    if bias:
+        params["dbias"] = b
+    h = 1e-5
+    for name, P in params.items():
+        fd = np.zeros_like(P)
+        for i in np.ndindex(P.shape):
+            old = P[i]
+            P[i] = old + h
+            lp = _loss(x, Wr, Wg, Wu, Wd, b, dout, k, idx, alpha)
+            P[i] = old - h
+            lm = _loss(x, Wr, Wg, Wu, Wd, b, dout, k, idx, alpha)
+            P[i] = old
+            fd[i] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g[name], fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_backward_special_cases():
+    x, Wr, Wg, Wu, Wd, b, dout = _bwd_case(40)
+    # zero down projection: every expert output is 0, so the gates get no
+    # gradient and nothing flows below W_down; dW_down is sum_t g dOut h^T
+    g = oracle.moe_backward(x, Wr, Wg, Wu, np.zeros_like(Wd), dout, 2)
+    for n in ("dx", "dW_router", "dW_gate", "dW_up"):
+        assert np.abs(g[n]).max() == 0.0, n
+    assert np.abs(g["dW_down"]).max() > 0
+    # one expert, top-1: the gate is constantly 1 (no router gradient) and the
+    # rest is the dense SwiGLU gradient, written out here per token
+    x1, Wr1, Wg1, Wu1, Wd1, _, d1 = _bwd_case(41, E=1, k=1, bias=False)
+    g1 = oracle.moe_backward(x1, Wr1, Wg1, Wu1, Wd1, d1, 1)
+    assert np.abs(g1["dW_router"]).max() == 0.0
+    W1, W3, W2 = Wg1[0], Wu1[0], Wd1[0]
+    for t in range(x1.shape[0]):
+        a, bb = W1 @ x1[t], W3 @ x1[t]
+        sg = 1 / (1 + np.exp(-a))
+        dh = W2.T @ d1[t]
+        da = dh * bb * (sg + a * sg * (1 - sg))
+        np.testing.assert_allclose(g1["dx"][t], W1.T @ da + W3.T @ (dh * a * sg),
+                                   rtol=1e-12, atol=1e-14)
+    # linear in dOut (with no balance term)
+    g2 = oracle.moe_backward(x, Wr, Wg, Wu, Wd, 2.5 * dout, 2, bias=b)
+    g0 = oracle.moe_backward(x, Wr, Wg, Wu, Wd, dout, 2, bias=b)
+    for n in ("dx", "dW_router", "dW_gate", "dW_up", "dW_down", "dbias"):
+        np.testing.assert_allclose(g2[n], 2.5 * g0[n], rtol=1e-12, atol=1e-14)
+    # the balance term alone: zero dOut leaves only the router gradient
+    gb = oracle.moe_backward(x, Wr, Wg, Wu, Wd, np.zeros_like(dout), 2, bias=b, alpha=0.1)
+    for n in ("dW_gate", "dW_up", "dW_down"):
+        assert np.abs(gb[n]).max() == 0.0
+    assert np.abs(gb["dW_router"]).max() > 0
+    np.testing.assert_allclose(gb["ds"].sum(axis=1), 0.0, atol=1e-15)  # softmax rows
