@@ -174,6 +174,42 @@ int moe_ffn_forward_int4(const void* x, const float* W_router, const uint8_t* Wg
                          int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
                          const moe_opts_t* opts);
 
+/*
+ * Backward pass of moe_ffn_forward (bf16 tensors): the gradients of
+ *   L = <dout, out> + alpha * N * sum_i f_i p_i
+ * ("Mistral/Mixtralのアーキテクチャ", section "ロードバランス損失": the
+ * training loss adds the balance loss to the language-model loss, whose
+ * gradient above the layer is dout).  f_i (the top-k counts over T) is
+ * piecewise constant, so the balance term reaches only the router scores
+ * through p_i.  The routing, the permutation and the pre-activations are
+ * recomputed from x (nothing is kept from a forward call).
+ *   x, W_router, W_gate, W_up, W_down, T .. k: as moe_ffn_forward, bf16
+ *   dout        [T][d_model] bf16 device: gradient of the loss w.r.t. out
+ *   alpha       >= 0, the balance-loss weight (0: no balance term)
+ *   dx          [T][d_model] bf16 (written)
+ *   dW_router   [d_model][E] float32 (written); dbias [E] float32 or NULL:
+ *               the gradient w.r.t. an additive router bias (opts->router_bias)
+ *   dW_gate, dW_up [E][d_ff][d_model], dW_down [E][d_model][d_ff] bf16 (written)
+ * d_model and d_ff must be multiples of 128.  opts: dtype must be MOE_BF16;
+ * stream, router_bias and workspace as for the forward, the workspace sized by
+ * moe_ffn_backward_workspace_size; routing and statistics outputs are not
+ * written; stage_events, if given, holds MOE_BWD_NUM_STAGES + 1 events
+ * (routing, recompute, Z = W2^T dout, row/router gradients, dX GEMMs, dx,
+ * dW_down, dW_gate and dW_up).  T = 0 writes zero weight gradients.
+ * Deterministic: fixed summation orders, no atomics.
+ */
+#define MOE_BWD_NUM_STAGES 8
+int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate,
+                     const void* W_up, const void* W_down, const void* dout, float alpha,
+                     void* dx, float* dW_router, float* dbias, void* dW_gate, void* dW_up,
+                     void* dW_down, int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
+                     int32_t k, const moe_opts_t* opts);
+
+/* Bytes of workspace moe_ffn_backward needs (0 if the shape is invalid or
+ * unsupported; T = 0 is sized as T = 1). */
+size_t moe_ffn_backward_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
+                                       int32_t k);
+
 /* Bytes of workspace moe_ffn_forward needs for this shape (0 if the shape is
  * invalid or unsupported; T = 0 is sized as T = 1). */
 size_t moe_ffn_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,

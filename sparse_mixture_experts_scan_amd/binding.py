@@ -16,7 +16,8 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_BF16, MOE_F32, MOE_W4A16 = 0, 1, 2
 
 EXPORTED = ("moe_opts_init", "moe_ffn_forward", "moe_block_forward", "moe_quantize_int4",
-            "moe_ffn_forward_int4", "moe_ffn_workspace_size",
+            "moe_ffn_forward_int4", "moe_ffn_backward", "moe_ffn_backward_workspace_size",
+            "moe_ffn_workspace_size",
             "moe_ffn_workspace_layout", "moe_status_string", "moe_last_error",
             "moe_release", "moe_version")
 
@@ -36,6 +37,9 @@ class MoeOpts(ctypes.Structure):
 
 MOE_NUM_STAGES = 6
 STAGE_NAMES = ("router", "scan", "scatter", "gateup", "down", "combine")
+MOE_BWD_NUM_STAGES = 8
+BWD_STAGE_NAMES = ("routing", "recompute", "z", "rows_router", "dxs", "dx", "dw_down",
+                   "dw_gate_up")
 
 
 class MoeWsLayout(ctypes.Structure):
@@ -81,6 +85,11 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_forward_int4.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, i64,
                                            i64, i32, i32, ctypes.POINTER(MoeOpts)]
         L.moe_ffn_forward_int4.restype = ctypes.c_int
+        L.moe_ffn_backward.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp,
+                                       vp, i64, i64, i64, i32, i32, ctypes.POINTER(MoeOpts)]
+        L.moe_ffn_backward.restype = ctypes.c_int
+        L.moe_ffn_backward_workspace_size.argtypes = [i64, i64, i64, i32, i32]
+        L.moe_ffn_backward_workspace_size.restype = sz
         L.moe_ffn_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
         L.moe_ffn_workspace_size.restype = sz
         L.moe_ffn_workspace_layout.argtypes = [i64, i64, i64, i32, i32, i32,
@@ -131,6 +140,19 @@ def moe_ffn_forward_int4(x, W_router, Wg_q, Wg_s, Wu_q, Wu_s, Wd_q, Wd_s, group,
     return lib().moe_ffn_forward_int4(x, W_router, Wg_q, Wg_s, Wu_q, Wu_s, Wd_q, Wd_s, group,
                                       out, T, d_model, d_ff, E, k,
                                       ctypes.byref(opts) if opts is not None else None)
+
+
+def moe_ffn_backward(x, W_router, W_gate, W_up, W_down, dout, alpha, dx, dW_router, dbias,
+                     dW_gate, dW_up, dW_down, T, d_model, d_ff, E, k,
+                     opts: Optional[MoeOpts] = None) -> int:
+    """Raw entry point of the backward pass."""
+    return lib().moe_ffn_backward(x, W_router, W_gate, W_up, W_down, dout, alpha, dx, dW_router,
+                                  dbias, dW_gate, dW_up, dW_down, T, d_model, d_ff, E, k,
+                                  ctypes.byref(opts) if opts is not None else None)
+
+
+def moe_ffn_backward_workspace_size(T, d_model, d_ff, E, k) -> int:
+    return lib().moe_ffn_backward_workspace_size(T, d_model, d_ff, E, k)
 
 
 def moe_ffn_workspace_size(T, d_model, d_ff, E, k, dtype=MOE_BF16) -> int:
@@ -322,3 +344,47 @@ def forward_int4(x, W_router, W_gate, W_up, W_down, group: int, k: int, *, bias=
     if status != MOE_OK:
         raise MoeError(status, "moe_ffn_forward_int4")
     return out
+
+
+def backward(x, W_router, W_gate, W_up, W_down, dout, k: int, *, alpha=0.0, bias=None,
+             want_dbias=False, workspace=None, stream=None, stage_events=None):
+    """One moe_ffn_backward call on bf16 device tensors.  Returns a dict of
+    new tensors: dx [T][d] bf16, dW_router [d][E] fp32, dW_gate, dW_up,
+    dW_down (bf16, the stacks' shapes) and, with want_dbias, dbias [E] fp32."""
+    import torch
+
+    T, d = x.shape
+    E = W_router.shape[1]
+    d_ff = W_gate.shape[1]
+    if x.dtype != torch.bfloat16:
+        raise TypeError("the backward takes bfloat16 tensors")
+    for t, shape, dt in ((x, (T, d), torch.bfloat16), (dout, (T, d), torch.bfloat16),
+                         (W_router, (d, E), torch.float32),
+                         (W_gate, (E, d_ff, d), torch.bfloat16),
+                         (W_up, (E, d_ff, d), torch.bfloat16),
+                         (W_down, (E, d, d_ff), torch.bfloat16)):
+        _check(t, shape, dt, x)
+    g = dict(dx=torch.empty_like(x),
+             dW_router=torch.empty((d, E), dtype=torch.float32, device=x.device),
+             dW_gate=torch.empty_like(W_gate), dW_up=torch.empty_like(W_up),
+             dW_down=torch.empty_like(W_down))
+    if want_dbias:
+        g["dbias"] = torch.empty((E,), dtype=torch.float32, device=x.device)
+    o, _, _keep = _opts(x, E, k, MOE_BF16, bias, g["dx"], workspace, None, None, None, stream,
+                        None, None, None)
+    arr = None
+    if stage_events is not None:
+        if len(stage_events) != MOE_BWD_NUM_STAGES + 1:
+            raise ValueError("stage_events needs MOE_BWD_NUM_STAGES + 1 events")
+        arr = (ctypes.c_void_p * len(stage_events))(*[ev.cuda_event for ev in stage_events])
+        o.stage_events = ctypes.cast(arr, ctypes.c_void_p)
+    with torch.cuda.device(x.device):
+        status = moe_ffn_backward(x.data_ptr(), W_router.data_ptr(), W_gate.data_ptr(),
+                                  W_up.data_ptr(), W_down.data_ptr(), dout.data_ptr(),
+                                  float(alpha), g["dx"].data_ptr(), g["dW_router"].data_ptr(),
+                                  g["dbias"].data_ptr() if want_dbias else None,
+                                  g["dW_gate"].data_ptr(), g["dW_up"].data_ptr(),
+                                  g["dW_down"].data_ptr(), T, d, d_ff, E, k, o)
+    if status != MOE_OK:
+        raise MoeError(status, "moe_ffn_backward")
+    return g

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_ffn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["route_permute.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_q4.hip", "moe_ffn.hip"]
+SOURCES = ["route_permute.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_q4.hip", "gemm_bwd.hip",
+           "moe_ffn.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are switched off for all device code; hipcc's host pass

@@ -1,0 +1,480 @@
+// Backward pass of the sparse MoE layer: a grouped bf16 GEMM for every
+// contraction the chain rule needs, and the elementwise, router and gather
+// steps around them.
+//
+// "Mistral/Mixtralのアーキテクチャ", sections "各エキスパートの構造" (E_i(x) =
+// W2 (SiLU(W1 x) * W3 x)), "Top-2ゲーティングの定式化" (gates = softmax over
+// the selected scores) and "ロードバランス損失" (the training loss adds
+// alpha * N * sum_i f_i p_i).  Per routed row r = (t, j) of expert e, with
+// a = W1 x_t, b = W3 x_t, h = SiLU(a) * b, upstream gradient dOut_t:
+//   Z = W2^T dOut_t, dg_tj = <Z, h>, dA = g Z * b * SiLU'(a), dB = g Z * SiLU(a)
+//   dX_r = W1^T dA + W3^T dB
+//   dW2 += (g dOut_t) h^T, dW1 += dA x_t^T, dW3 += dB x_t^T
+// then the softmax over the k gates, the balance term, the router weight
+// gradient and dx_t = sum_j dX_r + W_router ds_t.
+//
+// The grouped GEMM: C[M][N] = sum_k A[m][k] B[k][n] on 128x128 tiles, K in
+// steps of 32, four waves of 64x64 (v_mfma_f32_32x32x16_bf16), both operands
+// staged in LDS as [row][k] with k contiguous (the MFMA operand layout).  An
+// operand whose k is contiguous in memory is copied in 16-byte pieces; one
+// whose k is the slow index (a row-major matrix read down its columns) is
+// transposed on its way into LDS.  Groups are either row segments of the
+// permuted layout (a tile table: expert, first row, rows) with the expert's
+// weights as the other operand, or experts with the contraction running over
+// the expert's rows (weight gradients).  Fixed summation order throughout.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kGT = 256;          // threads
+constexpr int kGM = 128;          // tile rows (M)
+constexpr int kGN = 128;          // tile columns (N)
+constexpr int kGK = 32;           // K per stage
+constexpr int kGLd = kGK + 8;     // LDS row pitch in elements (80 bytes)
+constexpr int kGOper = kGM * kGLd;  // elements per operand tile
+constexpr int kBufCfg = 0x00020000;
+
+__device__ inline __amdgpu_buffer_rsrc_t g_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, kBufCfg);
+}
+
+__device__ __forceinline__ uint4 g_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ inline f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// One operand tile (128 rows x 32 k) of one stage: registers between the
+// global load and the LDS store.
+//   KC (k contiguous): 128 rows of 64 bytes; thread t loads rows t/4 and
+//     t/4 + 64, 16-byte piece t%4.
+//   KS (k slow): 32 rows of k, 128 contiguous elements each; thread t loads
+//     k = 2 (t%16) and k + 1, elements 8 (t/16) .. +8, and stores eight
+//     (k, k+1) pairs into eight LDS rows.
+template <bool KC>
+struct GOperand {
+  uint4 v0, v1;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t ld_bytes, int k0,
+                                       int col0, int tid) {
+    if constexpr (KC) {
+      const int row = tid >> 2, piece = tid & 3;
+      const uint32_t off = (uint32_t)row * ld_bytes + (uint32_t)(k0 + piece * 8) * 2;
+      v0 = g_load16(r, off);
+      v1 = g_load16(r, off + 64 * ld_bytes);
+    } else {
+      const int k = k0 + 2 * (tid & 15), c8 = tid >> 4;
+      const uint32_t off = (uint32_t)k * ld_bytes + (uint32_t)(col0 + c8 * 8) * 2;
+      v0 = g_load16(r, off);
+      v1 = g_load16(r, off + ld_bytes);
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
+    if constexpr (KC) {
+      const int row = tid >> 2, piece = tid & 3;
+      *reinterpret_cast<uint4*>(lds + row * kGLd + piece * 8) = v0;
+      *reinterpret_cast<uint4*>(lds + (row + 64) * kGLd + piece * 8) = v1;
+    } else {
+      const int kk = 2 * (tid & 15), c8 = tid >> 4;
+      const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w};
+      const uint32_t b[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t lo = (a[w] & 0xFFFFu) | (b[w] << 16);          // element 2w
+        const uint32_t hi = (a[w] >> 16) | (b[w] & 0xFFFF0000u);      // element 2w + 1
+        *reinterpret_cast<uint32_t*>(lds + (c8 * 8 + 2 * w) * kGLd + kk) = lo;
+        *reinterpret_cast<uint32_t*>(lds + (c8 * 8 + 2 * w + 1) * kGLd + kk) = hi;
+      }
+    }
+  }
+};
+
+}  // namespace
+
+// Grouped GEMM.  mode 0 (row segments): tile i of the table covers rows
+// tb_row0[i] .. + tb_rows[i] of A and C, which belong to expert tb_exp[i];
+// B is that expert's matrix (B + e * b_estride).  mode 1 (weight gradients):
+// blockIdx.z = expert e, the contraction runs over rows offsets[e] ..
+// offsets[e] + counts[e] of A and B (both k-slow), C = C + e * c_estride.
+// A: k-contiguous (KCA) rows of lda elements, or k-slow rows of k.  B:
+// k-contiguous rows of N (one row per output column) or k-slow rows of k.
+// C: float (accumulate: C += result) or bf16, row pitch ldc.
+template <bool KCA, bool KCB, int MODE, bool CBF16>
+__global__ __launch_bounds__(kGT) void grouped_gemm_kernel(
+    const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ B, int ldb,
+    size_t b_estride, void* __restrict__ C, int ldc, size_t c_estride, int M, int N, int K,
+    bool accumulate, const int32_t* __restrict__ tb_count, const int32_t* __restrict__ tb_exp,
+    const int32_t* __restrict__ tb_row0, const int32_t* __restrict__ tb_rows,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets) {
+  __shared__ __attribute__((aligned(16))) bf16_t lA[2][kGOper];
+  __shared__ __attribute__((aligned(16))) bf16_t lB[2][kGOper];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int n0 = blockIdx.x * kGN;
+
+  int m0, rows, kn;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  size_t c_base;
+  if constexpr (MODE == 0) {
+    const int i = blockIdx.y;
+    if (i >= *tb_count) return;
+    const int e = tb_exp[i];
+    m0 = tb_row0[i];
+    rows = tb_rows[i];
+    kn = K;
+    // A: rows m0 .. m0 + rows (k contiguous), past them zeros
+    ra = g_rsrc(A + (size_t)m0 * lda, (uint32_t)rows * lda * 2);
+    const bf16_t* Be = B + (size_t)e * b_estride;
+    if constexpr (KCB) rb = g_rsrc(Be + (size_t)n0 * ldb, (uint32_t)kGN * ldb * 2);
+    else rb = g_rsrc(Be, (uint32_t)K * ldb * 2);
+    c_base = (size_t)m0 * ldc;
+  } else {
+    const int e = blockIdx.z;
+    m0 = blockIdx.y * kGM;
+    rows = kGM;
+    kn = counts[e];
+    const int r0 = offsets[e];
+    ra = g_rsrc(A + (size_t)r0 * lda, (uint32_t)kn * lda * 2);
+    rb = g_rsrc(B + (size_t)r0 * ldb, (uint32_t)kn * ldb * 2);
+    c_base = (size_t)e * c_estride + (size_t)m0 * ldc;
+  }
+  const uint32_t lda_b = (uint32_t)lda * 2, ldb_b = (uint32_t)ldb * 2;
+  // A tile origin: k-contiguous rows start at m0 (already in the resource for
+  // mode 0); k-slow columns start at m0
+  const int a_col0 = KCA ? 0 : m0;
+  const int b_col0 = KCB ? 0 : n0;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
+
+  GOperand<KCA> ga;
+  GOperand<KCB> gb;
+  const int nk = (kn + kGK - 1) / kGK;
+  if (nk > 0) {
+    ga.load(ra, lda_b, 0, a_col0, tid);
+    gb.load(rb, ldb_b, 0, b_col0, tid);
+    ga.store(lA[0], tid);
+    gb.store(lB[0], tid);
+  }
+  __syncthreads();
+  const int r32 = lane & 31, half = lane >> 5;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      ga.load(ra, lda_b, (kt + 1) * kGK, a_col0, tid);
+      gb.load(rb, ldb_b, (kt + 1) * kGK, b_col0, tid);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks) {
+      uint4 af[2], bf[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        af[a] = *reinterpret_cast<const uint4*>(&lA[cur][(wm * 64 + a * 32 + r32) * kGLd +
+                                                          ks * 16 + half * 8]);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        bf[b] = *reinterpret_cast<const uint4*>(&lB[cur][(wn * 64 + b * 32 + r32) * kGLd +
+                                                          ks * 16 + half * 8]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bf[b], acc[a][b]);
+    }
+    if (kt + 1 < nk) {
+      ga.store(lA[cur ^ 1], tid);
+      gb.store(lB[cur ^ 1], tid);
+    }
+    __syncthreads();
+  }
+
+  // D of a 32x32 MFMA: lane holds column n = lane % 32 and rows
+  // 8 * (j / 4) + 4 * (lane / 32) + j % 4.
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int n = n0 + wn * 64 + b * 32 + r32;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int m = wm * 64 + a * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+        if (m >= rows || m0 + m >= M) continue;
+        const size_t idx = c_base + (size_t)m * ldc + n;
+        if constexpr (CBF16) {
+          reinterpret_cast<bf16_t*>(C)[idx] = Elem<bf16_t>::from_f32(acc[a][b][j]);
+        } else {
+          float* c = reinterpret_cast<float*>(C) + idx;
+          *c = accumulate ? *c + acc[a][b][j] : acc[a][b][j];
+        }
+      }
+    }
+}
+
+// Tile table of mode 0: expert segments in order, each cut into 128-row
+// tiles.  One thread (the table is at most E + rows / 128 long).
+__global__ void bwd_tile_table_kernel(const int32_t* __restrict__ counts,
+                                      const int32_t* __restrict__ offsets, int E, int max_tiles,
+                                      int32_t* __restrict__ tb_count, int32_t* __restrict__ tb_exp,
+                                      int32_t* __restrict__ tb_row0,
+                                      int32_t* __restrict__ tb_rows) {
+  if (threadIdx.x != 0) return;
+  int n = 0;
+  for (int e = 0; e < E; ++e) {
+    for (int r = 0; r < counts[e] && n < max_tiles; r += kGM, ++n) {
+      tb_exp[n] = e;
+      tb_row0[n] = offsets[e] + r;
+      tb_rows[n] = min(kGM, counts[e] - r);
+    }
+  }
+  *tb_count = n;
+}
+
+// Permuted copy of the upstream gradient: Dp[r] = dOut[token of r], zero
+// rows for padding.
+__global__ __launch_bounds__(256) void bwd_gather_kernel(const bf16_t* __restrict__ src,
+                                                         const int32_t* __restrict__ row_token,
+                                                         int d, bf16_t* __restrict__ dst) {
+  const int r = blockIdx.x;
+  const int t = row_token[r];
+  uint4* out = reinterpret_cast<uint4*>(dst + (size_t)r * d);
+  const uint4* in = reinterpret_cast<const uint4*>(src + (size_t)(t < 0 ? 0 : t) * d);
+  for (int c = threadIdx.x; c < d / 8; c += 256) out[c] = t < 0 ? make_uint4(0, 0, 0, 0) : in[c];
+}
+
+// Per permuted row: a, b (pre-activations, float32 from the recompute GEMMs),
+// Z = W2^T dOut_t.  dg[r] = <Z, h> (fixed-order block sum), dAB[r] = [g Z b
+// SiLU'(a) | g Z SiLU(a)] and Hg[r] = g h (bf16), zeros on padding rows.
+__global__ __launch_bounds__(256) void bwd_rows_kernel(
+    const float* __restrict__ AB, const float* __restrict__ Z, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ tok_row, const float* __restrict__ gates, int f, int k,
+    float* __restrict__ dg, bf16_t* __restrict__ dAB, bf16_t* __restrict__ Hg) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int t = row_token[r];
+  __shared__ float wsum[4];
+  float g = 0.f;
+  if (t >= 0)
+    for (int j = 0; j < k; ++j)
+      if (tok_row[(size_t)t * k + j] == r) g = gates[(size_t)t * k + j];
+  const float* a_row = AB + (size_t)r * 2 * f;
+  const float* b_row = a_row + f;
+  const float* z_row = Z + (size_t)r * f;
+  bf16_t* da_row = dAB + (size_t)r * 2 * f;
+  bf16_t* db_row = da_row + f;
+  bf16_t* hg_row = Hg + (size_t)r * f;
+  float part = 0.f;
+  for (int c = tid; c < f; c += 256) {
+    float dav = 0.f, dbv = 0.f, hgv = 0.f;
+    if (t >= 0) {
+      const float a = a_row[c], b = b_row[c], z = z_row[c];
+      const float sig = 1.0f / (1.0f + expf(-a));
+      const float s = a * sig;
+      const float h = s * b;
+      part = fmaf(z, h, part);
+      const float dh = g * z;
+      dav = dh * b * (sig * (1.0f + a * (1.0f - sig)));
+      dbv = dh * s;
+      hgv = g * h;
+    }
+    da_row[c] = Elem<bf16_t>::from_f32(dav);
+    db_row[c] = Elem<bf16_t>::from_f32(dbv);
+    hg_row[c] = Elem<bf16_t>::from_f32(hgv);
+  }
+  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+  if ((tid & 63) == 0) wsum[tid >> 6] = part;
+  __syncthreads();
+  if (tid == 0) dg[r] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
+// Per token: ds_t over all E experts.  Selected experts: the softmax over the
+// k gates, ds = g (dg - sum_l g_l dg_l); with alpha > 0 the balance term
+// (alpha N / T) P_tm (f_m - sum_i f_i P_ti), P the full softmax of the scores.
+__global__ __launch_bounds__(64) void bwd_router_kernel(
+    const float* __restrict__ logits, const int32_t* __restrict__ idx,
+    const float* __restrict__ gates, const int32_t* __restrict__ tok_row,
+    const float* __restrict__ dg_row, const int32_t* __restrict__ counts, int T, int E, int k,
+    float alpha, float* __restrict__ ds) {
+  const int t = blockIdx.x * 64 + threadIdx.x;
+  if (t >= T) return;
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j)
+    sum += gates[(size_t)t * k + j] * dg_row[tok_row[(size_t)t * k + j]];
+  const float* s = logits + (size_t)t * E;
+  float m = s[0], inv = 0.f, pc = 0.f;
+  // alpha N / T with f = counts / T
+  const float scale = alpha * (float)E / ((float)T * (float)T);
+  if (alpha != 0.f) {
+    for (int e = 1; e < E; ++e) m = fmaxf(m, s[e]);
+    float z = 0.f;
+    for (int e = 0; e < E; ++e) z += expf(s[e] - m);
+    inv = 1.f / z;
+    for (int e = 0; e < E; ++e) pc += expf(s[e] - m) * inv * (float)counts[e];
+  }
+  for (int e = 0; e < E; ++e) {
+    float v = 0.f;
+    for (int j = 0; j < k; ++j)
+      if (idx[(size_t)t * k + j] == e)
+        v = gates[(size_t)t * k + j] * (dg_row[tok_row[(size_t)t * k + j]] - sum);
+    if (alpha != 0.f) v += scale * (expf(s[e] - m) * inv) * ((float)counts[e] - pc);
+    ds[(size_t)t * E + e] = v;
+  }
+}
+
+// Router weight gradient, partial over a slice of tokens: part[s][j][e] =
+// sum over tokens of slice s (in order) of x[t][j] ds[t][e]; and the bias
+// gradient part (column j = d).  Block: 64 columns j x E experts.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(
+    const T* __restrict__ x, const float* __restrict__ ds, int Tn, int d, int E, int tslice,
+    float* __restrict__ part) {
+  const int j = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int s = blockIdx.y;
+  const int t0 = s * tslice, t1 = min(Tn, t0 + tslice);
+  for (int e = threadIdx.x >> 6; e < E; e += 4) {
+    float acc = 0.f;
+    if (j <= d)
+      for (int t = t0; t < t1; ++t)
+        acc = fmaf(j < d ? Elem<T>::to_f32(x[(size_t)t * d + j]) : 1.0f, ds[(size_t)t * E + e],
+                   acc);
+    if (j <= d) part[((size_t)s * (d + 1) + j) * E + e] = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_router_wgrad_reduce(const float* __restrict__ part,
+                                                               int slices, int d, int E,
+                                                               float* __restrict__ dWr,
+                                                               float* __restrict__ dbias) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= (d + 1) * E) return;
+  float acc = 0.f;
+  for (int s = 0; s < slices; ++s) acc += part[(size_t)s * (d + 1) * E + i];
+  if (i < d * E) dWr[i] = acc;
+  else if (dbias) dbias[i - d * E] = acc;
+}
+
+// dx_t = sum_j dX[tok_row[t][j]] (slot order) + sum_e W_router[.][e] ds_t[e]
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dX,
+                                                     const int32_t* __restrict__ tok_row,
+                                                     const float* __restrict__ Wr,
+                                                     const float* __restrict__ ds, int d, int E,
+                                                     int k, T* __restrict__ dx) {
+  const int t = blockIdx.x;
+  __shared__ float sds[64];
+  if (threadIdx.x < E) sds[threadIdx.x] = ds[(size_t)t * E + threadIdx.x];
+  __syncthreads();
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) acc += dX[(size_t)tok_row[(size_t)t * k + j] * d + c];
+    float rt = 0.f;
+    for (int e = 0; e < E; ++e) rt = fmaf(Wr[(size_t)c * E + e], sds[e], rt);
+    dx[(size_t)t * d + c] = Elem<T>::from_f32(acc + rt);
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* __restrict__ p, size_t n16,
+                                                        uint8_t* __restrict__ tail, int ntail) {
+  for (size_t i = blockIdx.x * (size_t)256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+// ---------------------------------------------------------------- launchers
+void launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
+  if (!p || bytes == 0) return;
+  const size_t n16 = bytes / 16;
+  const size_t want = (n16 + 255) / 256;
+  const unsigned grid = (unsigned)(want < 4096 ? (want > 0 ? want : 1) : 4096);
+  zero_fill_kernel<<<grid, 256, 0, s>>>((uint4*)p, n16, (uint8_t*)p + n16 * 16,
+                                        (int)(bytes - n16 * 16));
+}
+
+constexpr int kBwdRouterSlices = 32;
+
+int bwd_gemm_tile_rows() { return kGM; }
+int bwd_router_slices() { return kBwdRouterSlices; }
+
+void launch_bwd_tile_table(const Dims& D, const int32_t* counts, const int32_t* offsets,
+                           int max_tiles, int32_t* tb_count, int32_t* tb_exp, int32_t* tb_row0,
+                           int32_t* tb_rows, hipStream_t s) {
+  bwd_tile_table_kernel<<<1, 64, 0, s>>>(counts, offsets, D.E, max_tiles, tb_count, tb_exp,
+                                         tb_row0, tb_rows);
+}
+
+void launch_bwd_gather(const Dims& D, const void* src, const int32_t* row_token, void* dst,
+                       hipStream_t s) {
+  bwd_gather_kernel<<<D.max_rows, 256, 0, s>>>((const bf16_t*)src, row_token, D.d,
+                                               (bf16_t*)dst);
+}
+
+void launch_bwd_gemm_rows(const void* A, int lda, const void* B, int ldb, bool b_kcontig,
+                          size_t b_estride, float* C, int ldc, int M, int N, int K,
+                          bool accumulate, int max_tiles, const int32_t* tb_count,
+                          const int32_t* tb_exp, const int32_t* tb_row0, const int32_t* tb_rows,
+                          hipStream_t s) {
+  const dim3 grid(N / kGN, max_tiles);
+  if (b_kcontig)
+    grouped_gemm_kernel<true, true, 0, false><<<grid, kGT, 0, s>>>(
+        (const bf16_t*)A, lda, (const bf16_t*)B, ldb, b_estride, C, ldc, 0, M, N, K,
+        accumulate, tb_count, tb_exp, tb_row0, tb_rows, nullptr, nullptr);
+  else
+    grouped_gemm_kernel<true, false, 0, false><<<grid, kGT, 0, s>>>(
+        (const bf16_t*)A, lda, (const bf16_t*)B, ldb, b_estride, C, ldc, 0, M, N, K,
+        accumulate, tb_count, tb_exp, tb_row0, tb_rows, nullptr, nullptr);
+}
+
+void launch_bwd_gemm_wgrad(const Dims& D, const void* A, int lda, const void* B, int ldb,
+                           void* C, int M, int N, const int32_t* counts, const int32_t* offsets,
+                           hipStream_t s) {
+  const dim3 grid(N / kGN, M / kGM, D.E);
+  grouped_gemm_kernel<false, false, 1, true><<<grid, kGT, 0, s>>>(
+      (const bf16_t*)A, lda, (const bf16_t*)B, ldb, 0, C, N, (size_t)M * N, M, N, 0, false,
+      nullptr, nullptr, nullptr, nullptr, counts, offsets);
+}
+
+void launch_bwd_rows(const Dims& D, const float* AB, const float* Z, const int32_t* row_token,
+                     const int32_t* tok_row, const float* gates, float* dg, void* dAB, void* Hg,
+                     hipStream_t s) {
+  bwd_rows_kernel<<<D.max_rows, 256, 0, s>>>(AB, Z, row_token, tok_row, gates, D.f, D.k, dg,
+                                             (bf16_t*)dAB, (bf16_t*)Hg);
+}
+
+void launch_bwd_router(const Dims& D, const float* logits, const int32_t* idx, const float* gates,
+                       const int32_t* tok_row, const float* dg_row, const int32_t* counts,
+                       float alpha, float* ds, hipStream_t s) {
+  bwd_router_kernel<<<(D.T + 63) / 64, 64, 0, s>>>(logits, idx, gates, tok_row, dg_row, counts,
+                                                    D.T, D.E, D.k, alpha, ds);
+}
+
+void launch_bwd_router_wgrad(const Dims& D, const void* x, const float* ds, float* part,
+                             float* dWr, float* dbias, hipStream_t s) {
+  const int slices = kBwdRouterSlices;
+  const int tslice = (D.T + slices - 1) / slices;
+  const dim3 grid((D.d + 1 + 63) / 64, slices);
+  bwd_router_wgrad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)x, ds, D.T, D.d, D.E,
+                                                       tslice, part);
+  bwd_router_wgrad_reduce<<<((D.d + 1) * D.E + 255) / 256, 256, 0, s>>>(part, slices, D.d, D.E,
+                                                                       dWr, dbias);
+}
+
+void launch_bwd_dx(const Dims& D, const float* dX, const int32_t* tok_row, const float* Wr,
+                   const float* ds, void* dx, hipStream_t s) {
+  bwd_dx_kernel<bf16_t><<<D.T, 256, 0, s>>>(dX, tok_row, Wr, ds, D.d, D.E, D.k, (bf16_t*)dx);
+}
+
+}  // namespace moe

@@ -33,9 +33,10 @@ void launch_rmsnorm(const Dims& D, const void* x, const float* weight, float eps
 // blk_prob: [nblk][E] per-block full-softmax probability sums, or NULL.
 // gamma, rs (both or neither): scores of the RMS-normalised tokens,
 // rs[t] * sum_j x[t][j] gamma[j] W[j][e]
+// logits_out: [T][E] final scores (with bias), or NULL.
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
                    int32_t* idx, float* w, int32_t* blk_counts, float* part, float* blk_prob,
-                   const float* gamma, const float* rs, hipStream_t s);
+                   const float* gamma, const float* rs, float* logits_out, hipStream_t s);
 int router_splits_for(int nblk, int d);
 constexpr int kRouterPartStride = 64;  // floats per token row of the partial scores
 // a2: histogram reduce, padded offsets, per-block bases, tile table
@@ -80,6 +81,35 @@ void launch_gateup_q4(const Dims& D, const void* xs, const Q4Weights& Wg, const 
 void launch_down_q4(const Dims& D, const void* h, const Q4Weights& Wd, float* y,
                     const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                     const int32_t* tile_expert, hipStream_t s);
+// backward (bf16): grouped GEMMs and the steps around them
+int bwd_gemm_tile_rows();
+int bwd_router_slices();
+void launch_bwd_tile_table(const Dims& D, const int32_t* counts, const int32_t* offsets,
+                           int max_tiles, int32_t* tb_count, int32_t* tb_exp, int32_t* tb_row0,
+                           int32_t* tb_rows, hipStream_t s);
+void launch_bwd_gather(const Dims& D, const void* src, const int32_t* row_token, void* dst,
+                       hipStream_t s);
+// C[rows of tile][N] (+)= A[rows][K] (k contiguous) x B_e, per tile of the table
+void launch_bwd_gemm_rows(const void* A, int lda, const void* B, int ldb, bool b_kcontig,
+                          size_t b_estride, float* C, int ldc, int M, int N, int K,
+                          bool accumulate, int max_tiles, const int32_t* tb_count,
+                          const int32_t* tb_exp, const int32_t* tb_row0, const int32_t* tb_rows,
+                          hipStream_t s);
+// C_e[M][N] = sum over expert e's rows r of A[r][m] B[r][n] (bf16 out)
+void launch_bwd_gemm_wgrad(const Dims& D, const void* A, int lda, const void* B, int ldb,
+                           void* C, int M, int N, const int32_t* counts, const int32_t* offsets,
+                           hipStream_t s);
+void launch_bwd_rows(const Dims& D, const float* AB, const float* Z, const int32_t* row_token,
+                     const int32_t* tok_row, const float* gates, float* dg, void* dAB, void* Hg,
+                     hipStream_t s);
+void launch_bwd_router(const Dims& D, const float* logits, const int32_t* idx, const float* gates,
+                       const int32_t* tok_row, const float* dg_row, const int32_t* counts,
+                       float alpha, float* ds, hipStream_t s);
+void launch_bwd_router_wgrad(const Dims& D, const void* x, const float* ds, float* part,
+                             float* dWr, float* dbias, hipStream_t s);
+void launch_bwd_dx(const Dims& D, const float* dX, const int32_t* tok_row, const float* Wr,
+                   const float* ds, void* dx, hipStream_t s);
+void launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 // a5: gate-weighted gather-sum back to token order
 // resid: x for the block wrapper (out = x + layer), or NULL
 // T = 0: zero the optional statistics outputs (any may be null).

@@ -4,6 +4,7 @@
 // all asynchronous on the caller's stream with no host synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <map>
@@ -127,6 +128,29 @@ int hip_fail(hipError_t e, const char* what) {
   return fail(MOE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// The library-owned workspace of the current device, grown to `bytes`.
+int library_workspace(size_t bytes, char** ws) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  CachedWs& c = g_ws[dev];
+  if (c.bytes < bytes) {
+    if (c.ptr) {
+      e = hipDeviceSynchronize();  // the old buffer may still be in use
+      if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+      (void)hipFree(c.ptr);
+      c.ptr = nullptr;
+      c.bytes = 0;
+    }
+    e = hipMalloc(&c.ptr, bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+    c.bytes = bytes;
+  }
+  *ws = static_cast<char*>(c.ptr);
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -209,26 +233,7 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   // ---- validated; from here on HIP calls
   hipStream_t s = reinterpret_cast<hipStream_t>(o.stream);
   char* ws = static_cast<char*>(o.workspace);
-  if (!ws) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    CachedWs& c = g_ws[dev];
-    if (c.bytes < p.L.total) {
-      if (c.ptr) {
-        e = hipDeviceSynchronize();  // the old buffer may still be in use
-        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-        (void)hipFree(c.ptr);
-        c.ptr = nullptr;
-        c.bytes = 0;
-      }
-      e = hipMalloc(&c.ptr, p.L.total);
-      if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
-      c.bytes = p.L.total;
-    }
-    ws = static_cast<char*>(c.ptr);
-  }
+  if (!ws && (st = library_workspace(p.L.total, &ws)) != MOE_OK) return st;
   const moe::Dims& D = p.D;
   const moe_ws_layout_t& L = p.L;
   int32_t* idx = o.topk_idx_out ? o.topk_idx_out : reinterpret_cast<int32_t*>(ws + L.topk_idx);
@@ -259,7 +264,8 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
     moe::launch_rmsnorm(D, x, norm_w, eps, rs, xn, s);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "rmsnorm launch");
   }
-  moe::launch_router(D, x, W_router, o.router_bias, idx, w, blk, rpart, bprob, norm_w, rs, s);
+  moe::launch_router(D, x, W_router, o.router_bias, idx, w, blk, rpart, bprob, norm_w, rs,
+                     nullptr, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess)
     return hip_fail(e, "router launch");
   moe::launch_scan(D, blk, counts, offsets, num_tiles, tile_expert, row_token,
@@ -384,6 +390,214 @@ int moe_ffn_forward_int4(const void* x, const float* W_router, const uint8_t* Wg
   // the weight arguments of the plain path stand in for the non-null checks
   return run_layer(x, W_router, Wg_q, Wu_q, Wd_q, out, T, d_model, d_ff, E, k, nullptr, 0.f,
                    opts, q4, group);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Backward workspace: the forward routing and permutation (16-row padding),
+// the recomputed pre-activations and every gradient intermediate.
+struct BwdPlan {
+  moe::Dims D;
+  int max_tiles;  // rows of the 128-row tile table
+  size_t topk_idx, topk_w, block_counts, counts, offsets, num_tiles, tile_expert, row_token,
+      tok_row, xs, logits, router_partial, ab, z, dab, hg, dp, dxs, dg, ds, wpart, tb, total;
+};
+
+int make_bwd_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, BwdPlan* b) {
+  Plan p;
+  int st = make_plan(T, d, f, E, k, MOE_BF16, &p);
+  if (st != MOE_OK) return st;
+  if (d % 128 || f % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "the backward needs d_model and d_ff multiples of 128");
+  // 32-bit buffer ranges: one expert's rows of the widest row-major operand
+  if ((int64_t)T * std::max<int64_t>(2 * f, d) * 4 >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T * max(2 d_ff, d_model) too large for the backward");
+  moe::Dims& D = b->D;
+  D = p.D;
+  D.BT = 16;
+  const int64_t A = T * k;
+  int64_t max_rows = A + (int64_t)E * (D.BT - 1);
+  max_rows = (max_rows + D.BT - 1) / D.BT * D.BT;
+  D.max_rows = (int)max_rows;
+  D.max_tiles = (int)(max_rows / D.BT);
+  D.down_splits = 1;
+  const int tr = moe::bwd_gemm_tile_rows();
+  b->max_tiles = (int)((A + tr - 1) / tr + E);
+  const size_t R = (size_t)max_rows;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  b->topk_idx = take(4 * A);
+  b->topk_w = take(4 * A);
+  b->block_counts = take(4 * (size_t)D.nblk * E);
+  b->counts = take(4 * (size_t)E);
+  b->offsets = take(4 * (size_t)(E + 1));
+  b->num_tiles = take(4);
+  b->tile_expert = take(4 * (size_t)D.max_tiles);
+  b->row_token = take(4 * R);
+  b->tok_row = take(4 * A);
+  b->xs = take(2 * R * d);
+  b->logits = take(4 * (size_t)T * E);
+  b->router_partial = take(D.router_splits > 1 ? sizeof(float) * D.router_splits * D.nblk *
+                                                     moe::kRouterTokens * moe::kRouterPartStride
+                                               : 0);
+  b->ab = take(4 * R * 2 * f);
+  b->z = take(4 * R * f);
+  b->dab = take(2 * R * 2 * f);
+  b->hg = take(2 * R * f);
+  b->dp = take(2 * R * d);
+  b->dxs = take(4 * R * d);
+  b->dg = take(4 * R);
+  b->ds = take(4 * (size_t)T * E);
+  b->wpart = take(4 * (size_t)moe::bwd_router_slices() * (d + 1) * E);
+  b->tb = take(4 * (size_t)(1 + 3 * b->max_tiles));
+  b->total = off;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_ffn_backward_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
+                                       int32_t k) {
+  g_last_error.clear();
+  BwdPlan b;
+  if (make_bwd_plan(T == 0 ? 1 : T, d_model, d_ff, E, k, &b) != MOE_OK) return 0;
+  return b.total;
+}
+
+int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, const void* W_up,
+                     const void* W_down, const void* dout, float alpha, void* dx,
+                     float* dW_router, float* dbias, void* dW_gate, void* dW_up, void* dW_down,
+                     int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                     const moe_opts_t* opts) {
+  g_last_error.clear();
+  moe_opts_t o;
+  if (opts) o = *opts;
+  else moe_opts_init(&o);
+  if (o.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward takes bf16 tensors");
+  if (!(alpha >= 0.f) || alpha > 1e30f) return fail(MOE_ERR_INVALID_ARG, "alpha must be >= 0");
+  BwdPlan b;
+  int st = make_bwd_plan(T == 0 ? 1 : T, d_model, d_ff, E, k, &b);
+  if (st != MOE_OK) return st;
+  if (!dW_router || !dW_gate || !dW_up || !dW_down)
+    return fail(MOE_ERR_INVALID_ARG, "null gradient pointer");
+  for (const void* ptr : {(const void*)dW_router, (const void*)dbias, (const void*)o.router_bias})
+    if (reinterpret_cast<uintptr_t>(ptr) % 4)
+      return fail(MOE_ERR_INVALID_ARG, "dW_router, dbias and the bias must be 4-byte aligned");
+  for (const void* ptr : {dW_gate, dW_up, dW_down})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16)
+      return fail(MOE_ERR_INVALID_ARG, "weight gradients must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(o.stream);
+  const size_t wbytes = sizeof(uint16_t) * (size_t)E * d_model * d_ff;
+  hipError_t e;
+  if (T == 0) {
+    // an empty batch: every gradient is zero
+    moe::launch_zero_fill(dW_router, sizeof(float) * (size_t)d_model * E, s);
+    moe::launch_zero_fill(dbias, sizeof(float) * (size_t)E, s);
+    moe::launch_zero_fill(dW_gate, wbytes, s);
+    moe::launch_zero_fill(dW_up, wbytes, s);
+    moe::launch_zero_fill(dW_down, wbytes, s);
+    e = hipGetLastError();
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "zero-fill launch");
+  }
+  if (!x || !W_router || !W_gate || !W_up || !W_down || !dout || !dx)
+    return fail(MOE_ERR_INVALID_ARG, "null tensor pointer");
+  for (const void* ptr : {x, (const void*)W_router, W_gate, W_up, W_down, dout, (const void*)dx})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16)
+      return fail(MOE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (o.workspace) {
+    if (reinterpret_cast<uintptr_t>(o.workspace) % 256)
+      return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (o.workspace_bytes < b.total)
+      return fail(MOE_ERR_WORKSPACE, "workspace too small: need " + std::to_string(b.total) +
+                                         " bytes");
+  }
+  char* ws = static_cast<char*>(o.workspace);
+  if (!ws && (st = library_workspace(b.total, &ws)) != MOE_OK) return st;
+
+  const moe::Dims& D = b.D;
+  const int d = (int)d_model, f = (int)d_ff;
+  auto I = [&](size_t off) { return reinterpret_cast<int32_t*>(ws + off); };
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  int32_t* idx = I(b.topk_idx);
+  float* w = F(b.topk_w);
+  int32_t* counts = I(b.counts);
+  int32_t* offsets = I(b.offsets);
+  int32_t* row_token = I(b.row_token);
+  int32_t* tok_row = I(b.tok_row);
+  int32_t* tb = I(b.tb);
+  int32_t *tb_count = tb, *tb_exp = tb + 1, *tb_row0 = tb + 1 + b.max_tiles,
+          *tb_rows = tb + 1 + 2 * b.max_tiles;
+  char* xs = ws + b.xs;
+  char* dp = ws + b.dp;
+  char* dab = ws + b.dab;
+  char* hg = ws + b.hg;
+  float* ab = F(b.ab);
+  float* z = F(b.z);
+  float* dxs = F(b.dxs);
+  float* dg = F(b.dg);
+  float* ds = F(b.ds);
+  const size_t wstride = (size_t)d * f;   // elements per expert matrix
+
+  auto mark = [&](int i) -> hipError_t {
+    return o.stage_events ? hipEventRecord(static_cast<hipEvent_t>(o.stage_events[i]), s)
+                          : hipSuccess;
+  };
+  auto check = [&](int stage, const char* what) -> int {
+    if ((e = hipGetLastError()) != hipSuccess || (e = mark(stage)) != hipSuccess)
+      return hip_fail(e, what);
+    return MOE_OK;
+  };
+  if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
+  // routing and permutation of the forward pass, the permuted upstream
+  // gradient and the 128-row tile table
+  moe::launch_router(D, x, W_router, o.router_bias, idx, w, I(b.block_counts),
+                     F(b.router_partial), nullptr, nullptr, nullptr, F(b.logits), s);
+  moe::launch_scan(D, I(b.block_counts), counts, offsets, I(b.num_tiles), I(b.tile_expert),
+                   row_token, nullptr, nullptr, nullptr, nullptr, s);
+  moe::launch_scatter(D, x, idx, I(b.block_counts), offsets, tok_row, row_token, xs, s);
+  moe::launch_bwd_gather(D, dout, row_token, dp, s);
+  moe::launch_bwd_tile_table(D, counts, offsets, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows,
+                             s);
+  if ((st = check(1, "routing launch")) != MOE_OK) return st;
+  // pre-activations a = W1 x, b = W3 x of every routed row
+  moe::launch_bwd_gemm_rows(xs, d, W_gate, d, true, wstride, ab, 2 * f, D.max_rows, f, d, false,
+                            b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+  moe::launch_bwd_gemm_rows(xs, d, W_up, d, true, wstride, ab + f, 2 * f, D.max_rows, f, d,
+                            false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+  if ((st = check(2, "recompute launch")) != MOE_OK) return st;
+  // Z = W2^T dOut_t per routed row
+  moe::launch_bwd_gemm_rows(dp, d, W_down, f, false, wstride, z, f, D.max_rows, f, d, false,
+                            b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+  if ((st = check(3, "Z launch")) != MOE_OK) return st;
+  // dg, dA, dB, g h; the router scores' gradient; the router weight gradient
+  moe::launch_bwd_rows(D, ab, z, row_token, tok_row, w, dg, dab, hg, s);
+  moe::launch_bwd_router(D, F(b.logits), idx, w, tok_row, dg, counts, alpha, ds, s);
+  moe::launch_bwd_router_wgrad(D, x, ds, F(b.wpart), dW_router, dbias, s);
+  if ((st = check(4, "row/router backward launch")) != MOE_OK) return st;
+  // dX_r = W1^T dA + W3^T dB
+  moe::launch_bwd_gemm_rows(dab, 2 * f, W_gate, d, false, wstride, dxs, d, D.max_rows, d, f,
+                            false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+  moe::launch_bwd_gemm_rows(dab + 2 * (size_t)f, 2 * f, W_up, d, false, wstride, dxs, d,
+                            D.max_rows, d, f, true, b.max_tiles, tb_count, tb_exp, tb_row0,
+                            tb_rows, s);
+  if ((st = check(5, "dX launch")) != MOE_OK) return st;
+  moe::launch_bwd_dx(D, dxs, tok_row, W_router, ds, dx, s);
+  if ((st = check(6, "dx launch")) != MOE_OK) return st;
+  // weight gradients over each expert's rows
+  moe::launch_bwd_gemm_wgrad(D, dp, d, hg, f, dW_down, d, f, counts, offsets, s);
+  if ((st = check(7, "dW_down launch")) != MOE_OK) return st;
+  moe::launch_bwd_gemm_wgrad(D, dab, 2 * f, xs, d, dW_gate, f, d, counts, offsets, s);
+  moe::launch_bwd_gemm_wgrad(D, dab + 2 * (size_t)f, 2 * f, xs, d, dW_up, f, d, counts, offsets,
+                             s);
+  return check(8, "dW_gate/dW_up launch");
 }
 
 const char* moe_status_string(int status) {

@@ -157,7 +157,8 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
     int nT, int d, int E, int k, int splits, float* __restrict__ part,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t* __restrict__ blk_counts,
-    float* __restrict__ blk_prob, const float* __restrict__ gamma, const float* __restrict__ rs) {
+    float* __restrict__ blk_prob, const float* __restrict__ gamma, const float* __restrict__ rs,
+    float* __restrict__ logits_out) {
   constexpr int TB = kRouterTokens;
   constexpr int NB = TB / 16;            // token column blocks
   constexpr int MB = 64 / 16;            // expert row blocks (max)
@@ -276,6 +277,9 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
   }
   if (splits > 1) return;
   __syncthreads();
+  if (logits_out)
+    for (int i = tid; i < TB * E; i += kRouterMfmaThreads)
+      if (t0 + i / E < nT) logits_out[(size_t)(t0 + i / E) * E + i % E] = slog[i / E][i % E];
   if (tid < TB && t0 + tid < nT)
     select_topk_token(slog[tid], E, k, (size_t)(t0 + tid), idx_out, w_out, hist);
   __syncthreads();
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int nT, int E, int k,
     int splits, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
     int32_t* __restrict__ blk_counts, float* __restrict__ blk_prob,
-    const float* __restrict__ rs) {
+    const float* __restrict__ rs, float* __restrict__ logits_out) {
   constexpr int TB = kRouterTokens;
   __shared__ float slog[TB][65];
   __shared__ int hist[64];
@@ -318,6 +322,9 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     slog[tt][e] = v * sc + (bias ? bias[e] : 0.f);
   }
   __syncthreads();
+  if (logits_out)
+    for (int i = tid; i < TB * E; i += kSelectThreads)
+      if (t0 + i / E < nT) logits_out[(size_t)(t0 + i / E) * E + i % E] = slog[i / E][i % E];
   if (tid < TB && t0 + tid < nT)
     select_topk_token(slog[tid], E, k, (size_t)(t0 + tid), idx_out, w_out, hist);
   __syncthreads();
@@ -546,19 +553,19 @@ void launch_rmsnorm(const Dims& D, const void* x, const float* weight, float eps
 
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
                    int32_t* idx, float* w, int32_t* blk_counts, float* part, float* blk_prob,
-                   const float* gamma, const float* rs, hipStream_t s) {
+                   const float* gamma, const float* rs, float* logits_out, hipStream_t s) {
   const dim3 grid(D.nblk, D.router_splits);
   if (D.bf16)
     router_topk_kernel<bf16_t><<<grid, kRouterMfmaThreads, 0, s>>>(
         (const bf16_t*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts,
-        blk_prob, gamma, rs);
+        blk_prob, gamma, rs, logits_out);
   else
     router_topk_kernel<float><<<grid, kRouterMfmaThreads, 0, s>>>(
         (const float*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts,
-        blk_prob, gamma, rs);
+        blk_prob, gamma, rs, logits_out);
   if (D.router_splits > 1)
     router_select_kernel<<<D.nblk, kSelectThreads, 0, s>>>(
-        part, bias, D.T, D.E, D.k, D.router_splits, idx, w, blk_counts, blk_prob, rs);
+        part, bias, D.T, D.E, D.k, D.router_splits, idx, w, blk_counts, blk_prob, rs, logits_out);
 }
 
 int router_splits_for(int nblk, int d) {

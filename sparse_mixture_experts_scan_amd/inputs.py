@@ -29,7 +29,7 @@ from typing import Optional
 
 import numpy as np
 
-X_ID, ROUTER_ID, GATE_ID, UP_ID, DOWN_ID, NORM_ID = 0, 1, 2, 3, 4, 5
+X_ID, ROUTER_ID, GATE_ID, UP_ID, DOWN_ID, NORM_ID, DOUT_ID = 0, 1, 2, 3, 4, 5, 6
 
 
 @dataclasses.dataclass(frozen=True)
@@ -162,3 +162,9 @@ def make_block_inputs(cfg: MoEConfig, seed: int = 0, threads: Optional[int] = No
     res["norm_weight"] = (1.0 + 0.25 * g.standard_normal(cfg.d_model, dtype=np.float32)
                           ).astype(np.float32)
     return res
+
+
+def make_dout(cfg: MoEConfig, seed: int = 0) -> np.ndarray:
+    """Upstream gradient of the layer's output for the backward pass:
+    [T][d_model] N(0, 1), in the workload's element type."""
+    return _draw(seed, DOUT_ID, 0, (cfg.T, cfg.d_model), 1.0, cfg.dtype == "bf16")

@@ -227,3 +227,35 @@ def test_int4_workspace_layout():
     lay = moe.moe_ffn_workspace_layout(4096, 4096, 14336, 8, 2, B.MOE_W4A16)
     assert lay.gemm_variant == 1
     assert lay.total - lay.wdeq >= 6 * 8 * 4096 * 14336 and lay.wdeq % 256 == 0
+
+
+def bwd(T=16, d=256, f=512, E=8, k=2, alpha=0.0, ptrs=None, opts=None):
+    p = ptrs or [DUMMY * (i + 1) for i in range(12)]
+    return moe.moe_ffn_backward(p[0], p[1], p[2], p[3], p[4], p[5], alpha, p[6], p[7], p[8],
+                                p[9], p[10], p[11], T, d, f, E, k, opts)
+
+
+def test_backward_validation():
+    assert bwd(d=192) == B.MOE_ERR_UNSUPPORTED           # d_model % 128
+    assert bwd(f=320) == B.MOE_ERR_UNSUPPORTED           # d_ff % 128
+    assert bwd(k=9) == B.MOE_ERR_INVALID_ARG
+    for a in (-0.5, float("nan")):
+        assert bwd(alpha=a) == B.MOE_ERR_INVALID_ARG
+    o = moe.moe_opts_init()
+    o.dtype = B.MOE_F32
+    assert bwd(opts=o) == B.MOE_ERR_UNSUPPORTED
+    for i in range(12):
+        if i == 8:                                       # dbias may be NULL
+            continue
+        p = [DUMMY * (j + 1) for j in range(12)]
+        p[i] = None
+        assert bwd(ptrs=p) == B.MOE_ERR_INVALID_ARG, i
+    p = [DUMMY * (j + 1) for j in range(12)]
+    p[9] = DUMMY + 8                                     # dW_gate needs 16 bytes
+    assert bwd(ptrs=p) == B.MOE_ERR_INVALID_ARG
+    o = moe.moe_opts_init()
+    o.workspace = DUMMY
+    o.workspace_bytes = 1024
+    assert bwd(opts=o) == B.MOE_ERR_WORKSPACE
+    assert moe.moe_ffn_backward_workspace_size(16, 256, 512, 8, 2) > 0
+    assert moe.moe_ffn_backward_workspace_size(16, 192, 512, 8, 2) == 0

@@ -1,0 +1,125 @@
+"""Backward pass of the layer on the GPU (moe_ffn_backward through the C ABI)
+against the fp64 oracle's moe_backward.
+
+"Mistral/Mixtralのアーキテクチャ", section "ロードバランス損失": the gradients
+of <dOut, MoE(x)> + alpha * N * sum f_i p_i.  Routing: the GPU forward's
+indices (the backward recomputes the same routing with the same kernels),
+exact away from near ties, handed to the oracle.  Values: every gradient
+within max|err| / max|ref| <= 2e-2 (bf16 tensors, fp32 accumulation).
+Also: an empty batch gives zero weight gradients, a zero W_down gives exactly
+zero gradients below it, and two runs are bitwise equal."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import sparse_mixture_experts_scan_amd as moe  # noqa: E402
+from sparse_mixture_experts_scan_amd.inputs import MoEConfig, make_dout, make_inputs  # noqa: E402
+from tests import gpu_harness as H  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-2
+GRADS = ("dx", "dW_router", "dW_gate", "dW_up", "dW_down")
+
+
+def announce(msg):
+    print(f"[gpu-bwd] {msg}", file=sys.stderr, flush=True)
+
+
+def run_bwd(cfg, inp, dout, alpha, want_dbias=False):
+    d = H.upload(inp)
+    ddo = H.dev_tensor(dout)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    moe.forward(d["x"], d["W_router"], d["W_gate"], d["W_up"], d["W_down"], cfg.k,
+                bias=d["bias"], topk_idx=idx)
+    g = moe.backward(d["x"], d["W_router"], d["W_gate"], d["W_up"], d["W_down"], ddo, cfg.k,
+                     alpha=alpha, bias=d["bias"], want_dbias=want_dbias)
+    torch.cuda.synchronize()
+    out = {n: H.as_f32(H.to_host(t)).astype(np.float64) for n, t in g.items()}
+    out["idx"] = idx.cpu().numpy()
+    return out
+
+
+def compare(cfg, inp, dout, alpha, res, names=GRADS):
+    s = oracle.router_logits(inp["x"], inp["W_router"], inp["bias"])
+    ref_idx = oracle.select_topk(s, cfg.k)
+    gap, _ = oracle.routing_gaps(s, cfg.k)
+    ok = gap >= H.NEAR_TIE
+    np.testing.assert_array_equal(np.sort(res["idx"][ok], axis=1), np.sort(ref_idx[ok], axis=1))
+    ref = oracle.moe_backward(inp["x"], inp["W_router"], inp["W_gate"], inp["W_up"],
+                              inp["W_down"], dout, cfg.k, bias=inp["bias"], alpha=alpha,
+                              forced_idx=res["idx"].astype(np.int64))
+    errs = {}
+    for n in names:
+        got, want = res[n], ref[n]
+        assert got.shape == want.shape, n
+        assert np.isfinite(got).all(), n
+        errs[n] = float(np.abs(got - want).max() / max(np.abs(want).max(), 1e-30))
+        assert errs[n] <= TOL, (n, errs[n])
+    return errs
+
+
+CASES = [
+    (MoEConfig("bwd_small", 64, 128, 256, 8, 2, "bf16"), 0.0),
+    (MoEConfig("bwd_alpha", 96, 256, 128, 8, 2, "bf16"), 0.05),
+    (MoEConfig("bwd_ragged", 77, 256, 384, 6, 3, "bf16"), 0.01),
+    (MoEConfig("bwd_fine", 130, 128, 128, 16, 4, "bf16"), 0.02),
+    (MoEConfig("bwd_single", 1, 128, 128, 4, 2, "bf16"), 0.1),
+    (MoEConfig("bwd_top1", 50, 128, 256, 4, 1, "bf16"), 0.0),
+    (MoEConfig("bwd_tiles", 700, 512, 640, 8, 2, "bf16"), 0.01),   # several 128-row tiles
+]
+
+
+@pytest.mark.parametrize("cfg,alpha", CASES, ids=lambda c: getattr(c, "name", str(c)))
+def test_backward_parity(cfg, alpha):
+    announce(f"case {cfg.name} T={cfg.T} d={cfg.d_model} f={cfg.d_ff} E={cfg.E} k={cfg.k} "
+             f"alpha={alpha}")
+    inp = make_inputs(cfg, seed=21)
+    dout = make_dout(cfg, seed=21)
+    res = run_bwd(cfg, inp, dout, alpha)
+    errs = compare(cfg, inp, dout, alpha, res)
+    announce("  ok: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+
+
+def test_backward_router_bias_gradient():
+    cfg = MoEConfig("bwd_bias", 128, 128, 256, 8, 2, "bf16", router_bias=(0.5, -0.2, 0, 0, 0.3, 0,
+                                                                          0, -0.4))
+    inp = make_inputs(cfg, seed=22)
+    dout = make_dout(cfg, seed=22)
+    res = run_bwd(cfg, inp, dout, 0.03, want_dbias=True)
+    errs = compare(cfg, inp, dout, 0.03, res, names=GRADS + ("dbias",))
+    announce("  bias ok: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+
+
+def test_backward_zero_down_and_determinism():
+    cfg = MoEConfig("bwd_zero", 80, 128, 128, 8, 2, "bf16")
+    inp = make_inputs(cfg, seed=23)
+    inp["W_down"] = np.zeros_like(inp["W_down"])
+    dout = make_dout(cfg, seed=23)
+    res = run_bwd(cfg, inp, dout, 0.0)
+    for n in ("dx", "dW_router", "dW_gate", "dW_up"):
+        assert (res[n] == 0).all(), n
+    assert np.abs(res["dW_down"]).max() > 0
+    cfg2 = MoEConfig("bwd_det", 200, 256, 256, 8, 2, "bf16")
+    inp2 = make_inputs(cfg2, seed=24)
+    dout2 = make_dout(cfg2, seed=24)
+    a = run_bwd(cfg2, inp2, dout2, 0.01)
+    b = run_bwd(cfg2, inp2, dout2, 0.01)
+    for n in GRADS:
+        np.testing.assert_array_equal(a[n], b[n])
+
+
+def test_backward_empty_batch():
+    E, k, d, f = 8, 2, 128, 256
+    x = torch.empty((0, d), dtype=torch.bfloat16, device="cuda")
+    Wr = torch.ones((d, E), dtype=torch.float32, device="cuda")
+    Wg = torch.ones((E, f, d), dtype=torch.bfloat16, device="cuda")
+    Wd = torch.ones((E, d, f), dtype=torch.bfloat16, device="cuda")
+    g = moe.backward(x, Wr, Wg, Wg, Wd, x, k, want_dbias=True)
+    torch.cuda.synchronize()
+    for n in ("dW_router", "dW_gate", "dW_up", "dW_down", "dbias"):
+        assert (g[n].float().cpu() == 0).all(), n
+    assert g["dx"].shape == (0, d)
