@@ -19,7 +19,8 @@ import time
 
 import numpy as np
 
-from sparse_mixture_experts_scan_amd.inputs import CONFIGS, make_block_inputs, make_inputs
+from sparse_mixture_experts_scan_amd.inputs import (CONFIGS, make_block_inputs, make_dout,
+                                                    make_inputs)
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA
@@ -43,6 +44,10 @@ def parse():
                    help="expert weights as given (bf16) or INT4 with per-group float32 "
                         "scales (quantized on the GPU before warmup)")
     p.add_argument("--group", type=int, default=128, help="INT4 scale group size")
+    p.add_argument("--backward", action="store_true",
+                   help="time the backward pass (gradients of <dOut, out> + alpha * balance "
+                        "loss, routing and pre-activations recomputed) instead of the forward")
+    p.add_argument("--alpha", type=float, default=0.01, help="balance-loss weight (--backward)")
     p.add_argument("--block", action="store_true",
                    help="time the normalised block out = x + layer(RMSNorm(x)) instead of "
                         "the bare layer")
@@ -115,6 +120,71 @@ def cpu_baseline(cfg, inp, n_tokens, block=False):
                       f"(routing for all {cfg.T}), fp64 numpy, {dt:.2f} s"}
 
 
+def bench_backward(args, cfg, d, dev, stream):
+    """--backward: one step is one moe_ffn_backward call."""
+    import torch
+    import sparse_mixture_experts_scan_amd as moe
+    from sparse_mixture_experts_scan_amd.binding import BWD_STAGE_NAMES, MOE_BWD_NUM_STAGES
+
+    if cfg.dtype != "bf16" or args.block or args.weights != "bf16":
+        print("the backward takes bf16 tensors and the bare layer", file=sys.stderr)
+        sys.exit(2)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    dout = torch.from_numpy(make_dout(cfg, args.seed).view(np.int16)).view(torch.bfloat16).to(dev)
+    ws = torch.empty(moe.moe_ffn_backward_workspace_size(T, cfg.d_model, cfg.d_ff, E, k),
+                     dtype=torch.uint8, device=dev)
+
+    def step(events=None):
+        return moe.backward(d["x"], d["W_router"], d["W_gate"], d["W_up"], d["W_down"], dout, k,
+                            alpha=args.alpha, bias=d["bias"], workspace=ws, stream=stream,
+                            stage_events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    evs = []
+    for _ in range(args.steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(MOE_BWD_NUM_STAGES + 1)]
+        for ev in row:
+            ev.record(stream)
+        evs.append(row)
+    torch.cuda.synchronize()
+    for row in evs:
+        step(row)
+    torch.cuda.synchronize()
+    split = {name: float(np.mean([row[i].elapsed_time(row[i + 1]) for row in evs]))
+             for i, name in enumerate(BWD_STAGE_NAMES)}
+    A, dm, f = T * k, cfg.d_model, cfg.d_ff
+    flops = {"recompute": 4 * A * dm * f, "z": 2 * A * dm * f, "dxs": 4 * A * dm * f,
+             "dw_down": 2 * A * dm * f, "dw_gate_up": 4 * A * dm * f}
+    dom = max(flops, key=lambda n: split[n])
+    achieved = flops[dom] / (split[dom] * 1e-3) / 1e12
+    total = sum(flops.values()) + 4 * T * dm * E
+    secs = ms_step * 1e-3
+    record = {
+        "metric": "MoE-layer backward tokens/s (routing and pre-activations recomputed)",
+        "value": T / secs, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens and upstream gradient, N(0,1/fan_in) weights)",
+        "config": {"workload": cfg.name, "T": T, "d_model": dm, "d_ff": f, "E": E, "k": k,
+                   "alpha": args.alpha, "parallelism": "single GPU"},
+        "layer": {"TFLOP/s": total / secs / 1e12,
+                  "mfma_frac": total / secs / 1e12 / BF16_PEAK_TFLOPS, "kernel_ms": split},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": dom, "kernel_ms": split[dom]},
+    }
+    print(json.dumps(record), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -158,6 +228,9 @@ def main():
     probs = torch.zeros(E, dtype=torch.float32, device=dev) if args.router_stats else None
     bloss = torch.zeros(1, dtype=torch.float32, device=dev) if args.router_stats else None
     stream = torch.cuda.current_stream(dev)
+    if args.backward:
+        bench_backward(args, cfg, d, dev, stream)
+        return
 
     def step(events=None):
         if int4:
