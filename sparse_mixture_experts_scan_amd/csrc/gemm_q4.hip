@@ -185,6 +185,36 @@ struct Q4Batch {
     }
   }
 
+  // the first batch: codes and scales as soon as the expert is known,
+  // activations once their row range is
+  __device__ __forceinline__ void load_w(const __amdgpu_buffer_rsrc_t (&rw)[NW],
+                                         const __amdgpu_buffer_rsrc_t (&rs)[NW],
+                                         const uint32_t (&wo)[NF], const uint32_t (&so)[NF],
+                                         int run, int cpg, int gpc, uint32_t sgrp) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t c = (uint32_t)(run * U + u);
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          wq[w][f][u] = q4_load16(rw[w], wo[f], c * (kQ4Chunk / 2));
+          sc[w][f][u] = q4_load4(rs[w], so[f], (c / cpg) * gpc * sgrp);
+        }
+    }
+  }
+  __device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t ra, const uint32_t (&ao)[NT],
+                                         int run) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t c = (uint32_t)(run * U + u);
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xv[n][u][j] = q4_load16(ra, ao[n] + 16 * j, c * kQ4Chunk * 2);
+    }
+  }
+
   template <bool FULL>
   __device__ __forceinline__ void compute(f32x4 (&acc)[NW][NF][NT], int valid) {
 #pragma unroll
@@ -221,11 +251,12 @@ __device__ __forceinline__ void stream_q4_body(
   constexpr int NWAVE = kQ4Threads / kWave;
   __shared__ f32x4 red[NWAVE - 1][NW * NF * NT][kWave];
 
+  // tiles past those in use have expert -1; the first weight loads wait only
+  // for the expert lookup
   const int tile = blockIdx.y;
-  if (tile >= *num_tiles) return;
   const int e = tile_expert[tile];
+  if (e < 0) return;
   const int row0 = tile * BT;
-  const int valid_end = offsets[e] + counts[e];
   const int f0 = blockIdx.x * FT;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -245,8 +276,6 @@ __device__ __forceinline__ void stream_q4_body(
     rs[1] = q4_rsrc(S1 + (size_t)e * ngr * N + f0, sbytes);
   }
   const uint32_t arow = (uint32_t)K * 2;
-  const int nvalid = max(0, min(BT, valid_end - row0));
-  const __amdgpu_buffer_rsrc_t ra = q4_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * arow);
   uint32_t wo[NF], so[NF], ao[NT];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
@@ -273,7 +302,11 @@ __device__ __forceinline__ void stream_q4_body(
   // compute (the scheduler would otherwise merge the two phases).
   QB A, B;
   int b = 0;
-  if (nb > 0) A.template load<true>(rw, rs, ra, wo, so, ao, wave, U, cpg, gpc, sgrp);
+  if (nb > 0) A.load_w(rw, rs, wo, so, wave, cpg, gpc, sgrp);
+  const int valid_end = offsets[e] + counts[e];
+  const int nvalid = max(0, min(BT, valid_end - row0));
+  const __amdgpu_buffer_rsrc_t ra = q4_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * arow);
+  if (nb > 0) A.load_x(ra, ao, wave);
   for (; b + 2 < nb; b += 2) {
     B.template load<true>(rw, rs, ra, wo, so, ao, wave + (b + 1) * NWAVE, U, cpg, gpc, sgrp);
     __builtin_amdgcn_sched_barrier(0);

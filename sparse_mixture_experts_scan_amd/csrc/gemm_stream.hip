@@ -81,6 +81,28 @@ struct StreamBatch {
       }
     }
   }
+  // the first batch: weights as soon as the expert is known, tokens once
+  // their row range is
+  __device__ __forceinline__ void load_w(const __amdgpu_buffer_rsrc_t (&rw)[NW],
+                                         const uint32_t (&wo)[NF], int run) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t so = (uint32_t)(run * U + u) * KSTEP * sizeof(T);
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) wv[w][f][u] = sload(rw[w], wo[f], so);
+    }
+  }
+  __device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t ra, const uint32_t (&ao)[NT],
+                                         int run) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t so = (uint32_t)(run * U + u) * KSTEP * sizeof(T);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) av[n][u] = sload(ra, ao[n], so);
+    }
+  }
   template <bool FULL>
   __device__ __forceinline__ void compute(f32x4 (&acc)[NW][NF][NT], int valid) {
 #pragma unroll
@@ -109,11 +131,13 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gemm_kernel(
   constexpr int NWAVE = kStreamThreads / kWave;
   __shared__ f32x4 red[NWAVE - 1][NW * NF * NT][kWave];
 
+  // Tiles past those in use have expert -1.  One dependent lookup (the
+  // expert) stands between the launch and the first weight loads; the token
+  // row range (offsets, counts) is needed only for the token loads.
   const int tile = blockIdx.y;
-  if (tile >= *num_tiles) return;
   const int e = tile_expert[tile];
+  if (e < 0) return;
   const int row0 = tile * BT;
-  const int valid_end = offsets[e] + counts[e];
   const int f0 = blockIdx.x * FT;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
@@ -123,9 +147,6 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gemm_kernel(
   __amdgpu_buffer_rsrc_t rw[NW];
   rw[0] = stream_rsrc(W0 + ((size_t)e * N + f0) * K, FT * row_bytes);
   if constexpr (GATEUP) rw[1] = stream_rsrc(W1 + ((size_t)e * N + f0) * K, FT * row_bytes);
-  // token rows past the expert's count fall outside the resource: read as 0
-  const int nvalid = max(0, min(BT, valid_end - row0));
-  const __amdgpu_buffer_rsrc_t ra = stream_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
   uint32_t wo[NF], ao[NT];
 #pragma unroll
   for (int f = 0; f < NF; ++f) wo[f] = (uint32_t)(f * 16 + lr) * row_bytes + kg * 16;
@@ -146,7 +167,12 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gemm_kernel(
   const int nruns = nks / U, rem = nks % U;
   const int nb = nruns > wave ? (nruns - wave + NWAVE - 1) / NWAVE : 0;
   SB A, B;
-  if (nb > 0) A.template load<true>(rw, ra, wo, ao, wave, U);
+  if (nb > 0) A.load_w(rw, wo, wave);
+  // token rows past the expert's count fall outside the resource: read as 0
+  const int valid_end = offsets[e] + counts[e];
+  const int nvalid = max(0, min(BT, valid_end - row0));
+  const __amdgpu_buffer_rsrc_t ra = stream_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
+  if (nb > 0) A.load_x(ra, ao, wave);
   for (int b = 0; b < nb; b += 2) {
     if (b + 1 < nb) B.template load<true>(rw, ra, wo, ao, wave + (b + 1) * NWAVE, U);
     A.template compute<true>(acc, U);
