@@ -96,11 +96,12 @@ def main():
     ap.add_argument("--workload", required=True)
     ap.add_argument("--variant", choices=("stream", "tile", "q4"), required=True)
     ap.add_argument("--kt", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
+    ap.add_argument("--fetch", help="FETCH_SIZE run (omit with --write for a trace-only summary)")
+    ap.add_argument("--write")
     ap.add_argument("--cal-mib", type=int, default=512)
     ap.add_argument("--command-kt", required=True)
-    ap.add_argument("--command-pmc", required=True)
+    ap.add_argument("--command-pmc", default="")
+    ap.add_argument("--title", default="MoE layer")
     ap.add_argument("--algorithmic", default="{}",
                     help="JSON {kernel: algorithmic bytes per launch} for the table")
     ap.add_argument("--out", required=True)
@@ -109,13 +110,9 @@ def main():
     a = ap.parse_args()
 
     stats = read_stats(a.kt)
-    fetch, names = read_counter(a.fetch)
-    write, _ = read_counter(a.write)
-    cf = calibration(fetch, a.cal_mib, "fetch")
-    cw = calibration(write, a.cal_mib, "write")
     alg = json.loads(a.algorithmic)
 
-    lines = [f"# rocprofv3 summary: MoE layer, workload `{a.workload}`", "",
+    lines = [f"# rocprofv3 summary: {a.title}, workload `{a.workload}`", "",
              "Kernel trace (`--kernel-trace --stats`):", "", "```", a.command_kt, "```", "",
              "| kernel | calls | avg us | min us | max us | share % |",
              "|---|---|---|---|---|---|"]
@@ -123,6 +120,15 @@ def main():
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.2f} | "
                      f"{float(r['MinNs'])/1e3:.2f} | {float(r['MaxNs'])/1e3:.2f} | "
                      f"{float(r['Percentage']):.2f} |")
+    if not a.fetch or not a.write:
+        with open(a.out, "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+        print(f"wrote {a.out} (kernel trace only)")
+        return
+    fetch, names = read_counter(a.fetch)
+    write, _ = read_counter(a.write)
+    cf = calibration(fetch, a.cal_mib, "fetch")
+    cw = calibration(write, a.cal_mib, "write")
     lines += ["", "HBM traffic per launch (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, "
               "one run each):", "", "```", a.command_pmc.replace("<COUNTER>", "FETCH_SIZE"),
               a.command_pmc.replace("<COUNTER>", "WRITE_SIZE"), "```", "",
