@@ -29,12 +29,32 @@ namespace moe {
 
 namespace {
 
-constexpr int kGT = 256;          // threads
-constexpr int kGM = 128;          // tile rows (M)
-constexpr int kGN = 128;          // tile columns (N)
-constexpr int kGK = 32;           // K per stage
-constexpr int kGLd = kGK + 8;     // LDS row pitch in elements (80 bytes)
-constexpr int kGOper = kGM * kGLd;  // elements per operand tile
+// Tile shape: kGM x kGN outputs per workgroup, K in steps of kGK, kGWM x kGWN
+// waves each holding (kGM / kGWM) x (kGN / kGWN) in 32x32 fragments.
+#ifndef MOE_BG_M
+#define MOE_BG_M 256
+#endif
+#ifndef MOE_BG_N
+#define MOE_BG_N 128
+#endif
+#ifndef MOE_BG_K
+#define MOE_BG_K 32
+#endif
+#ifndef MOE_BG_WM
+#define MOE_BG_WM 4
+#endif
+#ifndef MOE_BG_WN
+#define MOE_BG_WN 2
+#endif
+constexpr int kGM = MOE_BG_M;
+constexpr int kGN = MOE_BG_N;
+constexpr int kGK = MOE_BG_K;
+constexpr int kGWM = MOE_BG_WM, kGWN = MOE_BG_WN;
+constexpr int kGT = 64 * kGWM * kGWN;        // threads
+constexpr int kGLd = kGK + 8;                // LDS row pitch in elements
+constexpr int kGFA = kGM / kGWM / 32;        // 32-row fragments per wave (M)
+constexpr int kGFB = kGN / kGWN / 32;        // 32-column fragments per wave (N)
+static_assert(kGFA >= 1 && kGFB >= 1 && kGK % 16 == 0, "tile shape");
 constexpr int kBufCfg = 0x00020000;
 
 __device__ inline __amdgpu_buffer_rsrc_t g_rsrc(const void* base, uint32_t bytes) {
@@ -56,45 +76,56 @@ __device__ inline f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// One operand tile (128 rows x 32 k) of one stage: registers between the
-// global load and the LDS store.
-//   KC (k contiguous): 128 rows of 64 bytes; thread t loads rows t/4 and
-//     t/4 + 64, 16-byte piece t%4.
-//   KS (k slow): 32 rows of k, 128 contiguous elements each; thread t loads
-//     k = 2 (t%16) and k + 1, elements 8 (t/16) .. +8, and stores eight
+// One operand tile (ROWS rows x kGK k) of one stage, in registers between
+// the global load and the LDS store.
+//   KC (k contiguous): ROWS rows of 2 kGK bytes, cut into 16-byte pieces;
+//     piece p = thread + i * kGT is row p / (kGK / 8), piece p % (kGK / 8).
+//   KS (k slow): kGK rows of k, ROWS contiguous elements each, cut into tasks
+//     of two k rows by 8 elements; task p = thread + i * kGT is k pair
+//     p % (kGK / 2), elements 8 (p / (kGK / 2)) .. +8; it stores eight
 //     (k, k+1) pairs into eight LDS rows.
-template <bool KC>
+template <bool KC, int ROWS>
 struct GOperand {
-  uint4 v0, v1;
+  static constexpr int TASKS = KC ? ROWS * kGK / 8 : (kGK / 2) * (ROWS / 8);
+  static constexpr int PIECES = (TASKS + kGT - 1) / kGT;
+  static constexpr bool EVEN = TASKS % kGT == 0;   // else the last round is partial
+  uint4 v0[PIECES], v1[KC ? 1 : PIECES];
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t ld_bytes, int k0,
                                        int col0, int tid) {
-    if constexpr (KC) {
-      const int row = tid >> 2, piece = tid & 3;
-      const uint32_t off = (uint32_t)row * ld_bytes + (uint32_t)(k0 + piece * 8) * 2;
-      v0 = g_load16(r, off);
-      v1 = g_load16(r, off + 64 * ld_bytes);
-    } else {
-      const int k = k0 + 2 * (tid & 15), c8 = tid >> 4;
-      const uint32_t off = (uint32_t)k * ld_bytes + (uint32_t)(col0 + c8 * 8) * 2;
-      v0 = g_load16(r, off);
-      v1 = g_load16(r, off + ld_bytes);
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+      const int p = tid + i * kGT;
+      if (!EVEN && p >= TASKS) break;
+      if constexpr (KC) {
+        const int row = p / (kGK / 8), piece = p % (kGK / 8);
+        v0[i] = g_load16(r, (uint32_t)row * ld_bytes + (uint32_t)(k0 + piece * 8) * 2);
+      } else {
+        const int k = k0 + 2 * (p % (kGK / 2)), c8 = p / (kGK / 2);
+        const uint32_t off = (uint32_t)k * ld_bytes + (uint32_t)(col0 + c8 * 8) * 2;
+        v0[i] = g_load16(r, off);
+        v1[i] = g_load16(r, off + ld_bytes);
+      }
     }
   }
   __device__ __forceinline__ void store(bf16_t* lds, int tid) const {
-    if constexpr (KC) {
-      const int row = tid >> 2, piece = tid & 3;
-      *reinterpret_cast<uint4*>(lds + row * kGLd + piece * 8) = v0;
-      *reinterpret_cast<uint4*>(lds + (row + 64) * kGLd + piece * 8) = v1;
-    } else {
-      const int kk = 2 * (tid & 15), c8 = tid >> 4;
-      const uint32_t a[4] = {v0.x, v0.y, v0.z, v0.w};
-      const uint32_t b[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t lo = (a[w] & 0xFFFFu) | (b[w] << 16);          // element 2w
-        const uint32_t hi = (a[w] >> 16) | (b[w] & 0xFFFF0000u);      // element 2w + 1
-        *reinterpret_cast<uint32_t*>(lds + (c8 * 8 + 2 * w) * kGLd + kk) = lo;
-        *reinterpret_cast<uint32_t*>(lds + (c8 * 8 + 2 * w + 1) * kGLd + kk) = hi;
+    for (int i = 0; i < PIECES; ++i) {
+      const int p = tid + i * kGT;
+      if (!EVEN && p >= TASKS) break;
+      if constexpr (KC) {
+        const int row = p / (kGK / 8), piece = p % (kGK / 8);
+        *reinterpret_cast<uint4*>(lds + row * kGLd + piece * 8) = v0[i];
+      } else {
+        const int kk = 2 * (p % (kGK / 2)), c8 = p / (kGK / 2);
+        const uint32_t a[4] = {v0[i].x, v0[i].y, v0[i].z, v0[i].w};
+        const uint32_t b[4] = {v1[i].x, v1[i].y, v1[i].z, v1[i].w};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t lo = (a[w] & 0xFFFFu) | (b[w] << 16);          // element 2w
+          const uint32_t hi = (a[w] >> 16) | (b[w] & 0xFFFF0000u);      // element 2w + 1
+          *reinterpret_cast<uint32_t*>(lds + (c8 * 8 + 2 * w) * kGLd + kk) = lo;
+          *reinterpret_cast<uint32_t*>(lds + (c8 * 8 + 2 * w + 1) * kGLd + kk) = hi;
+        }
       }
     }
   }
@@ -117,11 +148,11 @@ __global__ __launch_bounds__(kGT) void grouped_gemm_kernel(
     bool accumulate, const int32_t* __restrict__ tb_count, const int32_t* __restrict__ tb_exp,
     const int32_t* __restrict__ tb_row0, const int32_t* __restrict__ tb_rows,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets) {
-  __shared__ __attribute__((aligned(16))) bf16_t lA[2][kGOper];
-  __shared__ __attribute__((aligned(16))) bf16_t lB[2][kGOper];
+  __shared__ __attribute__((aligned(16))) bf16_t lA[2][kGM * kGLd];
+  __shared__ __attribute__((aligned(16))) bf16_t lB[2][kGN * kGLd];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % kGWM, wn = wave / kGWM;
   const int n0 = blockIdx.x * kGN;
 
   int m0, rows, kn;
@@ -137,7 +168,8 @@ __global__ __launch_bounds__(kGT) void grouped_gemm_kernel(
     // A: rows m0 .. m0 + rows (k contiguous), past them zeros
     ra = g_rsrc(A + (size_t)m0 * lda, (uint32_t)rows * lda * 2);
     const bf16_t* Be = B + (size_t)e * b_estride;
-    if constexpr (KCB) rb = g_rsrc(Be + (size_t)n0 * ldb, (uint32_t)kGN * ldb * 2);
+    // (columns past N read as zeros or as a neighbour's data; never stored)
+    if constexpr (KCB) rb = g_rsrc(Be + (size_t)n0 * ldb, (uint32_t)min(kGN, N - n0) * ldb * 2);
     else rb = g_rsrc(Be, (uint32_t)K * ldb * 2);
     c_base = (size_t)m0 * ldc;
   } else {
@@ -156,16 +188,16 @@ __global__ __launch_bounds__(kGT) void grouped_gemm_kernel(
   const int a_col0 = KCA ? 0 : m0;
   const int b_col0 = KCB ? 0 : n0;
 
-  f32x16 acc[2][2];
+  f32x16 acc[kGFA][kGFB];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < kGFA; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < kGFB; ++b)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
 
-  GOperand<KCA> ga;
-  GOperand<KCB> gb;
+  GOperand<KCA, kGM> ga;
+  GOperand<KCB, kGN> gb;
   const int nk = (kn + kGK - 1) / kGK;
   if (nk > 0) {
     ga.load(ra, lda_b, 0, a_col0, tid);
@@ -175,6 +207,7 @@ __global__ __launch_bounds__(kGT) void grouped_gemm_kernel(
   }
   __syncthreads();
   const int r32 = lane & 31, half = lane >> 5;
+  const int arow0 = wm * (kGM / kGWM), brow0 = wn * (kGN / kGWN);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < nk) {
@@ -183,19 +216,19 @@ __global__ __launch_bounds__(kGT) void grouped_gemm_kernel(
     }
 #pragma unroll
     for (int ks = 0; ks < kGK / 16; ++ks) {
-      uint4 af[2], bf[2];
+      uint4 af[kGFA], bf[kGFB];
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
-        af[a] = *reinterpret_cast<const uint4*>(&lA[cur][(wm * 64 + a * 32 + r32) * kGLd +
+      for (int a = 0; a < kGFA; ++a)
+        af[a] = *reinterpret_cast<const uint4*>(&lA[cur][(arow0 + a * 32 + r32) * kGLd +
                                                           ks * 16 + half * 8]);
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-        bf[b] = *reinterpret_cast<const uint4*>(&lB[cur][(wn * 64 + b * 32 + r32) * kGLd +
+      for (int b = 0; b < kGFB; ++b)
+        bf[b] = *reinterpret_cast<const uint4*>(&lB[cur][(brow0 + b * 32 + r32) * kGLd +
                                                           ks * 16 + half * 8]);
 #pragma unroll
-      for (int a = 0; a < 2; ++a)
+      for (int a = 0; a < kGFA; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = mfma32(af[a], bf[b], acc[a][b]);
+        for (int b = 0; b < kGFB; ++b) acc[a][b] = mfma32(af[a], bf[b], acc[a][b]);
     }
     if (kt + 1 < nk) {
       ga.store(lA[cur ^ 1], tid);
@@ -207,13 +240,14 @@ __global__ __launch_bounds__(kGT) void grouped_gemm_kernel(
   // D of a 32x32 MFMA: lane holds column n = lane % 32 and rows
   // 8 * (j / 4) + 4 * (lane / 32) + j % 4.
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < kGFA; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int n = n0 + wn * 64 + b * 32 + r32;
+    for (int b = 0; b < kGFB; ++b) {
+      const int n = n0 + brow0 + b * 32 + r32;
+      if (n >= N) continue;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int m = wm * 64 + a * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
+        const int m = arow0 + a * 32 + 8 * (j >> 2) + 4 * half + (j & 3);
         if (m >= rows || m0 + m >= M) continue;
         const size_t idx = c_base + (size_t)m * ldc + n;
         if constexpr (CBF16) {
@@ -427,7 +461,7 @@ void launch_bwd_gemm_rows(const void* A, int lda, const void* B, int ldb, bool b
                           bool accumulate, int max_tiles, const int32_t* tb_count,
                           const int32_t* tb_exp, const int32_t* tb_row0, const int32_t* tb_rows,
                           hipStream_t s) {
-  const dim3 grid(N / kGN, max_tiles);
+  const dim3 grid((N + kGN - 1) / kGN, max_tiles);
   if (b_kcontig)
     grouped_gemm_kernel<true, true, 0, false><<<grid, kGT, 0, s>>>(
         (const bf16_t*)A, lda, (const bf16_t*)B, ldb, b_estride, C, ldc, 0, M, N, K,
@@ -441,7 +475,7 @@ void launch_bwd_gemm_rows(const void* A, int lda, const void* B, int ldb, bool b
 void launch_bwd_gemm_wgrad(const Dims& D, const void* A, int lda, const void* B, int ldb,
                            void* C, int M, int N, const int32_t* counts, const int32_t* offsets,
                            hipStream_t s) {
-  const dim3 grid(N / kGN, M / kGM, D.E);
+  const dim3 grid((N + kGN - 1) / kGN, (M + kGM - 1) / kGM, D.E);
   grouped_gemm_kernel<false, false, 1, true><<<grid, kGT, 0, s>>>(
       (const bf16_t*)A, lda, (const bf16_t*)B, ldb, 0, C, N, (size_t)M * N, M, N, 0, false,
       nullptr, nullptr, nullptr, nullptr, counts, offsets);
