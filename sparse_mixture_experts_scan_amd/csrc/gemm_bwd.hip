@@ -371,21 +371,41 @@ __global__ __launch_bounds__(64) void bwd_router_kernel(
 
 // Router weight gradient, partial over a slice of tokens: part[s][j][e] =
 // sum over tokens of slice s (in order) of x[t][j] ds[t][e]; and the bias
-// gradient part (column j = d).  Block: 64 columns j x E experts.
+// gradient part (column j = d).  Thread per column j, eight experts per
+// pass held in registers; the slice's ds rows are staged in LDS and read as
+// broadcasts.
+constexpr int kWgradMaxSlice = 1024;   // tokens per slice staged at once
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(
     const T* __restrict__ x, const float* __restrict__ ds, int Tn, int d, int E, int tslice,
     float* __restrict__ part) {
-  const int j = blockIdx.x * 64 + (threadIdx.x & 63);
+  __shared__ float sds[kWgradMaxSlice * 8];
+  const int j = blockIdx.x * 256 + threadIdx.x;
   const int s = blockIdx.y;
   const int t0 = s * tslice, t1 = min(Tn, t0 + tslice);
-  for (int e = threadIdx.x >> 6; e < E; e += 4) {
-    float acc = 0.f;
+  for (int e0 = 0; e0 < E; e0 += 8) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    for (int c0 = t0; c0 < t1; c0 += kWgradMaxSlice) {
+      const int c1 = min(t1, c0 + kWgradMaxSlice);
+      __syncthreads();
+      for (int i = threadIdx.x; i < (c1 - c0) * 8; i += 256) {
+        const int t = c0 + i / 8, e = e0 + i % 8;
+        sds[i] = e < E ? ds[(size_t)t * E + e] : 0.f;
+      }
+      __syncthreads();
+      if (j <= d)
+        for (int t = c0; t < c1; ++t) {
+          const float xv = j < d ? Elem<T>::to_f32(x[(size_t)t * d + j]) : 1.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] = fmaf(xv, sds[(t - c0) * 8 + q], acc[q]);
+        }
+    }
     if (j <= d)
-      for (int t = t0; t < t1; ++t)
-        acc = fmaf(j < d ? Elem<T>::to_f32(x[(size_t)t * d + j]) : 1.0f, ds[(size_t)t * E + e],
-                   acc);
-    if (j <= d) part[((size_t)s * (d + 1) + j) * E + e] = acc;
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (e0 + q < E) part[((size_t)s * (d + 1) + j) * E + e0 + q] = acc[q];
   }
 }
 
@@ -499,7 +519,7 @@ void launch_bwd_router_wgrad(const Dims& D, const void* x, const float* ds, floa
                              float* dWr, float* dbias, hipStream_t s) {
   const int slices = kBwdRouterSlices;
   const int tslice = (D.T + slices - 1) / slices;
-  const dim3 grid((D.d + 1 + 63) / 64, slices);
+  const dim3 grid((D.d + 1 + 255) / 256, slices);
   bwd_router_wgrad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)x, ds, D.T, D.d, D.E,
                                                        tslice, part);
   bwd_router_wgrad_reduce<<<((D.d + 1) * D.E + 255) / 256, 256, 0, s>>>(part, slices, D.d, D.E,
