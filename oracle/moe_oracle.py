@@ -418,3 +418,66 @@ def moe_backward(x, W_router, W_gate, W_up, W_down, dout, k, bias=None, alpha=0.
     dx += ds @ Wr.T
     return dict(dx=dx, dW_router=xf.T @ ds, dbias=ds.sum(axis=0), dW_gate=dW1, dW_up=dW3,
                 dW_down=dW2, idx=idx, gates=g, ds=ds, dg=dg)
+
+
+def moe_backward_entries(x, W_router, W_gate, W_up, W_down, dout, k, tokens, feats,
+                         bias=None, alpha=0.0, forced_idx=None) -> dict:
+    """Parts of moe_backward's result at sizes where the whole is too costly,
+    each from the same definitions, expert by expert:
+      dx[t] for t in `tokens`;
+      dW_gate[e][i][:], dW_up[e][i][:] (rows) and dW_down[e][:][i] (columns)
+      for (e, i) in `feats`, i a d_ff index.
+    dx needs the gate gradients of only its own token; the weight gradients
+    need, per routed row of e, only feature i of a, b, W2^T dOut and h.
+    Returns dx [len(tokens)][d] and gate/up/down [len(feats)][d] (fp64)."""
+    xf = to_f64(x)
+    T, d = xf.shape
+    Wr = to_f64(W_router)
+    E = Wr.shape[1]
+    s = router_logits(xf, Wr, bias)
+    idx = select_topk(s, k) if forced_idx is None else np.asarray(forced_idx, dtype=np.int64)
+    g = topk_gates(s, idx)
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    go_tok = to_f64(dout[tokens])
+    dx = np.zeros((tokens.size, d))
+    dg = np.zeros((tokens.size, k))
+    gate = np.zeros((len(feats), d))
+    up = np.zeros((len(feats), d))
+    down = np.zeros((len(feats), d))
+    for e in range(E):
+        mine = [n for n, (fe, _) in enumerate(feats) if fe == e]
+        sel = [(n, j) for n, t in enumerate(tokens) for j in range(k) if idx[t, j] == e]
+        if not mine and not sel:
+            continue
+        W1, W3, W2 = to_f64(W_gate[e]), to_f64(W_up[e]), to_f64(W_down[e])
+        for n, j in sel:                                   # dx of sampled tokens
+            t = tokens[n]
+            a, b = W1 @ xf[t], W3 @ xf[t]
+            h = silu(a) * b
+            dg[n, j] = go_tok[n] @ (W2 @ h)
+            dh = W2.T @ (g[t, j] * go_tok[n])
+            dx[n] += W1.T @ (dh * b * silu_grad(a)) + W3.T @ (dh * silu(a))
+        if mine:
+            rows = np.nonzero((idx == e).any(axis=1))[0]   # tokens routed to e
+            slot = np.argmax(idx[rows] == e, axis=1)
+            gr = g[rows, slot]
+            X = xf[rows]
+            Go = to_f64(dout[rows])
+            for n in mine:
+                i = feats[n][1]
+                a, b = X @ W1[i], X @ W3[i]
+                dh = gr * (Go @ W2[:, i])
+                gate[n] = (dh * b * silu_grad(a)) @ X
+                up[n] = (dh * silu(a)) @ X
+                down[n] = (gr * silu(a) * b) @ Go
+    ds = np.zeros((tokens.size, E))
+    gt = g[tokens]
+    np.put_along_axis(ds, idx[tokens], gt * (dg - (gt * dg).sum(axis=1, keepdims=True)), axis=1)
+    if alpha:
+        z = np.exp(s[tokens] - s[tokens].max(axis=1, keepdims=True))
+        P = z / z.sum(axis=1, keepdims=True)
+        c = alpha * E * (counts / T) / T
+        ds += P * (c[None, :] - (P * c[None, :]).sum(axis=1, keepdims=True))
+    dx += ds @ Wr.T
+    return dict(dx=dx, dW_gate_rows=gate, dW_up_rows=up, dW_down_cols=down, idx=idx)

@@ -123,3 +123,45 @@ def test_backward_empty_batch():
     for n in ("dW_router", "dW_gate", "dW_up", "dW_down", "dbias"):
         assert (g[n].float().cpu() == 0).all(), n
     assert g["dx"].shape == (0, d)
+
+
+def test_backward_prefill_sampled():
+    # the full prefill shape of the benchmark (T = 4096, Mixtral layer),
+    # checked on sampled outputs: dx of sampled tokens, rows of dW_gate and
+    # dW_up and columns of dW_down of two features per expert
+    from sparse_mixture_experts_scan_amd.inputs import CONFIGS
+    cfg = CONFIGS["prefill"]
+    announce(f"case prefill T={cfg.T} d={cfg.d_model} f={cfg.d_ff} E={cfg.E} k={cfg.k} sampled")
+    inp = make_inputs(cfg, seed=0)
+    dout = make_dout(cfg, seed=0)
+    d = H.upload(inp)
+    idx_t = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    moe.forward(d["x"], d["W_router"], d["W_gate"], d["W_up"], d["W_down"], cfg.k,
+                bias=d["bias"], topk_idx=idx_t)
+    g = moe.backward(d["x"], d["W_router"], d["W_gate"], d["W_up"], d["W_down"],
+                     H.dev_tensor(dout), cfg.k, alpha=0.01, bias=d["bias"])
+    torch.cuda.synchronize()
+    res = {"idx": idx_t.cpu().numpy()}
+    s = oracle.router_logits(inp["x"], inp["W_router"], inp["bias"])
+    ref_idx = oracle.select_topk(s, cfg.k)
+    gap, _ = oracle.routing_gaps(s, cfg.k)
+    ok = gap >= H.NEAR_TIE
+    np.testing.assert_array_equal(np.sort(res["idx"][ok], axis=1), np.sort(ref_idx[ok], axis=1))
+    toks = H.sample_tokens(cfg, res["idx"], 6)
+    rng = np.random.default_rng(1)
+    feats = [(e, int(i)) for e in range(cfg.E) for i in rng.choice(cfg.d_ff, 2, replace=False)]
+    ref = oracle.moe_backward_entries(inp["x"], inp["W_router"], inp["W_gate"], inp["W_up"],
+                                      inp["W_down"], dout, cfg.k, toks, feats,
+                                      bias=inp["bias"], alpha=0.01,
+                                      forced_idx=res["idx"].astype(np.int64))
+    def host(t):
+        return H.as_f32(H.to_host(t.contiguous())).astype(np.float64)
+    got = {"dx": host(g["dx"][torch.as_tensor(toks, device="cuda")]),
+           "dW_gate_rows": np.array([host(g["dW_gate"][e, i]) for e, i in feats]),
+           "dW_up_rows": np.array([host(g["dW_up"][e, i]) for e, i in feats]),
+           "dW_down_cols": np.array([host(g["dW_down"][e, :, i]) for e, i in feats])}
+    errs = {}
+    for n, v in got.items():
+        errs[n] = float(np.abs(v - ref[n]).max() / np.abs(ref[n]).max())
+        assert errs[n] <= TOL, (n, errs[n])
+    announce("  ok: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))

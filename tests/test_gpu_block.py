@@ -115,3 +115,25 @@ def test_empty_batch_clears_statistics(block):
     torch.cuda.synchronize()
     assert out.shape == (0, d)
     assert (cnt.cpu() == 0).all() and (probs.cpu() == 0).all() and float(loss.cpu()[0]) == 0.0
+
+
+def test_block_prefill_sampled():
+    # the normalised block at the full prefill shape, sampled tokens
+    from sparse_mixture_experts_scan_amd.inputs import CONFIGS
+    cfg = CONFIGS["prefill"]
+    inp = make_block_inputs(cfg, seed=0)
+    res = run_block(cfg, inp)
+    xn_ref = oracle.rms_norm(inp["x"], inp["norm_weight"], EPS)
+    s = oracle.router_logits(xn_ref, inp["W_router"], inp["bias"])
+    toks = H.sample_tokens(cfg, oracle.select_topk(s, cfg.k), 24)
+    gap, order_gap = oracle.routing_gaps(s, cfg.k)
+    idx = oracle.select_topk(s, cfg.k)
+    H.check_routing(cfg, dict(idx=idx, gates=oracle.topk_gates(s, idx), gap=gap,
+                              order_gap=order_gap), res)
+    r = oracle.block_forward(inp["x"], inp["norm_weight"], EPS, inp["W_router"], inp["W_gate"],
+                             inp["W_up"], inp["W_down"], cfg.k, bias=inp["bias"], tokens=toks,
+                             forced_idx=res["idx"].astype(np.int64))
+    got = H.as_f32(res["out"][toks]).astype(np.float64)
+    err = np.abs(got - r["out"]).max() / np.abs(r["out"]).max()
+    assert err <= H.TOL["bf16"], err
+    announce(f"  prefill block ok: out err {err:.2e}")

@@ -168,3 +168,16 @@ def test_int4_decode_workload():
         np.testing.assert_array_equal(res["q"][n][1][e][:, trows].cpu().numpy(), s_ref)
     err, _ = check_layer(cfg, inp, 128, res, lazy=True)
     announce(f"  ok: max|err|/max|ref| {err:.2e}")
+
+
+def test_int4_prefill_sampled():
+    # the dequantize-then-tile path at the full prefill shape, sampled tokens
+    cfg = CONFIGS["prefill"]
+    announce(f"case prefill T={cfg.T} d={cfg.d_model} f={cfg.d_ff} E={cfg.E} k={cfg.k} group=128")
+    inp = make_inputs(cfg, seed=0)
+    res = run_int4(cfg, inp, 128)
+    assert res["layout"].gemm_variant == 1
+    s = oracle.router_logits(inp["x"], inp["W_router"], inp["bias"])
+    toks = H.sample_tokens(cfg, oracle.select_topk(s, cfg.k), 24)
+    err, _ = check_layer(cfg, inp, 128, res, tokens=toks, lazy=True)
+    announce(f"  ok: max|err|/max|ref| {err:.2e}")

@@ -557,3 +557,23 @@ def test_backward_special_cases():
         assert np.abs(gb[n]).max() == 0.0
     assert np.abs(gb["dW_router"]).max() > 0
     np.testing.assert_allclose(gb["ds"].sum(axis=1), 0.0, atol=1e-15)  # softmax rows
+
+
+@pytest.mark.parametrize("alpha", [0.0, 0.2])
+def test_backward_entries_equal_the_whole(alpha):
+    # the sampled backward (used at full sizes) against the central-difference
+    # pinned moe_backward, entry for entry, on a shape with every expert used
+    x, Wr, Wg, Wu, Wd, b, dout = _bwd_case(45, T=9, d=6, f=5, E=4, k=2)
+    whole = oracle.moe_backward(x, Wr, Wg, Wu, Wd, dout, 2, bias=b, alpha=alpha)
+    toks = [0, 3, 8]
+    feats = [(0, 1), (2, 4), (3, 0), (1, 2)]
+    part = oracle.moe_backward_entries(x, Wr, Wg, Wu, Wd, dout, 2, toks, feats, bias=b,
+                                       alpha=alpha)
+    np.testing.assert_allclose(part["dx"], whole["dx"][toks], rtol=1e-12, atol=1e-14)
+    for n, (e, i) in enumerate(feats):
+        np.testing.assert_allclose(part["dW_gate_rows"][n], whole["dW_gate"][e][i],
+                                   rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(part["dW_up_rows"][n], whole["dW_up"][e][i],
+                                   rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(part["dW_down_cols"][n], whole["dW_down"][e][:, i],
+                                   rtol=1e-12, atol=1e-14)
