@@ -1,6 +1,7 @@
 /*
- * moe_ffn.h -- C ABI of the sparse Mixture-of-Experts feed-forward layer
- * (forward pass) for AMD Instinct MI355X (gfx950).
+ * moe_ffn.h -- C ABI of the sparse Mixture-of-Experts feed-forward layer for
+ * AMD Instinct MI355X (gfx950): the forward pass (bf16 or fp32), its
+ * normalised-block wrapper, INT4 expert weights, and the backward pass.
  *
  * The layer ("Mistral/Mixtralのアーキテクチャ", disassemble-channel.com,
  * section "Top-2ゲーティングの定式化" and section "各エキスパートの構造";
@@ -19,13 +20,18 @@
  * Conventions for every entry point:
  *  - Tensor arguments are DEVICE pointers, row-major and contiguous, owned by
  *    the caller; x, W_router, W_gate, W_up, W_down and out 16-byte aligned,
- *    the bias and the optional outputs 4-byte aligned.  The library never frees them and keeps no reference after
- *    the work it enqueued has run.
+ *    the bias and the optional outputs 4-byte aligned.  The library never
+ *    frees them and keeps no reference after the work it enqueued has run.
  *  - Calls are asynchronous on the given stream (NULL = the default stream);
- *    device faults surface at the caller's next synchronisation.  Nothing on
- *    the forward path synchronises with the host or calls hipMemset, so the
- *    forward call can be captured into a HIP graph when a caller-owned
- *    workspace is passed.
+ *    device faults surface at the caller's next synchronisation.  No entry
+ *    point synchronises with the host or calls hipMemset once its workspace
+ *    exists, so a call with a caller-owned workspace can be captured into a
+ *    HIP graph.
+ *  - Workspace: a call that passes none uses one library-owned buffer per
+ *    device, shared by every such call and grown on demand (growing
+ *    synchronises the device).  Calls sharing it must be ordered (one stream,
+ *    or synchronised between streams); concurrent calls on different streams
+ *    must each pass their own workspace.
  *  - Arguments are validated on the host before any HIP call; a failed
  *    validation enqueues nothing.  Non-finite inputs give undefined results.
  *  - Return value: a moe_status_t.  On MOE_ERR_HIP, moe_last_error() holds
