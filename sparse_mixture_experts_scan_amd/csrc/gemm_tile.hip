@@ -5,26 +5,31 @@
 // Gate/up: H[r][f] = SiLU(sum_c W_gate[e][f][c] Xs[r][c]) * sum_c W_up[e][f][c] Xs[r][c]
 // Down:    Y[r][o] = sum_f W_down[e][o][f] H[r][f]   (fp32 out)
 //
-// Tile: 256 weight rows x 256 token rows per workgroup of 8 waves (two per
-// SIMD, so one wave's MFMAs cover the other's LDS and barrier stalls), each
-// wave 128 weight rows x 64 token rows in eight 32x32 fp32 accumulators fed
-// by v_mfma_f32_32x32x16_bf16 (A = weight rows, B = token rows, both
+// Tile: 256 weight rows x 256 token rows per workgroup of 8 waves, each wave
+// 128 weight rows x 64 token rows in eight 32x32 fp32 accumulators fed by
+// v_mfma_f32_32x32x16_bf16 (A = weight rows, B = token rows, both
 // K-contiguous).  For gate/up the 256 weight rows are 128 gate rows and the
 // same 128 up rows, and each wave holds gate and up accumulators of the same
 // features, so SiLU(gate) * up is applied in registers and only H is stored.
 //
-// K is staged 64 at a time through a ring of LDS stage buffers filled by
-// gfx950 buffer loads straight to LDS (no VGPR staging): each lane fetches the
-// 16 bytes that belong at its slot of the XOR-swizzled layout, the next stage
-// is issued right after the barrier that opens the current one, and each
-// wave waits for its own loads before that barrier.  LDS rows are 128 bytes;
-// chunk c of row r sits at c ^ ((r ^ r >> 3) & 7), so the 32 rows an MFMA
-// fragment reads fall in distinct banks (no bank conflicts measured).
+// K is staged 64 at a time through two LDS stage buffers filled by gfx950
+// buffer loads straight to LDS (no VGPR staging): each lane fetches the 16
+// bytes that belong at its slot of the XOR-swizzled layout.  LDS rows are 128
+// bytes; chunk c of row r sits at c ^ ((r ^ r >> 3) & 7), so the 32 rows an
+// MFMA fragment reads fall in distinct banks (no bank conflicts measured).
+//
+// Ping-pong: waves 0-3 (one per SIMD) and waves 4-7 run the same sequence per
+// stage -- read the stage's fragments from LDS into registers, barrier, run
+// the stage's 32 MFMAs, barrier -- but waves 4-7 pass one extra barrier first,
+// so each SIMD's two waves alternate: one reads while the other keeps the
+// matrix unit busy.  Waves 0-3 issue all the LDS DMA, one stage ahead.
 //
 // Token rows past the expert's count lie outside the token operand's buffer
 // range, so the hardware loads zeros; 32-row token fragments entirely past it
-// skip their MFMAs.  Work-group ids are remapped so that the tiles an XCD
-// runs together share weight and token panels in its L2.
+// skip their reads and MFMAs (a wave's two fragments are 128 rows apart, so
+// the two wave groups share a partly filled tile evenly).  Work-group ids are
+// remapped so that the tiles an XCD runs together share weight and token
+// panels in its L2.
 
 #include <algorithm>
 #include <cmath>
@@ -34,27 +39,16 @@
 
 namespace moe {
 
-#ifndef MOE_TILE_WAVES
-#define MOE_TILE_WAVES 8
-#endif
-constexpr int kTileWaves = MOE_TILE_WAVES;          // 4 (1 per SIMD) or 8 (2 per SIMD)
+constexpr int kTileWaves = 8;                       // two per SIMD
 constexpr int kTileThreads = 64 * kTileWaves;
-constexpr int kWaveTok = 256 / (kTileWaves / 2);    // token rows per wave (128 or 64)
-constexpr int kBFrags = kWaveTok / 32;              // 32-row token fragments per wave
+constexpr int kBFrags = 2;                          // 32-row token fragments per wave
+constexpr int kBStride = 128;                       // rows between a wave's token fragments
 constexpr int kTileBT = kTileTokens;  // token rows per tile (= padding unit)
 constexpr int kTileRows = 256;        // weight rows per tile
-#ifndef MOE_TILE_BK
-#define MOE_TILE_BK 64
-#endif
-#ifndef MOE_TILE_NS
-#define MOE_TILE_NS 2
-#endif
-constexpr int kTileBK = MOE_TILE_BK;  // K per LDS stage
-constexpr int kTileNS = MOE_TILE_NS;  // LDS ring depth (stages)
+constexpr int kTileBK = 64;           // K per LDS stage
+constexpr int kTileNS = 2;            // LDS stage buffers
+constexpr int kKSteps = kTileBK / 16;               // 32x32x16 MFMA k-steps per stage
 constexpr int kXcds = 8;
-#ifndef MOE_TILE_PERSISTENT
-#define MOE_TILE_PERSISTENT 0
-#endif
 #ifndef MOE_TILE_FEAT_GROUP
 #define MOE_TILE_FEAT_GROUP 4
 #endif
@@ -64,20 +58,14 @@ constexpr int kRowBytes = kTileBK * 2;              // LDS bytes per tile row
 constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per row
 constexpr int kOperBytes = 256 * kRowBytes;         // one operand tile in LDS
 constexpr int kStageBytes = 2 * kOperBytes;         // A + B
-constexpr int kDmaPerWave = 256 * kChunks / 64 / kTileWaves;  // 1 KiB DMA loads per wave per operand
-constexpr int kKSteps = kTileBK / 16;               // 32x32x16 MFMA k-steps per stage
-static_assert(kTileBK == 32 || kTileBK == 64, "stage K must be 32 or 64");
-static_assert(kTileNS >= 2 && kTileNS <= 4, "ring depth 2..4");
-static_assert(kTileNS * kStageBytes <= 160 * 1024, "LDS ring exceeds 160 KiB");
+constexpr int kDmaWaves = 4;                        // waves 0-3 issue the DMA
+constexpr int kDmaPerWave = 256 * kChunks / 64 / kDmaWaves;  // 1 KiB DMA loads per wave per operand
+static_assert(kChunks == 8 && kDmaPerWave == 8, "fragment and DMA addressing assume 8-chunk rows");
+static_assert(kTileNS * kStageBytes <= 160 * 1024, "LDS stages exceed 160 KiB");
 
 // XOR swizzle of the 16-byte chunks of LDS row r: the 32 rows an MFMA fragment
 // reads (and the rows a DMA fills) fall in distinct banks.
-__device__ inline int swz_key(int r) {
-  return kChunks == 8 ? ((r ^ (r >> 3)) & 7) : (((r >> 1) ^ (r >> 3)) & 3);
-}
-__device__ inline int swz(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ swz_key(row)) << 4);
-}
+__device__ inline int swz_key(int r) { return (r ^ (r >> 3)) & 7; }
 
 __device__ inline f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
@@ -116,8 +104,12 @@ struct TileCtx {
   uint32_t voffA[kDmaPerWave], voffB[kDmaPerWave];
   int dma_base;                    // this wave's first DMA slot (1 KiB units)
   uint32_t k_byte0;                // byte offset of this part's first K column
-  int arow[4];
-  int brow;                        // first token row of this wave inside the tile
+  // LDS byte offsets of this lane's first A and B fragment rows.  The swizzle
+  // of row arow + r (arow a multiple of 32, r < 32) is key(r) ^ 4 (arow / 32
+  // & 1), so a fragment at k-step kk sits at base ^ ((2 kk ^ that term) << 4)
+  // plus a constant row offset: a few registers and immediate offsets serve
+  // every read.
+  uint32_t lbA, lbB;
 };
 
 // Issue stage ks's DMA loads into stage buffer `buf`: each lane fetches the
@@ -134,176 +126,104 @@ __device__ __forceinline__ void tile_issue(const TileCtx& c, char* buf, int ks) 
         c.rB, (lds_void*)(buf + kOperBytes + (c.dma_base + j) * 1024), 16, c.voffB[j], so, 0, 0);
 }
 
-template <int NBV>
-__device__ __forceinline__ void tile_frags(const TileCtx& c, const char* buf, int kk, int lane,
-                                           uint4 (&af)[4], uint4 (&bf)[kBFrags]) {
-  const char* A = buf;
-  const char* B = buf + kOperBytes;
-  const int r32 = lane & 31, chunk = kk * 2 + (lane >> 5);
+// A stage's fragments: per k-step, the wave's four A fragments (32 weight
+// rows each) and its NBV valid token fragments.  A fragment a starts at
+// weight row arow(a) of the wave's half, token fragment b at row b * kBStride
+// of the wave's slice.
+template <int NBV, bool GATEUP>
+__device__ __forceinline__ void tile_load(const TileCtx& c, const char* buf,
+                                          uint4 (&fa)[kKSteps][4], uint4 (&fb)[kKSteps][kBFrags]) {
 #pragma unroll
-  for (int a = 0; a < 4; ++a) af[a] = *reinterpret_cast<const uint4*>(A + swz(c.arow[a] + r32, chunk));
+  for (int kk = 0; kk < kKSteps; ++kk) {
 #pragma unroll
-  for (int b = 0; b < NBV; ++b)
-    bf[b] = *reinterpret_cast<const uint4*>(B + swz(c.brow + b * 32 + r32, chunk));
+    for (int a = 0; a < 4; ++a) {
+      const int arow = GATEUP ? (a < 2 ? 0 : 128) + (a & 1) * 32 : a * 32;
+      const uint32_t off = c.lbA ^ (uint32_t)(((2 * kk) ^ (4 * (a & 1))) << 4);
+      fa[kk][a] = *reinterpret_cast<const uint4*>(buf + off + arow * kRowBytes);
+    }
+#pragma unroll
+    for (int b = 0; b < NBV; ++b) {
+      const uint32_t off = c.lbB ^ (uint32_t)((2 * kk) << 4);
+      fb[kk][b] =
+          *reinterpret_cast<const uint4*>(buf + kOperBytes + off + b * kBStride * kRowBytes);
+    }
+    // keep the reads in k-step order
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
-// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-
-#ifndef MOE_TILE_PRELOAD
-#define MOE_TILE_PRELOAD 0
-#endif
-
 template <int NBV>
-__device__ __forceinline__ void tile_compute(const TileCtx& c, const char* buf, int lane,
-                                             f32x16 (&acc)[4][kBFrags]) {
-#if MOE_TILE_PRELOAD
-  // all of the stage's fragments first (LDS returns in order, so each
-  // k-step's MFMAs wait only for their own reads), then the MFMAs
-  uint4 fa[kKSteps][4], fb[kKSteps][kBFrags];
-#pragma unroll
-  for (int kk = 0; kk < kKSteps; ++kk) tile_frags<NBV>(c, buf, kk, lane, fa[kk], fb[kk]);
+__device__ __forceinline__ void tile_mfma(const uint4 (&fa)[kKSteps][4],
+                                          const uint4 (&fb)[kKSteps][kBFrags],
+                                          f32x16 (&acc)[4][kBFrags]) {
 #pragma unroll
   for (int kk = 0; kk < kKSteps; ++kk)
 #pragma unroll
     for (int b = 0; b < NBV; ++b)
 #pragma unroll
       for (int a = 0; a < 4; ++a) acc[a][b] = mfma32(fa[kk][a], fb[kk][b], acc[a][b]);
-  return;
-#endif
-  uint4 af[4], bf[kBFrags], na[4], nb[kBFrags];
-  tile_frags<NBV>(c, buf, 0, lane, af, bf);
-#pragma unroll
-  for (int kk = 0; kk < kKSteps; ++kk) {
-    if (kk + 1 < kKSteps) tile_frags<NBV>(c, buf, kk + 1, lane, na, nb);
-#if MOE_TILE_SCHED
-    __builtin_amdgcn_sched_barrier(0);
-#endif
-#pragma unroll
-    for (int b = 0; b < NBV; ++b)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) acc[a][b] = mfma32(af[a], bf[b], acc[a][b]);
-#ifndef MOE_TILE_SCHED
-#define MOE_TILE_SCHED 0
-#endif
-#if MOE_TILE_SCHED
-    // hard grouping: the next k-step's reads were issued before this
-    // k-step's MFMAs and both fragment sets stay live
-    __builtin_amdgcn_sched_barrier(0);
-    if (false) {
-#else
-    // order: the next k-step's fragment reads one per MFMA, then the rest
-    // of the MFMAs, so the reads overlap this k-step's matrix work
-    if (kk + 1 < kKSteps) {
-#endif
-      constexpr int nr = 4 + NBV, nm = 4 * NBV;
-      constexpr int pairs = nr < nm ? nr : nm;
-#pragma unroll
-      for (int i = 0; i < pairs; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-      if (nm > pairs) __builtin_amdgcn_sched_group_barrier(kSchedMfma, nm - pairs, 0);
-      if (nr > pairs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, nr - pairs, 0);
-    }
-    if (kk + 1 < kKSteps) {
-#pragma unroll
-      for (int a = 0; a < 4; ++a) af[a] = na[a];
-#pragma unroll
-      for (int b = 0; b < kBFrags; ++b) bf[b] = nb[b];
-    }
+}
+
+// One stage s: its data sits in `cur`.  If ISSUE, waves 0-3 first send stage
+// s + 1 to `nxt` (the buffer of stage s - 1, whose last readers, waves 4-7,
+// finished a phase earlier).  After the MFMAs, waves 0-3 wait for that DMA,
+// so the barrier that follows opens stage s + 1 to every wave.
+template <int NBV, bool GATEUP, bool ISSUE>
+__device__ __forceinline__ void tile_stage(const TileCtx& c, char* cur, char* nxt, int s,
+                                           bool dma, uint4 (&fa)[kKSteps][4],
+                                           uint4 (&fb)[kKSteps][kBFrags],
+                                           f32x16 (&acc)[4][kBFrags]) {
+  if (ISSUE && dma) tile_issue(c, nxt, s + 1);
+  tile_load<NBV, GATEUP>(c, cur, fa, fb);
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  tile_mfma<NBV>(fa, fb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<0>();            // stage s + 1 landed (nothing outstanding in waves 4-7)
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Main loop over K (nk stages, a positive even number).  Stage s lives in
+// buffer s % 2; every wait count is a compile-time constant, so the
+// compiler's own wait analysis sees which buffer each DMA fills.
+template <int NBV, bool GATEUP>
+__device__ __forceinline__ void tile_main_loop(const TileCtx& c, char* st0, char* st1, int nk,
+                                               int g, f32x16 (&acc)[4][kBFrags]) {
+  uint4 fa[kKSteps][4], fb[kKSteps][kBFrags];
+  const bool dma = g == 0;
+  if (dma) tile_issue(c, st0, 0);
+  wait_vmcnt<0>();
+  lds_barrier();                                   // stage 0 visible
+  if (g == 1) lds_barrier();                       // waves 4-7 run one phase behind
+  __builtin_amdgcn_sched_barrier(0);
+  int s = 0;
+  for (; s < nk - 2; s += 2) {
+    tile_stage<NBV, GATEUP, true>(c, st0, st1, s, dma, fa, fb, acc);
+    tile_stage<NBV, GATEUP, true>(c, st1, st0, s + 1, dma, fa, fb, acc);
   }
+  tile_stage<NBV, GATEUP, true>(c, st0, st1, s, dma, fa, fb, acc);
+  tile_stage<NBV, GATEUP, false>(c, st1, st0, s + 1, dma, fa, fb, acc);
+  if (g == 0) lds_barrier();                       // same barrier count in both groups
 }
-
-// Wait for stage ks's loads: the loads of the n_after stages issued after it
-// may stay in flight.
-__device__ __forceinline__ void wait_stage(int n_after) {
-  constexpr int per_stage = 2 * kDmaPerWave;
-  if (n_after >= 2) wait_vmcnt<2 * per_stage>();
-  else if (n_after == 1) wait_vmcnt<per_stage>();
-  else wait_vmcnt<0>();
-}
-
-// Main loop over K.  Ring of kTileNS stage buffers: stage ks lives in buffer
-// ks % NS; after the barrier that opens stage ks (all waves have finished
-// stage ks - 1), the loads of stage ks + NS - 1 are issued into the buffer
-// stage ks - 1 used, so loads run NS - 1 stages ahead of the MFMAs.
-// nk is a multiple of kTileNS (checked on the host), so every pass of the
-// outer loop runs all kTileNS stages: no early exit inside the unrolled body.
-template <int NBV>
-__device__ __forceinline__ void tile_main_loop(const TileCtx& c, char* const (&bufs)[kTileNS],
-                                               int nk, int lane, f32x16 (&acc)[4][kBFrags]) {
-#pragma unroll
-  for (int s = 0; s < kTileNS - 1; ++s) tile_issue(c, bufs[s], s);
-  for (int ks0 = 0; ks0 < nk; ks0 += kTileNS) {
-    const bool last = ks0 + kTileNS >= nk;
-#pragma unroll
-    for (int u = 0; u < kTileNS; ++u) {
-      const int ks = ks0 + u;
-      // stages issued after ks: NS - 2 in steady state; in the last pass the
-      // loads stop at stage nk - 1 (issued at u = 0)
-      wait_stage(last ? min(kTileNS - 2, kTileNS - 1 - u) : kTileNS - 2);
-      lds_barrier();
-      // keep the DMA issue right after the barrier: the scheduler would
-      // otherwise sink it behind the MFMAs and shrink the prefetch distance
-      __builtin_amdgcn_sched_barrier(0);
-      if (!last || u == 0) tile_issue(c, bufs[(u + kTileNS - 1) % kTileNS], ks + kTileNS - 1);
-      __builtin_amdgcn_sched_barrier(0);
-      tile_compute<NBV>(c, bufs[u], lane, acc);
-    }
-  }
-}
-
-#ifdef MOE_TILE_WPE
-#define MOE_TILE_WPE_ATTR __attribute__((amdgpu_waves_per_eu(MOE_TILE_WPE, MOE_TILE_WPE)))
-#else
-#define MOE_TILE_WPE_ATTR
-#endif
 
 template <bool GATEUP>
-__global__ __launch_bounds__(kTileThreads, 1) MOE_TILE_WPE_ATTR void tile_gemm_kernel(
+__global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
     const bf16_t* __restrict__ act, const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
     void* __restrict__ outp, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ num_tiles,
     const int32_t* __restrict__ tile_expert, int N, int K, int n_ft, int n_tt, int per_xcd,
     int parts, size_t part_stride) {
-  // one __shared__ array per ring stage, so that the compiler can tell which
-  // DMA each LDS read depends on
+  // one __shared__ array per stage buffer, so that the compiler can tell
+  // which DMA each LDS read depends on
   __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
-#if MOE_TILE_NS > 2
-  __shared__ __attribute__((aligned(1024))) char st2[kStageBytes];
-#endif
-#if MOE_TILE_NS > 3
-  __shared__ __attribute__((aligned(1024))) char st3[kStageBytes];
-#endif
-  char* const bufs[kTileNS] = {st0, st1
-#if MOE_TILE_NS > 2
-                               , st2
-#endif
-#if MOE_TILE_NS > 3
-                               , st3
-#endif
-  };
   constexpr int FB = GATEUP ? kTileRows / 2 : kTileRows;  // output features per tile
 
   // ---- tile id: XCD-contiguous remap, then groups of kFeatGroup feature tiles
-#if MOE_TILE_PERSISTENT
-  // persistent: workgroup j of XCD x walks positions j, j + W, ... of that
-  // XCD's contiguous range, W = workgroups per XCD, so the W tiles an XCD runs
-  // together are W consecutive positions (shared panels) and stay in step
-  const int xcd = blockIdx.x % kXcds;
-  const int wg_per_xcd = gridDim.x / kXcds;
-  for (int pos = blockIdx.x / kXcds; pos < per_xcd; pos += wg_per_xcd) {
-  int Lp = xcd * per_xcd + pos;
-  if (Lp >= parts * n_ft * n_tt) break;
-#else
-  do {                                      // one tile; `continue` leaves
   const int L = blockIdx.x;
   int Lp = (L % kXcds) * per_xcd + L / kXcds;
   if (Lp >= parts * n_ft * n_tt) return;
-#endif
   const int part = Lp / (n_ft * n_tt);      // K-split part (slowest)
   Lp -= part * n_ft * n_tt;
   const int grp = Lp / (kFeatGroup * n_tt);
@@ -311,7 +231,7 @@ __global__ __launch_bounds__(kTileThreads, 1) MOE_TILE_WPE_ATTR void tile_gemm_k
   const int gsize = min(kFeatGroup, n_ft - grp * kFeatGroup);
   const int tt = rem / gsize;
   const int ft = grp * kFeatGroup + rem % gsize;
-  if (tt >= *num_tiles) continue;          // past the token tiles in use
+  if (tt >= *num_tiles) return;             // past the token tiles in use
   const int e = tile_expert[tt];
   const int row0 = tt * kTileBT;
   const int valid_end = offsets[e] + counts[e];
@@ -320,10 +240,11 @@ __global__ __launch_bounds__(kTileThreads, 1) MOE_TILE_WPE_ATTR void tile_gemm_k
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wf = wave & 1, wt = wave >> 1;   // weight half, token slice
+  const int g = wave >> 2;                   // wave group (ping-pong)
 
-  // ---- DMA assignment: wave w fills LDS slots [w * kDmaPerWave, +kDmaPerWave)
-  // of each operand (1 KiB each); slot q's lane i holds LDS chunk position
-  // p = q * 64 + i = row * kChunks + swizzled chunk.
+  // ---- DMA assignment: wave w < 4 fills LDS slots [w * kDmaPerWave,
+  // +kDmaPerWave) of each operand (1 KiB each); slot q's lane i holds LDS
+  // chunk position p = q * 64 + i = row * kChunks + swizzled chunk.
   TileCtx c;
   c.dma_base = wave * kDmaPerWave;
   const int Kp = K / parts;                 // K columns of this part
@@ -339,9 +260,8 @@ __global__ __launch_bounds__(kTileThreads, 1) MOE_TILE_WPE_ATTR void tile_gemm_k
     c.voffB[j] = (uint32_t)r * row_bytes + cg * 16;
   }
   if constexpr (GATEUP) {
-    // the first half of the waves fills A rows 0..127 (gate), the second
-    // half rows 128..255 (up)
-    const bf16_t* Wsrc = (wave < kTileWaves / 2 ? W0 : W1) + ((size_t)e * N + f0) * K;
+    // waves 0-1 fill A rows 0..127 (gate), waves 2-3 rows 128..255 (up)
+    const bf16_t* Wsrc = (wave < kDmaWaves / 2 ? W0 : W1) + ((size_t)e * N + f0) * K;
     c.rA = make_rsrc(Wsrc, 128 * row_bytes);
   } else {
     c.rA = make_rsrc(W0 + ((size_t)e * N + f0) * K, 256 * row_bytes);
@@ -349,13 +269,18 @@ __global__ __launch_bounds__(kTileThreads, 1) MOE_TILE_WPE_ATTR void tile_gemm_k
   // token rows past the expert's count fall outside the resource: read as 0
   const int nvalid = max(0, min(kTileBT, valid_end - row0));
   c.rB = make_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    if constexpr (GATEUP) c.arow[a] = (a < 2 ? 0 : 128) + wf * 64 + (a & 1) * 32;
-    else c.arow[a] = wf * 128 + a * 32;
+
+  // ---- fragment rows: A fragment a of wave half wf, token fragments at rows
+  // wt * 32 and wt * 32 + kBStride of the tile
+  {
+    const int r32 = lane & 31, h = lane >> 5;
+    const uint32_t lrow = (uint32_t)r32 * kRowBytes + (uint32_t)((h ^ swz_key(r32)) << 4);
+    c.lbA = (uint32_t)(GATEUP ? wf * 64 : wf * 128) * kRowBytes + lrow;
+    c.lbB = (uint32_t)(wt * 32) * kRowBytes + (lrow ^ (uint32_t)((4 * (wt & 1)) << 4));
   }
-  c.brow = wt * kWaveTok;
-  const int nbv = max(0, min(kBFrags, (valid_end - (row0 + wt * kWaveTok) + 31) / 32));
+  int nbv = 0;                              // valid token fragments of this wave
+#pragma unroll
+  for (int b = 0; b < kBFrags; ++b) nbv += row0 + wt * 32 + b * kBStride < valid_end;
 
   f32x16 acc[4][kBFrags];
 #pragma unroll
@@ -365,16 +290,12 @@ __global__ __launch_bounds__(kTileThreads, 1) MOE_TILE_WPE_ATTR void tile_gemm_k
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
 
-  // wave-uniform choice; every variant runs the same loads and barriers
+  // wave-uniform choice; every variant runs the same DMA and barriers
   const int nk = Kp / kTileBK;
   switch (nbv) {
-#if MOE_TILE_WAVES == 4
-    case 4: tile_main_loop<4>(c, bufs, nk, lane, acc); break;
-    case 3: tile_main_loop<3>(c, bufs, nk, lane, acc); break;
-#endif
-    case 2: tile_main_loop<2>(c, bufs, nk, lane, acc); break;
-    case 1: tile_main_loop<1>(c, bufs, nk, lane, acc); break;
-    default: tile_main_loop<0>(c, bufs, nk, lane, acc); break;
+    case 2: tile_main_loop<2, GATEUP>(c, st0, st1, nk, g, acc); break;
+    case 1: tile_main_loop<1, GATEUP>(c, st0, st1, nk, g, acc); break;
+    default: tile_main_loop<0, GATEUP>(c, st0, st1, nk, g, acc); break;
   }
 
   // ---- epilogue.  D of a 32x32 MFMA: lane holds column n = lane % 32 and rows
@@ -383,7 +304,7 @@ __global__ __launch_bounds__(kTileThreads, 1) MOE_TILE_WPE_ATTR void tile_gemm_k
   const int r32 = lane & 31, half = lane >> 5;
 #pragma unroll
   for (int b = 0; b < kBFrags; ++b) {
-    const size_t row = (size_t)(row0 + wt * kWaveTok + b * 32 + r32);
+    const size_t row = (size_t)(row0 + wt * 32 + b * kBStride + r32);
     if constexpr (GATEUP) {
       bf16_t* h = reinterpret_cast<bf16_t*>(outp) + row * N;
 #pragma unroll
@@ -414,11 +335,6 @@ __global__ __launch_bounds__(kTileThreads, 1) MOE_TILE_WPE_ATTR void tile_gemm_k
         }
     }
   }
-#if MOE_TILE_PERSISTENT
-  }  // tile loop
-#else
-  } while (0);
-#endif
 }
 
 template <bool GATEUP>
@@ -433,20 +349,7 @@ static void tile_launch(const Dims& D, const void* act, const void* W0, const vo
   const int parts = GATEUP ? 1 : D.down_splits;
   const int total = parts * n_ft * n_tt;
   const int per_xcd = (total + kXcds - 1) / kXcds;
-#if MOE_TILE_PERSISTENT
-  // one workgroup per CU (the LDS ring allows one), at most one per position
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      n_cu = 256;
-  }
-  const int wg_per_xcd = std::max(1, std::min(per_xcd, n_cu / kXcds));
-  const int grid = wg_per_xcd * kXcds;
-#else
   const int grid = per_xcd * kXcds;
-#endif
   tile_gemm_kernel<GATEUP><<<grid, kTileThreads, 0, s>>>(
       (const bf16_t*)act, (const bf16_t*)W0, (const bf16_t*)W1, out, counts, offsets, num_tiles,
       tile_expert, N, K, n_ft, n_tt, per_xcd, parts, (size_t)D.max_rows * N);
