@@ -12,17 +12,21 @@
 // same 128 up rows, and each wave holds gate and up accumulators of the same
 // features, so SiLU(gate) * up is applied in registers and only H is stored.
 //
-// K is staged 64 at a time through two LDS stage buffers filled by gfx950
-// buffer loads straight to LDS (no VGPR staging): each lane fetches the 16
-// bytes that belong at its slot of the XOR-swizzled layout.  LDS rows are 128
-// bytes; chunk c of row r sits at c ^ ((r ^ r >> 3) & 7), so the 32 rows an
-// MFMA fragment reads fall in distinct banks (no bank conflicts measured).
+// K is staged 64 at a time through LDS buffers filled by gfx950 buffer loads
+// straight to LDS (no VGPR staging): each lane fetches the 16 bytes that
+// belong at its slot of the XOR-swizzled layout.  LDS rows are 128 bytes;
+// chunk c of row r sits at c ^ ((r ^ r >> 3) & 7), so the 32 rows an MFMA
+// fragment reads fall in distinct banks (no bank conflicts measured).
 //
 // Ping-pong: waves 0-3 (one per SIMD) and waves 4-7 run the same sequence per
 // stage -- read the stage's fragments from LDS into registers, barrier, run
 // the stage's 32 MFMAs, barrier -- but waves 4-7 pass one extra barrier first,
 // so each SIMD's two waves alternate: one reads while the other keeps the
-// matrix unit busy.  Waves 0-3 issue all the LDS DMA, one stage ahead.
+// matrix unit busy.  The DMA is split so that the CU's address unit is busy in
+// both phases: waves 0-3 fetch the weight operand (A, two buffers, one stage
+// ahead) as they start reading, waves 4-7 the token operand (B, three
+// buffers, two stages ahead) after their reads.  The five 32 KiB buffers fill
+// the 160 KiB of LDS.
 //
 // Token rows past the expert's count lie outside the token operand's buffer
 // range, so the hardware loads zeros; 32-row token fragments entirely past it
@@ -46,7 +50,7 @@ constexpr int kBStride = 128;                       // rows between a wave's tok
 constexpr int kTileBT = kTileTokens;  // token rows per tile (= padding unit)
 constexpr int kTileRows = 256;        // weight rows per tile
 constexpr int kTileBK = 64;           // K per LDS stage
-constexpr int kTileNS = 2;            // LDS stage buffers
+constexpr int kTileNS = 2;            // A buffers: the K loop runs stages in pairs
 constexpr int kKSteps = kTileBK / 16;               // 32x32x16 MFMA k-steps per stage
 constexpr int kXcds = 8;
 #ifndef MOE_TILE_FEAT_GROUP
@@ -56,12 +60,11 @@ constexpr int kFeatGroup = MOE_TILE_FEAT_GROUP;  // feature tiles per XCD-local 
 
 constexpr int kRowBytes = kTileBK * 2;              // LDS bytes per tile row
 constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per row
-constexpr int kOperBytes = 256 * kRowBytes;         // one operand tile in LDS
-constexpr int kStageBytes = 2 * kOperBytes;         // A + B
-constexpr int kDmaWaves = 4;                        // waves 0-3 issue the DMA
-constexpr int kDmaPerWave = 256 * kChunks / 64 / kDmaWaves;  // 1 KiB DMA loads per wave per operand
+constexpr int kOperBytes = 256 * kRowBytes;         // one operand tile (one buffer) in LDS
+constexpr int kDmaWaves = 4;                        // waves issuing one operand's DMA
+constexpr int kDmaPerWave = 256 * kChunks / 64 / kDmaWaves;  // 1 KiB DMA loads per wave per stage
 static_assert(kChunks == 8 && kDmaPerWave == 8, "fragment and DMA addressing assume 8-chunk rows");
-static_assert(kTileNS * kStageBytes <= 160 * 1024, "LDS stages exceed 160 KiB");
+static_assert(5 * kOperBytes <= 160 * 1024, "LDS buffers exceed 160 KiB");
 
 // XOR swizzle of the 16-byte chunks of LDS row r: the 32 rows an MFMA fragment
 // reads (and the rows a DMA fills) fall in distinct banks.
@@ -112,26 +115,30 @@ struct TileCtx {
   uint32_t lbA, lbB;
 };
 
-// Issue stage ks's DMA loads into stage buffer `buf`: each lane fetches the
-// global 16 bytes that belong at LDS slot (dma_base + j) * 64 + lane.
-__device__ __forceinline__ void tile_issue(const TileCtx& c, char* buf, int ks) {
+// One operand of stage ks's DMA into buffer `buf`: A (weights) from waves
+// 0-3 (g = 0), B (tokens) from waves 4-7 (g = 1).  Lane i of a wave's load j
+// fetches the global 16 bytes that belong at LDS slot (dma_base + j) * 64 + i.
+__device__ __forceinline__ void tile_issue_half(const TileCtx& c, char* buf, int ks, int g) {
   const uint32_t so = c.k_byte0 + (uint32_t)ks * kTileBK * 2;
+  if (g == 0) {
 #pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        c.rA, (lds_void*)(buf + (c.dma_base + j) * 1024), 16, c.voffA[j], so, 0, 0);
+    for (int j = 0; j < kDmaPerWave; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          c.rA, (lds_void*)(buf + (c.dma_base + j) * 1024), 16, c.voffA[j], so, 0, 0);
+  } else {
 #pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        c.rB, (lds_void*)(buf + kOperBytes + (c.dma_base + j) * 1024), 16, c.voffB[j], so, 0, 0);
+    for (int j = 0; j < kDmaPerWave; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          c.rB, (lds_void*)(buf + (c.dma_base + j) * 1024), 16, c.voffB[j], so, 0, 0);
+  }
 }
 
-// A stage's fragments: per k-step, the wave's four A fragments (32 weight
-// rows each) and its NBV valid token fragments.  A fragment a starts at
+// A stage's fragments (A from `buf`, B from `bbuf`): per k-step, the wave's
+// four A fragments (32 weight rows each) and its NBV valid token fragments.  A fragment a starts at
 // weight row arow(a) of the wave's half, token fragment b at row b * kBStride
 // of the wave's slice.
 template <int NBV, bool GATEUP>
-__device__ __forceinline__ void tile_load(const TileCtx& c, const char* buf,
+__device__ __forceinline__ void tile_load(const TileCtx& c, const char* buf, const char* bbuf,
                                           uint4 (&fa)[kKSteps][4], uint4 (&fb)[kKSteps][kBFrags]) {
 #pragma unroll
   for (int kk = 0; kk < kKSteps; ++kk) {
@@ -144,8 +151,7 @@ __device__ __forceinline__ void tile_load(const TileCtx& c, const char* buf,
 #pragma unroll
     for (int b = 0; b < NBV; ++b) {
       const uint32_t off = c.lbB ^ (uint32_t)((2 * kk) << 4);
-      fb[kk][b] =
-          *reinterpret_cast<const uint4*>(buf + kOperBytes + off + b * kBStride * kRowBytes);
+      fb[kk][b] = *reinterpret_cast<const uint4*>(bbuf + off + b * kBStride * kRowBytes);
     }
     // keep the reads in k-step order
     __builtin_amdgcn_sched_barrier(0);
@@ -164,46 +170,61 @@ __device__ __forceinline__ void tile_mfma(const uint4 (&fa)[kKSteps][4],
       for (int a = 0; a < 4; ++a) acc[a][b] = mfma32(fa[kk][a], fb[kk][b], acc[a][b]);
 }
 
-// One stage s: its data sits in `cur`.  If ISSUE, waves 0-3 first send stage
-// s + 1 to `nxt` (the buffer of stage s - 1, whose last readers, waves 4-7,
-// finished a phase earlier).  After the MFMAs, waves 0-3 wait for that DMA,
-// so the barrier that follows opens stage s + 1 to every wave.
-template <int NBV, bool GATEUP, bool ISSUE>
-__device__ __forceinline__ void tile_stage(const TileCtx& c, char* cur, char* nxt, int s,
-                                           bool dma, uint4 (&fa)[kKSteps][4],
+// One stage s: A in `acur` (stage s + 1's A goes to `anxt`), B in `bcur`.
+// Waves 0-3 send A of stage s + 1 as they start reading stage s; waves 4-7
+// send B of stage s + 2 into `bnew` (the B buffer of stage s - 1) after
+// their reads.  XWAIT after the reads, then every wave waits for all of its
+// DMA after the MFMAs (waves 0-3: A of stage s + 1; waves 4-7: B of s + 2).
+template <int NBV, bool GATEUP, bool ISSUE_A, bool ISSUE_B, int XWAIT>
+__device__ __forceinline__ void tile_stage(const TileCtx& c, char* acur, char* anxt,
+                                           const char* bcur, char* bnew, int s, int g,
+                                           uint4 (&fa)[kKSteps][4],
                                            uint4 (&fb)[kKSteps][kBFrags],
                                            f32x16 (&acc)[4][kBFrags]) {
-  if (ISSUE && dma) tile_issue(c, nxt, s + 1);
-  tile_load<NBV, GATEUP>(c, cur, fa, fb);
+  if (ISSUE_A && g == 0) tile_issue_half(c, anxt, s + 1, 0);
+  tile_load<NBV, GATEUP>(c, acur, bcur, fa, fb);
+  if (ISSUE_B && g == 1) tile_issue_half(c, bnew, s + 2, 1);
+  wait_vmcnt<XWAIT>();
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
   tile_mfma<NBV>(fa, fb, acc);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<0>();            // stage s + 1 landed (nothing outstanding in waves 4-7)
+  wait_vmcnt<0>();
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Main loop over K (nk stages, a positive even number).  Stage s lives in
-// buffer s % 2; every wait count is a compile-time constant, so the
-// compiler's own wait analysis sees which buffer each DMA fills.
+// Main loop over K (nk stages, a positive even number).  A of stage s lives
+// in a0/a1 by s % 2 (compile-time), B in bring[s % 3] (run time); every wait
+// count is a compile-time constant, the same in both wave groups.
 template <int NBV, bool GATEUP>
-__device__ __forceinline__ void tile_main_loop(const TileCtx& c, char* st0, char* st1, int nk,
-                                               int g, f32x16 (&acc)[4][kBFrags]) {
+__device__ __forceinline__ void tile_main_loop(const TileCtx& c, char* a0, char* a1, char* bring,
+                                               int nk, int g, f32x16 (&acc)[4][kBFrags]) {
   uint4 fa[kKSteps][4], fb[kKSteps][kBFrags];
-  const bool dma = g == 0;
-  if (dma) tile_issue(c, st0, 0);
+  if (g == 0) {
+    tile_issue_half(c, a0, 0, 0);                  // A of stage 0
+  } else {
+    tile_issue_half(c, bring, 0, 1);               // B of stages 0 and 1
+    tile_issue_half(c, bring + kOperBytes, 1, 1);
+  }
   wait_vmcnt<0>();
   lds_barrier();                                   // stage 0 visible
   if (g == 1) lds_barrier();                       // waves 4-7 run one phase behind
   __builtin_amdgcn_sched_barrier(0);
+  int bs = 0;                                      // s % 3
+  auto bb = [&](int i) { return bring + i * kOperBytes; };
+  auto inc3 = [](int i) { return i == 2 ? 0 : i + 1; };
   int s = 0;
   for (; s < nk - 2; s += 2) {
-    tile_stage<NBV, GATEUP, true>(c, st0, st1, s, dma, fa, fb, acc);
-    tile_stage<NBV, GATEUP, true>(c, st1, st0, s + 1, dma, fa, fb, acc);
+    const int b1 = inc3(bs), b2 = inc3(b1), b3 = inc3(b2);
+    tile_stage<NBV, GATEUP, true, true, kDmaPerWave>(c, a0, a1, bb(bs), bb(b2), s, g, fa, fb, acc);
+    tile_stage<NBV, GATEUP, true, true, kDmaPerWave>(c, a1, a0, bb(b1), bb(b3), s + 1, g, fa, fb,
+                                                     acc);
+    bs = b2;
   }
-  tile_stage<NBV, GATEUP, true>(c, st0, st1, s, dma, fa, fb, acc);
-  tile_stage<NBV, GATEUP, false>(c, st1, st0, s + 1, dma, fa, fb, acc);
+  tile_stage<NBV, GATEUP, true, false, 0>(c, a0, a1, bb(bs), nullptr, s, g, fa, fb, acc);
+  tile_stage<NBV, GATEUP, false, false, 0>(c, a1, a0, bb(inc3(bs)), nullptr, s + 1, g, fa, fb,
+                                           acc);
   if (g == 0) lds_barrier();                       // same barrier count in both groups
 }
 
@@ -214,10 +235,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ num_tiles,
     const int32_t* __restrict__ tile_expert, int N, int K, int n_ft, int n_tt, int per_xcd,
     int parts, size_t part_stride) {
-  // one __shared__ array per stage buffer, so that the compiler can tell
-  // which DMA each LDS read depends on
-  __shared__ __attribute__((aligned(1024))) char st0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char st1[kStageBytes];
+  // separate __shared__ arrays for the A buffers and the B ring, so that the
+  // compiler can tell which DMA each LDS read depends on
+  __shared__ __attribute__((aligned(1024))) char sa0[kOperBytes];
+  __shared__ __attribute__((aligned(1024))) char sa1[kOperBytes];
+  __shared__ __attribute__((aligned(1024))) char sbr[3 * kOperBytes];
   constexpr int FB = GATEUP ? kTileRows / 2 : kTileRows;  // output features per tile
 
   // ---- tile id: XCD-contiguous remap, then groups of kFeatGroup feature tiles
@@ -242,11 +264,11 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
   const int wf = wave & 1, wt = wave >> 1;   // weight half, token slice
   const int g = wave >> 2;                   // wave group (ping-pong)
 
-  // ---- DMA assignment: wave w < 4 fills LDS slots [w * kDmaPerWave,
-  // +kDmaPerWave) of each operand (1 KiB each); slot q's lane i holds LDS
-  // chunk position p = q * 64 + i = row * kChunks + swizzled chunk.
+  // ---- DMA assignment: wave w fills LDS slots [(w % 4) * kDmaPerWave,
+  // +kDmaPerWave) of its operand (1 KiB each); slot q's lane i holds LDS chunk
+  // position p = q * 64 + i = row * kChunks + swizzled chunk.
   TileCtx c;
-  c.dma_base = wave * kDmaPerWave;
+  c.dma_base = (wave & 3) * kDmaPerWave;
   const int Kp = K / parts;                 // K columns of this part
   c.k_byte0 = (uint32_t)(part * Kp) * 2;
   const uint32_t row_bytes = (uint32_t)K * 2;
@@ -260,8 +282,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
     c.voffB[j] = (uint32_t)r * row_bytes + cg * 16;
   }
   if constexpr (GATEUP) {
-    // waves 0-1 fill A rows 0..127 (gate), waves 2-3 rows 128..255 (up)
-    const bf16_t* Wsrc = (wave < kDmaWaves / 2 ? W0 : W1) + ((size_t)e * N + f0) * K;
+    // waves 0-1 fill A rows 0..127 (gate), waves 2-3 rows 128..255 (up);
+    // waves 4-7 issue no A
+    const bf16_t* Wsrc = ((wave & 3) < kDmaWaves / 2 ? W0 : W1) + ((size_t)e * N + f0) * K;
     c.rA = make_rsrc(Wsrc, 128 * row_bytes);
   } else {
     c.rA = make_rsrc(W0 + ((size_t)e * N + f0) * K, 256 * row_bytes);
@@ -293,9 +316,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
   // wave-uniform choice; every variant runs the same DMA and barriers
   const int nk = Kp / kTileBK;
   switch (nbv) {
-    case 2: tile_main_loop<2, GATEUP>(c, st0, st1, nk, g, acc); break;
-    case 1: tile_main_loop<1, GATEUP>(c, st0, st1, nk, g, acc); break;
-    default: tile_main_loop<0, GATEUP>(c, st0, st1, nk, g, acc); break;
+    case 2: tile_main_loop<2, GATEUP>(c, sa0, sa1, sbr, nk, g, acc); break;
+    case 1: tile_main_loop<1, GATEUP>(c, sa0, sa1, sbr, nk, g, acc); break;
+    default: tile_main_loop<0, GATEUP>(c, sa0, sa1, sbr, nk, g, acc); break;
   }
 
   // ---- epilogue.  D of a 32x32 MFMA: lane holds column n = lane % 32 and rows
