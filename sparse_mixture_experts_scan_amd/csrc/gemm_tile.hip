@@ -70,6 +70,14 @@ static_assert(5 * kOperBytes <= 160 * 1024, "LDS buffers exceed 160 KiB");
 // reads (and the rows a DMA fills) fall in distinct banks.
 __device__ inline int swz_key(int r) { return (r ^ (r >> 3)) & 7; }
 
+// SiLU(z) = z * sigmoid(z) for the bf16 epilogue: sigmoid from the hardware
+// base-2 exponential and reciprocal (about one fp32 ulp each, far below the
+// bf16 rounding of the result); exp2 overflowing to +inf gives z * 0.
+__device__ inline float silu_bf16_out(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 __device__ inline f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -340,8 +348,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
           for (int q = 0; q < 2; ++q) {
             const float g0 = acc[a][b][jj * 4 + 2 * q], u0 = acc[a + 2][b][jj * 4 + 2 * q];
             const float g1 = acc[a][b][jj * 4 + 2 * q + 1], u1 = acc[a + 2][b][jj * 4 + 2 * q + 1];
-            p[q] = (uint32_t)Elem<bf16_t>::from_f32(silu_f32(g0) * u0) |
-                   ((uint32_t)Elem<bf16_t>::from_f32(silu_f32(g1) * u1) << 16);
+            p[q] = (uint32_t)Elem<bf16_t>::from_f32(silu_bf16_out(g0) * u0) |
+                   ((uint32_t)Elem<bf16_t>::from_f32(silu_bf16_out(g1) * u1) << 16);
           }
           *reinterpret_cast<uint2*>(h + feat) = make_uint2(p[0], p[1]);
         }
