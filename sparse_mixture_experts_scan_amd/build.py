@@ -21,6 +21,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_ffn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["route_permute.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_q4.hip", "gemm_bwd.hip",
+           "gemm_bwd_tile.hip",
            "moe_ffn.hip"]
 ARCH = "gfx950"
 

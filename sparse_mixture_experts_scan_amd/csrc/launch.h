@@ -96,6 +96,24 @@ void launch_bwd_gemm_rows(const void* A, int lda, const void* B, int ldb, bool b
                           const int32_t* tb_exp, const int32_t* tb_row0, const int32_t* tb_rows,
                           hipStream_t s);
 // C_e[M][N] = sum over expert e's rows r of A[r][m] B[r][n] (bf16 out)
+// Backward GEMMs on 256 x 256 tiles (d_model and d_ff multiples of 256):
+// one launch each for a | b, Z, dX (both terms), dW2, and dW1 | dW3.
+bool bwd_tile_shape_ok(int64_t d, int64_t f);
+int bwd_tile_rows();
+void launch_bwd_recompute(const Dims& D, const void* xs, const void* Wg, const void* Wu, float* ab,
+                          int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
+                          const int32_t* tb_row0, const int32_t* tb_rows, hipStream_t s);
+void launch_bwd_z(const Dims& D, const void* dp, const void* Wd, float* z, int max_tiles,
+                  const int32_t* tb_count, const int32_t* tb_exp, const int32_t* tb_row0,
+                  const int32_t* tb_rows, hipStream_t s);
+void launch_bwd_dxs(const Dims& D, const void* dab, const void* Wg, const void* Wu, float* dxs,
+                    int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
+                    const int32_t* tb_row0, const int32_t* tb_rows, hipStream_t s);
+void launch_bwd_wgrad_down(const Dims& D, const void* dp, const void* hg, void* dWd,
+                           const int32_t* counts, const int32_t* offsets, hipStream_t s);
+void launch_bwd_wgrad_gate_up(const Dims& D, const void* dab, const void* xs, void* dWg,
+                              void* dWu, const int32_t* counts, const int32_t* offsets,
+                              hipStream_t s);
 void launch_bwd_gemm_wgrad(const Dims& D, const void* A, int lda, const void* B, int ldb,
                            void* C, int M, int N, const int32_t* counts, const int32_t* offsets,
                            hipStream_t s);

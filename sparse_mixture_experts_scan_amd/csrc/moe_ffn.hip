@@ -567,15 +567,25 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   moe::launch_bwd_tile_table(D, counts, offsets, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows,
                              s);
   if ((st = check(1, "routing launch")) != MOE_OK) return st;
+  // the 256 x 256 ping-pong GEMMs when both widths allow, else the generic one
+  const bool tiled = moe::bwd_tile_shape_ok(d, f);
   // pre-activations a = W1 x, b = W3 x of every routed row
-  moe::launch_bwd_gemm_rows(xs, d, W_gate, d, true, wstride, ab, 2 * f, D.max_rows, f, d, false,
-                            b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
-  moe::launch_bwd_gemm_rows(xs, d, W_up, d, true, wstride, ab + f, 2 * f, D.max_rows, f, d,
-                            false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+  if (tiled) {
+    moe::launch_bwd_recompute(D, xs, W_gate, W_up, ab, b.max_tiles, tb_count, tb_exp, tb_row0,
+                              tb_rows, s);
+  } else {
+    moe::launch_bwd_gemm_rows(xs, d, W_gate, d, true, wstride, ab, 2 * f, D.max_rows, f, d,
+                              false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+    moe::launch_bwd_gemm_rows(xs, d, W_up, d, true, wstride, ab + f, 2 * f, D.max_rows, f, d,
+                              false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+  }
   if ((st = check(2, "recompute launch")) != MOE_OK) return st;
   // Z = W2^T dOut_t per routed row
-  moe::launch_bwd_gemm_rows(dp, d, W_down, f, false, wstride, z, f, D.max_rows, f, d, false,
-                            b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+  if (tiled)
+    moe::launch_bwd_z(D, dp, W_down, z, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+  else
+    moe::launch_bwd_gemm_rows(dp, d, W_down, f, false, wstride, z, f, D.max_rows, f, d, false,
+                              b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
   if ((st = check(3, "Z launch")) != MOE_OK) return st;
   // dg, dA, dB, g h; the router scores' gradient; the router weight gradient
   moe::launch_bwd_rows(D, ab, z, row_token, tok_row, w, dg, dab, hg, s);
@@ -583,20 +593,32 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   moe::launch_bwd_router_wgrad(D, x, ds, F(b.wpart), dW_router, dbias, s);
   if ((st = check(4, "row/router backward launch")) != MOE_OK) return st;
   // dX_r = W1^T dA + W3^T dB
-  moe::launch_bwd_gemm_rows(dab, 2 * f, W_gate, d, false, wstride, dxs, d, D.max_rows, d, f,
-                            false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
-  moe::launch_bwd_gemm_rows(dab + 2 * (size_t)f, 2 * f, W_up, d, false, wstride, dxs, d,
-                            D.max_rows, d, f, true, b.max_tiles, tb_count, tb_exp, tb_row0,
-                            tb_rows, s);
+  if (tiled) {
+    moe::launch_bwd_dxs(D, dab, W_gate, W_up, dxs, b.max_tiles, tb_count, tb_exp, tb_row0,
+                        tb_rows, s);
+  } else {
+    moe::launch_bwd_gemm_rows(dab, 2 * f, W_gate, d, false, wstride, dxs, d, D.max_rows, d, f,
+                              false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+    moe::launch_bwd_gemm_rows(dab + 2 * (size_t)f, 2 * f, W_up, d, false, wstride, dxs, d,
+                              D.max_rows, d, f, true, b.max_tiles, tb_count, tb_exp, tb_row0,
+                              tb_rows, s);
+  }
   if ((st = check(5, "dX launch")) != MOE_OK) return st;
   moe::launch_bwd_dx(D, dxs, tok_row, W_router, ds, dx, s);
   if ((st = check(6, "dx launch")) != MOE_OK) return st;
   // weight gradients over each expert's rows
-  moe::launch_bwd_gemm_wgrad(D, dp, d, hg, f, dW_down, d, f, counts, offsets, s);
+  if (tiled)
+    moe::launch_bwd_wgrad_down(D, dp, hg, dW_down, counts, offsets, s);
+  else
+    moe::launch_bwd_gemm_wgrad(D, dp, d, hg, f, dW_down, d, f, counts, offsets, s);
   if ((st = check(7, "dW_down launch")) != MOE_OK) return st;
-  moe::launch_bwd_gemm_wgrad(D, dab, 2 * f, xs, d, dW_gate, f, d, counts, offsets, s);
-  moe::launch_bwd_gemm_wgrad(D, dab + 2 * (size_t)f, 2 * f, xs, d, dW_up, f, d, counts, offsets,
-                             s);
+  if (tiled) {
+    moe::launch_bwd_wgrad_gate_up(D, dab, xs, dW_gate, dW_up, counts, offsets, s);
+  } else {
+    moe::launch_bwd_gemm_wgrad(D, dab, 2 * f, xs, d, dW_gate, f, d, counts, offsets, s);
+    moe::launch_bwd_gemm_wgrad(D, dab + 2 * (size_t)f, 2 * f, xs, d, dW_up, f, d, counts,
+                               offsets, s);
+  }
   return check(8, "dW_gate/dW_up launch");
 }
 
