@@ -408,6 +408,82 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
     Cb += (size_t)e * p.c_estride * (CBF16 ? 2 : 4);
     brow_base = bt_out * kBT;
   }
+  if constexpr (MODE == 1 && CBF16) {
+    // full tiles: stage each 128-row half of the bf16 tile in LDS (rows of
+    // kStagePitch bytes) and write whole rows with 16-byte stores
+    constexpr int kStagePitch = kBT * 2 + 16;
+    static_assert(128 * kStagePitch <= 3 * kBOper, "staging exceeds the B ring");
+    __syncthreads();                      // every wave is past its last LDS read
+#pragma unroll
+    for (int b = 0; b < kBFragB; ++b) {
+      const int lrow = wt * 32 + r32;     // row within this half
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int aidx = wf * 128 + a * 32 + jj * 8 + half * 4;
+          const f32x16& v = acc[a][b];
+          const uint32_t lo = (uint32_t)Elem<bf16_t>::from_f32(v[jj * 4]) |
+                              ((uint32_t)Elem<bf16_t>::from_f32(v[jj * 4 + 1]) << 16);
+          const uint32_t hi = (uint32_t)Elem<bf16_t>::from_f32(v[jj * 4 + 2]) |
+                              ((uint32_t)Elem<bf16_t>::from_f32(v[jj * 4 + 3]) << 16);
+          *reinterpret_cast<uint2*>(sbr + lrow * kStagePitch + aidx * 2) = make_uint2(lo, hi);
+        }
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < 128 * (kBT * 2 / 16) / kBThreads; ++it) {
+        const int q = it * kBThreads + tid;
+        const int lrow = q / (kBT * 2 / 16), chunk = q % (kBT * 2 / 16);
+        const uint4 v = *reinterpret_cast<const uint4*>(sbr + lrow * kStagePitch + chunk * 16);
+        const size_t off = (size_t)(brow_base + b * kBStrideB + lrow) * p.ldc +
+                           (size_t)at * kBT + chunk * 8;
+        *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(Cb) + off) = v;
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  if constexpr (!CBF16) {
+    // fp32: stage (token fragment b, column half ch) = 128 rows x 128 columns
+    // at a time in LDS, written by the waves of that half, then store whole
+    // 512-byte row pieces of the tile's valid rows
+    constexpr int kStagePitch = 128 * 4 + 16;
+    static_assert(128 * kStagePitch <= 3 * kBOper, "staging exceeds the B ring");
+    __syncthreads();                      // every wave is past its last LDS read
+#pragma unroll
+    for (int b = 0; b < kBFragB; ++b)
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        if (wf == ch) {
+          const int lrow = wt * 32 + r32;
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int col = a * 32 + jj * 8 + half * 4;
+              const f32x16& v = acc[a][b];
+              *reinterpret_cast<float4*>(sbr + lrow * kStagePitch + col * 4) =
+                  make_float4(v[jj * 4], v[jj * 4 + 1], v[jj * 4 + 2], v[jj * 4 + 3]);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < 128 * 32 / kBThreads; ++it) {
+          const int q = it * kBThreads + tid;
+          const int lrow = q / 32, chunk = q % 32;
+          const int brow = b * kBStrideB + lrow;
+          if (brow < rows) {
+            const uint4 v =
+                *reinterpret_cast<const uint4*>(sbr + lrow * kStagePitch + chunk * 16);
+            const size_t off = (size_t)(brow_base + brow) * p.ldc + (size_t)at * kBT + ch * 128 +
+                               chunk * 4;
+            *reinterpret_cast<uint4*>(reinterpret_cast<float*>(Cb) + off) = v;
+          }
+        }
+        __syncthreads();
+      }
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < kBFragB; ++b) {
     const int brow = wt * 32 + b * kBStrideB + r32;
