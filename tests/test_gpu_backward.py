@@ -78,6 +78,7 @@ CASES = [
     (MoEConfig("bwd256_single", 1, 256, 256, 4, 2, "bf16"), 0.1),
     (MoEConfig("bwd256_tiles", 900, 512, 768, 8, 2, "bf16"), 0.01),  # several 256-row tiles
     (MoEConfig("bwd256_many_e", 40, 256, 256, 64, 2, "bf16"), 0.0),  # experts left empty
+    (MoEConfig("bwd256_multi", 700, 256, 256, 4, 2, "bf16"), 0.01),  # two row tiles per expert
 ]
 
 

@@ -68,9 +68,11 @@ SMALL = [
     MoEConfig("tile_ragged", 777, 512, 256, 4, 1, "bf16"),
     MoEConfig("tile_fine", 900, 256, 128, 16, 4, "bf16"),
     MoEConfig("tile_split", 800, 1024, 512, 8, 2, "bf16"),   # down GEMM split along K
+    # about 550 rows per expert: two full 256-row token tiles and a short last one
+    MoEConfig("tile_multi", 1100, 256, 256, 4, 2, "bf16"),
 ]
 
-TILED = {"tile_small", "tile_ragged", "tile_fine", "tile_split"}
+TILED = {"tile_small", "tile_ragged", "tile_fine", "tile_split", "tile_multi"}
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
