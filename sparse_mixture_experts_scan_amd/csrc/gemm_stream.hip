@@ -7,8 +7,11 @@
 // for every permuted row r of expert e's segment.
 //
 // Shape of the work: with a handful of rows per expert the weights are read
-// exactly once and nothing is reused, so this form goes straight from HBM to
-// registers (no LDS staging of weights): the MFMA A operand is 16 weight rows
+// exactly once and nothing is reused.  Two kernels.  bf16 with K a multiple
+// of 128 (stream_dma_kernel, further down) stages each wave's weight runs
+// through LDS so that every load instruction fetches whole 256-byte pieces of
+// rows.  Otherwise (fp32, or K = 64 mod 128) stream_gemm_kernel goes
+// straight from HBM to registers: the MFMA A operand is 16 weight rows
 // (output features), the B operand 16 token rows, both K-contiguous, 16 bytes
 // per lane per raw buffer load (scalar resource, loop-invariant lane offsets,
 // the K advance in the scalar offset).  A workgroup owns FT output features
@@ -20,6 +23,8 @@
 //
 // Token rows past the expert's count (segment padding) read as zero, so the
 // padding rows of H are exactly zero and every row stored is in bounds.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -229,12 +234,194 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 form with the weights staged through LDS.  A wave's run is 128 k (256
+// bytes of each of the block's 32 weight rows); it is fetched by 8 LDS DMA
+// loads of 4 rows x 256 bytes each -- whole 256-byte pieces of a row per
+// load, which the memory system serves markedly faster than the 16 rows x 64
+// bytes of an MFMA-layout load -- into a per-wave slot where 16-byte chunk c
+// of row r sits at c ^ (r % 16); the MFMA fragments are then read from LDS
+// without bank conflicts.  Two slots (separate arrays, so that the compiler
+// can tell which DMA each read waits for) alternate: run i + 1 is in flight
+// while run i's MFMAs run.  Every step issues its loads unconditionally (past
+// the wave's last run it re-reads that run, from L2), so the waits before the
+// reads never depend on a branch.  Token rows as in the register form.
+// ---------------------------------------------------------------------------
+template <int BT, int FT, bool GATEUP>
+__device__ __forceinline__ void stream_dma_body(
+    const bf16_t* __restrict__ act, const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
+    void* __restrict__ outp, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_expert, int N, int K) {
+  constexpr int NW = GATEUP ? 2 : 1, NF = FT / 16, NT = BT / 16;
+  constexpr int NROW = NW * FT;                   // weight rows of the block
+  constexpr int kRunK = 128, kRunBytes = kRunK * 2;
+  constexpr int kSlot = NROW * kRunBytes;         // one wave's slot (8 KiB)
+  constexpr int kDma = kSlot / 1024;              // DMA loads per run
+  constexpr int NWAVE = kStreamThreads / kWave;
+  static_assert(NROW % 16 == 0 && FT % 4 == 0 && kDma * 4 == NROW, "block shape");
+  typedef __attribute__((address_space(3))) void lds_void;
+  __shared__ __attribute__((aligned(1024))) char sl0[NWAVE * kSlot];
+  __shared__ __attribute__((aligned(1024))) char sl1[NWAVE * kSlot];
+  __shared__ f32x4 red[NWAVE - 1][NW * NF * NT][kWave];
+
+  const int tile = blockIdx.y;
+  const int e = tile_expert[tile];
+  if (e < 0) return;
+  const int row0 = tile * BT;
+  const int f0 = blockIdx.x * FT;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lr = lane & 15, kg = lane >> 4;
+
+  const uint32_t row_bytes = (uint32_t)K * 2;
+  __amdgpu_buffer_rsrc_t rw[NW];
+  rw[0] = stream_rsrc(W0 + ((size_t)e * N + f0) * K, FT * row_bytes);
+  if constexpr (GATEUP) rw[1] = stream_rsrc(W1 + ((size_t)e * N + f0) * K, FT * row_bytes);
+  // DMA load j: block rows 4 j .. 4 j + 3; lane i fills row 4 j + i / 16,
+  // stored chunk i % 16 = global chunk (i % 16) ^ (row % 16)
+  uint32_t dvo[kDma];
+#pragma unroll
+  for (int j = 0; j < kDma; ++j) {
+    const int rr = 4 * j + lane / 16;
+    dvo[j] = (uint32_t)(rr % FT) * row_bytes + (uint32_t)(((lane & 15) ^ (rr & 15)) * 16);
+  }
+  // fragment (w, f) at k-step ks: row w * FT + f * 16 + lr, chunk ks * 4 + kg
+  uint32_t fro[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    fro[ks] = (uint32_t)wave * kSlot + (uint32_t)lr * kRunBytes + (uint32_t)(((ks * 4 + kg) ^ lr) * 16);
+  uint32_t ao[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) ao[n] = (uint32_t)(n * 16 + lr) * row_bytes + kg * 16;
+
+  f32x4 acc[NW][NF][NT];
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[w][f][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nrun = K / kRunK;
+  const int nb = nrun > wave ? (nrun - wave + NWAVE - 1) / NWAVE : 0;
+  const int valid_end = offsets[e] + counts[e];
+  const int nvalid = max(0, min(BT, valid_end - row0));
+  const __amdgpu_buffer_rsrc_t ra =
+      stream_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
+
+  uint4 t0[NT][4], t1[NT][4];
+  // run i of this wave (clamped to its last run)
+  auto issue = [&](char* slot, uint4 (&tk)[NT][4], int i) {
+    const int run = wave + NWAVE * min(i, nb - 1);
+    const uint32_t so = (uint32_t)run * kRunBytes;
+#pragma unroll
+    for (int j = 0; j < kDma; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[(4 * j) / FT],
+                                               (lds_void*)(slot + wave * kSlot + j * 1024), 16,
+                                               dvo[j], so, 0, 0);
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) tk[n][ks] = sload(ra, ao[n], so + ks * 64);
+  };
+  auto compute = [&](const char* slot, const uint4 (&tk)[NT][4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const uint4 wf = *reinterpret_cast<const uint4*>(slot + fro[ks] + (w * FT + f * 16) * kRunBytes);
+#pragma unroll
+          for (int n = 0; n < NT; ++n) acc[w][f][n] = Elem<bf16_t>::mfma16(wf, tk[n][ks], acc[w][f][n]);
+        }
+  };
+  // the scheduling barriers keep each run's loads (token rows included) where
+  // they are written, a full run ahead of their use; the LDS wait before a
+  // slot is refilled orders its last fragment reads before the DMA writes
+  if (nb > 0) {
+    issue(sl0, t0, 0);
+    for (int i = 0; i < nb; i += 2) {
+      issue(sl1, t1, i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(sl0, t0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+      issue(sl0, t0, i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < nb) compute(sl1, t1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): no DMA left in flight
+  }
+
+  // cross-wave reduction in fixed order 0,1,2,3
+  if (wave > 0) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) red[wave - 1][(w * NF + f) * NT + n][lane] = acc[w][f][n];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          f32x4 a = acc[w][f][n];
+#pragma unroll
+          for (int q = 0; q < NWAVE - 1; ++q) a += red[q][(w * NF + f) * NT + n][lane];
+          acc[w][f][n] = a;
+        }
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const size_t r = (size_t)(row0 + n * 16 + lr);
+        const int col = f0 + f * 16 + 4 * kg;
+        if constexpr (GATEUP) {
+          bf16_t* h = reinterpret_cast<bf16_t*>(outp) + r * N + col;
+          const f32x4 g = acc[0][f][n], u = acc[1][f][n];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) h[i] = Elem<bf16_t>::from_f32(silu_f32(g[i]) * u[i]);
+        } else {
+          float* y = reinterpret_cast<float*>(outp) + r * N + col;
+          *reinterpret_cast<float4*>(y) =
+              make_float4(acc[0][f][n][0], acc[0][f][n][1], acc[0][f][n][2], acc[0][f][n][3]);
+        }
+      }
+  }
+}
+
+template <int BT, int FT, bool GATEUP>
+__global__ __launch_bounds__(kStreamThreads) void stream_dma_kernel(
+    const bf16_t* __restrict__ act, const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
+    void* __restrict__ outp, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ num_tiles,
+    const int32_t* __restrict__ tile_expert, int N, int K) {
+  (void)num_tiles;
+  stream_dma_body<BT, FT, GATEUP>(act, W0, W1, outp, counts, offsets, tile_expert, N, K);
+}
+
 template <typename T, int BT>
 static void gateup_stream(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* h,
                           const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                           const int32_t* tile_expert, hipStream_t s) {
   constexpr int FT = MOE_STREAM_FT_GU;
   dim3 grid(D.f / FT, D.max_tiles);
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (D.d % 128 == 0) {
+      stream_dma_kernel<BT, FT, true><<<grid, kStreamThreads, 0, s>>>(
+          (const bf16_t*)xs, (const bf16_t*)Wg, (const bf16_t*)Wu, h, counts, offsets, num_tiles,
+          tile_expert, D.f, D.d);
+      return;
+    }
+  }
   stream_gemm_kernel<T, BT, FT, true, MOE_STREAM_U><<<grid, kStreamThreads, 0, s>>>(
       (const T*)xs, (const T*)Wg, (const T*)Wu, h, counts, offsets, num_tiles, tile_expert, D.f,
       D.d);
@@ -246,6 +433,14 @@ static void down_stream(const Dims& D, const void* h, const void* Wd, float* y,
                         const int32_t* tile_expert, hipStream_t s) {
   constexpr int FT = MOE_STREAM_FT_DN;
   dim3 grid(D.d / FT, D.max_tiles);
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (D.f % 128 == 0) {
+      stream_dma_kernel<BT, FT, false><<<grid, kStreamThreads, 0, s>>>(
+          (const bf16_t*)h, (const bf16_t*)Wd, nullptr, y, counts, offsets, num_tiles,
+          tile_expert, D.d, D.f);
+      return;
+    }
+  }
   stream_gemm_kernel<T, BT, FT, false, MOE_STREAM_U><<<grid, kStreamThreads, 0, s>>>(
       (const T*)h, (const T*)Wd, nullptr, y, counts, offsets, num_tiles, tile_expert, D.d, D.f);
 }
