@@ -46,6 +46,8 @@ def kernel_key(name: str) -> str:
     """Short role of a kernel from its demangled name."""
     if "stream_gemm_kernel" in name:
         return "gateup" if ", true," in name else "down"
+    if "stream_dma_kernel" in name:
+        return "gateup" if ", true>" in name else "down"
     if "tile_gemm_kernel" in name:
         return "gateup" if "<true>" in name else "down"
     if "stream_q4_kernel" in name:

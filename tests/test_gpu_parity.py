@@ -63,6 +63,11 @@ SMALL = [
     MoEConfig("one_expert", 40, 64, 64, 1, 1, "f32"),
     MoEConfig("ragged33", 33, 192, 320, 6, 3, "bf16"),
     MoEConfig("many_tiles", 1000, 128, 256, 8, 2, "bf16"),
+    # weight-streaming form with K a multiple of 512 (persistent blocks that
+    # each take several (token tile, feature tile) units, crossing tiles):
+    # 32-row token tiles, then 16-row ones
+    MoEConfig("stream_units32", 300, 512, 1024, 8, 2, "bf16"),
+    MoEConfig("stream_units16", 40, 512, 2048, 8, 2, "bf16"),
     # LDS-tiled variant (>= 96 rows per expert, bf16, d % 256, d_ff % 128)
     MoEConfig("tile_small", 1000, 256, 384, 8, 2, "bf16"),
     MoEConfig("tile_ragged", 777, 512, 256, 4, 1, "bf16"),
