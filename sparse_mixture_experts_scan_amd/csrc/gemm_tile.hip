@@ -53,10 +53,6 @@ constexpr int kTileBK = 64;           // K per LDS stage
 constexpr int kTileNS = 2;            // A buffers: the K loop runs stages in pairs
 constexpr int kKSteps = kTileBK / 16;               // 32x32x16 MFMA k-steps per stage
 constexpr int kXcds = 8;
-#ifndef MOE_TILE_FEAT_GROUP
-#define MOE_TILE_FEAT_GROUP 4
-#endif
-constexpr int kFeatGroup = MOE_TILE_FEAT_GROUP;  // feature tiles per XCD-local group
 
 constexpr int kRowBytes = kTileBK * 2;              // LDS bytes per tile row
 constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per row
@@ -242,7 +238,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
     void* __restrict__ outp, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ num_tiles,
     const int32_t* __restrict__ tile_expert, int N, int K, int n_ft, int n_tt, int per_xcd,
-    int parts, size_t part_stride) {
+    int parts, size_t part_stride, int fgroup) {
   // separate __shared__ arrays for the A buffers and the B ring, so that the
   // compiler can tell which DMA each LDS read depends on
   __shared__ __attribute__((aligned(1024))) char sa0[kOperBytes];
@@ -250,17 +246,17 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) char sbr[3 * kOperBytes];
   constexpr int FB = GATEUP ? kTileRows / 2 : kTileRows;  // output features per tile
 
-  // ---- tile id: XCD-contiguous remap, then groups of kFeatGroup feature tiles
+  // ---- tile id: XCD-contiguous remap, then groups of `fgroup` feature tiles
   const int L = blockIdx.x;
   int Lp = (L % kXcds) * per_xcd + L / kXcds;
   if (Lp >= parts * n_ft * n_tt) return;
   const int part = Lp / (n_ft * n_tt);      // K-split part (slowest)
   Lp -= part * n_ft * n_tt;
-  const int grp = Lp / (kFeatGroup * n_tt);
-  const int rem = Lp - grp * kFeatGroup * n_tt;
-  const int gsize = min(kFeatGroup, n_ft - grp * kFeatGroup);
+  const int grp = Lp / (fgroup * n_tt);
+  const int rem = Lp - grp * fgroup * n_tt;
+  const int gsize = min(fgroup, n_ft - grp * fgroup);
   const int tt = rem / gsize;
-  const int ft = grp * kFeatGroup + rem % gsize;
+  const int ft = grp * fgroup + rem % gsize;
   if (tt >= *num_tiles) return;             // past the token tiles in use
   const int e = tile_expert[tt];
   const int row0 = tt * kTileBT;
@@ -368,6 +364,19 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
   }
 }
 
+// Feature tiles per XCD-local group of the tile order.  Consecutive
+// workgroups of one XCD take the group's feature tiles for one token tile,
+// then the next token tile, so about 32 / fgroup token tiles share each
+// weight panel while they run.  Measured on MI355X: with about 1000 or more
+// rows per expert (4+ token tiles) groups of 4 are best for both GEMMs; with
+// about 500 (E = 64, top-8) groups of 3 for gate/up and 2 for down are 4% and
+// 13% faster than 4, while 1 and wider groups (8 to 28) are slower.
+static int tile_feat_group(const Dims& D, bool gateup) {
+  const int64_t rows_per_expert = (int64_t)D.T * D.k / D.E;
+  if (rows_per_expert >= 3 * kTileBT) return 4;
+  return gateup ? 3 : 2;
+}
+
 template <bool GATEUP>
 static void tile_launch(const Dims& D, const void* act, const void* W0, const void* W1,
                         void* out, const int32_t* counts, const int32_t* offsets,
@@ -383,7 +392,8 @@ static void tile_launch(const Dims& D, const void* act, const void* W0, const vo
   const int grid = per_xcd * kXcds;
   tile_gemm_kernel<GATEUP><<<grid, kTileThreads, 0, s>>>(
       (const bf16_t*)act, (const bf16_t*)W0, (const bf16_t*)W1, out, counts, offsets, num_tiles,
-      tile_expert, N, K, n_ft, n_tt, per_xcd, parts, (size_t)D.max_rows * N);
+      tile_expert, N, K, n_ft, n_tt, per_xcd, parts, (size_t)D.max_rows * N,
+      tile_feat_group(D, GATEUP));
 }
 
 bool tile_shape_ok(const Dims& D) {
