@@ -117,6 +117,11 @@ struct TileCtx {
   // plus a constant row offset: a few registers and immediate offsets serve
   // every read.
   uint32_t lbA, lbB;
+  // B waves: whether this wave's 64 token rows start before the tile's last
+  // valid row.  A wave whose rows are all past it issues no B at all (nobody
+  // reads those rows: their fragments are skipped), for the whole tile, so
+  // its waits on its own DMA pass at once.
+  bool b_on;
 };
 
 // One operand of stage ks's DMA into buffer `buf`: A (weights) from waves
@@ -129,7 +134,7 @@ __device__ __forceinline__ void tile_issue_half(const TileCtx& c, char* buf, int
     for (int j = 0; j < kDmaPerWave; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           c.rA, (lds_void*)(buf + (c.dma_base + j) * 1024), 16, c.voffA[j], so, 0, 0);
-  } else {
+  } else if (c.b_on) {
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -296,6 +301,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
   // token rows past the expert's count fall outside the resource: read as 0
   const int nvalid = max(0, min(kTileBT, valid_end - row0));
   c.rB = make_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
+  c.b_on = c.dma_base * (1024 / kRowBytes) < nvalid;
 
   // ---- fragment rows: A fragment a of wave half wf, token fragments at rows
   // wt * 32 and wt * 32 + kBStride of the tile
