@@ -34,16 +34,30 @@ void launch_rmsnorm(const Dims& D, const void* x, const float* weight, float eps
 // gamma, rs (both or neither): scores of the RMS-normalised tokens,
 // rs[t] * sum_j x[t][j] gamma[j] W[j][e]
 // logits_out: [T][E] final scores (with bias), or NULL.
+// outputs of the expert scan (a2, part 1); counts_out, prob_out, loss_out
+// may be NULL
+struct ScanArgs {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* num_tiles;
+  int32_t* tile_expert;
+  int32_t* row_token;
+  int32_t* counts_out;
+  float* prob_out;
+  float* loss_out;
+};
+// With a single router block the router's select pass also runs the expert
+// scan (launch_scan is then a no-op), which saves a launch for small T.
+bool router_fuses_scan(const Dims& D);
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
                    int32_t* idx, float* w, int32_t* blk_counts, float* part, float* blk_prob,
-                   const float* gamma, const float* rs, float* logits_out, hipStream_t s);
+                   const float* gamma, const float* rs, float* logits_out, const ScanArgs& sa,
+                   hipStream_t s);
 int router_splits_for(int nblk, int d);
 constexpr int kRouterPartStride = 64;  // floats per token row of the partial scores
 // a2: histogram reduce, padded offsets, per-block bases, tile table
 // router statistics (when blk_prob is non-NULL): prob_out [E], loss_out [1]
-void launch_scan(const Dims& D, int32_t* blk_counts, int32_t* counts, int32_t* offsets,
-                 int32_t* num_tiles, int32_t* tile_expert, int32_t* row_token,
-                 int32_t* counts_out, const float* blk_prob, float* prob_out, float* loss_out,
+void launch_scan(const Dims& D, int32_t* blk_counts, const ScanArgs& sa, const float* blk_prob,
                  hipStream_t s);
 // a2: stable row maps and gather of x into expert-contiguous rows
 void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int32_t* blk_base,

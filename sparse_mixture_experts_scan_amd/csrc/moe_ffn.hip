@@ -264,12 +264,13 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
     moe::launch_rmsnorm(D, x, norm_w, eps, rs, xn, s);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "rmsnorm launch");
   }
+  const moe::ScanArgs sa{counts,    offsets,   num_tiles,         tile_expert,
+                         row_token, o.expert_counts_out, o.router_prob_out, o.balance_loss_out};
   moe::launch_router(D, x, W_router, o.router_bias, idx, w, blk, rpart, bprob, norm_w, rs,
-                     nullptr, s);
+                     nullptr, sa, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess)
     return hip_fail(e, "router launch");
-  moe::launch_scan(D, blk, counts, offsets, num_tiles, tile_expert, row_token,
-                   o.expert_counts_out, bprob, o.router_prob_out, o.balance_loss_out, s);
+  moe::launch_scan(D, blk, sa, bprob, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess)
     return hip_fail(e, "scan launch");
   moe::launch_scatter(D, norm_w ? xn : x, idx, blk, offsets, tok_row, row_token, xs, s);
@@ -558,10 +559,11 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   // routing and permutation of the forward pass, the permuted upstream
   // gradient and the 128-row tile table
+  const moe::ScanArgs sa{counts, offsets, I(b.num_tiles), I(b.tile_expert), row_token,
+                         nullptr, nullptr, nullptr};
   moe::launch_router(D, x, W_router, o.router_bias, idx, w, I(b.block_counts),
-                     F(b.router_partial), nullptr, nullptr, nullptr, F(b.logits), s);
-  moe::launch_scan(D, I(b.block_counts), counts, offsets, I(b.num_tiles), I(b.tile_expert),
-                   row_token, nullptr, nullptr, nullptr, nullptr, s);
+                     F(b.router_partial), nullptr, nullptr, nullptr, F(b.logits), sa, s);
+  moe::launch_scan(D, I(b.block_counts), sa, nullptr, s);
   moe::launch_scatter(D, x, idx, I(b.block_counts), offsets, tok_row, row_token, xs, s);
   moe::launch_bwd_gather(D, dout, row_token, dp, s);
   moe::launch_bwd_tile_table(D, counts, offsets, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows,

@@ -290,8 +290,17 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
   }
 }
 
+__device__ __forceinline__ void expert_scan_block(
+    int32_t* __restrict__ blk, int nblk, int E, int Epow2, int BT, int max_rows, int max_tiles,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ num_tiles,
+    int32_t* __restrict__ tile_expert, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ counts_out, int nT, const float* __restrict__ blk_prob,
+    float* __restrict__ prob_out, float* __restrict__ loss_out);
+
 // Second pass of a split router: per token, the split partial scores are
 // added in split order (deterministic), the bias added, then top-k/softmax.
+// With a single router block (do_scan) the same block then runs the expert
+// scan (a2, part 1) on the counts it has just written, which saves a launch.
 constexpr int kSelectThreads = 256;
 constexpr int kMaxRouterSplits = 16;
 
@@ -299,7 +308,9 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int nT, int E, int k,
     int splits, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
     int32_t* __restrict__ blk_counts, float* __restrict__ blk_prob,
-    const float* __restrict__ rs, float* __restrict__ logits_out) {
+    const float* __restrict__ rs, float* __restrict__ logits_out, ScanArgs sa, int do_scan,
+    int Epow2, int BT, int max_rows, int max_tiles) {
+  static_assert(kSelectThreads == 256, "the fused expert scan runs on 256 threads");
   constexpr int TB = kRouterTokens;
   __shared__ float slog[TB][65];
   __shared__ int hist[64];
@@ -333,6 +344,12 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     __shared__ float smax[TB], sinv[TB];
     block_prob_sums(slog, t0, nT, E, smax, sinv, blk_prob + (size_t)blockIdx.x * E);
   }
+  if (do_scan) {
+    __syncthreads();
+    expert_scan_block(blk_counts, 1, E, Epow2, BT, max_rows, max_tiles, sa.counts, sa.offsets,
+                      sa.num_tiles, sa.tile_expert, sa.row_token, sa.counts_out, nT, blk_prob,
+                      sa.prob_out, sa.loss_out);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -341,7 +358,8 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
 // padded to BT rows (offsets = exclusive scan of padded counts); each token
 // tile gets its expert (or -1); padding rows of row_token are set to -1.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void expert_scan_kernel(
+// Run by all 256 threads of one block (contains barriers).
+__device__ __forceinline__ void expert_scan_block(
     int32_t* __restrict__ blk, int nblk, int E, int Epow2, int BT, int max_rows, int max_tiles,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ num_tiles,
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ row_token,
@@ -426,6 +444,15 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(
       *loss_out = (float)E * L;
     }
   }
+}
+
+__global__ __launch_bounds__(256) void expert_scan_kernel(ScanArgs a, int32_t* __restrict__ blk,
+                                                          int nblk, int E, int Epow2, int BT,
+                                                          int max_rows, int max_tiles, int nT,
+                                                          const float* __restrict__ blk_prob) {
+  expert_scan_block(blk, nblk, E, Epow2, BT, max_rows, max_tiles, a.counts, a.offsets,
+                    a.num_tiles, a.tile_expert, a.row_token, a.counts_out, nT, blk_prob,
+                    a.prob_out, a.loss_out);
 }
 
 // ---------------------------------------------------------------------------
@@ -551,9 +578,12 @@ void launch_rmsnorm(const Dims& D, const void* x, const float* weight, float eps
     rmsnorm_kernel<float><<<D.T, 256, 0, s>>>((const float*)x, weight, eps, D.d, rs, (float*)xn);
 }
 
+bool router_fuses_scan(const Dims& D) { return D.nblk == 1 && D.router_splits > 1; }
+
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
                    int32_t* idx, float* w, int32_t* blk_counts, float* part, float* blk_prob,
-                   const float* gamma, const float* rs, float* logits_out, hipStream_t s) {
+                   const float* gamma, const float* rs, float* logits_out, const ScanArgs& sa,
+                   hipStream_t s) {
   const dim3 grid(D.nblk, D.router_splits);
   if (D.bf16)
     router_topk_kernel<bf16_t><<<grid, kRouterMfmaThreads, 0, s>>>(
@@ -565,7 +595,8 @@ void launch_router(const Dims& D, const void* x, const float* Wr, const float* b
         blk_prob, gamma, rs, logits_out);
   if (D.router_splits > 1)
     router_select_kernel<<<D.nblk, kSelectThreads, 0, s>>>(
-        part, bias, D.T, D.E, D.k, D.router_splits, idx, w, blk_counts, blk_prob, rs, logits_out);
+        part, bias, D.T, D.E, D.k, D.router_splits, idx, w, blk_counts, blk_prob, rs, logits_out,
+        sa, router_fuses_scan(D) ? 1 : 0, D.Epow2, D.BT, D.max_rows, D.max_tiles);
 }
 
 int router_splits_for(int nblk, int d) {
@@ -577,13 +608,11 @@ int router_splits_for(int nblk, int d) {
   return sp;
 }
 
-void launch_scan(const Dims& D, int32_t* blk_counts, int32_t* counts, int32_t* offsets,
-                 int32_t* num_tiles, int32_t* tile_expert, int32_t* row_token,
-                 int32_t* counts_out, const float* blk_prob, float* prob_out, float* loss_out,
+void launch_scan(const Dims& D, int32_t* blk_counts, const ScanArgs& sa, const float* blk_prob,
                  hipStream_t s) {
-  expert_scan_kernel<<<1, 256, 0, s>>>(blk_counts, D.nblk, D.E, D.Epow2, D.BT, D.max_rows,
-                                       D.max_tiles, counts, offsets, num_tiles, tile_expert,
-                                       row_token, counts_out, D.T, blk_prob, prob_out, loss_out);
+  if (router_fuses_scan(D)) return;   // done by the router's select block
+  expert_scan_kernel<<<1, 256, 0, s>>>(sa, blk_counts, D.nblk, D.E, D.Epow2, D.BT, D.max_rows,
+                                       D.max_tiles, D.T, blk_prob);
 }
 
 void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int32_t* blk_base,
