@@ -22,6 +22,8 @@
 // permuted layout (a tile table: expert, first row, rows) with the expert's
 // weights as the other operand, or experts with the contraction running over
 // the expert's rows (weight gradients).  Fixed summation order throughout.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -291,11 +293,11 @@ __global__ __launch_bounds__(256) void bwd_gather_kernel(const bf16_t* __restric
   for (int c = threadIdx.x; c < d / 8; c += 256) out[c] = t < 0 ? make_uint4(0, 0, 0, 0) : in[c];
 }
 
-// Per permuted row: a, b (pre-activations, float32 from the recompute GEMMs),
-// Z = W2^T dOut_t.  dg[r] = <Z, h> (fixed-order block sum), dAB[r] = [g Z b
+// Per permuted row: a, b (pre-activations from the recompute GEMMs) and
+// Z = W2^T dOut_t, all bf16 (fp32 products rounded once).  dg[r] = <Z, h> (fixed-order block sum), dAB[r] = [g Z b
 // SiLU'(a) | g Z SiLU(a)] and Hg[r] = g h (bf16), zeros on padding rows.
 __global__ __launch_bounds__(256) void bwd_rows_kernel(
-    const float* __restrict__ AB, const float* __restrict__ Z, const int32_t* __restrict__ row_token,
+    const bf16_t* __restrict__ AB, const bf16_t* __restrict__ Z, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ tok_row, const float* __restrict__ gates, int f, int k,
     float* __restrict__ dg, bf16_t* __restrict__ dAB, bf16_t* __restrict__ Hg) {
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -305,29 +307,54 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
   if (t >= 0)
     for (int j = 0; j < k; ++j)
       if (tok_row[(size_t)t * k + j] == r) g = gates[(size_t)t * k + j];
-  const float* a_row = AB + (size_t)r * 2 * f;
-  const float* b_row = a_row + f;
-  const float* z_row = Z + (size_t)r * f;
+  const bf16_t* a_row = AB + (size_t)r * 2 * f;
+  const bf16_t* b_row = a_row + f;
+  const bf16_t* z_row = Z + (size_t)r * f;
   bf16_t* da_row = dAB + (size_t)r * 2 * f;
   bf16_t* db_row = da_row + f;
   bf16_t* hg_row = Hg + (size_t)r * f;
   float part = 0.f;
-  for (int c = tid; c < f; c += 256) {
-    float dav = 0.f, dbv = 0.f, hgv = 0.f;
+  // 8 consecutive columns per thread and step (f is a multiple of 64)
+  for (int c = tid * 8; c < f; c += 256 * 8) {
+    uint4 da = make_uint4(0, 0, 0, 0), db = da, hv = da;
     if (t >= 0) {
-      const float a = a_row[c], b = b_row[c], z = z_row[c];
-      const float sig = 1.0f / (1.0f + expf(-a));
-      const float s = a * sig;
-      const float h = s * b;
-      part = fmaf(z, h, part);
-      const float dh = g * z;
-      dav = dh * b * (sig * (1.0f + a * (1.0f - sig)));
-      dbv = dh * s;
-      hgv = g * h;
+      const uint4 av = *reinterpret_cast<const uint4*>(a_row + c);
+      const uint4 bv = *reinterpret_cast<const uint4*>(b_row + c);
+      const uint4 zv = *reinterpret_cast<const uint4*>(z_row + c);
+      const uint32_t* ap = &av.x;
+      const uint32_t* bp = &bv.x;
+      const uint32_t* zp = &zv.x;
+      uint32_t* dap = &da.x;
+      uint32_t* dbp = &db.x;
+      uint32_t* hp = &hv.x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t oa = 0, ob = 0, oh = 0;
+#pragma unroll
+        for (int hgh = 0; hgh < 2; ++hgh) {
+          const float a = __uint_as_float((ap[i] >> (16 * hgh)) << 16);
+          const float b = __uint_as_float((bp[i] >> (16 * hgh)) << 16);
+          const float z = __uint_as_float((zp[i] >> (16 * hgh)) << 16);
+          const float sig = 1.0f / (1.0f + expf(-a));
+          const float sv = a * sig;
+          const float h = sv * b;
+          part = fmaf(z, h, part);
+          const float dh = g * z;
+          const float dav = dh * b * (sig * (1.0f + a * (1.0f - sig)));
+          const float dbv = dh * sv;
+          const float hgv = g * h;
+          oa |= (uint32_t)Elem<bf16_t>::from_f32(dav) << (16 * hgh);
+          ob |= (uint32_t)Elem<bf16_t>::from_f32(dbv) << (16 * hgh);
+          oh |= (uint32_t)Elem<bf16_t>::from_f32(hgv) << (16 * hgh);
+        }
+        dap[i] = oa;
+        dbp[i] = ob;
+        hp[i] = oh;
+      }
     }
-    da_row[c] = Elem<bf16_t>::from_f32(dav);
-    db_row[c] = Elem<bf16_t>::from_f32(dbv);
-    hg_row[c] = Elem<bf16_t>::from_f32(hgv);
+    *reinterpret_cast<uint4*>(da_row + c) = da;
+    *reinterpret_cast<uint4*>(db_row + c) = db;
+    *reinterpret_cast<uint4*>(hg_row + c) = hv;
   }
   for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
   if ((tid & 63) == 0) wsum[tid >> 6] = part;
@@ -477,19 +504,26 @@ void launch_bwd_gather(const Dims& D, const void* src, const int32_t* row_token,
 }
 
 void launch_bwd_gemm_rows(const void* A, int lda, const void* B, int ldb, bool b_kcontig,
-                          size_t b_estride, float* C, int ldc, int M, int N, int K,
-                          bool accumulate, int max_tiles, const int32_t* tb_count,
+                          size_t b_estride, void* C, bool c_bf16, int ldc, int M, int N,
+                          int K, bool accumulate, int max_tiles, const int32_t* tb_count,
                           const int32_t* tb_exp, const int32_t* tb_row0, const int32_t* tb_rows,
                           hipStream_t s) {
   const dim3 grid((N + kGN - 1) / kGN, max_tiles);
-  if (b_kcontig)
-    grouped_gemm_kernel<true, true, 0, false><<<grid, kGT, 0, s>>>(
+  // bf16 output never accumulates
+  auto run = [&](auto kc, auto cb) {
+    grouped_gemm_kernel<true, decltype(kc)::value, 0, decltype(cb)::value><<<grid, kGT, 0, s>>>(
         (const bf16_t*)A, lda, (const bf16_t*)B, ldb, b_estride, C, ldc, 0, M, N, K,
-        accumulate, tb_count, tb_exp, tb_row0, tb_rows, nullptr, nullptr);
-  else
-    grouped_gemm_kernel<true, false, 0, false><<<grid, kGT, 0, s>>>(
-        (const bf16_t*)A, lda, (const bf16_t*)B, ldb, b_estride, C, ldc, 0, M, N, K,
-        accumulate, tb_count, tb_exp, tb_row0, tb_rows, nullptr, nullptr);
+        accumulate && !decltype(cb)::value, tb_count, tb_exp, tb_row0, tb_rows, nullptr, nullptr);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (b_kcontig) {
+    if (c_bf16) run(T_{}, T_{});
+    else run(T_{}, F_{});
+  } else {
+    if (c_bf16) run(F_{}, T_{});
+    else run(F_{}, F_{});
+  }
 }
 
 void launch_bwd_gemm_wgrad(const Dims& D, const void* A, int lda, const void* B, int ldb,
@@ -501,11 +535,12 @@ void launch_bwd_gemm_wgrad(const Dims& D, const void* A, int lda, const void* B,
       nullptr, nullptr, nullptr, nullptr, counts, offsets);
 }
 
-void launch_bwd_rows(const Dims& D, const float* AB, const float* Z, const int32_t* row_token,
+void launch_bwd_rows(const Dims& D, const void* AB, const void* Z, const int32_t* row_token,
                      const int32_t* tok_row, const float* gates, float* dg, void* dAB, void* Hg,
                      hipStream_t s) {
-  bwd_rows_kernel<<<D.max_rows, 256, 0, s>>>(AB, Z, row_token, tok_row, gates, D.f, D.k, dg,
-                                             (bf16_t*)dAB, (bf16_t*)Hg);
+  bwd_rows_kernel<<<D.max_rows, 256, 0, s>>>((const bf16_t*)AB, (const bf16_t*)Z, row_token,
+                                             tok_row, gates, D.f, D.k, dg, (bf16_t*)dAB,
+                                             (bf16_t*)Hg);
 }
 
 void launch_bwd_router(const Dims& D, const float* logits, const int32_t* idx, const float* gates,

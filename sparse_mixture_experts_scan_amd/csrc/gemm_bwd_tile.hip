@@ -408,9 +408,10 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
     Cb += (size_t)e * p.c_estride * (CBF16 ? 2 : 4);
     brow_base = bt_out * kBT;
   }
-  if constexpr (MODE == 1 && CBF16) {
-    // full tiles: stage each 128-row half of the bf16 tile in LDS (rows of
-    // kStagePitch bytes) and write whole rows with 16-byte stores
+  if constexpr (CBF16) {
+    // stage each 128-row half of the bf16 tile in LDS (rows of kStagePitch
+    // bytes) and write whole rows of the tile's valid rows with 16-byte
+    // stores
     constexpr int kStagePitch = kBT * 2 + 16;
     static_assert(128 * kStagePitch <= 3 * kBOper, "staging exceeds the B ring");
     __syncthreads();                      // every wave is past its last LDS read
@@ -434,16 +435,19 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
       for (int it = 0; it < 128 * (kBT * 2 / 16) / kBThreads; ++it) {
         const int q = it * kBThreads + tid;
         const int lrow = q / (kBT * 2 / 16), chunk = q % (kBT * 2 / 16);
-        const uint4 v = *reinterpret_cast<const uint4*>(sbr + lrow * kStagePitch + chunk * 16);
-        const size_t off = (size_t)(brow_base + b * kBStrideB + lrow) * p.ldc +
-                           (size_t)at * kBT + chunk * 8;
-        *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(Cb) + off) = v;
+        const int brow = b * kBStrideB + lrow;
+        if (brow < rows) {
+          const uint4 v =
+              *reinterpret_cast<const uint4*>(sbr + lrow * kStagePitch + chunk * 16);
+          const size_t off =
+              (size_t)(brow_base + brow) * p.ldc + (size_t)at * kBT + chunk * 8;
+          *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(Cb) + off) = v;
+        }
       }
       __syncthreads();
     }
     return;
-  }
-  if constexpr (!CBF16) {
+  } else {
     // fp32: stage (token fragment b, column half ch) = 128 rows x 128 columns
     // at a time in LDS, written by the waves of that half, then store whole
     // 512-byte row pieces of the tile's valid rows
@@ -482,31 +486,6 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
         }
         __syncthreads();
       }
-    return;
-  }
-#pragma unroll
-  for (int b = 0; b < kBFragB; ++b) {
-    const int brow = wt * 32 + b * kBStrideB + r32;
-    if (brow >= rows) continue;
-    const size_t rowoff = (size_t)(brow_base + brow) * p.ldc + (size_t)at * kBT;
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int aidx = wf * 128 + a * 32 + jj * 8 + half * 4;
-        const f32x16& v = acc[a][b];
-        if constexpr (CBF16) {
-          const uint32_t lo = (uint32_t)Elem<bf16_t>::from_f32(v[jj * 4]) |
-                              ((uint32_t)Elem<bf16_t>::from_f32(v[jj * 4 + 1]) << 16);
-          const uint32_t hi = (uint32_t)Elem<bf16_t>::from_f32(v[jj * 4 + 2]) |
-                              ((uint32_t)Elem<bf16_t>::from_f32(v[jj * 4 + 3]) << 16);
-          *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(Cb) + rowoff + aidx) =
-              make_uint2(lo, hi);
-        } else {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(Cb) + rowoff + aidx) =
-              make_float4(v[jj * 4], v[jj * 4 + 1], v[jj * 4 + 2], v[jj * 4 + 3]);
-        }
-      }
   }
 }
 
@@ -540,7 +519,7 @@ bool bwd_tile_shape_ok(int64_t d, int64_t f) { return d % kBT == 0 && f % kBT ==
 int bwd_tile_rows() { return kBT; }
 
 // a | b = [W1 | W3] x_r: one launch, aidx over 2 d_ff (W1's tiles, then W3's)
-void launch_bwd_recompute(const Dims& D, const void* xs, const void* Wg, const void* Wu, float* ab,
+void launch_bwd_recompute(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* ab,
                           int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
                           const int32_t* tb_row0, const int32_t* tb_rows, hipStream_t s) {
   BgArgs p = bg_rows_args(tb_count, tb_exp, tb_row0, tb_rows, max_tiles);
@@ -555,11 +534,11 @@ void launch_bwd_recompute(const Dims& D, const void* xs, const void* Wg, const v
   p.ldc = 2 * D.f;
   p.K = D.d;
   p.n_at = 2 * D.f / kBT;
-  bg_launch<false, false, 0, false>(p, 1, s);
+  bg_launch<false, false, 0, true>(p, 1, s);
 }
 
 // Z = W2^T dOut_r: A = W2 read down its columns (index f, k = d)
-void launch_bwd_z(const Dims& D, const void* dp, const void* Wd, float* z, int max_tiles,
+void launch_bwd_z(const Dims& D, const void* dp, const void* Wd, void* z, int max_tiles,
                   const int32_t* tb_count, const int32_t* tb_exp, const int32_t* tb_row0,
                   const int32_t* tb_rows, hipStream_t s) {
   BgArgs p = bg_rows_args(tb_count, tb_exp, tb_row0, tb_rows, max_tiles);
@@ -573,7 +552,7 @@ void launch_bwd_z(const Dims& D, const void* dp, const void* Wd, float* z, int m
   p.ldc = D.f;
   p.K = D.d;
   p.n_at = D.f / kBT;
-  bg_launch<true, false, 0, false>(p, 1, s);
+  bg_launch<true, false, 0, true>(p, 1, s);
 }
 
 // dX_r = W1^T dA + W3^T dB: A = [W1; W3] down its columns (index d, k = 2 d_ff)

@@ -105,8 +105,8 @@ void launch_bwd_gather(const Dims& D, const void* src, const int32_t* row_token,
                        hipStream_t s);
 // C[rows of tile][N] (+)= A[rows][K] (k contiguous) x B_e, per tile of the table
 void launch_bwd_gemm_rows(const void* A, int lda, const void* B, int ldb, bool b_kcontig,
-                          size_t b_estride, float* C, int ldc, int M, int N, int K,
-                          bool accumulate, int max_tiles, const int32_t* tb_count,
+                          size_t b_estride, void* C, bool c_bf16, int ldc, int M, int N,
+                          int K, bool accumulate, int max_tiles, const int32_t* tb_count,
                           const int32_t* tb_exp, const int32_t* tb_row0, const int32_t* tb_rows,
                           hipStream_t s);
 // C_e[M][N] = sum over expert e's rows r of A[r][m] B[r][n] (bf16 out)
@@ -114,10 +114,10 @@ void launch_bwd_gemm_rows(const void* A, int lda, const void* B, int ldb, bool b
 // one launch each for a | b, Z, dX (both terms), dW2, and dW1 | dW3.
 bool bwd_tile_shape_ok(int64_t d, int64_t f);
 int bwd_tile_rows();
-void launch_bwd_recompute(const Dims& D, const void* xs, const void* Wg, const void* Wu, float* ab,
+void launch_bwd_recompute(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* ab,
                           int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
                           const int32_t* tb_row0, const int32_t* tb_rows, hipStream_t s);
-void launch_bwd_z(const Dims& D, const void* dp, const void* Wd, float* z, int max_tiles,
+void launch_bwd_z(const Dims& D, const void* dp, const void* Wd, void* z, int max_tiles,
                   const int32_t* tb_count, const int32_t* tb_exp, const int32_t* tb_row0,
                   const int32_t* tb_rows, hipStream_t s);
 void launch_bwd_dxs(const Dims& D, const void* dab, const void* Wg, const void* Wu, float* dxs,
@@ -131,7 +131,7 @@ void launch_bwd_wgrad_gate_up(const Dims& D, const void* dab, const void* xs, vo
 void launch_bwd_gemm_wgrad(const Dims& D, const void* A, int lda, const void* B, int ldb,
                            void* C, int M, int N, const int32_t* counts, const int32_t* offsets,
                            hipStream_t s);
-void launch_bwd_rows(const Dims& D, const float* AB, const float* Z, const int32_t* row_token,
+void launch_bwd_rows(const Dims& D, const void* AB, const void* Z, const int32_t* row_token,
                      const int32_t* tok_row, const float* gates, float* dg, void* dAB, void* Hg,
                      hipStream_t s);
 void launch_bwd_router(const Dims& D, const float* logits, const int32_t* idx, const float* gates,

@@ -447,8 +447,8 @@ int make_bwd_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, BwdPlan
   b->router_partial = take(D.router_splits > 1 ? sizeof(float) * D.router_splits * D.nblk *
                                                      moe::kRouterTokens * moe::kRouterPartStride
                                                : 0);
-  b->ab = take(4 * R * 2 * f);
-  b->z = take(4 * R * f);
+  b->ab = take(2 * R * 2 * f);   // bf16 a | b
+  b->z = take(2 * R * f);        // bf16 Z
   b->dab = take(2 * R * 2 * f);
   b->hg = take(2 * R * f);
   b->dp = take(2 * R * d);
@@ -540,8 +540,8 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   char* dp = ws + b.dp;
   char* dab = ws + b.dab;
   char* hg = ws + b.hg;
-  float* ab = F(b.ab);
-  float* z = F(b.z);
+  moe::bf16_t* ab = reinterpret_cast<moe::bf16_t*>(ws + b.ab);
+  moe::bf16_t* z = reinterpret_cast<moe::bf16_t*>(ws + b.z);
   float* dxs = F(b.dxs);
   float* dg = F(b.dg);
   float* ds = F(b.ds);
@@ -576,18 +576,18 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
     moe::launch_bwd_recompute(D, xs, W_gate, W_up, ab, b.max_tiles, tb_count, tb_exp, tb_row0,
                               tb_rows, s);
   } else {
-    moe::launch_bwd_gemm_rows(xs, d, W_gate, d, true, wstride, ab, 2 * f, D.max_rows, f, d,
-                              false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
-    moe::launch_bwd_gemm_rows(xs, d, W_up, d, true, wstride, ab + f, 2 * f, D.max_rows, f, d,
-                              false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+    moe::launch_bwd_gemm_rows(xs, d, W_gate, d, true, wstride, ab, true, 2 * f, D.max_rows, f,
+                              d, false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+    moe::launch_bwd_gemm_rows(xs, d, W_up, d, true, wstride, ab + f, true, 2 * f, D.max_rows, f,
+                              d, false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
   }
   if ((st = check(2, "recompute launch")) != MOE_OK) return st;
   // Z = W2^T dOut_t per routed row
   if (tiled)
     moe::launch_bwd_z(D, dp, W_down, z, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
   else
-    moe::launch_bwd_gemm_rows(dp, d, W_down, f, false, wstride, z, f, D.max_rows, f, d, false,
-                              b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+    moe::launch_bwd_gemm_rows(dp, d, W_down, f, false, wstride, z, true, f, D.max_rows, f, d,
+                              false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
   if ((st = check(3, "Z launch")) != MOE_OK) return st;
   // dg, dA, dB, g h; the router scores' gradient; the router weight gradient
   moe::launch_bwd_rows(D, ab, z, row_token, tok_row, w, dg, dab, hg, s);
@@ -599,9 +599,9 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
     moe::launch_bwd_dxs(D, dab, W_gate, W_up, dxs, b.max_tiles, tb_count, tb_exp, tb_row0,
                         tb_rows, s);
   } else {
-    moe::launch_bwd_gemm_rows(dab, 2 * f, W_gate, d, false, wstride, dxs, d, D.max_rows, d, f,
-                              false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
-    moe::launch_bwd_gemm_rows(dab + 2 * (size_t)f, 2 * f, W_up, d, false, wstride, dxs, d,
+    moe::launch_bwd_gemm_rows(dab, 2 * f, W_gate, d, false, wstride, dxs, false, d, D.max_rows,
+                              d, f, false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+    moe::launch_bwd_gemm_rows(dab + 2 * (size_t)f, 2 * f, W_up, d, false, wstride, dxs, false, d,
                               D.max_rows, d, f, true, b.max_tiles, tb_count, tb_exp, tb_row0,
                               tb_rows, s);
   }
