@@ -242,8 +242,9 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gemm_kernel(
 
 // ---------------------------------------------------------------------------
 // bf16 form with the weights staged through LDS.  A wave's run is 128 k (256
-// bytes of each of the block's 32 weight rows); it is fetched by 8 LDS DMA
-// loads of 4 rows x 256 bytes each -- whole 256-byte pieces of a row per
+// bytes of each of the block's weight rows: 32 for gate/up, 16 gate + 16 up,
+// and 16 for down); it is fetched by LDS DMA loads of 4 rows x 256 bytes
+// each -- whole 256-byte pieces of a row per
 // load, which the memory system serves markedly faster than the 16 rows x 64
 // bytes of an MFMA-layout load -- into a per-wave slot where 16-byte chunk c
 // of row r sits at c ^ (r % 16); the MFMA fragments are then read from LDS
