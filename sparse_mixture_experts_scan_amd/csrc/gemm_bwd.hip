@@ -450,7 +450,7 @@ __global__ __launch_bounds__(256) void bwd_router_wgrad_reduce(const float* __re
 
 // dx_t = sum_j dX[tok_row[t][j]] (slot order) + sum_e W_router[.][e] ds_t[e]
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dX,
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dX, size_t plane,
                                                      const int32_t* __restrict__ tok_row,
                                                      const float* __restrict__ Wr,
                                                      const float* __restrict__ ds, int d, int E,
@@ -461,7 +461,10 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
   __syncthreads();
   for (int c = threadIdx.x; c < d; c += 256) {
     float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc += dX[(size_t)tok_row[(size_t)t * k + j] * d + c];
+    for (int j = 0; j < k; ++j) {
+      const size_t o = (size_t)tok_row[(size_t)t * k + j] * d + c;
+      acc += dX[o] + dX[plane + o];
+    }
     float rt = 0.f;
     for (int e = 0; e < E; ++e) rt = fmaf(Wr[(size_t)c * E + e], sds[e], rt);
     dx[(size_t)t * d + c] = Elem<T>::from_f32(acc + rt);
@@ -561,9 +564,10 @@ void launch_bwd_router_wgrad(const Dims& D, const void* x, const float* ds, floa
                                                                        dWr, dbias);
 }
 
-void launch_bwd_dx(const Dims& D, const float* dX, const int32_t* tok_row, const float* Wr,
-                   const float* ds, void* dx, hipStream_t s) {
-  bwd_dx_kernel<bf16_t><<<D.T, 256, 0, s>>>(dX, tok_row, Wr, ds, D.d, D.E, D.k, (bf16_t*)dx);
+void launch_bwd_dx(const Dims& D, const float* dX, size_t plane, const int32_t* tok_row,
+                   const float* Wr, const float* ds, void* dx, hipStream_t s) {
+  bwd_dx_kernel<bf16_t><<<D.T, 256, 0, s>>>(dX, plane, tok_row, Wr, ds, D.d, D.E, D.k,
+                                            (bf16_t*)dx);
 }
 
 }  // namespace moe

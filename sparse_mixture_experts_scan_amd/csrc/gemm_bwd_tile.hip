@@ -115,6 +115,11 @@ struct BgArgs {
   const int32_t* tb_rows;
   const int32_t* counts;
   const int32_t* offsets;
+  // mode 0: K split into `kparts` (1 or 2) equal parts, the slowest tile
+  // dimension.  Part 1 takes A from A1, B from column K of its rows, and
+  // writes the C plane c_pstride elements after C0.
+  int kparts;
+  size_t c_pstride;
 };
 
 namespace {
@@ -279,10 +284,13 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
   const int L = blockIdx.x;
   int Lp = (L % kBXcds) * p.per_xcd + L / kBXcds;
   if (Lp >= p.total) return;
-  int e = 0;
+  int e = 0, part = 0;
   if constexpr (MODE == 1) {
     e = Lp / (p.n_at * p.n_bt);
     Lp -= e * p.n_at * p.n_bt;
+  } else {
+    part = Lp / (p.n_at * p.n_bt);
+    Lp -= part * p.n_at * p.n_bt;
   }
   const int grp = Lp / (kBFeatGroup * p.n_bt);
   const int rem = Lp - grp * kBFeatGroup * p.n_bt;
@@ -312,7 +320,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
   // ---- the operand this wave fetches
   if (g == 0) {
     // A: aidx tile `at`
-    const bf16_t* Am = p.A0;
+    const bf16_t* Am = part == 0 ? p.A0 : p.A1;
     int a_tile = at;
     if (at >= p.a_split_tile) { Am = p.A1; a_tile = at - p.a_split_tile; }
     c.ld_bytes = (uint32_t)p.lda * 2;
@@ -335,7 +343,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
     c.ld_bytes = (uint32_t)p.ldb * 2;
     if constexpr (MODE == 0) {
       // token rows row0 .. + rows (k contiguous); past them zeros
-      c.r = b_rsrc(p.B + (size_t)row0 * p.ldb, (uint32_t)rows * c.ld_bytes);
+      c.r = b_rsrc(p.B + (size_t)row0 * p.ldb + (size_t)part * p.K,
+                   (uint32_t)rows * c.ld_bytes);
     } else {
       c.ks_base = reinterpret_cast<const char*>(p.B + (size_t)p.offsets[e] * p.ldb +
                                                 (size_t)bt * kBT);
@@ -399,7 +408,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
   char* Cb;
   int brow_base;
   if constexpr (MODE == 0) {
-    Cb = reinterpret_cast<char*>(p.C0);
+    Cb = reinterpret_cast<char*>(p.C0) + (size_t)part * p.c_pstride * (CBF16 ? 2 : 4);
     brow_base = row0;
   } else {
     int bt_out = bt;
@@ -510,6 +519,7 @@ BgArgs bg_rows_args(const int32_t* tb_count, const int32_t* tb_exp, const int32_
   p.a_split_tile = 1 << 30;
   p.a_split_k = 1 << 30;
   p.c_split_tile = 1 << 30;
+  p.kparts = 1;
   return p;
 }
 
@@ -557,21 +567,25 @@ void launch_bwd_z(const Dims& D, const void* dp, const void* Wd, void* z, int ma
 
 // dX_r = W1^T dA + W3^T dB: A = [W1; W3] down its columns (index d, k = 2 d_ff)
 void launch_bwd_dxs(const Dims& D, const void* dab, const void* Wg, const void* Wu, float* dxs,
-                    int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
+                    size_t plane, int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
                     const int32_t* tb_row0, const int32_t* tb_rows, hipStream_t s) {
+  // two K parts (the d_ff of W1, then that of W3), one plane each: twice the
+  // workgroups of one K = 2 d_ff pass, which on prefill fill 4.5 rounds of
+  // the CUs instead of 2.25
   BgArgs p = bg_rows_args(tb_count, tb_exp, tb_row0, tb_rows, max_tiles);
   p.A0 = (const bf16_t*)Wg;
   p.A1 = (const bf16_t*)Wu;
   p.a_estride = (size_t)D.f * D.d;
   p.lda = D.d;
-  p.a_split_k = D.f;
   p.B = (const bf16_t*)dab;
   p.ldb = 2 * D.f;
   p.C0 = dxs;
   p.ldc = D.d;
-  p.K = 2 * D.f;
+  p.K = D.f;
   p.n_at = D.d / kBT;
-  bg_launch<true, false, 0, false>(p, 1, s);
+  p.kparts = 2;
+  p.c_pstride = plane;
+  bg_launch<true, false, 0, false>(p, 2, s);
 }
 
 // dW2[e] = Hg^T dOut over the expert's rows: C[o][f], A = Hg (index f),

@@ -121,7 +121,7 @@ void launch_bwd_z(const Dims& D, const void* dp, const void* Wd, void* z, int ma
                   const int32_t* tb_count, const int32_t* tb_exp, const int32_t* tb_row0,
                   const int32_t* tb_rows, hipStream_t s);
 void launch_bwd_dxs(const Dims& D, const void* dab, const void* Wg, const void* Wu, float* dxs,
-                    int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
+                    size_t plane, int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
                     const int32_t* tb_row0, const int32_t* tb_rows, hipStream_t s);
 void launch_bwd_wgrad_down(const Dims& D, const void* dp, const void* hg, void* dWd,
                            const int32_t* counts, const int32_t* offsets, hipStream_t s);
@@ -139,8 +139,10 @@ void launch_bwd_router(const Dims& D, const float* logits, const int32_t* idx, c
                        float alpha, float* ds, hipStream_t s);
 void launch_bwd_router_wgrad(const Dims& D, const void* x, const float* ds, float* part,
                              float* dWr, float* dbias, hipStream_t s);
-void launch_bwd_dx(const Dims& D, const float* dX, const int32_t* tok_row, const float* Wr,
-                   const float* ds, void* dx, hipStream_t s);
+// dX holds two planes (the W1 and W3 halves of the contraction), `plane`
+// elements apart
+void launch_bwd_dx(const Dims& D, const float* dX, size_t plane, const int32_t* tok_row,
+                   const float* Wr, const float* ds, void* dx, hipStream_t s);
 void launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 // a5: gate-weighted gather-sum back to token order
 // resid: x for the block wrapper (out = x + layer), or NULL

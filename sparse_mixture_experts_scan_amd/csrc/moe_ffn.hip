@@ -452,7 +452,7 @@ int make_bwd_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, BwdPlan
   b->dab = take(2 * R * 2 * f);
   b->hg = take(2 * R * f);
   b->dp = take(2 * R * d);
-  b->dxs = take(4 * R * d);
+  b->dxs = take(4 * 2 * R * d);   // two planes: the W1 and W3 halves of dX
   b->dg = take(4 * R);
   b->ds = take(4 * (size_t)T * E);
   b->wpart = take(4 * (size_t)moe::bwd_router_slices() * (d + 1) * E);
@@ -543,6 +543,7 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   moe::bf16_t* ab = reinterpret_cast<moe::bf16_t*>(ws + b.ab);
   moe::bf16_t* z = reinterpret_cast<moe::bf16_t*>(ws + b.z);
   float* dxs = F(b.dxs);
+  const size_t dx_plane = (size_t)D.max_rows * d;   // dxs: [2][max_rows][d]
   float* dg = F(b.dg);
   float* ds = F(b.ds);
   const size_t wstride = (size_t)d * f;   // elements per expert matrix
@@ -596,17 +597,17 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   if ((st = check(4, "row/router backward launch")) != MOE_OK) return st;
   // dX_r = W1^T dA + W3^T dB
   if (tiled) {
-    moe::launch_bwd_dxs(D, dab, W_gate, W_up, dxs, b.max_tiles, tb_count, tb_exp, tb_row0,
-                        tb_rows, s);
+    moe::launch_bwd_dxs(D, dab, W_gate, W_up, dxs, dx_plane, b.max_tiles, tb_count, tb_exp,
+                        tb_row0, tb_rows, s);
   } else {
     moe::launch_bwd_gemm_rows(dab, 2 * f, W_gate, d, false, wstride, dxs, false, d, D.max_rows,
                               d, f, false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
-    moe::launch_bwd_gemm_rows(dab + 2 * (size_t)f, 2 * f, W_up, d, false, wstride, dxs, false, d,
-                              D.max_rows, d, f, true, b.max_tiles, tb_count, tb_exp, tb_row0,
-                              tb_rows, s);
+    moe::launch_bwd_gemm_rows(dab + 2 * (size_t)f, 2 * f, W_up, d, false, wstride,
+                              dxs + dx_plane, false, d, D.max_rows, d, f, false, b.max_tiles,
+                              tb_count, tb_exp, tb_row0, tb_rows, s);
   }
   if ((st = check(5, "dX launch")) != MOE_OK) return st;
-  moe::launch_bwd_dx(D, dxs, tok_row, W_router, ds, dx, s);
+  moe::launch_bwd_dx(D, dxs, dx_plane, tok_row, W_router, ds, dx, s);
   if ((st = check(6, "dx launch")) != MOE_OK) return st;
   // weight gradients over each expert's rows
   if (tiled)
