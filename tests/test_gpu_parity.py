@@ -58,6 +58,8 @@ SMALL = [
     MoEConfig("small_f32", 300, 256, 512, 8, 2, "f32"),
     MoEConfig("small_fine", 200, 128, 192, 64, 8, "bf16"),
     MoEConfig("single_token", 1, 128, 256, 8, 2, "bf16"),
+    # one router block with 64 experts, top-8: the select pass runs the scan
+    MoEConfig("decode_fine", 20, 256, 256, 64, 8, "bf16"),
     MoEConfig("top1", 77, 128, 256, 8, 1, "bf16"),
     MoEConfig("k_equals_E", 50, 128, 128, 4, 4, "f32"),
     MoEConfig("one_expert", 40, 64, 64, 1, 1, "f32"),
