@@ -137,6 +137,10 @@ struct BCtx {
   int dma_base;
   uint32_t lA[4];             // A fragment bases (KC: lA[0], lA[1] used)
   uint32_t lB;                // B fragment base
+  // KC operand: false when all of this wave's 64 rows lie past the tile's
+  // valid rows (token rows of a short tile); the wave then issues no DMA for
+  // the tile, nobody reads those rows, and its waits pass at once
+  bool on;
 };
 
 // One operand's DMA for stage s into `buf` (this wave's 8 slots).
@@ -155,7 +159,7 @@ __device__ __forceinline__ void b_issue(const BCtx& c, char* buf, int s) {
     for (int j = 0; j < kBSlots; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(buf + (c.dma_base + j) * 1024), 16,
                                                c.voff[j], 0, 0, 0);
-  } else {
+  } else if (c.on) {
 #pragma unroll
     for (int j = 0; j < kBSlots; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.r, (lds_void*)(buf + (c.dma_base + j) * 1024),
@@ -366,6 +370,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
       c.voff[j] = (uint32_t)kr * c.ld_bytes + (uint32_t)((cs ^ ((kr & 3) << 2)) * 16);
     }
   }
+  // a KC slot holds 8 rows; only the token rows of mode 0 can run short
+  c.on = g == 0 || MODE != 0 || KSB || c.dma_base * 8 < rows;
   // fragment bases
   {
     const int r32 = lane & 31, h = lane >> 5;
