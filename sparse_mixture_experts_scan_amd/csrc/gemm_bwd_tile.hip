@@ -209,17 +209,22 @@ __device__ __forceinline__ void b_mfma_stage(const uint4 (&fa)[kBKSteps][4],
       for (int a = 0; a < 4; ++a) acc[a][b] = b_mfma(fa[kk][a], fb[kk][b], acc[a][b]);
 }
 
-// One stage s (as the forward): waves 0-3 send A of s + 1 to `anxt`, waves
-// 4-7 send B of s + 2 to `bnew` after their reads; XWAIT after the reads,
-// then everything of this wave's DMA after the MFMAs.
-template <bool KSA, bool KSB, int NBV, bool ISSUE_A, bool ISSUE_B, int XWAIT>
-__device__ __forceinline__ void b_stage(const BCtx& c, char* acur, char* anxt, const char* bcur,
-                                        char* bnew, int s, int g, uint4 (&fa)[kBKSteps][4],
+// One stage s (as the forward): waves 0-3 send the pair operand of s + 1 to
+// `pnxt`, waves 4-7 the ring operand of s + 2 to `rnew` after their reads;
+// XWAIT after the reads, then everything of this wave's DMA after the MFMAs.
+// The pair operand is A and the ring operand B, or the other way round with
+// SWAP (what waves 4-7 send is read one phase later, so the deeper ring goes
+// to whichever operand waits longer on memory; chosen per GEMM by
+// measurement).
+template <bool KSA, bool KSB, bool SWAP, int NBV, bool ISSUE_P, bool ISSUE_R, int XWAIT>
+__device__ __forceinline__ void b_stage(const BCtx& c, char* pcur, char* pnxt, const char* rcur,
+                                        char* rnew, int s, int g, uint4 (&fa)[kBKSteps][4],
                                         uint4 (&fb)[kBKSteps][kBFragB],
                                         f32x16 (&acc)[4][kBFragB]) {
-  if (ISSUE_A && g == 0) b_issue<KSA>(c, anxt, s + 1);
-  b_load<KSA, KSB, NBV>(c, acur, bcur, fa, fb);
-  if (ISSUE_B && g == 1) b_issue<KSB>(c, bnew, s + 2);
+  if (ISSUE_P && g == 0) b_issue<SWAP ? KSB : KSA>(c, pnxt, s + 1);
+  if constexpr (SWAP) b_load<KSA, KSB, NBV>(c, rcur, pcur, fa, fb);
+  else b_load<KSA, KSB, NBV>(c, pcur, rcur, fa, fb);
+  if (ISSUE_R && g == 1) b_issue<SWAP ? KSA : KSB>(c, rnew, s + 2);
   b_wait_vmcnt<XWAIT>();
   b_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -230,17 +235,17 @@ __device__ __forceinline__ void b_stage(const BCtx& c, char* acur, char* anxt, c
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// nk stages (a positive even number); A of stage s in a0/a1 by s % 2, B in
-// bring[s % 3].
-template <bool KSA, bool KSB, int NBV>
+// nk stages (a positive even number); the pair operand of stage s in a0/a1
+// by s % 2, the ring operand in bring[s % 3].
+template <bool KSA, bool KSB, bool SWAP, int NBV>
 __device__ __forceinline__ void b_main_loop(const BCtx& c, char* a0, char* a1, char* bring,
                                             int nk, int g, f32x16 (&acc)[4][kBFragB]) {
   uint4 fa[kBKSteps][4], fb[kBKSteps][kBFragB];
   if (g == 0) {
-    b_issue<KSA>(c, a0, 0);
+    b_issue<SWAP ? KSB : KSA>(c, a0, 0);
   } else {
-    b_issue<KSB>(c, bring, 0);
-    b_issue<KSB>(c, bring + kBOper, 1);
+    b_issue<SWAP ? KSA : KSB>(c, bring, 0);
+    b_issue<SWAP ? KSA : KSB>(c, bring + kBOper, 1);
   }
   b_wait_vmcnt<0>();
   b_barrier();
@@ -252,14 +257,15 @@ __device__ __forceinline__ void b_main_loop(const BCtx& c, char* a0, char* a1, c
   int s = 0;
   for (; s < nk - 2; s += 2) {
     const int b1 = inc3(bs), b2 = inc3(b1), b3 = inc3(b2);
-    b_stage<KSA, KSB, NBV, true, true, kBSlots>(c, a0, a1, bb(bs), bb(b2), s, g, fa, fb, acc);
-    b_stage<KSA, KSB, NBV, true, true, kBSlots>(c, a1, a0, bb(b1), bb(b3), s + 1, g, fa, fb,
-                                                acc);
+    b_stage<KSA, KSB, SWAP, NBV, true, true, kBSlots>(c, a0, a1, bb(bs), bb(b2), s, g, fa, fb,
+                                                      acc);
+    b_stage<KSA, KSB, SWAP, NBV, true, true, kBSlots>(c, a1, a0, bb(b1), bb(b3), s + 1, g, fa,
+                                                      fb, acc);
     bs = b2;
   }
-  b_stage<KSA, KSB, NBV, true, false, 0>(c, a0, a1, bb(bs), nullptr, s, g, fa, fb, acc);
-  b_stage<KSA, KSB, NBV, false, false, 0>(c, a1, a0, bb(inc3(bs)), nullptr, s + 1, g, fa, fb,
-                                          acc);
+  b_stage<KSA, KSB, SWAP, NBV, true, false, 0>(c, a0, a1, bb(bs), nullptr, s, g, fa, fb, acc);
+  b_stage<KSA, KSB, SWAP, NBV, false, false, 0>(c, a1, a0, bb(inc3(bs)), nullptr, s + 1, g, fa,
+                                                fb, acc);
   if (g == 0) b_barrier();
 }
 
@@ -278,7 +284,7 @@ __device__ inline uint32_t ks_lane_base(int lane, int q) {
 
 }  // namespace
 
-template <bool KSA, bool KSB, int MODE, bool CBF16>
+template <bool KSA, bool KSB, int MODE, bool CBF16, bool SWAP>
 __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
   __shared__ __attribute__((aligned(1024))) char sa0[kBOper];
   __shared__ __attribute__((aligned(1024))) char sa1[kBOper];
@@ -322,7 +328,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
   c.split_k = kn;
   c.kn = kn;
   // ---- the operand this wave fetches
-  if (g == 0) {
+  const int ga = SWAP ? 1 : 0;               // the wave group that sends A
+  if (g == ga) {
     // A: aidx tile `at`
     const bf16_t* Am = part == 0 ? p.A0 : p.A1;
     int a_tile = at;
@@ -358,7 +365,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
   // DMA offsets: KC slot j lane i -> row (dma_base + j) * 8 + i / 8, chunk
   // i % 8 (swizzled); KS slot j lane i -> k row 2 (dma_base + j) + i / 32,
   // chunk i % 32 (64-byte blocks swizzled by k row mod 4)
-  const bool ks_mine = g == 0 ? KSA : KSB;
+  const bool ks_mine = g == ga ? KSA : KSB;
 #pragma unroll
   for (int j = 0; j < kBSlots; ++j) {
     const int q = (c.dma_base + j) * 64 + lane;
@@ -371,7 +378,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
     }
   }
   // a KC slot holds 8 rows; only the token rows of mode 0 can run short
-  c.on = g == 0 || MODE != 0 || KSB || c.dma_base * 8 < rows;
+  c.on = g == ga || MODE != 0 || KSB || c.dma_base * 8 < rows;
   // fragment bases
   {
     const int r32 = lane & 31, h = lane >> 5;
@@ -402,9 +409,9 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
   nk += nk & 1;
   if (nk > 0) {
     switch (nbv) {
-      case 2: b_main_loop<KSA, KSB, 2>(c, sa0, sa1, sbr, nk, g, acc); break;
-      case 1: b_main_loop<KSA, KSB, 1>(c, sa0, sa1, sbr, nk, g, acc); break;
-      default: b_main_loop<KSA, KSB, 0>(c, sa0, sa1, sbr, nk, g, acc); break;
+      case 2: b_main_loop<KSA, KSB, SWAP, 2>(c, sa0, sa1, sbr, nk, g, acc); break;
+      case 1: b_main_loop<KSA, KSB, SWAP, 1>(c, sa0, sa1, sbr, nk, g, acc); break;
+      default: b_main_loop<KSA, KSB, SWAP, 0>(c, sa0, sa1, sbr, nk, g, acc); break;
     }
   }
 
@@ -506,12 +513,12 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
 
 namespace {
 
-template <bool KSA, bool KSB, int MODE, bool CBF16>
+template <bool KSA, bool KSB, int MODE, bool CBF16, bool SWAP = false>
 void bg_launch(BgArgs p, int groups, hipStream_t s) {
   p.total = groups * p.n_at * p.n_bt;
   p.per_xcd = (p.total + kBXcds - 1) / kBXcds;
   const int grid = p.per_xcd * kBXcds;
-  if (grid > 0) bwd_tile_kernel<KSA, KSB, MODE, CBF16><<<grid, kBThreads, 0, s>>>(p);
+  if (grid > 0) bwd_tile_kernel<KSA, KSB, MODE, CBF16, SWAP><<<grid, kBThreads, 0, s>>>(p);
 }
 
 BgArgs bg_rows_args(const int32_t* tb_count, const int32_t* tb_exp, const int32_t* tb_row0,
@@ -550,7 +557,7 @@ void launch_bwd_recompute(const Dims& D, const void* xs, const void* Wg, const v
   p.ldc = 2 * D.f;
   p.K = D.d;
   p.n_at = 2 * D.f / kBT;
-  bg_launch<false, false, 0, true>(p, 1, s);
+  bg_launch<false, false, 0, true, true>(p, 1, s);
 }
 
 // Z = W2^T dOut_r: A = W2 read down its columns (index f, k = d)
@@ -633,7 +640,7 @@ void launch_bwd_wgrad_gate_up(const Dims& D, const void* dab, const void* xs, vo
   p.n_at = D.d / kBT;
   p.counts = counts;
   p.offsets = offsets;
-  bg_launch<true, true, 1, true>(p, D.E, s);
+  bg_launch<true, true, 1, true, true>(p, D.E, s);
 }
 
 }  // namespace moe
