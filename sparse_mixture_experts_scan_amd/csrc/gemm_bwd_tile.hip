@@ -48,7 +48,10 @@ constexpr int kBStrideB = 128;              // rows between a wave's B fragments
 constexpr int kBOper = kBT * kBK * 2;       // one operand tile in LDS (32 KiB)
 constexpr int kBSlots = kBOper / 1024 / 4;  // 1 KiB DMA loads per wave per stage (8)
 constexpr int kBXcds = 8;
-constexpr int kBFeatGroup = 4;
+#ifndef MOE_BWD_FEAT_GROUP
+#define MOE_BWD_FEAT_GROUP 4
+#endif
+constexpr int kBFeatGroup = MOE_BWD_FEAT_GROUP;  // feature tiles per XCD-local group
 constexpr int kKCRow = kBK * 2;             // KC: bytes per LDS row (128)
 constexpr int kKSRow = kBT * 2;             // KS: bytes per LDS row (512)
 static_assert(5 * kBOper <= 160 * 1024, "LDS buffers exceed 160 KiB");
