@@ -340,18 +340,22 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
 
   // ---- epilogue.  D of a 32x32 MFMA: lane holds column n = lane % 32 and rows
   // 8 * (j / 4) + 4 * (lane / 32) + j % 4, j = 0..15: four consecutive
-  // features.  Skipped fragments hold zeros (padding rows).
+  // features.  Skipped fragments hold zeros (padding rows).  The tile is
+  // staged in the (now idle) B ring and written back as whole rows with
+  // 16-byte stores; every row of the tile is written, padding rows as zeros.
   const int r32 = lane & 31, half = lane >> 5;
+  lds_barrier();                            // every wave is past its last LDS read
+  if constexpr (GATEUP) {
+    constexpr int kPitch = FB * 2 + 16;     // bf16 row of the h tile, padded
+    static_assert(kTileBT * kPitch <= 3 * kOperBytes, "staging exceeds the B ring");
 #pragma unroll
-  for (int b = 0; b < kBFrags; ++b) {
-    const size_t row = (size_t)(row0 + wt * 32 + b * kBStride + r32);
-    if constexpr (GATEUP) {
-      bf16_t* h = reinterpret_cast<bf16_t*>(outp) + row * N;
+    for (int b = 0; b < kBFrags; ++b) {
+      const int lrow = wt * 32 + b * kBStride + r32;
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int feat = f0 + wf * 64 + a * 32 + jj * 8 + half * 4;
+          const int lfeat = wf * 64 + a * 32 + jj * 8 + half * 4;
           uint32_t p[2];
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
@@ -360,20 +364,52 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
             p[q] = (uint32_t)Elem<bf16_t>::from_f32(silu_bf16_out(g0) * u0) |
                    ((uint32_t)Elem<bf16_t>::from_f32(silu_bf16_out(g1) * u1) << 16);
           }
-          *reinterpret_cast<uint2*>(h + feat) = make_uint2(p[0], p[1]);
-        }
-    } else {
-      float* y = reinterpret_cast<float*>(outp) + part * part_stride + row * N;
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int feat = f0 + wf * 128 + a * 32 + jj * 8 + half * 4;
-          *reinterpret_cast<float4*>(y + feat) =
-              make_float4(acc[a][b][jj * 4], acc[a][b][jj * 4 + 1], acc[a][b][jj * 4 + 2],
-                          acc[a][b][jj * 4 + 3]);
+          *reinterpret_cast<uint2*>(sbr + lrow * kPitch + lfeat * 2) = make_uint2(p[0], p[1]);
         }
     }
+    lds_barrier();
+    constexpr int kChunksRow = FB * 2 / 16;  // 16-byte pieces per h row
+    bf16_t* h = reinterpret_cast<bf16_t*>(outp) + (size_t)row0 * N + f0;
+#pragma unroll
+    for (int it = 0; it < kTileBT * kChunksRow / kTileThreads; ++it) {
+      const int q = it * kTileThreads + tid;
+      const int lrow = q / kChunksRow, ch = q % kChunksRow;
+      const uint4 v = *reinterpret_cast<const uint4*>(sbr + lrow * kPitch + ch * 16);
+      *reinterpret_cast<uint4*>(h + (size_t)lrow * N + ch * 8) = v;
+    }
+  } else {
+    // fp32: (token fragment b, feature half ch) = 128 rows x 128 features
+    // at a time, written by the waves of that half
+    constexpr int kPitch = 128 * 4 + 16;
+    static_assert(128 * kPitch <= 3 * kOperBytes, "staging exceeds the B ring");
+    float* y = reinterpret_cast<float*>(outp) + part * part_stride + (size_t)row0 * N + f0;
+#pragma unroll
+    for (int b = 0; b < kBFrags; ++b)
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        if (wf == ch) {
+          const int lrow = wt * 32 + r32;
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int col = a * 32 + jj * 8 + half * 4;
+              *reinterpret_cast<float4*>(sbr + lrow * kPitch + col * 4) =
+                  make_float4(acc[a][b][jj * 4], acc[a][b][jj * 4 + 1], acc[a][b][jj * 4 + 2],
+                              acc[a][b][jj * 4 + 3]);
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int it = 0; it < 128 * 32 / kTileThreads; ++it) {
+          const int q = it * kTileThreads + tid;
+          const int lrow = q / 32, chunk = q % 32;
+          const uint4 v = *reinterpret_cast<const uint4*>(sbr + lrow * kPitch + chunk * 16);
+          *reinterpret_cast<uint4*>(y + (size_t)(b * kBStride + lrow) * N + ch * 128 +
+                                    chunk * 4) = v;
+        }
+        lds_barrier();
+      }
   }
 }
 
