@@ -246,7 +246,10 @@ typedef struct moe_ws_layout {
   size_t tile_expert;       /* [max_rows / block_rows] expert of each tile     */
   size_t row_token;         /* [max_rows] token of each permuted row or -1     */
   size_t tok_row;           /* [T][k] permuted row of each (token, slot)       */
-  size_t xs;                /* [max_rows][d_model] dtype: gathered tokens      */
+  size_t xs;                /* [max_rows][d_model] dtype: gathered tokens.  Not
+                               written when the LDS-tiled form reads the tokens
+                               in place through row_token instead (k >= 4 and
+                               T * d_model * 2 < 2^31)                         */
   size_t h;                 /* [max_rows][d_ff] dtype: SiLU(gate) * up         */
   size_t y;                 /* [down_splits][max_rows][d_model] float32:
                                partial expert outputs (their sum is W2 H)       */

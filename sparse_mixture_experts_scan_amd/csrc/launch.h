@@ -59,7 +59,8 @@ constexpr int kRouterPartStride = 64;  // floats per token row of the partial sc
 // router statistics (when blk_prob is non-NULL): prob_out [E], loss_out [1]
 void launch_scan(const Dims& D, int32_t* blk_counts, const ScanArgs& sa, const float* blk_prob,
                  hipStream_t s);
-// a2: stable row maps and gather of x into expert-contiguous rows
+// a2: stable row maps and gather of x into expert-contiguous rows (xs NULL:
+// the row maps only)
 void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int32_t* blk_base,
                     const int32_t* offsets, int32_t* tok_row, int32_t* row_token, void* xs,
                     hipStream_t s);
@@ -74,9 +75,13 @@ void launch_down_stream(const Dims& D, const void* h, const void* Wd, float* y,
 constexpr int kTileTokens = 256;  // token tile of the tiled form (= padding unit)
 bool tile_shape_ok(const Dims& D);
 int tile_down_splits(const Dims& D);  // K-split count for the tiled down GEMM
-void launch_gateup_tile(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* h,
-                        const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
-                        const int32_t* tile_expert, hipStream_t s);
+// row_token non-NULL: `x` is the token matrix [T][d] and each tile gathers its
+// rows through row_token; NULL: `x` is the gathered Xs
+void launch_gateup_tile(const Dims& D, const void* x, const int32_t* row_token, const void* Wg,
+                        const void* Wu, void* h, const int32_t* counts, const int32_t* offsets,
+                        const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s);
+// whether the tiled gate/up GEMM can gather token rows in place (32-bit offsets)
+bool tile_gathers_in_place(const Dims& D);
 void launch_down_tile(const Dims& D, const void* h, const void* Wd, float* y,
                       const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                       const int32_t* tile_expert, hipStream_t s);

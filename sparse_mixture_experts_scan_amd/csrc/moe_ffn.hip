@@ -273,7 +273,11 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   moe::launch_scan(D, blk, sa, bprob, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess)
     return hip_fail(e, "scan launch");
-  moe::launch_scatter(D, norm_w ? xn : x, idx, blk, offsets, tok_row, row_token, xs, s);
+  // the tiled gate/up GEMM reads token rows in place through row_token, so
+  // the scatter then only writes the row maps
+  const void* tok = norm_w ? xn : x;
+  const bool gather = L.gemm_variant == 1 && moe::tile_gathers_in_place(D);
+  moe::launch_scatter(D, tok, idx, blk, offsets, tok_row, row_token, gather ? nullptr : xs, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess)
     return hip_fail(e, "scatter launch");
   if (q4 && L.gemm_variant == 1) {
@@ -294,7 +298,8 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   if (q4 && L.gemm_variant == 0)
     moe::launch_gateup_q4(D, xs, q4[0], q4[1], h, counts, offsets, num_tiles, tile_expert, s);
   else if (L.gemm_variant == 1)
-    moe::launch_gateup_tile(D, xs, W_gate, W_up, h, counts, offsets, num_tiles, tile_expert, s);
+    moe::launch_gateup_tile(D, gather ? tok : xs, gather ? row_token : nullptr, W_gate, W_up,
+                            h, counts, offsets, num_tiles, tile_expert, s);
   else
     moe::launch_gateup_stream(D, xs, W_gate, W_up, h, counts, offsets, num_tiles, tile_expert, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess)

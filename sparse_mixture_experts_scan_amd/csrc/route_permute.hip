@@ -500,6 +500,7 @@ __global__ __launch_bounds__(kRouterThreads) void scatter_gather_kernel(
       row_token[row] = t;
     }
   }
+  if (xs == nullptr) return;               // row maps only: the GEMM gathers in place
   sRow[tid] = row;
   sTok[tid] = t;
   __syncthreads();
@@ -629,7 +630,7 @@ void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int3
   const int cpr = D.d * (D.bf16 ? 2 : 4) / 16;
   int cs = 1;
   while (D.nblk * cs < 256 && cs * 2 <= cpr / 16 && cpr % (cs * 2) == 0) cs *= 2;
-  const dim3 grid(D.nblk, cs);
+  const dim3 grid(D.nblk, xs ? cs : 1);
   if (D.bf16)
     scatter_gather_kernel<bf16_t><<<grid, kRouterThreads, 0, s>>>(
         (const bf16_t*)x, idx, blk_base, offsets, D.T, D.d, D.E, D.k, tok_row, row_token,

@@ -38,7 +38,9 @@ def capture(fn):
 @pytest.mark.parametrize("cfg", [MoEConfig("graph_stream", 48, 256, 512, 8, 2, "bf16"),
                                  # one router block: the select pass runs the scan
                                  MoEConfig("graph_decode", 16, 512, 1024, 8, 2, "bf16"),
-                                 MoEConfig("graph_tile", 1000, 256, 384, 8, 2, "bf16")],
+                                 MoEConfig("graph_tile", 1000, 256, 384, 8, 2, "bf16"),
+                                 # top-4: the tiled form reads the tokens in place
+                                 MoEConfig("graph_tile_k4", 600, 256, 256, 8, 4, "bf16")],
                          ids=lambda c: c.name)
 def test_forward_graph_replays(cfg):
     announce(f"case {cfg.name}")
