@@ -28,6 +28,7 @@ CASES = [
     MoEConfig("block_stream_bf16", 300, 256, 512, 8, 2, "bf16"),
     MoEConfig("block_f32", 100, 256, 256, 8, 2, "f32"),
     MoEConfig("block_tile_bf16", 1000, 512, 384, 8, 2, "bf16"),      # LDS-tiled GEMMs
+    MoEConfig("block_tile_k4", 800, 256, 256, 8, 4, "bf16"),         # tiled, tokens read in place
     MoEConfig("block_split_router", 40, 2048, 256, 16, 4, "bf16"),   # router split over d
     MoEConfig("block_single", 1, 128, 128, 4, 2, "bf16"),
 ]

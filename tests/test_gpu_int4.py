@@ -123,6 +123,7 @@ CASES = [
     (MoEConfig("q4_bt32", 300, 256, 256, 8, 2, "bf16"), 128, 0),     # 32-row token tiles
     (MoEConfig("q4_single", 1, 128, 128, 4, 1, "bf16"), 128, 0),
     (MoEConfig("q4_tiled", 1000, 256, 384, 8, 2, "bf16"), 128, 1),   # dequantize + tile
+    (MoEConfig("q4_tiled_k4", 600, 256, 256, 8, 4, "bf16"), 128, 1),  # tiled, tokens in place
     (MoEConfig("q4_fine", 200, 128, 256, 64, 8, "bf16"), 128, 0),
 ]
 
