@@ -111,7 +111,7 @@ struct BgArgs {
   int c_split_tile;
   int K;                // mode 0 contraction length
   int n_at, n_bt;       // tiles along aidx; along brow (mode 0: tile-table capacity)
-  int per_xcd, total;
+  int per_xcd, total;   // tiles per XCD (mode 1: per expert); experts or K parts
   const int32_t* tb_count;
   const int32_t* tb_exp;
   const int32_t* tb_row0;
@@ -293,15 +293,23 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
   __shared__ __attribute__((aligned(1024))) char sa1[kBOper];
   __shared__ __attribute__((aligned(1024))) char sbr[3 * kBOper];
 
-  // ---- tile: XCD-contiguous remap, then (expert,) groups of feature tiles
+  // ---- tile.  Work-groups go to the XCDs round robin.  Mode 1: XCD x takes
+  // the x-th contiguous share of each expert's tiles, expert by expert, so
+  // that every XCD gets the same work however unevenly the rows are spread
+  // over the experts (with skewed routing, one expert per XCD left two XCDs
+  // with most of it).  Mode 0: XCD-contiguous ranges of all tiles, K part
+  // slowest (each XCD then streams one weight matrix of dX, which its L2
+  // serves better).  Then groups of feature tiles.
   const int L = blockIdx.x;
-  int Lp = (L % kBXcds) * p.per_xcd + L / kBXcds;
-  if (Lp >= p.total) return;
-  int e = 0, part = 0;
+  int e = 0, part = 0, Lp;
   if constexpr (MODE == 1) {
-    e = Lp / (p.n_at * p.n_bt);
-    Lp -= e * p.n_at * p.n_bt;
+    const int xcd = L % kBXcds, li = L / kBXcds;
+    e = li / p.per_xcd;                     // per_xcd: tiles per expert and XCD
+    Lp = xcd * p.per_xcd + (li - e * p.per_xcd);
+    if (e >= p.total || Lp >= p.n_at * p.n_bt) return;
   } else {
+    Lp = (L % kBXcds) * p.per_xcd + L / kBXcds;  // per_xcd: tiles per XCD
+    if (Lp >= p.total * p.n_at * p.n_bt) return;
     part = Lp / (p.n_at * p.n_bt);
     Lp -= part * p.n_at * p.n_bt;
   }
@@ -518,9 +526,11 @@ namespace {
 
 template <bool KSA, bool KSB, int MODE, bool CBF16, bool SWAP = false>
 void bg_launch(BgArgs p, int groups, hipStream_t s) {
-  p.total = groups * p.n_at * p.n_bt;
-  p.per_xcd = (p.total + kBXcds - 1) / kBXcds;
-  const int grid = p.per_xcd * kBXcds;
+  p.total = groups;                                  // experts or K parts
+  const int tiles = p.n_at * p.n_bt;
+  p.per_xcd = MODE == 1 ? (tiles + kBXcds - 1) / kBXcds              // per expert
+                        : (groups * tiles + kBXcds - 1) / kBXcds;    // all tiles
+  const int grid = p.per_xcd * kBXcds * (MODE == 1 ? groups : 1);
   if (grid > 0) bwd_tile_kernel<KSA, KSB, MODE, CBF16, SWAP><<<grid, kBThreads, 0, s>>>(p);
 }
 
