@@ -9,6 +9,8 @@
 namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t bf16_t;  // storage type of bfloat16 data
@@ -22,6 +24,13 @@ constexpr int kRouterThreads = 256;
 // f32:  one chunk = 4 elements = four v_mfma_f32_16x16x4_f32, element i of the
 //       chunk feeding the i-th instruction.  A and B use the same mapping, so
 //       every k is paired with itself exactly once.
+// Two floats rounded to nearest-even bf16 in one conversion (lo in the low
+// half); the same rounding as a scalar conversion of each.
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> {
   static constexpr int kVec = 8;  // elements per 16-byte chunk

@@ -457,10 +457,8 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
         for (int jj = 0; jj < 4; ++jj) {
           const int aidx = wf * 128 + a * 32 + jj * 8 + half * 4;
           const f32x16& v = acc[a][b];
-          const uint32_t lo = (uint32_t)Elem<bf16_t>::from_f32(v[jj * 4]) |
-                              ((uint32_t)Elem<bf16_t>::from_f32(v[jj * 4 + 1]) << 16);
-          const uint32_t hi = (uint32_t)Elem<bf16_t>::from_f32(v[jj * 4 + 2]) |
-                              ((uint32_t)Elem<bf16_t>::from_f32(v[jj * 4 + 3]) << 16);
+          const uint32_t lo = pack_bf16x2(v[jj * 4], v[jj * 4 + 1]);
+          const uint32_t hi = pack_bf16x2(v[jj * 4 + 2], v[jj * 4 + 3]);
           *reinterpret_cast<uint2*>(sbr + lrow * kStagePitch + aidx * 2) = make_uint2(lo, hi);
         }
       __syncthreads();

@@ -362,8 +362,9 @@ __device__ __forceinline__ void stream_q4_body(
         if constexpr (GATEUP) {
           bf16_t* h = reinterpret_cast<bf16_t*>(outp) + r * N + col;
           const f32x4 g = acc[0][f][n], u = acc[1][f][n];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) h[i] = Elem<bf16_t>::from_f32(silu_f32(g[i]) * u[i]);
+          *reinterpret_cast<uint2*>(h) =
+              make_uint2(pack_bf16x2(silu_f32(g[0]) * u[0], silu_f32(g[1]) * u[1]),
+                         pack_bf16x2(silu_f32(g[2]) * u[2], silu_f32(g[3]) * u[3]));
         } else {
           float* y = reinterpret_cast<float*>(outp) + r * N + col;
           *reinterpret_cast<float4*>(y) =

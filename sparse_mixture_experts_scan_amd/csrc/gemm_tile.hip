@@ -368,8 +368,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
           for (int q = 0; q < 2; ++q) {
             const float g0 = acc[a][b][jj * 4 + 2 * q], u0 = acc[a + 2][b][jj * 4 + 2 * q];
             const float g1 = acc[a][b][jj * 4 + 2 * q + 1], u1 = acc[a + 2][b][jj * 4 + 2 * q + 1];
-            p[q] = (uint32_t)Elem<bf16_t>::from_f32(silu_bf16_out(g0) * u0) |
-                   ((uint32_t)Elem<bf16_t>::from_f32(silu_bf16_out(g1) * u1) << 16);
+            p[q] = pack_bf16x2(silu_bf16_out(g0) * u0, silu_bf16_out(g1) * u1);
           }
           *reinterpret_cast<uint2*>(sbr + lrow * kPitch + lfeat * 2) = make_uint2(p[0], p[1]);
         }

@@ -562,10 +562,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       a.z += Elem<T>::to_f32(xr[2]);
       a.w += Elem<T>::to_f32(xr[3]);
     }
-    o[0] = Elem<T>::from_f32(a.x);
-    o[1] = Elem<T>::from_f32(a.y);
-    o[2] = Elem<T>::from_f32(a.z);
-    o[3] = Elem<T>::from_f32(a.w);
+    if constexpr (sizeof(T) == 2)
+      *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+    else
+      *reinterpret_cast<float4*>(o) = make_float4(a.x, a.y, a.z, a.w);
   }
 }
 
