@@ -237,6 +237,10 @@ typedef struct moe_ws_layout {
   int32_t down_splits;      /* K-splits of the down GEMM: y holds this many
                                partial [max_rows][d_model] blocks, summed by
                                the combine                                     */
+  int32_t tokens_in_place;  /* 1: the gate/up GEMM reads each row's token from
+                               x (or xn) through row_token and xs is not
+                               written; 0: it reads the gathered rows of xs    */
+  int32_t reserved;         /* 0                                               */
   size_t topk_idx;          /* [T][k]                                          */
   size_t topk_w;            /* [T][k] float32                                  */
   size_t block_counts;      /* [router_blocks][E]: per-block counts, then bases */
@@ -247,9 +251,10 @@ typedef struct moe_ws_layout {
   size_t row_token;         /* [max_rows] token of each permuted row or -1     */
   size_t tok_row;           /* [T][k] permuted row of each (token, slot)       */
   size_t xs;                /* [max_rows][d_model] dtype: gathered tokens.  Not
-                               written when the LDS-tiled form reads the tokens
-                               in place through row_token instead (k >= 4 and
-                               T * d_model * 2 < 2^31)                         */
+                               written when tokens_in_place is 1: bf16 tokens
+                               with T * d_model * 2 < 2^31, and either the
+                               weight-streaming form with d_model a multiple of
+                               128 (not INT4) or the LDS-tiled form with k >= 4 */
   size_t h;                 /* [max_rows][d_ff] dtype: SiLU(gate) * up         */
   size_t y;                 /* [down_splits][max_rows][d_model] float32:
                                partial expert outputs (their sum is W2 H)       */

@@ -47,7 +47,9 @@ class MoeWsLayout(ctypes.Structure):
                 ("max_rows", ctypes.c_int64),
                 ("router_blocks", ctypes.c_int64),
                 ("gemm_variant", ctypes.c_int32),
-                ("down_splits", ctypes.c_int32)] + [
+                ("down_splits", ctypes.c_int32),
+                ("tokens_in_place", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)] + [
         (name, ctypes.c_size_t) for name in
         ("topk_idx", "topk_w", "block_counts", "counts", "offsets", "num_tiles",
          "tile_expert", "row_token", "tok_row", "xs", "h", "y", "block_probs", "norm_rs", "xn",

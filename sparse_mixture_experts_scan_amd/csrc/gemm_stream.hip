@@ -258,7 +258,8 @@ template <int BT, int FT, bool GATEUP>
 __device__ __forceinline__ void stream_dma_body(
     const bf16_t* __restrict__ act, const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
     void* __restrict__ outp, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_expert, int N, int K) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ tile_expert, int N, int K,
+    const int32_t* __restrict__ row_token, int nT) {
   constexpr int NW = GATEUP ? 2 : 1, NF = FT / 16, NT = BT / 16;
   constexpr int NROW = NW * FT;                   // weight rows of the block
   constexpr int kRunK = 128, kRunBytes = kRunK * 2;
@@ -272,13 +273,20 @@ __device__ __forceinline__ void stream_dma_body(
   __shared__ f32x4 red[NWAVE - 1][NW * NF * NT][kWave];
 
   const int tile = blockIdx.y;
+  const int row0 = tile * BT;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int lr = lane & 15, kg = lane >> 4;
+  // tokens in place: the token of each of this lane's rows (the load does
+  // not wait on the expert lookup)
+  int tok[NT];
+  if (row_token != nullptr) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) tok[n] = row_token[row0 + n * 16 + lr];
+  }
   const int e = tile_expert[tile];
   if (e < 0) return;
-  const int row0 = tile * BT;
   const int f0 = blockIdx.x * FT;
-  const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lr = lane & 15, kg = lane >> 4;
 
   const uint32_t row_bytes = (uint32_t)K * 2;
   __amdgpu_buffer_rsrc_t rw[NW];
@@ -297,9 +305,6 @@ __device__ __forceinline__ void stream_dma_body(
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     fro[ks] = (uint32_t)wave * kSlot + (uint32_t)lr * kRunBytes + (uint32_t)(((ks * 4 + kg) ^ lr) * 16);
-  uint32_t ao[NT];
-#pragma unroll
-  for (int n = 0; n < NT; ++n) ao[n] = (uint32_t)(n * 16 + lr) * row_bytes + kg * 16;
 
   f32x4 acc[NW][NF][NT];
 #pragma unroll
@@ -313,8 +318,21 @@ __device__ __forceinline__ void stream_dma_body(
   const int nb = nrun > wave ? (nrun - wave + NWAVE - 1) / NWAVE : 0;
   const int valid_end = offsets[e] + counts[e];
   const int nvalid = max(0, min(BT, valid_end - row0));
-  const __amdgpu_buffer_rsrc_t ra =
-      stream_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
+  // token rows past the expert's count load as zeros: outside the gathered
+  // rows' range, or (in place) at an offset past the end of x
+  uint32_t ao[NT];
+  __amdgpu_buffer_rsrc_t ra;
+  if (row_token != nullptr) {
+    ra = stream_rsrc(act, (uint32_t)nT * row_bytes);
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      ao[n] = (n * 16 + lr < nvalid && tok[n] >= 0) ? (uint32_t)tok[n] * row_bytes + kg * 16
+                                                     : 0x80000000u;
+  } else {
+    ra = stream_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) ao[n] = (uint32_t)(n * 16 + lr) * row_bytes + kg * 16;
+  }
 
   uint4 t0[NT][4], t1[NT][4];
   // run i of this wave (clamped to its last run)
@@ -411,22 +429,28 @@ __global__ __launch_bounds__(kStreamThreads) void stream_dma_kernel(
     const bf16_t* __restrict__ act, const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
     void* __restrict__ outp, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ num_tiles,
-    const int32_t* __restrict__ tile_expert, int N, int K) {
+    const int32_t* __restrict__ tile_expert, int N, int K, const int32_t* __restrict__ row_token,
+    int nT) {
   (void)num_tiles;
-  stream_dma_body<BT, FT, GATEUP>(act, W0, W1, outp, counts, offsets, tile_expert, N, K);
+  stream_dma_body<BT, FT, GATEUP>(act, W0, W1, outp, counts, offsets, tile_expert, N, K,
+                                  row_token, nT);
+}
+
+bool stream_gathers_in_place(const Dims& D) {
+  return D.bf16 && !D.w4 && D.d % 128 == 0 && (int64_t)D.T * D.d * 2 < (int64_t(1) << 31);
 }
 
 template <typename T, int BT>
-static void gateup_stream(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* h,
-                          const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
-                          const int32_t* tile_expert, hipStream_t s) {
+static void gateup_stream(const Dims& D, const void* xs, const int32_t* row_token, const void* Wg,
+                          const void* Wu, void* h, const int32_t* counts, const int32_t* offsets,
+                          const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s) {
   constexpr int FT = MOE_STREAM_FT_GU;
   dim3 grid(D.f / FT, D.max_tiles);
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (D.d % 128 == 0) {
       stream_dma_kernel<BT, FT, true><<<grid, kStreamThreads, 0, s>>>(
           (const bf16_t*)xs, (const bf16_t*)Wg, (const bf16_t*)Wu, h, counts, offsets, num_tiles,
-          tile_expert, D.f, D.d);
+          tile_expert, D.f, D.d, row_token, D.T);
       return;
     }
   }
@@ -446,7 +470,7 @@ static void down_stream(const Dims& D, const void* h, const void* Wd, float* y,
       constexpr int FTD = MOE_STREAM_DMA_FT_DN;
       stream_dma_kernel<BT, FTD, false><<<dim3(D.d / FTD, D.max_tiles), kStreamThreads, 0, s>>>(
           (const bf16_t*)h, (const bf16_t*)Wd, nullptr, y, counts, offsets, num_tiles,
-          tile_expert, D.d, D.f);
+          tile_expert, D.d, D.f, nullptr, 0);
       return;
     }
   }
@@ -454,15 +478,24 @@ static void down_stream(const Dims& D, const void* h, const void* Wd, float* y,
       (const T*)h, (const T*)Wd, nullptr, y, counts, offsets, num_tiles, tile_expert, D.d, D.f);
 }
 
-void launch_gateup_stream(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* h,
-                          const int32_t* counts, const int32_t* offsets,
-                          const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s) {
+void launch_gateup_stream(const Dims& D, const void* act, const int32_t* row_token,
+                          const void* Wg, const void* Wu, void* h, const int32_t* counts,
+                          const int32_t* offsets, const int32_t* num_tiles,
+                          const int32_t* tile_expert, hipStream_t s) {
   if (D.bf16) {
-    if (D.BT == 16) gateup_stream<bf16_t, 16>(D, xs, Wg, Wu, h, counts, offsets, num_tiles, tile_expert, s);
-    else gateup_stream<bf16_t, 32>(D, xs, Wg, Wu, h, counts, offsets, num_tiles, tile_expert, s);
+    if (D.BT == 16)
+      gateup_stream<bf16_t, 16>(D, act, row_token, Wg, Wu, h, counts, offsets, num_tiles,
+                                tile_expert, s);
+    else
+      gateup_stream<bf16_t, 32>(D, act, row_token, Wg, Wu, h, counts, offsets, num_tiles,
+                                tile_expert, s);
   } else {
-    if (D.BT == 16) gateup_stream<float, 16>(D, xs, Wg, Wu, h, counts, offsets, num_tiles, tile_expert, s);
-    else gateup_stream<float, 32>(D, xs, Wg, Wu, h, counts, offsets, num_tiles, tile_expert, s);
+    if (D.BT == 16)
+      gateup_stream<float, 16>(D, act, nullptr, Wg, Wu, h, counts, offsets, num_tiles,
+                               tile_expert, s);
+    else
+      gateup_stream<float, 32>(D, act, nullptr, Wg, Wu, h, counts, offsets, num_tiles,
+                               tile_expert, s);
   }
 }
 

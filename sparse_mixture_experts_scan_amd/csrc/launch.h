@@ -45,6 +45,9 @@ struct ScanArgs {
   int32_t* counts_out;
   float* prob_out;
   float* loss_out;
+  // with a single router block: non-NULL makes the select pass also write the
+  // row maps (tok_row, row_token), for a GEMM that reads the tokens in place
+  int32_t* tok_row;
 };
 // With a single router block the router's select pass also runs the expert
 // scan (launch_scan is then a no-op), which saves a launch for small T.
@@ -64,10 +67,14 @@ void launch_scan(const Dims& D, int32_t* blk_counts, const ScanArgs& sa, const f
 void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int32_t* blk_base,
                     const int32_t* offsets, int32_t* tok_row, int32_t* row_token, void* xs,
                     hipStream_t s);
-// a3 + a4: grouped GEMMs, weight-streaming form (few rows per expert)
-void launch_gateup_stream(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* h,
-                          const int32_t* counts, const int32_t* offsets,
-                          const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s);
+// a3 + a4: grouped GEMMs, weight-streaming form (few rows per expert).
+// row_token NULL: act is the gathered rows (xs); else act is x (or xn) and
+// each row's token comes from row_token (only when stream_gathers_in_place).
+bool stream_gathers_in_place(const Dims& D);
+void launch_gateup_stream(const Dims& D, const void* act, const int32_t* row_token,
+                          const void* Wg, const void* Wu, void* h, const int32_t* counts,
+                          const int32_t* offsets, const int32_t* num_tiles,
+                          const int32_t* tile_expert, hipStream_t s);
 void launch_down_stream(const Dims& D, const void* h, const void* Wd, float* y,
                         const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                         const int32_t* tile_expert, hipStream_t s);

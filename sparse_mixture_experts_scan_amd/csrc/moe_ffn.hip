@@ -87,6 +87,8 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   L.router_blocks = D.nblk;
   L.gemm_variant = variant;
   L.down_splits = D.down_splits;
+  L.tokens_in_place =
+      variant == 1 ? moe::tile_gathers_in_place(D) : moe::stream_gathers_in_place(D);
   const size_t es = D.bf16 ? 2 : 4;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -264,8 +266,15 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
     moe::launch_rmsnorm(D, x, norm_w, eps, rs, xn, s);
     if ((e = hipGetLastError()) != hipSuccess) return hip_fail(e, "rmsnorm launch");
   }
+  // the gate/up GEMM reads token rows in place through row_token, so the
+  // scatter then only writes the row maps, or (one router block) the
+  // router's select pass does and there is no scatter launch
+  const void* tok = norm_w ? xn : x;
+  const bool gather = L.tokens_in_place != 0;
+  const bool maps_in_router = gather && moe::router_fuses_scan(D);
   const moe::ScanArgs sa{counts,    offsets,   num_tiles,         tile_expert,
-                         row_token, o.expert_counts_out, o.router_prob_out, o.balance_loss_out};
+                         row_token, o.expert_counts_out, o.router_prob_out, o.balance_loss_out,
+                         maps_in_router ? tok_row : nullptr};
   moe::launch_router(D, x, W_router, o.router_bias, idx, w, blk, rpart, bprob, norm_w, rs,
                      nullptr, sa, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess)
@@ -273,11 +282,8 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   moe::launch_scan(D, blk, sa, bprob, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess)
     return hip_fail(e, "scan launch");
-  // the tiled gate/up GEMM reads token rows in place through row_token, so
-  // the scatter then only writes the row maps
-  const void* tok = norm_w ? xn : x;
-  const bool gather = L.gemm_variant == 1 && moe::tile_gathers_in_place(D);
-  moe::launch_scatter(D, tok, idx, blk, offsets, tok_row, row_token, gather ? nullptr : xs, s);
+  if (!maps_in_router)
+    moe::launch_scatter(D, tok, idx, blk, offsets, tok_row, row_token, gather ? nullptr : xs, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess)
     return hip_fail(e, "scatter launch");
   if (q4 && L.gemm_variant == 1) {
@@ -301,7 +307,8 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
     moe::launch_gateup_tile(D, gather ? tok : xs, gather ? row_token : nullptr, W_gate, W_up,
                             h, counts, offsets, num_tiles, tile_expert, s);
   else
-    moe::launch_gateup_stream(D, xs, W_gate, W_up, h, counts, offsets, num_tiles, tile_expert, s);
+    moe::launch_gateup_stream(D, gather ? tok : xs, gather ? row_token : nullptr, W_gate, W_up,
+                              h, counts, offsets, num_tiles, tile_expert, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess)
     return hip_fail(e, "gate/up launch");
   if (q4 && L.gemm_variant == 0)
@@ -566,7 +573,7 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   // routing and permutation of the forward pass, the permuted upstream
   // gradient and the 128-row tile table
   const moe::ScanArgs sa{counts, offsets, I(b.num_tiles), I(b.tile_expert), row_token,
-                         nullptr, nullptr, nullptr};
+                         nullptr, nullptr, nullptr, nullptr};
   moe::launch_router(D, x, W_router, o.router_bias, idx, w, I(b.block_counts),
                      F(b.router_partial), nullptr, nullptr, nullptr, F(b.logits), sa, s);
   moe::launch_scan(D, I(b.block_counts), sa, nullptr, s);

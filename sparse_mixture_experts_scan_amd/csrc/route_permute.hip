@@ -297,10 +297,54 @@ __device__ __forceinline__ void expert_scan_block(
     int32_t* __restrict__ counts_out, int nT, const float* __restrict__ blk_prob,
     float* __restrict__ prob_out, float* __restrict__ loss_out);
 
+// Row maps of one router block (kRouterTokens tokens), run by all
+// kRouterThreads threads (contains a barrier): thread p < kRouterTokens * k
+// takes pair (t0 + p / k, p % k); its rank among the block's earlier pairs on
+// the same expert (wave ballots per expert plus the counts of earlier waves)
+// gives row offsets[e] + base[e] + rank, so rows inside an expert segment are
+// in ascending (token, slot) order.  sRow[p], sTok[p] get the row and token
+// (-1 past the batch); with write_maps, tok_row and row_token are written.
+__device__ __forceinline__ void scatter_rows_block(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ offsets, int nT, int E, int k, int t0, bool write_maps,
+    int32_t* __restrict__ tok_row, int32_t* __restrict__ row_token, int* sRow, int* sTok) {
+  constexpr int NWAVE = kRouterThreads / kWave;
+  __shared__ int wcnt[NWAVE][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int np = kRouterTokens * k;
+  int e = -1, t = -1;
+  if (tid < np) {
+    t = t0 + tid / k;
+    if (t < nT) e = idx[(size_t)t0 * k + tid];
+    else t = -1;
+  }
+  int rank_w = 0;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int ex = 0; ex < E; ++ex) {
+    const uint64_t msk = __ballot(e == ex);
+    if (e == ex) rank_w = __popcll(msk & lt);
+    if (lane == 0) wcnt[wave][ex] = __popcll(msk);
+  }
+  __syncthreads();
+  int row = -1;
+  if (e >= 0) {
+    int rank = rank_w;
+    for (int w = 0; w < wave; ++w) rank += wcnt[w][e];
+    row = offsets[e] + base[e] + rank;
+    if (write_maps) {
+      tok_row[(size_t)t0 * k + tid] = row;
+      row_token[row] = t;
+    }
+  }
+  sRow[tid] = row;
+  sTok[tid] = t;
+}
+
 // Second pass of a split router: per token, the split partial scores are
 // added in split order (deterministic), the bias added, then top-k/softmax.
 // With a single router block (do_scan) the same block then runs the expert
-// scan (a2, part 1) on the counts it has just written, which saves a launch.
+// scan (a2, part 1) on the counts it has just written, which saves a launch,
+// and with sa.tok_row set the row maps as well (no scatter launch).
 constexpr int kSelectThreads = 256;
 constexpr int kMaxRouterSplits = 16;
 
@@ -310,7 +354,8 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     int32_t* __restrict__ blk_counts, float* __restrict__ blk_prob,
     const float* __restrict__ rs, float* __restrict__ logits_out, ScanArgs sa, int do_scan,
     int Epow2, int BT, int max_rows, int max_tiles) {
-  static_assert(kSelectThreads == 256, "the fused expert scan runs on 256 threads");
+  static_assert(kSelectThreads == 256 && kSelectThreads == kRouterThreads,
+                "the fused expert scan and row maps run on 256 threads");
   constexpr int TB = kRouterTokens;
   __shared__ float slog[TB][65];
   __shared__ int hist[64];
@@ -349,6 +394,12 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     expert_scan_block(blk_counts, 1, E, Epow2, BT, max_rows, max_tiles, sa.counts, sa.offsets,
                       sa.num_tiles, sa.tile_expert, sa.row_token, sa.counts_out, nT, blk_prob,
                       sa.prob_out, sa.loss_out);
+    if (sa.tok_row != nullptr) {   // the row maps too (the GEMM reads tokens in place)
+      __shared__ int sRow[kRouterThreads], sTok[kRouterThreads];
+      __syncthreads();
+      scatter_rows_block(idx_out, blk_counts, sa.offsets, nT, E, k, 0, true, sa.tok_row,
+                         sa.row_token, sRow, sTok);
+    }
   }
 }
 
@@ -369,7 +420,9 @@ __device__ __forceinline__ void expert_scan_block(
   __shared__ int s_cnt[64];
   __shared__ int s_off[65];
   const int tid = threadIdx.x;
-  const int C = 256 / Epow2;       // block chunks scanned in parallel per expert
+  // block chunks scanned in parallel per expert (no more chunks than blocks:
+  // one thread per expert then walks the chunks in order)
+  const int C = min(256 / Epow2, max(nblk, 1));
   const int e = tid % Epow2, c = tid / Epow2;
   const int per = (nblk + C - 1) / C;
   const int b0 = min(nblk, c * per), b1 = min(nblk, b0 + per);
@@ -469,46 +522,19 @@ __global__ __launch_bounds__(kRouterThreads) void scatter_gather_kernel(
     const T* __restrict__ x, const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
     const int32_t* __restrict__ offsets, int nT, int d, int E, int k,
     int32_t* __restrict__ tok_row, int32_t* __restrict__ row_token, T* __restrict__ xs) {
-  constexpr int NWAVE = kRouterThreads / kWave;
-  __shared__ int wcnt[NWAVE][64];
   __shared__ int sRow[kRouterThreads];
   __shared__ int sTok[kRouterThreads];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * kRouterTokens;
-  const int np = kRouterTokens * k;
-  int e = -1, t = -1;
-  if (tid < np) {
-    t = t0 + tid / k;
-    if (t < nT) e = idx[(size_t)t0 * k + tid];
-    else t = -1;
-  }
-  int rank_w = 0;
-  const uint64_t lt = (1ull << lane) - 1ull;
-  for (int ex = 0; ex < E; ++ex) {
-    const uint64_t msk = __ballot(e == ex);
-    if (e == ex) rank_w = __popcll(msk & lt);
-    if (lane == 0) wcnt[wave][ex] = __popcll(msk);
-  }
-  __syncthreads();
-  int row = -1;
-  if (e >= 0) {
-    int rank = rank_w;
-    for (int w = 0; w < wave; ++w) rank += wcnt[w][e];
-    row = offsets[e] + base[(size_t)blockIdx.x * E + e] + rank;
-    if (blockIdx.y == 0) {
-      tok_row[(size_t)t0 * k + tid] = row;
-      row_token[row] = t;
-    }
-  }
+  scatter_rows_block(idx, base + (size_t)blockIdx.x * E, offsets, nT, E, k, t0, blockIdx.y == 0,
+                     tok_row, row_token, sRow, sTok);
   if (xs == nullptr) return;               // row maps only: the GEMM gathers in place
-  sRow[tid] = row;
-  sTok[tid] = t;
   __syncthreads();
+  const int np = kRouterTokens * k;
   const int per_chunk = 16 / (int)sizeof(T);
   const int cpr = d / per_chunk;                       // 16-byte chunks per row
   const int cps = cpr / gridDim.y;                     // chunks in this column slice
   const int c0 = blockIdx.y * cps;
-  for (int i = tid; i < np * cps; i += kRouterThreads) {
+  for (int i = threadIdx.x; i < np * cps; i += kRouterThreads) {
     const int p = i / cps, c = c0 + (i - p * cps);
     const int r = sRow[p];
     if (r >= 0)

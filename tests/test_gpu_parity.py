@@ -39,8 +39,8 @@ def full_check(cfg: MoEConfig, seed=0, inp=None, value_tokens=None, n_hidden=2):
     H.check_permutation(cfg, inp, res)
     toks = np.arange(cfg.T) if value_tokens is None else value_tokens
     valid_rows = np.nonzero(res["row_token"] >= 0)[0]
-    # with k >= 4 the tiled form reads the tokens in place and writes no Xs
-    if res["layout"].gemm_variant == 0 or cfg.k < 4:
+    # a GEMM that reads the tokens in place through row_token writes no Xs
+    if not res["layout"].tokens_in_place:
         H.check_gather(cfg, inp, res, valid_rows[:: max(1, valid_rows.size // 64)])
     err = H.check_values(cfg, inp, res, toks)
     eh, ey = H.check_hidden_and_expert_outputs(cfg, inp, res, toks[:n_hidden])
