@@ -12,8 +12,8 @@ plain elementwise kernel that reads N MiB and writes N MiB; what the two
 counters read for it gives the scale factor from counter units to bytes,
 applied to every other kernel.  The per-kernel traffic is also merged into
 ``profiles/traffic.json`` keyed by workload and kernel, with the SHA-256 of
-the kernel's source files, so a reader can tell when the numbers no longer
-describe the code."""
+the code text (comments and whitespace dropped) of the kernel's source
+files, so a reader can tell when the numbers no longer describe the code."""
 from __future__ import annotations
 
 import argparse
@@ -22,6 +22,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -34,11 +35,23 @@ KERNEL_SOURCES = {
 }
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def code_text(src: str) -> str:
+    """The source with its comments removed and whitespace collapsed: what
+    decides the compiled kernel (the kernel sources hold no string literals
+    that contain comment markers)."""
+    return " ".join(_COMMENT.sub(" ", src).split())
+
+
 def source_hash(files) -> str:
+    """SHA-256 over the code text of `files`, so that a change to a comment
+    does not mark the recorded counters as stale."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()
 
 
