@@ -253,8 +253,9 @@ typedef struct moe_ws_layout {
   size_t xs;                /* [max_rows][d_model] dtype: gathered tokens.  Not
                                written when tokens_in_place is 1: bf16 tokens
                                with T * d_model * 2 < 2^31, and either the
-                               weight-streaming form with d_model a multiple of
-                               128 (not INT4) or the LDS-tiled form with k >= 4 */
+                               weight-streaming form (bf16 weights with d_model
+                               a multiple of 128, or INT4 weights) or the
+                               LDS-tiled form with k >= 4                      */
   size_t h;                 /* [max_rows][d_ff] dtype: SiLU(gate) * up         */
   size_t y;                 /* [down_splits][max_rows][d_model] float32:
                                partial expert outputs (their sum is W2 H)       */

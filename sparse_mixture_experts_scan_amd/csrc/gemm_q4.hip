@@ -245,7 +245,8 @@ __device__ __forceinline__ void stream_q4_body(
     const float* __restrict__ S0, const uint8_t* __restrict__ Q1, const float* __restrict__ S1,
     void* __restrict__ outp, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ num_tiles,
-    const int32_t* __restrict__ tile_expert, int N, int K, int G) {
+    const int32_t* __restrict__ tile_expert, int N, int K, int G,
+    const int32_t* __restrict__ row_token, int nT) {
   using QB = Q4Batch<BT, FT, GATEUP, U>;
   constexpr int NF = QB::NF, NT = QB::NT, NW = QB::NW;
   constexpr int NWAVE = kQ4Threads / kWave;
@@ -254,13 +255,19 @@ __device__ __forceinline__ void stream_q4_body(
   // tiles past those in use have expert -1; the first weight loads wait only
   // for the expert lookup
   const int tile = blockIdx.y;
+  const int row0 = tile * BT;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int lr = lane & 15, kg = lane >> 4;
+  // tokens read in place: the token of each of this lane's rows
+  int tok[NT];
+  if (row_token != nullptr) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) tok[n] = row_token[row0 + n * 16 + lr];
+  }
   const int e = tile_expert[tile];
   if (e < 0) return;
-  const int row0 = tile * BT;
   const int f0 = blockIdx.x * FT;
-  const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lr = lane & 15, kg = lane >> 4;
 
   const int ngr = K / G;
   const int cpg = G >= kQ4Chunk ? G / kQ4Chunk : 1;   // chunks per group
@@ -305,7 +312,18 @@ __device__ __forceinline__ void stream_q4_body(
   if (nb > 0) A.load_w(rw, rs, wo, so, wave, cpg, gpc, sgrp);
   const int valid_end = offsets[e] + counts[e];
   const int nvalid = max(0, min(BT, valid_end - row0));
-  const __amdgpu_buffer_rsrc_t ra = q4_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * arow);
+  // token rows past the expert's count load as zeros: outside the gathered
+  // rows' range, or (in place) at an offset past the end of x
+  __amdgpu_buffer_rsrc_t ra;
+  if (row_token != nullptr) {
+    ra = q4_rsrc(act, (uint32_t)nT * arow);
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      ao[n] = (n * 16 + lr < nvalid && tok[n] >= 0) ? (uint32_t)tok[n] * arow + kg * 64
+                                                     : 0x80000000u;
+  } else {
+    ra = q4_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * arow);
+  }
   if (nb > 0) A.load_x(ra, ao, wave);
   for (; b + 2 < nb; b += 2) {
     B.template load<true>(rw, rs, ra, wo, so, ao, wave + (b + 1) * NWAVE, U, cpg, gpc, sgrp);
@@ -386,8 +404,9 @@ __device__ __forceinline__ void stream_q4_body(
       const float *__restrict__ S1, void *__restrict__ outp,                                 \
       const int32_t *__restrict__ counts, const int32_t *__restrict__ offsets,               \
       const int32_t *__restrict__ num_tiles, const int32_t *__restrict__ tile_expert, int N, \
-      int K, int G
-#define MOE_Q4_ARGS act, Q0, S0, Q1, S1, outp, counts, offsets, num_tiles, tile_expert, N, K, G
+      int K, int G, const int32_t *__restrict__ row_token, int nT
+#define MOE_Q4_ARGS \
+  act, Q0, S0, Q1, S1, outp, counts, offsets, num_tiles, tile_expert, N, K, G, row_token, nT
 
 template <int FT, bool GATEUP, int U>
 __global__ __launch_bounds__(kQ4Threads)
@@ -438,16 +457,17 @@ void launch_dequant_int4(const void* packed, const float* scales, int64_t rows, 
 }
 
 template <int BT>
-static void gateup_q4(const Dims& D, const void* xs, const Q4Weights& Wg, const Q4Weights& Wu,
-                      void* h, const int32_t* counts, const int32_t* offsets,
-                      const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s) {
+static void gateup_q4(const Dims& D, const void* xs, const int32_t* row_token,
+                      const Q4Weights& Wg, const Q4Weights& Wu, void* h, const int32_t* counts,
+                      const int32_t* offsets, const int32_t* num_tiles,
+                      const int32_t* tile_expert, hipStream_t s) {
   constexpr int FT = MOE_Q4_FT_GU;
   dim3 grid(D.f / FT, D.max_tiles);
   auto kern = BT == 16 ? stream_q4_kernel16<FT, true, MOE_Q4_U>
                        : stream_q4_kernel32<FT, true, MOE_Q4_U>;
   kern<<<grid, kQ4Threads, 0, s>>>((const bf16_t*)xs, (const uint8_t*)Wg.q, Wg.s,
                                    (const uint8_t*)Wu.q, Wu.s, h, counts, offsets, num_tiles,
-                                   tile_expert, D.f, D.d, D.group);
+                                   tile_expert, D.f, D.d, D.group, row_token, D.T);
 }
 
 template <int BT>
@@ -460,14 +480,17 @@ static void down_q4(const Dims& D, const void* h, const Q4Weights& Wd, float* y,
                        : stream_q4_kernel32<FT, false, MOE_Q4_U>;
   kern<<<grid, kQ4Threads, 0, s>>>((const bf16_t*)h, (const uint8_t*)Wd.q, Wd.s, nullptr,
                                    nullptr, y, counts, offsets, num_tiles, tile_expert, D.d,
-                                   D.f, D.group);
+                                   D.f, D.group, nullptr, 0);
 }
 
-void launch_gateup_q4(const Dims& D, const void* xs, const Q4Weights& Wg, const Q4Weights& Wu,
-                      void* h, const int32_t* counts, const int32_t* offsets,
-                      const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s) {
-  if (D.BT == 16) gateup_q4<16>(D, xs, Wg, Wu, h, counts, offsets, num_tiles, tile_expert, s);
-  else gateup_q4<32>(D, xs, Wg, Wu, h, counts, offsets, num_tiles, tile_expert, s);
+void launch_gateup_q4(const Dims& D, const void* act, const int32_t* row_token,
+                      const Q4Weights& Wg, const Q4Weights& Wu, void* h, const int32_t* counts,
+                      const int32_t* offsets, const int32_t* num_tiles,
+                      const int32_t* tile_expert, hipStream_t s) {
+  if (D.BT == 16)
+    gateup_q4<16>(D, act, row_token, Wg, Wu, h, counts, offsets, num_tiles, tile_expert, s);
+  else
+    gateup_q4<32>(D, act, row_token, Wg, Wu, h, counts, offsets, num_tiles, tile_expert, s);
 }
 
 void launch_down_q4(const Dims& D, const void* h, const Q4Weights& Wd, float* y,

@@ -438,8 +438,11 @@ __global__ __launch_bounds__(kStreamThreads) void stream_dma_kernel(
                                   row_token, nT);
 }
 
+// bf16 tokens: the LDS-staged bf16 kernel (d_model % 128 == 0) and the INT4
+// kernel (whose group rule already makes d_model a multiple of 128) read
+// them in place; offsets into x are 32-bit
 bool stream_gathers_in_place(const Dims& D) {
-  return D.bf16 && !D.w4 && D.d % 128 == 0 && (int64_t)D.T * D.d * 2 < (int64_t(1) << 31);
+  return D.bf16 && (D.w4 || D.d % 128 == 0) && (int64_t)D.T * D.d * 2 < (int64_t(1) << 31);
 }
 
 template <typename T, int BT>

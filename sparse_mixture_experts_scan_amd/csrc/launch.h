@@ -101,9 +101,11 @@ void launch_quantize_int4(const void* W, bool bf16, int64_t rows, int N, int K, 
                           void* packed, float* scales, hipStream_t s);
 void launch_dequant_int4(const void* packed, const float* scales, int64_t rows, int N, int K,
                          int G, void* out, hipStream_t s);
-void launch_gateup_q4(const Dims& D, const void* xs, const Q4Weights& Wg, const Q4Weights& Wu,
-                      void* h, const int32_t* counts, const int32_t* offsets,
-                      const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s);
+// row_token as for launch_gateup_stream
+void launch_gateup_q4(const Dims& D, const void* act, const int32_t* row_token,
+                      const Q4Weights& Wg, const Q4Weights& Wu, void* h, const int32_t* counts,
+                      const int32_t* offsets, const int32_t* num_tiles,
+                      const int32_t* tile_expert, hipStream_t s);
 void launch_down_q4(const Dims& D, const void* h, const Q4Weights& Wd, float* y,
                     const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                     const int32_t* tile_expert, hipStream_t s);

@@ -302,7 +302,8 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
     W_down = wd + 2 * mat;
   }
   if (q4 && L.gemm_variant == 0)
-    moe::launch_gateup_q4(D, xs, q4[0], q4[1], h, counts, offsets, num_tiles, tile_expert, s);
+    moe::launch_gateup_q4(D, gather ? tok : xs, gather ? row_token : nullptr, q4[0], q4[1], h,
+                          counts, offsets, num_tiles, tile_expert, s);
   else if (L.gemm_variant == 1)
     moe::launch_gateup_tile(D, gather ? tok : xs, gather ? row_token : nullptr, W_gate, W_up,
                             h, counts, offsets, num_tiles, tile_expert, s);

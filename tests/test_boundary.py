@@ -118,11 +118,13 @@ def test_workspace_layout_is_consistent():
     assert moe.moe_ffn_workspace_layout(4096, 4096, 14336, 8, 2, 0).down_splits == 2
     assert moe.moe_ffn_workspace_layout(4096, 4096, 3584, 64, 8, 0).down_splits == 1
     assert moe.moe_ffn_workspace_layout(16, 4096, 14336, 8, 2, 0).down_splits == 1
-    # which gate/up GEMMs read the tokens in place (no Xs): bf16 weight-
-    # streaming with d_model % 128 == 0, and the tiled form with k >= 4
+    # which gate/up GEMMs read the tokens in place (no Xs): weight-streaming
+    # with bf16 weights and d_model % 128 == 0 or with INT4 weights, and the
+    # tiled form with k >= 4
     inplace = {(16, 4096, 14336, 8, 2, 0): 1, (4096, 4096, 14336, 8, 2, 0): 0,
                (4096, 4096, 3584, 64, 8, 0): 1, (64, 128, 512, 8, 2, 1): 0,
-               (33, 192, 320, 6, 3, 0): 0, (16, 4096, 14336, 8, 2, 2): 0}
+               (33, 192, 320, 6, 3, 0): 0, (16, 4096, 14336, 8, 2, 2): 1,
+               (4096, 4096, 14336, 8, 2, 2): 0}
     for shape, want in inplace.items():
         lay = moe.moe_ffn_workspace_layout(*shape)
         assert (lay.tokens_in_place, lay.reserved) == (want, 0), shape
