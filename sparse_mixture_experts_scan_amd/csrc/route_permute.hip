@@ -85,7 +85,8 @@ constexpr int kRouterUnroll = 4;         // k-groups whose loads are issued toge
 // the block histogram.
 __device__ inline void select_topk_token(const float* srow, int E, int k, size_t t,
                                          int32_t* __restrict__ idx_out,
-                                         float* __restrict__ w_out, int* hist) {
+                                         float* __restrict__ w_out, int* hist,
+                                         int* s_sel = nullptr) {
   uint64_t taken = 0;
   float sel[MOE_MAX_TOPK];
   int sid[MOE_MAX_TOPK];
@@ -120,6 +121,7 @@ __device__ inline void select_topk_token(const float* srow, int E, int k, size_t
       idx_out[t * k + j] = sid[j];
       w_out[t * k + j] = z[j] / sum;
       atomicAdd(&hist[sid[j]], 1);
+      if (s_sel) s_sel[t * k + j] = sid[j];
     }
 }
 
@@ -340,6 +342,111 @@ __device__ __forceinline__ void scatter_rows_block(
   sTok[tid] = t;
 }
 
+// Workgroup barrier for data exchanged through LDS only: unlike
+// __syncthreads it does not wait for the block's global stores to complete.
+__device__ __forceinline__ void lds_only_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The select pass of a batch that fits one router block, run by all
+// kRouterThreads threads once slog holds the final scores: top-k and
+// softmax, the router statistics, the expert scan and (sa.tok_row set) the
+// row maps, with the same arithmetic as select_topk_token, block_prob_sums,
+// expert_scan_block and scatter_rows_block for one block.  Every value that
+// a later phase needs stays in LDS and the barriers are LDS-only, so the
+// outputs' global stores drain once, at the end of the kernel.
+__device__ __forceinline__ void select_single_block(
+    const float (*slog)[65], int* hist, int nT, int E, int k, int BT, int max_rows,
+    int max_tiles, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+    int32_t* __restrict__ blk_counts, float* __restrict__ blk_prob, const ScanArgs& sa) {
+  constexpr int TB = kRouterTokens;
+  constexpr int NWAVE = kRouterThreads / kWave;
+  __shared__ int s_sel[TB * MOE_MAX_TOPK];
+  __shared__ int s_off[65];
+  __shared__ float smax[TB], sinv[TB], s_p[64];
+  __shared__ int wcnt[NWAVE][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < nT) select_topk_token(slog[tid], E, k, (size_t)tid, idx_out, w_out, hist, s_sel);
+  if (blk_prob && tid < TB) {            // full-softmax constants of each token
+    float m = slog[tid][0];
+    for (int e = 1; e < E; ++e) m = fmaxf(m, slog[tid][e]);
+    float z = 0.f;
+    for (int e = 0; e < E; ++e) z += expf(slog[tid][e] - m);
+    smax[tid] = m;
+    sinv[tid] = 1.f / z;
+  }
+  lds_only_barrier();
+  // expert scan: segments padded to BT rows
+  if (tid == 0) {
+    int off = 0;
+    for (int x = 0; x < E; ++x) {
+      s_off[x] = off;
+      off += (hist[x] + BT - 1) / BT * BT;
+    }
+    s_off[E] = off;
+  }
+  if (blk_prob && tid < E) {              // p_i: the mean full-softmax probability
+    float acc = 0.f;
+    for (int t = 0; t < TB; ++t)
+      if (t < nT) acc += expf(slog[t][tid] - smax[t]) * sinv[t];
+    blk_prob[tid] = acc;
+    s_p[tid] = acc / (float)nT;
+    if (sa.prob_out) sa.prob_out[tid] = s_p[tid];
+  }
+  lds_only_barrier();
+  if (tid < E) {
+    sa.counts[tid] = hist[tid];
+    if (sa.counts_out) sa.counts_out[tid] = hist[tid];
+    blk_counts[tid] = 0;                  // the one block's per-expert bases
+  }
+  if (tid <= E) sa.offsets[tid] = s_off[tid];
+  const int P = s_off[E];
+  const int ntiles = P / BT;
+  if (tid == 0) *sa.num_tiles = ntiles;
+  for (int i = tid; i < max_tiles; i += kRouterThreads) {
+    int ex = -1;
+    if (i < ntiles) {
+      const int r = i * BT;
+      ex = 0;
+      while (s_off[ex + 1] <= r) ++ex;
+    }
+    sa.tile_expert[i] = ex;
+  }
+  for (int x = 0; x < E; ++x)
+    for (int r = s_off[x] + hist[x] + tid; r < s_off[x + 1]; r += kRouterThreads)
+      sa.row_token[r] = -1;
+  for (int r = P + tid; r < max_rows; r += kRouterThreads) sa.row_token[r] = -1;
+  if (blk_prob && tid == 0 && sa.loss_out) {   // N * sum_i f_i p_i
+    float L = 0.f;
+    for (int x = 0; x < E; ++x) L += ((float)hist[x] / (float)nT) * s_p[x];
+    *sa.loss_out = (float)E * L;
+  }
+  if (sa.tok_row == nullptr) return;
+  // row maps: rank of pair (t, j) among the earlier pairs on its expert
+  const int np = TB * k;
+  int e = -1, t = -1;
+  if (tid < np) {
+    t = tid / k;
+    if (t < nT) e = s_sel[tid];
+    else t = -1;
+  }
+  int rank_w = 0;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  for (int ex = 0; ex < E; ++ex) {
+    const uint64_t msk = __ballot(e == ex);
+    if (e == ex) rank_w = __popcll(msk & lt);
+    if (lane == 0) wcnt[wave][ex] = __popcll(msk);
+  }
+  lds_only_barrier();
+  if (e >= 0) {
+    int rank = rank_w;
+    for (int w = 0; w < wave; ++w) rank += wcnt[w][e];
+    const int row = s_off[e] + rank;
+    sa.tok_row[tid] = row;
+    sa.row_token[row] = t;
+  }
+}
+
 // Second pass of a split router: per token, the split partial scores are
 // added in split order (deterministic), the bias added, then top-k/softmax.
 // With a single router block (do_scan) the same block then runs the expert
@@ -381,6 +488,11 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
   if (logits_out)
     for (int i = tid; i < TB * E; i += kSelectThreads)
       if (t0 + i / E < nT) logits_out[(size_t)(t0 + i / E) * E + i % E] = slog[i / E][i % E];
+  if (do_scan) {   // one router block: select, statistics, scan and row maps here
+    select_single_block(slog, hist, nT, E, k, BT, max_rows, max_tiles, idx_out, w_out,
+                        blk_counts, blk_prob, sa);
+    return;
+  }
   if (tid < TB && t0 + tid < nT)
     select_topk_token(slog[tid], E, k, (size_t)(t0 + tid), idx_out, w_out, hist);
   __syncthreads();
@@ -388,18 +500,6 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
   if (blk_prob) {
     __shared__ float smax[TB], sinv[TB];
     block_prob_sums(slog, t0, nT, E, smax, sinv, blk_prob + (size_t)blockIdx.x * E);
-  }
-  if (do_scan) {
-    __syncthreads();
-    expert_scan_block(blk_counts, 1, E, Epow2, BT, max_rows, max_tiles, sa.counts, sa.offsets,
-                      sa.num_tiles, sa.tile_expert, sa.row_token, sa.counts_out, nT, blk_prob,
-                      sa.prob_out, sa.loss_out);
-    if (sa.tok_row != nullptr) {   // the row maps too (the GEMM reads tokens in place)
-      __shared__ int sRow[kRouterThreads], sTok[kRouterThreads];
-      __syncthreads();
-      scatter_rows_block(idx_out, blk_counts, sa.offsets, nT, E, k, 0, true, sa.tok_row,
-                         sa.row_token, sRow, sTok);
-    }
   }
 }
 
