@@ -670,7 +670,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     s_w[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < d / 4; c += 256) {
+  // blockIdx.y: column slice (small T spreads a token over several blocks)
+  for (int c = blockIdx.y * 256 + threadIdx.x; c < d / 4; c += 256 * gridDim.y) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
       float4 v = reinterpret_cast<const float4*>(y + (size_t)s_row[j] * d)[c];
@@ -800,11 +801,15 @@ void launch_empty_stats(int E, int32_t* counts_out, float* prob_out, float* loss
 void launch_combine(const Dims& D, const float* y, const int32_t* tok_row, const float* w,
                     const void* resid, void* out, hipStream_t s) {
   const size_t stride = (size_t)D.max_rows * D.d;
+  // column slices of 256 float4 chunks while the tokens alone give few blocks
+  int cs = 1;
+  while (D.T * cs < 256 && cs * 2 * 256 * 4 <= D.d) cs *= 2;
+  const dim3 grid(D.T, cs);
   if (D.bf16)
-    combine_kernel<bf16_t><<<D.T, 256, 0, s>>>(y, tok_row, w, D.d, D.k, D.down_splits, stride,
+    combine_kernel<bf16_t><<<grid, 256, 0, s>>>(y, tok_row, w, D.d, D.k, D.down_splits, stride,
                                                 (const bf16_t*)resid, (bf16_t*)out);
   else
-    combine_kernel<float><<<D.T, 256, 0, s>>>(y, tok_row, w, D.d, D.k, D.down_splits, stride,
+    combine_kernel<float><<<grid, 256, 0, s>>>(y, tok_row, w, D.d, D.k, D.down_splits, stride,
                                                (const float*)resid, (float*)out);
 }
 
