@@ -460,7 +460,12 @@ __device__ __forceinline__ void select_single_block(
 // scan (a2, part 1) on the counts it has just written, which saves a launch,
 // and with sa.tok_row set the row maps as well (no scatter launch).
 constexpr int kSelectThreads = 256;
-constexpr int kMaxRouterSplits = 16;
+// d_model splits of the score GEMM at most (measured on MI355X at decode,
+// one token block: 32 splits take the router stage 1 us longer than 16)
+#ifndef MOE_ROUTER_MAX_SPLITS
+#define MOE_ROUTER_MAX_SPLITS 16
+#endif
+constexpr int kMaxRouterSplits = MOE_ROUTER_MAX_SPLITS;
 
 __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int nT, int E, int k,
