@@ -20,6 +20,9 @@ CASES = [
     MoEConfig("stats_fused", 5000, 256, 256, 16, 2, "bf16"),        # many token blocks
     MoEConfig("stats_split", 100, 512, 128, 64, 8, "bf16"),         # router split over d_model
     MoEConfig("stats_f32", 64, 128, 512, 8, 2, "f32"),
+    # one router block: the select pass also runs the statistics and the scan
+    MoEConfig("stats_single_block", 16, 512, 256, 8, 2, "bf16"),
+    MoEConfig("stats_single_e64", 27, 256, 256, 64, 8, "bf16"),
 ]
 
 
