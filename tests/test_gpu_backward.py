@@ -70,6 +70,8 @@ CASES = [
     (MoEConfig("bwd_single", 1, 128, 128, 4, 2, "bf16"), 0.1),
     (MoEConfig("bwd_top1", 50, 128, 256, 4, 1, "bf16"), 0.0),
     (MoEConfig("bwd_tiles", 700, 512, 640, 8, 2, "bf16"), 0.01),   # several 128-row tiles
+    # one router block (decode-sized): routing, scan and scores from one select pass
+    (MoEConfig("bwd_decode", 16, 256, 384, 8, 2, "bf16"), 0.02),
     # widths that are multiples of 256: the 256 x 256 ping-pong GEMMs (k-strided operands
     # read through transposing LDS loads), one launch per contraction
     (MoEConfig("bwd256_small", 64, 256, 256, 8, 2, "bf16"), 0.0),
@@ -79,6 +81,7 @@ CASES = [
     (MoEConfig("bwd256_tiles", 900, 512, 768, 8, 2, "bf16"), 0.01),  # several 256-row tiles
     (MoEConfig("bwd256_many_e", 40, 256, 256, 64, 2, "bf16"), 0.0),  # experts left empty
     (MoEConfig("bwd256_multi", 700, 256, 256, 4, 2, "bf16"), 0.01),  # two row tiles per expert
+    (MoEConfig("bwd256_decode", 24, 256, 256, 8, 2, "bf16"), 0.01),  # one router block
 ]
 
 
