@@ -539,8 +539,12 @@ __device__ __forceinline__ void expert_scan_block(
   const int per = (nblk + C - 1) / C;
   const int b0 = min(nblk, c * per), b1 = min(nblk, b0 + per);
   int sum = 0;
-  if (e < E)
+  // unrolled so that the loads of a chunk are in flight together (with 64
+  // experts a thread walks 32 blocks per chunk)
+  if (e < E) {
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) sum += blk[(size_t)b * E + e];
+  }
   part[tid] = sum;
   __syncthreads();
   if (tid < E) {
@@ -555,6 +559,7 @@ __device__ __forceinline__ void expert_scan_block(
   __syncthreads();
   if (e < E) {
     int run = part[tid];
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) {
       const int v = blk[(size_t)b * E + e];
       blk[(size_t)b * E + e] = run;
