@@ -451,13 +451,17 @@ def moe_backward_entries(x, W_router, W_gate, W_up, W_down, dout, k, tokens, fea
         if not mine and not sel:
             continue
         W1, W3, W2 = to_f64(W_gate[e]), to_f64(W_up[e]), to_f64(W_down[e])
-        for n, j in sel:                                   # dx of sampled tokens
-            t = tokens[n]
-            a, b = W1 @ xf[t], W3 @ xf[t]
+        if sel:                                            # dx of sampled tokens
+            ns = np.array([n for n, _ in sel])
+            js = np.array([j for _, j in sel])
+            ts = tokens[ns]
+            Xt = xf[ts]                                    # one row per (token, slot)
+            a, b = Xt @ W1.T, Xt @ W3.T
             h = silu(a) * b
-            dg[n, j] = go_tok[n] @ (W2 @ h)
-            dh = W2.T @ (g[t, j] * go_tok[n])
-            dx[n] += W1.T @ (dh * b * silu_grad(a)) + W3.T @ (dh * silu(a))
+            dg[ns, js] = (go_tok[ns] * (h @ W2.T)).sum(axis=1)
+            dh = (g[ts, js][:, None] * go_tok[ns]) @ W2
+            # a token routes to e in at most one slot, so the rows of ns differ
+            dx[ns] += (dh * b * silu_grad(a)) @ W1 + (dh * silu(a)) @ W3
         if mine:
             rows = np.nonzero((idx == e).any(axis=1))[0]   # tokens routed to e
             slot = np.argmax(idx[rows] == e, axis=1)
