@@ -130,8 +130,9 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate,
  * The router scores the normalised tokens in fp32 (from x, norm_weight and
  * the per-token 1/rms); the experts take the normalised tokens rounded to
  * the element type; the residual is added in fp32 before the single rounding
- * of out.  out must not alias x.  Other arguments, outputs, limits and errors
- * as moe_ffn_forward; the same workspace size applies.
+ * of out.  out must not alias x.  A caller workspace is sized by
+ * moe_block_workspace_size (the layer's plus the normalised tokens and their
+ * 1/rms).  Other arguments, outputs, limits and errors as moe_ffn_forward.
  */
 int moe_block_forward(const void* x, const float* norm_weight, float eps, const float* W_router,
                       const void* W_gate, const void* W_up, const void* W_down, void* out,
@@ -216,10 +217,16 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate,
 size_t moe_ffn_backward_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
                                        int32_t k);
 
-/* Bytes of workspace moe_ffn_forward needs for this shape (0 if the shape is
+/* Bytes of workspace moe_ffn_forward (dtype MOE_BF16 or MOE_F32) or
+ * moe_ffn_forward_int4 (MOE_W4A16) needs for this shape (0 if the shape is
  * invalid or unsupported; T = 0 is sized as T = 1). */
 size_t moe_ffn_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
                               int32_t k, int32_t dtype);
+
+/* Bytes of workspace moe_block_forward needs (dtype MOE_BF16 or MOE_F32; 0 if
+ * the shape or dtype is invalid or unsupported; T = 0 is sized as T = 1). */
+size_t moe_block_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
+                                int32_t k, int32_t dtype);
 
 /*
  * Where the forward pass keeps its intermediates inside a caller workspace,
@@ -250,19 +257,21 @@ typedef struct moe_ws_layout {
   size_t tile_expert;       /* [max_rows / block_rows] expert of each tile     */
   size_t row_token;         /* [max_rows] token of each permuted row or -1     */
   size_t tok_row;           /* [T][k] permuted row of each (token, slot)       */
-  size_t xs;                /* [max_rows][d_model] dtype: gathered tokens.  Not
-                               written when tokens_in_place is 1: bf16 tokens
-                               with T * d_model * 2 < 2^31, and either the
-                               weight-streaming form (bf16 weights with d_model
-                               a multiple of 128, or INT4 weights) or the
-                               LDS-tiled form with k >= 4                      */
+  size_t xs;                /* [max_rows][d_model] dtype: gathered tokens.
+                               0 bytes (not used) when tokens_in_place is 1:
+                               bf16 tokens with T * d_model * 2 < 2^31, and
+                               either the weight-streaming form (bf16 weights
+                               with d_model a multiple of 128, or INT4
+                               weights) or the LDS-tiled form with k >= 4      */
   size_t h;                 /* [max_rows][d_ff] dtype: SiLU(gate) * up         */
   size_t y;                 /* [down_splits][max_rows][d_model] float32:
                                partial expert outputs (their sum is W2 H)       */
   size_t block_probs;       /* [router_blocks][E] float32: per-block sums of the
                                full-softmax probabilities (router statistics)  */
-  size_t norm_rs;           /* [T] float32: 1/rms of each token (block wrapper)  */
-  size_t xn;                /* [T][d_model] dtype: RMS-normalised tokens        */
+  size_t norm_rs;           /* [T] float32: 1/rms of each token; block wrapper
+                               only (0 bytes in the layer's layout)            */
+  size_t xn;                /* [T][d_model] dtype: RMS-normalised tokens; block
+                               wrapper only (0 bytes in the layer's layout)    */
   size_t router_partial;    /* router scratch: partial scores when the score GEMM
                                is split over d_model (few token blocks)        */
   size_t wdeq;              /* MOE_W4A16 with the LDS-tiled form only: the three
@@ -273,6 +282,9 @@ typedef struct moe_ws_layout {
 
 int moe_ffn_workspace_layout(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
                              int32_t k, int32_t dtype, moe_ws_layout_t* layout);
+/* The same for moe_block_forward (dtype MOE_BF16 or MOE_F32). */
+int moe_block_workspace_layout(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
+                               int32_t k, int32_t dtype, moe_ws_layout_t* layout);
 
 /* Static, human-readable text for a status code. */
 const char* moe_status_string(int status);

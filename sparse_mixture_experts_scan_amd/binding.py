@@ -17,8 +17,8 @@ MOE_BF16, MOE_F32, MOE_W4A16 = 0, 1, 2
 
 EXPORTED = ("moe_opts_init", "moe_ffn_forward", "moe_block_forward", "moe_quantize_int4",
             "moe_ffn_forward_int4", "moe_ffn_backward", "moe_ffn_backward_workspace_size",
-            "moe_ffn_workspace_size",
-            "moe_ffn_workspace_layout", "moe_status_string", "moe_last_error",
+            "moe_ffn_workspace_size", "moe_block_workspace_size",
+            "moe_ffn_workspace_layout", "moe_block_workspace_layout", "moe_status_string", "moe_last_error",
             "moe_release", "moe_version")
 
 
@@ -97,6 +97,11 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_workspace_layout.argtypes = [i64, i64, i64, i32, i32, i32,
                                                ctypes.POINTER(MoeWsLayout)]
         L.moe_ffn_workspace_layout.restype = ctypes.c_int
+        L.moe_block_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
+        L.moe_block_workspace_size.restype = sz
+        L.moe_block_workspace_layout.argtypes = [i64, i64, i64, i32, i32, i32,
+                                                 ctypes.POINTER(MoeWsLayout)]
+        L.moe_block_workspace_layout.restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_last_error.argtypes = []
@@ -166,6 +171,18 @@ def moe_ffn_workspace_layout(T, d_model, d_ff, E, k, dtype=MOE_BF16) -> MoeWsLay
     st = lib().moe_ffn_workspace_layout(T, d_model, d_ff, E, k, dtype, ctypes.byref(lay))
     if st != MOE_OK:
         raise MoeError(st, "moe_ffn_workspace_layout")
+    return lay
+
+
+def moe_block_workspace_size(T, d_model, d_ff, E, k, dtype=MOE_BF16) -> int:
+    return lib().moe_block_workspace_size(T, d_model, d_ff, E, k, dtype)
+
+
+def moe_block_workspace_layout(T, d_model, d_ff, E, k, dtype=MOE_BF16) -> MoeWsLayout:
+    lay = MoeWsLayout()
+    st = lib().moe_block_workspace_layout(T, d_model, d_ff, E, k, dtype, ctypes.byref(lay))
+    if st != MOE_OK:
+        raise MoeError(st, "moe_block_workspace_layout")
     return lay
 
 

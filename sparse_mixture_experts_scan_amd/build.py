@@ -1,9 +1,11 @@
-"""Builds libmoe_ffn.so in-tree with hipcc for gfx950.
+"""Builds libmoe_ffn.so (the layer) and libmoe_probe.so (the bandwidth and
+MFMA microbenchmarks the benchmark reports as measured peaks) in-tree with
+hipcc for gfx950.
 
     python -m sparse_mixture_experts_scan_amd.build [-v]
 
-Each HIP source is compiled to an object in parallel, then linked into one
-shared library next to this file.  Always rebuilds (it is the "does it build"
+Each HIP source is compiled to an object in parallel, then linked into the
+shared libraries next to this file.  Always rebuilds (it is the "does it build"
 check as well as the build)."""
 from __future__ import annotations
 
@@ -20,9 +22,11 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libmoe_ffn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+PROBE_LIB_PATH = os.path.join(PKG, "libmoe_probe.so")
+PROBE_SOURCES = ["peak_probe.hip"]
 SOURCES = ["route_permute.hip", "gemm_stream.hip", "gemm_tile.hip", "gemm_q4.hip", "gemm_bwd.hip",
            "gemm_bwd_tile.hip",
-           "moe_ffn.hip"]
+           "moe_ffn.hip", "plan.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are switched off for all device code; hipcc's host pass
@@ -55,17 +59,19 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
-    objs = []
     cmds = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
-        objs.append(obj)
-        cmds.append([cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+
+    def obj_of(src):
+        return os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    for src in SOURCES + PROBE_SOURCES:
+        cmds.append([cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj_of(src)])
     with ThreadPoolExecutor(min(len(cmds), 8)) as pool:
         list(pool.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB_PATH + ".tmp"
-    _run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB_PATH)
+    for path, srcs in ((LIB_PATH, SOURCES), (PROBE_LIB_PATH, PROBE_SOURCES)):
+        tmp = path + ".tmp"
+        _run([cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *map(obj_of, srcs), "-o", tmp],
+             verbose)
+        os.replace(tmp, path)
     return LIB_PATH
 
 

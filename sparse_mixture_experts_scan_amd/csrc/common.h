@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "moe_ffn.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -16,7 +17,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint16_t bf16_t;  // storage type of bfloat16 data
 
 constexpr int kWave = 64;
-constexpr int kRouterTokens = 32;   // tokens per router / scatter block
 constexpr int kRouterThreads = 256;
 
 // Element-type traits: how a 16-byte chunk of K is fed to 16x16 MFMA.
@@ -60,6 +60,38 @@ template <> struct Elem<float> {
 };
 
 __device__ inline float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// ---- buffer loads and the waits around them (gfx950)
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kBufferCfg = 0x00020000;  // raw buffer, 32-bit data format
+
+// A raw buffer resource of `bytes` bytes from `base`: loads past the range
+// return zeros.  Resources must sit in scalar registers, so every field is
+// made provably wave-uniform; otherwise each load is wrapped in a per-lane
+// loop.
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, kBufferCfg);
+}
+
+// Wait until at most N of this wave's vector-memory operations (loads, LDS
+// DMA loads) are outstanding; the LDS and export counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// All of this wave's LDS operations done, then the workgroup barrier.  No
+// memory fence: unlike __syncthreads it does not wait for global stores, and
+// LDS DMA completion is waited for explicitly with wait_vmcnt.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ inline void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }

@@ -33,9 +33,6 @@ namespace {
 
 // Tile shape: kGM x kGN outputs per workgroup, K in steps of kGK, kGWM x kGWN
 // waves each holding (kGM / kGWM) x (kGN / kGWN) in 32x32 fragments.
-#ifndef MOE_BG_M
-#define MOE_BG_M 256
-#endif
 #ifndef MOE_BG_N
 #define MOE_BG_N 128
 #endif
@@ -57,16 +54,7 @@ constexpr int kGLd = kGK + 8;                // LDS row pitch in elements
 constexpr int kGFA = kGM / kGWM / 32;        // 32-row fragments per wave (M)
 constexpr int kGFB = kGN / kGWN / 32;        // 32-column fragments per wave (N)
 static_assert(kGFA >= 1 && kGFB >= 1 && kGK % 16 == 0, "tile shape");
-constexpr int kBufCfg = 0x00020000;
 
-__device__ inline __amdgpu_buffer_rsrc_t g_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, kBufCfg);
-}
 
 __device__ __forceinline__ uint4 g_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
@@ -168,11 +156,11 @@ __global__ __launch_bounds__(kGT) void grouped_gemm_kernel(
     rows = tb_rows[i];
     kn = K;
     // A: rows m0 .. m0 + rows (k contiguous), past them zeros
-    ra = g_rsrc(A + (size_t)m0 * lda, (uint32_t)rows * lda * 2);
+    ra = buffer_rsrc(A + (size_t)m0 * lda, (uint32_t)rows * lda * 2);
     const bf16_t* Be = B + (size_t)e * b_estride;
     // (columns past N read as zeros or as a neighbour's data; never stored)
-    if constexpr (KCB) rb = g_rsrc(Be + (size_t)n0 * ldb, (uint32_t)min(kGN, N - n0) * ldb * 2);
-    else rb = g_rsrc(Be, (uint32_t)K * ldb * 2);
+    if constexpr (KCB) rb = buffer_rsrc(Be + (size_t)n0 * ldb, (uint32_t)min(kGN, N - n0) * ldb * 2);
+    else rb = buffer_rsrc(Be, (uint32_t)K * ldb * 2);
     c_base = (size_t)m0 * ldc;
   } else {
     const int e = blockIdx.z;
@@ -180,8 +168,8 @@ __global__ __launch_bounds__(kGT) void grouped_gemm_kernel(
     rows = kGM;
     kn = counts[e];
     const int r0 = offsets[e];
-    ra = g_rsrc(A + (size_t)r0 * lda, (uint32_t)kn * lda * 2);
-    rb = g_rsrc(B + (size_t)r0 * ldb, (uint32_t)kn * ldb * 2);
+    ra = buffer_rsrc(A + (size_t)r0 * lda, (uint32_t)kn * lda * 2);
+    rb = buffer_rsrc(B + (size_t)r0 * ldb, (uint32_t)kn * ldb * 2);
     c_base = (size_t)e * c_estride + (size_t)m0 * ldc;
   }
   const uint32_t lda_b = (uint32_t)lda * 2, ldb_b = (uint32_t)ldb * 2;
@@ -488,10 +476,7 @@ void launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
                                         (int)(bytes - n16 * 16));
 }
 
-constexpr int kBwdRouterSlices = 32;
 
-int bwd_gemm_tile_rows() { return kGM; }
-int bwd_router_slices() { return kBwdRouterSlices; }
 
 void launch_bwd_tile_table(const Dims& D, const int32_t* counts, const int32_t* offsets,
                            int max_tiles, int32_t* tb_count, int32_t* tb_exp, int32_t* tb_row0,

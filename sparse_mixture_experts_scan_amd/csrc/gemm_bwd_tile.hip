@@ -55,29 +55,10 @@ constexpr int kBFeatGroup = MOE_BWD_FEAT_GROUP;  // feature tiles per XCD-local 
 constexpr int kKCRow = kBK * 2;             // KC: bytes per LDS row (128)
 constexpr int kKSRow = kBT * 2;             // KS: bytes per LDS row (512)
 static_assert(5 * kBOper <= 160 * 1024, "LDS buffers exceed 160 KiB");
-constexpr int kBufCfg = 0x00020000;
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-__device__ inline __amdgpu_buffer_rsrc_t b_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, kBufCfg);
-}
-
-template <int N>
-__device__ __forceinline__ void b_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-__device__ __forceinline__ void b_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 __device__ inline int kc_key(int r) { return (r ^ (r >> 3)) & 7; }
 
@@ -157,7 +138,7 @@ __device__ __forceinline__ void b_issue(const BCtx& c, char* buf, int s) {
     int kk0 = k0, kend = c.split_k;
     if (k0 >= c.split_k) { base = c.ks_base1; kk0 = k0 - c.split_k; kend = c.kn - c.split_k; }
     const int rows = max(0, min(kBK, kend - kk0));
-    const __amdgpu_buffer_rsrc_t r = b_rsrc(base + (size_t)kk0 * c.ld_bytes, rows * c.ld_bytes);
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(base + (size_t)kk0 * c.ld_bytes, rows * c.ld_bytes);
 #pragma unroll
     for (int j = 0; j < kBSlots; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(buf + (c.dma_base + j) * 1024), 16,
@@ -228,13 +209,13 @@ __device__ __forceinline__ void b_stage(const BCtx& c, char* pcur, char* pnxt, c
   if constexpr (SWAP) b_load<KSA, KSB, NBV>(c, rcur, pcur, fa, fb);
   else b_load<KSA, KSB, NBV>(c, pcur, rcur, fa, fb);
   if (ISSUE_R && g == 1) b_issue<SWAP ? KSA : KSB>(c, rnew, s + 2);
-  b_wait_vmcnt<XWAIT>();
-  b_barrier();
+  wait_vmcnt<XWAIT>();
+  lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
   b_mfma_stage<NBV>(fa, fb, acc);
   __builtin_amdgcn_sched_barrier(0);
-  b_wait_vmcnt<0>();
-  b_barrier();
+  wait_vmcnt<0>();
+  lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -250,9 +231,9 @@ __device__ __forceinline__ void b_main_loop(const BCtx& c, char* a0, char* a1, c
     b_issue<SWAP ? KSA : KSB>(c, bring, 0);
     b_issue<SWAP ? KSA : KSB>(c, bring + kBOper, 1);
   }
-  b_wait_vmcnt<0>();
-  b_barrier();
-  if (g == 1) b_barrier();
+  wait_vmcnt<0>();
+  lds_barrier();
+  if (g == 1) lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
   int bs = 0;
   auto bb = [&](int i) { return bring + i * kBOper; };
@@ -269,7 +250,7 @@ __device__ __forceinline__ void b_main_loop(const BCtx& c, char* a0, char* a1, c
   b_stage<KSA, KSB, SWAP, NBV, true, false, 0>(c, a0, a1, bb(bs), nullptr, s, g, fa, fb, acc);
   b_stage<KSA, KSB, SWAP, NBV, false, false, 0>(c, a1, a0, bb(inc3(bs)), nullptr, s + 1, g, fa,
                                                 fb, acc);
-  if (g == 0) b_barrier();
+  if (g == 0) lds_barrier();
 }
 
 // LDS byte offset, inside a KS tile, of the first 8-byte piece lane l reads
@@ -358,14 +339,14 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
                                                    first_row * p.lda + (size_t)a_tile * kBT);
       }
     } else {
-      c.r = b_rsrc(Am + (size_t)a_tile * kBT * p.lda, kBT * c.ld_bytes);
+      c.r = buffer_rsrc(Am + (size_t)a_tile * kBT * p.lda, kBT * c.ld_bytes);
     }
   } else {
     // B: brow tile `bt`
     c.ld_bytes = (uint32_t)p.ldb * 2;
     if constexpr (MODE == 0) {
       // token rows row0 .. + rows (k contiguous); past them zeros
-      c.r = b_rsrc(p.B + (size_t)row0 * p.ldb + (size_t)part * p.K,
+      c.r = buffer_rsrc(p.B + (size_t)row0 * p.ldb + (size_t)part * p.K,
                    (uint32_t)rows * c.ld_bytes);
     } else {
       c.ks_base = reinterpret_cast<const char*>(p.B + (size_t)p.offsets[e] * p.ldb +
@@ -549,8 +530,7 @@ BgArgs bg_rows_args(const int32_t* tb_count, const int32_t* tb_exp, const int32_
 
 }  // namespace
 
-bool bwd_tile_shape_ok(int64_t d, int64_t f) { return d % kBT == 0 && f % kBT == 0; }
-int bwd_tile_rows() { return kBT; }
+static_assert(kBT == kBwdTileBT, "the plan's tile extent");
 
 // a | b = [W1 | W3] x_r: one launch, aidx over 2 d_ff (W1's tiles, then W3's)
 void launch_bwd_recompute(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* ab,

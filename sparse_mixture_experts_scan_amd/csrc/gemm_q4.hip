@@ -28,20 +28,10 @@ namespace moe {
 namespace {
 
 constexpr int kQ4Threads = 256;
-constexpr int kQ4Chunk = 128;          // K per 16-byte weight load of one 4-lane row group
-constexpr int kBufCfg = 0x00020000;    // raw buffer, 32-bit data format
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-__device__ inline __amdgpu_buffer_rsrc_t q4_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, kBufCfg);
-}
 
 __device__ __forceinline__ uint4 q4_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
                                            uint32_t soff) {
@@ -276,11 +266,11 @@ __device__ __forceinline__ void stream_q4_body(
   const uint32_t qrow = (uint32_t)K / 2, sgrp = (uint32_t)N * 4;
   const uint32_t sbytes = (uint32_t)(ngr - 1) * sgrp + FT * 4;
   __amdgpu_buffer_rsrc_t rw[NW], rs[NW];
-  rw[0] = q4_rsrc(Q0 + ((size_t)e * N + f0) * qrow, FT * qrow);
-  rs[0] = q4_rsrc(S0 + (size_t)e * ngr * N + f0, sbytes);
+  rw[0] = buffer_rsrc(Q0 + ((size_t)e * N + f0) * qrow, FT * qrow);
+  rs[0] = buffer_rsrc(S0 + (size_t)e * ngr * N + f0, sbytes);
   if constexpr (GATEUP) {
-    rw[1] = q4_rsrc(Q1 + ((size_t)e * N + f0) * qrow, FT * qrow);
-    rs[1] = q4_rsrc(S1 + (size_t)e * ngr * N + f0, sbytes);
+    rw[1] = buffer_rsrc(Q1 + ((size_t)e * N + f0) * qrow, FT * qrow);
+    rs[1] = buffer_rsrc(S1 + (size_t)e * ngr * N + f0, sbytes);
   }
   const uint32_t arow = (uint32_t)K * 2;
   uint32_t wo[NF], so[NF], ao[NT];
@@ -316,13 +306,13 @@ __device__ __forceinline__ void stream_q4_body(
   // rows' range, or (in place) at an offset past the end of x
   __amdgpu_buffer_rsrc_t ra;
   if (row_token != nullptr) {
-    ra = q4_rsrc(act, (uint32_t)nT * arow);
+    ra = buffer_rsrc(act, (uint32_t)nT * arow);
 #pragma unroll
     for (int n = 0; n < NT; ++n)
       ao[n] = (n * 16 + lr < nvalid && tok[n] >= 0) ? (uint32_t)tok[n] * arow + kg * 64
                                                      : 0x80000000u;
   } else {
-    ra = q4_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * arow);
+    ra = buffer_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * arow);
   }
   if (nb > 0) A.load_x(ra, ao, wave);
   for (; b + 2 < nb; b += 2) {
@@ -428,13 +418,6 @@ __global__ __launch_bounds__(kQ4Threads) void stream_q4_kernel32(MOE_Q4_PARAMS) 
 #ifndef MOE_Q4_FT_DN
 #define MOE_Q4_FT_DN 64
 #endif
-
-bool q4_group_ok(int K, int G) {
-  if (G < 32 || G % 32 || K % G || K % kQ4Chunk) return false;
-  return G % kQ4Chunk == 0 || kQ4Chunk % G == 0;
-}
-
-int q4_quantize_max_k() { return 65536; }
 
 void launch_quantize_int4(const void* W, bool bf16, int64_t rows, int N, int K, int G,
                           void* packed, float* scales, hipStream_t s) {

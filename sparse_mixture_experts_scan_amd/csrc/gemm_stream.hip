@@ -48,18 +48,7 @@ constexpr int kStreamThreads = 256;
 #ifndef MOE_STREAM_DMA_FT_DN
 #define MOE_STREAM_DMA_FT_DN 16
 #endif
-constexpr int kBufCfg = 0x00020000;  // raw buffer, 32-bit data format
 
-// Buffer resources must sit in scalar registers: make every field provably
-// wave-uniform.
-__device__ inline __amdgpu_buffer_rsrc_t stream_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, kBufCfg);
-}
 
 __device__ __forceinline__ uint4 sload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
@@ -158,8 +147,8 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gemm_kernel(
 
   const uint32_t row_bytes = (uint32_t)K * sizeof(T);
   __amdgpu_buffer_rsrc_t rw[NW];
-  rw[0] = stream_rsrc(W0 + ((size_t)e * N + f0) * K, FT * row_bytes);
-  if constexpr (GATEUP) rw[1] = stream_rsrc(W1 + ((size_t)e * N + f0) * K, FT * row_bytes);
+  rw[0] = buffer_rsrc(W0 + ((size_t)e * N + f0) * K, FT * row_bytes);
+  if constexpr (GATEUP) rw[1] = buffer_rsrc(W1 + ((size_t)e * N + f0) * K, FT * row_bytes);
   uint32_t wo[NF], ao[NT];
 #pragma unroll
   for (int f = 0; f < NF; ++f) wo[f] = (uint32_t)(f * 16 + lr) * row_bytes + kg * 16;
@@ -184,7 +173,7 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gemm_kernel(
   // token rows past the expert's count fall outside the resource: read as 0
   const int valid_end = offsets[e] + counts[e];
   const int nvalid = max(0, min(BT, valid_end - row0));
-  const __amdgpu_buffer_rsrc_t ra = stream_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
   if (nb > 0) A.load_x(ra, ao, wave);
   for (int b = 0; b < nb; b += 2) {
     if (b + 1 < nb) B.template load<true>(rw, ra, wo, ao, wave + (b + 1) * NWAVE, U);
@@ -269,7 +258,6 @@ __device__ __forceinline__ void stream_dma_body(
   constexpr int kDma = kSlot / 1024;              // DMA loads per run
   constexpr int NWAVE = kStreamThreads / kWave;
   static_assert(NROW % 16 == 0 && FT % 4 == 0 && kDma * 4 == NROW, "block shape");
-  typedef __attribute__((address_space(3))) void lds_void;
   __shared__ __attribute__((aligned(1024))) char sl0[NWAVE * kSlot];
   __shared__ __attribute__((aligned(1024))) char sl1[NWAVE * kSlot];
   __shared__ f32x4 red[NWAVE - 1][NW * NF * NT][kWave];
@@ -292,8 +280,8 @@ __device__ __forceinline__ void stream_dma_body(
 
   const uint32_t row_bytes = (uint32_t)K * 2;
   __amdgpu_buffer_rsrc_t rw[NW];
-  rw[0] = stream_rsrc(W0 + ((size_t)e * N + f0) * K, FT * row_bytes);
-  if constexpr (GATEUP) rw[1] = stream_rsrc(W1 + ((size_t)e * N + f0) * K, FT * row_bytes);
+  rw[0] = buffer_rsrc(W0 + ((size_t)e * N + f0) * K, FT * row_bytes);
+  if constexpr (GATEUP) rw[1] = buffer_rsrc(W1 + ((size_t)e * N + f0) * K, FT * row_bytes);
   // DMA load j: block rows 4 j .. 4 j + 3; lane i fills row 4 j + i / 16,
   // stored chunk i % 16 = global chunk (i % 16) ^ (row % 16)
   uint32_t dvo[kDma];
@@ -325,13 +313,13 @@ __device__ __forceinline__ void stream_dma_body(
   uint32_t ao[NT];
   __amdgpu_buffer_rsrc_t ra;
   if (row_token != nullptr) {
-    ra = stream_rsrc(act, (uint32_t)nT * row_bytes);
+    ra = buffer_rsrc(act, (uint32_t)nT * row_bytes);
 #pragma unroll
     for (int n = 0; n < NT; ++n)
       ao[n] = (n * 16 + lr < nvalid && tok[n] >= 0) ? (uint32_t)tok[n] * row_bytes + kg * 16
                                                      : 0x80000000u;
   } else {
-    ra = stream_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
+    ra = buffer_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
 #pragma unroll
     for (int n = 0; n < NT; ++n) ao[n] = (uint32_t)(n * 16 + lr) * row_bytes + kg * 16;
   }
@@ -436,13 +424,6 @@ __global__ __launch_bounds__(kStreamThreads) void stream_dma_kernel(
   (void)num_tiles;
   stream_dma_body<BT, FT, GATEUP>(act, W0, W1, outp, counts, offsets, tile_expert, N, K,
                                   row_token, nT);
-}
-
-// bf16 tokens: the LDS-staged bf16 kernel (d_model % 128 == 0) and the INT4
-// kernel (whose group rule already makes d_model a multiple of 128) read
-// them in place; offsets into x are 32-bit
-bool stream_gathers_in_place(const Dims& D) {
-  return D.bf16 && (D.w4 || D.d % 128 == 0) && (int64_t)D.T * D.d * 2 < (int64_t(1) << 31);
 }
 
 template <typename T, int BT>

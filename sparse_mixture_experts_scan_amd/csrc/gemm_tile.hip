@@ -52,9 +52,6 @@ constexpr int kTileThreads = 64 * kTileWaves;
 constexpr int kBFrags = 2;                          // 32-row token fragments per wave
 constexpr int kBStride = 128;                       // rows between a wave's token fragments
 constexpr int kTileBT = kTileTokens;  // token rows per tile (= padding unit)
-constexpr int kTileRows = 256;        // weight rows per tile
-constexpr int kTileBK = 64;           // K per LDS stage
-constexpr int kTileNS = 2;            // pair buffers (B): the K loop runs stages in pairs
 constexpr int kKSteps = kTileBK / 16;               // 32x32x16 MFMA k-steps per stage
 constexpr int kXcds = 8;
 
@@ -83,32 +80,6 @@ __device__ inline f32x16 mfma32(uint4 a, uint4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-constexpr int kBufferCfg = 0x00020000;  // raw buffer, 32-bit data format
-
-// Buffer resources must live in scalar registers: the fields are made provably
-// wave-uniform, otherwise each load is wrapped in a per-lane loop.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
-  void* p = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)n, kBufferCfg);
-}
-
-// Wait until at most N of this wave's vector-memory operations (here: LDS DMA
-// loads) are outstanding; lgkm/exp counters untouched.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-// All of this wave's LDS reads done, then the workgroup barrier.  No memory
-// fence: LDS DMA completion is waited for explicitly with wait_vmcnt.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 struct TileCtx {
   __amdgpu_buffer_rsrc_t rA, rB;   // this wave's A resource (gate or up half), B
@@ -307,14 +278,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
     // waves 4-5 fill A rows 0..127 (gate), waves 6-7 rows 128..255 (up);
     // waves 0-3 issue no A
     const bf16_t* Wsrc = ((wave & 3) < kDmaWaves / 2 ? W0 : W1) + ((size_t)e * N + f0) * K;
-    c.rA = make_rsrc(Wsrc, 128 * row_bytes);
+    c.rA = buffer_rsrc(Wsrc, 128 * row_bytes);
   } else {
-    c.rA = make_rsrc(W0 + ((size_t)e * N + f0) * K, 256 * row_bytes);
+    c.rA = buffer_rsrc(W0 + ((size_t)e * N + f0) * K, 256 * row_bytes);
   }
   // token rows past the expert's count fall outside the resource: read as 0
   const int nvalid = max(0, min(kTileBT, valid_end - row0));
-  c.rB = (GATEUP && row_token) ? make_rsrc(act, (uint32_t)nT * row_bytes)
-                               : make_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
+  c.rB = (GATEUP && row_token) ? buffer_rsrc(act, (uint32_t)nT * row_bytes)
+                               : buffer_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
   c.b_on = c.dma_base * (1024 / kRowBytes) < nvalid;
 
   // ---- fragment rows: A fragment a of wave half wf, token fragments at rows
@@ -450,37 +421,6 @@ static void tile_launch(const Dims& D, const void* act, const int32_t* row_token
       (const bf16_t*)act, (const bf16_t*)W0, (const bf16_t*)W1, out, counts, offsets, num_tiles,
       tile_expert, N, K, n_ft, n_tt, per_xcd, parts, (size_t)D.max_rows * N,
       tile_feat_group(D, GATEUP), row_token, D.T);
-}
-
-bool tile_shape_ok(const Dims& D) {
-  // buffer offsets are 32-bit: 256 rows of either K must stay below 2 GiB
-  const int64_t kmax = D.d > D.f ? D.d : D.f;
-  return D.bf16 && D.BT == kTileBT && D.f % (kTileRows / 2) == 0 && D.d % kTileRows == 0 &&
-         D.d % (kTileBK * kTileNS) == 0 && D.f % (kTileBK * kTileNS) == 0 &&
-         kTileRows * kmax * 2 < (int64_t(1) << 31);
-}
-
-// K-splits of the down GEMM: the expected tile count (ceil(rows / BT) plus
-// about half a tile of padding per expert) is spread over the CUs; a split
-// that fills the last round of workgroups markedly better is taken.
-int tile_down_splits(const Dims& D) {
-  constexpr int kCus = 256;
-  const int n_ft = D.d / kTileRows;
-  const double tiles = n_ft * ((double)D.T * D.k / kTileBT + D.E * 0.5);
-  auto fill = [&](int sp) {
-    const double t = tiles * sp;
-    return t / (std::ceil(t / kCus) * kCus);
-  };
-  const bool can2 = D.f % (2 * kTileBK * kTileNS) == 0;
-  return (can2 && fill(1) < 0.9 && fill(2) > fill(1) + 0.05) ? 2 : 1;
-}
-
-// Reading the tokens in place saves the scatter's copy of k rows per token
-// but spreads each tile's token panel over x.  Measured on MI355X: with
-// top-8 (E = 64) the step is 3.5% faster; with top-2 the gate/up GEMM loses
-// about what the copy costs, so those keep the copy.
-bool tile_gathers_in_place(const Dims& D) {
-  return D.k >= 4 && (int64_t)D.T * D.d * 2 < (int64_t(1) << 31);
 }
 
 void launch_gateup_tile(const Dims& D, const void* x, const int32_t* row_token, const void* Wg,

@@ -4,21 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "plan.h"
+
 namespace moe {
 
-struct Dims {
-  int T, d, f, E, k;   // tokens, d_model, d_ff, experts, top-k
-  int Epow2;           // smallest power of two >= E
-  int nblk;            // router / scatter blocks (kRouterTokens tokens each)
-  int BT;              // token tile = padding unit of expert segments
-  int max_rows;        // rows reserved for the permuted layout
-  int max_tiles;       // max_rows / BT
-  int down_splits;     // K-splits of the down GEMM (partial Y blocks)
-  int router_splits;   // d_model splits of the router scores (1 = fused kernel)
-  bool bf16;           // element type of x / weights / out
-  bool w4;             // expert weights in INT4 (bf16 activations)
-  int group;           // INT4 scale group (input features per scale)
-};
 
 // INT4 weights of one matrix stack: packed codes and float32 scales
 struct Q4Weights {
@@ -49,15 +38,12 @@ struct ScanArgs {
   // row maps (tok_row, row_token), for a GEMM that reads the tokens in place
   int32_t* tok_row;
 };
-// With a single router block the router's select pass also runs the expert
-// scan (launch_scan is then a no-op), which saves a launch for small T.
-bool router_fuses_scan(const Dims& D);
+// With a single router block (router_fuses_scan) the select pass also runs
+// the expert scan and launch_scan is a no-op, which saves a launch for small T.
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
                    int32_t* idx, float* w, int32_t* blk_counts, float* part, float* blk_prob,
                    const float* gamma, const float* rs, float* logits_out, const ScanArgs& sa,
                    hipStream_t s);
-int router_splits_for(int nblk, int d);
-constexpr int kRouterPartStride = 64;  // floats per token row of the partial scores
 // a2: histogram reduce, padded offsets, per-block bases, tile table
 // router statistics (when blk_prob is non-NULL): prob_out [E], loss_out [1]
 void launch_scan(const Dims& D, int32_t* blk_counts, const ScanArgs& sa, const float* blk_prob,
@@ -70,7 +56,6 @@ void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int3
 // a3 + a4: grouped GEMMs, weight-streaming form (few rows per expert).
 // row_token NULL: act is the gathered rows (xs); else act is x (or xn) and
 // each row's token comes from row_token (only when stream_gathers_in_place).
-bool stream_gathers_in_place(const Dims& D);
 void launch_gateup_stream(const Dims& D, const void* act, const int32_t* row_token,
                           const void* Wg, const void* Wu, void* h, const int32_t* counts,
                           const int32_t* offsets, const int32_t* num_tiles,
@@ -79,23 +64,16 @@ void launch_down_stream(const Dims& D, const void* h, const void* Wd, float* y,
                         const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                         const int32_t* tile_expert, hipStream_t s);
 // a3 + a4: grouped GEMMs, LDS-tiled MFMA form (many rows per expert, bf16)
-constexpr int kTileTokens = 256;  // token tile of the tiled form (= padding unit)
-bool tile_shape_ok(const Dims& D);
-int tile_down_splits(const Dims& D);  // K-split count for the tiled down GEMM
 // row_token non-NULL: `x` is the token matrix [T][d] and each tile gathers its
 // rows through row_token; NULL: `x` is the gathered Xs
 void launch_gateup_tile(const Dims& D, const void* x, const int32_t* row_token, const void* Wg,
                         const void* Wu, void* h, const int32_t* counts, const int32_t* offsets,
                         const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s);
-// whether the tiled gate/up GEMM can gather token rows in place (32-bit offsets)
-bool tile_gathers_in_place(const Dims& D);
 void launch_down_tile(const Dims& D, const void* h, const void* Wd, float* y,
                       const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                       const int32_t* tile_expert, hipStream_t s);
 // INT4 expert weights: quantizer, dequantizer (to bf16, for the tiled form)
 // and the weight-streaming GEMMs that read INT4 directly
-bool q4_group_ok(int K, int G);
-int q4_quantize_max_k();
 // rows = batch * N matrices rows; scales group-major per matrix ([K/G][N])
 void launch_quantize_int4(const void* W, bool bf16, int64_t rows, int N, int K, int G,
                           void* packed, float* scales, hipStream_t s);
@@ -110,8 +88,6 @@ void launch_down_q4(const Dims& D, const void* h, const Q4Weights& Wd, float* y,
                     const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                     const int32_t* tile_expert, hipStream_t s);
 // backward (bf16): grouped GEMMs and the steps around them
-int bwd_gemm_tile_rows();
-int bwd_router_slices();
 void launch_bwd_tile_table(const Dims& D, const int32_t* counts, const int32_t* offsets,
                            int max_tiles, int32_t* tb_count, int32_t* tb_exp, int32_t* tb_row0,
                            int32_t* tb_rows, hipStream_t s);
@@ -123,11 +99,8 @@ void launch_bwd_gemm_rows(const void* A, int lda, const void* B, int ldb, bool b
                           int K, bool accumulate, int max_tiles, const int32_t* tb_count,
                           const int32_t* tb_exp, const int32_t* tb_row0, const int32_t* tb_rows,
                           hipStream_t s);
-// C_e[M][N] = sum over expert e's rows r of A[r][m] B[r][n] (bf16 out)
 // Backward GEMMs on 256 x 256 tiles (d_model and d_ff multiples of 256):
 // one launch each for a | b, Z, dX (both terms), dW2, and dW1 | dW3.
-bool bwd_tile_shape_ok(int64_t d, int64_t f);
-int bwd_tile_rows();
 void launch_bwd_recompute(const Dims& D, const void* xs, const void* Wg, const void* Wu, void* ab,
                           int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
                           const int32_t* tb_row0, const int32_t* tb_rows, hipStream_t s);

@@ -24,99 +24,22 @@ int fail(int status, const std::string& why) {
   return status;
 }
 
-struct Plan {
-  moe::Dims D;
-  moe_ws_layout_t L;
-};
+using moe::BwdPlan;
+using moe::Plan;
 
-size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+// make_plan / make_bwd_plan of plan.h, with the reason of a failure kept as
+// this thread's last error
+int plan_forward(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dtype,
+                 bool block, Plan* p) {
+  std::string why;
+  const int st = moe::make_plan(T, d, f, E, k, dtype, block, p, &why);
+  return st == MOE_OK ? st : fail(st, why);
+}
 
-// average rows per expert from which the LDS-tiled GEMMs are used
-constexpr int64_t kTileMinRows = 96;
-
-// Validates a shape and builds the launch plan and workspace layout.
-// Touches no HIP API.
-int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dtype, Plan* p) {
-  if (T < 1 || d < 1 || f < 1 || E < 1 || k < 1)
-    return fail(MOE_ERR_INVALID_ARG, "T must be >= 0; d_model, d_ff, E and k >= 1");
-  if (k > E) return fail(MOE_ERR_INVALID_ARG, "k must be <= E");
-  if (dtype != MOE_BF16 && dtype != MOE_F32 && dtype != MOE_W4A16)
-    return fail(MOE_ERR_INVALID_ARG, "unknown dtype");
-  if (E > MOE_MAX_EXPERTS) return fail(MOE_ERR_UNSUPPORTED, "E > 64");
-  if (k > MOE_MAX_TOPK) return fail(MOE_ERR_UNSUPPORTED, "k > 8");
-  if (d % MOE_DIM_ALIGN || f % MOE_DIM_ALIGN)
-    return fail(MOE_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 64");
-  if (T > (int64_t(1) << 24)) return fail(MOE_ERR_UNSUPPORTED, "T > 2^24");
-  if (d > 32768 || f > 131072) return fail(MOE_ERR_UNSUPPORTED, "d_model > 32768 or d_ff > 131072");
-
-  moe::Dims& D = p->D;
-  D.T = (int)T;
-  D.d = (int)d;
-  D.f = (int)f;
-  D.E = E;
-  D.k = k;
-  D.bf16 = dtype != MOE_F32;
-  D.w4 = dtype == MOE_W4A16;
-  D.group = 0;
-  D.Epow2 = 1;
-  while (D.Epow2 < E) D.Epow2 *= 2;
-  D.nblk = (D.T + moe::kRouterTokens - 1) / moe::kRouterTokens;
-  D.router_splits = moe::router_splits_for(D.nblk, D.d);
-  const int64_t A = T * k;                       // (token, slot) assignments
-  const int64_t rows_avg = (A + E - 1) / E;
-  // GEMM form: weight-streaming for few rows per expert (weights read once,
-  // HBM-bound), LDS-tiled MFMA for many (compute-bound).
-  D.BT = moe::kTileTokens;
-  int variant = 1;
-  if (!(D.bf16 && rows_avg >= kTileMinRows && moe::tile_shape_ok(D))) {
-    variant = 0;
-    D.BT = rows_avg <= 16 ? 16 : 32;
-  }
-  D.down_splits = 1;
-  int64_t max_rows = A + (int64_t)E * (D.BT - 1);
-  max_rows = (max_rows + D.BT - 1) / D.BT * D.BT;
-  if (max_rows > (int64_t(1) << 30)) return fail(MOE_ERR_UNSUPPORTED, "too many rows");
-  D.max_rows = (int)max_rows;
-  D.max_tiles = (int)(max_rows / D.BT);
-  if (variant == 1) D.down_splits = moe::tile_down_splits(D);
-
-  moe_ws_layout_t& L = p->L;
-  std::memset(&L, 0, sizeof(L));
-  L.block_rows = D.BT;
-  L.max_rows = D.max_rows;
-  L.router_blocks = D.nblk;
-  L.gemm_variant = variant;
-  L.down_splits = D.down_splits;
-  L.tokens_in_place =
-      variant == 1 ? moe::tile_gathers_in_place(D) : moe::stream_gathers_in_place(D);
-  const size_t es = D.bf16 ? 2 : 4;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off = align256(off + bytes);
-    return o;
-  };
-  L.topk_idx = take(sizeof(int32_t) * A);
-  L.topk_w = take(sizeof(float) * A);
-  L.block_counts = take(sizeof(int32_t) * D.nblk * E);
-  L.counts = take(sizeof(int32_t) * E);
-  L.offsets = take(sizeof(int32_t) * (E + 1));
-  L.num_tiles = take(sizeof(int32_t));
-  L.tile_expert = take(sizeof(int32_t) * D.max_tiles);
-  L.row_token = take(sizeof(int32_t) * D.max_rows);
-  L.tok_row = take(sizeof(int32_t) * A);
-  L.xs = take(es * D.max_rows * d);
-  L.h = take(es * D.max_rows * f);
-  L.y = take(sizeof(float) * D.down_splits * D.max_rows * d);
-  L.block_probs = take(sizeof(float) * D.nblk * E);
-  L.norm_rs = take(sizeof(float) * T);
-  L.xn = take(es * T * d);
-  L.router_partial = take(D.router_splits > 1 ? sizeof(float) * D.router_splits * D.nblk *
-                                                    moe::kRouterTokens * moe::kRouterPartStride
-                                              : 0);
-  L.wdeq = take(D.w4 && variant == 1 ? sizeof(uint16_t) * 3 * (size_t)E * d * f : 0);
-  L.total = off;
-  return MOE_OK;
+int plan_backward(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, BwdPlan* b) {
+  std::string why;
+  const int st = moe::make_bwd_plan(T, d, f, E, k, b, &why);
+  return st == MOE_OK ? st : fail(st, why);
 }
 
 struct CachedWs {
@@ -166,7 +89,7 @@ void moe_opts_init(moe_opts_t* o) {
 size_t moe_ffn_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
                               int32_t dtype) {
   Plan p;
-  if (make_plan(T == 0 ? 1 : T, d_model, d_ff, E, k, dtype, &p) != MOE_OK) return 0;
+  if (plan_forward(T == 0 ? 1 : T, d_model, d_ff, E, k, dtype, false, &p) != MOE_OK) return 0;
   return p.L.total;
 }
 
@@ -175,7 +98,29 @@ int moe_ffn_workspace_layout(int64_t T, int64_t d_model, int64_t d_ff, int32_t E
   g_last_error.clear();
   if (!layout) return fail(MOE_ERR_INVALID_ARG, "layout is NULL");
   Plan p;
-  const int st = make_plan(T == 0 ? 1 : T, d_model, d_ff, E, k, dtype, &p);
+  const int st = plan_forward(T == 0 ? 1 : T, d_model, d_ff, E, k, dtype, false, &p);
+  if (st != MOE_OK) return st;
+  *layout = p.L;
+  return MOE_OK;
+}
+
+size_t moe_block_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                                int32_t dtype) {
+  Plan p;
+  if (dtype == MOE_W4A16 ||
+      plan_forward(T == 0 ? 1 : T, d_model, d_ff, E, k, dtype, true, &p) != MOE_OK)
+    return 0;
+  return p.L.total;
+}
+
+int moe_block_workspace_layout(int64_t T, int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                               int32_t dtype, moe_ws_layout_t* layout) {
+  g_last_error.clear();
+  if (!layout) return fail(MOE_ERR_INVALID_ARG, "layout is NULL");
+  if (dtype == MOE_W4A16)
+    return fail(MOE_ERR_INVALID_ARG, "the block wrapper takes bf16 or float32 weights");
+  Plan p;
+  const int st = plan_forward(T == 0 ? 1 : T, d_model, d_ff, E, k, dtype, true, &p);
   if (st != MOE_OK) return st;
   *layout = p.L;
   return MOE_OK;
@@ -198,7 +143,7 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   Plan p;
   // an empty batch checks the other sizes as for one token, reads no tensor
   // and only clears the optional statistics
-  int st = make_plan(T == 0 ? 1 : T, d_model, d_ff, E, k, o.dtype, &p);
+  int st = plan_forward(T == 0 ? 1 : T, d_model, d_ff, E, k, o.dtype, norm_w != nullptr, &p);
   if (st != MOE_OK) return st;
   p.D.group = group;
   if (T == 0) {
@@ -408,81 +353,13 @@ int moe_ffn_forward_int4(const void* x, const float* W_router, const uint8_t* Wg
 
 }  // extern "C"
 
-namespace {
-
-// Backward workspace: the forward routing and permutation (16-row padding),
-// the recomputed pre-activations and every gradient intermediate.
-struct BwdPlan {
-  moe::Dims D;
-  int max_tiles;  // rows of the 128-row tile table
-  size_t topk_idx, topk_w, block_counts, counts, offsets, num_tiles, tile_expert, row_token,
-      tok_row, xs, logits, router_partial, ab, z, dab, hg, dp, dxs, dg, ds, wpart, tb, total;
-};
-
-int make_bwd_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, BwdPlan* b) {
-  Plan p;
-  int st = make_plan(T, d, f, E, k, MOE_BF16, &p);
-  if (st != MOE_OK) return st;
-  if (d % 128 || f % 128)
-    return fail(MOE_ERR_UNSUPPORTED, "the backward needs d_model and d_ff multiples of 128");
-  // 32-bit buffer ranges: one expert's rows of the widest row-major operand
-  if ((int64_t)T * std::max<int64_t>(2 * f, d) * 4 >= (int64_t(1) << 31))
-    return fail(MOE_ERR_UNSUPPORTED, "T * max(2 d_ff, d_model) too large for the backward");
-  moe::Dims& D = b->D;
-  D = p.D;
-  D.BT = 16;
-  const int64_t A = T * k;
-  int64_t max_rows = A + (int64_t)E * (D.BT - 1);
-  max_rows = (max_rows + D.BT - 1) / D.BT * D.BT;
-  D.max_rows = (int)max_rows;
-  D.max_tiles = (int)(max_rows / D.BT);
-  D.down_splits = 1;
-  const int tr = moe::bwd_gemm_tile_rows();
-  b->max_tiles = (int)((A + tr - 1) / tr + E);
-  const size_t R = (size_t)max_rows;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off = align256(off + bytes);
-    return o;
-  };
-  b->topk_idx = take(4 * A);
-  b->topk_w = take(4 * A);
-  b->block_counts = take(4 * (size_t)D.nblk * E);
-  b->counts = take(4 * (size_t)E);
-  b->offsets = take(4 * (size_t)(E + 1));
-  b->num_tiles = take(4);
-  b->tile_expert = take(4 * (size_t)D.max_tiles);
-  b->row_token = take(4 * R);
-  b->tok_row = take(4 * A);
-  b->xs = take(2 * R * d);
-  b->logits = take(4 * (size_t)T * E);
-  b->router_partial = take(D.router_splits > 1 ? sizeof(float) * D.router_splits * D.nblk *
-                                                     moe::kRouterTokens * moe::kRouterPartStride
-                                               : 0);
-  b->ab = take(2 * R * 2 * f);   // bf16 a | b
-  b->z = take(2 * R * f);        // bf16 Z
-  b->dab = take(2 * R * 2 * f);
-  b->hg = take(2 * R * f);
-  b->dp = take(2 * R * d);
-  b->dxs = take(4 * 2 * R * d);   // two planes: the W1 and W3 halves of dX
-  b->dg = take(4 * R);
-  b->ds = take(4 * (size_t)T * E);
-  b->wpart = take(4 * (size_t)moe::bwd_router_slices() * (d + 1) * E);
-  b->tb = take(4 * (size_t)(1 + 3 * b->max_tiles));
-  b->total = off;
-  return MOE_OK;
-}
-
-}  // namespace
-
 extern "C" {
 
 size_t moe_ffn_backward_workspace_size(int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
                                        int32_t k) {
   g_last_error.clear();
   BwdPlan b;
-  if (make_bwd_plan(T == 0 ? 1 : T, d_model, d_ff, E, k, &b) != MOE_OK) return 0;
+  if (plan_backward(T == 0 ? 1 : T, d_model, d_ff, E, k, &b) != MOE_OK) return 0;
   return b.total;
 }
 
@@ -498,7 +375,7 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   if (o.dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "the backward takes bf16 tensors");
   if (!(alpha >= 0.f) || alpha > 1e30f) return fail(MOE_ERR_INVALID_ARG, "alpha must be >= 0");
   BwdPlan b;
-  int st = make_bwd_plan(T == 0 ? 1 : T, d_model, d_ff, E, k, &b);
+  int st = plan_backward(T == 0 ? 1 : T, d_model, d_ff, E, k, &b);
   if (st != MOE_OK) return st;
   if (!dW_router || !dW_gate || !dW_up || !dW_down)
     return fail(MOE_ERR_INVALID_ARG, "null gradient pointer");

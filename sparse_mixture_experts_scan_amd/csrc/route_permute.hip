@@ -349,12 +349,6 @@ __device__ __forceinline__ void scatter_rows_block(
   sTok[tid] = t;
 }
 
-// Workgroup barrier for data exchanged through LDS only: unlike
-// __syncthreads it does not wait for the block's global stores to complete.
-__device__ __forceinline__ void lds_only_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // The select pass of a batch that fits one router block, run by all
 // kRouterThreads threads once slog holds the final scores: top-k and
 // softmax, the router statistics, the expert scan and (sa.tok_row set) the
@@ -382,7 +376,7 @@ __device__ __forceinline__ void select_single_block(
     smax[tid] = m;
     sinv[tid] = 1.f / z;
   }
-  lds_only_barrier();
+  lds_barrier();
   // expert scan: segments padded to BT rows
   if (tid == 0) {
     int off = 0;
@@ -400,7 +394,7 @@ __device__ __forceinline__ void select_single_block(
     s_p[tid] = acc / (float)nT;
     if (sa.prob_out) sa.prob_out[tid] = s_p[tid];
   }
-  lds_only_barrier();
+  lds_barrier();
   if (tid < E) {
     sa.counts[tid] = hist[tid];
     if (sa.counts_out) sa.counts_out[tid] = hist[tid];
@@ -444,7 +438,7 @@ __device__ __forceinline__ void select_single_block(
     if (e == ex) rank_w = __popcll(msk & lt);
     if (lane == 0) wcnt[wave][ex] = __popcll(msk);
   }
-  lds_only_barrier();
+  lds_barrier();
   if (e >= 0) {
     int rank = rank_w;
     for (int w = 0; w < wave; ++w) rank += wcnt[w][e];
@@ -460,12 +454,6 @@ __device__ __forceinline__ void select_single_block(
 // scan (a2, part 1) on the counts it has just written, which saves a launch,
 // and with sa.tok_row set the row maps as well (no scatter launch).
 constexpr int kSelectThreads = 256;
-// d_model splits of the score GEMM at most (measured on MI355X at decode,
-// one token block: 32 splits take the router stage 1 us longer than 16)
-#ifndef MOE_ROUTER_MAX_SPLITS
-#define MOE_ROUTER_MAX_SPLITS 16
-#endif
-constexpr int kMaxRouterSplits = MOE_ROUTER_MAX_SPLITS;
 
 __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, int nT, int E, int k,
@@ -723,8 +711,6 @@ void launch_rmsnorm(const Dims& D, const void* x, const float* weight, float eps
     rmsnorm_kernel<float><<<D.T, 256, 0, s>>>((const float*)x, weight, eps, D.d, rs, (float*)xn);
 }
 
-bool router_fuses_scan(const Dims& D) { return D.nblk == 1 && D.router_splits > 1; }
-
 void launch_router(const Dims& D, const void* x, const float* Wr, const float* bias,
                    int32_t* idx, float* w, int32_t* blk_counts, float* part, float* blk_prob,
                    const float* gamma, const float* rs, float* logits_out, const ScanArgs& sa,
@@ -742,22 +728,6 @@ void launch_router(const Dims& D, const void* x, const float* Wr, const float* b
     router_select_kernel<<<D.nblk, kSelectThreads, 0, s>>>(
         part, bias, D.T, D.E, D.k, D.router_splits, idx, w, blk_counts, blk_prob, rs, logits_out,
         sa, router_fuses_scan(D) ? 1 : 0, D.Epow2, D.BT, D.max_rows, D.max_tiles);
-}
-
-#ifndef MOE_ROUTER_MIN_BLOCKS
-#define MOE_ROUTER_MIN_BLOCKS 256
-#endif
-int router_splits_for(int nblk, int d) {
-  // split d_model over blocks until about one block per CU runs (measured on
-  // MI355X: 128 blocks left T = 4096 at 0.065 ms, 256 take 0.044 ms, 512 or
-  // more are slower again); each split keeps a whole number of 16-element
-  // k-groups
-  const int groups = d / 16;
-  int sp = 1;
-  while (nblk * sp < MOE_ROUTER_MIN_BLOCKS && sp * 2 <= kMaxRouterSplits &&
-         groups % (sp * 2) == 0)
-    sp *= 2;
-  return sp;
 }
 
 void launch_scan(const Dims& D, int32_t* blk_counts, const ScanArgs& sa, const float* blk_prob,

@@ -28,6 +28,23 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_probe_library_exports_every_declared_symbol():
+    from sparse_mixture_experts_scan_amd import probe
+    hdr = os.path.join(os.path.dirname(HEADER), "moe_probe.h")
+    text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+    assert set(declared) == set(probe.EXPORTED)
+    lib = probe.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    # host-side argument checks enqueue nothing (no GPU needed)
+    assert lib.moe_probe_read(None, 16, DUMMY, 1, None) == 1
+    assert lib.moe_probe_read(DUMMY, 15, DUMMY, 1, None) == 1
+    assert lib.moe_probe_copy(DUMMY, DUMMY + 8, 16, 1, None) == 1
+    assert lib.moe_probe_mfma(None, 1, 1, None) == 1
+    assert lib.moe_probe_mfma_flops(2, 3) == 2.0 * 32 * 32 * 16 * 8 * 3 * 8 * 2
+
+
 def test_version_and_status_strings():
     assert re.match(r"^\d+\.\d+\.\d+$", moe.moe_version())
     for st in range(5):
@@ -87,32 +104,53 @@ def test_rejects_small_or_misaligned_workspace():
     assert fwd(opts=o) == B.MOE_ERR_WORKSPACE
 
 
+def layout_spans(lay, T, d, f, E, k, dt, block):
+    es = 2 if dt in (0, 2) else 4
+    in_place = lay.tokens_in_place == 1
+    return [("topk_idx", 4 * T * k), ("topk_w", 4 * T * k),
+            ("block_counts", 4 * lay.router_blocks * E), ("counts", 4 * E),
+            ("offsets", 4 * (E + 1)), ("num_tiles", 4),
+            ("tile_expert", 4 * lay.max_rows // lay.block_rows), ("row_token", 4 * lay.max_rows),
+            ("tok_row", 4 * T * k), ("xs", 0 if in_place else es * lay.max_rows * d),
+            ("h", es * lay.max_rows * f), ("y", 4 * lay.down_splits * lay.max_rows * d),
+            ("block_probs", 4 * lay.router_blocks * E),
+            ("norm_rs", 4 * T if block else 0), ("xn", es * T * d if block else 0)]
+
+
 def test_workspace_layout_is_consistent():
     for (T, d, f, E, k, dt) in [(16, 4096, 14336, 8, 2, 0), (4096, 4096, 14336, 8, 2, 0),
                                 (4096, 4096, 3584, 64, 8, 0), (64, 128, 512, 8, 2, 1),
-                                (1, 64, 64, 1, 1, 1)]:
-        lay = moe.moe_ffn_workspace_layout(T, d, f, E, k, dt)
-        assert lay.total == moe.moe_ffn_workspace_size(T, d, f, E, k, dt)
-        BT = lay.block_rows
-        # worst case of the padded permuted layout fits
-        assert lay.max_rows >= T * k + E * (BT - 1) and lay.max_rows % BT == 0
-        assert lay.router_blocks == (T + 31) // 32
+                                (1, 64, 64, 1, 1, 1), (33, 192, 320, 6, 3, 0)]:
+        for block in (False, True):
+            if block:
+                lay = moe.moe_block_workspace_layout(T, d, f, E, k, dt)
+                assert lay.total == moe.moe_block_workspace_size(T, d, f, E, k, dt)
+            else:
+                lay = moe.moe_ffn_workspace_layout(T, d, f, E, k, dt)
+                assert lay.total == moe.moe_ffn_workspace_size(T, d, f, E, k, dt)
+            BT = lay.block_rows
+            # worst case of the padded permuted layout fits
+            assert lay.max_rows >= T * k + E * (BT - 1) and lay.max_rows % BT == 0
+            assert lay.router_blocks == (T + 31) // 32
+            fields = layout_spans(lay, T, d, f, E, k, dt, block)
+            assert lay.router_partial >= lay.xn + dict(fields)["xn"]
+            assert lay.router_partial <= lay.total
+            spans = sorted((getattr(lay, n), getattr(lay, n) + size) for n, size in fields)
+            for (a0, a1), (b0, _) in zip(spans, spans[1:]):
+                assert a1 <= b0                      # no overlap
+            assert all(s % 256 == 0 for s, _ in spans)
+            assert spans[-1][1] <= lay.total
+        # the block's layout is the layer's plus the normalised tokens and 1/rms
         es = 2 if dt == 0 else 4
-        fields = [("topk_idx", 4 * T * k), ("topk_w", 4 * T * k),
-                  ("block_counts", 4 * lay.router_blocks * E), ("counts", 4 * E),
-                  ("offsets", 4 * (E + 1)), ("num_tiles", 4),
-                  ("tile_expert", 4 * lay.max_rows // BT), ("row_token", 4 * lay.max_rows),
-                  ("tok_row", 4 * T * k), ("xs", es * lay.max_rows * d),
-                  ("h", es * lay.max_rows * f), ("y", 4 * lay.down_splits * lay.max_rows * d),
-                  ("block_probs", 4 * lay.router_blocks * E), ("norm_rs", 4 * T),
-                  ("xn", es * T * d)]
-        assert lay.router_partial >= lay.xn + es * T * d
-        assert lay.router_partial <= lay.total
-        spans = sorted((getattr(lay, n), getattr(lay, n) + size) for n, size in fields)
-        for (a0, a1), (b0, _) in zip(spans, spans[1:]):
-            assert a1 <= b0                      # no overlap
-        assert all(s % 256 == 0 for s, _ in spans)
-        assert spans[-1][1] <= lay.total
+        extra = moe.moe_block_workspace_size(T, d, f, E, k, dt) - \
+            moe.moe_ffn_workspace_size(T, d, f, E, k, dt)
+        assert es * T * d + 4 * T <= extra <= es * T * d + 4 * T + 512
+    # the fine-grained shape reads its tokens in place: no gathered copy
+    lay = moe.moe_ffn_workspace_layout(4096, 4096, 3584, 64, 8, 0)
+    assert lay.tokens_in_place == 1 and lay.h == lay.xs
+    assert moe.moe_block_workspace_size(16, 256, 512, 8, 2, B.MOE_W4A16) == 0
+    with pytest.raises(moe.MoeError):
+        moe.moe_block_workspace_layout(16, 256, 512, 8, 2, B.MOE_W4A16)
     # the tiled down GEMM of the Mixtral prefill shape is split along K (its
     # 576 tiles fill 256 CUs badly), the fine-grained shape's is not
     assert moe.moe_ffn_workspace_layout(4096, 4096, 14336, 8, 2, 0).down_splits == 2
