@@ -49,7 +49,8 @@ def run_gpu(cfg: MoEConfig, dinp: dict, *, device="cuda", keep_ws=True, block_ep
     block_eps given: the normalised block (dinp["norm_weight"], that eps)."""
     T, d, f, E, k = cfg.T, cfg.d_model, cfg.d_ff, cfg.E, cfg.k
     dt = moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32
-    lay = moe.moe_ffn_workspace_layout(T, d, f, E, k, dt)
+    lay = (moe.moe_block_workspace_layout(T, d, f, E, k, dt) if block_eps is not None
+           else moe.moe_ffn_workspace_layout(T, d, f, E, k, dt))
     ws = torch.empty(lay.total, dtype=torch.uint8, device=device)
     idx = torch.full((T, k), -7, dtype=torch.int32, device=device)
     w = torch.full((T, k), -7.0, dtype=torch.float32, device=device)
@@ -189,25 +190,62 @@ def check_values(cfg: MoEConfig, inp: dict, res: dict, tokens, orc_full=None) ->
     return float(err)
 
 
-def check_hidden_and_expert_outputs(cfg: MoEConfig, inp: dict, res: dict, tokens) -> tuple:
-    """H = SiLU(W1 x) * W3 x and Y = W2 H rows of sampled (token, slot) pairs
-    vs the oracle's expert_hidden / swiglu_expert."""
-    tokens = np.asarray(tokens)
+def check_hidden_and_expert_outputs(cfg: MoEConfig, inp: dict, res: dict, rows) -> tuple:
+    """H = SiLU(W1 x) * W3 x and Y = W2 H of the given permuted rows vs the
+    oracle's expert_hidden / swiglu_expert, one oracle call per expert on
+    all of that expert's sampled rows."""
+    rows = np.asarray(rows, dtype=np.int64)
+    rt = res["row_token"]
+    offs = res["offsets"]
+    expert_of = np.searchsorted(offs, rows, side="right") - 1
+    h = ws_rows(res, cfg, "h", rows).astype(np.float64)
+    y = ws_rows(res, cfg, "y", rows)
     errs_h, errs_y = [], []
-    for t in tokens:
-        for j in range(cfg.k):
-            e = int(res["idx"][t, j])
-            row = int(res["tok_row"][t, j])
-            href = oracle.expert_hidden(inp["x"][t:t + 1], inp["W_gate"][e], inp["W_up"][e])[0]
-            yref = oracle.swiglu_expert(inp["x"][t:t + 1], inp["W_gate"][e], inp["W_up"][e],
-                                        inp["W_down"][e])[0]
-            h = ws_rows(res, cfg, "h", [row])[0].astype(np.float64)
-            y = ws_rows(res, cfg, "y", [row])[0].astype(np.float64)
-            errs_h.append(np.abs(h - href).max() / max(np.abs(href).max(), 1e-30))
-            errs_y.append(np.abs(y - yref).max() / max(np.abs(yref).max(), 1e-30))
+    for e in np.unique(expert_of):
+        sel = np.nonzero(expert_of == e)[0]
+        toks = rt[rows[sel]]
+        assert (toks >= 0).all(), "sampled a padding row"
+        xr = inp["x"][toks]
+        href = oracle.expert_hidden(xr, inp["W_gate"][e], inp["W_up"][e])
+        yref = oracle.swiglu_expert(xr, inp["W_gate"][e], inp["W_up"][e], inp["W_down"][e])
+        for i, n in enumerate(sel):
+            errs_h.append(np.abs(h[n] - href[i]).max() / max(np.abs(href[i]).max(), 1e-30))
+            errs_y.append(np.abs(y[n] - yref[i]).max() / max(np.abs(yref[i]).max(), 1e-30))
     eh, ey = max(errs_h), max(errs_y)
     assert eh <= TOL[cfg.dtype] and ey <= TOL[cfg.dtype], (eh, ey)
     return eh, ey
+
+
+def tile_rows(res: dict, per_tile: int = 1, seed: int = 0) -> np.ndarray:
+    """Permuted rows that reach every unit of the grouped GEMMs' work:
+    `per_tile` random valid rows of every token tile in use (so every
+    (expert, token tile) pair, and with it every XCD share of the tile
+    order, is value-checked) plus the first and last valid row of every
+    expert segment (the ragged end of its last tile)."""
+    lay = res["layout"]
+    BT = int(lay.block_rows)
+    rt = res["row_token"]
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for t in range(int(res["num_tiles"])):
+        valid = np.nonzero(rt[t * BT:(t + 1) * BT] >= 0)[0]
+        if valid.size:
+            pick = rng.choice(valid, size=min(per_tile, valid.size), replace=False)
+            rows.update((t * BT + pick).tolist())
+    offs, cnt = res["offsets"], res["ws_counts"]
+    for e in range(cnt.size):
+        if cnt[e]:
+            rows.update([int(offs[e]), int(offs[e] + cnt[e] - 1)])
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def tile_tokens(res: dict, per_tile: int = 1, seed: int = 0) -> np.ndarray:
+    """Tokens whose (token, slot) rows include tile_rows(res, per_tile), plus
+    the first, the last and a ragged-tail token."""
+    T = res["idx"].shape[0]
+    toks = set(res["row_token"][tile_rows(res, per_tile, seed)].tolist())
+    toks.update({0, T - 1, max(0, T - 1 - (T % 32))})
+    return np.array(sorted(toks), dtype=np.int64)
 
 
 def sample_tokens(cfg: MoEConfig, orc_idx: np.ndarray, n: int, seed: int = 0) -> np.ndarray:

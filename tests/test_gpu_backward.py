@@ -137,13 +137,37 @@ def test_backward_empty_batch():
     assert g["dx"].shape == (0, d)
 
 
+def row_chunk_tokens(idx, E, chunk, seed=0):
+    """Tokens covering every `chunk`-row piece of every expert's rows in the
+    permuted (token, slot) order the grouped GEMMs tile (one random pair of
+    each piece, and every expert's last pair)."""
+    k = idx.shape[1]
+    rng = np.random.default_rng(seed)
+    flat = idx.ravel()
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=E)
+    toks, pos = set(), 0
+    for e in range(E):
+        pairs = order[pos:pos + counts[e]]
+        pos += counts[e]
+        for c0 in range(0, pairs.size, chunk):
+            piece = pairs[c0:c0 + chunk]
+            toks.add(int(piece[rng.integers(piece.size)] // k))
+        if pairs.size:
+            toks.add(int(pairs[-1] // k))
+    return np.array(sorted(toks), dtype=np.int64)
+
+
 def test_backward_prefill_sampled():
     # the full prefill shape of the benchmark (T = 4096, Mixtral layer),
-    # checked on sampled outputs: dx of sampled tokens, rows of dW_gate and
-    # dW_up and columns of dW_down of two features per expert
+    # checked on stratified outputs: dx of a token from every 128-row piece of
+    # every expert's rows (each row tile of the recompute, Z and dX GEMMs), and
+    # of every expert, one feature from every 256-feature tile of d_ff: its
+    # rows of dW_gate and dW_up and its column of dW_down (each tile of the
+    # weight-gradient GEMMs along d_ff, all of their tiles along d_model)
     from sparse_mixture_experts_scan_amd.inputs import CONFIGS
     cfg = CONFIGS["prefill"]
-    announce(f"case prefill T={cfg.T} d={cfg.d_model} f={cfg.d_ff} E={cfg.E} k={cfg.k} sampled")
+    announce(f"case prefill T={cfg.T} d={cfg.d_model} f={cfg.d_ff} E={cfg.E} k={cfg.k} stratified")
     inp = make_inputs(cfg, seed=0)
     dout = make_dout(cfg, seed=0)
     d = H.upload(inp)
@@ -159,21 +183,27 @@ def test_backward_prefill_sampled():
     gap, _ = oracle.routing_gaps(s, cfg.k)
     ok = gap >= H.NEAR_TIE
     np.testing.assert_array_equal(np.sort(res["idx"][ok], axis=1), np.sort(ref_idx[ok], axis=1))
-    toks = H.sample_tokens(cfg, res["idx"], 6)
+    toks = row_chunk_tokens(res["idx"], cfg.E, 128)
     rng = np.random.default_rng(1)
-    feats = [(e, int(i)) for e in range(cfg.E) for i in rng.choice(cfg.d_ff, 2, replace=False)]
+    feats = [(e, int(f0 + rng.integers(256))) for e in range(cfg.E)
+             for f0 in range(0, cfg.d_ff, 256)]
     ref = oracle.moe_backward_entries(inp["x"], inp["W_router"], inp["W_gate"], inp["W_up"],
                                       inp["W_down"], dout, cfg.k, toks, feats,
                                       bias=inp["bias"], alpha=0.01,
                                       forced_idx=res["idx"].astype(np.int64))
+
     def host(t):
         return H.as_f32(H.to_host(t.contiguous())).astype(np.float64)
+    fe = torch.as_tensor([e for e, _ in feats], device="cuda")
+    fi = torch.as_tensor([i for _, i in feats], device="cuda")
     got = {"dx": host(g["dx"][torch.as_tensor(toks, device="cuda")]),
-           "dW_gate_rows": np.array([host(g["dW_gate"][e, i]) for e, i in feats]),
-           "dW_up_rows": np.array([host(g["dW_up"][e, i]) for e, i in feats]),
-           "dW_down_cols": np.array([host(g["dW_down"][e, :, i]) for e, i in feats])}
+           "dW_gate_rows": host(g["dW_gate"][fe, fi]),
+           "dW_up_rows": host(g["dW_up"][fe, fi]),
+           "dW_down_cols": host(g["dW_down"][fe, :, fi])}
     errs = {}
     for n, v in got.items():
+        assert v.shape == ref[n].shape, n
         errs[n] = float(np.abs(v - ref[n]).max() / np.abs(ref[n]).max())
         assert errs[n] <= TOL, (n, errs[n])
-    announce("  ok: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    announce(f"  ok over {toks.size} tokens and {len(feats)} features: "
+             + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
