@@ -120,6 +120,27 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate,
                     const moe_opts_t* opts);
 
 /*
+ * moe_ffn_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * it calls no hipMalloc, hipFree or other allocating routine.  Arguments,
+ * outputs, layouts and errors as moe_ffn_forward, except that
+ * opts->workspace must be NULL: the intermediates live in a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) of device memory that the library holds
+ * on every GPU it runs on until the process ends.  That covers the layer's
+ * workspace (moe_ffn_workspace_size) for decode-sized batches, e.g. T <= 256
+ * at the Mixtral 8x7B shape; a larger shape returns MOE_ERR_WORKSPACE before
+ * anything is enqueued.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents (nothing in it needs clearing): calls that
+ * overlap on one GPU (unordered streams, or several host threads) race and
+ * give undefined results.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_ffn_forward_noalloc(const void* x, const float* W_router, const void* W_gate,
+                            const void* W_up, const void* W_down, void* out, int64_t T,
+                            int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                            const moe_opts_t* opts);
+
+/*
  * One MoE sub-block of a Mixtral transformer block: out = x + layer(RMSNorm(x)).
  * "Mistral/Mixtralのアーキテクチャ", section "Mixtralのアーキテクチャ",
  * lists the second half of each block as normalisation, then the MoE layer,

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libmoe_ffn.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_BF16, MOE_F32, MOE_W4A16 = 0, 1, 2
 
-EXPORTED = ("moe_opts_init", "moe_ffn_forward", "moe_block_forward", "moe_quantize_int4",
+EXPORTED = ("moe_opts_init", "moe_ffn_forward", "moe_ffn_forward_noalloc", "moe_block_forward", "moe_quantize_int4",
             "moe_ffn_forward_int4", "moe_ffn_backward", "moe_ffn_backward_workspace_size",
             "moe_ffn_workspace_size", "moe_block_workspace_size",
             "moe_ffn_workspace_layout", "moe_block_workspace_layout", "moe_status_string", "moe_last_error",
@@ -79,6 +79,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
                                       ctypes.POINTER(MoeOpts)]
         L.moe_ffn_forward.restype = ctypes.c_int
+        L.moe_ffn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
+                                              ctypes.POINTER(MoeOpts)]
+        L.moe_ffn_forward_noalloc.restype = ctypes.c_int
         L.moe_block_forward.argtypes = [vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, i64, i64,
                                         i64, i32, i32, ctypes.POINTER(MoeOpts)]
         L.moe_block_forward.restype = ctypes.c_int
@@ -126,6 +129,14 @@ def moe_ffn_forward(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E,
     """Raw entry point: integer device addresses, returns the status code."""
     return lib().moe_ffn_forward(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E,
                                  k, ctypes.byref(opts) if opts is not None else None)
+
+
+def moe_ffn_forward_noalloc(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E, k,
+                            opts: Optional[MoeOpts] = None) -> int:
+    """Raw entry point of the forward that allocates nothing (library scratch)."""
+    return lib().moe_ffn_forward_noalloc(x, W_router, W_gate, W_up, W_down, out, T, d_model,
+                                         d_ff, E, k,
+                                         ctypes.byref(opts) if opts is not None else None)
 
 
 def moe_block_forward(x, norm_weight, eps, W_router, W_gate, W_up, W_down, out, T, d_model,
@@ -260,7 +271,7 @@ def _opts(x, E, k, dtype, bias, out, workspace, topk_idx, topk_w, expert_counts,
 def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
             workspace=None, topk_idx=None, topk_w=None, expert_counts=None, stream=None,
             stage_events=None, router_probs=None, balance_loss=None, norm_weight=None,
-            eps=1e-5):
+            eps=1e-5, noalloc=False):
     """One moe_ffn_forward call on torch device tensors.
 
     x [T][d] (bf16 or fp32), W_router [d][E] fp32, W_gate/W_up [E][d_ff][d],
@@ -271,7 +282,8 @@ def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
     norm_weight [d] fp32 the call is the block wrapper
     out = x + layer(RMSNorm(x)) (moe_block_forward, with `eps`).  `workspace`
     is a uint8 device tensor (see moe_ffn_workspace_size) or None for the
-    library's own.  Returns out."""
+    library's own.  noalloc: call moe_ffn_forward_noalloc (no workspace, the
+    library's fixed scratch; the bare layer only).  Returns out."""
     import torch
 
     T, d = x.shape
@@ -289,6 +301,9 @@ def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
         _check(t, shape, dt, x)
     if norm_weight is not None:
         _check(norm_weight, (d,), torch.float32, x)
+    if noalloc and (norm_weight is not None or workspace is not None):
+        raise ValueError("noalloc is the bare layer with the library's scratch: "
+                         "no norm_weight, no workspace")
     o, out, _keep = _opts(x, E, k, dtype, bias, out, workspace, topk_idx, topk_w,
                           expert_counts, stream, stage_events, router_probs, balance_loss)
     with torch.cuda.device(x.device):
@@ -297,9 +312,10 @@ def forward(x, W_router, W_gate, W_up, W_down, k: int, *, bias=None, out=None,
                                        W_router.data_ptr(), W_gate.data_ptr(), W_up.data_ptr(),
                                        W_down.data_ptr(), out.data_ptr(), T, d, d_ff, E, k, o)
         else:
-            status = moe_ffn_forward(x.data_ptr(), W_router.data_ptr(), W_gate.data_ptr(),
-                                     W_up.data_ptr(), W_down.data_ptr(), out.data_ptr(), T, d,
-                                     d_ff, E, k, o)
+            entry = moe_ffn_forward_noalloc if noalloc else moe_ffn_forward
+            status = entry(x.data_ptr(), W_router.data_ptr(), W_gate.data_ptr(),
+                           W_up.data_ptr(), W_down.data_ptr(), out.data_ptr(), T, d, d_ff, E, k,
+                           o)
     if status != MOE_OK:
         raise MoeError(status, "moe_ffn_forward")
     return out

@@ -78,6 +78,39 @@ int library_workspace(size_t bytes, char** ws) {
 
 }  // namespace
 
+// Scratch memory of moe_ffn_forward_noalloc: a file-scope device array, so
+// that entry point allocates nothing.  Each GPU the library runs on holds its
+// own copy until the process ends.  In host code the array's name is only a
+// stand-in for the symbol, never a device address: the address comes from
+// hipGetSymbolAddress, once per device, and only that address is handed to
+// kernels.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+std::map<int, char*> g_scratch;   // device -> device address of its scratch
+
+// The current device's scratch address, looked up on the first call on that
+// device (with it current) and kept.
+int scratch_address(char** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  auto it = g_scratch.find(dev);
+  if (it == g_scratch.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    it = g_scratch.emplace(dev, static_cast<char*>(p)).first;
+  }
+  *ptr = it->second;
+  return MOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 void moe_opts_init(moe_opts_t* o) {
@@ -132,10 +165,12 @@ namespace {
 
 // The whole launch sequence.  norm_w != NULL selects the block wrapper:
 // out = x + layer(RMSNorm(x)).
+// noalloc: the intermediates go to the device scratch array instead of a
+// caller or library workspace (moe_ffn_forward_noalloc).
 int run_layer(const void* x, const float* W_router, const void* W_gate, const void* W_up,
               const void* W_down, void* out, int64_t T, int64_t d_model, int64_t d_ff, int32_t E,
               int32_t k, const float* norm_w, float eps, const moe_opts_t* opts,
-              const moe::Q4Weights* q4 = nullptr, int group = 0) {
+              const moe::Q4Weights* q4 = nullptr, int group = 0, bool noalloc = false) {
   moe_opts_t o;
   if (opts) o = *opts;
   else moe_opts_init(&o);
@@ -145,6 +180,16 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   // and only clears the optional statistics
   int st = plan_forward(T == 0 ? 1 : T, d_model, d_ff, E, k, o.dtype, norm_w != nullptr, &p);
   if (st != MOE_OK) return st;
+  if (noalloc) {
+    if (o.workspace)
+      return fail(MOE_ERR_INVALID_ARG,
+                  "moe_ffn_forward_noalloc takes no workspace (opts->workspace must be NULL)");
+    if (p.L.total > MOE_NOALLOC_SCRATCH_BYTES)
+      return fail(MOE_ERR_WORKSPACE,
+                  "this shape needs " + std::to_string(p.L.total) +
+                      " bytes of workspace; moe_ffn_forward_noalloc's scratch holds " +
+                      std::to_string((size_t)MOE_NOALLOC_SCRATCH_BYTES));
+  }
   p.D.group = group;
   if (T == 0) {
     for (const void* ptr : {(const void*)o.expert_counts_out, (const void*)o.router_prob_out,
@@ -180,7 +225,11 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   // ---- validated; from here on HIP calls
   hipStream_t s = reinterpret_cast<hipStream_t>(o.stream);
   char* ws = static_cast<char*>(o.workspace);
-  if (!ws && (st = library_workspace(p.L.total, &ws)) != MOE_OK) return st;
+  if (noalloc) {
+    if ((st = scratch_address(&ws)) != MOE_OK) return st;
+  } else if (!ws && (st = library_workspace(p.L.total, &ws)) != MOE_OK) {
+    return st;
+  }
   const moe::Dims& D = p.D;
   const moe_ws_layout_t& L = p.L;
   int32_t* idx = o.topk_idx_out ? o.topk_idx_out : reinterpret_cast<int32_t*>(ws + L.topk_idx);
@@ -283,6 +332,17 @@ int moe_ffn_forward(const void* x, const float* W_router, const void* W_gate, co
     return fail(MOE_ERR_INVALID_ARG, "MOE_W4A16 weights go through moe_ffn_forward_int4");
   return run_layer(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E, k, nullptr, 0.f,
                    opts);
+}
+
+int moe_ffn_forward_noalloc(const void* x, const float* W_router, const void* W_gate,
+                            const void* W_up, const void* W_down, void* out, int64_t T,
+                            int64_t d_model, int64_t d_ff, int32_t E, int32_t k,
+                            const moe_opts_t* opts) {
+  g_last_error.clear();
+  if (opts && opts->dtype == MOE_W4A16)
+    return fail(MOE_ERR_INVALID_ARG, "MOE_W4A16 weights go through moe_ffn_forward_int4");
+  return run_layer(x, W_router, W_gate, W_up, W_down, out, T, d_model, d_ff, E, k, nullptr, 0.f,
+                   opts, nullptr, 0, true);
 }
 
 int moe_block_forward(const void* x, const float* norm_weight, float eps, const float* W_router,

@@ -171,6 +171,25 @@ def test_workspace_layout_is_consistent():
     assert moe.moe_ffn_workspace_size(16, 100, 512, 8, 2, 0) == 0
 
 
+def test_noalloc_validation():
+    # no workspace argument, and shapes beyond the fixed scratch are refused
+    # before anything is enqueued
+    p = [DUMMY] * 6
+    o = moe.moe_opts_init()
+    o.workspace = DUMMY
+    o.workspace_bytes = 1 << 30
+    assert moe.moe_ffn_forward_noalloc(*p, 16, 256, 512, 8, 2, o) == B.MOE_ERR_INVALID_ARG
+    assert moe.moe_ffn_workspace_size(4096, 4096, 14336, 8, 2, 0) > (64 << 20)
+    assert moe.moe_ffn_forward_noalloc(*p, 4096, 4096, 14336, 8, 2, None) == B.MOE_ERR_WORKSPACE
+    assert "scratch" in moe.moe_last_error()
+    assert moe.moe_ffn_forward_noalloc(*p, 16, 100, 512, 8, 2, None) == B.MOE_ERR_UNSUPPORTED
+    o = moe.moe_opts_init()
+    o.dtype = B.MOE_W4A16
+    assert moe.moe_ffn_forward_noalloc(*p, 16, 256, 512, 8, 2, o) == B.MOE_ERR_INVALID_ARG
+    # Mixtral-shaped decode batches fit the 64 MiB scratch
+    assert moe.moe_ffn_workspace_size(256, 4096, 14336, 8, 2, 0) <= (64 << 20)
+
+
 def test_opts_defaults():
     o = moe.moe_opts_init()
     assert o.dtype == B.MOE_BF16 and not o.stream and not o.workspace and not o.router_bias
