@@ -50,7 +50,6 @@ namespace moe {
 constexpr int kTileWaves = 8;                       // two per SIMD
 constexpr int kTileThreads = 64 * kTileWaves;
 constexpr int kBFrags = 2;                          // 32-row token fragments per wave
-constexpr int kBStride = 128;                       // rows between a wave's token fragments
 constexpr int kTileBT = kTileTokens;  // token rows per tile (= padding unit)
 constexpr int kKSteps = kTileBK / 16;               // 32x32x16 MFMA k-steps per stage
 constexpr int kXcds = 8;
@@ -118,15 +117,18 @@ __device__ __forceinline__ void tile_issue_half(const TileCtx& c, char* buf, int
   }
 }
 
-// A stage's fragments (A from `buf`, B from `bbuf`): per k-step, the wave's
-// four A fragments (32 weight rows each) and its NBV valid token fragments.  A fragment a starts at
-// weight row arow(a) of the wave's half, token fragment b at row b * kBStride
-// of the wave's slice.
-template <int NBV, bool GATEUP>
+// A stage's fragments (A from `buf`, B from `bbuf`) for the wave's KS k-steps
+// of the stage (its K part: the stage's k-steps KS * kpart ... + KS - 1, folded
+// into the bases): per k-step, the wave's four A fragments (32 weight rows
+// each) and its NBV valid token fragments.  A fragment a starts at weight row
+// arow(a) of the wave's half, token fragment b at row b * 32 * KS of the
+// wave's slice.  The swizzle term of a token fragment follows the parity of
+// its 32-row block (wt + b * KS), folded into lbB for b = 0.
+template <int NBV, bool GATEUP, int KS>
 __device__ __forceinline__ void tile_load(const TileCtx& c, const char* buf, const char* bbuf,
                                           uint4 (&fa)[kKSteps][4], uint4 (&fb)[kKSteps][kBFrags]) {
 #pragma unroll
-  for (int kk = 0; kk < kKSteps; ++kk) {
+  for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int arow = GATEUP ? (a < 2 ? 0 : 128) + (a & 1) * 32 : a * 32;
@@ -135,20 +137,21 @@ __device__ __forceinline__ void tile_load(const TileCtx& c, const char* buf, con
     }
 #pragma unroll
     for (int b = 0; b < NBV; ++b) {
-      const uint32_t off = c.lbB ^ (uint32_t)((2 * kk) << 4);
-      fb[kk][b] = *reinterpret_cast<const uint4*>(bbuf + off + b * kBStride * kRowBytes);
+      const int par = (b * KS) & 1;
+      const uint32_t off = c.lbB ^ (uint32_t)(((2 * kk) ^ (4 * par)) << 4);
+      fb[kk][b] = *reinterpret_cast<const uint4*>(bbuf + off + b * 32 * KS * kRowBytes);
     }
     // keep the reads in k-step order
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int NBV>
+template <int NBV, int KS>
 __device__ __forceinline__ void tile_mfma(const uint4 (&fa)[kKSteps][4],
                                           const uint4 (&fb)[kKSteps][kBFrags],
                                           f32x16 (&acc)[4][kBFrags]) {
 #pragma unroll
-  for (int kk = 0; kk < kKSteps; ++kk)
+  for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
     for (int b = 0; b < NBV; ++b)
 #pragma unroll
@@ -161,19 +164,19 @@ __device__ __forceinline__ void tile_mfma(const uint4 (&fa)[kKSteps][4],
 // buffer of stage s - 1) after their reads.  XWAIT after the reads, then every
 // wave waits for all of its DMA after the MFMAs (waves 0-3: B of stage s + 1;
 // waves 4-7: A of s + 2).
-template <int NBV, bool GATEUP, bool ISSUE_P, bool ISSUE_R, int XWAIT>
+template <int NBV, bool GATEUP, int KS, bool ISSUE_P, bool ISSUE_R, int XWAIT>
 __device__ __forceinline__ void tile_stage(const TileCtx& c, char* pcur, char* pnxt,
                                            const char* rcur, char* rnew, int s, int g,
                                            uint4 (&fa)[kKSteps][4],
                                            uint4 (&fb)[kKSteps][kBFrags],
                                            f32x16 (&acc)[4][kBFrags]) {
   if (ISSUE_P && g == 0) tile_issue_half(c, pnxt, s + 1, 1);
-  tile_load<NBV, GATEUP>(c, rcur, pcur, fa, fb);
+  tile_load<NBV, GATEUP, KS>(c, rcur, pcur, fa, fb);
   if (ISSUE_R && g == 1) tile_issue_half(c, rnew, s + 2, 0);
   wait_vmcnt<XWAIT>();
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  tile_mfma<NBV>(fa, fb, acc);
+  tile_mfma<NBV, KS>(fa, fb, acc);
   __builtin_amdgcn_sched_barrier(0);
   wait_vmcnt<0>();
   lds_barrier();
@@ -183,7 +186,7 @@ __device__ __forceinline__ void tile_stage(const TileCtx& c, char* pcur, char* p
 // Main loop over K (nk stages, a positive even number).  B of stage s lives
 // in p0/p1 by s % 2 (compile-time), A in ring[s % 3] (run time); every wait
 // count is a compile-time constant, the same in both wave groups.
-template <int NBV, bool GATEUP>
+template <int NBV, bool GATEUP, int KS>
 __device__ __forceinline__ void tile_main_loop(const TileCtx& c, char* p0, char* p1, char* ring,
                                                int nk, int g, f32x16 (&acc)[4][kBFrags]) {
   uint4 fa[kKSteps][4], fb[kKSteps][kBFrags];
@@ -203,15 +206,192 @@ __device__ __forceinline__ void tile_main_loop(const TileCtx& c, char* p0, char*
   int s = 0;
   for (; s < nk - 2; s += 2) {
     const int b1 = inc3(bs), b2 = inc3(b1), b3 = inc3(b2);
-    tile_stage<NBV, GATEUP, true, true, kDmaPerWave>(c, p0, p1, bb(bs), bb(b2), s, g, fa, fb, acc);
-    tile_stage<NBV, GATEUP, true, true, kDmaPerWave>(c, p1, p0, bb(b1), bb(b3), s + 1, g, fa, fb,
-                                                     acc);
+    tile_stage<NBV, GATEUP, KS, true, true, kDmaPerWave>(c, p0, p1, bb(bs), bb(b2), s, g, fa, fb,
+                                                         acc);
+    tile_stage<NBV, GATEUP, KS, true, true, kDmaPerWave>(c, p1, p0, bb(b1), bb(b3), s + 1, g, fa,
+                                                         fb, acc);
     bs = b2;
   }
-  tile_stage<NBV, GATEUP, true, false, 0>(c, p0, p1, bb(bs), nullptr, s, g, fa, fb, acc);
-  tile_stage<NBV, GATEUP, false, false, 0>(c, p1, p0, bb(inc3(bs)), nullptr, s + 1, g, fa, fb,
-                                           acc);
+  tile_stage<NBV, GATEUP, KS, true, false, 0>(c, p0, p1, bb(bs), nullptr, s, g, fa, fb, acc);
+  tile_stage<NBV, GATEUP, KS, false, false, 0>(c, p1, p0, bb(inc3(bs)), nullptr, s + 1, g, fa, fb,
+                                               acc);
   if (g == 0) lds_barrier();                       // same barrier count in both groups
+}
+
+// Split tiles (KS < 4): the waves of K part p > 0 hand their partial sums to
+// the waves of part 0 through LDS (`red`, 64 KiB used), half of the
+// accumulators at a time.  KS = 2: part 1 (waves 4-7) to part 0 (waves 0-3).
+// KS = 1: parts 2, 3 (waves 4-7) to parts 0, 1 (waves 0-3), then part 1
+// (waves 2, 3) to part 0 (waves 0, 1): (p0 + p2) + (p1 + p3), a fixed order.
+// Called with every wave past its last read of the LDS buffers.
+template <int KS>
+__device__ __forceinline__ void tile_reduce_parts(f32x16 (&acc)[4][kBFrags], char* red,
+                                                  int wave, int lane) {
+  float* buf = reinterpret_cast<float*>(red);
+  constexpr int kRounds = KS == 2 ? 1 : 2;
+#pragma unroll
+  for (int r = 0; r < kRounds; ++r) {
+    const int half = r == 0 ? 4 : 2;   // waves [half, 2 half) send to [0, half)
+#pragma unroll
+    for (int ah = 0; ah < 2; ++ah) {   // accumulators a = 2 ah, 2 ah + 1
+      if (wave >= half && wave < 2 * half) {
+        const int slot = wave - half;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int b = 0; b < kBFrags; ++b)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              buf[((slot * 64 + (i * kBFrags + b) * 16 + j) << 6) + lane] = acc[2 * ah + i][b][j];
+      }
+      lds_barrier();
+      if (wave < half) {
+        const int slot = wave;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int b = 0; b < kBFrags; ++b)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              acc[2 * ah + i][b][j] += buf[((slot * 64 + (i * kBFrags + b) * 16 + j) << 6) + lane];
+      }
+      lds_barrier();
+    }
+  }
+}
+
+// Everything after the tile's set-up, for KS k-steps per wave per stage:
+// KS = 4, the whole stage (waves = 2 weight halves x 4 token slices of 32
+// rows, fragments 128 rows apart: 256 rows); KS = 2 (at most 128 valid rows),
+// the two wave groups take the stage's two K halves over 128 rows; KS = 1 (at
+// most 64), four wave pairs take its four k-steps over 64 rows.  Each wave
+// keeps the 128 x 64 fragment shape, so a split tile issues the same MFMAs per
+// LDS read as a full one and takes about KS / 4 of its time.
+template <int KS, bool GATEUP>
+__device__ __forceinline__ void tile_run(TileCtx& c, char* sa0, char* sa1, char* sbr, void* outp,
+                                         int wave, int lane, int tid, int nk, int row0,
+                                         int valid_end, int N, int f0, int part,
+                                         size_t part_stride) {
+  constexpr int FB = GATEUP ? kTileRows / 2 : kTileRows;  // output features per tile
+  constexpr int kStride = 32 * KS;          // rows between a wave's token fragments
+  constexpr int kRowsOut = 2 * kStride;     // tile rows the split tile computes
+  const int wf = wave & 1;                  // weight half
+  const int q = wave >> 1;
+  const int wt = q % KS;                    // token slice
+  const int kpart = q / KS;                 // K part (split tiles)
+  const int g = wave >> 2;                  // wave group (ping-pong)
+
+  // ---- fragment rows: A fragment a of wave half wf, token fragments at rows
+  // wt * 32 and wt * 32 + kStride of the tile; the K part's first k-step
+  // folded into both bases (its chunk bits do not overlap the lane's half bit)
+  {
+    const int r32 = lane & 31, h = lane >> 5;
+    const uint32_t lrow = (uint32_t)r32 * kRowBytes + (uint32_t)((h ^ swz_key(r32)) << 4);
+    const uint32_t kx = (uint32_t)((2 * KS * kpart) << 4);
+    c.lbA = ((uint32_t)(GATEUP ? wf * 64 : wf * 128) * kRowBytes + lrow) ^ kx;
+    c.lbB = ((uint32_t)(wt * 32) * kRowBytes + (lrow ^ (uint32_t)((4 * (wt & 1)) << 4))) ^ kx;
+  }
+  int nbv = 0;                              // valid token fragments of this wave
+#pragma unroll
+  for (int b = 0; b < kBFrags; ++b) nbv += row0 + wt * 32 + b * kStride < valid_end;
+
+  f32x16 acc[4][kBFrags];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < kBFrags; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
+
+  // wave-uniform choice; every variant runs the same DMA and barriers
+  switch (nbv) {
+    case 2: tile_main_loop<2, GATEUP, KS>(c, sa0, sa1, sbr, nk, g, acc); break;
+    case 1: tile_main_loop<1, GATEUP, KS>(c, sa0, sa1, sbr, nk, g, acc); break;
+    default: tile_main_loop<0, GATEUP, KS>(c, sa0, sa1, sbr, nk, g, acc); break;
+  }
+
+  // ---- epilogue.  D of a 32x32 MFMA: lane holds column n = lane % 32 and rows
+  // 8 * (j / 4) + 4 * (lane / 32) + j % 4, j = 0..15: four consecutive
+  // features.  Skipped fragments hold zeros (padding rows).  The tile is
+  // staged in the (now idle) B ring and written back as whole rows with
+  // 16-byte stores.
+  const int r32 = lane & 31, half = lane >> 5;
+  lds_barrier();                            // every wave is past its last LDS read
+  if constexpr (KS < 4) tile_reduce_parts<KS>(acc, sbr, wave, lane);
+  if constexpr (GATEUP) {
+    // every row of the tile's H is written, padding rows (and rows past a
+    // split tile's) as zeros
+    constexpr int kPitch = FB * 2 + 16;     // bf16 row of the h tile, padded
+    static_assert(kTileBT * kPitch <= 3 * kOperBytes, "staging exceeds the B ring");
+    if (kpart == 0) {
+#pragma unroll
+      for (int b = 0; b < kBFrags; ++b) {
+        const int lrow = wt * 32 + b * kStride + r32;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int lfeat = wf * 64 + a * 32 + jj * 8 + half * 4;
+            uint32_t p[2];
+#pragma unroll
+            for (int qq = 0; qq < 2; ++qq) {
+              const float g0 = acc[a][b][jj * 4 + 2 * qq], u0 = acc[a + 2][b][jj * 4 + 2 * qq];
+              const float g1 = acc[a][b][jj * 4 + 2 * qq + 1],
+                          u1 = acc[a + 2][b][jj * 4 + 2 * qq + 1];
+              p[qq] = pack_bf16x2(silu_bf16_out(g0) * u0, silu_bf16_out(g1) * u1);
+            }
+            *reinterpret_cast<uint2*>(sbr + lrow * kPitch + lfeat * 2) = make_uint2(p[0], p[1]);
+          }
+      }
+    }
+    lds_barrier();
+    constexpr int kChunksRow = FB * 2 / 16;  // 16-byte pieces per h row
+    bf16_t* h = reinterpret_cast<bf16_t*>(outp) + (size_t)row0 * N + f0;
+#pragma unroll
+    for (int it = 0; it < kTileBT * kChunksRow / kTileThreads; ++it) {
+      const int qi = it * kTileThreads + tid;
+      const int lrow = qi / kChunksRow, ch = qi % kChunksRow;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (KS == 4 || lrow < kRowsOut)
+        v = *reinterpret_cast<const uint4*>(sbr + lrow * kPitch + ch * 16);
+      *reinterpret_cast<uint4*>(h + (size_t)lrow * N + ch * 8) = v;
+    }
+  } else {
+    // fp32: (token fragment b, feature half ch) = 32 KS rows x 128 features
+    // at a time, written by the part-0 waves of that half.  Rows past a split
+    // tile's are padding, never read, and not written.
+    constexpr int kPitch = 128 * 4 + 16;
+    constexpr int kSlab = 32 * KS;            // rows per (b, ch) round
+    static_assert(kSlab * kPitch <= 3 * kOperBytes, "staging exceeds the B ring");
+    float* y = reinterpret_cast<float*>(outp) + part * part_stride + (size_t)row0 * N + f0;
+#pragma unroll
+    for (int b = 0; b < kBFrags; ++b)
+#pragma unroll
+      for (int ch = 0; ch < 2; ++ch) {
+        if (wf == ch && kpart == 0) {
+          const int lrow = wt * 32 + r32;
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int col = a * 32 + jj * 8 + half * 4;
+              *reinterpret_cast<float4*>(sbr + lrow * kPitch + col * 4) =
+                  make_float4(acc[a][b][jj * 4], acc[a][b][jj * 4 + 1], acc[a][b][jj * 4 + 2],
+                              acc[a][b][jj * 4 + 3]);
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int it = 0; it < kSlab * 32 / kTileThreads; ++it) {
+          const int qi = it * kTileThreads + tid;
+          const int lrow = qi / 32, chunk = qi % 32;
+          const uint4 v = *reinterpret_cast<const uint4*>(sbr + lrow * kPitch + chunk * 16);
+          *reinterpret_cast<uint4*>(y + (size_t)(b * kStride + lrow) * N + ch * 128 +
+                                    chunk * 4) = v;
+        }
+        lds_barrier();
+      }
+  }
 }
 
 template <bool GATEUP>
@@ -248,8 +428,6 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wf = wave & 1, wt = wave >> 1;   // weight half, token slice
-  const int g = wave >> 2;                   // wave group (ping-pong)
 
   // ---- DMA assignment: wave w fills LDS slots [(w % 4) * kDmaPerWave,
   // +kDmaPerWave) of its operand (1 KiB each); slot q's lane i holds LDS chunk
@@ -288,106 +466,17 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
                                : buffer_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
   c.b_on = c.dma_base * (1024 / kRowBytes) < nvalid;
 
-  // ---- fragment rows: A fragment a of wave half wf, token fragments at rows
-  // wt * 32 and wt * 32 + kBStride of the tile
-  {
-    const int r32 = lane & 31, h = lane >> 5;
-    const uint32_t lrow = (uint32_t)r32 * kRowBytes + (uint32_t)((h ^ swz_key(r32)) << 4);
-    c.lbA = (uint32_t)(GATEUP ? wf * 64 : wf * 128) * kRowBytes + lrow;
-    c.lbB = (uint32_t)(wt * 32) * kRowBytes + (lrow ^ (uint32_t)((4 * (wt & 1)) << 4));
-  }
-  int nbv = 0;                              // valid token fragments of this wave
-#pragma unroll
-  for (int b = 0; b < kBFrags; ++b) nbv += row0 + wt * 32 + b * kBStride < valid_end;
-
-  f32x16 acc[4][kBFrags];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < kBFrags; ++b)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
-
-  // wave-uniform choice; every variant runs the same DMA and barriers
+  // short tiles split each stage's k-steps over the wave groups (see tile_run)
   const int nk = Kp / kTileBK;
-  switch (nbv) {
-    case 2: tile_main_loop<2, GATEUP>(c, sa0, sa1, sbr, nk, g, acc); break;
-    case 1: tile_main_loop<1, GATEUP>(c, sa0, sa1, sbr, nk, g, acc); break;
-    default: tile_main_loop<0, GATEUP>(c, sa0, sa1, sbr, nk, g, acc); break;
-  }
-
-  // ---- epilogue.  D of a 32x32 MFMA: lane holds column n = lane % 32 and rows
-  // 8 * (j / 4) + 4 * (lane / 32) + j % 4, j = 0..15: four consecutive
-  // features.  Skipped fragments hold zeros (padding rows).  The tile is
-  // staged in the (now idle) B ring and written back as whole rows with
-  // 16-byte stores; every row of the tile is written, padding rows as zeros.
-  const int r32 = lane & 31, half = lane >> 5;
-  lds_barrier();                            // every wave is past its last LDS read
-  if constexpr (GATEUP) {
-    constexpr int kPitch = FB * 2 + 16;     // bf16 row of the h tile, padded
-    static_assert(kTileBT * kPitch <= 3 * kOperBytes, "staging exceeds the B ring");
-#pragma unroll
-    for (int b = 0; b < kBFrags; ++b) {
-      const int lrow = wt * 32 + b * kBStride + r32;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int lfeat = wf * 64 + a * 32 + jj * 8 + half * 4;
-          uint32_t p[2];
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const float g0 = acc[a][b][jj * 4 + 2 * q], u0 = acc[a + 2][b][jj * 4 + 2 * q];
-            const float g1 = acc[a][b][jj * 4 + 2 * q + 1], u1 = acc[a + 2][b][jj * 4 + 2 * q + 1];
-            p[q] = pack_bf16x2(silu_bf16_out(g0) * u0, silu_bf16_out(g1) * u1);
-          }
-          *reinterpret_cast<uint2*>(sbr + lrow * kPitch + lfeat * 2) = make_uint2(p[0], p[1]);
-        }
-    }
-    lds_barrier();
-    constexpr int kChunksRow = FB * 2 / 16;  // 16-byte pieces per h row
-    bf16_t* h = reinterpret_cast<bf16_t*>(outp) + (size_t)row0 * N + f0;
-#pragma unroll
-    for (int it = 0; it < kTileBT * kChunksRow / kTileThreads; ++it) {
-      const int q = it * kTileThreads + tid;
-      const int lrow = q / kChunksRow, ch = q % kChunksRow;
-      const uint4 v = *reinterpret_cast<const uint4*>(sbr + lrow * kPitch + ch * 16);
-      *reinterpret_cast<uint4*>(h + (size_t)lrow * N + ch * 8) = v;
-    }
-  } else {
-    // fp32: (token fragment b, feature half ch) = 128 rows x 128 features
-    // at a time, written by the waves of that half
-    constexpr int kPitch = 128 * 4 + 16;
-    static_assert(128 * kPitch <= 3 * kOperBytes, "staging exceeds the B ring");
-    float* y = reinterpret_cast<float*>(outp) + part * part_stride + (size_t)row0 * N + f0;
-#pragma unroll
-    for (int b = 0; b < kBFrags; ++b)
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        if (wf == ch) {
-          const int lrow = wt * 32 + r32;
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              const int col = a * 32 + jj * 8 + half * 4;
-              *reinterpret_cast<float4*>(sbr + lrow * kPitch + col * 4) =
-                  make_float4(acc[a][b][jj * 4], acc[a][b][jj * 4 + 1], acc[a][b][jj * 4 + 2],
-                              acc[a][b][jj * 4 + 3]);
-            }
-        }
-        lds_barrier();
-#pragma unroll
-        for (int it = 0; it < 128 * 32 / kTileThreads; ++it) {
-          const int q = it * kTileThreads + tid;
-          const int lrow = q / 32, chunk = q % 32;
-          const uint4 v = *reinterpret_cast<const uint4*>(sbr + lrow * kPitch + chunk * 16);
-          *reinterpret_cast<uint4*>(y + (size_t)(b * kBStride + lrow) * N + ch * 128 +
-                                    chunk * 4) = v;
-        }
-        lds_barrier();
-      }
-  }
+  if (nvalid > 128)
+    tile_run<4, GATEUP>(c, sa0, sa1, sbr, outp, wave, lane, tid, nk, row0, valid_end, N, f0, part,
+                        part_stride);
+  else if (nvalid > 64)
+    tile_run<2, GATEUP>(c, sa0, sa1, sbr, outp, wave, lane, tid, nk, row0, valid_end, N, f0, part,
+                        part_stride);
+  else
+    tile_run<1, GATEUP>(c, sa0, sa1, sbr, outp, wave, lane, tid, nk, row0, valid_end, N, f0, part,
+                        part_stride);
 }
 
 // Feature tiles per XCD-local group of the tile order.  Consecutive

@@ -94,18 +94,29 @@ SMALL = [
     MoEConfig("tile_ragged", 777, 512, 256, 4, 1, "bf16"),
     MoEConfig("tile_fine", 900, 256, 128, 16, 4, "bf16"),
     MoEConfig("tile_split", 800, 1024, 512, 8, 2, "bf16"),   # down GEMM split along K
-    # about 550 rows per expert: two full 256-row token tiles and a short last one
+    # about 550 rows per expert: two full 256-row token tiles and a short last
+    # one (seed 1: 40, 53 and 60 rows, so the tile splits each stage's K over
+    # four wave pairs)
     MoEConfig("tile_multi", 1100, 256, 256, 4, 2, "bf16"),
+    # last tiles of 75 to 105 rows (seed 1): K split over the two wave groups
+    # (and the down GEMM split along K, as in the three cases below)
+    MoEConfig("tile_short128", 700, 512, 256, 4, 2, "bf16"),
+    # last tiles of 123, 128 (the largest split one), 141 and 160 rows
+    MoEConfig("tile_short_edge", 1300, 512, 256, 4, 2, "bf16"),
+    # last tiles of 35, 53, 63 and 65 rows with the down GEMM split along K
+    MoEConfig("tile_short_ksplit", 620, 512, 512, 4, 2, "bf16"),
 ]
 
-TILED = {"tile_small", "tile_ragged", "tile_fine", "tile_split", "tile_multi"}
+TILED = {"tile_small", "tile_ragged", "tile_fine", "tile_split", "tile_multi", "tile_short128",
+         "tile_short_edge", "tile_short_ksplit"}
+DOWN_SPLIT = {"tile_split", "tile_short128", "tile_short_edge", "tile_short_ksplit"}
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_small_shapes(cfg):
     res, _ = full_check(cfg, seed=1)
     assert res["layout"].gemm_variant == (1 if cfg.name in TILED else 0)
-    assert res["layout"].down_splits == (2 if cfg.name == "tile_split" else 1)
+    assert res["layout"].down_splits == (2 if cfg.name in DOWN_SPLIT else 1)
 
 
 def test_all_tokens_to_one_expert():
