@@ -261,10 +261,11 @@ typedef struct moe_ws_layout {
   int64_t block_rows;       /* padding unit of expert segments (token tile)   */
   int64_t max_rows;         /* rows reserved for the permuted layout          */
   int64_t router_blocks;    /* token blocks of the router / scatter kernels   */
+  int64_t y_part_rows;      /* rows of each extra down-GEMM part plane (y_parts) */
   int32_t gemm_variant;     /* 0 = weight-streaming, 1 = LDS-tiled             */
-  int32_t down_splits;      /* K-splits of the down GEMM: y holds this many
-                               partial [max_rows][d_model] blocks, summed by
-                               the combine                                     */
+  int32_t down_splits;      /* K parts into which the down GEMM may split the
+                               token tiles of a partial last round of work-
+                               groups (1: never); see down_sched               */
   int32_t tokens_in_place;  /* 1: the gate/up GEMM reads each row's token from
                                x (or xn) through row_token and xs is not
                                written; 0: it reads the gathered rows of xs    */
@@ -285,8 +286,18 @@ typedef struct moe_ws_layout {
                                with d_model a multiple of 128, or INT4
                                weights) or the LDS-tiled form with k >= 4      */
   size_t h;                 /* [max_rows][d_ff] dtype: SiLU(gate) * up         */
-  size_t y;                 /* [down_splits][max_rows][d_model] float32:
-                               partial expert outputs (their sum is W2 H)       */
+  size_t y;                 /* [max_rows][d_model] float32: expert outputs
+                               W2 H of each row; for the rows of a split token
+                               tile, the first of its K parts                  */
+  size_t y_parts;           /* [down_splits - 1][y_part_rows][d_model] float32:
+                               the other K parts of the split token tiles' rows,
+                               row r at r - down_sched[1]; W2 H is their sum
+                               with y, added in part order                     */
+  size_t down_sched;        /* [2] int32, LDS-tiled form only (else 0 bytes):
+                               written by the expert scan from the token tiles
+                               in use: K parts s in use (1: none split) and the
+                               first row of the split token tiles (the last
+                               ones)                                           */
   size_t block_probs;       /* [router_blocks][E] float32: per-block sums of the
                                full-softmax probabilities (router statistics)  */
   size_t norm_rs;           /* [T] float32: 1/rms of each token; block wrapper

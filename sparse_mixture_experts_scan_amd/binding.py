@@ -46,13 +46,15 @@ class MoeWsLayout(ctypes.Structure):
     _fields_ = [("block_rows", ctypes.c_int64),
                 ("max_rows", ctypes.c_int64),
                 ("router_blocks", ctypes.c_int64),
+                ("y_part_rows", ctypes.c_int64),
                 ("gemm_variant", ctypes.c_int32),
                 ("down_splits", ctypes.c_int32),
                 ("tokens_in_place", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)] + [
         (name, ctypes.c_size_t) for name in
         ("topk_idx", "topk_w", "block_counts", "counts", "offsets", "num_tiles",
-         "tile_expert", "row_token", "tok_row", "xs", "h", "y", "block_probs", "norm_rs", "xn",
+         "tile_expert", "row_token", "tok_row", "xs", "h", "y", "y_parts", "down_sched",
+         "block_probs", "norm_rs", "xn",
          "router_partial", "wdeq", "total")]
 
 

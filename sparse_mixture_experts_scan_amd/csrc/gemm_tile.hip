@@ -270,8 +270,7 @@ __device__ __forceinline__ void tile_reduce_parts(f32x16 (&acc)[4][kBFrags], cha
 template <int KS, bool GATEUP>
 __device__ __forceinline__ void tile_run(TileCtx& c, char* sa0, char* sa1, char* sbr, void* outp,
                                          int wave, int lane, int tid, int nk, int row0,
-                                         int valid_end, int N, int f0, int part,
-                                         size_t part_stride) {
+                                         int valid_end, int N, int f0) {
   constexpr int FB = GATEUP ? kTileRows / 2 : kTileRows;  // output features per tile
   constexpr int kStride = 32 * KS;          // rows between a wave's token fragments
   constexpr int kRowsOut = 2 * kStride;     // tile rows the split tile computes
@@ -346,7 +345,7 @@ __device__ __forceinline__ void tile_run(TileCtx& c, char* sa0, char* sa1, char*
     }
     lds_barrier();
     constexpr int kChunksRow = FB * 2 / 16;  // 16-byte pieces per h row
-    bf16_t* h = reinterpret_cast<bf16_t*>(outp) + (size_t)row0 * N + f0;
+    bf16_t* h = reinterpret_cast<bf16_t*>(outp) + f0;   // outp: this tile's first row
 #pragma unroll
     for (int it = 0; it < kTileBT * kChunksRow / kTileThreads; ++it) {
       const int qi = it * kTileThreads + tid;
@@ -363,7 +362,7 @@ __device__ __forceinline__ void tile_run(TileCtx& c, char* sa0, char* sa1, char*
     constexpr int kPitch = 128 * 4 + 16;
     constexpr int kSlab = 32 * KS;            // rows per (b, ch) round
     static_assert(kSlab * kPitch <= 3 * kOperBytes, "staging exceeds the B ring");
-    float* y = reinterpret_cast<float*>(outp) + part * part_stride + (size_t)row0 * N + f0;
+    float* y = reinterpret_cast<float*>(outp) + f0;   // outp: this tile's first row
 #pragma unroll
     for (int b = 0; b < kBFrags; ++b)
 #pragma unroll
@@ -399,8 +398,9 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
     const bf16_t* __restrict__ act, const bf16_t* __restrict__ W0, const bf16_t* __restrict__ W1,
     void* __restrict__ outp, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ num_tiles,
-    const int32_t* __restrict__ tile_expert, int N, int K, int n_ft, int n_tt, int per_xcd,
-    int parts, size_t part_stride, int fgroup, const int32_t* __restrict__ row_token, int nT) {
+    const int32_t* __restrict__ tile_expert, int N, int K, int n_ft,
+    const int32_t* __restrict__ down_sched, float* __restrict__ y_parts, size_t part_stride,
+    int fgroup, const int32_t* __restrict__ row_token, int nT) {
   // separate __shared__ arrays for the token operand's pair of buffers and
   // the weight operand's ring, so that the compiler can tell which DMA each
   // LDS read depends on
@@ -409,18 +409,43 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) char sbr[3 * kOperBytes];
   constexpr int FB = GATEUP ? kTileRows / 2 : kTileRows;  // output features per tile
 
-  // ---- tile id: XCD-contiguous remap, then groups of `fgroup` feature tiles
+  // ---- tile id.  The grid covers the largest possible work list.  Unsplit
+  // tiles first: the tiles of the first nu token tiles (all of those in use
+  // for gate/up) are dealt out in equal contiguous ranges, one per XCD
+  // (work-groups reach the XCDs round robin, so work-group L runs on XCD
+  // L % 8); inside a range, groups of `fgroup` feature tiles: consecutive
+  // work-groups of an XCD take the group's feature tiles for one token tile,
+  // then the next token tile.  Then (down GEMM, down_sched) the K parts of
+  // the remaining token tiles' tiles, dispatched last so that they fill the
+  // final round.  Work-groups past the list exit at once.
+  const int nt = *num_tiles;                // token tiles in use
+  int parts = 1, nu = nt;                   // K parts of split tiles, unsplit token tiles
+  if (!GATEUP) {
+    parts = down_sched[0];
+    nu = down_sched[1] / kTileBT;
+  }
+  const int n_un = nu * n_ft;
+  const int per_xcd = (n_un + kXcds - 1) / kXcds;
   const int L = blockIdx.x;
-  int Lp = (L % kXcds) * per_xcd + L / kXcds;
-  if (Lp >= parts * n_ft * n_tt) return;
-  const int part = Lp / (n_ft * n_tt);      // K-split part (slowest)
-  Lp -= part * n_ft * n_tt;
-  const int grp = Lp / (fgroup * n_tt);
-  const int rem = Lp - grp * fgroup * n_tt;
-  const int gsize = min(fgroup, n_ft - grp * fgroup);
-  const int tt = rem / gsize;
-  const int ft = grp * fgroup + rem % gsize;
-  if (tt >= *num_tiles) return;             // past the token tiles in use
+  int part = 0, tparts = 1, tt, ft;         // this tile's K part and part count
+  if (L < per_xcd * kXcds) {
+    int Lp = (L % kXcds) * per_xcd + L / kXcds;
+    if (Lp >= n_un) return;
+    const int grp = Lp / (fgroup * nu);
+    const int rem = Lp - grp * fgroup * nu;
+    const int gsize = min(fgroup, n_ft - grp * fgroup);
+    tt = rem / gsize;
+    ft = grp * fgroup + rem % gsize;
+  } else {
+    const int n_sp = (nt - nu) * n_ft;      // split tiles
+    const int i = L - per_xcd * kXcds;
+    if (parts == 1 || i >= parts * n_sp) return;
+    tparts = parts;
+    part = i / n_sp;
+    const int j = i - part * n_sp;
+    tt = nu + j / n_ft;
+    ft = j % n_ft;
+  }
   const int e = tile_expert[tt];
   const int row0 = tt * kTileBT;
   const int valid_end = offsets[e] + counts[e];
@@ -434,7 +459,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
   // position p = q * 64 + i = row * kChunks + swizzled chunk.
   TileCtx c;
   c.dma_base = (wave & 3) * kDmaPerWave;
-  const int Kp = K / parts;                 // K columns of this part
+  const int Kp = K / tparts;                // K columns of this part (unsplit: all)
   c.k_byte0 = (uint32_t)(part * Kp) * 2;
   const uint32_t row_bytes = (uint32_t)K * 2;
 #pragma unroll
@@ -466,17 +491,23 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
                                : buffer_rsrc(act + (size_t)row0 * K, (uint32_t)nvalid * row_bytes);
   c.b_on = c.dma_base * (1024 / kRowBytes) < nvalid;
 
+  // output rows of this tile: H, or the first K part of Y in y, or (a later
+  // part of a split token tile) its plane of y_parts
+  void* dst;
+  if constexpr (GATEUP) {
+    dst = reinterpret_cast<bf16_t*>(outp) + (size_t)row0 * N;
+  } else {
+    dst = part == 0 ? reinterpret_cast<float*>(outp) + (size_t)row0 * N
+                    : y_parts + (part - 1) * part_stride + (size_t)(row0 - nu * kTileBT) * N;
+  }
   // short tiles split each stage's k-steps over the wave groups (see tile_run)
   const int nk = Kp / kTileBK;
   if (nvalid > 128)
-    tile_run<4, GATEUP>(c, sa0, sa1, sbr, outp, wave, lane, tid, nk, row0, valid_end, N, f0, part,
-                        part_stride);
+    tile_run<4, GATEUP>(c, sa0, sa1, sbr, dst, wave, lane, tid, nk, row0, valid_end, N, f0);
   else if (nvalid > 64)
-    tile_run<2, GATEUP>(c, sa0, sa1, sbr, outp, wave, lane, tid, nk, row0, valid_end, N, f0, part,
-                        part_stride);
+    tile_run<2, GATEUP>(c, sa0, sa1, sbr, dst, wave, lane, tid, nk, row0, valid_end, N, f0);
   else
-    tile_run<1, GATEUP>(c, sa0, sa1, sbr, outp, wave, lane, tid, nk, row0, valid_end, N, f0, part,
-                        part_stride);
+    tile_run<1, GATEUP>(c, sa0, sa1, sbr, dst, wave, lane, tid, nk, row0, valid_end, N, f0);
 }
 
 // Feature tiles per XCD-local group of the tile order.  Consecutive
@@ -494,34 +525,37 @@ static int tile_feat_group(const Dims& D, bool gateup) {
 
 template <bool GATEUP>
 static void tile_launch(const Dims& D, const void* act, const int32_t* row_token, const void* W0,
-                        const void* W1, void* out, const int32_t* counts,
-                        const int32_t* offsets, const int32_t* num_tiles,
-                        const int32_t* tile_expert, hipStream_t s) {
+                        const void* W1, void* out, float* y_parts, int64_t part_rows,
+                        const int32_t* down_sched, const int32_t* counts, const int32_t* offsets,
+                        const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s) {
   const int N = GATEUP ? D.f : D.d;
   const int K = GATEUP ? D.d : D.f;
   const int FB = GATEUP ? kTileRows / 2 : kTileRows;
   const int n_ft = N / FB;
-  const int n_tt = D.max_tiles;
-  const int parts = GATEUP ? 1 : D.down_splits;
-  const int total = parts * n_ft * n_tt;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int grid = per_xcd * kXcds;
+  // the longest work list: every tile unsplit, plus the extra pieces of at
+  // most kCus / 2 split tiles (3 x kCus / 4 with four parts, kCus / 2 with
+  // two), plus the rounding of the XCD ranges; unused work-groups exit
+  const int total = n_ft * D.max_tiles + (GATEUP ? 0 : kCus) + kXcds;
+  const int grid = (total + kXcds - 1) / kXcds * kXcds;
   tile_gemm_kernel<GATEUP><<<grid, kTileThreads, 0, s>>>(
       (const bf16_t*)act, (const bf16_t*)W0, (const bf16_t*)W1, out, counts, offsets, num_tiles,
-      tile_expert, N, K, n_ft, n_tt, per_xcd, parts, (size_t)D.max_rows * N,
+      tile_expert, N, K, n_ft, down_sched, y_parts, (size_t)part_rows * N,
       tile_feat_group(D, GATEUP), row_token, D.T);
 }
 
 void launch_gateup_tile(const Dims& D, const void* x, const int32_t* row_token, const void* Wg,
                         const void* Wu, void* h, const int32_t* counts, const int32_t* offsets,
                         const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s) {
-  tile_launch<true>(D, x, row_token, Wg, Wu, h, counts, offsets, num_tiles, tile_expert, s);
+  tile_launch<true>(D, x, row_token, Wg, Wu, h, nullptr, 0, nullptr, counts, offsets, num_tiles,
+                    tile_expert, s);
 }
 
-void launch_down_tile(const Dims& D, const void* h, const void* Wd, float* y,
-                      const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
+void launch_down_tile(const Dims& D, const void* h, const void* Wd, float* y, float* y_parts,
+                      int64_t part_rows, const int32_t* down_sched, const int32_t* counts,
+                      const int32_t* offsets, const int32_t* num_tiles,
                       const int32_t* tile_expert, hipStream_t s) {
-  tile_launch<false>(D, h, nullptr, Wd, nullptr, y, counts, offsets, num_tiles, tile_expert, s);
+  tile_launch<false>(D, h, nullptr, Wd, nullptr, y, y_parts, part_rows, down_sched, counts,
+                     offsets, num_tiles, tile_expert, s);
 }
 
 }  // namespace moe

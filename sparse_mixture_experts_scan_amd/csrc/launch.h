@@ -37,6 +37,12 @@ struct ScanArgs {
   // with a single router block: non-NULL makes the select pass also write the
   // row maps (tok_row, row_token), for a GEMM that reads the tokens in place
   int32_t* tok_row;
+  // LDS-tiled form: the down GEMM's schedule (K parts in use, first split
+  // row), from the token tiles in use, its feature tiles and the most parts
+  // the plan allows; NULL otherwise
+  int32_t* down_sched;
+  int down_n_ft;
+  int down_max_parts;
 };
 // With a single router block (router_fuses_scan) the select pass also runs
 // the expert scan and launch_scan is a no-op, which saves a launch for small T.
@@ -69,8 +75,11 @@ void launch_down_stream(const Dims& D, const void* h, const void* Wd, float* y,
 void launch_gateup_tile(const Dims& D, const void* x, const int32_t* row_token, const void* Wg,
                         const void* Wu, void* h, const int32_t* counts, const int32_t* offsets,
                         const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s);
-void launch_down_tile(const Dims& D, const void* h, const void* Wd, float* y,
-                      const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
+// y: the first K part of every row; y_parts: [D.down_splits - 1][part_rows]
+// further parts of the split token tiles' rows (see down_sched)
+void launch_down_tile(const Dims& D, const void* h, const void* Wd, float* y, float* y_parts,
+                      int64_t part_rows, const int32_t* down_sched, const int32_t* counts,
+                      const int32_t* offsets, const int32_t* num_tiles,
                       const int32_t* tile_expert, hipStream_t s);
 // INT4 expert weights: quantizer, dequantizer (to bf16, for the tiled form)
 // and the weight-streaming GEMMs that read INT4 directly
@@ -137,7 +146,9 @@ void launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 void launch_empty_stats(int E, int32_t* counts_out, float* prob_out, float* loss_out,
                         hipStream_t s);
 
-void launch_combine(const Dims& D, const float* y, const int32_t* tok_row, const float* w,
+// y_parts / down_sched as for launch_down_tile (down_sched NULL: y alone)
+void launch_combine(const Dims& D, const float* y, const float* y_parts, int64_t part_rows,
+                    const int32_t* down_sched, const int32_t* tok_row, const float* w,
                     const void* resid, void* out, hipStream_t s);
 
 }  // namespace moe

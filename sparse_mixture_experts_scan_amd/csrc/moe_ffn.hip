@@ -244,6 +244,9 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   void* xs = ws + L.xs;
   void* h = ws + L.h;
   float* y = reinterpret_cast<float*>(ws + L.y);
+  float* y_parts = reinterpret_cast<float*>(ws + L.y_parts);
+  int32_t* down_sched = L.gemm_variant == 1 ? reinterpret_cast<int32_t*>(ws + L.down_sched)
+                                            : nullptr;
   float* rpart = reinterpret_cast<float*>(ws + L.router_partial);
   float* bprob = (o.router_prob_out || o.balance_loss_out)
                      ? reinterpret_cast<float*>(ws + L.block_probs) : nullptr;
@@ -266,9 +269,18 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   const void* tok = norm_w ? xn : x;
   const bool gather = L.tokens_in_place != 0;
   const bool maps_in_router = gather && moe::router_fuses_scan(D);
-  const moe::ScanArgs sa{counts,    offsets,   num_tiles,         tile_expert,
-                         row_token, o.expert_counts_out, o.router_prob_out, o.balance_loss_out,
-                         maps_in_router ? tok_row : nullptr};
+  const moe::ScanArgs sa{counts,
+                         offsets,
+                         num_tiles,
+                         tile_expert,
+                         row_token,
+                         o.expert_counts_out,
+                         o.router_prob_out,
+                         o.balance_loss_out,
+                         maps_in_router ? tok_row : nullptr,
+                         down_sched,
+                         (int)(d_model / moe::kTileRows),
+                         D.down_splits};
   moe::launch_router(D, x, W_router, o.router_bias, idx, w, blk, rpart, bprob, norm_w, rs,
                      nullptr, sa, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(1)) != hipSuccess)
@@ -309,12 +321,14 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   if (q4 && L.gemm_variant == 0)
     moe::launch_down_q4(D, h, q4[2], y, counts, offsets, num_tiles, tile_expert, s);
   else if (L.gemm_variant == 1)
-    moe::launch_down_tile(D, h, W_down, y, counts, offsets, num_tiles, tile_expert, s);
+    moe::launch_down_tile(D, h, W_down, y, y_parts, L.y_part_rows, down_sched, counts, offsets,
+                          num_tiles, tile_expert, s);
   else
     moe::launch_down_stream(D, h, W_down, y, counts, offsets, num_tiles, tile_expert, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(5)) != hipSuccess)
     return hip_fail(e, "down launch");
-  moe::launch_combine(D, y, tok_row, w, norm_w ? x : nullptr, out, s);
+  moe::launch_combine(D, y, y_parts, L.y_part_rows, down_sched, tok_row, w, norm_w ? x : nullptr,
+                      out, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(6)) != hipSuccess)
     return hip_fail(e, "combine launch");
   return MOE_OK;
@@ -510,8 +524,9 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   if ((e = mark(0)) != hipSuccess) return hip_fail(e, "hipEventRecord");
   // routing and permutation of the forward pass, the permuted upstream
   // gradient and the 128-row tile table
-  const moe::ScanArgs sa{counts, offsets, I(b.num_tiles), I(b.tile_expert), row_token,
-                         nullptr, nullptr, nullptr, nullptr};
+  const moe::ScanArgs sa{counts,  offsets, I(b.num_tiles), I(b.tile_expert), row_token,
+                         nullptr, nullptr, nullptr,          nullptr,          nullptr,
+                         0,       1};
   moe::launch_router(D, x, W_router, o.router_bias, idx, w, I(b.block_counts),
                      F(b.router_partial), nullptr, nullptr, nullptr, F(b.logits), sa, s);
   moe::launch_scan(D, I(b.block_counts), sa, nullptr, s);

@@ -62,19 +62,19 @@ bool tile_shape_ok(const Dims& D) {
          kTileRows * kmax * 2 < (int64_t(1) << 31);
 }
 
-// K-splits of the down GEMM: the expected tile count (ceil(rows / BT) plus
-// about half a tile of padding per expert) is spread over the CUs; a split
-// that fills the last round of workgroups markedly better is taken.
+// Each K part of a split tile must be whole pairs of K stages.
 int tile_down_splits(const Dims& D) {
-  constexpr int kCus = 256;
+  if (D.f % (4 * kTileBK * kTileNS) == 0) return 4;
+  if (D.f % (2 * kTileBK * kTileNS) == 0) return 2;
+  return 1;
+}
+
+// The scan splits whole token tiles whose parts fit one round of kCus
+// work-groups: at most kCus / 2 tiles (two parts each), kCus / 2 / n_ft
+// token tiles.
+int tile_down_split_tiles(const Dims& D) {
   const int n_ft = D.d / kTileRows;
-  const double tiles = n_ft * ((double)D.T * D.k / kTileTokens + D.E * 0.5);
-  auto fill = [&](int sp) {
-    const double t = tiles * sp;
-    return t / (std::ceil(t / kCus) * kCus);
-  };
-  const bool can2 = D.f % (2 * kTileBK * kTileNS) == 0;
-  return (can2 && fill(1) < 0.9 && fill(2) > fill(1) + 0.05) ? 2 : 1;
+  return std::max(1, std::min(D.max_tiles, kCus / 2 / n_ft));
 }
 
 // Reading the tokens in place saves the scatter's copy of k rows per token
@@ -160,7 +160,10 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   // gathered rows only when the gate/up GEMM does not read the tokens in place
   L.xs = c.take(L.tokens_in_place ? 0 : es * D.max_rows * d);
   L.h = c.take(es * D.max_rows * f);
-  L.y = c.take(sizeof(float) * D.down_splits * D.max_rows * d);
+  L.y = c.take(sizeof(float) * D.max_rows * d);
+  L.y_part_rows = D.down_splits > 1 ? (int64_t)tile_down_split_tiles(D) * D.BT : 0;
+  L.y_parts = c.take(sizeof(float) * (D.down_splits - 1) * L.y_part_rows * d);
+  L.down_sched = c.take(variant == 1 ? 2 * sizeof(int32_t) : 0);
   L.block_probs = c.take(sizeof(float) * D.nblk * E);
   // the normalised tokens and their 1/rms only for the block wrapper
   L.norm_rs = c.take(block ? sizeof(float) * T : 0);

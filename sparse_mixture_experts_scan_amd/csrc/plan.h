@@ -33,6 +33,7 @@ constexpr int kBwdRowTile = MOE_BG_M;
 constexpr int kBwdTileBT = 256;        // tile extent of the 256 x 256 backward GEMMs
 constexpr int kBwdRouterSlices = 32;   // token slices of the router weight gradient
 constexpr int kTileMinRows = 96;       // average rows per expert from which the tiled form runs
+constexpr int kCus = 256;              // compute units the tile schedules fill (MI355X)
 
 struct Dims {
   int T, d, f, E, k;   // tokens, d_model, d_ff, experts, top-k
@@ -41,7 +42,7 @@ struct Dims {
   int BT;              // token tile = padding unit of expert segments
   int max_rows;        // rows reserved for the permuted layout
   int max_tiles;       // max_rows / BT
-  int down_splits;     // K-splits of the down GEMM (partial Y blocks)
+  int down_splits;     // K parts into which the down GEMM may split a token tile (1: never)
   int router_splits;   // d_model splits of the router scores (1 = fused kernel)
   bool bf16;           // element type of x / weights / out
   bool w4;             // expert weights in INT4 (bf16 activations)
@@ -55,7 +56,12 @@ bool router_fuses_scan(const Dims& D);
 // whether the weight-streaming gate/up GEMM reads the tokens in place
 bool stream_gathers_in_place(const Dims& D);
 bool tile_shape_ok(const Dims& D);
-int tile_down_splits(const Dims& D);   // K-split count of the tiled down GEMM
+// K parts into which the tiled down GEMM may split the token tiles of a
+// partial last round (see expert_scan_kernel's schedule): 4 or 2 when d_ff
+// splits into whole pairs of K stages, else 1
+int tile_down_splits(const Dims& D);
+// token tiles whose down-GEMM parts the extra Y planes hold at most
+int tile_down_split_tiles(const Dims& D);
 // whether the tiled gate/up GEMM reads the tokens in place
 bool tile_gathers_in_place(const Dims& D);
 bool q4_group_ok(int K, int G);

@@ -304,7 +304,29 @@ __device__ __forceinline__ void expert_scan_block(
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ num_tiles,
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ row_token,
     int32_t* __restrict__ counts_out, int nT, const float* __restrict__ blk_prob,
-    float* __restrict__ prob_out, float* __restrict__ loss_out);
+    float* __restrict__ prob_out, float* __restrict__ loss_out, const ScanArgs& sa);
+
+// Schedule of the LDS-tiled down GEMM, from the ntiles token tiles in use and
+// its n_ft feature tiles: whole rounds of kCus work-groups run unsplit tiles.
+// The tiles left for a partial last round, rounded up to whole token tiles
+// (the last ones), are split along K into 4 parts if the pieces fit one
+// round, else into 2 if those fit, which fills that round with short pieces
+// instead of leaving most CUs idle.  Writes the parts in use (1: none) and
+// the first row of the split token tiles.
+__device__ inline void write_down_schedule(const ScanArgs& sa, int ntiles, int BT) {
+  const int n_ft = sa.down_n_ft;
+  int parts = 1, split_tt = ntiles;
+  const int rest = (ntiles * n_ft) % kCus;
+  if (rest > 0) {
+    const int n_sp_tt = min(ntiles, (rest + n_ft - 1) / n_ft);
+    const int n_sp = n_sp_tt * n_ft;
+    if (sa.down_max_parts >= 4 && 4 * n_sp <= kCus) parts = 4;
+    else if (sa.down_max_parts >= 2 && 2 * n_sp <= kCus) parts = 2;
+    if (parts > 1) split_tt = ntiles - n_sp_tt;
+  }
+  sa.down_sched[0] = parts;
+  sa.down_sched[1] = split_tt * BT;
+}
 
 // Row maps of one router block (kRouterTokens tokens), run by all
 // kRouterThreads threads (contains a barrier): thread p < kRouterTokens * k
@@ -403,7 +425,10 @@ __device__ __forceinline__ void select_single_block(
   if (tid <= E) sa.offsets[tid] = s_off[tid];
   const int P = s_off[E];
   const int ntiles = P / BT;
-  if (tid == 0) *sa.num_tiles = ntiles;
+  if (tid == 0) {
+    *sa.num_tiles = ntiles;
+    if (sa.down_sched) write_down_schedule(sa, ntiles, BT);
+  }
   for (int i = tid; i < max_tiles; i += kRouterThreads) {
     int ex = -1;
     if (i < ntiles) {
@@ -515,7 +540,7 @@ __device__ __forceinline__ void expert_scan_block(
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ num_tiles,
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ row_token,
     int32_t* __restrict__ counts_out, int nT, const float* __restrict__ blk_prob,
-    float* __restrict__ prob_out, float* __restrict__ loss_out) {
+    float* __restrict__ prob_out, float* __restrict__ loss_out, const ScanArgs& sa) {
   __shared__ int part[256];
   __shared__ int s_cnt[64];
   __shared__ int s_off[65];
@@ -570,7 +595,10 @@ __device__ __forceinline__ void expert_scan_block(
   if (tid <= E) offsets[tid] = s_off[tid];
   const int P = s_off[E];
   const int ntiles = P / BT;
-  if (tid == 0) *num_tiles = ntiles;
+  if (tid == 0) {
+    *num_tiles = ntiles;
+    if (sa.down_sched) write_down_schedule(sa, ntiles, BT);
+  }
   for (int i = tid; i < max_tiles; i += 256) {
     int ex = -1;
     if (i < ntiles) {
@@ -610,7 +638,7 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(ScanArgs a, int32_t* _
                                                           const float* __restrict__ blk_prob) {
   expert_scan_block(blk, nblk, E, Epow2, BT, max_rows, max_tiles, a.counts, a.offsets,
                     a.num_tiles, a.tile_expert, a.row_token, a.counts_out, nT, blk_prob,
-                    a.prob_out, a.loss_out);
+                    a.prob_out, a.loss_out, a);
 }
 
 // ---------------------------------------------------------------------------
@@ -649,32 +677,39 @@ __global__ __launch_bounds__(kRouterThreads) void scatter_gather_kernel(
 
 // ---------------------------------------------------------------------------
 // a5: out[t] = sum_j w[t][j] * Y[tok_row[t][j]], fp32 FMA in slot order,
-// one rounding to the output type.  A gather, so no atomics.  When the down
-// GEMM was split along K, Y[r] is the sum of its partial blocks, added in
-// block order before the gate weight is applied.
+// one rounding to the output type.  A gather, so no atomics.  Rows of the
+// token tiles the down GEMM split along K (down_sched) sum their K parts in
+// part order before the gate weight is applied.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+                                                      const float* __restrict__ y_parts,
+                                                      size_t part_stride,
+                                                      const int32_t* __restrict__ down_sched,
                                                       const int32_t* __restrict__ tok_row,
                                                       const float* __restrict__ w, int d, int k,
-                                                      int splits, size_t split_stride,
                                                       const T* __restrict__ resid,
                                                       T* __restrict__ out) {
   const int t = blockIdx.x;
   __shared__ int s_row[MOE_MAX_TOPK];
   __shared__ float s_w[MOE_MAX_TOPK];
+  __shared__ int s_parts[MOE_MAX_TOPK];
   if (threadIdx.x < k) {
-    s_row[threadIdx.x] = tok_row[(size_t)t * k + threadIdx.x];
+    const int r = tok_row[(size_t)t * k + threadIdx.x];
+    s_row[threadIdx.x] = r;
     s_w[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+    s_parts[threadIdx.x] = (down_sched && r >= down_sched[1]) ? down_sched[0] : 1;
   }
   __syncthreads();
+  const int split_row0 = down_sched ? down_sched[1] : 0;
   // blockIdx.y: column slice (small T spreads a token over several blocks)
   for (int c = blockIdx.y * 256 + threadIdx.x; c < d / 4; c += 256 * gridDim.y) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
       float4 v = reinterpret_cast<const float4*>(y + (size_t)s_row[j] * d)[c];
-      for (int p = 1; p < splits; ++p) {   // partial K blocks, fixed order
-        const float4 q = reinterpret_cast<const float4*>(y + p * split_stride + (size_t)s_row[j] * d)[c];
+      for (int p = 1; p < s_parts[j]; ++p) {   // further K parts, in part order
+        const float4 q = reinterpret_cast<const float4*>(
+            y_parts + (p - 1) * part_stride + (size_t)(s_row[j] - split_row0) * d)[c];
         v.x += q.x;
         v.y += q.y;
         v.z += q.z;
@@ -778,19 +813,20 @@ void launch_empty_stats(int E, int32_t* counts_out, float* prob_out, float* loss
   empty_stats_kernel<<<1, 64, 0, s>>>(E, counts_out, prob_out, loss_out);
 }
 
-void launch_combine(const Dims& D, const float* y, const int32_t* tok_row, const float* w,
+void launch_combine(const Dims& D, const float* y, const float* y_parts, int64_t part_rows,
+                    const int32_t* down_sched, const int32_t* tok_row, const float* w,
                     const void* resid, void* out, hipStream_t s) {
-  const size_t stride = (size_t)D.max_rows * D.d;
+  const size_t stride = (size_t)part_rows * D.d;
   // column slices of 256 float4 chunks while the tokens alone give few blocks
   int cs = 1;
   while (D.T * cs < 256 && cs * 2 * 256 * 4 <= D.d) cs *= 2;
   const dim3 grid(D.T, cs);
   if (D.bf16)
-    combine_kernel<bf16_t><<<grid, 256, 0, s>>>(y, tok_row, w, D.d, D.k, D.down_splits, stride,
-                                                (const bf16_t*)resid, (bf16_t*)out);
+    combine_kernel<bf16_t><<<grid, 256, 0, s>>>(y, y_parts, stride, down_sched, tok_row, w, D.d,
+                                                D.k, (const bf16_t*)resid, (bf16_t*)out);
   else
-    combine_kernel<float><<<grid, 256, 0, s>>>(y, tok_row, w, D.d, D.k, D.down_splits, stride,
-                                               (const float*)resid, (float*)out);
+    combine_kernel<float><<<grid, 256, 0, s>>>(y, y_parts, stride, down_sched, tok_row, w, D.d,
+                                               D.k, (const float*)resid, (float*)out);
 }
 
 }  // namespace moe

@@ -72,6 +72,9 @@ def run_gpu(cfg: MoEConfig, dinp: dict, *, device="cuda", keep_ws=True, block_ep
             num_tiles=int(i32(lay.num_tiles, 1)[0]),
             tile_expert=i32(lay.tile_expert, R // lay.block_rows),
             row_token=i32(lay.row_token, R), tok_row=i32(lay.tok_row, T * k).reshape(T, k))
+        # the down GEMM's schedule: K parts of the split token tiles, first split row
+        res["down_sched"] = (tuple(int(v) for v in i32(lay.down_sched, 2))
+                             if lay.gemm_variant == 1 else (1, R))
         if block_eps is not None:
             res["norm_rs"] = ws[lay.norm_rs:lay.norm_rs + 4 * T].view(torch.float32).cpu().numpy()
             es = 2 if cfg.dtype == "bf16" else 4
@@ -83,20 +86,26 @@ def run_gpu(cfg: MoEConfig, dinp: dict, *, device="cuda", keep_ws=True, block_ep
 
 
 def ws_rows(res, cfg: MoEConfig, which: str, rows) -> np.ndarray:
-    """Rows of a workspace matrix (xs, h: element type; y: fp32, the sum of
-    its K-split partial blocks) as float32 (float64 for y)."""
+    """Rows of a workspace matrix (xs, h: element type; y: fp32, for rows of
+    the token tiles the down GEMM split along K the sum of their parts in y and
+    y_parts, in part order) as float32 (float64 for y)."""
     lay = res["layout"]
     ws = res["_ws"]
     width = cfg.d_ff if which == "h" else cfg.d_model
     es = 4 if (which == "y" or cfg.dtype == "f32") else 2
     off = getattr(lay, which)
-    parts = lay.down_splits if which == "y" else 1
+    sparts, split_row0 = res.get("down_sched", (1, lay.max_rows))
     out = []
     for r in rows:
         acc = None
+        parts = sparts if (which == "y" and r >= split_row0) else 1
         for p in range(parts):
-            base = off + p * lay.max_rows * width * es
-            b = ws[base + r * width * es: base + (r + 1) * width * es]
+            if p == 0:
+                base, rr = off, r
+            else:
+                base = lay.y_parts + (p - 1) * lay.y_part_rows * width * es
+                rr = r - split_row0
+            b = ws[base + rr * width * es: base + (rr + 1) * width * es]
             if es == 2:
                 v = as_f32(b.view(torch.int16).cpu().numpy().view(np.uint16))
             else:

@@ -112,7 +112,9 @@ def layout_spans(lay, T, d, f, E, k, dt, block):
             ("offsets", 4 * (E + 1)), ("num_tiles", 4),
             ("tile_expert", 4 * lay.max_rows // lay.block_rows), ("row_token", 4 * lay.max_rows),
             ("tok_row", 4 * T * k), ("xs", 0 if in_place else es * lay.max_rows * d),
-            ("h", es * lay.max_rows * f), ("y", 4 * lay.down_splits * lay.max_rows * d),
+            ("h", es * lay.max_rows * f), ("y", 4 * lay.max_rows * d),
+            ("y_parts", 4 * (lay.down_splits - 1) * lay.y_part_rows * d),
+            ("down_sched", 8 if lay.gemm_variant == 1 else 0),
             ("block_probs", 4 * lay.router_blocks * E),
             ("norm_rs", 4 * T if block else 0), ("xn", es * T * d if block else 0)]
 
@@ -151,11 +153,16 @@ def test_workspace_layout_is_consistent():
     assert moe.moe_block_workspace_size(16, 256, 512, 8, 2, B.MOE_W4A16) == 0
     with pytest.raises(moe.MoeError):
         moe.moe_block_workspace_layout(16, 256, 512, 8, 2, B.MOE_W4A16)
-    # the tiled down GEMM of the Mixtral prefill shape is split along K (its
-    # 576 tiles fill 256 CUs badly), the fine-grained shape's is not
-    assert moe.moe_ffn_workspace_layout(4096, 4096, 14336, 8, 2, 0).down_splits == 2
-    assert moe.moe_ffn_workspace_layout(4096, 4096, 3584, 64, 8, 0).down_splits == 1
-    assert moe.moe_ffn_workspace_layout(16, 4096, 14336, 8, 2, 0).down_splits == 1
+    # the tiled down GEMM may split token tiles into 4 K parts when d_ff is a
+    # multiple of 512 (whole pairs of 64-wide stages per part), 2 for 256;
+    # the extra part planes hold up to kCus / 2 / n_ft token tiles
+    for shape, parts, rows in (((4096, 4096, 14336, 8, 2, 0), 4, 8 * 256),
+                               ((4096, 4096, 3584, 64, 8, 0), 4, 8 * 256),
+                               ((1000, 256, 384, 8, 2, 0), 1, 0),
+                               ((700, 512, 256, 4, 2, 0), 2, 10 * 256),   # every token tile
+                               ((16, 4096, 14336, 8, 2, 0), 1, 0)):
+        lay = moe.moe_ffn_workspace_layout(*shape)
+        assert (lay.down_splits, lay.y_part_rows) == (parts, rows), shape
     # which gate/up GEMMs read the tokens in place (no Xs): weight-streaming
     # with bf16 weights and d_model % 128 == 0 or with INT4 weights, and the
     # tiled form with k >= 4

@@ -105,18 +105,35 @@ SMALL = [
     MoEConfig("tile_short_edge", 1300, 512, 256, 4, 2, "bf16"),
     # last tiles of 35, 53, 63 and 65 rows with the down GEMM split along K
     MoEConfig("tile_short_ksplit", 620, 512, 512, 4, 2, "bf16"),
+    # the down GEMM's schedule at d_model 4096 (16 feature tiles): 20 token
+    # tiles (seed 1) = one full round of 256 tiles and 64 more, so the last 4
+    # token tiles run in 4 K parts; 22 token tiles: the last 6 in 2 parts;
+    # 16 token tiles: exactly one round, nothing split
+    MoEConfig("tile_sched4", 2048, 4096, 512, 8, 2, "bf16"),
+    MoEConfig("tile_sched2", 2100, 4096, 512, 8, 2, "bf16"),
+    MoEConfig("tile_sched1", 1800, 4096, 512, 8, 2, "bf16"),
 ]
 
 TILED = {"tile_small", "tile_ragged", "tile_fine", "tile_split", "tile_multi", "tile_short128",
-         "tile_short_edge", "tile_short_ksplit"}
-DOWN_SPLIT = {"tile_split", "tile_short128", "tile_short_edge", "tile_short_ksplit"}
+         "tile_short_edge", "tile_short_ksplit", "tile_sched4", "tile_sched2", "tile_sched1"}
+# the down GEMM's schedule (K parts, first split token tile) at seed 1;
+# fewer tiles than CUs: every token tile split
+DOWN_SCHED = {"tile_split": (4, 0), "tile_short128": (2, 0), "tile_short_ksplit": (4, 0),
+              "tile_sched4": (4, 16), "tile_sched2": (2, 16), "tile_sched1": (1, 16)}
 
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_small_shapes(cfg):
     res, _ = full_check(cfg, seed=1)
-    assert res["layout"].gemm_variant == (1 if cfg.name in TILED else 0)
-    assert res["layout"].down_splits == (2 if cfg.name in DOWN_SPLIT else 1)
+    lay = res["layout"]
+    assert lay.gemm_variant == (1 if cfg.name in TILED else 0)
+    if lay.gemm_variant == 1:
+        # the most K parts d_ff allows (whole pairs of 64-wide K stages)
+        want = 4 if cfg.d_ff % 512 == 0 else 2 if cfg.d_ff % 256 == 0 else 1
+        assert lay.down_splits == want
+    if cfg.name in DOWN_SCHED:
+        parts, tt0 = DOWN_SCHED[cfg.name]
+        assert res["down_sched"] == (parts, tt0 * 256), res["down_sched"]
 
 
 def test_all_tokens_to_one_expert():
@@ -163,6 +180,12 @@ def test_workload_full_tensor(name):
     cfg = CONFIGS[name]
     res, _ = full_check(cfg, seed=0)
     assert res["layout"].gemm_variant == 1
+    # the down GEMM's schedule: prefill's 36 token tiles x 16 feature tiles
+    # leave 64 tiles past two rounds (the last 4 token tiles in 4 K parts);
+    # skewed's 67 leave 48 (3 token tiles, 4 parts); fine's 157 leave 208,
+    # whose parts would not fit one round, so nothing is split
+    want = {"prefill": (4, 32 * 256), "skewed": (4, 64 * 256), "fine": (1, 157 * 256)}[name]
+    assert res["down_sched"] == want, res["down_sched"]
     if name == "skewed":
         share = res["counts"] / res["counts"].sum()
         announce(f"  skewed shares {np.round(share, 4).tolist()}")
