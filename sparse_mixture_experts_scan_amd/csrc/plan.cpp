@@ -29,18 +29,16 @@ struct Carver {
 
 }  // namespace
 
-#ifndef MOE_ROUTER_MIN_BLOCKS
-#define MOE_ROUTER_MIN_BLOCKS 256
-#endif
-int router_splits_for(int nblk, int d) {
-  // split d_model over blocks until about one block per CU runs (measured on
-  // MI355X: 128 blocks left T = 4096 at 0.065 ms, 256 take 0.044 ms, 512 or
-  // more are slower again); each split keeps a whole number of 16-element
-  // k-groups
+int router_splits_for(int nblk, int d, int E) {
+  // split d_model over blocks until about one block per CU runs, two with
+  // few experts (measured on MI355X with d_model 4096: for 8 experts, 512
+  // blocks take T = 4096 from 44 to 34 us and T = 8192 from 70 to 52 us
+  // against 256; for 64 experts, whose blocks each do 8 times the MFMA work,
+  // 256 stay faster); each split keeps a whole number of 16-element k-groups
+  const int min_blocks = E <= 16 ? 2 * kCus : kCus;
   const int groups = d / 16;
   int sp = 1;
-  while (nblk * sp < MOE_ROUTER_MIN_BLOCKS && sp * 2 <= kMaxRouterSplits &&
-         groups % (sp * 2) == 0)
+  while (nblk * sp < min_blocks && sp * 2 <= kMaxRouterSplits && groups % (sp * 2) == 0)
     sp *= 2;
   return sp;
 }
@@ -119,7 +117,7 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   D.Epow2 = 1;
   while (D.Epow2 < E) D.Epow2 *= 2;
   D.nblk = (D.T + kRouterTokens - 1) / kRouterTokens;
-  D.router_splits = router_splits_for(D.nblk, D.d);
+  D.router_splits = router_splits_for(D.nblk, D.d, E);
   const int64_t A = T * k;                       // (token, slot) assignments
   const int64_t rows_avg = (A + E - 1) / E;
   // GEMM form: weight-streaming for few rows per expert (weights read once,

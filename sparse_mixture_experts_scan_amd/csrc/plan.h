@@ -50,7 +50,7 @@ struct Dims {
 };
 
 // ---- decisions the plan takes (also used by the launchers)
-int router_splits_for(int nblk, int d);
+int router_splits_for(int nblk, int d, int E);
 // with a single router block the select pass also runs the expert scan
 bool router_fuses_scan(const Dims& D);
 // whether the weight-streaming gate/up GEMM reads the tokens in place

@@ -86,50 +86,75 @@ constexpr int kRouterMfmaThreads = 512;  // 8 waves split K
 constexpr int kRouterUnroll = MOE_ROUTER_UNROLL;  // k-groups whose loads are issued together
 
 
-// Top-k of one token's E scores (k passes of an arg-max, strict '>' in
-// ascending expert order: equal scores go to the lower index), then the
-// softmax over the selected k shifted by the largest.  Counts the choices in
-// the block histogram.
-__device__ inline void select_topk_token(const float* srow, int E, int k, size_t t,
+// Top-k of one token's E scores, by the kSelGroup consecutive lanes of its
+// group (lane q takes experts q, q + 8, ...): k rounds of an arg-max whose
+// order is the larger score, then the lower expert index, reduced over the
+// group with xor-shuffles, so every lane of the group ends each round with
+// the same winner.  This is the choice of k passes of a sequential scan with
+// strict '>' in ascending expert order: equal scores go to the lower index.
+// Then the softmax over the selected k, shifted by the largest.  Lane q
+// writes slot q (q < k) and counts it in the block histogram.  Called by
+// whole waves (the shuffles need every lane of a group); valid = the token
+// exists.
+constexpr int kSelGroup = 8;
+static_assert(MOE_MAX_EXPERTS <= 8 * kSelGroup && MOE_MAX_TOPK <= kSelGroup,
+              "each lane holds at most 8 experts and writes at most one slot");
+__device__ inline void select_topk_group(const float* srow, int E, int k, size_t t, bool valid,
                                          int32_t* __restrict__ idx_out,
                                          float* __restrict__ w_out, int* hist,
                                          int* s_sel = nullptr) {
-  uint64_t taken = 0;
+  const int q = threadIdx.x & (kSelGroup - 1);
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (q + kSelGroup * i < E) ? srow[q + kSelGroup * i] : 0.f;
+  uint32_t taken = 0;            // bit i: expert q + 8 i already selected
   float sel[MOE_MAX_TOPK];
   int sid[MOE_MAX_TOPK];
 #pragma unroll
   for (int j = 0; j < MOE_MAX_TOPK; ++j) {
     if (j < k) {
-      float best = 0.f;
+      float bv = 0.f;
       int bi = -1;
-      for (int e = 0; e < E; ++e) {
-        const float v = srow[e];
-        if (!((taken >> e) & 1ull) && (bi < 0 || v > best)) {
-          best = v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = q + kSelGroup * i;
+        if (e < E && !((taken >> i) & 1u) && (bi < 0 || v[i] > bv)) {
+          bv = v[i];
           bi = e;
         }
       }
-      taken |= 1ull << bi;
-      sel[j] = best;
+#pragma unroll
+      for (int off = 1; off < kSelGroup; off <<= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((bi & (kSelGroup - 1)) == q) taken |= 1u << (bi / kSelGroup);
+      sel[j] = bv;
       sid[j] = bi;
     }
   }
-  float z[MOE_MAX_TOPK];
-  float sum = 0.f;
+  float sum = 0.f, zq = 0.f;
+  int eq = 0;
 #pragma unroll
   for (int j = 0; j < MOE_MAX_TOPK; ++j)
     if (j < k) {
-      z[j] = expf(sel[j] - sel[0]);
-      sum += z[j];
+      const float z = expf(sel[j] - sel[0]);
+      sum += z;
+      if (j == q) {
+        zq = z;
+        eq = sid[j];
+      }
     }
-#pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j)
-    if (j < k) {
-      idx_out[t * k + j] = sid[j];
-      w_out[t * k + j] = z[j] / sum;
-      atomicAdd(&hist[sid[j]], 1);
-      if (s_sel) s_sel[t * k + j] = sid[j];
-    }
+  if (valid && q < k) {
+    idx_out[t * k + q] = eq;
+    w_out[t * k + q] = zq / sum;
+    atomicAdd(&hist[eq], 1);
+    if (s_sel) s_sel[t * k + q] = eq;
+  }
 }
 
 // Router statistics of one block (load-balancing loss: p_i is the mean over
@@ -289,8 +314,9 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
   if (logits_out)
     for (int i = tid; i < TB * E; i += kRouterMfmaThreads)
       if (t0 + i / E < nT) logits_out[(size_t)(t0 + i / E) * E + i % E] = slog[i / E][i % E];
-  if (tid < TB && t0 + tid < nT)
-    select_topk_token(slog[tid], E, k, (size_t)(t0 + tid), idx_out, w_out, hist);
+  if (tid < TB * kSelGroup)
+    select_topk_group(slog[tid / kSelGroup], E, k, (size_t)(t0 + tid / kSelGroup),
+                      t0 + tid / kSelGroup < nT, idx_out, w_out, hist);
   __syncthreads();
   if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = hist[tid];
   if (blk_prob) {
@@ -374,7 +400,7 @@ __device__ __forceinline__ void scatter_rows_block(
 // The select pass of a batch that fits one router block, run by all
 // kRouterThreads threads once slog holds the final scores: top-k and
 // softmax, the router statistics, the expert scan and (sa.tok_row set) the
-// row maps, with the same arithmetic as select_topk_token, block_prob_sums,
+// row maps, with the same arithmetic as select_topk_group, block_prob_sums,
 // expert_scan_block and scatter_rows_block for one block.  Every value that
 // a later phase needs stays in LDS and the barriers are LDS-only, so the
 // outputs' global stores drain once, at the end of the kernel.
@@ -389,7 +415,8 @@ __device__ __forceinline__ void select_single_block(
   __shared__ float smax[TB], sinv[TB], s_p[64];
   __shared__ int wcnt[NWAVE][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < nT) select_topk_token(slog[tid], E, k, (size_t)tid, idx_out, w_out, hist, s_sel);
+  select_topk_group(slog[tid / kSelGroup], E, k, (size_t)(tid / kSelGroup), tid / kSelGroup < nT,
+                    idx_out, w_out, hist, s_sel);
   if (blk_prob && tid < TB) {            // full-softmax constants of each token
     float m = slog[tid][0];
     for (int e = 1; e < E; ++e) m = fmaxf(m, slog[tid][e]);
@@ -518,8 +545,9 @@ __global__ __launch_bounds__(kSelectThreads) void router_select_kernel(
                         blk_counts, blk_prob, sa);
     return;
   }
-  if (tid < TB && t0 + tid < nT)
-    select_topk_token(slog[tid], E, k, (size_t)(t0 + tid), idx_out, w_out, hist);
+  if (tid < TB * kSelGroup)
+    select_topk_group(slog[tid / kSelGroup], E, k, (size_t)(t0 + tid / kSelGroup),
+                      t0 + tid / kSelGroup < nT, idx_out, w_out, hist);
   __syncthreads();
   if (tid < E) blk_counts[(size_t)blockIdx.x * E + tid] = hist[tid];
   if (blk_prob) {
