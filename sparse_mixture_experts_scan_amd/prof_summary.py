@@ -7,7 +7,11 @@
 <dir> are rocprofv3 ``-d`` output directories (``--output-format csv``):
 ``--kt`` from ``--kernel-trace --stats``, ``--fetch``/``--write`` from
 ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of ``bench.py
---copy-calibration-mib N``.  That option runs, before the timed steps, a
+--copy-calibration-mib N``, and optionally ``--dram`` from a
+``--pmc TCC_EA0_RDREQ_DRAM_32B_sum TCC_EA0_WRREQ_WRITE_DRAM_32B_sum`` run: the
+L2's read and write requests to memory in 32-byte units (a 64-byte request
+counts 2, a 128-byte one 4), bytes by the counters' own definition, which
+cross-checks the calibrated FETCH_SIZE / WRITE_SIZE figures.  That option runs, before the timed steps, a
 plain elementwise kernel that reads N MiB and writes N MiB; what the two
 counters read for it gives the scale factor from counter units to bytes,
 applied to every other kernel.  The per-kernel traffic is also merged into
@@ -28,10 +32,12 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 KERNEL_SOURCES = {
-    "gateup": {"stream": ["gemm_stream.hip", "common.h"], "tile": ["gemm_tile.hip", "common.h"],
-               "q4": ["gemm_q4.hip", "common.h"]},
-    "down": {"stream": ["gemm_stream.hip", "common.h"], "tile": ["gemm_tile.hip", "common.h"],
-             "q4": ["gemm_q4.hip", "common.h"]},
+    "gateup": {"stream": ["gemm_stream.hip", "common.h", "plan.h"],
+               "tile": ["gemm_tile.hip", "common.h", "plan.h"],
+               "q4": ["gemm_q4.hip", "common.h", "plan.h"]},
+    "down": {"stream": ["gemm_stream.hip", "common.h", "plan.h"],
+             "tile": ["gemm_tile.hip", "common.h", "plan.h"],
+             "q4": ["gemm_q4.hip", "common.h", "plan.h"]},
 }
 
 
@@ -78,12 +84,15 @@ def kernel_key(name: str) -> str:
     return name[:40]
 
 
-def read_counter(d: str):
-    """{kernel_key: [value per dispatch]} and the dispatches' kernel names."""
+def read_counter(d: str, counter: str = ""):
+    """{kernel_key: [value per dispatch]} and the dispatches' kernel names;
+    with `counter`, only that counter's rows of a multi-counter run."""
     path = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
     per = defaultdict(lambda: defaultdict(float))
     names = {}
     for r in csv.DictReader(open(path)):
+        if counter and r.get("Counter_Name") != counter:
+            continue
         key = kernel_key(r["Kernel_Name"])
         per[key][r["Dispatch_Id"]] += float(r["Counter_Value"])
         names[key] = r["Kernel_Name"]
@@ -113,6 +122,8 @@ def main():
     ap.add_argument("--kt", required=True)
     ap.add_argument("--fetch", help="FETCH_SIZE run (omit with --write for a trace-only summary)")
     ap.add_argument("--write")
+    ap.add_argument("--dram", help="TCC_EA0_RDREQ_DRAM_32B_sum / TCC_EA0_WRREQ_WRITE_DRAM_32B_sum "
+                                   "run (a cross-check in 32-byte units)")
     ap.add_argument("--cal-mib", type=int, default=512)
     ap.add_argument("--command-kt", required=True)
     ap.add_argument("--command-pmc", default="")
@@ -144,14 +155,28 @@ def main():
     write, _ = read_counter(a.write)
     cf = calibration(fetch, a.cal_mib, "fetch")
     cw = calibration(write, a.cal_mib, "write")
+    dram_r = dram_w = None
+    if a.dram:
+        dram_r, _ = read_counter(a.dram, "TCC_EA0_RDREQ_DRAM_32B_sum")
+        dram_w, _ = read_counter(a.dram, "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
     lines += ["", "HBM traffic per launch (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, "
               "one run each):", "", "```", a.command_pmc.replace("<COUNTER>", "FETCH_SIZE"),
               a.command_pmc.replace("<COUNTER>", "WRITE_SIZE"), "```", "",
               f"Scale from counter units to bytes, from the reference elementwise kernel "
               f"that reads {a.cal_mib} MiB and writes {a.cal_mib} MiB: FETCH_SIZE x {cf:.4g} "
-              f"B/unit, WRITE_SIZE x {cw:.4g} B/unit.", "",
-              "| kernel | fetch GB | write GB | algorithmic GB | traffic / algorithmic |",
-              "|---|---|---|---|---|"]
+              f"B/unit, WRITE_SIZE x {cw:.4g} B/unit.", ""]
+    if a.dram:
+        ref_r = sorted(dram_r["elementwise"])[-1] * 32
+        ref_w = sum(dram_w["elementwise"]) * 32
+        known = a.cal_mib << 20
+        lines += ["Cross-check (`--pmc TCC_EA0_RDREQ_DRAM_32B_sum TCC_EA0_WRREQ_WRITE_DRAM_32B_sum`"
+                  ", one run; 32 bytes per unit by the counters' definition):", "", "```",
+                  a.command_pmc.replace("<COUNTER>", "TCC_EA0_RDREQ_DRAM_32B_sum "
+                                        "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"), "```", "",
+                  f"On the reference kernel these read {ref_r / known:.3f} x and write "
+                  f"{ref_w / (2 * known):.3f} x its known bytes.", ""]
+    lines += ["| kernel | fetch GB | write GB | DRAM read GB | DRAM write GB | algorithmic GB "
+              "| traffic / algorithmic |", "|---|---|---|---|---|---|---|"]
     record = {}
     for key in ("router_topk", "router_select", "expert_scan", "scatter_gather", "gateup",
                 "down", "combine"):
@@ -159,15 +184,23 @@ def main():
             continue
         fb = sum(fetch[key]) / len(fetch[key]) * cf
         wb = sum(write.get(key, [0.0])) / max(1, len(write.get(key, [0.0]))) * cw
+        dr = dw = None
+        if a.dram and key in dram_r:
+            dr = sum(dram_r[key]) / len(dram_r[key]) * 32
+            dws = dram_w.get(key, [0.0])
+            dw = sum(dws) / max(1, len(dws)) * 32
         al = alg.get(key)
         ratio = f"{(fb + wb) / al:.2f}" if al else "-"
-        lines.append(f"| {key} | {fb/1e9:.4f} | {wb/1e9:.4f} | "
+        fmt = (lambda v: f"{v/1e9:.4f}" if v is not None else "-")
+        lines.append(f"| {key} | {fb/1e9:.4f} | {wb/1e9:.4f} | {fmt(dr)} | {fmt(dw)} | "
                      f"{al/1e9 if al else float('nan'):.4f} | {ratio} |")
         if key in KERNEL_SOURCES:
             files = KERNEL_SOURCES[key][a.variant]
             record[key] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb,
                            "source_files": files, "source_sha256": source_hash(files),
                            "profile": os.path.basename(a.out)}
+            if dr is not None:
+                record[key].update(dram_read_bytes=dr, dram_write_bytes=dw)
     with open(a.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     try:
