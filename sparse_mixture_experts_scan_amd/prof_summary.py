@@ -126,7 +126,9 @@ def main():
                                    "run (a cross-check in 32-byte units)")
     ap.add_argument("--cal-mib", type=int, default=512)
     ap.add_argument("--command-kt", required=True)
-    ap.add_argument("--command-pmc", default="")
+    ap.add_argument("--command-pmc", default="",
+                    help="counter-run command with <COUNTER> (the counters) and <DIR> (the "
+                         "output directory suffix: FETCH_SIZE, WRITE_SIZE or DRAM)")
     ap.add_argument("--title", default="MoE layer")
     ap.add_argument("--algorithmic", default="{}",
                     help="JSON {kernel: algorithmic bytes per launch} for the table")
@@ -160,8 +162,10 @@ def main():
         dram_r, _ = read_counter(a.dram, "TCC_EA0_RDREQ_DRAM_32B_sum")
         dram_w, _ = read_counter(a.dram, "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
     lines += ["", "HBM traffic per launch (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, "
-              "one run each):", "", "```", a.command_pmc.replace("<COUNTER>", "FETCH_SIZE"),
-              a.command_pmc.replace("<COUNTER>", "WRITE_SIZE"), "```", "",
+              "one run each):", "", "```",
+              a.command_pmc.replace("<COUNTER>", "FETCH_SIZE").replace("<DIR>", "FETCH_SIZE"),
+              a.command_pmc.replace("<COUNTER>", "WRITE_SIZE").replace("<DIR>", "WRITE_SIZE"),
+              "```", "",
               f"Scale from counter units to bytes, from the reference elementwise kernel "
               f"that reads {a.cal_mib} MiB and writes {a.cal_mib} MiB: FETCH_SIZE x {cf:.4g} "
               f"B/unit, WRITE_SIZE x {cw:.4g} B/unit.", ""]
@@ -172,7 +176,8 @@ def main():
         lines += ["Cross-check (`--pmc TCC_EA0_RDREQ_DRAM_32B_sum TCC_EA0_WRREQ_WRITE_DRAM_32B_sum`"
                   ", one run; 32 bytes per unit by the counters' definition):", "", "```",
                   a.command_pmc.replace("<COUNTER>", "TCC_EA0_RDREQ_DRAM_32B_sum "
-                                        "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum"), "```", "",
+                                        "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum")
+                  .replace("<DIR>", "DRAM"), "```", "",
                   f"On the reference kernel these read {ref_r / known:.3f} x and write "
                   f"{ref_w / (2 * known):.3f} x its known bytes.", ""]
     lines += ["| kernel | fetch GB | write GB | DRAM read GB | DRAM write GB | algorithmic GB "
