@@ -269,7 +269,10 @@ typedef struct moe_ws_layout {
   int32_t tokens_in_place;  /* 1: the gate/up GEMM reads each row's token from
                                x (or xn) through row_token and xs is not
                                written; 0: it reads the gathered rows of xs    */
-  int32_t reserved;         /* 0                                               */
+  int32_t y_weighted;       /* 1 (LDS-tiled form): y holds bf16 rows that
+                               already carry their gate weight (row_w), and
+                               y_parts float32 rows likewise; 0: y holds
+                               float32 W2 H and the combine applies the gates */
   size_t topk_idx;          /* [T][k]                                          */
   size_t topk_w;            /* [T][k] float32                                  */
   size_t block_counts;      /* [router_blocks][E]: per-block counts, then bases */
@@ -279,6 +282,10 @@ typedef struct moe_ws_layout {
   size_t tile_expert;       /* [max_rows / block_rows] expert of each tile     */
   size_t row_token;         /* [max_rows] token of each permuted row or -1     */
   size_t tok_row;           /* [T][k] permuted row of each (token, slot)       */
+  size_t row_w;             /* [max_rows] float32, y_weighted only (else 0
+                               bytes): the gate weight of each permuted row
+                               (padding rows: not written; their y rows are
+                               zeros)                                          */
   size_t xs;                /* [max_rows][d_model] dtype: gathered tokens.
                                0 bytes (not used) when tokens_in_place is 1:
                                bf16 tokens with T * d_model * 2 < 2^31, and
@@ -286,12 +293,15 @@ typedef struct moe_ws_layout {
                                with d_model a multiple of 128, or INT4
                                weights) or the LDS-tiled form with k >= 4      */
   size_t h;                 /* [max_rows][d_ff] dtype: SiLU(gate) * up         */
-  size_t y;                 /* [max_rows][d_model] float32: expert outputs
-                               W2 H of each row; for the rows of a split token
-                               tile, the first of its K parts                  */
+  size_t y;                 /* [max_rows][d_model]: expert outputs W2 H of
+                               each row, float32; with y_weighted, bf16 and
+                               times the row's gate weight (row_w).  For the
+                               rows of a split token tile, the first of its K
+                               parts                                           */
   size_t y_parts;           /* [down_splits - 1][y_part_rows][d_model] float32:
-                               the other K parts of the split token tiles' rows,
-                               row r at r - down_sched[1]; W2 H is their sum
+                               the other K parts of the split token tiles' rows
+                               (times row_w when y_weighted), row r at
+                               r - down_sched[1]; the row's output is their sum
                                with y, added in part order                     */
   size_t down_sched;        /* [2] int32, LDS-tiled form only (else 0 bytes):
                                written by the expert scan from the token tiles

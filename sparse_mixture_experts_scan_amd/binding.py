@@ -50,10 +50,11 @@ class MoeWsLayout(ctypes.Structure):
                 ("gemm_variant", ctypes.c_int32),
                 ("down_splits", ctypes.c_int32),
                 ("tokens_in_place", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)] + [
+                ("y_weighted", ctypes.c_int32)] + [
         (name, ctypes.c_size_t) for name in
         ("topk_idx", "topk_w", "block_counts", "counts", "offsets", "num_tiles",
-         "tile_expert", "row_token", "tok_row", "xs", "h", "y", "y_parts", "down_sched",
+         "tile_expert", "row_token", "tok_row", "row_w", "xs", "h", "y", "y_parts",
+         "down_sched",
          "block_probs", "norm_rs", "xn",
          "router_partial", "wdeq", "total")]
 

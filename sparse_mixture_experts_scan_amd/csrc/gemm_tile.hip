@@ -270,7 +270,8 @@ __device__ __forceinline__ void tile_reduce_parts(f32x16 (&acc)[4][kBFrags], cha
 template <int KS, bool GATEUP>
 __device__ __forceinline__ void tile_run(TileCtx& c, char* sa0, char* sa1, char* sbr, void* outp,
                                          int wave, int lane, int tid, int nk, int row0,
-                                         int valid_end, int N, int f0) {
+                                         int valid_end, int N, int f0, const float* wrow,
+                                         bool part0) {
   constexpr int FB = GATEUP ? kTileRows / 2 : kTileRows;  // output features per tile
   constexpr int kStride = 32 * KS;          // rows between a wave's token fragments
   constexpr int kRowsOut = 2 * kStride;     // tile rows the split tile computes
@@ -293,6 +294,17 @@ __device__ __forceinline__ void tile_run(TileCtx& c, char* sa0, char* sa1, char*
   int nbv = 0;                              // valid token fragments of this wave
 #pragma unroll
   for (int b = 0; b < kBFrags; ++b) nbv += row0 + wt * 32 + b * kStride < valid_end;
+  // down: the gate weights of this lane's token rows (0 for padding rows,
+  // whose row weights are not written), loaded now so that they have arrived
+  // by the epilogue
+  float gw[kBFrags];
+  if constexpr (!GATEUP) {
+#pragma unroll
+    for (int b = 0; b < kBFrags; ++b) {
+      const int r = wt * 32 + b * kStride + (lane & 31);
+      gw[b] = row0 + r < valid_end ? wrow[r] : 0.f;
+    }
+  }
 
   f32x16 acc[4][kBFrags];
 #pragma unroll
@@ -355,10 +367,44 @@ __device__ __forceinline__ void tile_run(TileCtx& c, char* sa0, char* sa1, char*
         v = *reinterpret_cast<const uint4*>(sbr + lrow * kPitch + ch * 16);
       *reinterpret_cast<uint4*>(h + (size_t)lrow * N + ch * 8) = v;
     }
-  } else {
-    // fp32: (token fragment b, feature half ch) = 32 KS rows x 128 features
-    // at a time, written by the part-0 waves of that half.  Rows past a split
+  } else if (part0) {
+    // down, the tile's first (or only) K part: each row times its gate
+    // weight, rounded to bf16.  One token fragment b = 32 KS rows x 256
+    // features at a time, written by the part-0 waves.  Rows past a split
     // tile's are padding, never read, and not written.
+    constexpr int kPitch = kTileRows * 2 + 16;
+    constexpr int kSlab = 32 * KS;            // rows per round
+    static_assert(kSlab * kPitch <= 3 * kOperBytes, "staging exceeds the B ring");
+    bf16_t* y = reinterpret_cast<bf16_t*>(outp) + f0;  // outp: this tile's first row
+#pragma unroll
+    for (int b = 0; b < kBFrags; ++b) {
+      if (kpart == 0) {
+        const int lrow = wt * 32 + r32;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int col = wf * 128 + a * 32 + jj * 8 + half * 4;
+            const f32x16& v = acc[a][b];
+            *reinterpret_cast<uint2*>(sbr + lrow * kPitch + col * 2) =
+                make_uint2(pack_bf16x2(gw[b] * v[jj * 4], gw[b] * v[jj * 4 + 1]),
+                           pack_bf16x2(gw[b] * v[jj * 4 + 2], gw[b] * v[jj * 4 + 3]));
+          }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int it = 0; it < kSlab * 32 / kTileThreads; ++it) {
+        const int qi = it * kTileThreads + tid;
+        const int lrow = qi / 32, chunk = qi % 32;
+        const uint4 v = *reinterpret_cast<const uint4*>(sbr + lrow * kPitch + chunk * 16);
+        *reinterpret_cast<uint4*>(y + (size_t)(b * kStride + lrow) * N + chunk * 8) = v;
+      }
+      lds_barrier();
+    }
+  } else {
+    // down, a later K part of a split token tile: float32 rows times the gate
+    // weight.  (token fragment b, feature half ch) = 32 KS rows x 128
+    // features at a time, written by the part-0 waves of that half.
     constexpr int kPitch = 128 * 4 + 16;
     constexpr int kSlab = 32 * KS;            // rows per (b, ch) round
     static_assert(kSlab * kPitch <= 3 * kOperBytes, "staging exceeds the B ring");
@@ -374,9 +420,10 @@ __device__ __forceinline__ void tile_run(TileCtx& c, char* sa0, char* sa1, char*
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
               const int col = a * 32 + jj * 8 + half * 4;
+              const f32x16& v = acc[a][b];
               *reinterpret_cast<float4*>(sbr + lrow * kPitch + col * 4) =
-                  make_float4(acc[a][b][jj * 4], acc[a][b][jj * 4 + 1], acc[a][b][jj * 4 + 2],
-                              acc[a][b][jj * 4 + 3]);
+                  make_float4(gw[b] * v[jj * 4], gw[b] * v[jj * 4 + 1], gw[b] * v[jj * 4 + 2],
+                              gw[b] * v[jj * 4 + 3]);
             }
         }
         lds_barrier();
@@ -400,7 +447,7 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ num_tiles,
     const int32_t* __restrict__ tile_expert, int N, int K, int n_ft,
     const int32_t* __restrict__ down_sched, float* __restrict__ y_parts, size_t part_stride,
-    int fgroup, const int32_t* __restrict__ row_token, int nT) {
+    int fgroup, const int32_t* __restrict__ row_token, int nT, const float* __restrict__ row_w) {
   // separate __shared__ arrays for the token operand's pair of buffers and
   // the weight operand's ring, so that the compiler can tell which DMA each
   // LDS read depends on
@@ -497,17 +544,21 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
   if constexpr (GATEUP) {
     dst = reinterpret_cast<bf16_t*>(outp) + (size_t)row0 * N;
   } else {
-    dst = part == 0 ? reinterpret_cast<float*>(outp) + (size_t)row0 * N
+    dst = part == 0 ? reinterpret_cast<void*>(reinterpret_cast<bf16_t*>(outp) + (size_t)row0 * N)
                     : y_parts + (part - 1) * part_stride + (size_t)(row0 - nu * kTileBT) * N;
   }
+  const float* wrow = GATEUP ? nullptr : row_w + row0;
   // short tiles split each stage's k-steps over the wave groups (see tile_run)
   const int nk = Kp / kTileBK;
   if (nvalid > 128)
-    tile_run<4, GATEUP>(c, sa0, sa1, sbr, dst, wave, lane, tid, nk, row0, valid_end, N, f0);
+    tile_run<4, GATEUP>(c, sa0, sa1, sbr, dst, wave, lane, tid, nk, row0, valid_end, N, f0, wrow,
+                        part == 0);
   else if (nvalid > 64)
-    tile_run<2, GATEUP>(c, sa0, sa1, sbr, dst, wave, lane, tid, nk, row0, valid_end, N, f0);
+    tile_run<2, GATEUP>(c, sa0, sa1, sbr, dst, wave, lane, tid, nk, row0, valid_end, N, f0, wrow,
+                        part == 0);
   else
-    tile_run<1, GATEUP>(c, sa0, sa1, sbr, dst, wave, lane, tid, nk, row0, valid_end, N, f0);
+    tile_run<1, GATEUP>(c, sa0, sa1, sbr, dst, wave, lane, tid, nk, row0, valid_end, N, f0, wrow,
+                        part == 0);
 }
 
 // Feature tiles per XCD-local group of the tile order.  Consecutive
@@ -526,8 +577,9 @@ static int tile_feat_group(const Dims& D, bool gateup) {
 template <bool GATEUP>
 static void tile_launch(const Dims& D, const void* act, const int32_t* row_token, const void* W0,
                         const void* W1, void* out, float* y_parts, int64_t part_rows,
-                        const int32_t* down_sched, const int32_t* counts, const int32_t* offsets,
-                        const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s) {
+                        const int32_t* down_sched, const float* row_w, const int32_t* counts,
+                        const int32_t* offsets, const int32_t* num_tiles,
+                        const int32_t* tile_expert, hipStream_t s) {
   const int N = GATEUP ? D.f : D.d;
   const int K = GATEUP ? D.d : D.f;
   const int FB = GATEUP ? kTileRows / 2 : kTileRows;
@@ -540,22 +592,22 @@ static void tile_launch(const Dims& D, const void* act, const int32_t* row_token
   tile_gemm_kernel<GATEUP><<<grid, kTileThreads, 0, s>>>(
       (const bf16_t*)act, (const bf16_t*)W0, (const bf16_t*)W1, out, counts, offsets, num_tiles,
       tile_expert, N, K, n_ft, down_sched, y_parts, (size_t)part_rows * N,
-      tile_feat_group(D, GATEUP), row_token, D.T);
+      tile_feat_group(D, GATEUP), row_token, D.T, row_w);
 }
 
 void launch_gateup_tile(const Dims& D, const void* x, const int32_t* row_token, const void* Wg,
                         const void* Wu, void* h, const int32_t* counts, const int32_t* offsets,
                         const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s) {
-  tile_launch<true>(D, x, row_token, Wg, Wu, h, nullptr, 0, nullptr, counts, offsets, num_tiles,
-                    tile_expert, s);
+  tile_launch<true>(D, x, row_token, Wg, Wu, h, nullptr, 0, nullptr, nullptr, counts, offsets,
+                    num_tiles, tile_expert, s);
 }
 
-void launch_down_tile(const Dims& D, const void* h, const void* Wd, float* y, float* y_parts,
-                      int64_t part_rows, const int32_t* down_sched, const int32_t* counts,
-                      const int32_t* offsets, const int32_t* num_tiles,
+void launch_down_tile(const Dims& D, const void* h, const void* Wd, void* y, float* y_parts,
+                      int64_t part_rows, const int32_t* down_sched, const float* row_w,
+                      const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                       const int32_t* tile_expert, hipStream_t s) {
-  tile_launch<false>(D, h, nullptr, Wd, nullptr, y, y_parts, part_rows, down_sched, counts,
-                     offsets, num_tiles, tile_expert, s);
+  tile_launch<false>(D, h, nullptr, Wd, nullptr, y, y_parts, part_rows, down_sched, row_w,
+                     counts, offsets, num_tiles, tile_expert, s);
 }
 
 }  // namespace moe

@@ -56,9 +56,10 @@ void launch_scan(const Dims& D, int32_t* blk_counts, const ScanArgs& sa, const f
                  hipStream_t s);
 // a2: stable row maps and gather of x into expert-contiguous rows (xs NULL:
 // the row maps only)
-void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int32_t* blk_base,
-                    const int32_t* offsets, int32_t* tok_row, int32_t* row_token, void* xs,
-                    hipStream_t s);
+// (row_w non-NULL: also the gate weight w of each row)
+void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const float* w,
+                    const int32_t* blk_base, const int32_t* offsets, int32_t* tok_row,
+                    int32_t* row_token, float* row_w, void* xs, hipStream_t s);
 // a3 + a4: grouped GEMMs, weight-streaming form (few rows per expert).
 // row_token NULL: act is the gathered rows (xs); else act is x (or xn) and
 // each row's token comes from row_token (only when stream_gathers_in_place).
@@ -77,9 +78,10 @@ void launch_gateup_tile(const Dims& D, const void* x, const int32_t* row_token, 
                         const int32_t* num_tiles, const int32_t* tile_expert, hipStream_t s);
 // y: the first K part of every row; y_parts: [D.down_splits - 1][part_rows]
 // further parts of the split token tiles' rows (see down_sched)
-void launch_down_tile(const Dims& D, const void* h, const void* Wd, float* y, float* y_parts,
-                      int64_t part_rows, const int32_t* down_sched, const int32_t* counts,
-                      const int32_t* offsets, const int32_t* num_tiles,
+// (y: bf16 rows times their gate weight row_w; y_parts float32, weighted)
+void launch_down_tile(const Dims& D, const void* h, const void* Wd, void* y, float* y_parts,
+                      int64_t part_rows, const int32_t* down_sched, const float* row_w,
+                      const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                       const int32_t* tile_expert, hipStream_t s);
 // INT4 expert weights: quantizer, dequantizer (to bf16, for the tiled form)
 // and the weight-streaming GEMMs that read INT4 directly
@@ -146,9 +148,11 @@ void launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 void launch_empty_stats(int E, int32_t* counts_out, float* prob_out, float* loss_out,
                         hipStream_t s);
 
-// y_parts / down_sched as for launch_down_tile (down_sched NULL: y alone)
-void launch_combine(const Dims& D, const float* y, const float* y_parts, int64_t part_rows,
-                    const int32_t* down_sched, const int32_t* tok_row, const float* w,
-                    const void* resid, void* out, hipStream_t s);
+// y_parts / down_sched as for launch_down_tile (down_sched NULL: y alone).
+// weighted: y is bf16 and already carries the gate weights (the LDS-tiled
+// form); else float32 and the combine applies w
+void launch_combine(const Dims& D, const void* y, bool weighted, const float* y_parts,
+                    int64_t part_rows, const int32_t* down_sched, const int32_t* tok_row,
+                    const float* w, const void* resid, void* out, hipStream_t s);
 
 }  // namespace moe

@@ -243,8 +243,9 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   int32_t* tok_row = reinterpret_cast<int32_t*>(ws + L.tok_row);
   void* xs = ws + L.xs;
   void* h = ws + L.h;
-  float* y = reinterpret_cast<float*>(ws + L.y);
+  void* y = ws + L.y;
   float* y_parts = reinterpret_cast<float*>(ws + L.y_parts);
+  float* row_w = L.y_weighted ? reinterpret_cast<float*>(ws + L.row_w) : nullptr;
   int32_t* down_sched = L.gemm_variant == 1 ? reinterpret_cast<int32_t*>(ws + L.down_sched)
                                             : nullptr;
   float* rpart = reinterpret_cast<float*>(ws + L.router_partial);
@@ -269,6 +270,9 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   const void* tok = norm_w ? xn : x;
   const bool gather = L.tokens_in_place != 0;
   const bool maps_in_router = gather && moe::router_fuses_scan(D);
+  // one router block means at most 32 rows per expert: never the tiled form,
+  // whose row weights the scatter writes
+  if (maps_in_router && row_w) return fail(MOE_ERR_UNSUPPORTED, "row weights need the scatter");
   const moe::ScanArgs sa{counts,
                          offsets,
                          num_tiles,
@@ -289,7 +293,8 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(2)) != hipSuccess)
     return hip_fail(e, "scan launch");
   if (!maps_in_router)
-    moe::launch_scatter(D, tok, idx, blk, offsets, tok_row, row_token, gather ? nullptr : xs, s);
+    moe::launch_scatter(D, tok, idx, w, blk, offsets, tok_row, row_token, row_w,
+                        gather ? nullptr : xs, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(3)) != hipSuccess)
     return hip_fail(e, "scatter launch");
   if (q4 && L.gemm_variant == 1) {
@@ -319,16 +324,18 @@ int run_layer(const void* x, const float* W_router, const void* W_gate, const vo
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(4)) != hipSuccess)
     return hip_fail(e, "gate/up launch");
   if (q4 && L.gemm_variant == 0)
-    moe::launch_down_q4(D, h, q4[2], y, counts, offsets, num_tiles, tile_expert, s);
+    moe::launch_down_q4(D, h, q4[2], static_cast<float*>(y), counts, offsets, num_tiles,
+                        tile_expert, s);
   else if (L.gemm_variant == 1)
-    moe::launch_down_tile(D, h, W_down, y, y_parts, L.y_part_rows, down_sched, counts, offsets,
-                          num_tiles, tile_expert, s);
+    moe::launch_down_tile(D, h, W_down, y, y_parts, L.y_part_rows, down_sched, row_w, counts,
+                          offsets, num_tiles, tile_expert, s);
   else
-    moe::launch_down_stream(D, h, W_down, y, counts, offsets, num_tiles, tile_expert, s);
+    moe::launch_down_stream(D, h, W_down, static_cast<float*>(y), counts, offsets, num_tiles,
+                            tile_expert, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(5)) != hipSuccess)
     return hip_fail(e, "down launch");
-  moe::launch_combine(D, y, y_parts, L.y_part_rows, down_sched, tok_row, w, norm_w ? x : nullptr,
-                      out, s);
+  moe::launch_combine(D, y, L.y_weighted != 0, y_parts, L.y_part_rows, down_sched, tok_row, w,
+                      norm_w ? x : nullptr, out, s);
   if ((e = hipGetLastError()) != hipSuccess || (e = mark(6)) != hipSuccess)
     return hip_fail(e, "combine launch");
   return MOE_OK;
@@ -530,7 +537,8 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   moe::launch_router(D, x, W_router, o.router_bias, idx, w, I(b.block_counts),
                      F(b.router_partial), nullptr, nullptr, nullptr, F(b.logits), sa, s);
   moe::launch_scan(D, I(b.block_counts), sa, nullptr, s);
-  moe::launch_scatter(D, x, idx, I(b.block_counts), offsets, tok_row, row_token, xs, s);
+  moe::launch_scatter(D, x, idx, nullptr, I(b.block_counts), offsets, tok_row, row_token, nullptr,
+                      xs, s);
   moe::launch_bwd_gather(D, dout, row_token, dp, s);
   moe::launch_bwd_tile_table(D, counts, offsets, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows,
                              s);

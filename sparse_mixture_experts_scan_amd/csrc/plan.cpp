@@ -155,10 +155,13 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
   L.tile_expert = c.take(sizeof(int32_t) * D.max_tiles);
   L.row_token = c.take(sizeof(int32_t) * D.max_rows);
   L.tok_row = c.take(sizeof(int32_t) * A);
+  // the LDS-tiled down GEMM applies the gate weights and stores bf16 rows
+  L.y_weighted = variant == 1;
+  L.row_w = c.take(L.y_weighted ? sizeof(float) * D.max_rows : 0);
   // gathered rows only when the gate/up GEMM does not read the tokens in place
   L.xs = c.take(L.tokens_in_place ? 0 : es * D.max_rows * d);
   L.h = c.take(es * D.max_rows * f);
-  L.y = c.take(sizeof(float) * D.max_rows * d);
+  L.y = c.take((L.y_weighted ? sizeof(uint16_t) : sizeof(float)) * D.max_rows * d);
   L.y_part_rows = D.down_splits > 1 ? (int64_t)tile_down_split_tiles(D) * D.BT : 0;
   L.y_parts = c.take(sizeof(float) * (D.down_splits - 1) * L.y_part_rows * d);
   L.down_sched = c.take(variant == 1 ? 2 * sizeof(int32_t) : 0);

@@ -360,11 +360,13 @@ __device__ inline void write_down_schedule(const ScanArgs& sa, int ntiles, int B
 // the same expert (wave ballots per expert plus the counts of earlier waves)
 // gives row offsets[e] + base[e] + rank, so rows inside an expert segment are
 // in ascending (token, slot) order.  sRow[p], sTok[p] get the row and token
-// (-1 past the batch); with write_maps, tok_row and row_token are written.
+// (-1 past the batch); with write_maps, tok_row and row_token are written,
+// and (row_w non-NULL) the pair's gate weight w as row_w of its row.
 __device__ __forceinline__ void scatter_rows_block(
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ offsets, int nT, int E, int k, int t0, bool write_maps,
-    int32_t* __restrict__ tok_row, int32_t* __restrict__ row_token, int* sRow, int* sTok) {
+    const int32_t* __restrict__ idx, const float* __restrict__ w,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ offsets, int nT, int E, int k,
+    int t0, bool write_maps, int32_t* __restrict__ tok_row, int32_t* __restrict__ row_token,
+    float* __restrict__ row_w, int* sRow, int* sTok) {
   constexpr int NWAVE = kRouterThreads / kWave;
   __shared__ int wcnt[NWAVE][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -391,6 +393,7 @@ __device__ __forceinline__ void scatter_rows_block(
     if (write_maps) {
       tok_row[(size_t)t0 * k + tid] = row;
       row_token[row] = t;
+      if (row_w) row_w[row] = w[(size_t)t0 * k + tid];
     }
   }
   sRow[tid] = row;
@@ -680,14 +683,15 @@ __global__ __launch_bounds__(256) void expert_scan_kernel(ScanArgs a, int32_t* _
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kRouterThreads) void scatter_gather_kernel(
-    const T* __restrict__ x, const int32_t* __restrict__ idx, const int32_t* __restrict__ base,
-    const int32_t* __restrict__ offsets, int nT, int d, int E, int k,
-    int32_t* __restrict__ tok_row, int32_t* __restrict__ row_token, T* __restrict__ xs) {
+    const T* __restrict__ x, const int32_t* __restrict__ idx, const float* __restrict__ w,
+    const int32_t* __restrict__ base, const int32_t* __restrict__ offsets, int nT, int d, int E,
+    int k, int32_t* __restrict__ tok_row, int32_t* __restrict__ row_token,
+    float* __restrict__ row_w, T* __restrict__ xs) {
   __shared__ int sRow[kRouterThreads];
   __shared__ int sTok[kRouterThreads];
   const int t0 = blockIdx.x * kRouterTokens;
-  scatter_rows_block(idx, base + (size_t)blockIdx.x * E, offsets, nT, E, k, t0, blockIdx.y == 0,
-                     tok_row, row_token, sRow, sTok);
+  scatter_rows_block(idx, w, base + (size_t)blockIdx.x * E, offsets, nT, E, k, t0,
+                     blockIdx.y == 0, tok_row, row_token, row_w, sRow, sTok);
   if (xs == nullptr) return;               // row maps only: the GEMM gathers in place
   __syncthreads();
   const int np = kRouterTokens * k;
@@ -704,13 +708,15 @@ __global__ __launch_bounds__(kRouterThreads) void scatter_gather_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// a5: out[t] = sum_j w[t][j] * Y[tok_row[t][j]], fp32 FMA in slot order,
-// one rounding to the output type.  A gather, so no atomics.  Rows of the
-// token tiles the down GEMM split along K (down_sched) sum their K parts in
-// part order before the gate weight is applied.
+// a5: out[t] = sum_j w[t][j] * Y[tok_row[t][j]], fp32 in slot order, one
+// rounding to the output type.  A gather, so no atomics.  Rows of the token
+// tiles the down GEMM split along K (down_sched) sum their K parts in part
+// order.  WEIGHTED (the LDS-tiled form): the down GEMM has already applied
+// the gate weights and stored bf16 rows (float32 for the later K parts), so
+// the rows are only summed; else fp32 FMA of w with the float32 rows.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+template <typename T, bool WEIGHTED>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
                                                       const float* __restrict__ y_parts,
                                                       size_t part_stride,
                                                       const int32_t* __restrict__ down_sched,
@@ -734,7 +740,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int c = blockIdx.y * 256 + threadIdx.x; c < d / 4; c += 256 * gridDim.y) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
-      float4 v = reinterpret_cast<const float4*>(y + (size_t)s_row[j] * d)[c];
+      float4 v;
+      if constexpr (WEIGHTED) {
+        const uint2 u = reinterpret_cast<const uint2*>(
+            reinterpret_cast<const bf16_t*>(y) + (size_t)s_row[j] * d)[c];
+        v = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+      } else {
+        v = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(y) +
+                                            (size_t)s_row[j] * d)[c];
+      }
       for (int p = 1; p < s_parts[j]; ++p) {   // further K parts, in part order
         const float4 q = reinterpret_cast<const float4*>(
             y_parts + (p - 1) * part_stride + (size_t)(s_row[j] - split_row0) * d)[c];
@@ -743,11 +758,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         v.z += q.z;
         v.w += q.w;
       }
-      const float g = s_w[j];
-      a.x = fmaf(g, v.x, a.x);
-      a.y = fmaf(g, v.y, a.y);
-      a.z = fmaf(g, v.z, a.z);
-      a.w = fmaf(g, v.w, a.w);
+      if constexpr (WEIGHTED) {
+        a.x += v.x;
+        a.y += v.y;
+        a.z += v.z;
+        a.w += v.w;
+      } else {
+        const float g = s_w[j];
+        a.x = fmaf(g, v.x, a.x);
+        a.y = fmaf(g, v.y, a.y);
+        a.z = fmaf(g, v.z, a.z);
+        a.w = fmaf(g, v.w, a.w);
+      }
     }
     T* o = out + (size_t)t * d + 4 * c;
     if (resid) {   // block wrapper: x + MoE(RMSNorm(x)), one rounding
@@ -807,9 +829,9 @@ void launch_scan(const Dims& D, int32_t* blk_counts, const ScanArgs& sa, const f
 #ifndef MOE_SCATTER_MIN_BLOCKS
 #define MOE_SCATTER_MIN_BLOCKS 1024
 #endif
-void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int32_t* blk_base,
-                    const int32_t* offsets, int32_t* tok_row, int32_t* row_token, void* xs,
-                    hipStream_t s) {
+void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const float* w,
+                    const int32_t* blk_base, const int32_t* offsets, int32_t* tok_row,
+                    int32_t* row_token, float* row_w, void* xs, hipStream_t s) {
   // column slices so that small T still spreads the copy over many blocks
   const int cpr = D.d * (D.bf16 ? 2 : 4) / 16;
   int cs = 1;
@@ -818,12 +840,12 @@ void launch_scatter(const Dims& D, const void* x, const int32_t* idx, const int3
   const dim3 grid(D.nblk, xs ? cs : 1);
   if (D.bf16)
     scatter_gather_kernel<bf16_t><<<grid, kRouterThreads, 0, s>>>(
-        (const bf16_t*)x, idx, blk_base, offsets, D.T, D.d, D.E, D.k, tok_row, row_token,
-        (bf16_t*)xs);
+        (const bf16_t*)x, idx, w, blk_base, offsets, D.T, D.d, D.E, D.k, tok_row, row_token,
+        row_w, (bf16_t*)xs);
   else
     scatter_gather_kernel<float><<<grid, kRouterThreads, 0, s>>>(
-        (const float*)x, idx, blk_base, offsets, D.T, D.d, D.E, D.k, tok_row, row_token,
-        (float*)xs);
+        (const float*)x, idx, w, blk_base, offsets, D.T, D.d, D.E, D.k, tok_row, row_token,
+        row_w, (float*)xs);
 }
 
 __global__ void empty_stats_kernel(int E, int32_t* counts_out, float* prob_out,
@@ -841,20 +863,27 @@ void launch_empty_stats(int E, int32_t* counts_out, float* prob_out, float* loss
   empty_stats_kernel<<<1, 64, 0, s>>>(E, counts_out, prob_out, loss_out);
 }
 
-void launch_combine(const Dims& D, const float* y, const float* y_parts, int64_t part_rows,
-                    const int32_t* down_sched, const int32_t* tok_row, const float* w,
-                    const void* resid, void* out, hipStream_t s) {
+void launch_combine(const Dims& D, const void* y, bool weighted, const float* y_parts,
+                    int64_t part_rows, const int32_t* down_sched, const int32_t* tok_row,
+                    const float* w, const void* resid, void* out, hipStream_t s) {
   const size_t stride = (size_t)part_rows * D.d;
-  // column slices of 256 float4 chunks while the tokens alone give few blocks
+  // column slices of 256 four-column chunks while the tokens alone give few
+  // blocks
   int cs = 1;
   while (D.T * cs < 256 && cs * 2 * 256 * 4 <= D.d) cs *= 2;
   const dim3 grid(D.T, cs);
-  if (D.bf16)
-    combine_kernel<bf16_t><<<grid, 256, 0, s>>>(y, y_parts, stride, down_sched, tok_row, w, D.d,
-                                                D.k, (const bf16_t*)resid, (bf16_t*)out);
+  if (D.bf16 && weighted)
+    combine_kernel<bf16_t, true><<<grid, 256, 0, s>>>(y, y_parts, stride, down_sched, tok_row, w,
+                                                      D.d, D.k, (const bf16_t*)resid,
+                                                      (bf16_t*)out);
+  else if (D.bf16)
+    combine_kernel<bf16_t, false><<<grid, 256, 0, s>>>(y, y_parts, stride, down_sched, tok_row,
+                                                       w, D.d, D.k, (const bf16_t*)resid,
+                                                       (bf16_t*)out);
   else
-    combine_kernel<float><<<grid, 256, 0, s>>>(y, y_parts, stride, down_sched, tok_row, w, D.d,
-                                               D.k, (const float*)resid, (float*)out);
+    combine_kernel<float, false><<<grid, 256, 0, s>>>(y, y_parts, stride, down_sched, tok_row, w,
+                                                      D.d, D.k, (const float*)resid,
+                                                      (float*)out);
 }
 
 }  // namespace moe

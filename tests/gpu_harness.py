@@ -75,6 +75,8 @@ def run_gpu(cfg: MoEConfig, dinp: dict, *, device="cuda", keep_ws=True, block_ep
         # the down GEMM's schedule: K parts of the split token tiles, first split row
         res["down_sched"] = (tuple(int(v) for v in i32(lay.down_sched, 2))
                              if lay.gemm_variant == 1 else (1, R))
+        if lay.y_weighted:   # gate weight of each permuted row (tiled form)
+            res["row_w"] = ws[lay.row_w:lay.row_w + 4 * R].view(torch.float32).cpu().numpy()
         if block_eps is not None:
             res["norm_rs"] = ws[lay.norm_rs:lay.norm_rs + 4 * T].view(torch.float32).cpu().numpy()
             es = 2 if cfg.dtype == "bf16" else 4
@@ -86,13 +88,17 @@ def run_gpu(cfg: MoEConfig, dinp: dict, *, device="cuda", keep_ws=True, block_ep
 
 
 def ws_rows(res, cfg: MoEConfig, which: str, rows) -> np.ndarray:
-    """Rows of a workspace matrix (xs, h: element type; y: fp32, for rows of
-    the token tiles the down GEMM split along K the sum of their parts in y and
-    y_parts, in part order) as float32 (float64 for y)."""
+    """Rows of a workspace matrix (xs, h: element type; y: fp32, or bf16 when
+    the layout's y_weighted is set; for rows of the token tiles the down GEMM
+    split along K the sum of their parts in y and y_parts (fp32), in part
+    order) as float32 (float64 for y)."""
     lay = res["layout"]
     ws = res["_ws"]
     width = cfg.d_ff if which == "h" else cfg.d_model
-    es = 4 if (which == "y" or cfg.dtype == "f32") else 2
+    if which == "y":
+        es = 2 if lay.y_weighted else 4
+    else:
+        es = 4 if cfg.dtype == "f32" else 2
     off = getattr(lay, which)
     sparts, split_row0 = res.get("down_sched", (1, lay.max_rows))
     out = []
@@ -101,12 +107,13 @@ def ws_rows(res, cfg: MoEConfig, which: str, rows) -> np.ndarray:
         parts = sparts if (which == "y" and r >= split_row0) else 1
         for p in range(parts):
             if p == 0:
-                base, rr = off, r
+                base, rr, pes = off, r, es
             else:
-                base = lay.y_parts + (p - 1) * lay.y_part_rows * width * es
+                pes = 4
+                base = lay.y_parts + (p - 1) * lay.y_part_rows * width * pes
                 rr = r - split_row0
-            b = ws[base + rr * width * es: base + (rr + 1) * width * es]
-            if es == 2:
+            b = ws[base + rr * width * pes: base + (rr + 1) * width * pes]
+            if pes == 2:
                 v = as_f32(b.view(torch.int16).cpu().numpy().view(np.uint16))
             else:
                 v = b.view(torch.float32).cpu().numpy()
@@ -150,6 +157,8 @@ def check_permutation(cfg: MoEConfig, inp: dict, res: dict):
         want_tr.reshape(-1)[pairs] = rows
     np.testing.assert_array_equal(res["row_token"], want_rt)
     np.testing.assert_array_equal(res["tok_row"], want_tr)
+    if "row_w" in res:   # each row carries its (token, slot)'s gate (padding: unwritten)
+        np.testing.assert_array_equal(res["row_w"][want_tr.ravel()], res["w"].ravel())
 
 
 def check_gather(cfg: MoEConfig, inp: dict, res: dict, rows):
@@ -202,7 +211,9 @@ def check_values(cfg: MoEConfig, inp: dict, res: dict, tokens, orc_full=None) ->
 def check_hidden_and_expert_outputs(cfg: MoEConfig, inp: dict, res: dict, rows) -> tuple:
     """H = SiLU(W1 x) * W3 x and Y = W2 H of the given permuted rows vs the
     oracle's expert_hidden / swiglu_expert, one oracle call per expert on
-    all of that expert's sampled rows."""
+    all of that expert's sampled rows.  When the layout stores gate-weighted
+    rows (y_weighted), Y is compared with the row's gate times the oracle's
+    (the gates themselves are checked by check_routing and check_permutation)."""
     rows = np.asarray(rows, dtype=np.int64)
     rt = res["row_token"]
     offs = res["offsets"]
@@ -217,6 +228,8 @@ def check_hidden_and_expert_outputs(cfg: MoEConfig, inp: dict, res: dict, rows) 
         xr = inp["x"][toks]
         href = oracle.expert_hidden(xr, inp["W_gate"][e], inp["W_up"][e])
         yref = oracle.swiglu_expert(xr, inp["W_gate"][e], inp["W_up"][e], inp["W_down"][e])
+        if res["layout"].y_weighted:
+            yref = yref * res["row_w"][rows[sel]].astype(np.float64)[:, None]
         for i, n in enumerate(sel):
             errs_h.append(np.abs(h[n] - href[i]).max() / max(np.abs(href[i]).max(), 1e-30))
             errs_y.append(np.abs(y[n] - yref[i]).max() / max(np.abs(yref[i]).max(), 1e-30))

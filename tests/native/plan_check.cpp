@@ -27,10 +27,11 @@ int main() {
                            ? b.total : 0;
     std::printf("0 %lld %lld %lld %lld %d %d %d %d", (long long)L.block_rows,
                 (long long)L.max_rows, (long long)L.router_blocks, (long long)L.y_part_rows,
-                L.gemm_variant, L.down_splits, L.tokens_in_place, L.reserved);
+                L.gemm_variant, L.down_splits, L.tokens_in_place, L.y_weighted);
     const size_t fields[] = {L.topk_idx,    L.topk_w,    L.block_counts, L.counts,
                              L.offsets,     L.num_tiles, L.tile_expert,  L.row_token,
-                             L.tok_row,     L.xs,        L.h,            L.y,
+                             L.tok_row,     L.row_w,     L.xs,           L.h,
+                             L.y,
                              L.y_parts,     L.down_sched, L.block_probs, L.norm_rs,
                              L.xn,          L.router_partial, L.wdeq,    L.total};
     for (size_t v : fields) std::printf(" %zu", v);

@@ -111,8 +111,9 @@ def layout_spans(lay, T, d, f, E, k, dt, block):
             ("block_counts", 4 * lay.router_blocks * E), ("counts", 4 * E),
             ("offsets", 4 * (E + 1)), ("num_tiles", 4),
             ("tile_expert", 4 * lay.max_rows // lay.block_rows), ("row_token", 4 * lay.max_rows),
-            ("tok_row", 4 * T * k), ("xs", 0 if in_place else es * lay.max_rows * d),
-            ("h", es * lay.max_rows * f), ("y", 4 * lay.max_rows * d),
+            ("tok_row", 4 * T * k), ("row_w", 4 * lay.max_rows if lay.y_weighted else 0),
+            ("xs", 0 if in_place else es * lay.max_rows * d),
+            ("h", es * lay.max_rows * f), ("y", (2 if lay.y_weighted else 4) * lay.max_rows * d),
             ("y_parts", 4 * (lay.down_splits - 1) * lay.y_part_rows * d),
             ("down_sched", 8 if lay.gemm_variant == 1 else 0),
             ("block_probs", 4 * lay.router_blocks * E),
@@ -172,7 +173,9 @@ def test_workspace_layout_is_consistent():
                (4096, 4096, 14336, 8, 2, 2): 0}
     for shape, want in inplace.items():
         lay = moe.moe_ffn_workspace_layout(*shape)
-        assert (lay.tokens_in_place, lay.reserved) == (want, 0), shape
+        assert lay.tokens_in_place == want, shape
+        # the tiled form stores gate-weighted bf16 expert outputs
+        assert lay.y_weighted == (1 if lay.gemm_variant == 1 else 0), shape
     with pytest.raises(moe.MoeError):
         moe.moe_ffn_workspace_layout(16, 100, 512, 8, 2, 0)
     assert moe.moe_ffn_workspace_size(16, 100, 512, 8, 2, 0) == 0

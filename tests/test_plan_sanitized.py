@@ -16,7 +16,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "sparse_mixture_experts_scan_amd", "csrc")
 
 FIELDS = ("topk_idx", "topk_w", "block_counts", "counts", "offsets", "num_tiles",
-          "tile_expert", "row_token", "tok_row", "xs", "h", "y", "y_parts", "down_sched",
+          "tile_expert", "row_token", "tok_row", "row_w", "xs", "h", "y", "y_parts", "down_sched",
           "block_probs", "norm_rs", "xn", "router_partial", "wdeq", "total")
 
 
@@ -74,7 +74,7 @@ def test_plan_under_sanitizers_matches_library(driver):
         lay = (moe.moe_block_workspace_layout if block else moe.moe_ffn_workspace_layout)(
             T, d, f, E, k, dtype)
         head = [lay.block_rows, lay.max_rows, lay.router_blocks, lay.y_part_rows,
-                lay.gemm_variant, lay.down_splits, lay.tokens_in_place, lay.reserved]
+                lay.gemm_variant, lay.down_splits, lay.tokens_in_place, lay.y_weighted]
         assert vals[1:9] == head, s
         assert vals[9:9 + len(FIELDS)] == [getattr(lay, n) for n in FIELDS], s
         assert size == lay.total
