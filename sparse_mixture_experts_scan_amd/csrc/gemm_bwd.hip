@@ -24,6 +24,8 @@
 // the expert's rows (weight gradients).  Fixed summation order throughout.
 #include <type_traits>
 
+#include <climits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -250,13 +252,20 @@ __global__ __launch_bounds__(kGT) void grouped_gemm_kernel(
     }
 }
 
-// Tile table of mode 0: expert segments in order, each cut into 128-row
-// tiles.  One thread (the table is at most E + rows / 128 long).
+// Tile table of mode 0: expert segments in order, each cut into kGM-row
+// tiles.  One thread (the table is at most E + rows / kGM long).  Then the
+// tiled dX GEMM's schedule (n_at feature tiles; two K halves per tile): the
+// tiles of a partial last round of kCus work-groups, rounded up to whole
+// token tiles (the last ones), run as four K quarters each if those fit the
+// round and at most max_split token tiles are involved; sched = {split token
+// tiles (0: none), first row of the first of them}.
 __global__ void bwd_tile_table_kernel(const int32_t* __restrict__ counts,
                                       const int32_t* __restrict__ offsets, int E, int max_tiles,
-                                      int32_t* __restrict__ tb_count, int32_t* __restrict__ tb_exp,
+                                      int n_at, int max_split, int32_t* __restrict__ tb_count,
+                                      int32_t* __restrict__ tb_exp,
                                       int32_t* __restrict__ tb_row0,
-                                      int32_t* __restrict__ tb_rows) {
+                                      int32_t* __restrict__ tb_rows,
+                                      int32_t* __restrict__ sched) {
   if (threadIdx.x != 0) return;
   int n = 0;
   for (int e = 0; e < E; ++e) {
@@ -267,6 +276,14 @@ __global__ void bwd_tile_table_kernel(const int32_t* __restrict__ counts,
     }
   }
   *tb_count = n;
+  int sp = 0;
+  const int rest = (2 * n * n_at) % kCus;
+  if (rest > 0 && n_at > 0) {
+    sp = min(n, (rest + 2 * n_at - 1) / (2 * n_at));
+    if (sp > max_split || 4 * sp * n_at > kCus) sp = 0;
+  }
+  sched[0] = sp;
+  sched[1] = sp > 0 ? tb_row0[n - sp] : 0;
 }
 
 // Permuted copy of the upstream gradient: Dp[r] = dOut[token of r], zero
@@ -439,6 +456,9 @@ __global__ __launch_bounds__(256) void bwd_router_wgrad_reduce(const float* __re
 // dx_t = sum_j dX[tok_row[t][j]] (slot order) + sum_e W_router[.][e] ds_t[e]
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dX, size_t plane,
+                                                     const float* __restrict__ dX_extra,
+                                                     size_t extra_plane,
+                                                     const int32_t* __restrict__ sched,
                                                      const int32_t* __restrict__ tok_row,
                                                      const float* __restrict__ Wr,
                                                      const float* __restrict__ ds, int d, int E,
@@ -447,11 +467,19 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
   __shared__ float sds[64];
   if (threadIdx.x < E) sds[threadIdx.x] = ds[(size_t)t * E + threadIdx.x];
   __syncthreads();
+  // rows of split token tiles (from sched[1] on) add their second quarters
+  const int split_row0 = (sched && sched[0] > 0) ? sched[1] : INT_MAX;
   for (int c = threadIdx.x; c < d; c += 256) {
     float acc = 0.f;
     for (int j = 0; j < k; ++j) {
-      const size_t o = (size_t)tok_row[(size_t)t * k + j] * d + c;
-      acc += dX[o] + dX[plane + o];
+      const int r = tok_row[(size_t)t * k + j];
+      const size_t o = (size_t)r * d + c;
+      if (r >= split_row0) {
+        const size_t oe = (size_t)(r - split_row0) * d + c;
+        acc += (dX[o] + dX_extra[oe]) + (dX[plane + o] + dX_extra[extra_plane + oe]);
+      } else {
+        acc += dX[o] + dX[plane + o];
+      }
     }
     float rt = 0.f;
     for (int e = 0; e < E; ++e) rt = fmaf(Wr[(size_t)c * E + e], sds[e], rt);
@@ -479,10 +507,10 @@ void launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
 
 
 void launch_bwd_tile_table(const Dims& D, const int32_t* counts, const int32_t* offsets,
-                           int max_tiles, int32_t* tb_count, int32_t* tb_exp, int32_t* tb_row0,
-                           int32_t* tb_rows, hipStream_t s) {
-  bwd_tile_table_kernel<<<1, 64, 0, s>>>(counts, offsets, D.E, max_tiles, tb_count, tb_exp,
-                                         tb_row0, tb_rows);
+                           int max_tiles, int max_split, int32_t* tb_count, int32_t* tb_exp,
+                           int32_t* tb_row0, int32_t* tb_rows, int32_t* sched, hipStream_t s) {
+  bwd_tile_table_kernel<<<1, 64, 0, s>>>(counts, offsets, D.E, max_tiles, D.d / kBwdTileBT,
+                                         max_split, tb_count, tb_exp, tb_row0, tb_rows, sched);
 }
 
 void launch_bwd_gather(const Dims& D, const void* src, const int32_t* row_token, void* dst,
@@ -549,10 +577,11 @@ void launch_bwd_router_wgrad(const Dims& D, const void* x, const float* ds, floa
                                                                        dWr, dbias);
 }
 
-void launch_bwd_dx(const Dims& D, const float* dX, size_t plane, const int32_t* tok_row,
+void launch_bwd_dx(const Dims& D, const float* dX, size_t plane, const float* dX_extra,
+                   size_t extra_plane, const int32_t* sched, const int32_t* tok_row,
                    const float* Wr, const float* ds, void* dx, hipStream_t s) {
-  bwd_dx_kernel<bf16_t><<<D.T, 256, 0, s>>>(dX, plane, tok_row, Wr, ds, D.d, D.E, D.k,
-                                            (bf16_t*)dx);
+  bwd_dx_kernel<bf16_t><<<D.T, 256, 0, s>>>(dX, plane, dX_extra, extra_plane, sched, tok_row, Wr,
+                                            ds, D.d, D.E, D.k, (bf16_t*)dx);
 }
 
 }  // namespace moe

@@ -104,6 +104,13 @@ struct BgArgs {
   // writes the C plane c_pstride elements after C0.
   int kparts;
   size_t c_pstride;
+  // mode 0, two parts (dX): sched = {split token tiles sp, their first row}
+  // from the tile table.  The last sp token tiles run each part as two K
+  // halves (quarters of the whole); a part's second half goes to the extra
+  // plane C_extra + part * extra_pstride, row r at r - sched[1].  NULL: none.
+  const int32_t* sched;
+  float* C_extra;
+  size_t extra_pstride;
 };
 
 namespace {
@@ -283,30 +290,60 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
   // serves better).  Then groups of feature tiles.
   const int L = blockIdx.x;
   int e = 0, part = 0, Lp;
+  int ntb = p.n_bt;                         // token tiles of the tile order
+  int ksub = -1;                            // K half of a split tile's part (-1: unsplit)
+  int bt, at;
   if constexpr (MODE == 1) {
     const int xcd = L % kBXcds, li = L / kBXcds;
     e = li / p.per_xcd;                     // per_xcd: tiles per expert and XCD
     Lp = xcd * p.per_xcd + (li - e * p.per_xcd);
     if (e >= p.total || Lp >= p.n_at * p.n_bt) return;
-  } else {
+  } else if (p.sched == nullptr) {
     Lp = (L % kBXcds) * p.per_xcd + L / kBXcds;  // per_xcd: tiles per XCD
     if (Lp >= p.total * p.n_at * p.n_bt) return;
     part = Lp / (p.n_at * p.n_bt);
     Lp -= part * p.n_at * p.n_bt;
+  } else {
+    // the unsplit token tiles' tiles in XCD-contiguous ranges as above, then
+    // the quarters of the split ones (quarter slowest) to fill the last round
+    const int sp = p.sched[0];
+    ntb = *p.tb_count - sp;
+    const int n_un = p.total * p.n_at * ntb;
+    const int per = (n_un + kBXcds - 1) / kBXcds;
+    if (L < per * kBXcds) {
+      Lp = (L % kBXcds) * per + L / kBXcds;
+      if (Lp >= n_un) return;
+      part = Lp / (p.n_at * ntb);
+      Lp -= part * p.n_at * ntb;
+    } else {
+      const int i = L - per * kBXcds;
+      if (i >= 2 * p.total * p.n_at * sp) return;
+      const int q = i / (p.n_at * sp), j = i - q * (p.n_at * sp);
+      part = q >> 1;
+      ksub = q & 1;
+      bt = ntb + j / p.n_at;
+      at = j % p.n_at;
+    }
   }
-  const int grp = Lp / (kBFeatGroup * p.n_bt);
-  const int rem = Lp - grp * kBFeatGroup * p.n_bt;
-  const int gsize = min(kBFeatGroup, p.n_at - grp * kBFeatGroup);
-  const int bt = rem / gsize;
-  const int at = grp * kBFeatGroup + rem % gsize;
+  if (ksub < 0) {
+    const int grp = Lp / (kBFeatGroup * ntb);
+    const int rem = Lp - grp * kBFeatGroup * ntb;
+    const int gsize = min(kBFeatGroup, p.n_at - grp * kBFeatGroup);
+    bt = rem / gsize;
+    at = grp * kBFeatGroup + rem % gsize;
+  }
 
-  int row0 = 0, rows = kBT, kn;
+  int row0 = 0, rows = kBT, kn, koff = 0;
   if constexpr (MODE == 0) {
     if (bt >= *p.tb_count) return;
     e = p.tb_exp[bt];
     row0 = p.tb_row0[bt];
     rows = p.tb_rows[bt];
     kn = p.K;
+    if (ksub >= 0) {                        // a quarter: half of the part's K
+      kn = p.K / 2;
+      koff = ksub * kn;
+    }
   } else {
     kn = p.counts[e];
   }
@@ -329,7 +366,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
     c.ld_bytes = (uint32_t)p.lda * 2;
     if constexpr (MODE == 0) Am += (size_t)e * p.a_estride;
     if constexpr (KSA) {
-      size_t first_row = 0;
+      size_t first_row = (size_t)koff;      // mode 0: the K range's first row of A
       if constexpr (MODE == 1) first_row = (size_t)p.offsets[e];
       c.ks_base = reinterpret_cast<const char*>(Am + first_row * p.lda + (size_t)a_tile * kBT);
       c.ks_base1 = c.ks_base;
@@ -346,7 +383,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
     c.ld_bytes = (uint32_t)p.ldb * 2;
     if constexpr (MODE == 0) {
       // token rows row0 .. + rows (k contiguous); past them zeros
-      c.r = buffer_rsrc(p.B + (size_t)row0 * p.ldb + (size_t)part * p.K,
+      c.r = buffer_rsrc(p.B + (size_t)row0 * p.ldb + (size_t)part * p.K + koff,
                    (uint32_t)rows * c.ld_bytes);
     } else {
       c.ks_base = reinterpret_cast<const char*>(p.B + (size_t)p.offsets[e] * p.ldb +
@@ -413,8 +450,13 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
   char* Cb;
   int brow_base;
   if constexpr (MODE == 0) {
-    Cb = reinterpret_cast<char*>(p.C0) + (size_t)part * p.c_pstride * (CBF16 ? 2 : 4);
-    brow_base = row0;
+    if (ksub == 1) {                        // a part's second half: its extra plane
+      Cb = reinterpret_cast<char*>(p.C_extra) + (size_t)part * p.extra_pstride * (CBF16 ? 2 : 4);
+      brow_base = row0 - p.sched[1];
+    } else {
+      Cb = reinterpret_cast<char*>(p.C0) + (size_t)part * p.c_pstride * (CBF16 ? 2 : 4);
+      brow_base = row0;
+    }
   } else {
     int bt_out = bt;
     Cb = reinterpret_cast<char*>(p.C0);
@@ -509,7 +551,9 @@ void bg_launch(BgArgs p, int groups, hipStream_t s) {
   const int tiles = p.n_at * p.n_bt;
   p.per_xcd = MODE == 1 ? (tiles + kBXcds - 1) / kBXcds              // per expert
                         : (groups * tiles + kBXcds - 1) / kBXcds;    // all tiles
-  const int grid = p.per_xcd * kBXcds * (MODE == 1 ? groups : 1);
+  // with a schedule, up to kCus / 2 more work-groups: the split tiles' extra
+  // quarters
+  const int grid = p.per_xcd * kBXcds * (MODE == 1 ? groups : 1) + (p.sched ? kCus / 2 : 0);
   if (grid > 0) bwd_tile_kernel<KSA, KSB, MODE, CBF16, SWAP><<<grid, kBThreads, 0, s>>>(p);
 }
 
@@ -571,7 +615,8 @@ void launch_bwd_z(const Dims& D, const void* dp, const void* Wd, void* z, int ma
 
 // dX_r = W1^T dA + W3^T dB: A = [W1; W3] down its columns (index d, k = 2 d_ff)
 void launch_bwd_dxs(const Dims& D, const void* dab, const void* Wg, const void* Wu, float* dxs,
-                    size_t plane, int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
+                    size_t plane, float* dxs_extra, size_t extra_plane, const int32_t* sched,
+                    int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
                     const int32_t* tb_row0, const int32_t* tb_rows, hipStream_t s) {
   // two K parts (the d_ff of W1, then that of W3), one plane each: twice the
   // workgroups of one K = 2 d_ff pass, which on prefill fill 4.5 rounds of
@@ -589,6 +634,9 @@ void launch_bwd_dxs(const Dims& D, const void* dab, const void* Wg, const void* 
   p.n_at = D.d / kBT;
   p.kparts = 2;
   p.c_pstride = plane;
+  p.sched = sched;
+  p.C_extra = dxs_extra;
+  p.extra_pstride = extra_plane;
   bg_launch<true, false, 0, false>(p, 2, s);
 }
 

@@ -90,6 +90,11 @@ bool q4_group_ok(int K, int G) {
 
 bool bwd_tile_shape_ok(int64_t d, int64_t f) { return d % kBwdTileBT == 0 && f % kBwdTileBT == 0; }
 
+// The dX GEMM runs two K halves of each (token tile, feature tile); the
+// token tiles of a partial last round may instead run four K quarters each,
+// if those quarters fit one round: kCus / 4 per feature-tile row.
+int bwd_dx_split_tiles(int64_t d) { return (int)(kCus / (4 * (d / kBwdTileBT))); }
+
 int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dtype, bool block,
               Plan* p, std::string* why) {
   if (T < 1 || d < 1 || f < 1 || E < 1 || k < 1)
@@ -190,7 +195,7 @@ int make_bwd_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, BwdPlan
                 "T * max(2 d_ff, d_model) too large for the backward");
   Dims& D = b->D;
   D = p.D;
-  D.BT = 16;
+  D.BT = kBwdPadRows;
   const int64_t A = T * k;
   int64_t max_rows = A + (int64_t)E * (D.BT - 1);
   max_rows = (max_rows + D.BT - 1) / D.BT * D.BT;
@@ -220,10 +225,15 @@ int make_bwd_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, BwdPlan
   b->hg = c.take(2 * R * f);
   b->dp = c.take(2 * R * d);
   b->dxs = c.take(4 * 2 * R * d);   // two planes: the W1 and W3 halves of dX
+  // two more for the split token tiles' second quarters (tiled form): their
+  // rows span at most the tiles plus the padding between experts
+  b->dx_max_split = bwd_tile_shape_ok(d, f) ? bwd_dx_split_tiles(d) : 0;
+  b->dx_split_rows = b->dx_max_split * (kBwdTileBT + kBwdPadRows);
+  b->dxs_extra = c.take(4 * 2 * (size_t)b->dx_split_rows * d);
   b->dg = c.take(4 * R);
   b->ds = c.take(4 * (size_t)T * E);
   b->wpart = c.take(4 * (size_t)kBwdRouterSlices * (d + 1) * E);
-  b->tb = c.take(4 * (size_t)(1 + 3 * b->max_tiles));
+  b->tb = c.take(4 * (size_t)(1 + 3 * b->max_tiles + 2));
   b->total = c.off;
   return MOE_OK;
 }

@@ -31,6 +31,7 @@ constexpr int kQ4Chunk = 128;          // K per 16-byte INT4 weight load of a 4-
 #endif
 constexpr int kBwdRowTile = MOE_BG_M;
 constexpr int kBwdTileBT = 256;        // tile extent of the 256 x 256 backward GEMMs
+constexpr int kBwdPadRows = 16;        // padding unit of the backward's expert segments
 constexpr int kBwdRouterSlices = 32;   // token slices of the router weight gradient
 constexpr int kTileMinRows = 96;       // average rows per expert from which the tiled form runs
 constexpr int kCus = 256;              // compute units the tile schedules fill (MI355X)
@@ -67,6 +68,9 @@ bool tile_gathers_in_place(const Dims& D);
 bool q4_group_ok(int K, int G);
 constexpr int q4_quantize_max_k() { return 65536; }
 bool bwd_tile_shape_ok(int64_t d, int64_t f);
+// token tiles whose dX work the tiled backward may split into K quarters to
+// fill a partial last round of work-groups (0: never)
+int bwd_dx_split_tiles(int64_t d);
 
 // ---- forward plan
 struct Plan {
@@ -84,9 +88,14 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
 // offsets into the workspace)
 struct BwdPlan {
   Dims D;
-  int max_tiles;  // rows of the row-tile table
+  int max_tiles;     // rows of the row-tile table
+  int dx_max_split;  // token tiles the dX schedule may split (0: none)
+  int dx_split_rows; // rows of each extra dX plane (the split token tiles' span)
+  // tb: [1 + 3 max_tiles + 2] int32: count, experts, first rows, row counts,
+  // then the dX schedule (split token tiles, first row of the first one)
   size_t topk_idx, topk_w, block_counts, counts, offsets, num_tiles, tile_expert, row_token,
-      tok_row, xs, logits, router_partial, ab, z, dab, hg, dp, dxs, dg, ds, wpart, tb, total;
+      tok_row, xs, logits, router_partial, ab, z, dab, hg, dp, dxs, dxs_extra, dg, ds, wpart, tb,
+      total;
 };
 int make_bwd_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, BwdPlan* b,
                   std::string* why);
