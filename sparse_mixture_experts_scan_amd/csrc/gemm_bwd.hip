@@ -48,6 +48,7 @@ namespace {
 #define MOE_BG_WN 2
 #endif
 constexpr int kGM = MOE_BG_M;
+constexpr int kDxTokens = 16;                // tokens per block of the dx kernel
 constexpr int kGN = MOE_BG_N;
 constexpr int kGK = MOE_BG_K;
 constexpr int kGWM = MOE_BG_WM, kGWN = MOE_BG_WN;
@@ -454,36 +455,67 @@ __global__ __launch_bounds__(256) void bwd_router_wgrad_reduce(const float* __re
 }
 
 // dx_t = sum_j dX[tok_row[t][j]] (slot order) + sum_e W_router[.][e] ds_t[e]
-template <typename T>
+template <typename T, int EB>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dX, size_t plane,
                                                      const float* __restrict__ dX_extra,
                                                      size_t extra_plane,
                                                      const int32_t* __restrict__ sched,
                                                      const int32_t* __restrict__ tok_row,
                                                      const float* __restrict__ Wr,
-                                                     const float* __restrict__ ds, int d, int E,
-                                                     int k, T* __restrict__ dx) {
-  const int t = blockIdx.x;
-  __shared__ float sds[64];
-  if (threadIdx.x < E) sds[threadIdx.x] = ds[(size_t)t * E + threadIdx.x];
+                                                     const float* __restrict__ ds, int nT, int d,
+                                                     int E, int k, T* __restrict__ dx) {
+  // block: kDxTokens tokens x 256 columns; thread: one column, its E router
+  // weights held in registers across the tokens (EB >= E of them, zeros past
+  // E, which add exact zeros)
+  __shared__ float sds[kDxTokens][EB];
+  __shared__ int srow[kDxTokens][MOE_MAX_TOPK];
+  const int t0 = blockIdx.x * kDxTokens, tid = threadIdx.x;
+  for (int i = tid; i < kDxTokens * EB; i += 256) {
+    const int t = t0 + i / EB, e = i % EB;
+    sds[i / EB][e] = (t < nT && e < E) ? ds[(size_t)t * E + e] : 0.f;
+  }
+  for (int i = tid; i < kDxTokens * k; i += 256) {
+    const int t = t0 + i / k;
+    srow[i / k][i % k] = t < nT ? tok_row[(size_t)t * k + i % k] : 0;
+  }
+  const int c = blockIdx.y * 256 + tid;
+  float wr[EB];
+#pragma unroll
+  for (int e = 0; e < EB; ++e) wr[e] = (c < d && e < E) ? Wr[(size_t)c * E + e] : 0.f;
   __syncthreads();
+  if (c >= d) return;
   // rows of split token tiles (from sched[1] on) add their second quarters
   const int split_row0 = (sched && sched[0] > 0) ? sched[1] : INT_MAX;
-  for (int c = threadIdx.x; c < d; c += 256) {
-    float acc = 0.f;
-    for (int j = 0; j < k; ++j) {
-      const int r = tok_row[(size_t)t * k + j];
-      const size_t o = (size_t)r * d + c;
-      if (r >= split_row0) {
-        const size_t oe = (size_t)(r - split_row0) * d + c;
-        acc += (dX[o] + dX_extra[oe]) + (dX[plane + o] + dX_extra[extra_plane + oe]);
-      } else {
-        acc += dX[o] + dX[plane + o];
+  const int nt = min(kDxTokens, nT - t0);
+  for (int i = 0; i < nt; ++i) {
+    // every load of the token first (they are independent), then the sum in
+    // slot order
+    float v[MOE_MAX_TOPK][4];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k) {
+        const int r = srow[i][j];
+        const size_t o = (size_t)r * d + c;
+        v[j][0] = dX[o];
+        v[j][1] = dX[plane + o];
+        v[j][2] = v[j][3] = 0.f;
+        if (r >= split_row0) {
+          const size_t oe = (size_t)(r - split_row0) * d + c;
+          v[j][2] = dX_extra[oe];
+          v[j][3] = dX_extra[extra_plane + oe];
+        }
       }
     }
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j < k) acc += (srow[i][j] >= split_row0) ? (v[j][0] + v[j][2]) + (v[j][1] + v[j][3])
+                                                   : v[j][0] + v[j][1];
+    // W_router . ds in expert order
     float rt = 0.f;
-    for (int e = 0; e < E; ++e) rt = fmaf(Wr[(size_t)c * E + e], sds[e], rt);
-    dx[(size_t)t * d + c] = Elem<T>::from_f32(acc + rt);
+#pragma unroll
+    for (int e = 0; e < EB; ++e) rt = fmaf(wr[e], sds[i][e], rt);
+    dx[(size_t)(t0 + i) * d + c] = Elem<T>::from_f32(acc + rt);
   }
 }
 
@@ -580,8 +612,16 @@ void launch_bwd_router_wgrad(const Dims& D, const void* x, const float* ds, floa
 void launch_bwd_dx(const Dims& D, const float* dX, size_t plane, const float* dX_extra,
                    size_t extra_plane, const int32_t* sched, const int32_t* tok_row,
                    const float* Wr, const float* ds, void* dx, hipStream_t s) {
-  bwd_dx_kernel<bf16_t><<<D.T, 256, 0, s>>>(dX, plane, dX_extra, extra_plane, sched, tok_row, Wr,
-                                            ds, D.d, D.E, D.k, (bf16_t*)dx);
+  const dim3 grid((D.T + kDxTokens - 1) / kDxTokens, (D.d + 255) / 256);
+  auto run = [&](auto eb) {
+    bwd_dx_kernel<bf16_t, decltype(eb)::value><<<grid, 256, 0, s>>>(
+        dX, plane, dX_extra, extra_plane, sched, tok_row, Wr, ds, D.T, D.d, D.E, D.k,
+        (bf16_t*)dx);
+  };
+  if (D.E <= 8) run(std::integral_constant<int, 8>{});
+  else if (D.E <= 16) run(std::integral_constant<int, 16>{});
+  else if (D.E <= 32) run(std::integral_constant<int, 32>{});
+  else run(std::integral_constant<int, 64>{});
 }
 
 }  // namespace moe
