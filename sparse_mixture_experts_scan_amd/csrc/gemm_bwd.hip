@@ -404,42 +404,49 @@ __global__ __launch_bounds__(64) void bwd_router_kernel(
 
 // Router weight gradient, partial over a slice of tokens: part[s][j][e] =
 // sum over tokens of slice s (in order) of x[t][j] ds[t][e]; and the bias
-// gradient part (column j = d).  Thread per column j, eight experts per
-// pass held in registers; the slice's ds rows are staged in LDS and read as
-// broadcasts.
-constexpr int kWgradMaxSlice = 1024;   // tokens per slice staged at once
-template <typename T>
+// gradient part (column j = d).  Thread per column j, every expert's sum in
+// registers; the slice's ds rows are staged in LDS, kWgradChunk tokens at a
+// time, and read as broadcasts.
+constexpr int kWgradChunk = 128;       // tokens of a slice staged in LDS at once
+template <typename T, int EB>
 __global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(
     const T* __restrict__ x, const float* __restrict__ ds, int Tn, int d, int E, int tslice,
     float* __restrict__ part) {
-  __shared__ float sds[kWgradMaxSlice * 8];
+  __shared__ float sds[kWgradChunk][EB];
   const int j = blockIdx.x * 256 + threadIdx.x;
   const int s = blockIdx.y;
   const int t0 = s * tslice, t1 = min(Tn, t0 + tslice);
-  for (int e0 = 0; e0 < E; e0 += 8) {
-    float acc[8];
+  // all EB (>= E; zeros past E) accumulators at once, so x is read once
+  float acc[EB];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-    for (int c0 = t0; c0 < t1; c0 += kWgradMaxSlice) {
-      const int c1 = min(t1, c0 + kWgradMaxSlice);
-      __syncthreads();
-      for (int i = threadIdx.x; i < (c1 - c0) * 8; i += 256) {
-        const int t = c0 + i / 8, e = e0 + i % 8;
-        sds[i] = e < E ? ds[(size_t)t * E + e] : 0.f;
-      }
-      __syncthreads();
-      if (j <= d)
-        for (int t = c0; t < c1; ++t) {
-          const float xv = j < d ? Elem<T>::to_f32(x[(size_t)t * d + j]) : 1.0f;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) acc[q] = fmaf(xv, sds[(t - c0) * 8 + q], acc[q]);
-        }
+  for (int q = 0; q < EB; ++q) acc[q] = 0.f;
+  for (int c0 = t0; c0 < t1; c0 += kWgradChunk) {
+    const int c1 = min(t1, c0 + kWgradChunk);
+    __syncthreads();
+    for (int i = threadIdx.x; i < (c1 - c0) * EB; i += 256) {
+      const int t = c0 + i / EB, e = i % EB;
+      sds[i / EB][e] = e < E ? ds[(size_t)t * E + e] : 0.f;
     }
-    if (j <= d)
+    __syncthreads();
+    if (j <= d) {
+      for (int t = c0; t < c1; ++t) {
+        const float xv = j < d ? Elem<T>::to_f32(x[(size_t)t * d + j]) : 1.0f;
+        const float4* row = reinterpret_cast<const float4*>(sds[t - c0]);
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (e0 + q < E) part[((size_t)s * (d + 1) + j) * E + e0 + q] = acc[q];
+        for (int q4 = 0; q4 < EB / 4; ++q4) {
+          const float4 v = row[q4];
+          acc[4 * q4] = fmaf(xv, v.x, acc[4 * q4]);
+          acc[4 * q4 + 1] = fmaf(xv, v.y, acc[4 * q4 + 1]);
+          acc[4 * q4 + 2] = fmaf(xv, v.z, acc[4 * q4 + 2]);
+          acc[4 * q4 + 3] = fmaf(xv, v.w, acc[4 * q4 + 3]);
+        }
+      }
+    }
   }
+  if (j <= d)
+#pragma unroll
+    for (int q = 0; q < EB; ++q)
+      if (q < E) part[((size_t)s * (d + 1) + j) * E + q] = acc[q];
 }
 
 __global__ __launch_bounds__(256) void bwd_router_wgrad_reduce(const float* __restrict__ part,
@@ -603,8 +610,14 @@ void launch_bwd_router_wgrad(const Dims& D, const void* x, const float* ds, floa
   const int slices = kBwdRouterSlices;
   const int tslice = (D.T + slices - 1) / slices;
   const dim3 grid((D.d + 1 + 255) / 256, slices);
-  bwd_router_wgrad_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)x, ds, D.T, D.d, D.E,
-                                                       tslice, part);
+  auto run = [&](auto eb) {
+    bwd_router_wgrad_kernel<bf16_t, decltype(eb)::value><<<grid, 256, 0, s>>>(
+        (const bf16_t*)x, ds, D.T, D.d, D.E, tslice, part);
+  };
+  if (D.E <= 8) run(std::integral_constant<int, 8>{});
+  else if (D.E <= 16) run(std::integral_constant<int, 16>{});
+  else if (D.E <= 32) run(std::integral_constant<int, 32>{});
+  else run(std::integral_constant<int, 64>{});
   bwd_router_wgrad_reduce<<<((D.d + 1) * D.E + 255) / 256, 256, 0, s>>>(part, slices, D.d, D.E,
                                                                        dWr, dbias);
 }
