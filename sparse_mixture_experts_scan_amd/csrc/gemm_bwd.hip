@@ -371,35 +371,38 @@ __global__ __launch_bounds__(256) void bwd_rows_kernel(
 // Per token: ds_t over all E experts.  Selected experts: the softmax over the
 // k gates, ds = g (dg - sum_l g_l dg_l); with alpha > 0 the balance term
 // (alpha N / T) P_tm (f_m - sum_i f_i P_ti), P the full softmax of the scores.
-__global__ __launch_bounds__(64) void bwd_router_kernel(
+__global__ __launch_bounds__(256) void bwd_router_kernel(
     const float* __restrict__ logits, const int32_t* __restrict__ idx,
     const float* __restrict__ gates, const int32_t* __restrict__ tok_row,
     const float* __restrict__ dg_row, const int32_t* __restrict__ counts, int T, int E, int k,
     float alpha, float* __restrict__ ds) {
-  const int t = blockIdx.x * 64 + threadIdx.x;
+  // one wave per token, lane e = expert e (E <= 64)
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int e = threadIdx.x & 63;
   if (t >= T) return;
-  float sum = 0.f;
+  float sum = 0.f;                          // sum_j g_j dg_j, slot order (same in every lane)
   for (int j = 0; j < k; ++j)
     sum += gates[(size_t)t * k + j] * dg_row[tok_row[(size_t)t * k + j]];
-  const float* s = logits + (size_t)t * E;
-  float m = s[0], inv = 0.f, pc = 0.f;
-  // alpha N / T with f = counts / T
-  const float scale = alpha * (float)E / ((float)T * (float)T);
+  float v = 0.f;
+  for (int j = 0; j < k; ++j)
+    if (idx[(size_t)t * k + j] == e)
+      v = gates[(size_t)t * k + j] * (dg_row[tok_row[(size_t)t * k + j]] - sum);
   if (alpha != 0.f) {
-    for (int e = 1; e < E; ++e) m = fmaxf(m, s[e]);
-    float z = 0.f;
-    for (int e = 0; e < E; ++e) z += expf(s[e] - m);
-    inv = 1.f / z;
-    for (int e = 0; e < E; ++e) pc += expf(s[e] - m) * inv * (float)counts[e];
+    // alpha N / T with f = counts / T; full-softmax p by wave reductions
+    const float scale = alpha * (float)E / ((float)T * (float)T);
+    const float se = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+    float m = se;
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    const float ex = e < E ? expf(se - m) : 0.f;
+    float z = ex;
+    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off);
+    const float inv = 1.f / z;
+    const float p = ex * inv;
+    float pc = e < E ? p * (float)counts[e] : 0.f;
+    for (int off = 32; off > 0; off >>= 1) pc += __shfl_xor(pc, off);
+    v += scale * p * ((e < E ? (float)counts[e] : 0.f) - pc);
   }
-  for (int e = 0; e < E; ++e) {
-    float v = 0.f;
-    for (int j = 0; j < k; ++j)
-      if (idx[(size_t)t * k + j] == e)
-        v = gates[(size_t)t * k + j] * (dg_row[tok_row[(size_t)t * k + j]] - sum);
-    if (alpha != 0.f) v += scale * (expf(s[e] - m) * inv) * ((float)counts[e] - pc);
-    ds[(size_t)t * E + e] = v;
-  }
+  if (e < E) ds[(size_t)t * E + e] = v;
 }
 
 // Router weight gradient, partial over a slice of tokens: part[s][j][e] =
@@ -486,18 +489,18 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
     srow[i / k][i % k] = t < nT ? tok_row[(size_t)t * k + i % k] : 0;
   }
   const int c = blockIdx.y * 256 + tid;
+  const int cc = min(c, d - 1);             // lanes past d load a valid column, unused
   float wr[EB];
 #pragma unroll
-  for (int e = 0; e < EB; ++e) wr[e] = (c < d && e < E) ? Wr[(size_t)c * E + e] : 0.f;
+  for (int e = 0; e < EB; ++e) wr[e] = e < E ? Wr[(size_t)cc * E + e] : 0.f;
   __syncthreads();
   if (c >= d) return;
   // rows of split token tiles (from sched[1] on) add their second quarters
   const int split_row0 = (sched && sched[0] > 0) ? sched[1] : INT_MAX;
   const int nt = min(kDxTokens, nT - t0);
-  for (int i = 0; i < nt; ++i) {
-    // every load of the token first (they are independent), then the sum in
-    // slot order
-    float v[MOE_MAX_TOPK][4];
+  // the row loads of token i: both halves' planes (and a split row's extra
+  // planes), all issued before any is used
+  auto load = [&](int i, float (&v)[MOE_MAX_TOPK][4]) {
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
       if (j < k) {
@@ -513,16 +516,31 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
         }
       }
     }
+  };
+  // the slot-order sum plus W_router . ds in expert order
+  auto finish = [&](int i, const float (&v)[MOE_MAX_TOPK][4]) {
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j)
       if (j < k) acc += (srow[i][j] >= split_row0) ? (v[j][0] + v[j][2]) + (v[j][1] + v[j][3])
                                                    : v[j][0] + v[j][1];
-    // W_router . ds in expert order
     float rt = 0.f;
 #pragma unroll
     for (int e = 0; e < EB; ++e) rt = fmaf(wr[e], sds[i][e], rt);
     dx[(size_t)(t0 + i) * d + c] = Elem<T>::from_f32(acc + rt);
+  };
+  // two tokens' loads in flight at a time
+  float va[MOE_MAX_TOPK][4], vb[MOE_MAX_TOPK][4];
+  int i = 0;
+  for (; i + 1 < nt; i += 2) {
+    load(i, va);
+    load(i + 1, vb);
+    finish(i, va);
+    finish(i + 1, vb);
+  }
+  if (i < nt) {
+    load(i, va);
+    finish(i, va);
   }
 }
 
@@ -601,8 +619,8 @@ void launch_bwd_rows(const Dims& D, const void* AB, const void* Z, const int32_t
 void launch_bwd_router(const Dims& D, const float* logits, const int32_t* idx, const float* gates,
                        const int32_t* tok_row, const float* dg_row, const int32_t* counts,
                        float alpha, float* ds, hipStream_t s) {
-  bwd_router_kernel<<<(D.T + 63) / 64, 64, 0, s>>>(logits, idx, gates, tok_row, dg_row, counts,
-                                                    D.T, D.E, D.k, alpha, ds);
+  bwd_router_kernel<<<(D.T + 3) / 4, 256, 0, s>>>(logits, idx, gates, tok_row, dg_row, counts,
+                                                  D.T, D.E, D.k, alpha, ds);
 }
 
 void launch_bwd_router_wgrad(const Dims& D, const void* x, const float* ds, float* part,
