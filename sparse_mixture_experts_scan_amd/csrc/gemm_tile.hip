@@ -564,14 +564,14 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
 // Feature tiles per XCD-local group of the tile order.  Consecutive
 // workgroups of one XCD take the group's feature tiles for one token tile,
 // then the next token tile, so about 32 / fgroup token tiles share each
-// weight panel while they run.  Measured on MI355X: with about 1000 or more
-// rows per expert (4+ token tiles) groups of 4 are best for both GEMMs; with
-// about 500 (E = 64, top-8) groups of 3 for gate/up and 2 for down are 4% and
-// 13% faster than 4, while 1 and wider groups (8 to 28) are slower.
+// weight panel while they run.  Measured on MI355X: groups of 4 are best for
+// gate/up (against 2, 3, 5, 6, 7 and 8: 0.5-2% slower); for down, 4 with
+// about 1000 or more rows per expert (4+ token tiles; 3 and 6 are 0.5-1%
+// slower) and 2 with about 500 (E = 64, top-8; 1, 3 and 4 are 2-4% slower).
 static int tile_feat_group(const Dims& D, bool gateup) {
   const int64_t rows_per_expert = (int64_t)D.T * D.k / D.E;
-  if (rows_per_expert >= 3 * kTileBT) return 4;
-  return gateup ? 3 : 2;
+  if (gateup || rows_per_expert >= 3 * kTileBT) return 4;
+  return 2;
 }
 
 template <bool GATEUP>
