@@ -80,6 +80,7 @@ CASES = [
     (MoEConfig("bwd256_single", 1, 256, 256, 4, 2, "bf16"), 0.1),
     (MoEConfig("bwd256_tiles", 900, 512, 768, 8, 2, "bf16"), 0.01),  # several 256-row tiles
     (MoEConfig("bwd256_many_e", 40, 256, 256, 64, 2, "bf16"), 0.0),  # experts left empty
+    (MoEConfig("bwd256_e32", 96, 256, 256, 32, 4, "bf16"), 0.02),   # 17-32 experts
     (MoEConfig("bwd256_multi", 700, 256, 256, 4, 2, "bf16"), 0.01),  # two row tiles per expert
     (MoEConfig("bwd256_decode", 24, 256, 256, 8, 2, "bf16"), 0.01),  # one router block
 ]
@@ -158,16 +159,20 @@ def row_chunk_tokens(idx, E, chunk, seed=0):
     return np.array(sorted(toks), dtype=np.int64)
 
 
-def test_backward_prefill_sampled():
-    # the full prefill shape of the benchmark (T = 4096, Mixtral layer),
-    # checked on stratified outputs: dx of a token from every 128-row piece of
-    # every expert's rows (each row tile of the recompute, Z and dX GEMMs), and
-    # of every expert, one feature from every 256-feature tile of d_ff: its
-    # rows of dW_gate and dW_up and its column of dW_down (each tile of the
-    # weight-gradient GEMMs along d_ff, all of their tiles along d_model)
+@pytest.mark.parametrize("workload", ["prefill", "fine"])
+def test_backward_prefill_sampled(workload):
+    # the full shapes of the benchmark (T = 4096: the Mixtral layer, and 64
+    # experts of d_ff 3584 with top-8), checked on stratified outputs: dx of
+    # a token from every 128-row piece of every expert's rows (each row tile
+    # of the recompute, Z and dX GEMMs, including the dX schedule's split
+    # tiles), and of every expert, one feature from every 256-feature tile of
+    # d_ff: its rows of dW_gate and dW_up and its column of dW_down (each tile
+    # of the weight-gradient GEMMs along d_ff, all of their tiles along
+    # d_model)
     from sparse_mixture_experts_scan_amd.inputs import CONFIGS
-    cfg = CONFIGS["prefill"]
-    announce(f"case prefill T={cfg.T} d={cfg.d_model} f={cfg.d_ff} E={cfg.E} k={cfg.k} stratified")
+    cfg = CONFIGS[workload]
+    announce(f"case {workload} T={cfg.T} d={cfg.d_model} f={cfg.d_ff} E={cfg.E} k={cfg.k} "
+             "stratified")
     inp = make_inputs(cfg, seed=0)
     dout = make_dout(cfg, seed=0)
     d = H.upload(inp)
