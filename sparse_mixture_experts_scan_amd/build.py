@@ -37,6 +37,12 @@ HIP_FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
              "-Wno-unused-command-line-argument", "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-source additions: the INT4 streaming kernels post-scale every MFMA
+# result with the VALU, and with MFMA accumulators in AGPRs each of those
+# reads is an extra copy; the VGPR form of the MFMAs avoids it.
+SOURCE_FLAGS = {"gemm_q4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -64,7 +70,8 @@ def build(verbose: bool = False) -> str:
     def obj_of(src):
         return os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     for src in SOURCES + PROBE_SOURCES:
-        cmds.append([cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj_of(src)])
+        cmds.append([cc, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+                     "-o", obj_of(src)])
     with ThreadPoolExecutor(min(len(cmds), 8)) as pool:
         list(pool.map(lambda c: _run(c, verbose), cmds))
     for path, srcs in ((LIB_PATH, SOURCES), (PROBE_LIB_PATH, PROBE_SOURCES)):

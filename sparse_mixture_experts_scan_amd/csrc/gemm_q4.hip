@@ -75,11 +75,20 @@ __device__ inline uint4 dequant8(uint32_t w, float s) {
 
 // 8 nibbles (element i at bits 4i) -> bf16(128 + u) of each, as the pairs
 // (0, 4), (1, 5), (2, 6), (3, 7): 128 in bf16 is 0x4300 and its 7 mantissa
-// bits count units of 1, so OR-ing u into bits 0..3 adds u exactly
-__device__ inline uint4 codes8(uint32_t w) {
-  constexpr uint32_t kMask = 0x000F000Fu, kMagic = 0x43004300u;
-  return make_uint4((w & kMask) | kMagic, ((w >> 4) & kMask) | kMagic,
-                    ((w >> 8) & kMask) | kMagic, ((w >> 12) & kMask) | kMagic);
+// bits count units of 1, so OR-ing u into bits 0..3 adds u exactly.
+// The constants come in registers (CodeConsts): a VOP3 and-or cannot encode
+// two literals, and with them inline the compiler emits a separate and + or.
+struct CodeConsts {
+  uint32_t mask, magic;   // 0x000F000F, 0x43004300
+  __device__ static CodeConsts make() {
+    CodeConsts c{0x000F000Fu, 0x43004300u};
+    asm volatile("" : "+v"(c.mask), "+v"(c.magic));   // keep them in VGPRs
+    return c;
+  }
+};
+__device__ inline uint4 codes8(uint32_t w, CodeConsts c) {
+  return make_uint4((w & c.mask) | c.magic, ((w >> 4) & c.mask) | c.magic,
+                    ((w >> 8) & c.mask) | c.magic, ((w >> 12) & c.mask) | c.magic);
 }
 
 // 8 consecutive bf16 activations (pairs (0,1), (2,3), (4,5), (6,7)) into the
@@ -281,6 +290,7 @@ struct Q4Batch {
   template <bool FULL>
   __device__ __forceinline__ void compute_post(f32x4 (&acc)[NW][NF][NT], int valid) {
     const uint4 neg136 = make_uint4(kNeg136x2, kNeg136x2, kNeg136x2, kNeg136x2);
+    const CodeConsts cc = CodeConsts::make();
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (FULL || u < valid) {
@@ -306,7 +316,7 @@ struct Q4Batch {
             for (int n = 0; n < NT; ++n) t[n] = off[n];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const uint4 a = codes8(words[j]);
+              const uint4 a = codes8(words[j], cc);
 #pragma unroll
               for (int n = 0; n < NT; ++n) t[n] = Elem<bf16_t>::mfma16(a, xp[n][j], t[n]);
             }
@@ -619,6 +629,7 @@ __device__ __forceinline__ void stream_q4_dma_body(
           tk[n][q][j] = q4_load16(ra, ao[n] + 16 * j, ab + q * (kQ4Chunk * 2));
   };
   const uint4 neg136 = make_uint4(kNeg136x2, kNeg136x2, kNeg136x2, kNeg136x2);
+  const CodeConsts cc = CodeConsts::make();
   auto compute = [&](const char* slot, const float* ss, const uint4 (&tk)[NT][2][4]) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -647,7 +658,7 @@ __device__ __forceinline__ void stream_q4_dma_body(
           for (int n = 0; n < NT; ++n) t[n] = off[n];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const uint4 a = codes8(words[j]);
+            const uint4 a = codes8(words[j], cc);
 #pragma unroll
             for (int n = 0; n < NT; ++n) t[n] = Elem<bf16_t>::mfma16(a, xp[n][j], t[n]);
           }
