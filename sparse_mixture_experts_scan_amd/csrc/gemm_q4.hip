@@ -512,12 +512,15 @@ __device__ __forceinline__ void stream_q4_dma_body(
   constexpr int kRunBytes = kRunK / 2;          // bytes of a row per run
   constexpr int kSlot = NROW * kRunBytes;       // one wave's weight slot
   constexpr int kDma = kSlot / 1024;            // 16-byte DMAs per run
-  constexpr int kSSlot = NW * 2 * FT;           // one wave's scales (floats)
-  constexpr int kSDma = FT / 32;                // 4-byte DMAs per matrix per run
+  // a matrix's scales of one run: [2 groups][FT rows], padded to whole
+  // 64-lane 4-byte DMAs (lanes past 2 FT load out of range, into the pad)
+  constexpr int kSReg = 2 * FT < 64 ? 64 : 2 * FT;
+  constexpr int kSSlot = NW * kSReg;            // one wave's scales (floats)
+  constexpr int kSDma = kSReg / 64;             // 4-byte DMAs per matrix per run
   constexpr int NWAVE = kQ4Threads / kWave;
   // loads of one run: all outstanding after the next run is issued
   constexpr int kIssue = kDma + NW * kSDma + NT * 8;
-  static_assert(FT % 32 == 0 && NROW % 8 == 0 && kIssue < 64, "block shape");
+  static_assert(FT % 16 == 0 && NROW % 8 == 0 && kSReg % 64 == 0 && kIssue < 64, "block shape");
   static_assert(NW * NF * NT * kWave * 16 <= kSlot, "partial sums fit a wave's slot");
   __shared__ __attribute__((aligned(1024))) char sl0[NWAVE * kSlot];
   __shared__ __attribute__((aligned(1024))) char sl1[NWAVE * kSlot];
@@ -557,6 +560,7 @@ __device__ __forceinline__ void stream_q4_dma_body(
     dvo[j] = (uint32_t)(rr % FT) * qrow + (uint32_t)(((lane & 7) ^ (rr & 7)) * 16);
   }
   // scale DMA m of a matrix: float m * 64 + lane of its [2][FT] run block
+  // (sq = 2 or more: padding)
   int sq[kSDma], sr[kSDma];
 #pragma unroll
   for (int m = 0; m < kSDma; ++m) {
@@ -617,8 +621,8 @@ __device__ __forceinline__ void stream_q4_dma_body(
 #pragma unroll
       for (int m = 0; m < kSDma; ++m)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs[w], (lds_void*)(ss + wave * kSSlot + w * 2 * FT + m * 64), 4,
-            (uint32_t)sr[m] * 4 + (sq[m] ? g1 : g0) * sgrp, 0, 0, 0);
+            rs[w], (lds_void*)(ss + wave * kSSlot + w * kSReg + m * 64), 4,
+            sq[m] < 2 ? (uint32_t)sr[m] * 4 + (sq[m] ? g1 : g0) * sgrp : 0x80000000u, 0, 0, 0);
     const uint32_t ab = (uint32_t)run * (kRunK * 2);
 #pragma unroll
     for (int n = 0; n < NT; ++n)
@@ -630,9 +634,26 @@ __device__ __forceinline__ void stream_q4_dma_body(
   };
   const uint4 neg136 = make_uint4(kNeg136x2, kNeg136x2, kNeg136x2, kNeg136x2);
   const CodeConsts cc = CodeConsts::make();
+  // the LDS reads of the run's fragments and scales first; then per chunk
+  // the codes, then the MFMAs with the fragments' accumulation chains
+  // interleaved (no MFMA waits on the one before it)
   auto compute = [&](const char* slot, const float* ss, const uint4 (&tk)[NT][2][4]) {
+    uint4 wqs[2][NW][NF];
+    f32x4 svs[2][NW][NF];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          wqs[q][w][f] =
+              *reinterpret_cast<const uint4*>(slot + fro[q] + (w * FT + f * 16) * kRunBytes);
+          svs[q][w][f] = *reinterpret_cast<const f32x4*>(ss + sro + w * kSReg + q * FT + f * 16);
+        }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
+      const uint4 (&wq)[NW][NF] = wqs[q];
+      const f32x4 (&sv)[NW][NF] = svs[q];
       f32x4 off[NT];
       uint4 xp[NT][4];
 #pragma unroll
@@ -644,29 +665,41 @@ __device__ __forceinline__ void stream_q4_dma_body(
           xp[n][j] = pair_like_codes(tk[n][q][j]);
         }
       }
+      f32x4 t[NW][NF][NT];
 #pragma unroll
       for (int w = 0; w < NW; ++w)
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          const uint4 wq =
-              *reinterpret_cast<const uint4*>(slot + fro[q] + (w * FT + f * 16) * kRunBytes);
-          const f32x4 sv =
-              *reinterpret_cast<const f32x4*>(ss + sro + (w * 2 + q) * FT + f * 16);
-          const uint32_t words[4] = {wq.x, wq.y, wq.z, wq.w};
-          f32x4 t[NT];
+        for (int f = 0; f < NF; ++f)
 #pragma unroll
-          for (int n = 0; n < NT; ++n) t[n] = off[n];
+          for (int n = 0; n < NT; ++n) t[w][f][n] = off[n];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint4 a = codes8(words[j], cc);
+      for (int j = 0; j < 4; ++j) {
+        uint4 a[NW][NF];
 #pragma unroll
-            for (int n = 0; n < NT; ++n) t[n] = Elem<bf16_t>::mfma16(a, xp[n][j], t[n]);
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+          for (int f = 0; f < NF; ++f) {
+            const uint32_t word = j == 0 ? wq[w][f].x : j == 1 ? wq[w][f].y
+                                : j == 2 ? wq[w][f].z : wq[w][f].w;
+            a[w][f] = codes8(word, cc);
           }
+#pragma unroll
+        for (int w = 0; w < NW; ++w)
+#pragma unroll
+          for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+              t[w][f][n] = Elem<bf16_t>::mfma16(a[w][f], xp[n][j], t[w][f][n]);
+      }
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
 #pragma unroll
           for (int n = 0; n < NT; ++n)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[w][f][n][i] = fmaf(sv[i], t[n][i], acc[w][f][n][i]);
-        }
+            for (int i = 0; i < 4; ++i)
+              acc[w][f][n][i] = fmaf(sv[w][f][i], t[w][f][n][i], acc[w][f][n][i]);
     }
   };
   // vmcnt(kIssue) before a compute: the run it reads has landed in LDS (the
@@ -807,8 +840,8 @@ static auto q4_kernel(int G) {
 #ifndef MOE_Q4_FT_DN
 #define MOE_Q4_FT_DN 64
 #endif
-// output features per block of the LDS-staged form (8 KiB wave slots: two
-// blocks per CU)
+// output features per block of the LDS-staged form (wave slots of
+// NW * FT * 128 bytes)
 #ifndef MOE_Q4_DMA_FT_GU
 #define MOE_Q4_DMA_FT_GU 32
 #endif
