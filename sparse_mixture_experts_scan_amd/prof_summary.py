@@ -71,6 +71,8 @@ def kernel_key(name: str) -> str:
         return "gateup" if "<true>" in name else "down"
     if "stream_q4_kernel" in name:
         return "gateup" if ", true," in name else "down"
+    if "stream_q4_dma_kernel" in name:
+        return "gateup" if ", true>" in name else "down"
     for k in ("quantize_int4", "dequant_int4", "rmsnorm"):
         if k in name:
             return k

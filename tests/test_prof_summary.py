@@ -16,3 +16,5 @@ def test_kernel_roles():
     assert P.kernel_key("void moe::stream_dma_kernel<16, 16, false>(unsigned short const*)") == "down"
     assert P.kernel_key("void moe::tile_gemm_kernel<true>(unsigned short const*)") == "gateup"
     assert P.kernel_key("void moe::tile_gemm_kernel<false>(unsigned short const*)") == "down"
+    assert P.kernel_key("void moe::stream_q4_dma_kernel<16, 32, true>(unsigned short const*)") == "gateup"
+    assert P.kernel_key("void moe::stream_q4_dma_kernel<16, 64, false>(unsigned short const*)") == "down"
