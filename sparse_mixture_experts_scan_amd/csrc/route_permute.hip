@@ -715,7 +715,40 @@ __global__ __launch_bounds__(kRouterThreads) void scatter_gather_kernel(
 // the gate weights and stored bf16 rows (float32 for the later K parts), so
 // the rows are only summed; else fp32 FMA of w with the float32 rows.
 // ---------------------------------------------------------------------------
+// V columns per lane and step: 8 (one 16-byte load of a bf16 row) in the
+// weighted form, else 4 (one 16-byte load of a float32 row).  KT > 0: the
+// top-k at compile time, so that the loads of all k rows are in flight
+// together before the sums (in the same order as with a runtime k).
 template <typename T, bool WEIGHTED>
+struct CombineCols {
+  static constexpr int V = WEIGHTED ? 8 : 4;
+  float v[V];
+  // row r's columns V c .. V c + V - 1 (the first K part)
+  __device__ __forceinline__ void load(const void* y, size_t r, int d, int c) {
+    if constexpr (WEIGHTED) {
+      const uint4 u = reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(y) + r * d)[c];
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w4[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
+      }
+    } else {
+      const float4 f = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(y) + r * d)[c];
+      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    }
+  }
+  // plus a later K part (float32 rows)
+  __device__ __forceinline__ void add_part(const float* yp, int d, int c) {
+#pragma unroll
+    for (int h = 0; h < V / 4; ++h) {
+      const float4 q = reinterpret_cast<const float4*>(yp)[(size_t)c * (V / 4) + h];
+      v[4 * h] += q.x; v[4 * h + 1] += q.y; v[4 * h + 2] += q.z; v[4 * h + 3] += q.w;
+    }
+  }
+};
+
+template <typename T, bool WEIGHTED, int KT>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
                                                       const float* __restrict__ y_parts,
                                                       size_t part_stride,
@@ -724,65 +757,60 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                                                       const float* __restrict__ w, int d, int k,
                                                       const T* __restrict__ resid,
                                                       T* __restrict__ out) {
+  using Cols = CombineCols<T, WEIGHTED>;
+  constexpr int V = Cols::V;
+  constexpr int KB = KT > 0 ? KT : MOE_MAX_TOPK;   // rows held at once
   const int t = blockIdx.x;
+  const int kk = KT > 0 ? KT : k;
   __shared__ int s_row[MOE_MAX_TOPK];
   __shared__ float s_w[MOE_MAX_TOPK];
   __shared__ int s_parts[MOE_MAX_TOPK];
-  if (threadIdx.x < k) {
-    const int r = tok_row[(size_t)t * k + threadIdx.x];
+  if (threadIdx.x < kk) {
+    const int r = tok_row[(size_t)t * kk + threadIdx.x];
     s_row[threadIdx.x] = r;
-    s_w[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+    s_w[threadIdx.x] = w[(size_t)t * kk + threadIdx.x];
     s_parts[threadIdx.x] = (down_sched && r >= down_sched[1]) ? down_sched[0] : 1;
   }
   __syncthreads();
   const int split_row0 = down_sched ? down_sched[1] : 0;
   // blockIdx.y: column slice (small T spreads a token over several blocks)
-  for (int c = blockIdx.y * 256 + threadIdx.x; c < d / 4; c += 256 * gridDim.y) {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      float4 v;
-      if constexpr (WEIGHTED) {
-        const uint2 u = reinterpret_cast<const uint2*>(
-            reinterpret_cast<const bf16_t*>(y) + (size_t)s_row[j] * d)[c];
-        v = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
-                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
-      } else {
-        v = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(y) +
-                                            (size_t)s_row[j] * d)[c];
-      }
-      for (int p = 1; p < s_parts[j]; ++p) {   // further K parts, in part order
-        const float4 q = reinterpret_cast<const float4*>(
-            y_parts + (p - 1) * part_stride + (size_t)(s_row[j] - split_row0) * d)[c];
-        v.x += q.x;
-        v.y += q.y;
-        v.z += q.z;
-        v.w += q.w;
-      }
-      if constexpr (WEIGHTED) {
-        a.x += v.x;
-        a.y += v.y;
-        a.z += v.z;
-        a.w += v.w;
-      } else {
-        const float g = s_w[j];
-        a.x = fmaf(g, v.x, a.x);
-        a.y = fmaf(g, v.y, a.y);
-        a.z = fmaf(g, v.z, a.z);
-        a.w = fmaf(g, v.w, a.w);
+  for (int c = blockIdx.y * 256 + threadIdx.x; c < d / V; c += 256 * gridDim.y) {
+    Cols rows[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j)
+      if (KT > 0 || j < kk) rows[j].load(y, (size_t)s_row[j], d, c);
+    float a[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) a[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (KT == 0 && j >= kk) break;
+      for (int p = 1; p < s_parts[j]; ++p)   // further K parts, in part order
+        rows[j].add_part(y_parts + (p - 1) * part_stride + (size_t)(s_row[j] - split_row0) * d,
+                         d, c);
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        if constexpr (WEIGHTED) a[i] += rows[j].v[i];
+        else a[i] = fmaf(s_w[j], rows[j].v[i], a[i]);
       }
     }
-    T* o = out + (size_t)t * d + 4 * c;
+    T* o = out + (size_t)t * d + V * c;
     if (resid) {   // block wrapper: x + MoE(RMSNorm(x)), one rounding
-      const T* xr = resid + (size_t)t * d + 4 * c;
-      a.x += Elem<T>::to_f32(xr[0]);
-      a.y += Elem<T>::to_f32(xr[1]);
-      a.z += Elem<T>::to_f32(xr[2]);
-      a.w += Elem<T>::to_f32(xr[3]);
+      const T* xr = resid + (size_t)t * d + V * c;
+#pragma unroll
+      for (int i = 0; i < V; ++i) a[i] += Elem<T>::to_f32(xr[i]);
     }
-    if constexpr (sizeof(T) == 2)
-      *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
-    else
-      *reinterpret_cast<float4*>(o) = make_float4(a.x, a.y, a.z, a.w);
+    if constexpr (sizeof(T) == 2) {
+      if constexpr (V == 8)
+        *reinterpret_cast<uint4*>(o) = make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                                                  pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7]));
+      else
+        *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+    } else {
+#pragma unroll
+      for (int h = 0; h < V / 4; ++h)
+        reinterpret_cast<float4*>(o)[h] = make_float4(a[4 * h], a[4 * h + 1], a[4 * h + 2], a[4 * h + 3]);
+    }
   }
 }
 
@@ -867,23 +895,32 @@ void launch_combine(const Dims& D, const void* y, bool weighted, const float* y_
                     int64_t part_rows, const int32_t* down_sched, const int32_t* tok_row,
                     const float* w, const void* resid, void* out, hipStream_t s) {
   const size_t stride = (size_t)part_rows * D.d;
-  // column slices of 256 four-column chunks while the tokens alone give few
-  // blocks
+  const bool w8 = D.bf16 && weighted;   // 8 columns per lane and step, else 4
+  const int V = w8 ? 8 : 4;
+  // column slices of 256 chunks while the tokens alone give few blocks
   int cs = 1;
-  while (D.T * cs < 256 && cs * 2 * 256 * 4 <= D.d) cs *= 2;
+  while (D.T * cs < 256 && cs * 2 * 256 * V <= D.d) cs *= 2;
   const dim3 grid(D.T, cs);
-  if (D.bf16 && weighted)
-    combine_kernel<bf16_t, true><<<grid, 256, 0, s>>>(y, y_parts, stride, down_sched, tok_row, w,
-                                                      D.d, D.k, (const bf16_t*)resid,
-                                                      (bf16_t*)out);
-  else if (D.bf16)
-    combine_kernel<bf16_t, false><<<grid, 256, 0, s>>>(y, y_parts, stride, down_sched, tok_row,
-                                                       w, D.d, D.k, (const bf16_t*)resid,
-                                                       (bf16_t*)out);
-  else
-    combine_kernel<float, false><<<grid, 256, 0, s>>>(y, y_parts, stride, down_sched, tok_row, w,
-                                                      D.d, D.k, (const float*)resid,
-                                                      (float*)out);
+#define MOE_COMBINE(TT, WW, KK)                                                             \
+  combine_kernel<TT, WW, KK><<<grid, 256, 0, s>>>(y, y_parts, stride, down_sched, tok_row, w, \
+                                                  D.d, D.k, (const TT*)resid, (TT*)out)
+#define MOE_COMBINE_K(TT, WW)          \
+  switch (D.k) {                       \
+    case 1: MOE_COMBINE(TT, WW, 1); break; \
+    case 2: MOE_COMBINE(TT, WW, 2); break; \
+    case 4: MOE_COMBINE(TT, WW, 4); break; \
+    case 8: MOE_COMBINE(TT, WW, 8); break; \
+    default: MOE_COMBINE(TT, WW, 0); break; \
+  }
+  if (w8) {
+    MOE_COMBINE_K(bf16_t, true)
+  } else if (D.bf16) {
+    MOE_COMBINE_K(bf16_t, false)
+  } else {
+    MOE_COMBINE_K(float, false)
+  }
+#undef MOE_COMBINE_K
+#undef MOE_COMBINE
 }
 
 }  // namespace moe
