@@ -262,7 +262,8 @@ __global__ __launch_bounds__(kGT) void grouped_gemm_kernel(
 // tiles (0: none), first row of the first of them}.
 __global__ void bwd_tile_table_kernel(const int32_t* __restrict__ counts,
                                       const int32_t* __restrict__ offsets, int E, int max_tiles,
-                                      int n_at, int max_split, int32_t* __restrict__ tb_count,
+                                      int n_at, int max_split, int parts,
+                                      int32_t* __restrict__ tb_count,
                                       int32_t* __restrict__ tb_exp,
                                       int32_t* __restrict__ tb_row0,
                                       int32_t* __restrict__ tb_rows,
@@ -277,11 +278,13 @@ __global__ void bwd_tile_table_kernel(const int32_t* __restrict__ counts,
     }
   }
   *tb_count = n;
+  // dX schedule: the last sp token tiles run each K part as two halves, so
+  // that the pieces fill the last round of the CUs
   int sp = 0;
-  const int rest = (2 * n * n_at) % kCus;
+  const int rest = (parts * n * n_at) % kCus;
   if (rest > 0 && n_at > 0) {
-    sp = min(n, (rest + 2 * n_at - 1) / (2 * n_at));
-    if (sp > max_split || 4 * sp * n_at > kCus) sp = 0;
+    sp = min(n, (rest + parts * n_at - 1) / (parts * n_at));
+    if (sp > max_split || 2 * parts * sp * n_at > kCus) sp = 0;
   }
   sched[0] = sp;
   sched[1] = sp > 0 ? tb_row0[n - sp] : 0;
@@ -466,7 +469,8 @@ __global__ __launch_bounds__(256) void bwd_router_wgrad_reduce(const float* __re
 
 // dx_t = sum_j dX[tok_row[t][j]] (slot order) + sum_e W_router[.][e] ds_t[e]
 template <typename T, int EB>
-__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dX, size_t plane,
+__global__ __launch_bounds__(256) void bwd_dx_kernel(int nplanes, const float* __restrict__ dX,
+                                                     size_t plane,
                                                      const float* __restrict__ dX_extra,
                                                      size_t extra_plane,
                                                      const int32_t* __restrict__ sched,
@@ -498,8 +502,9 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
   // rows of split token tiles (from sched[1] on) add their second quarters
   const int split_row0 = (sched && sched[0] > 0) ? sched[1] : INT_MAX;
   const int nt = min(kDxTokens, nT - t0);
-  // the row loads of token i: both halves' planes (and a split row's extra
-  // planes), all issued before any is used
+  // the row loads of token i: its planes (and a split row's extra planes),
+  // all issued before any is used; a plane not in use reads as zero
+  const bool two = nplanes > 1;
   auto load = [&](int i, float (&v)[MOE_MAX_TOPK][4]) {
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
@@ -507,12 +512,12 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
         const int r = srow[i][j];
         const size_t o = (size_t)r * d + c;
         v[j][0] = dX[o];
-        v[j][1] = dX[plane + o];
+        v[j][1] = two ? dX[plane + o] : 0.f;
         v[j][2] = v[j][3] = 0.f;
         if (r >= split_row0) {
           const size_t oe = (size_t)(r - split_row0) * d + c;
           v[j][2] = dX_extra[oe];
-          v[j][3] = dX_extra[extra_plane + oe];
+          if (two) v[j][3] = dX_extra[extra_plane + oe];
         }
       }
     }
@@ -564,10 +569,12 @@ void launch_zero_fill(void* p, size_t bytes, hipStream_t s) {
 
 
 void launch_bwd_tile_table(const Dims& D, const int32_t* counts, const int32_t* offsets,
-                           int max_tiles, int max_split, int32_t* tb_count, int32_t* tb_exp,
-                           int32_t* tb_row0, int32_t* tb_rows, int32_t* sched, hipStream_t s) {
+                           int max_tiles, int max_split, int dx_parts, int32_t* tb_count,
+                           int32_t* tb_exp, int32_t* tb_row0, int32_t* tb_rows, int32_t* sched,
+                           hipStream_t s) {
   bwd_tile_table_kernel<<<1, 64, 0, s>>>(counts, offsets, D.E, max_tiles, D.d / kBwdTileBT,
-                                         max_split, tb_count, tb_exp, tb_row0, tb_rows, sched);
+                                         max_split, dx_parts, tb_count, tb_exp, tb_row0, tb_rows,
+                                         sched);
 }
 
 void launch_bwd_gather(const Dims& D, const void* src, const int32_t* row_token, void* dst,
@@ -640,13 +647,14 @@ void launch_bwd_router_wgrad(const Dims& D, const void* x, const float* ds, floa
                                                                        dWr, dbias);
 }
 
-void launch_bwd_dx(const Dims& D, const float* dX, size_t plane, const float* dX_extra,
-                   size_t extra_plane, const int32_t* sched, const int32_t* tok_row,
-                   const float* Wr, const float* ds, void* dx, hipStream_t s) {
+void launch_bwd_dx(const Dims& D, int nplanes, const float* dX, size_t plane,
+                   const float* dX_extra, size_t extra_plane, const int32_t* sched,
+                   const int32_t* tok_row, const float* Wr, const float* ds, void* dx,
+                   hipStream_t s) {
   const dim3 grid((D.T + kDxTokens - 1) / kDxTokens, (D.d + 255) / 256);
   auto run = [&](auto eb) {
     bwd_dx_kernel<bf16_t, decltype(eb)::value><<<grid, 256, 0, s>>>(
-        dX, plane, dX_extra, extra_plane, sched, tok_row, Wr, ds, D.T, D.d, D.E, D.k,
+        nplanes, dX, plane, dX_extra, extra_plane, sched, tok_row, Wr, ds, D.T, D.d, D.E, D.k,
         (bf16_t*)dx);
   };
   if (D.E <= 8) run(std::integral_constant<int, 8>{});

@@ -104,10 +104,10 @@ struct BgArgs {
   // writes the C plane c_pstride elements after C0.
   int kparts;
   size_t c_pstride;
-  // mode 0, two parts (dX): sched = {split token tiles sp, their first row}
-  // from the tile table.  The last sp token tiles run each part as two K
-  // halves (quarters of the whole); a part's second half goes to the extra
-  // plane C_extra + part * extra_pstride, row r at r - sched[1].  NULL: none.
+  // mode 0 (dX): sched = {split token tiles sp, their first row} from the
+  // tile table.  The last sp token tiles run each part as two K halves; a
+  // part's second half goes to the extra plane C_extra + part *
+  // extra_pstride, row r at r - sched[1].  NULL: none.
   const int32_t* sched;
   float* C_extra;
   size_t extra_pstride;
@@ -366,14 +366,21 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
     c.ld_bytes = (uint32_t)p.lda * 2;
     if constexpr (MODE == 0) Am += (size_t)e * p.a_estride;
     if constexpr (KSA) {
-      size_t first_row = (size_t)koff;      // mode 0: the K range's first row of A
+      // mode 0: the K range [koff, koff + kn) of A's rows; A1 takes over at
+      // row a_split_k (from its own first row), so a range can lie in A0, in
+      // A1, or cross from one to the other
+      size_t first_row = (size_t)koff;
       if constexpr (MODE == 1) first_row = (size_t)p.offsets[e];
+      const bf16_t* A1m = p.A1 + (MODE == 0 ? (size_t)e * p.a_estride : 0);
+      if (MODE == 0 && koff >= p.a_split_k) {
+        Am = A1m;
+        first_row = (size_t)(koff - p.a_split_k);
+      }
       c.ks_base = reinterpret_cast<const char*>(Am + first_row * p.lda + (size_t)a_tile * kBT);
       c.ks_base1 = c.ks_base;
-      if (p.a_split_k < kn) {
-        c.split_k = p.a_split_k;
-        c.ks_base1 = reinterpret_cast<const char*>(p.A1 + (MODE == 0 ? (size_t)e * p.a_estride : 0) +
-                                                   first_row * p.lda + (size_t)a_tile * kBT);
+      if (koff < p.a_split_k && p.a_split_k < koff + kn) {
+        c.split_k = p.a_split_k - koff;
+        c.ks_base1 = reinterpret_cast<const char*>(A1m + (size_t)a_tile * kBT);
       }
     } else {
       c.r = buffer_rsrc(Am + (size_t)a_tile * kBT * p.lda, kBT * c.ld_bytes);
@@ -551,9 +558,9 @@ void bg_launch(BgArgs p, int groups, hipStream_t s) {
   const int tiles = p.n_at * p.n_bt;
   p.per_xcd = MODE == 1 ? (tiles + kBXcds - 1) / kBXcds              // per expert
                         : (groups * tiles + kBXcds - 1) / kBXcds;    // all tiles
-  // with a schedule, up to kCus / 2 more work-groups: the split tiles' extra
-  // quarters
-  const int grid = p.per_xcd * kBXcds * (MODE == 1 ? groups : 1) + (p.sched ? kCus / 2 : 0);
+  // with a schedule, kCus more work-groups for the split tiles' extra K
+  // halves (at most kCus / 2 beyond the tiles they replace; the rest exit)
+  const int grid = p.per_xcd * kBXcds * (MODE == 1 ? groups : 1) + (p.sched ? kCus : 0);
   if (grid > 0) bwd_tile_kernel<KSA, KSB, MODE, CBF16, SWAP><<<grid, kBThreads, 0, s>>>(p);
 }
 
@@ -614,13 +621,14 @@ void launch_bwd_z(const Dims& D, const void* dp, const void* Wd, void* z, int ma
 }
 
 // dX_r = W1^T dA + W3^T dB: A = [W1; W3] down its columns (index d, k = 2 d_ff)
-void launch_bwd_dxs(const Dims& D, const void* dab, const void* Wg, const void* Wu, float* dxs,
-                    size_t plane, float* dxs_extra, size_t extra_plane, const int32_t* sched,
-                    int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
-                    const int32_t* tb_row0, const int32_t* tb_rows, hipStream_t s) {
-  // two K parts (the d_ff of W1, then that of W3), one plane each: twice the
-  // workgroups of one K = 2 d_ff pass, which on prefill fill 4.5 rounds of
-  // the CUs instead of 2.25
+void launch_bwd_dxs(const Dims& D, int parts, const void* dab, const void* Wg, const void* Wu,
+                    float* dxs, size_t plane, float* dxs_extra, size_t extra_plane,
+                    const int32_t* sched, int max_tiles, const int32_t* tb_count,
+                    const int32_t* tb_exp, const int32_t* tb_row0, const int32_t* tb_rows,
+                    hipStream_t s) {
+  // parts = 2: the d_ff of W1, then that of W3, one plane each, twice the
+  // work-groups of one pass (on prefill 4.5 rounds of the CUs instead of
+  // 2.25); parts = 1: one K = 2 d_ff pass, A switching from W1 to W3 at d_ff
   BgArgs p = bg_rows_args(tb_count, tb_exp, tb_row0, tb_rows, max_tiles);
   p.A0 = (const bf16_t*)Wg;
   p.A1 = (const bf16_t*)Wu;
@@ -630,14 +638,15 @@ void launch_bwd_dxs(const Dims& D, const void* dab, const void* Wg, const void* 
   p.ldb = 2 * D.f;
   p.C0 = dxs;
   p.ldc = D.d;
-  p.K = D.f;
+  p.K = parts == 1 ? 2 * D.f : D.f;
+  if (parts == 1) p.a_split_k = D.f;
   p.n_at = D.d / kBT;
-  p.kparts = 2;
+  p.kparts = parts;
   p.c_pstride = plane;
   p.sched = sched;
   p.C_extra = dxs_extra;
   p.extra_pstride = extra_plane;
-  bg_launch<true, false, 0, false>(p, 2, s);
+  bg_launch<true, false, 0, false>(p, parts, s);
 }
 
 // dW2[e] = Hg^T dOut over the expert's rows: C[o][f], A = Hg (index f),

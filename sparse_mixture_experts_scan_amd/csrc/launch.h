@@ -99,10 +99,12 @@ void launch_down_q4(const Dims& D, const void* h, const Q4Weights& Wd, float* y,
                     const int32_t* counts, const int32_t* offsets, const int32_t* num_tiles,
                     const int32_t* tile_expert, hipStream_t s);
 // backward (bf16): grouped GEMMs and the steps around them
-// (and the dX schedule in sched[2]; at most max_split split token tiles)
+// (and the dX schedule in sched[2] for a dX GEMM of dx_parts K parts; at
+// most max_split split token tiles)
 void launch_bwd_tile_table(const Dims& D, const int32_t* counts, const int32_t* offsets,
-                           int max_tiles, int max_split, int32_t* tb_count, int32_t* tb_exp,
-                           int32_t* tb_row0, int32_t* tb_rows, int32_t* sched, hipStream_t s);
+                           int max_tiles, int max_split, int dx_parts, int32_t* tb_count,
+                           int32_t* tb_exp, int32_t* tb_row0, int32_t* tb_rows, int32_t* sched,
+                           hipStream_t s);
 void launch_bwd_gather(const Dims& D, const void* src, const int32_t* row_token, void* dst,
                        hipStream_t s);
 // C[rows of tile][N] (+)= A[rows][K] (k contiguous) x B_e, per tile of the table
@@ -119,13 +121,14 @@ void launch_bwd_recompute(const Dims& D, const void* xs, const void* Wg, const v
 void launch_bwd_z(const Dims& D, const void* dp, const void* Wd, void* z, int max_tiles,
                   const int32_t* tb_count, const int32_t* tb_exp, const int32_t* tb_row0,
                   const int32_t* tb_rows, hipStream_t s);
-// dX in two K halves, one plane each; the split token tiles of sched in four
-// K quarters, the second quarter of each half into the extra planes (row r
-// at r - sched[1])
-void launch_bwd_dxs(const Dims& D, const void* dab, const void* Wg, const void* Wu, float* dxs,
-                    size_t plane, float* dxs_extra, size_t extra_plane, const int32_t* sched,
-                    int max_tiles, const int32_t* tb_count, const int32_t* tb_exp,
-                    const int32_t* tb_row0, const int32_t* tb_rows, hipStream_t s);
+// dX in `parts` K parts (1: K = 2 d_ff; 2: the W1 and the W3 half), one plane
+// each; the split token tiles of sched run each part as two K halves, the
+// second half of each part into its extra plane (row r at r - sched[1])
+void launch_bwd_dxs(const Dims& D, int parts, const void* dab, const void* Wg, const void* Wu,
+                    float* dxs, size_t plane, float* dxs_extra, size_t extra_plane,
+                    const int32_t* sched, int max_tiles, const int32_t* tb_count,
+                    const int32_t* tb_exp, const int32_t* tb_row0, const int32_t* tb_rows,
+                    hipStream_t s);
 void launch_bwd_wgrad_down(const Dims& D, const void* dp, const void* hg, void* dWd,
                            const int32_t* counts, const int32_t* offsets, hipStream_t s);
 void launch_bwd_wgrad_gate_up(const Dims& D, const void* dab, const void* xs, void* dWg,
@@ -142,12 +145,13 @@ void launch_bwd_router(const Dims& D, const float* logits, const int32_t* idx, c
                        float alpha, float* ds, hipStream_t s);
 void launch_bwd_router_wgrad(const Dims& D, const void* x, const float* ds, float* part,
                              float* dWr, float* dbias, hipStream_t s);
-// dX holds two planes (the W1 and W3 halves of the contraction), `plane`
-// elements apart, plus (sched non-NULL, sched[0] > 0) the split rows' extra
-// planes, `extra_plane` apart
-void launch_bwd_dx(const Dims& D, const float* dX, size_t plane, const float* dX_extra,
-                   size_t extra_plane, const int32_t* sched, const int32_t* tok_row,
-                   const float* Wr, const float* ds, void* dx, hipStream_t s);
+// dX holds `nplanes` planes (1, or 2: the W1 and W3 halves of the
+// contraction), `plane` elements apart, plus (sched non-NULL, sched[0] > 0)
+// as many extra planes for the split rows, `extra_plane` apart
+void launch_bwd_dx(const Dims& D, int nplanes, const float* dX, size_t plane,
+                   const float* dX_extra, size_t extra_plane, const int32_t* sched,
+                   const int32_t* tok_row, const float* Wr, const float* ds, void* dx,
+                   hipStream_t s);
 void launch_zero_fill(void* p, size_t bytes, hipStream_t s);
 // a5: gate-weighted gather-sum back to token order
 // resid: x for the block wrapper (out = x + layer), or NULL

@@ -515,7 +515,7 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   moe::bf16_t* z = reinterpret_cast<moe::bf16_t*>(ws + b.z);
   float* dxs = F(b.dxs);
   const size_t dx_plane = (size_t)D.max_rows * d;   // dxs: [2][max_rows][d]
-  float* dxs_extra = F(b.dxs_extra);                 // [2][dx_split_rows][d]
+  float* dxs_extra = F(b.dxs_extra);                 // [dx_parts][dx_split_rows][d]
   const size_t dx_extra_plane = (size_t)b.dx_split_rows * d;
   float* dg = F(b.dg);
   float* ds = F(b.ds);
@@ -542,8 +542,8 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   moe::launch_scatter(D, x, idx, nullptr, I(b.block_counts), offsets, tok_row, row_token, nullptr,
                       xs, s);
   moe::launch_bwd_gather(D, dout, row_token, dp, s);
-  moe::launch_bwd_tile_table(D, counts, offsets, b.max_tiles, b.dx_max_split, tb_count, tb_exp,
-                             tb_row0, tb_rows, dx_sched, s);
+  moe::launch_bwd_tile_table(D, counts, offsets, b.max_tiles, b.dx_max_split, b.dx_parts,
+                             tb_count, tb_exp, tb_row0, tb_rows, dx_sched, s);
   if ((st = check(1, "routing launch")) != MOE_OK) return st;
   // the 256 x 256 ping-pong GEMMs when both widths allow, else the generic one
   const bool tiled = moe::bwd_tile_shape_ok(d, f);
@@ -572,8 +572,9 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
   if ((st = check(4, "row/router backward launch")) != MOE_OK) return st;
   // dX_r = W1^T dA + W3^T dB
   if (tiled) {
-    moe::launch_bwd_dxs(D, dab, W_gate, W_up, dxs, dx_plane, dxs_extra, dx_extra_plane,
-                        dx_sched, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
+    moe::launch_bwd_dxs(D, b.dx_parts, dab, W_gate, W_up, dxs, dx_plane, dxs_extra,
+                        dx_extra_plane, dx_sched, b.max_tiles, tb_count, tb_exp, tb_row0,
+                        tb_rows, s);
   } else {
     moe::launch_bwd_gemm_rows(dab, 2 * f, W_gate, d, false, wstride, dxs, false, d, D.max_rows,
                               d, f, false, b.max_tiles, tb_count, tb_exp, tb_row0, tb_rows, s);
@@ -582,8 +583,8 @@ int moe_ffn_backward(const void* x, const float* W_router, const void* W_gate, c
                               tb_count, tb_exp, tb_row0, tb_rows, s);
   }
   if ((st = check(5, "dX launch")) != MOE_OK) return st;
-  moe::launch_bwd_dx(D, dxs, dx_plane, dxs_extra, dx_extra_plane, tiled ? dx_sched : nullptr,
-                     tok_row, W_router, ds, dx, s);
+  moe::launch_bwd_dx(D, tiled ? b.dx_parts : 2, dxs, dx_plane, dxs_extra, dx_extra_plane,
+                     tiled ? dx_sched : nullptr, tok_row, W_router, ds, dx, s);
   if ((st = check(6, "dx launch")) != MOE_OK) return st;
   // weight gradients over each expert's rows
   if (tiled)

@@ -93,7 +93,23 @@ bool bwd_tile_shape_ok(int64_t d, int64_t f) { return d % kBwdTileBT == 0 && f %
 // The dX GEMM runs two K halves of each (token tile, feature tile); the
 // token tiles of a partial last round may instead run four K quarters each,
 // if those quarters fit one round: kCus / 4 per feature-tile row.
-int bwd_dx_split_tiles(int64_t d) { return (int)(kCus / (4 * (d / kBwdTileBT))); }
+// split token tiles whose 2 * parts K pieces per feature tile fit one round
+int bwd_dx_split_tiles(int64_t d, int parts) {
+  return (int)(kCus / (2 * parts * (d / kBwdTileBT)));
+}
+
+// dX = W1^T dA + W3^T dB in one K = 2 d_ff pass when the token tiles alone
+// (at least T k / 256 of them) fill about MOE_DX_ONE_PART_ROUNDS rounds of
+// the CUs: each routed row's dX is then one fp32 plane, half the GEMM's
+// stores and half the dx kernel's loads.  Fewer tiles: two K parts (the W1
+// and the W3 half), twice the work-groups.
+#ifndef MOE_DX_ONE_PART_ROUNDS
+#define MOE_DX_ONE_PART_ROUNDS 4
+#endif
+int bwd_dx_parts(int64_t T, int64_t d, int32_t k) {
+  const int64_t tiles = (T * k / kBwdTileBT) * (d / kBwdTileBT);
+  return tiles >= (int64_t)MOE_DX_ONE_PART_ROUNDS * kCus ? 1 : 2;
+}
 
 int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dtype, bool block,
               Plan* p, std::string* why) {
@@ -225,11 +241,13 @@ int make_bwd_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, BwdPlan
   b->hg = c.take(2 * R * f);
   b->dp = c.take(2 * R * d);
   b->dxs = c.take(4 * 2 * R * d);   // two planes: the W1 and W3 halves of dX
-  // two more for the split token tiles' second quarters (tiled form): their
-  // rows span at most the tiles plus the padding between experts
-  b->dx_max_split = bwd_tile_shape_ok(d, f) ? bwd_dx_split_tiles(d) : 0;
+  // (the tiled form with one K part uses the first)
+  b->dx_parts = bwd_tile_shape_ok(d, f) ? bwd_dx_parts(T, d, k) : 2;
+  // one more per part for the split token tiles' second K halves (tiled
+  // form): their rows span at most the tiles plus the padding between experts
+  b->dx_max_split = bwd_tile_shape_ok(d, f) ? bwd_dx_split_tiles(d, b->dx_parts) : 0;
   b->dx_split_rows = b->dx_max_split * (kBwdTileBT + kBwdPadRows);
-  b->dxs_extra = c.take(4 * 2 * (size_t)b->dx_split_rows * d);
+  b->dxs_extra = c.take(4 * (size_t)b->dx_parts * b->dx_split_rows * d);
   b->dg = c.take(4 * R);
   b->ds = c.take(4 * (size_t)T * E);
   b->wpart = c.take(4 * (size_t)kBwdRouterSlices * (d + 1) * E);

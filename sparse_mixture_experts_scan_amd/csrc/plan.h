@@ -70,7 +70,9 @@ constexpr int q4_quantize_max_k() { return 65536; }
 bool bwd_tile_shape_ok(int64_t d, int64_t f);
 // token tiles whose dX work the tiled backward may split into K quarters to
 // fill a partial last round of work-groups (0: never)
-int bwd_dx_split_tiles(int64_t d);
+int bwd_dx_split_tiles(int64_t d, int parts);
+// K parts of the tiled dX GEMM (1 or 2) for T tokens, top-k and d_model
+int bwd_dx_parts(int64_t T, int64_t d, int32_t k);
 
 // ---- forward plan
 struct Plan {
@@ -89,6 +91,7 @@ int make_plan(int64_t T, int64_t d, int64_t f, int32_t E, int32_t k, int32_t dty
 struct BwdPlan {
   Dims D;
   int max_tiles;     // rows of the row-tile table
+  int dx_parts;      // K parts of the tiled dX GEMM, one fp32 plane each (1 or 2)
   int dx_max_split;  // token tiles the dX schedule may split (0: none)
   int dx_split_rows; // rows of each extra dX plane (the split token tiles' span)
   // tb: [1 + 3 max_tiles + 2] int32: count, experts, first rows, row counts,

@@ -159,10 +159,14 @@ def row_chunk_tokens(idx, E, chunk, seed=0):
     return np.array(sorted(toks), dtype=np.int64)
 
 
-@pytest.mark.parametrize("workload", ["prefill", "fine"])
+@pytest.mark.parametrize("workload", ["prefill", "fine", "skewed"])
 def test_backward_prefill_sampled(workload):
     # the full shapes of the benchmark (T = 4096: the Mixtral layer, and 64
-    # experts of d_ff 3584 with top-8), checked on stratified outputs: dx of
+    # experts of d_ff 3584 with top-8; T = 8192 with skewed routing), checked
+    # on stratified outputs.  The dX GEMM runs in two K parts on prefill and
+    # in one K = 2 d_ff pass on the other two, and at seed 0 the skewed
+    # routing leaves a partial last round that the schedule splits into K
+    # halves.  The outputs: dx of
     # a token from every 128-row piece of every expert's rows (each row tile
     # of the recompute, Z and dX GEMMs, including the dX schedule's split
     # tiles), and of every expert, one feature from every 256-feature tile of
