@@ -494,9 +494,24 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(int nplanes, const float* _
   }
   const int c = blockIdx.y * 256 + tid;
   const int cc = min(c, d - 1);             // lanes past d load a valid column, unused
+  // the column's E router weights (contiguous in W_router [d][E]): 16-byte
+  // loads when rows are 16-byte aligned, so that a wave touches each of its
+  // 64 rows' lines once per 4 experts rather than once per expert
   float wr[EB];
+  if (E % 4 == 0 && reinterpret_cast<uintptr_t>(Wr) % 16 == 0) {
+    const float4* wrow = reinterpret_cast<const float4*>(Wr + (size_t)cc * E);
 #pragma unroll
-  for (int e = 0; e < EB; ++e) wr[e] = e < E ? Wr[(size_t)cc * E + e] : 0.f;
+    for (int j = 0; j < EB / 4; ++j) {
+      const float4 v = 4 * j < E ? wrow[j] : make_float4(0.f, 0.f, 0.f, 0.f);
+      wr[4 * j] = v.x;
+      wr[4 * j + 1] = v.y;
+      wr[4 * j + 2] = v.z;
+      wr[4 * j + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EB; ++e) wr[e] = e < E ? Wr[(size_t)cc * E + e] : 0.f;
+  }
   __syncthreads();
   if (c >= d) return;
   // rows of split token tiles (from sched[1] on) add their second quarters
