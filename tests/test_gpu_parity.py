@@ -112,10 +112,15 @@ SMALL = [
     MoEConfig("tile_sched4", 2048, 4096, 512, 8, 2, "bf16"),
     MoEConfig("tile_sched2", 2100, 4096, 512, 8, 2, "bf16"),
     MoEConfig("tile_sched1", 1800, 4096, 512, 8, 2, "bf16"),
+    # top-k outside 1, 2, 4, 8 on the tiled form: the combine's runtime-k path
+    # over gate-weighted bf16 rows (top-6 also reads the tokens in place)
+    MoEConfig("tile_top3", 900, 256, 256, 8, 3, "bf16"),
+    MoEConfig("tile_top6", 600, 256, 384, 16, 6, "bf16"),
 ]
 
 TILED = {"tile_small", "tile_ragged", "tile_fine", "tile_split", "tile_multi", "tile_short128",
-         "tile_short_edge", "tile_short_ksplit", "tile_sched4", "tile_sched2", "tile_sched1"}
+         "tile_short_edge", "tile_short_ksplit", "tile_sched4", "tile_sched2", "tile_sched1",
+         "tile_top3", "tile_top6"}
 # the down GEMM's schedule (K parts, first split token tile) at seed 1;
 # fewer tiles than CUs: every token tile split
 DOWN_SCHED = {"tile_split": (4, 0), "tile_short128": (2, 0), "tile_short_ksplit": (4, 0),
