@@ -121,6 +121,8 @@ CASES = [
     (MoEConfig("q4_ragged", 33, 384, 256, 6, 3, "bf16"), 64, 0),
     (MoEConfig("q4_group32", 20, 256, 384, 4, 2, "bf16"), 32, 0),
     (MoEConfig("q4_group256", 24, 512, 256, 8, 2, "bf16"), 256, 0),  # two chunks per group
+    # three chunks per group: a 256-K run of the LDS-staged form straddles two groups
+    (MoEConfig("q4_group384", 24, 768, 768, 8, 2, "bf16"), 384, 0),
     (MoEConfig("q4_bt32", 300, 256, 256, 8, 2, "bf16"), 128, 0),     # 32-row token tiles
     (MoEConfig("q4_single", 1, 128, 128, 4, 1, "bf16"), 128, 0),
     (MoEConfig("q4_tiled", 1000, 256, 384, 8, 2, "bf16"), 128, 1),   # dequantize + tile
