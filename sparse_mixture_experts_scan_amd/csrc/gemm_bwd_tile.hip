@@ -275,6 +275,20 @@ __device__ inline uint32_t ks_lane_base(int lane, int q) {
 
 }  // namespace
 
+// Epilogue stores of the weight gradients (written once, never read by the
+// layer) are non-temporal: measured on MI355X, dW_gate | dW_up 1.3% faster
+// on the Mixtral prefill shape and 2.5% on the 64-expert top-8 one.  The
+// a | b, Z and dX outputs, read again by the next kernels, keep the default
+// policy (non-temporal there: even, or slower overall).
+typedef uint32_t bwd_u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ void bwd_store16(void* p, uint4 v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(bwd_u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<bwd_u32x4*>(p));
+  else
+    *reinterpret_cast<uint4*>(p) = v;
+}
+
 template <bool KSA, bool KSB, int MODE, bool CBF16, bool SWAP>
 __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
   __shared__ __attribute__((aligned(1024))) char sa0[kBOper];
@@ -502,7 +516,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
               *reinterpret_cast<const uint4*>(sbr + lrow * kStagePitch + chunk * 16);
           const size_t off =
               (size_t)(brow_base + brow) * p.ldc + (size_t)at * kBT + chunk * 8;
-          *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(Cb) + off) = v;
+          bwd_store16<MODE == 1>(reinterpret_cast<bf16_t*>(Cb) + off, v);
         }
       }
       __syncthreads();
@@ -542,7 +556,7 @@ __global__ __launch_bounds__(kBThreads, 1) void bwd_tile_kernel(BgArgs p) {
                 *reinterpret_cast<const uint4*>(sbr + lrow * kStagePitch + chunk * 16);
             const size_t off = (size_t)(brow_base + brow) * p.ldc + (size_t)at * kBT + ch * 128 +
                                chunk * 4;
-            *reinterpret_cast<uint4*>(reinterpret_cast<float*>(Cb) + off) = v;
+            bwd_store16<false>(reinterpret_cast<float*>(Cb) + off, v);
           }
         }
         __syncthreads();
