@@ -8,6 +8,8 @@
 //   section "MoEレイヤー全体の実装": the per-expert token mask and gather,
 //     and the weighted scatter-add back into a zeros_like(x) output, which is
 //     done here as a gather-sum (each token reads its k expert rows).
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -185,8 +187,9 @@ __device__ inline void block_prob_sums(const float (*slog)[65], int t0, int nT, 
 // Scores of kRouterTokens tokens over the d_model range of split blockIdx.y
 // (all of d_model when splits == 1).  splits == 1: adds the bias, selects
 // and writes the routing; splits > 1: writes the partial scores to `part`
-// ([split][token][kRouterPartStride]) for router_select_kernel.
-template <typename T>
+// ([split][token][kRouterPartStride]) for router_select_kernel.  MB: 16-row
+// expert blocks in use, (E + 15) / 16.
+template <typename T, int MB>
 __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
     const T* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
     int nT, int d, int E, int k, int splits, float* __restrict__ part,
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
     float* __restrict__ logits_out) {
   constexpr int TB = kRouterTokens;
   constexpr int NB = TB / 16;            // token column blocks
-  constexpr int MB = 64 / 16;            // expert row blocks (max)
+  static_assert(MB >= 1 && MB * 16 <= 64, "expert row blocks");
   constexpr int NWAVE = kRouterMfmaThreads / kWave;
   constexpr int U = kRouterUnroll;
   __shared__ f32x4 red[4][MB * NB][kWave];
@@ -205,7 +208,6 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t0 = blockIdx.x * TB;
-  const int mb_used = (E + 15) / 16;
   const int m = lane & 15, g = lane >> 4;
   if (tid < 64) hist[tid] = 0;
 
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
       for (int a = 0; a < MB; ++a) {
         const int ex = a * 16 + m;
         av[u][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (kok && a < mb_used && ex < E) {
+        if (kok && ex < E) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             av[u][a][i] = gamma ? Wr[(size_t)(k0 + i) * E + ex] * gamma[k0 + i]
@@ -250,17 +252,18 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
         }
       }
     }
+    // k-step i outermost: consecutive MFMAs go to different accumulators, so
+    // none waits on the one before it (each accumulator still sees the k
+    // steps in the same order)
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int a = 0; a < MB; ++a)
-        if (a < mb_used) {
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int a = 0; a < MB; ++a)
 #pragma unroll
           for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][a][i], bv[u][b][i], acc[a][b], 0, 0, 0);
-        }
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][a][i], bv[u][b][i], acc[a][b], 0, 0, 0);
   }
   // fixed-order reduction of the 8 wave partials: (w + w+4), then 0 + 1 + 2 + 3
   static_assert(NWAVE == 8, "two-phase reduction assumes 8 waves");
@@ -829,14 +832,23 @@ void launch_router(const Dims& D, const void* x, const float* Wr, const float* b
                    const float* gamma, const float* rs, float* logits_out, const ScanArgs& sa,
                    hipStream_t s) {
   const dim3 grid(D.nblk, D.router_splits);
-  if (D.bf16)
-    router_topk_kernel<bf16_t><<<grid, kRouterMfmaThreads, 0, s>>>(
-        (const bf16_t*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts,
-        blk_prob, gamma, rs, logits_out);
-  else
-    router_topk_kernel<float><<<grid, kRouterMfmaThreads, 0, s>>>(
-        (const float*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w, blk_counts,
-        blk_prob, gamma, rs, logits_out);
+  auto run = [&](auto mb) {
+    constexpr int MB = decltype(mb)::value;
+    if (D.bf16)
+      router_topk_kernel<bf16_t, MB><<<grid, kRouterMfmaThreads, 0, s>>>(
+          (const bf16_t*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w,
+          blk_counts, blk_prob, gamma, rs, logits_out);
+    else
+      router_topk_kernel<float, MB><<<grid, kRouterMfmaThreads, 0, s>>>(
+          (const float*)x, Wr, bias, D.T, D.d, D.E, D.k, D.router_splits, part, idx, w,
+          blk_counts, blk_prob, gamma, rs, logits_out);
+  };
+  switch ((D.E + 15) / 16) {
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    case 3: run(std::integral_constant<int, 3>{}); break;
+    default: run(std::integral_constant<int, 4>{}); break;
+  }
   if (D.router_splits > 1)
     router_select_kernel<<<D.nblk, kSelectThreads, 0, s>>>(
         part, bias, D.T, D.E, D.k, D.router_splits, idx, w, blk_counts, blk_prob, rs, logits_out,
