@@ -159,7 +159,14 @@ def row_chunk_tokens(idx, E, chunk, seed=0):
     return np.array(sorted(toks), dtype=np.int64)
 
 
-@pytest.mark.parametrize("workload", ["prefill", "fine", "skewed"])
+# smaller shapes whose token tiles fill four rounds of the CUs, so that dX
+# runs as one K = 2 d_ff pass: at seed 0 the schedule splits the last 8 token
+# tiles into K halves (the second in W3 alone), at seed 1 nothing is split
+ONE_PART = {"onepart_split": (MoEConfig("bwd_onepart", 2048, 4096, 256, 16, 8, "bf16"), 0),
+            "onepart": (MoEConfig("bwd_onepart", 2048, 4096, 256, 16, 8, "bf16"), 1)}
+
+
+@pytest.mark.parametrize("workload", ["prefill", "fine", "skewed", "onepart_split", "onepart"])
 def test_backward_prefill_sampled(workload):
     # the full shapes of the benchmark (T = 4096: the Mixtral layer, and 64
     # experts of d_ff 3584 with top-8; T = 8192 with skewed routing), checked
@@ -174,11 +181,11 @@ def test_backward_prefill_sampled(workload):
     # of the weight-gradient GEMMs along d_ff, all of their tiles along
     # d_model)
     from sparse_mixture_experts_scan_amd.inputs import CONFIGS
-    cfg = CONFIGS[workload]
+    cfg, seed = ONE_PART[workload] if workload in ONE_PART else (CONFIGS[workload], 0)
     announce(f"case {workload} T={cfg.T} d={cfg.d_model} f={cfg.d_ff} E={cfg.E} k={cfg.k} "
-             "stratified")
-    inp = make_inputs(cfg, seed=0)
-    dout = make_dout(cfg, seed=0)
+             f"seed={seed} stratified")
+    inp = make_inputs(cfg, seed=seed)
+    dout = make_dout(cfg, seed=seed)
     d = H.upload(inp)
     idx_t = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
     moe.forward(d["x"], d["W_router"], d["W_gate"], d["W_up"], d["W_down"], cfg.k,
