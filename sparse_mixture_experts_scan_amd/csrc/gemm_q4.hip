@@ -38,10 +38,18 @@ namespace {
 
 constexpr int kQ4Threads = 256;
 // cache policy of the LDS-staged form's code DMA (gfx950 bits: 1 sc0, 2 nt,
-// 16 sc1): non-temporal, measured on MI355X at the Mixtral decode shape with
-// group 128: gate/up 97.0 -> 95.8 us, down 50.6 -> 46.6 us
+// 16 sc1), measured on MI355X at the Mixtral decode shape with group 128:
+// non-temporal for the down codes (50.6 -> 46.6 us); for gate/up on the up
+// codes only (95 -> 91.6 us; on both 95, on neither 97, on the gate codes
+// only 91.7)
 #ifndef MOE_Q4_CPOL
-#define MOE_Q4_CPOL 2
+#define MOE_Q4_CPOL 2                 // down codes
+#endif
+#ifndef MOE_Q4_CPOL_GU0
+#define MOE_Q4_CPOL_GU0 0             // gate codes (Q1) of the gate/up kernel
+#endif
+#ifndef MOE_Q4_CPOL_GU1
+#define MOE_Q4_CPOL_GU1 2             // up codes (Q3)
 #endif
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -615,10 +623,16 @@ __device__ __forceinline__ void stream_q4_dma_body(
     const int run = wave + NWAVE * min(i, nb - 1);
     const uint32_t so = (uint32_t)run * kRunBytes;
 #pragma unroll
-    for (int j = 0; j < kDma; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[(8 * j) / FT],
-                                               (lds_void*)(slot + wave * kSlot + j * 1024), 16,
-                                               dvo[j], so, 0, MOE_Q4_CPOL);
+    for (int j = 0; j < kDma; ++j) {
+      lds_void* dst = (lds_void*)(slot + wave * kSlot + j * 1024);
+      if (!GATEUP)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[0], dst, 16, dvo[j], so, 0, MOE_Q4_CPOL);
+      else if ((8 * j) / FT == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[0], dst, 16, dvo[j], so, 0, MOE_Q4_CPOL_GU0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[NW - 1], dst, 16, dvo[j], so, 0,
+                                                 MOE_Q4_CPOL_GU1);
+    }
     // the groups of the run's two chunks
     const uint32_t g0 = (uint32_t)(2 * run) / (uint32_t)cpg;
     const uint32_t g1 = (uint32_t)(2 * run + 1) / (uint32_t)cpg;

@@ -34,11 +34,15 @@ namespace moe {
 
 constexpr int kStreamThreads = 256;
 // cache policy of the LDS-staged kernel's weight DMA (gfx950 bits: 1 sc0,
-// 2 nt, 16 sc1).  Non-temporal for the down GEMM: measured on MI355X at the
-// Mixtral decode shape, 0.164 -> 0.150 ms; the gate/up GEMM keeps the
-// default (0.330 ms against 0.338 with nt).
+// 2 nt, 16 sc1), measured on MI355X at the Mixtral decode shape:
+// non-temporal for the down GEMM (0.164 -> 0.150 ms); for gate/up on the up
+// matrix only (0.329 -> 0.319 ms; on the gate matrix only 0.322, on both
+// 0.338)
 #ifndef MOE_WSTREAM_CPOL_GU
-#define MOE_WSTREAM_CPOL_GU 0
+#define MOE_WSTREAM_CPOL_GU 0     // gate matrix (W1)
+#endif
+#ifndef MOE_WSTREAM_CPOL_GU1
+#define MOE_WSTREAM_CPOL_GU1 2    // up matrix (W3)
 #endif
 #ifndef MOE_WSTREAM_CPOL_DN
 #define MOE_WSTREAM_CPOL_DN 2
@@ -340,11 +344,18 @@ __device__ __forceinline__ void stream_dma_body(
     const int run = wave + NWAVE * min(i, nb - 1);
     const uint32_t so = (uint32_t)run * kRunBytes;
 #pragma unroll
-    for (int j = 0; j < kDma; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[(4 * j) / FT],
-                                               (lds_void*)(slot + wave * kSlot + j * 1024), 16,
-                                               dvo[j], so, 0,
-                                               GATEUP ? MOE_WSTREAM_CPOL_GU : MOE_WSTREAM_CPOL_DN);
+    for (int j = 0; j < kDma; ++j) {
+      lds_void* dst = (lds_void*)(slot + wave * kSlot + j * 1024);
+      if (!GATEUP)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[0], dst, 16, dvo[j], so, 0,
+                                                 MOE_WSTREAM_CPOL_DN);
+      else if ((4 * j) / FT == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[0], dst, 16, dvo[j], so, 0,
+                                                 MOE_WSTREAM_CPOL_GU);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[GATEUP ? 1 : 0], dst, 16, dvo[j], so, 0,
+                                                 MOE_WSTREAM_CPOL_GU1);
+    }
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
