@@ -410,6 +410,18 @@ __device__ __forceinline__ void scatter_rows_block(
 // expert_scan_block and scatter_rows_block for one block.  Every value that
 // a later phase needs stays in LDS and the barriers are LDS-only, so the
 // outputs' global stores drain once, at the end of the kernel.
+// The expert whose padded segment holds row r < off[E]: the first x with
+// off[x + 1] > r (empty segments are skipped), by binary search.
+__device__ inline int tile_owner(const int* off, int E, int r) {
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid + 1] > r) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
 __device__ __forceinline__ void select_single_block(
     const float (*slog)[65], int* hist, int nT, int E, int k, int BT, int max_rows,
     int max_tiles, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
@@ -432,14 +444,18 @@ __device__ __forceinline__ void select_single_block(
     sinv[tid] = 1.f / z;
   }
   lds_barrier();
-  // expert scan: segments padded to BT rows
-  if (tid == 0) {
-    int off = 0;
-    for (int x = 0; x < E; ++x) {
-      s_off[x] = off;
-      off += (hist[x] + BT - 1) / BT * BT;
+  // expert scan: segments padded to BT rows, offsets by wave 0 (lane =
+  // expert)
+  if (tid < 64) {
+    const int pad = tid < E ? (hist[tid] + BT - 1) / BT * BT : 0;
+    int run = pad;
+#pragma unroll
+    for (int st = 1; st < 64; st <<= 1) {
+      const int o = __shfl_up(run, st);
+      if (tid >= st) run += o;
     }
-    s_off[E] = off;
+    if (tid < E) s_off[tid] = run - pad;
+    if (tid == E - 1) s_off[E] = run;
   }
   if (blk_prob && tid < E) {              // p_i: the mean full-softmax probability
     float acc = 0.f;
@@ -464,16 +480,18 @@ __device__ __forceinline__ void select_single_block(
   }
   for (int i = tid; i < max_tiles; i += kRouterThreads) {
     int ex = -1;
-    if (i < ntiles) {
-      const int r = i * BT;
-      ex = 0;
-      while (s_off[ex + 1] <= r) ++ex;
-    }
+    if (i < ntiles) ex = tile_owner(s_off, E, i * BT);
     sa.tile_expert[i] = ex;
   }
-  for (int x = 0; x < E; ++x)
-    for (int r = s_off[x] + hist[x] + tid; r < s_off[x + 1]; r += kRouterThreads)
-      sa.row_token[r] = -1;
+  {
+    // padding rows: expert x's by its kRouterThreads / Epow2 threads
+    int ep = 1;
+    while (ep < E) ep <<= 1;
+    const int x = tid % ep;
+    if (x < E)
+      for (int r = s_off[x] + hist[x] + tid / ep; r < s_off[x + 1]; r += kRouterThreads / ep)
+        sa.row_token[r] = -1;
+  }
   for (int r = P + tid; r < max_rows; r += kRouterThreads) sa.row_token[r] = -1;
   if (blk_prob && tid == 0 && sa.loss_out) {   // N * sum_i f_i p_i
     float L = 0.f;
@@ -575,51 +593,74 @@ __device__ __forceinline__ void expert_scan_block(
     int32_t* __restrict__ tile_expert, int32_t* __restrict__ row_token,
     int32_t* __restrict__ counts_out, int nT, const float* __restrict__ blk_prob,
     float* __restrict__ prob_out, float* __restrict__ loss_out, const ScanArgs& sa) {
+  constexpr int kBatch = 32;                  // block counts a thread holds in flight
   __shared__ int part[256];
   __shared__ int s_cnt[64];
   __shared__ int s_off[65];
   const int tid = threadIdx.x;
-  // block chunks scanned in parallel per expert (no more chunks than blocks:
-  // one thread per expert then walks the chunks in order)
+  // thread (e, c) = (tid % Epow2, tid / Epow2) sums chunk c of expert e's
+  // per-block counts (C chunks, no more than blocks); its exclusive base is
+  // then the sum of the earlier chunks
   const int C = min(256 / Epow2, max(nblk, 1));
   const int e = tid % Epow2, c = tid / Epow2;
   const int per = (nblk + C - 1) / C;
   const int b0 = min(nblk, c * per), b1 = min(nblk, b0 + per);
+  int v[kBatch];
   int sum = 0;
-  // unrolled so that the loads of a chunk are in flight together (with 64
-  // experts a thread walks 32 blocks per chunk)
   if (e < E) {
-#pragma unroll 8
-    for (int b = b0; b < b1; ++b) sum += blk[(size_t)b * E + e];
-  }
-  part[tid] = sum;
-  __syncthreads();
-  if (tid < E) {
-    int run = 0;
-    for (int cc = 0; cc < C; ++cc) {
-      const int v = part[cc * Epow2 + tid];
-      part[cc * Epow2 + tid] = run;
-      run += v;
+    for (int b = b0; b < b1; b += kBatch) {
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) v[i] = b + i < b1 ? blk[(size_t)(b + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) sum += v[i];
     }
-    s_cnt[tid] = run;
   }
+  // inclusive scan over the chunks of each expert (Hillis-Steele)
+  int incl = sum;
+  part[tid] = incl;
   __syncthreads();
+  for (int st = 1; st < C; st <<= 1) {
+    const int add = c >= st ? part[tid - st * Epow2] : 0;
+    __syncthreads();
+    incl += add;
+    part[tid] = incl;
+    __syncthreads();
+  }
+  // per-block counts rewritten in place as exclusive per-expert bases (from
+  // the registers when the chunk fits one batch)
   if (e < E) {
-    int run = part[tid];
-#pragma unroll 8
-    for (int b = b0; b < b1; ++b) {
-      const int v = blk[(size_t)b * E + e];
-      blk[(size_t)b * E + e] = run;
-      run += v;
+    int run = incl - sum;
+    if (per <= kBatch) {
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i)
+        if (b0 + i < b1) {
+          blk[(size_t)(b0 + i) * E + e] = run;
+          run += v[i];
+        }
+    } else {
+      for (int b = b0; b < b1; ++b) {
+        const int x = blk[(size_t)b * E + e];
+        blk[(size_t)b * E + e] = run;
+        run += x;
+      }
     }
   }
-  if (tid == 0) {
-    int off = 0;
-    for (int x = 0; x < E; ++x) {
-      s_off[x] = off;
-      off += (s_cnt[x] + BT - 1) / BT * BT;
+  // segments padded to BT rows; offsets = exclusive scan of the padded
+  // counts, by wave 0 (lane = expert)
+  if (tid < 64) {
+    const int cnt = tid < E ? part[(C - 1) * Epow2 + tid] : 0;
+    const int pad = (cnt + BT - 1) / BT * BT;
+    int run = pad;
+#pragma unroll
+    for (int st = 1; st < 64; st <<= 1) {
+      const int o = __shfl_up(run, st);
+      if (tid >= st) run += o;
     }
-    s_off[E] = off;
+    if (tid < E) {
+      s_cnt[tid] = cnt;
+      s_off[tid] = run - pad;
+    }
+    if (tid == E - 1) s_off[E] = run;
   }
   __syncthreads();
   if (tid < E) {
@@ -633,17 +674,17 @@ __device__ __forceinline__ void expert_scan_block(
     *num_tiles = ntiles;
     if (sa.down_sched) write_down_schedule(sa, ntiles, BT);
   }
+  // each token tile's expert
   for (int i = tid; i < max_tiles; i += 256) {
     int ex = -1;
     if (i < ntiles) {
-      const int r = i * BT;
-      ex = 0;
-      while (s_off[ex + 1] <= r) ++ex;
+      ex = tile_owner(s_off, E, i * BT);
     }
     tile_expert[i] = ex;
   }
-  for (int x = 0; x < E; ++x)
-    for (int r = s_off[x] + s_cnt[x] + tid; r < s_off[x + 1]; r += 256) row_token[r] = -1;
+  // padding rows: expert e's by its 256 / Epow2 threads
+  if (e < E)
+    for (int r = s_off[e] + s_cnt[e] + c; r < s_off[e + 1]; r += 256 / Epow2) row_token[r] = -1;
   for (int r = P + tid; r < max_rows; r += 256) row_token[r] = -1;
 
   // router statistics (the load-balancing loss): p_i = mean full-softmax
