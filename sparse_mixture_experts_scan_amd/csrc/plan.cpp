@@ -34,9 +34,10 @@ int router_splits_for(int nblk, int d, int E) {
   // few experts (measured on MI355X with d_model 4096: for 8 experts, 512
   // blocks take T = 4096 from 44 to 34 us and T = 8192 from 70 to 52 us
   // against 256; for 64 experts, whose blocks each do 8 times the MFMA work,
-  // 256 stay faster); each split keeps a whole number of 16-element k-groups
+  // 256 stay faster); each split keeps a whole number of 32-element k-groups
+  // (the K of one bf16 MFMA 16x16x32 of the score kernel)
   const int min_blocks = E <= 16 ? 2 * kCus : kCus;
-  const int groups = d / 16;
+  const int groups = d / 32;
   int sp = 1;
   while (nblk * sp < min_blocks && sp * 2 <= kMaxRouterSplits && groups % (sp * 2) == 0)
     sp *= 2;

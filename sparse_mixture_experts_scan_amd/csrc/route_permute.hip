@@ -55,10 +55,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x,
 
 // ---------------------------------------------------------------------------
 // a1: router.  One block = kRouterTokens tokens (two 16-token MFMA columns) x
-// all E experts (16-expert MFMA rows, zero-padded).  Scores are an fp32 GEMM
-// on v_mfma_f32_16x16x4_f32: A = W_router^T (expert rows), B = x^T (token
-// columns, bf16 widened exactly), K = d_model split over 8 waves in
-// interleaved 16-element groups; wave partials are added in fixed order.
+// all E experts (16-expert MFMA rows, zero-padded).  Scores are an fp32 GEMM:
+// A = W_router^T (expert rows), B = x^T (token columns).  bf16 tokens: each
+// fp32 weight is split exactly into three bf16 pieces, each multiplied on
+// v_mfma_f32_16x16x32_bf16 (bf16 products are exact in fp32); float32
+// tokens: v_mfma_f32_16x16x4_f32.  K = d_model split over 8 waves in
+// interleaved 32- (bf16) or 16-element groups; wave partials are added in
+// fixed order.
 // Top-k: one thread per token, k passes of an arg-max over E (strict '>' in
 // ascending expert order, so equal scores go to the lower index).
 // Softmax over the selected k, shifted by the largest selected score.
@@ -75,6 +78,21 @@ __device__ inline f32x4 load4_f32<bf16_t>(const bf16_t* p) {
   const uint2 v = *reinterpret_cast<const uint2*>(p);
   return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
                __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+}
+
+// Three bf16 pieces of an fp32 value, by truncation: hi keeps its sign,
+// exponent and first 8 significant bits, mid the next 8 of the exact
+// remainder, lo what is left (at most 8 bits), so w = hi + mid + lo exactly
+// for |w| >= 2^-110 (below that lo falls under fp32's normal range and may
+// lose bits).  Returned as bf16 bit patterns.
+__device__ inline void split_bf16x3(float w, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const uint32_t hb = __float_as_uint(w) & 0xffff0000u;
+  const float r1 = w - __uint_as_float(hb);        // exact: the low 16 bits of w
+  const uint32_t mb = __float_as_uint(r1) & 0xffff0000u;
+  const float r2 = r1 - __uint_as_float(mb);       // exact, at most 8 significant bits
+  hi = hb >> 16;
+  mid = mb >> 16;
+  lo = __float_as_uint(r2) >> 16;
 }
 
 constexpr int kRouterMfmaThreads = 512;  // 8 waves split K
@@ -218,11 +236,84 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
     for (int b = 0; b < NB; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   bool tok_ok[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) tok_ok[b] = t0 + b * 16 + m < nT;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    // bf16 tokens: each fp32 router weight (times gamma) is split into three
+    // bf16 pieces (split_bf16x3) and every piece goes through a bf16 MFMA
+    // 16x16x32 with the token values as they are.  bf16 products are exact
+    // in fp32, so this is the fp32 product summed in fp32, at 3 bf16 MFMAs
+    // (the pieces below hi in a second accumulator) per 32 k instead of 8
+    // fp32 16x16x4 ones.  K in 32-element groups; lane group g holds k
+    // 8 g .. 8 g + 7 of a group.
+    f32x4 acc2[MB][NB];
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc2[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16_t* xp[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      xp[b] = x + (size_t)(tok_ok[b] ? t0 + b * 16 + m : 0) * d + 8 * g;
+    const int ngroups = d / 32;                    // 32-element k-groups
+    const int gps = ngroups / splits;              // k-groups of this split
+    const int g0 = blockIdx.y * gps, g1 = g0 + gps;
+    for (int kb = g0 + wave; kb < g1; kb += NWAVE * U) {
+      uint4 bv[U][NB];
+      float wv[U][MB][8];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kg = kb + NWAVE * u;
+        const bool kok = kg < g1;
+        const int k0 = kg * 32 + 8 * g;            // this lane's 8 consecutive k
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          bv[u][b] = (kok && tok_ok[b]) ? *reinterpret_cast<const uint4*>(xp[b] + kg * 32)
+                                        : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int a = 0; a < MB; ++a) {
+          const int ex = a * 16 + m;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            wv[u][a][i] = (kok && ex < E) ? (gamma ? Wr[(size_t)(k0 + i) * E + ex] * gamma[k0 + i]
+                                                   : Wr[(size_t)(k0 + i) * E + ex])
+                                          : 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int a = 0; a < MB; ++a) {
+          uint32_t ph[4], pm[4], pl[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint32_t h0, m0, l0, h1, m1, l1;
+            split_bf16x3(wv[u][a][2 * i], h0, m0, l0);
+            split_bf16x3(wv[u][a][2 * i + 1], h1, m1, l1);
+            ph[i] = h0 | (h1 << 16);
+            pm[i] = m0 | (m1 << 16);
+            pl[i] = l0 | (l1 << 16);
+          }
+          const uint4 ah = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+          const uint4 am = make_uint4(pm[0], pm[1], pm[2], pm[3]);
+          const uint4 al = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            acc[a][b] = Elem<bf16_t>::mfma16(ah, bv[u][b], acc[a][b]);
+            acc2[a][b] = Elem<bf16_t>::mfma16(am, bv[u][b], acc2[a][b]);
+            acc2[a][b] = Elem<bf16_t>::mfma16(al, bv[u][b], acc2[a][b]);
+          }
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < MB; ++a)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[a][b] += acc2[a][b];
+  } else {
   const T* xp[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int t = t0 + b * 16 + m;
-    tok_ok[b] = t < nT;
     xp[b] = x + (size_t)(tok_ok[b] ? t : 0) * d + 4 * g;
   }
   const int ngroups = d / 16;                      // 16-element k-groups
@@ -264,6 +355,7 @@ __global__ __launch_bounds__(kRouterMfmaThreads) void router_topk_kernel(
 #pragma unroll
           for (int b = 0; b < NB; ++b)
             acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][a][i], bv[u][b][i], acc[a][b], 0, 0, 0);
+  }
   }
   // fixed-order reduction of the 8 wave partials: (w + w+4), then 0 + 1 + 2 + 3
   static_assert(NWAVE == 8, "two-phase reduction assumes 8 waves");
