@@ -84,6 +84,9 @@ SMALL = [
     MoEConfig("one_expert", 40, 64, 64, 1, 1, "f32"),
     MoEConfig("ragged33", 33, 192, 320, 6, 3, "bf16"),
     MoEConfig("many_tiles", 1000, 128, 256, 8, 2, "bf16"),
+    # the narrowest d_model: two 32-element k-groups of the bf16 score GEMM
+    MoEConfig("narrow_d64", 40, 64, 128, 8, 2, "bf16"),
+    MoEConfig("narrow_d64_one", 1, 64, 64, 4, 1, "bf16"),
     # weight-streaming form with K a multiple of 512 (persistent blocks that
     # each take several (token tile, feature tile) units, crossing tiles):
     # 32-row token tiles, then 16-row ones
