@@ -414,6 +414,7 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(
 // registers; the slice's ds rows are staged in LDS, kWgradChunk tokens at a
 // time, and read as broadcasts.
 constexpr int kWgradChunk = 128;       // tokens of a slice staged in LDS at once
+constexpr int kWgradLoads = 32;        // tokens whose x loads a thread issues together
 template <typename T, int EB>
 __global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(
     const T* __restrict__ x, const float* __restrict__ ds, int Tn, int d, int E, int tslice,
@@ -435,8 +436,9 @@ __global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(
     }
     __syncthreads();
     if (j <= d) {
-      for (int t = c0; t < c1; ++t) {
-        const float xv = j < d ? Elem<T>::to_f32(x[(size_t)t * d + j]) : 1.0f;
+      // kWgradLoads tokens' x loads in flight together, then their FMAs in
+      // token order (each accumulator still adds the tokens in order)
+      auto fma_row = [&](float xv, int t) {
         const float4* row = reinterpret_cast<const float4*>(sds[t - c0]);
 #pragma unroll
         for (int q4 = 0; q4 < EB / 4; ++q4) {
@@ -446,13 +448,34 @@ __global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(
           acc[4 * q4 + 2] = fmaf(xv, v.z, acc[4 * q4 + 2]);
           acc[4 * q4 + 3] = fmaf(xv, v.w, acc[4 * q4 + 3]);
         }
+      };
+      int t = c0;
+      for (; t + kWgradLoads <= c1; t += kWgradLoads) {
+        float xv[kWgradLoads];
+#pragma unroll
+        for (int u = 0; u < kWgradLoads; ++u)
+          xv[u] = j < d ? Elem<T>::to_f32(x[(size_t)(t + u) * d + j]) : 1.0f;
+#pragma unroll
+        for (int u = 0; u < kWgradLoads; ++u) fma_row(xv[u], t + u);
       }
+      for (; t < c1; ++t) fma_row(j < d ? Elem<T>::to_f32(x[(size_t)t * d + j]) : 1.0f, t);
     }
   }
-  if (j <= d)
+  if (j <= d) {
+    float* prow = part + ((size_t)s * (d + 1) + j) * E;
+    if (E % 4 == 0 && reinterpret_cast<uintptr_t>(part) % 16 == 0) {
+      // 16-byte stores of the row's E partial sums
 #pragma unroll
-    for (int q = 0; q < EB; ++q)
-      if (q < E) part[((size_t)s * (d + 1) + j) * E + q] = acc[q];
+      for (int q4 = 0; q4 < EB / 4; ++q4)
+        if (4 * q4 < E)
+          *reinterpret_cast<float4*>(prow + 4 * q4) =
+              make_float4(acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < EB; ++q)
+        if (q < E) prow[q] = acc[q];
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void bwd_router_wgrad_reduce(const float* __restrict__ part,
