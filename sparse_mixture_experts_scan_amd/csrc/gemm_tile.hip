@@ -462,7 +462,8 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
   // (work-groups reach the XCDs round robin, so work-group L runs on XCD
   // L % 8); inside a range, groups of `fgroup` feature tiles: consecutive
   // work-groups of an XCD take the group's feature tiles for one token tile,
-  // then the next token tile.  Then (down GEMM, down_sched) the K parts of
+  // then the next token tile (fgroup 0: expert-major, below).  Then (down
+  // GEMM, down_sched) the K parts of
   // the remaining token tiles' tiles, dispatched last so that they fill the
   // final round.  Work-groups past the list exit at once.
   const int nt = *num_tiles;                // token tiles in use
@@ -478,11 +479,25 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
   if (L < per_xcd * kXcds) {
     int Lp = (L % kXcds) * per_xcd + L / kXcds;
     if (Lp >= n_un) return;
-    const int grp = Lp / (fgroup * nu);
-    const int rem = Lp - grp * fgroup * nu;
-    const int gsize = min(fgroup, n_ft - grp * fgroup);
-    tt = rem / gsize;
-    ft = grp * fgroup + rem % gsize;
+    if (fgroup == 0) {
+      // expert-major: expert by expert (its unsplit token tiles first_tt ..
+      // first_tt + ntt - 1), feature tile by feature tile, token tile
+      // fastest, so that the tiles sharing a weight panel run back to back.
+      // The tiles before expert e number first_tt(e) * n_ft, so the expert
+      // of token tile Lp / n_ft is this tile's.
+      const int ex = tile_expert[Lp / n_ft];
+      const int first_tt = offsets[ex] / kTileBT;
+      const int ntt = min(offsets[ex + 1] / kTileBT, nu) - first_tt;
+      const int local = Lp - first_tt * n_ft;
+      ft = local / ntt;
+      tt = first_tt + local % ntt;
+    } else {
+      const int grp = Lp / (fgroup * nu);
+      const int rem = Lp - grp * fgroup * nu;
+      const int gsize = min(fgroup, n_ft - grp * fgroup);
+      tt = rem / gsize;
+      ft = grp * fgroup + rem % gsize;
+    }
   } else {
     const int n_sp = (nt - nu) * n_ft;      // split tiles
     const int i = L - per_xcd * kXcds;
@@ -561,17 +576,22 @@ __global__ __launch_bounds__(kTileThreads, 1) void tile_gemm_kernel(
                         part == 0);
 }
 
-// Feature tiles per XCD-local group of the tile order.  Consecutive
-// workgroups of one XCD take the group's feature tiles for one token tile,
-// then the next token tile, so about 32 / fgroup token tiles share each
-// weight panel while they run.  Measured on MI355X: groups of 4 are best for
-// gate/up (against 2, 3, 5, 6, 7 and 8: 0.5-2% slower); for down, 4 with
-// about 1000 or more rows per expert (4+ token tiles; 3 and 6 are 0.5-1%
-// slower) and 2 with about 500 (E = 64, top-8; 1, 3 and 4 are 2-4% slower).
+// The tile order: feature tiles per XCD-local group (consecutive workgroups
+// of one XCD take the group's feature tiles for one token tile, then the
+// next token tile, so about 32 / fgroup token tiles share each weight panel
+// while they run), or 0 for the expert-major order.  Measured on MI355X:
+// gate/up with fewer than 6 token tiles per expert runs expert-major (on the
+// Mixtral prefill shape, 4 tiles per expert, gate/up is even and the down
+// GEMM that follows 2.6% faster, 0.9% on the step, on two boxes; the 64-
+// expert top-8 shape is even); with more (skewed routing, 8 on average) in
+// groups of 4 (expert-major 2% slower; 2, 3, 5, 6, 7 and 8 0.5-2% slower).
+// Down: groups of 4 with about 1000 or more rows per expert (4+ token tiles;
+// 3 and 6 are 0.5-1% slower, expert-major even to 1% slower) and 2 with
+// about 500 (E = 64, top-8; 1, 3 and 4 are 2-4% slower).
 static int tile_feat_group(const Dims& D, bool gateup) {
   const int64_t rows_per_expert = (int64_t)D.T * D.k / D.E;
-  if (gateup || rows_per_expert >= 3 * kTileBT) return 4;
-  return 2;
+  if (gateup) return rows_per_expert < 6 * kTileBT ? 0 : 4;
+  return rows_per_expert >= 3 * kTileBT ? 4 : 2;
 }
 
 template <bool GATEUP>
