@@ -618,19 +618,23 @@ __device__ __forceinline__ void stream_q4_dma_body(
 
   uint4 t0[NT][2][4], t1[NT][2][4];
   // run i of this wave (clamped to its last run, so that every issue has
-  // the same number of loads)
+  // the same number of loads); a run past the last (the steady state issues
+  // one; nothing reads its slot) takes offsets past the buffer ranges: it
+  // loads zeros and moves no bytes
   auto issue = [&](char* slot, float* ss, uint4 (&tk)[NT][2][4], int i) {
+    const bool past = i >= nb;
     const int run = wave + NWAVE * min(i, nb - 1);
     const uint32_t so = (uint32_t)run * kRunBytes;
 #pragma unroll
     for (int j = 0; j < kDma; ++j) {
       lds_void* dst = (lds_void*)(slot + wave * kSlot + j * 1024);
+      const uint32_t vo = past ? 0x80000000u : dvo[j];
       if (!GATEUP)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[0], dst, 16, dvo[j], so, 0, MOE_Q4_CPOL);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[0], dst, 16, vo, so, 0, MOE_Q4_CPOL);
       else if ((8 * j) / FT == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[0], dst, 16, dvo[j], so, 0, MOE_Q4_CPOL_GU0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[0], dst, 16, vo, so, 0, MOE_Q4_CPOL_GU0);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[NW - 1], dst, 16, dvo[j], so, 0,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[NW - 1], dst, 16, vo, so, 0,
                                                  MOE_Q4_CPOL_GU1);
     }
     // the groups of the run's two chunks
@@ -642,15 +646,17 @@ __device__ __forceinline__ void stream_q4_dma_body(
       for (int m = 0; m < kSDma; ++m)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs[w], (lds_void*)(ss + wave * kSSlot + w * kSReg + m * 64), 4,
-            sq[m] < 2 ? (uint32_t)sr[m] * 4 + (sq[m] ? g1 : g0) * sgrp : 0x80000000u, 0, 0, 0);
+            (sq[m] < 2 && !past) ? (uint32_t)sr[m] * 4 + (sq[m] ? g1 : g0) * sgrp : 0x80000000u,
+            0, 0, 0);
     const uint32_t ab = (uint32_t)run * (kRunK * 2);
+    const uint32_t aob = past ? 0x80000000u : 0u;
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          tk[n][q][j] = q4_load16(ra, ao[n] + 16 * j, ab + q * (kQ4Chunk * 2));
+          tk[n][q][j] = q4_load16(ra, (ao[n] | aob) + 16 * j, ab + q * (kQ4Chunk * 2));
   };
   const uint4 neg136 = make_uint4(kNeg136x2, kNeg136x2, kNeg136x2, kNeg136x2);
   const CodeConsts cc = CodeConsts::make();

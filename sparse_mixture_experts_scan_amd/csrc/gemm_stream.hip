@@ -340,26 +340,31 @@ __device__ __forceinline__ void stream_dma_body(
 
   uint4 t0[NT][4], t1[NT][4];
   // run i of this wave (clamped to its last run)
+  // Run i past the wave's last (the steady state issues one, so that every
+  // wait counts the same loads; nothing reads its slot) takes offsets past
+  // the buffer ranges: it loads zeros and moves no bytes.
   auto issue = [&](char* slot, uint4 (&tk)[NT][4], int i) {
+    const bool past = i >= nb;
     const int run = wave + NWAVE * min(i, nb - 1);
     const uint32_t so = (uint32_t)run * kRunBytes;
 #pragma unroll
     for (int j = 0; j < kDma; ++j) {
       lds_void* dst = (lds_void*)(slot + wave * kSlot + j * 1024);
+      const uint32_t vo = past ? 0x80000000u : dvo[j];
       if (!GATEUP)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[0], dst, 16, dvo[j], so, 0,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[0], dst, 16, vo, so, 0,
                                                  MOE_WSTREAM_CPOL_DN);
       else if ((4 * j) / FT == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[0], dst, 16, dvo[j], so, 0,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[0], dst, 16, vo, so, 0,
                                                  MOE_WSTREAM_CPOL_GU);
       else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[GATEUP ? 1 : 0], dst, 16, dvo[j], so, 0,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw[GATEUP ? 1 : 0], dst, 16, vo, so, 0,
                                                  MOE_WSTREAM_CPOL_GU1);
     }
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) tk[n][ks] = sload(ra, ao[n], so + ks * 64);
+      for (int ks = 0; ks < 4; ++ks) tk[n][ks] = sload(ra, past ? 0x80000000u : ao[n], so + ks * 64);
   };
   auto compute = [&](const char* slot, const uint4 (&tk)[NT][4]) {
 #pragma unroll
