@@ -256,8 +256,9 @@ __global__ __launch_bounds__(kStreamThreads) void stream_gemm_kernel(
 // without bank conflicts.  Two slots (separate arrays, so that the compiler
 // can tell which DMA each read waits for) alternate: run i + 1 is in flight
 // while run i's MFMAs run.  Every step issues its loads unconditionally (past
-// the wave's last run it re-reads that run, from L2), so the waits before the
-// reads never depend on a branch.  Token rows as in the register form.
+// the wave's last run with offsets beyond the buffer ranges, which load
+// zeros and move no bytes), so the waits before the reads never depend on a
+// branch.  Token rows as in the register form.
 // ---------------------------------------------------------------------------
 template <int BT, int FT, bool GATEUP>
 __device__ __forceinline__ void stream_dma_body(
@@ -339,10 +340,10 @@ __device__ __forceinline__ void stream_dma_body(
   }
 
   uint4 t0[NT][4], t1[NT][4];
-  // run i of this wave (clamped to its last run)
-  // Run i past the wave's last (the steady state issues one, so that every
-  // wait counts the same loads; nothing reads its slot) takes offsets past
-  // the buffer ranges: it loads zeros and moves no bytes.
+  // Run i of this wave (clamped to its last run).  A run past the wave's
+  // last (the steady state issues one, so that every wait counts the same
+  // loads; nothing reads its slot) takes offsets past the buffer ranges: it
+  // loads zeros and moves no bytes.
   auto issue = [&](char* slot, uint4 (&tk)[NT][4], int i) {
     const bool past = i >= nb;
     const int run = wave + NWAVE * min(i, nb - 1);
