@@ -201,7 +201,7 @@ def test_workload_full_tensor(name):
 
 
 # other seeds: a tile-stratified token sample
-@pytest.mark.parametrize("name,seed", [("prefill", 1), ("fine", 2)])
+@pytest.mark.parametrize("name,seed", [("prefill", 1), ("fine", 2), ("skewed", 1)])
 def test_workload_tile_sampled(name, seed):
     res, _ = full_check(CONFIGS[name], seed=seed, value_tokens="tiles")
     assert res["layout"].gemm_variant == 1
