@@ -29,14 +29,35 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x,
                                                       const float* __restrict__ weight, float eps,
                                                       int d, float* __restrict__ rs_out,
                                                       T* __restrict__ xn) {
+  // 16-byte chunks of the row (d is a multiple of 64): thread tid takes
+  // chunks tid, tid + 256, ... in both passes; the second re-reads them
+  constexpr int V = 16 / sizeof(T);
   const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float wsum[4];
   __shared__ float s_rs;
   const T* xr = x + (size_t)t * d;
+  const int nch = d / V;
+  auto widen = [](const uint4& raw, float (&v)[V]) {
+    if constexpr (V == 8) {
+      const uint32_t* p = &raw.x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(p[i] << 16);
+        v[2 * i + 1] = __uint_as_float(p[i] & 0xffff0000u);
+      }
+    } else {
+      v[0] = __uint_as_float(raw.x);
+      v[1] = __uint_as_float(raw.y);
+      v[2] = __uint_as_float(raw.z);
+      v[3] = __uint_as_float(raw.w);
+    }
+  };
   float ss = 0.f;
-  for (int j = tid; j < d; j += 256) {
-    const float v = Elem<T>::to_f32(xr[j]);
-    ss = fmaf(v, v, ss);
+  for (int c = tid; c < nch; c += 256) {
+    float v[V];
+    widen(*reinterpret_cast<const uint4*>(xr + (size_t)c * V), v);
+#pragma unroll
+    for (int i = 0; i < V; ++i) ss = fmaf(v[i], v[i], ss);
   }
   // fixed-order reduction: lanes by xor-shuffle, then the 4 waves in order
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
@@ -49,8 +70,32 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const T* __restrict__ x,
   }
   __syncthreads();
   const float r = s_rs;
-  for (int j = tid; j < d; j += 256)
-    xn[(size_t)t * d + j] = Elem<T>::from_f32(Elem<T>::to_f32(xr[j]) * r * weight[j]);
+  const bool w16 = reinterpret_cast<uintptr_t>(weight) % 16 == 0;
+  for (int c = tid; c < nch; c += 256) {
+    float v[V];
+    widen(*reinterpret_cast<const uint4*>(xr + (size_t)c * V), v);
+    const float* wc = weight + (size_t)c * V;
+    float o[V];
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      // the weight needs only 4-byte alignment: 16-byte loads when it has it
+      const float4 w = w16 ? reinterpret_cast<const float4*>(wc)[q]
+                           : make_float4(wc[4 * q], wc[4 * q + 1], wc[4 * q + 2], wc[4 * q + 3]);
+      o[4 * q] = v[4 * q] * r * w.x;
+      o[4 * q + 1] = v[4 * q + 1] * r * w.y;
+      o[4 * q + 2] = v[4 * q + 2] * r * w.z;
+      o[4 * q + 3] = v[4 * q + 3] * r * w.w;
+    }
+    uint4 out;
+    if constexpr (V == 8) {
+      out = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                       pack_bf16x2(o[6], o[7]));
+    } else {
+      out = make_uint4(__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                       __float_as_uint(o[3]));
+    }
+    *reinterpret_cast<uint4*>(xn + (size_t)t * d + (size_t)c * V) = out;
+  }
 }
 
 // ---------------------------------------------------------------------------
