@@ -415,6 +415,7 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(
 // time, and read as broadcasts.
 constexpr int kWgradChunk = 128;       // tokens of a slice staged in LDS at once
 constexpr int kWgradLoads = 32;        // tokens whose x loads a thread issues together
+constexpr int kWgrad8Loads = 8;        // the same for the eight-column form (16-byte loads)
 template <typename T, int EB>
 __global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(
     const T* __restrict__ x, const float* __restrict__ ds, int Tn, int d, int E, int tslice,
@@ -475,6 +476,90 @@ __global__ __launch_bounds__(256) void bwd_router_wgrad_kernel(
       for (int q = 0; q < EB; ++q)
         if (q < E) prow[q] = acc[q];
     }
+  }
+}
+
+// The same partial sums for few experts (EB <= 16), eight consecutive
+// columns per thread: one 16-byte load of x per token, 8 x EB accumulators.
+// Chunk c = d / 8 is the bias column (x = 1) alone.  Same token order for
+// every sum as bwd_router_wgrad_kernel, so the same results.
+template <int EB>
+__global__ __launch_bounds__(64) void bwd_router_wgrad8_kernel(
+    const bf16_t* __restrict__ x, const float* __restrict__ ds, int Tn, int d, int E, int tslice,
+    float* __restrict__ part) {
+  __shared__ float sds[kWgradChunk][EB];
+  const int c = blockIdx.x * 64 + threadIdx.x;   // 8-column chunk; d / 8 = the bias
+  const int nch = d / 8;
+  const int s = blockIdx.y;
+  const int t0 = s * tslice, t1 = min(Tn, t0 + tslice);
+  float acc[8][EB];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int q = 0; q < EB; ++q) acc[i][q] = 0.f;
+  for (int c0 = t0; c0 < t1; c0 += kWgradChunk) {
+    const int c1 = min(t1, c0 + kWgradChunk);
+    __syncthreads();
+    for (int i = threadIdx.x; i < (c1 - c0) * EB; i += 64) {
+      const int t = c0 + i / EB, e = i % EB;
+      sds[i / EB][e] = e < E ? ds[(size_t)t * E + e] : 0.f;
+    }
+    __syncthreads();
+    if (c <= nch) {
+      auto fma_row = [&](const uint4& xv, int t) {
+        float xf[8];
+        if (c < nch) {
+          const uint32_t* p = &xv.x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            xf[2 * i] = __uint_as_float(p[i] << 16);
+            xf[2 * i + 1] = __uint_as_float(p[i] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) xf[i] = i == 0 ? 1.0f : 0.f;
+        }
+        const float4* row = reinterpret_cast<const float4*>(sds[t - c0]);
+#pragma unroll
+        for (int q4 = 0; q4 < EB / 4; ++q4) {
+          const float4 v = row[q4];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            acc[i][4 * q4] = fmaf(xf[i], v.x, acc[i][4 * q4]);
+            acc[i][4 * q4 + 1] = fmaf(xf[i], v.y, acc[i][4 * q4 + 1]);
+            acc[i][4 * q4 + 2] = fmaf(xf[i], v.z, acc[i][4 * q4 + 2]);
+            acc[i][4 * q4 + 3] = fmaf(xf[i], v.w, acc[i][4 * q4 + 3]);
+          }
+        }
+      };
+      int t = c0;
+      for (; t + kWgrad8Loads <= c1; t += kWgrad8Loads) {
+        uint4 xv[kWgrad8Loads];
+#pragma unroll
+        for (int u = 0; u < kWgrad8Loads; ++u)
+          xv[u] = c < nch ? *reinterpret_cast<const uint4*>(x + (size_t)(t + u) * d + 8 * c)
+                          : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < kWgrad8Loads; ++u) fma_row(xv[u], t + u);
+      }
+      for (; t < c1; ++t)
+        fma_row(c < nch ? *reinterpret_cast<const uint4*>(x + (size_t)t * d + 8 * c)
+                        : make_uint4(0, 0, 0, 0), t);
+    }
+  }
+  if (c < nch) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float* prow = part + ((size_t)s * (d + 1) + 8 * c + i) * E;
+#pragma unroll
+      for (int q = 0; q < EB; ++q)
+        if (q < E) prow[q] = acc[i][q];
+    }
+  } else if (c == nch) {
+    float* prow = part + ((size_t)s * (d + 1) + d) * E;
+#pragma unroll
+    for (int q = 0; q < EB; ++q)
+      if (q < E) prow[q] = acc[0][q];
   }
 }
 
@@ -677,8 +762,14 @@ void launch_bwd_router_wgrad(const Dims& D, const void* x, const float* ds, floa
     bwd_router_wgrad_kernel<bf16_t, decltype(eb)::value><<<grid, 256, 0, s>>>(
         (const bf16_t*)x, ds, D.T, D.d, D.E, tslice, part);
   };
-  if (D.E <= 8) run(std::integral_constant<int, 8>{});
-  else if (D.E <= 16) run(std::integral_constant<int, 16>{});
+  // few experts: eight columns a thread (one 16-byte x load per token)
+  const dim3 grid8((D.d / 8 + 1 + 63) / 64, slices);
+  if (D.E <= 8)
+    bwd_router_wgrad8_kernel<8><<<grid8, 64, 0, s>>>((const bf16_t*)x, ds, D.T, D.d, D.E, tslice,
+                                                     part);
+  else if (D.E <= 16)
+    bwd_router_wgrad8_kernel<16><<<grid8, 64, 0, s>>>((const bf16_t*)x, ds, D.T, D.d, D.E,
+                                                      tslice, part);
   else if (D.E <= 32) run(std::integral_constant<int, 32>{});
   else run(std::integral_constant<int, 64>{});
   bwd_router_wgrad_reduce<<<((D.d + 1) * D.E + 255) / 256, 256, 0, s>>>(part, slices, D.d, D.E,
