@@ -176,7 +176,8 @@ def test_deterministic_bitwise():
 
 
 # seed 0 is the measured workload; seeds 1 and 2 are robustness runs
-@pytest.mark.parametrize("name,seed", [("tiny", 0), ("decode", 0), ("decode", 1), ("decode", 2)])
+@pytest.mark.parametrize("name,seed", [("tiny", 0), ("decode", 0), ("decode", 1), ("decode", 2),
+                                       ("decode", 3)])
 def test_workload_all_tokens(name, seed):
     full_check(CONFIGS[name], seed=seed)
 
@@ -201,7 +202,8 @@ def test_workload_full_tensor(name):
 
 
 # other seeds: a tile-stratified token sample
-@pytest.mark.parametrize("name,seed", [("prefill", 1), ("fine", 2), ("skewed", 1)])
+@pytest.mark.parametrize("name,seed", [("prefill", 1), ("prefill", 3), ("fine", 2), ("fine", 3),
+                                       ("skewed", 1), ("skewed", 2)])
 def test_workload_tile_sampled(name, seed):
     res, _ = full_check(CONFIGS[name], seed=seed, value_tokens="tiles")
     assert res["layout"].gemm_variant == 1
